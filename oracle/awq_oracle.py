@@ -1,0 +1,322 @@
+"""Plain, slow CPU oracle of the AWQ (Activation-aware Weight Quantization) hot path.
+
+TEST INFRASTRUCTURE ONLY: used by the tests, by the smoke check and by the
+``cpu_baseline`` leg of the benchmark. The product path never imports it, and it
+imports nothing from the product path.
+
+Sources (web pages; cited by title and section):
+
+* [AWQ-PRACTICE] "AWQ量化实战：无需重训，把大模型压进4bit显存" (xdnf.cn), the
+  practitioner's walk-through: §1.1 (RTN baseline), §1.3 (scale salient channels
+  by s > 1 before uniform low-bit quantization), §2.1 (weight is out x in,
+  channels are input channels, statistic = mean absolute activation), §2.2 (grid
+  search of s so that outputs before/after quantization agree; 1/s undone on the
+  other side), §2.3 (128 consecutive input channels share one step), §3.3 (the
+  per-layer steps: statistics -> search s -> 4-bit g128 quantize -> save scales).
+* [AWQ-SKILL] "AWQ量化技术Skill" (skillsbot.cn awq-quantization usage page),
+  "如何使用该技能 / 步骤 2": quant_config zero_point=True, q_group_size=128,
+  w_bit=4; "主要功能和特点": 70B model 140 GB -> 35 GB.
+* [GPTQ-VS-AWQ] "大模型量化部署实战：GPTQ与AWQ算法" (yunthe.com), section
+  "大模型量化的核心原理与位宽选择": a 4-bit integer plus a scale and a zero point
+  for dequantization; per-group (128) quantization.
+* [AWQ-WIKI] "什么是激活感知权重量化（AWQ）" (aiboss88.com), section "工作机制":
+  the protection is an equivalent transformation whose scale comes from offline
+  activation statistics; no backpropagation or reconstruction.
+
+Readings taken where the pages are silent (each is listed with its reason in the
+design notes of the repository):
+
+* codes are unsigned 0..15 with a zero point (asymmetric), dequant = (q - z) * scale;
+* min/max affine group quantizer, computed in fp32 with IEEE round-to-nearest-even;
+  the codes are rounded against the stored fp16 scale;
+* scale floored at 2^-14, clamped to 65504 (flagged);
+* statistic = plain mean of |x| over all calibration tokens;
+* s = (max(mean|x|, 2^-14))^alpha, alpha_i = i / n_grid, i = 0..n_grid-1, s stored as fp16;
+* error = sum of squares of X * D^T with D = W - Q(W diag(s)) diag(1/s), ties -> smallest i.
+
+Every function spells out the steps in order; numpy supplies only elementwise IEEE
+operations, reductions and (fp64) matrix products.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "GROUP", "QMAX", "N_GRID", "ACT_FLOOR", "SCALE_FLOOR", "SCALE_MAX",
+    "FLAG_NONFINITE_INPUT", "FLAG_SCALE_CLAMPED",
+    "activation_mean_abs", "candidate_scales", "quantize_groups", "pack", "unpack",
+    "quantize_pack", "dequantize", "search_errors", "search_scales", "linear_reference",
+    "linear_within_tolerance", "fp16_midpoint_distance", "relative_gap", "packed_bytes",
+]
+
+GROUP = 128                       # [AWQ-PRACTICE] §2.3; [AWQ-SKILL] q_group_size
+QMAX = 15                         # 4-bit unsigned codes 0..15 with a zero point
+N_GRID = 20                       # alpha grid: 20 points in [0, 1)
+ACT_FLOOR = 2.0 ** -14            # floor of the activation statistic (smallest normal fp16)
+SCALE_FLOOR = np.float32(2.0 ** -14)
+SCALE_MAX = np.float32(65504.0)   # largest finite fp16
+MAX_CALIB_TOKENS = 8192           # keeps the |x| column sums exact in fp64
+
+FLAG_NONFINITE_INPUT = 1
+FLAG_SCALE_CLAMPED = 2
+
+_F32 = np.float32
+_F64 = np.float64
+
+
+# --------------------------------------------------------------------------- a1
+def activation_mean_abs(X16: np.ndarray) -> tuple[np.ndarray, int]:
+    """Per-input-channel mean absolute activation, a_k = (1/T) sum_t |X_tk|.
+
+    [AWQ-PRACTICE] §2.1: accumulate the calibration activations per input channel and
+    take the mean absolute value ("激活强度"); a plain mean over all tokens.
+
+    Every fp16 value is an integer multiple of 2^-24 and below 2^16, so for
+    T <= 8192 every partial sum is a multiple of 2^-24 below 2^29 and is exact in
+    fp64: the summation order cannot matter, and the only rounding is the final
+    division by T (fp64, round-to-nearest-even).
+    Returns (a fp64 [K], flags).
+    """
+    X16 = np.asarray(X16)
+    assert X16.dtype == np.float16 and X16.ndim == 2
+    T = X16.shape[0]
+    assert 1 <= T <= MAX_CALIB_TOKENS
+    Xd = X16.astype(_F64)
+    flags = 0 if np.all(np.isfinite(Xd)) else FLAG_NONFINITE_INPUT
+    col_sum = np.abs(Xd).sum(axis=0)
+    a = col_sum / _F64(T)
+    return a, flags
+
+
+# --------------------------------------------------------------------------- a2
+def candidate_scales(a: np.ndarray, n_grid: int = N_GRID) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Candidate per-channel scales for each grid point.
+
+    [AWQ-PRACTICE] §1.3/§2.2 and [AWQ-WIKI] "工作机制": the scale comes from the
+    offline activation statistic and is picked by a grid search over a candidate
+    interval, one coefficient per layer (§5.1). Reading: s_ik = a_k^alpha_i with
+    alpha_i = i / n_grid, a floored at 2^-14; pow in fp64, then one
+    round-to-nearest-even conversion to fp16. alpha_0 = 0 gives s = 1 (plain RTN).
+    Returns (alpha fp64 [n_grid], s fp16 [n_grid][K], s_exact fp64 [n_grid][K]).
+    """
+    a = np.maximum(np.asarray(a, dtype=_F64), _F64(ACT_FLOOR))
+    alpha = np.arange(n_grid, dtype=_F64) / _F64(n_grid)
+    s64 = np.empty((n_grid, a.shape[0]), dtype=_F64)
+    for i in range(n_grid):
+        s64[i] = np.power(a, alpha[i])
+    s16 = s64.astype(np.float16)          # numpy converts fp64 -> fp16 in one RNE step
+    return alpha, s16, s64
+
+
+# --------------------------------------------------------------------------- a3
+def quantize_groups(W16: np.ndarray, s16: np.ndarray | None = None) -> dict:
+    """Group-wise asymmetric 4-bit quantization of W * diag(s).
+
+    [AWQ-PRACTICE] §2.3 (128 consecutive input channels share one step) and §2.1
+    (W is out x in, groups run along the input dimension); [GPTQ-VS-AWQ] (a 4-bit
+    integer with a scale and a zero point, dequant = (q - z) * scale);
+    [AWQ-SKILL] step 2 (w_bit 4, q_group_size 128, zero_point True).
+
+    Steps per row n and group j (k in [128 j, 128 j + 128)), all in fp32, RNE:
+      1. w' = f32(w) * f32(s)                  (exact: 11 + 11 significant bits)
+      2. mx, mn = max / min of the 128 values w'
+      3. sc = (mx - mn) / 15
+      4. sc = max(sc, 2^-14); if sc > 65504 then sc = 65504 (flag SCALE_CLAMPED)
+      5. sc_h = fp16(sc)                        (the stored scale)
+      6. z = clamp(rint(-mn / f32(sc_h)), 0, 15)
+      7. q = clamp(rint(w' / f32(sc_h)) + z, 0, 15)
+    Returns dict(q uint8 [N][K], z uint8 [N][G], scale fp16 [N][G], flags int).
+    """
+    W16 = np.asarray(W16)
+    assert W16.dtype == np.float16 and W16.ndim == 2
+    N, K = W16.shape
+    assert K % GROUP == 0
+    G = K // GROUP
+    w = W16.astype(_F32)
+    if s16 is not None:
+        s16 = np.asarray(s16)
+        assert s16.dtype == np.float16 and s16.shape == (K,)
+        w = w * s16.astype(_F32)[None, :]
+    flags = 0
+    if not np.all(np.isfinite(w)):
+        flags |= FLAG_NONFINITE_INPUT
+    wg = w.reshape(N, G, GROUP)
+    mx = wg.max(axis=2)
+    mn = wg.min(axis=2)
+    sc = (mx - mn) / _F32(QMAX)
+    sc = np.maximum(sc, SCALE_FLOOR)
+    if np.any(sc > SCALE_MAX):
+        flags |= FLAG_SCALE_CLAMPED
+    sc = np.minimum(sc, SCALE_MAX)
+    sc_h = sc.astype(np.float16)
+    sc_f = sc_h.astype(_F32)
+    with np.errstate(invalid="ignore"):
+        z = np.clip(np.rint(-mn / sc_f), _F32(0), _F32(QMAX))
+        q = np.clip(np.rint(wg / sc_f[:, :, None]) + z[:, :, None], _F32(0), _F32(QMAX))
+    q = np.nan_to_num(q, nan=0.0).astype(np.uint8).reshape(N, K)
+    z = np.nan_to_num(z, nan=0.0).astype(np.uint8)
+    return {"q": q, "z": z, "scale": sc_h, "flags": flags}
+
+
+# --------------------------------------------------------------------------- a4
+def pack(q: np.ndarray, z: np.ndarray, scale: np.ndarray) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Nibble packing of codes and zero points.
+
+    The pages give no layout ([AWQ-WIKI] only names "platform-aware weight
+    packing"). Reading: qweight uint32 [N][K/8] where nibble j (bits 4j..4j+3) of
+    word w is the code of input channel k = 8 w + j; zeros uint8 [N][ceil(G/2)]
+    where the low nibble holds the even group and the high nibble the odd group;
+    scales fp16 [N][G].
+    """
+    q = np.asarray(q, dtype=np.uint8)
+    N, K = q.shape
+    G = K // GROUP
+    qweight = np.zeros((N, K // 8), dtype=np.uint32)
+    for j in range(8):
+        qweight |= q[:, j::8].astype(np.uint32) << np.uint32(4 * j)
+    zeros = np.zeros((N, (G + 1) // 2), dtype=np.uint8)
+    zeros |= z[:, 0::2].astype(np.uint8)
+    zeros[:, : G // 2] |= (z[:, 1::2].astype(np.uint8) << np.uint8(4))
+    return qweight, np.asarray(scale, dtype=np.float16).copy(), zeros
+
+
+def unpack(qweight: np.ndarray, scales: np.ndarray, zeros: np.ndarray, K: int):
+    """Inverse of :func:`pack`: returns (q uint8 [N][K], z uint8 [N][G], scale fp16 [N][G])."""
+    N = qweight.shape[0]
+    G = K // GROUP
+    q = np.empty((N, K), dtype=np.uint8)
+    for j in range(8):
+        q[:, j::8] = ((qweight >> np.uint32(4 * j)) & np.uint32(0xF)).astype(np.uint8)
+    z = np.empty((N, G), dtype=np.uint8)
+    z[:, 0::2] = zeros[:, : (G + 1) // 2] & np.uint8(0xF)
+    z[:, 1::2] = zeros[:, : G // 2] >> np.uint8(4)
+    return q, z, np.asarray(scales, dtype=np.float16)
+
+
+def quantize_pack(W16: np.ndarray, s16: np.ndarray | None = None):
+    """a3 + a4: returns (qweight, scales, zeros, flags)."""
+    r = quantize_groups(W16, s16)
+    qweight, scales, zeros = pack(r["q"], r["z"], r["scale"])
+    return qweight, scales, zeros, r["flags"]
+
+
+def dequantize(q: np.ndarray, z: np.ndarray, scale: np.ndarray, s16: np.ndarray | None = None) -> np.ndarray:
+    """(q - z) * scale in fp64, divided by s when given: the weight the quantized layer stands for.
+
+    [GPTQ-VS-AWQ]: dequant = (q - z) * scale; [AWQ-PRACTICE] §2.2: the 1/s is undone.
+    """
+    N, K = q.shape
+    zz = np.repeat(z.astype(_F64), GROUP, axis=1)
+    ss = np.repeat(scale.astype(_F64), GROUP, axis=1)
+    w = (q.astype(_F64) - zz) * ss
+    if s16 is not None:
+        w = w / s16.astype(_F64)[None, :]
+    return w
+
+
+# --------------------------------------------------------------------------- a5/a6
+def search_errors(X16: np.ndarray, W16: np.ndarray, n_grid: int = N_GRID, grid_points=None) -> dict:
+    """Output error of every candidate scale.
+
+    [AWQ-PRACTICE] §2.2 and §3.3 step 4: grid search over a candidate interval so
+    that the layer output on the calibration set before and after quantization
+    agrees as closely as possible; [AWQ-WIKI] "工作机制": applied as the equivalent
+    transform W diag(s), X diag(1/s).
+
+      err_i = sum_t sum_n ( sum_k X_tk * D_nk )^2,
+      D     = W - Q(W diag(s_i)) diag(1/s_i)            (fp64)
+
+    ``grid_points`` restricts the evaluation to some indices (for bounded timing);
+    the other entries of ``err`` are NaN.
+    Returns dict(alpha, a, s16, s64, err fp64 [n_grid], flags).
+    """
+    a, flags = activation_mean_abs(X16)
+    alpha, s16, s64 = candidate_scales(a, n_grid)
+    Xd = X16.astype(_F64)
+    Wd = W16.astype(_F64)
+    err = np.full(n_grid, np.nan, dtype=_F64)
+    points = range(n_grid) if grid_points is None else grid_points
+    for i in points:
+        r = quantize_groups(W16, s16[i])
+        flags |= r["flags"]
+        What = dequantize(r["q"], r["z"], r["scale"], s16[i])
+        D = Wd - What
+        E = Xd @ D.T
+        err[i] = np.sum(E * E)
+    return {"alpha": alpha, "a": a, "s16": s16, "s64": s64, "err": err, "flags": flags}
+
+
+def search_scales(X16: np.ndarray, W16: np.ndarray, n_grid: int = N_GRID) -> dict:
+    """a1..a6: the chosen grid index (first minimum), its scale and its packed weights.
+
+    [AWQ-PRACTICE] §3.3 steps 4-5: pick the s with the smallest error, then
+    quantize with it and keep the scale. Ties go to the smallest index (closest to
+    plain RTN).
+    """
+    r = search_errors(X16, W16, n_grid)
+    err = r["err"]
+    best = 0
+    for i in range(1, n_grid):
+        if err[i] < err[best]:
+            best = i
+    s_best = r["s16"][best].copy()
+    qweight, scales, zeros, f = quantize_pack(W16, s_best)
+    r.update(best_idx=best, s_best=s_best, qweight=qweight, scales=scales, zeros=zeros,
+             gap=relative_gap(err), flags=r["flags"] | f)
+    return r
+
+
+# --------------------------------------------------------------------------- a7/a8
+def linear_reference(X16: np.ndarray, qweight: np.ndarray, scales: np.ndarray, zeros: np.ndarray, K: int):
+    """W4A16 linear, y = X deq(W)^T, in fp64, with its error bound.
+
+    [AWQ-PRACTICE] §3.4 / [AWQ-WIKI]: weight-only quantization, activations stay in
+    16-bit. y_mn = sum_k x_mk (q_nk - z) sc, and bound_mn = sum_k |x_mk| |(q_nk - z) sc|.
+    Returns (y fp64 [M][N], bound fp64 [M][N]).
+    """
+    q, z, sc = unpack(qweight, scales, zeros, K)
+    Wdeq = dequantize(q, z, sc)
+    Xd = np.asarray(X16).astype(_F64)
+    return Xd @ Wdeq.T, np.abs(Xd) @ np.abs(Wdeq).T
+
+
+def linear_within_tolerance(y, y_ref, bound, rel: float = 2e-3) -> np.ndarray:
+    """Per-element check |y - y_ref| <= rel * bound (returns a boolean mask)."""
+    y = np.asarray(y, dtype=_F64)
+    return np.abs(y - y_ref) <= rel * bound
+
+
+# --------------------------------------------------------------------------- hazards
+def fp16_midpoint_distance(v: np.ndarray) -> np.ndarray:
+    """Relative distance of fp64 values from the nearest fp16 rounding midpoint.
+
+    Where a pow result lies within a few fp64 ulps of such a midpoint, two
+    faithful pow implementations may round to different fp16 values; parity of s is
+    then not decidable from the pages, and a test must treat that case as unpinned.
+    """
+    v = np.abs(np.asarray(v, dtype=_F64))
+    h = v.astype(np.float16)
+    hf = h.astype(_F64)
+    up = np.nextafter(h, np.float16(np.inf)).astype(_F64)
+    dn = np.nextafter(h, np.float16(0)).astype(_F64)
+    mid_up = (hf + up) / 2.0
+    mid_dn = (hf + dn) / 2.0
+    d = np.minimum(np.abs(v - mid_up), np.abs(v - mid_dn))
+    return d / np.maximum(v, np.finfo(_F64).tiny)
+
+
+def relative_gap(err: np.ndarray) -> float:
+    """(second smallest - smallest) / smallest over the finite errors (inf when unique and 0)."""
+    e = np.sort(np.asarray(err, dtype=_F64)[np.isfinite(err)])
+    if e.size < 2:
+        return float("inf")
+    if e[0] == 0.0:
+        return float("inf") if e[1] > 0.0 else 0.0
+    return float((e[1] - e[0]) / e[0])
+
+
+def packed_bytes(N: int, K: int) -> int:
+    """Bytes of the packed format for one [N][K] weight: codes + fp16 scales + zero nibbles."""
+    G = K // GROUP
+    return N * (K // 2) + N * G * 2 + N * ((G + 1) // 2)

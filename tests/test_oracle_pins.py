@@ -1,0 +1,338 @@
+"""CPU pins of the oracle against what the AWQ pages and the mathematics fix.
+
+Each test names the passage or the mathematical fact it holds the oracle to. None
+of these tests re-types the oracle's formulas: they use hand-worked values
+(tests/golden/hand_worked.json), exact rational arithmetic, brute force over the
+16 codes, closed forms and invariants.
+"""
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic_inputs as si
+from tests import pins
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")))
+
+
+def golden_group_row(g):
+    w = np.full(128, g["fill"], dtype=np.float16)
+    for k, v in g["values"].items():
+        w[int(k)] = v
+    return w
+
+
+# ----------------------------------------------------------------- hand-worked values
+@pytest.mark.parametrize("g", GOLDEN["groups"], ids=[g["name"] for g in GOLDEN["groups"]])
+def test_golden_group(g):
+    """Hand-worked groups ('AWQ量化实战' §2.3; 'GPTQ与AWQ' 4-bit + scale + zero point)."""
+    W = golden_group_row(g)[None, :]
+    r = oracle.quantize_groups(W)
+    assert r["scale"].view(np.uint16)[0, 0] == int(g["scale_bits"], 16)
+    assert r["z"][0, 0] == g["zero"]
+    for k in range(128):
+        want = g["codes"].get(str(k), g["fill_code"])
+        assert r["q"][0, k] == want, (k, r["q"][0, k], want)
+
+
+def test_golden_packing():
+    p = GOLDEN["packing"]
+    q = np.zeros((1, 3 * 128), dtype=np.uint8)
+    q[0, :8] = p["codes_k0_to_k7"]
+    z = np.array([p["zeros_groups"]], dtype=np.uint8)
+    sc = np.ones((1, 3), dtype=np.float16)
+    qw, _, zb = oracle.pack(q, z, sc)
+    assert int(qw[0, 0]) == int(p["word"], 16)
+    assert [int(b) for b in zb[0]] == [int(b, 16) for b in p["zeros_bytes"]]
+
+
+def test_golden_activation_mean():
+    g = GOLDEN["activation_mean"]
+    a, flags = oracle.activation_mean_abs(np.array(g["X"], dtype=np.float16))
+    assert flags == 0
+    assert a.tolist() == g["a"]
+
+
+def test_golden_candidate_scales():
+    g = GOLDEN["candidate_scales"]
+    _, s16, _ = oracle.candidate_scales(np.array(g["a"]), g["n_grid"])
+    assert s16.astype(np.float64).tolist() == g["s"]
+
+
+def test_golden_search_error():
+    """One token e_0 through the 'straddling zero' group: err = D_0^2 = 2^-24, worked by hand."""
+    W = golden_group_row(GOLDEN["groups"][0])[None, :]
+    X = np.zeros((1, 128), dtype=np.float16)
+    X[0, 0] = 1.0
+    r = oracle.search_errors(X, W, n_grid=1)
+    assert r["err"][0] == GOLDEN["search_error"]["err"]
+
+
+# ----------------------------------------------------------------- a1 statistic
+def test_activation_mean_exact_vs_rationals():
+    """a_k = (1/T) sum |x|: compare with exact rational sums, correctly rounded to fp64."""
+    g = np.random.default_rng(1)
+    bits = g.integers(0, 0x7C00, size=(37, 9), dtype=np.uint16)   # every finite fp16 magnitude
+    sign = g.integers(0, 2, size=bits.shape, dtype=np.uint16) << 15
+    X = (bits | sign).view(np.float16)
+    a, flags = oracle.activation_mean_abs(X)
+    assert flags == 0
+    for k in range(X.shape[1]):
+        exact = sum((abs(Fraction(float(v))) for v in X[:, k]), Fraction(0)) / X.shape[0]
+        assert a[k] == float(exact)
+
+
+def test_activation_mean_extreme_and_order():
+    """Largest calibration set, largest fp16 magnitudes plus subnormals: still exact and order-free."""
+    T = oracle.awq_oracle.MAX_CALIB_TOKENS
+    X = np.full((T, 2), 65504.0, dtype=np.float16)
+    X[::3, 1] = np.float16(2.0 ** -24)
+    X[1::7, 0] = -X[1::7, 0]
+    a, _ = oracle.activation_mean_abs(X)
+    exact0 = Fraction(65504) * T / T
+    n_sub = len(range(0, T, 3))
+    exact1 = (Fraction(65504) * (T - n_sub) + Fraction(1, 2 ** 24) * n_sub) / T
+    assert a[0] == float(exact0) and a[1] == float(exact1)
+    perm = np.random.default_rng(2).permutation(T)
+    a2, _ = oracle.activation_mean_abs(X[perm])
+    assert np.array_equal(a, a2)
+
+
+def test_activation_nonfinite_flag():
+    X = np.ones((4, 8), dtype=np.float16)
+    X[2, 3] = np.inf
+    assert oracle.activation_mean_abs(X)[1] & oracle.FLAG_NONFINITE_INPUT
+
+
+# ----------------------------------------------------------------- a2 candidate scales
+def test_fp16_conversion_is_single_rounding():
+    """fp64 -> fp16 must round once (RNE); going through fp32 would double-round."""
+    vals = [1.0 + 2.0 ** -11 + 2.0 ** -40, 1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11,
+            2.0 ** -14 * (1 + 2.0 ** -11 + 2.0 ** -45), 65519.99, 0.1, 1 / 3]
+    for v in vals:
+        got = Fraction(float(np.float64(v).astype(np.float16)))
+        assert got == pins.rne_fp16(Fraction(v)), v
+
+
+def test_candidate_scales_closed_forms():
+    """alpha_0 = 0 gives s = 1 (plain RTN, 'AWQ量化实战' §1.1); powers of two are exact."""
+    a = np.array([4096.0, 0.25, 1.0, 2.0 ** -30, 37.5])
+    alpha, s16, s64 = oracle.candidate_scales(a, 20)
+    assert alpha.tolist() == [i / 20 for i in range(20)]
+    assert np.all(s16[0] == 1.0)
+    # 4096^(i/20) = 2^(12 i / 20): exact powers of two at i = 5, 10, 15
+    assert s16[5, 0] == 8.0 and s16[10, 0] == 64.0 and s16[15, 0] == 512.0
+    assert s16[10, 1] == 0.25 ** 0.5
+    assert np.all(s16[:, 2] == 1.0)
+    # the floor: a below 2^-14 behaves like 2^-14
+    _, s_floor, _ = oracle.candidate_scales(np.array([2.0 ** -14]), 20)
+    assert np.array_equal(s16[:, 3], s_floor[:, 0])
+    # monotone in alpha: increasing for a > 1, decreasing for a < 1
+    assert np.all(np.diff(s16[:, 4].astype(np.float64)) >= 0)
+    assert np.all(np.diff(s16[:, 1].astype(np.float64)) <= 0)
+    # each stored value is the RNE fp16 of a value within 1e-15 relative of the real power
+    for i in range(20):
+        for k in range(a.size):
+            real = max(a[k], 2.0 ** -14) ** (i / 20)
+            assert abs(s64[i, k] - real) <= 1e-15 * real
+
+
+# ----------------------------------------------------------------- a3 quantizer
+def _scaled(W16, s16):
+    w = W16.astype(np.float32)
+    return w if s16 is None else w * s16.astype(np.float32)[None, :]
+
+
+@pytest.mark.parametrize("use_s", [False, True])
+def test_codes_are_nearest_bruteforce(use_s):
+    """P1: each code is the nearest of the 16 levels (exact arithmetic) for the stored scale."""
+    W = si.weights(3, 256, offset=11)
+    W[0, 5] = 0.3                                  # plant a few special values
+    W[1, :128] = np.float16(0.01)                  # one constant group
+    s = None
+    if use_s:
+        a, _ = oracle.activation_mean_abs(si.activations(16, 256, offset=3))
+        s = oracle.candidate_scales(a, 20)[1][13]
+    r = oracle.quantize_groups(W, s)
+    bad = pins.check_codes_nearest(_scaled(W, s), r["q"], r["z"], r["scale"])
+    assert not bad, bad[:5]
+
+
+def test_scale_and_zero_closed_form():
+    """P2: sc_h = fp16((mx - mn)/15) (up to fp32 roundings), 0 <= z <= 15, -z sc_h ~ mn."""
+    W = si.weights(4, 512, offset=12)
+    W[2, 128:256] = np.abs(W[2, 128:256]) + np.float16(0.05)  # a group that does not straddle 0
+    r = oracle.quantize_groups(W)
+    assert not pins.check_scale_zero(_scaled(W, None), r["z"], r["scale"])
+
+
+def test_rtn_is_unit_scale():
+    """P4: s = 1 reproduces plain round-to-nearest ('AWQ量化实战' §1.1)."""
+    W = si.weights(5, 384, offset=13)
+    a = oracle.quantize_groups(W)
+    b = oracle.quantize_groups(W, np.ones(384, dtype=np.float16))
+    for key in ("q", "z"):
+        assert np.array_equal(a[key], b[key])
+    assert np.array_equal(a["scale"].view(np.uint16), b["scale"].view(np.uint16))
+
+
+def test_power_of_two_equivariance():
+    """P5: min/max affine quantization commutes with exact power-of-two scaling."""
+    W = si.weights(4, 256, offset=14)
+    base = oracle.quantize_groups(W)
+    for e in (-3, 2, 5):
+        r = oracle.quantize_groups((W.astype(np.float32) * 2.0 ** e).astype(np.float16))
+        assert np.array_equal(base["q"], r["q"]) and np.array_equal(base["z"], r["z"])
+        assert np.array_equal(base["scale"].astype(np.float64) * 2.0 ** e, r["scale"].astype(np.float64))
+
+
+def test_group_locality():
+    """P6: a group's codes, scale and zero depend on its own 128 values only ('AWQ量化实战' §2.3)."""
+    W = si.weights(3, 512, offset=15)
+    base = oracle.quantize_groups(W)
+    W2 = W.copy()
+    W2[1, 256:384] = (W2[1, 256:384].astype(np.float32) * 3 + 0.01).astype(np.float16)
+    r = oracle.quantize_groups(W2)
+    changed_q = np.argwhere(np.any(base["q"] != r["q"], axis=0)).ravel()
+    assert changed_q.size and changed_q.min() >= 256 and changed_q.max() < 384
+    diff_groups = np.argwhere(base["scale"] != r["scale"])
+    assert diff_groups.tolist() == [[1, 2]]
+
+
+def test_scale_clamp_flag():
+    W = np.zeros((1, 128), dtype=np.float16)
+    W[0, 0], W[0, 1] = -60000.0, 60000.0
+    s = np.full(128, 20.0, dtype=np.float16)
+    r = oracle.quantize_groups(W, s)
+    assert r["flags"] & oracle.FLAG_SCALE_CLAMPED
+    assert float(r["scale"][0, 0]) == 65504.0
+
+
+# ----------------------------------------------------------------- a4 packing
+def test_pack_roundtrip_odd_groups():
+    g = np.random.default_rng(5)
+    for K in (128, 384, 1024):
+        q = g.integers(0, 16, size=(3, K), dtype=np.uint8)
+        z = g.integers(0, 16, size=(3, K // 128), dtype=np.uint8)
+        sc = g.standard_normal((3, K // 128)).astype(np.float16)
+        qw, s2, zb = oracle.pack(q, z, sc)
+        assert qw.dtype == np.uint32 and qw.shape == (3, K // 8)
+        assert zb.shape == (3, (K // 128 + 1) // 2)
+        q2, z2, s3 = oracle.unpack(qw, s2, zb, K)
+        assert np.array_equal(q, q2) and np.array_equal(z, z2) and np.array_equal(sc, s3)
+    if (K // 128) % 2:
+        assert np.all(zb[:, -1] >> 4 == 0)
+
+
+def test_one_hot_extracts_dequantized_column():
+    """P3: x = e_k returns (q_nk - z) sc exactly, from the packed words read by hand."""
+    W = si.weights(6, 256, offset=16)
+    qw, sc, zb, _ = oracle.quantize_pack(W)
+    for k in (0, 7, 8, 129, 255):
+        X = np.zeros((1, 256), dtype=np.float16)
+        X[0, k] = 1.0
+        y, bound = oracle.linear_reference(X, qw, sc, zb, 256)
+        for n in range(6):
+            code = (int(qw[n, k // 8]) >> (4 * (k % 8))) & 0xF
+            j = k // 128
+            zero = (int(zb[n, j // 2]) >> (4 * (j % 2))) & 0xF
+            assert y[0, n] == (code - zero) * float(sc[n, j])
+            assert bound[0, n] == abs(y[0, n])
+
+
+# ----------------------------------------------------------------- a5/a6 search
+def test_search_error_exact_rationals():
+    """P7: fp64 errors agree with exact rational errors on tiny problems, same argmin."""
+    for (T, N, K, off) in ((3, 2, 128, 0), (2, 1, 256, 1)):
+        X = si.activations(T, K, offset=20 + off)
+        W = si.weights(N, K, offset=20 + off)
+        r = oracle.search_errors(X, W, n_grid=4)
+        exact = []
+        for i in range(4):
+            qz = oracle.quantize_groups(W, r["s16"][i])
+            exact.append(pins.exact_search_error(X, W, r["s16"][i], qz["q"], qz["z"], qz["scale"]))
+        for i in range(4):
+            assert abs(r["err"][i] - float(exact[i])) <= 1e-12 * float(exact[i])
+        assert int(np.argmin(r["err"])) == min(range(4), key=lambda i: (exact[i], i))
+
+
+def test_search_never_worse_than_rtn():
+    """P8: alpha = 0 (plain RTN) is on the grid, so the chosen error cannot exceed it."""
+    X = si.activations(64, 512, offset=30)
+    W = si.weights(64, 512, offset=30)
+    r = oracle.search_scales(X, W)
+    assert r["err"][r["best_idx"]] <= r["err"][0]
+    assert r["best_idx"] > 0 and r["err"][r["best_idx"]] < r["err"][0]  # heavy tail helps (sanity)
+
+
+def test_unit_activations_tie_to_first():
+    """P9: |x| = 1 everywhere -> a = 1 -> s = 1 for every alpha -> equal errors -> index 0."""
+    g = np.random.default_rng(7)
+    X = np.where(g.integers(0, 2, size=(8, 256)) == 1, 1.0, -1.0).astype(np.float16)
+    W = si.weights(16, 256, offset=31)
+    r = oracle.search_scales(X, W)
+    assert np.all(r["err"] == r["err"][0])
+    assert r["best_idx"] == 0 and np.all(r["s_best"] == 1.0)
+
+
+def test_search_result_is_pack_with_best_scale():
+    X = si.activations(32, 256, offset=32)
+    W = si.weights(8, 256, offset=32)
+    r = oracle.search_scales(X, W)
+    qw, sc, zb, _ = oracle.quantize_pack(W, r["s16"][r["best_idx"]])
+    assert np.array_equal(qw, r["qweight"]) and np.array_equal(zb, r["zeros"])
+
+
+# ----------------------------------------------------------------- a7/a8 linear
+def test_linear_zero_and_row_independence():
+    """P10: X = 0 gives 0; an M-row batch equals M single-row products."""
+    W = si.weights(9, 384, offset=40)
+    qw, sc, zb, _ = oracle.quantize_pack(W)
+    y0, b0 = oracle.linear_reference(np.zeros((2, 384), dtype=np.float16), qw, sc, zb, 384)
+    assert np.all(y0 == 0) and np.all(b0 == 0)
+    X = si.activations(5, 384, offset=40)
+    y, _ = oracle.linear_reference(X, qw, sc, zb, 384)
+    for m in range(5):
+        ym, _ = oracle.linear_reference(X[m:m + 1], qw, sc, zb, 384)
+        assert np.allclose(ym[0], y[m], rtol=1e-14, atol=1e-14)
+
+
+def test_linear_reference_vs_rationals():
+    W = si.weights(3, 128, offset=41)
+    qw, sc, zb, _ = oracle.quantize_pack(W)
+    X = si.activations(2, 128, offset=41)
+    y, bound = oracle.linear_reference(X, qw, sc, zb, 128)
+    q, z, s = oracle.unpack(qw, sc, zb, 128)
+    for m in range(2):
+        for n in range(3):
+            terms = [Fraction(float(X[m, k])) * (int(q[n, k]) - int(z[n, 0])) * Fraction(float(s[n, 0]))
+                     for k in range(128)]
+            assert abs(y[m, n] - float(sum(terms))) <= 1e-14 * float(sum(abs(t) for t in terms))
+            assert abs(bound[m, n] - float(sum(abs(t) for t in terms))) <= 1e-14 * bound[m, n]
+
+
+# ----------------------------------------------------------------- hazards and format
+def test_midpoint_hazard_detector():
+    """P11: values next to an fp16 rounding midpoint are detected; ordinary values are not."""
+    mid = 1.0 + 2.0 ** -11
+    d = oracle.fp16_midpoint_distance(np.array([mid * (1 + 2.0 ** -50), 1.3, mid]))
+    assert d[0] < 2.0 ** -40 and d[1] > 1e-4 and d[2] == 0.0
+
+
+def test_relative_gap():
+    assert oracle.relative_gap(np.array([3.0, 1.0, 1.5])) == 0.5
+    assert oracle.relative_gap(np.array([2.0, 2.0])) == 0.0
+
+
+def test_format_size_matches_70b_figure():
+    """P13: 80 Llama-2-70B layers pack to ~35 GB ('AWQ量化技术Skill': 70B 140 GB -> 35 GB)."""
+    per_layer = sum(oracle.packed_bytes(n, k) for n, k in si.LLAMA2_70B_LINEARS.values())
+    total = per_layer * si.LLAMA2_70B_LAYERS
+    assert total == 68_451_041_280 * 133 // 256   # 0.51953125 B per weight = 35.56 GB
+    assert 33e9 < total < 37e9
+    assert oracle.packed_bytes(4096, 4096) * 8 == 4096 * 4096 * 4 + 4096 * 32 * 16 + 4096 * 16 * 8
