@@ -1,0 +1,172 @@
+/*
+ * awq.h -- C ABI of the MI355X (gfx950) AWQ W4A16 hot-path library (libawq_mi355x.so).
+ *
+ * AWQ (activation-aware weight quantization) keeps activations in 16-bit and stores
+ * weights as 4-bit integers, one fp16 scale and one 4-bit zero point per group of
+ * 128 consecutive input channels; before quantizing, input channel k of the weight is
+ * multiplied by a scale s_k picked from offline activation magnitudes, and the
+ * activation side carries 1/s_k (an equivalent transform).
+ *
+ * Sources (web pages, cited by title and section):
+ *   "AWQ量化实战：无需重训，把大模型压进4bit显存" (xdnf.cn)            -- [PRACTICE]
+ *   "AWQ量化技术Skill" (skillsbot.cn, awq-quantization usage page)  -- [SKILL]
+ *   "大模型量化部署实战：GPTQ与AWQ算法" (yunthe.com)                 -- [GPTQ-AWQ]
+ *   "什么是激活感知权重量化（AWQ）" (aiboss88.com)                   -- [WIKI]
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller. The library never
+ *     allocates, frees, copies to the host or synchronizes. Work is enqueued on
+ *     `stream` (a hipStream_t; NULL = the default stream) and is complete when the
+ *     stream reaches it.
+ *   - fp16 = IEEE binary16, passed as void*. All matrices are dense row-major.
+ *   - W is [N][K] (out features x in features), X is [rows][K], Y = X * W^T is [M][N]
+ *     ([PRACTICE] §2.1: the weight is "output dim x input dim", channels are input dims).
+ *   - Argument errors are detected on the host before anything is enqueued; the call
+ *     then returns a non-zero status and touches no output. Launch failures return
+ *     AWQ_ERR_HIP. Conditions that only the data reveals are OR-ed into the optional
+ *     device word `flags` (never cleared by the library).
+ *   - Identical inputs give bitwise-identical outputs (no floating-point atomics).
+ *   - Base pointers must be 16-byte aligned.
+ */
+#ifndef AWQ_MI355X_H
+#define AWQ_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum awq_status {
+  AWQ_OK = 0,
+  AWQ_ERR_NULL_POINTER = 1,  /* a required pointer is NULL                          */
+  AWQ_ERR_BAD_SHAPE = 2,     /* a size < 1, K % 128 != 0, T above 8192, ...          */
+  AWQ_ERR_UNSUPPORTED = 3,   /* config other than w_bit 4 / group 128 / zero point on */
+  AWQ_ERR_MISALIGNED = 4,    /* a base pointer is not 16-byte aligned                */
+  AWQ_ERR_WORKSPACE = 5,     /* workspace missing or smaller than the query returns  */
+  AWQ_ERR_HIP = 6            /* the HIP runtime reported an error on launch          */
+} awq_status;
+
+/* Quantization config ([SKILL] "如何使用该技能 / 步骤 2": quant_config zero_point, q_group_size,
+ * w_bit; the page's "version" GEMM/GEMV switch becomes dispatch on M inside
+ * awq_linear_w4a16). Supported: w_bit = 4, group_size = 128, zero_point = 1,
+ * 1 <= n_grid <= 64. NULL config pointers mean {4, 128, 1, 20}. */
+typedef struct awq_config {
+  int32_t w_bit;
+  int32_t group_size;
+  int32_t zero_point;
+  int32_t n_grid; /* number of alpha grid points: alpha_i = i / n_grid, i = 0 .. n_grid-1 */
+} awq_config;
+
+#define AWQ_FLAG_NONFINITE_INPUT 1u /* NaN or Inf met in W, s or X (outputs unspecified) */
+#define AWQ_FLAG_SCALE_CLAMPED 2u   /* a group scale above 65504 was clamped to 65504   */
+#define AWQ_FLAG_SEARCH_RANGE 4u    /* a search error term left the fp16 split's range  */
+
+#define AWQ_MAX_CALIB_TOKENS 8192
+
+/* Which linear kernel awq_linear_w4a16_ex runs. */
+typedef enum awq_linear_kernel {
+  AWQ_LINEAR_AUTO = 0, /* GEMV for M <= the crossover, MFMA GEMM above        */
+  AWQ_LINEAR_GEMV = 1, /* wave-per-rows dequant-fused GEMV (any M <= 8)       */
+  AWQ_LINEAR_GEMM = 2  /* MFMA dequant-GEMM (any M)                           */
+} awq_linear_kernel;
+
+/*
+ * awq_quantize_pack -- group-wise asymmetric 4-bit quantization of W * diag(s), packed.
+ *   [PRACTICE] §2.3 (128 consecutive input channels share one step), §3.3 step 5;
+ *   [GPTQ-AWQ] "大模型量化的核心原理与位宽选择" (4-bit integer + scale + zero point).
+ *   Per row n and group j, in fp32 with round-to-nearest-even:
+ *     w' = w * s_k;  sc = max((max w' - min w') / 15, 2^-14) (clamped at 65504);
+ *     sc_h = fp16(sc);  z = clamp(rint(-min w' / sc_h), 0, 15);
+ *     q = clamp(rint(w' / sc_h) + z, 0, 15).
+ *   W        fp16 [N][K]          input, K % 128 == 0
+ *   s        fp16 [K]             per-input-channel scale; NULL means s = 1 (plain RTN)
+ *   qweight  uint32 [N][K/8]      out: nibble j (bits 4j..4j+3) of word w = code of k = 8w + j
+ *   scales   fp16 [N][K/128]      out: sc_h
+ *   zeros    uint8 [N][ceil(G/2)] out: G = K/128; low nibble = even group, high = odd group
+ *   flags    uint32 [1] or NULL   NONFINITE_INPUT, SCALE_CLAMPED
+ */
+awq_status awq_quantize_pack(const void* W, int64_t N, int64_t K, const void* s,
+                             const awq_config* cfg, uint32_t* qweight, void* scales,
+                             uint8_t* zeros, uint32_t* flags, void* stream);
+
+/*
+ * awq_activation_stats -- per-input-channel mean absolute activation.
+ *   [PRACTICE] §2.1 (accumulate calibration activations per input channel and take the
+ *   mean absolute value); [WIKI] "工作机制" (offline activation statistics).
+ *   a_k = (sum_t |X_tk|) / T, with the sum exact (fixed point) and one fp64 division.
+ *   X         fp16 [T][K], 1 <= T <= 8192
+ *   act_mean  fp64 [K]   out
+ *   workspace device scratch of awq_activation_stats_workspace_size(T, K) bytes
+ *   flags     NONFINITE_INPUT
+ */
+size_t awq_activation_stats_workspace_size(int64_t T, int64_t K);
+awq_status awq_activation_stats(const void* X, int64_t T, int64_t K, double* act_mean,
+                                void* workspace, size_t workspace_bytes, uint32_t* flags,
+                                void* stream);
+
+/*
+ * awq_candidate_scales -- the per-channel scale of every alpha grid point.
+ *   [PRACTICE] §2.2 (grid search over a candidate interval), §5.1 (one coefficient per
+ *   layer); [WIKI] "工作机制" (scale set from offline activation statistics).
+ *   s_grid[i][k] = fp16_rne(pow(max(act_mean[k], 2^-14), i / n_grid)) (fp64 pow), so row
+ *   0 is all ones (plain RTN).
+ *   act_mean fp64 [K];  s_grid fp16 [n_grid][K] out.
+ */
+awq_status awq_candidate_scales(const double* act_mean, int64_t K, const awq_config* cfg,
+                                void* s_grid, void* stream);
+
+/*
+ * awq_search_scales -- activation-aware grid search of the per-channel scale.
+ *   [PRACTICE] §2.2 / §3.3 step 4: pick, over the grid, the s whose quantized layer keeps
+ *   the calibration outputs closest to the original ones; [WIKI] "工作机制" (equivalent
+ *   transform W diag(s), X diag(1/s); no backpropagation).
+ *     err_i = sum_t sum_n ( sum_k X_tk (W_nk - deq(Q(W diag(s_i)))_nk / s_ik) )^2
+ *     best  = smallest i with err_i == min err
+ *   Linears that share one input (q|k|v, gate|up) share one s: pass them concatenated
+ *   along N.
+ *   X         fp16 [T][K], 1 <= T <= 8192 (calibration activations)
+ *   W         fp16 [N][K]
+ *   s_best    fp16 [K]          out: s_{best}
+ *   best_idx  int32 [1]         out: best
+ *   err       fp64 [n_grid]     out (may be NULL)
+ *   s_grid    fp16 [n_grid][K]  out (may be NULL): every candidate scale
+ *   workspace device scratch of awq_search_workspace_size(T, N, K, cfg) bytes
+ *   flags     NONFINITE_INPUT, SCALE_CLAMPED, SEARCH_RANGE
+ *   Follow with awq_quantize_pack(W, s_best) to obtain the packed weights.
+ */
+size_t awq_search_workspace_size(int64_t T, int64_t N, int64_t K, const awq_config* cfg);
+awq_status awq_search_scales(const void* X, int64_t T, const void* W, int64_t N, int64_t K,
+                             const awq_config* cfg, void* s_best, int32_t* best_idx,
+                             double* err, void* s_grid, void* workspace,
+                             size_t workspace_bytes, uint32_t* flags, void* stream);
+
+/*
+ * awq_linear_w4a16 -- Y = X * deq(W)^T with 4-bit packed weights and fp16 activations.
+ *   [PRACTICE] §3.4 (decode is memory-bound: smaller weights, faster tokens); [SKILL]
+ *   "主要功能和特点" (GEMV kernel for single-token decode, GEMM kernel for batches).
+ *   deq(W)_nk = (q_nk - z_nj) * sc_nj; products accumulate in fp32; Y is rounded to fp16.
+ *   X fp16 [M][K]; qweight/scales/zeros as written by awq_quantize_pack; Y fp16 [M][N].
+ *   M <= 8 runs the dequant-fused GEMV, larger M the MFMA dequant-GEMM.
+ */
+awq_status awq_linear_w4a16(const void* X, int64_t M, const uint32_t* qweight,
+                            const void* scales, const uint8_t* zeros, int64_t N, int64_t K,
+                            const awq_config* cfg, void* Y, uint32_t* flags, void* stream);
+
+/* Same as awq_linear_w4a16 with an explicit kernel choice (GEMV requires M <= 8). */
+awq_status awq_linear_w4a16_ex(const void* X, int64_t M, const uint32_t* qweight,
+                               const void* scales, const uint8_t* zeros, int64_t N, int64_t K,
+                               const awq_config* cfg, void* Y, uint32_t* flags,
+                               awq_linear_kernel kernel, void* stream);
+
+/* Largest M served by the GEMV kernel under AWQ_LINEAR_AUTO. */
+int32_t awq_gemv_max_m(void);
+
+/* Human-readable text of a status code (static storage). */
+const char* awq_status_string(awq_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* AWQ_MI355X_H */

@@ -1,0 +1,185 @@
+"""Thin PyTorch binding of the AWQ W4A16 C ABI (argument marshalling only).
+
+torch provides device memory and the current stream; every step of the path runs in
+the library's HIP kernels. Each function checks that its tensors live on the GPU,
+have the expected dtype and are contiguous (a host pointer handed to a kernel would
+fault the device), allocates outputs, and raises AwqError on a non-OK status.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+
+import torch
+
+from . import _abi
+
+GROUP = 128
+
+
+def _ptr(t):
+    return C.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, dtype, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+@dataclass
+class PackedLinear:
+    """Packed 4-bit weight of one [N][K] linear: codes, fp16 group scales, zero nibbles."""
+    qweight: torch.Tensor  # int32 [N][K/8] (the bits of uint32 words)
+    scales: torch.Tensor   # fp16 [N][K/128]
+    zeros: torch.Tensor    # uint8 [N][ceil(G/2)]
+    N: int
+    K: int
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in (self.qweight, self.scales, self.zeros))
+
+
+def alloc_packed(N: int, K: int, device) -> PackedLinear:
+    G = K // GROUP
+    return PackedLinear(
+        torch.empty((N, K // 8), dtype=torch.int32, device=device),
+        torch.empty((N, G), dtype=torch.float16, device=device),
+        torch.empty((N, (G + 1) // 2), dtype=torch.uint8, device=device), N, K)
+
+
+def quantize_pack(W: torch.Tensor, s: torch.Tensor | None = None, flags: torch.Tensor | None = None,
+                  out: PackedLinear | None = None) -> PackedLinear:
+    """awq_quantize_pack: 4-bit group-128 quantization of W * diag(s) (s = None: plain RTN)."""
+    lib = _abi.load()
+    _need(W, torch.float16, "W")
+    if W.dim() != 2:
+        raise ValueError("W must be [N][K]")
+    N, K = W.shape
+    if s is not None:
+        _need(s, torch.float16, "s")
+        if s.shape != (K,):
+            raise ValueError("s must be [K]")
+    if flags is not None:
+        _need(flags, torch.int32, "flags")
+    p = out if out is not None else alloc_packed(N, K, W.device)
+    for name, t, dt in (("qweight", p.qweight, torch.int32), ("scales", p.scales, torch.float16),
+                        ("zeros", p.zeros, torch.uint8)):
+        _need(t, dt, name)
+    if p.N != N or p.K != K:
+        raise ValueError("output packed buffers have the wrong shape")
+    cfg = _abi.config()
+    _abi.check("awq_quantize_pack", lib.awq_quantize_pack(
+        _ptr(W), N, K, _ptr(s), C.byref(cfg), _ptr(p.qweight), _ptr(p.scales), _ptr(p.zeros),
+        _ptr(flags), _stream()))
+    return p
+
+
+def activation_stats(X: torch.Tensor, flags: torch.Tensor | None = None) -> torch.Tensor:
+    """awq_activation_stats: fp64 [K] mean |x| per input channel."""
+    lib = _abi.load()
+    _need(X, torch.float16, "X")
+    T, K = X.shape
+    act = torch.empty(K, dtype=torch.float64, device=X.device)
+    ws_bytes = lib.awq_activation_stats_workspace_size(T, K)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=X.device)
+    if flags is not None:
+        _need(flags, torch.int32, "flags")
+    _abi.check("awq_activation_stats", lib.awq_activation_stats(
+        _ptr(X), T, K, _ptr(act), _ptr(ws), ws_bytes, _ptr(flags), _stream()))
+    return act
+
+
+def candidate_scales(act: torch.Tensor, n_grid: int = 20) -> torch.Tensor:
+    """awq_candidate_scales: fp16 [n_grid][K], row i = fp16(max(act, 2^-14)^(i/n_grid))."""
+    lib = _abi.load()
+    _need(act, torch.float64, "act")
+    K = act.shape[0]
+    out = torch.empty((n_grid, K), dtype=torch.float16, device=act.device)
+    cfg = _abi.config(n_grid)
+    _abi.check("awq_candidate_scales", lib.awq_candidate_scales(
+        _ptr(act), K, C.byref(cfg), _ptr(out), _stream()))
+    return out
+
+
+@dataclass
+class SearchResult:
+    s_best: torch.Tensor    # fp16 [K]
+    best_idx: torch.Tensor  # int32 [1] (device)
+    err: torch.Tensor       # fp64 [n_grid]
+    s_grid: torch.Tensor    # fp16 [n_grid][K]
+
+
+class SearchWorkspace:
+    """Reusable device scratch for awq_search_scales (sized by the library's query)."""
+
+    def __init__(self, T: int, N: int, K: int, device, n_grid: int = 20):
+        lib = _abi.load()
+        cfg = _abi.config(n_grid)
+        self.nbytes = lib.awq_search_workspace_size(T, N, K, C.byref(cfg))
+        if self.nbytes == 0:
+            raise ValueError("unsupported search shape")
+        self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+
+
+def search_scales(X: torch.Tensor, W: torch.Tensor, n_grid: int = 20,
+                  workspace: SearchWorkspace | None = None, flags: torch.Tensor | None = None,
+                  out: SearchResult | None = None) -> SearchResult:
+    """awq_search_scales: grid search of s = mean|x|^alpha minimizing the output error."""
+    lib = _abi.load()
+    _need(X, torch.float16, "X")
+    _need(W, torch.float16, "W")
+    T, K = X.shape
+    N, K2 = W.shape
+    if K != K2:
+        raise ValueError("X and W disagree on K")
+    dev = W.device
+    if out is None:
+        out = SearchResult(torch.empty(K, dtype=torch.float16, device=dev),
+                           torch.empty(1, dtype=torch.int32, device=dev),
+                           torch.empty(n_grid, dtype=torch.float64, device=dev),
+                           torch.empty((n_grid, K), dtype=torch.float16, device=dev))
+    ws = workspace if workspace is not None else SearchWorkspace(T, N, K, dev, n_grid)
+    if flags is not None:
+        _need(flags, torch.int32, "flags")
+    cfg = _abi.config(n_grid)
+    _abi.check("awq_search_scales", lib.awq_search_scales(
+        _ptr(X), T, _ptr(W), N, K, C.byref(cfg), _ptr(out.s_best), _ptr(out.best_idx),
+        _ptr(out.err), _ptr(out.s_grid), _ptr(ws.buf), ws.nbytes, _ptr(flags), _stream()))
+    return out
+
+
+_KERNELS = {"auto": _abi.KERNEL_AUTO, "gemv": _abi.KERNEL_GEMV, "gemm": _abi.KERNEL_GEMM}
+
+
+def linear_w4a16(X: torch.Tensor, w: PackedLinear, kernel: str = "auto",
+                 out: torch.Tensor | None = None) -> torch.Tensor:
+    """awq_linear_w4a16: Y[M][N] = X[M][K] deq(W)^T in fp16 with fp32 accumulation."""
+    lib = _abi.load()
+    _need(X, torch.float16, "X")
+    M, K = X.shape
+    if K != w.K:
+        raise ValueError("X and the packed weight disagree on K")
+    Y = out if out is not None else torch.empty((M, w.N), dtype=torch.float16, device=X.device)
+    _need(Y, torch.float16, "Y")
+    if Y.shape != (M, w.N):
+        raise ValueError("Y has the wrong shape")
+    cfg = _abi.config()
+    _abi.check("awq_linear_w4a16_ex", lib.awq_linear_w4a16_ex(
+        _ptr(X), M, _ptr(w.qweight), _ptr(w.scales), _ptr(w.zeros), w.N, K, C.byref(cfg),
+        _ptr(Y), None, _KERNELS[kernel], _stream()))
+    return Y
+
+
+def gemv_max_m() -> int:
+    return int(_abi.load().awq_gemv_max_m())

@@ -1,0 +1,200 @@
+// C ABI of libawq_mi355x: argument validation, workspace layout, kernel dispatch.
+// The operations and their sources are documented in include/awq.h.
+#include <stdlib.h>
+
+#include "awq.h"
+#include "launch.hpp"
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+
+awq_config resolve(const awq_config* cfg) {
+  if (cfg) return *cfg;
+  return awq_config{4, 128, 1, 20};
+}
+
+bool supported(const awq_config& c) {
+  return c.w_bit == 4 && c.group_size == 128 && c.zero_point == 1 && c.n_grid >= 1 &&
+         c.n_grid <= 64;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+bool good_nk(int64_t N, int64_t K) {
+  return N >= 1 && K >= 128 && K % 128 == 0 && N < kMaxDim && K < kMaxDim;
+}
+
+awq_status hip_status(hipError_t e) { return e == hipSuccess ? AWQ_OK : AWQ_ERR_HIP; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Search workspace: [u: int64 K][act: fp64 K][s_grid: fp16 n_grid K][partials: fp64 ...]
+struct SearchLayout {
+  size_t u, act, sgrid, partials, total;
+  int64_t n_partials;  // per grid point
+};
+
+SearchLayout search_layout(int64_t T, int64_t N, int64_t K, int n_grid) {
+  SearchLayout L;
+  const int64_t ntiles = (N + awq::search_row_tile() - 1) / awq::search_row_tile();
+  const int64_t chunk = awq::search_token_chunk(T);
+  L.n_partials = ntiles * ((T + chunk - 1) / chunk);
+  L.u = 0;
+  L.act = align256(L.u + (size_t)K * 8);
+  L.sgrid = align256(L.act + (size_t)K * 8);
+  L.partials = align256(L.sgrid + (size_t)n_grid * K * 2);
+  L.total = align256(L.partials + (size_t)n_grid * L.n_partials * 8);
+  return L;
+}
+
+int gemv_max_m_from_env() {
+  const char* e = getenv("AWQ_GEMV_MAX_M");
+  if (!e) return awq::kGemvMaxM;
+  int v = atoi(e);
+  if (v < 0) v = 0;
+  if (v > awq::kGemvMaxM) v = awq::kGemvMaxM;
+  return v;
+}
+
+const int g_gemv_max_m = gemv_max_m_from_env();
+
+}  // namespace
+
+extern "C" {
+
+const char* awq_status_string(awq_status s) {
+  switch (s) {
+    case AWQ_OK: return "ok";
+    case AWQ_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case AWQ_ERR_BAD_SHAPE: return "bad shape (sizes must be >= 1, K a multiple of 128, T <= 8192)";
+    case AWQ_ERR_UNSUPPORTED: return "unsupported config (w_bit 4, group_size 128, zero_point 1, 1 <= n_grid <= 64)";
+    case AWQ_ERR_MISALIGNED: return "a base pointer is not 16-byte aligned";
+    case AWQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case AWQ_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+int32_t awq_gemv_max_m(void) { return g_gemv_max_m; }
+
+awq_status awq_quantize_pack(const void* W, int64_t N, int64_t K, const void* s,
+                             const awq_config* cfg, uint32_t* qweight, void* scales,
+                             uint8_t* zeros, uint32_t* flags, void* stream) {
+  const awq_config c = resolve(cfg);
+  if (!W || !qweight || !scales || !zeros) return AWQ_ERR_NULL_POINTER;
+  if (!supported(c)) return AWQ_ERR_UNSUPPORTED;
+  if (!good_nk(N, K)) return AWQ_ERR_BAD_SHAPE;
+  if (!aligned16(W) || !aligned16(qweight) || !aligned16(scales) || !aligned16(zeros) ||
+      (s && !aligned16(s)) || (flags && !aligned4(flags)))
+    return AWQ_ERR_MISALIGNED;
+  return hip_status(awq::launch_quant_pack((const uint16_t*)W, N, K, (const uint16_t*)s, qweight,
+                                           (uint16_t*)scales, zeros, flags, (hipStream_t)stream));
+}
+
+size_t awq_activation_stats_workspace_size(int64_t T, int64_t K) {
+  (void)T;
+  return K > 0 ? align256((size_t)K * 8) : 0;
+}
+
+awq_status awq_activation_stats(const void* X, int64_t T, int64_t K, double* act_mean,
+                                void* workspace, size_t workspace_bytes, uint32_t* flags,
+                                void* stream) {
+  if (!X || !act_mean) return AWQ_ERR_NULL_POINTER;
+  if (T < 1 || T > AWQ_MAX_CALIB_TOKENS || !good_nk(1, K)) return AWQ_ERR_BAD_SHAPE;
+  if (!workspace || workspace_bytes < awq_activation_stats_workspace_size(T, K))
+    return AWQ_ERR_WORKSPACE;
+  if (!aligned16(X) || !aligned16(act_mean) || !aligned16(workspace) ||
+      (flags && !aligned4(flags)))
+    return AWQ_ERR_MISALIGNED;
+  hipStream_t st = (hipStream_t)stream;
+  auto* u = (unsigned long long*)workspace;
+  hipError_t e = awq::launch_zero_u64(u, K, st);
+  if (e == hipSuccess) e = awq::launch_act_sums((const uint16_t*)X, T, K, u, flags, st);
+  if (e == hipSuccess) e = awq::launch_act_finalize(u, T, K, act_mean, st);
+  return hip_status(e);
+}
+
+awq_status awq_candidate_scales(const double* act_mean, int64_t K, const awq_config* cfg,
+                                void* s_grid, void* stream) {
+  const awq_config c = resolve(cfg);
+  if (!act_mean || !s_grid) return AWQ_ERR_NULL_POINTER;
+  if (!supported(c)) return AWQ_ERR_UNSUPPORTED;
+  if (!good_nk(1, K)) return AWQ_ERR_BAD_SHAPE;
+  if (!aligned16(act_mean) || !aligned16(s_grid)) return AWQ_ERR_MISALIGNED;
+  return hip_status(
+      awq::launch_scalegen(act_mean, K, c.n_grid, (uint16_t*)s_grid, (hipStream_t)stream));
+}
+
+size_t awq_search_workspace_size(int64_t T, int64_t N, int64_t K, const awq_config* cfg) {
+  const awq_config c = resolve(cfg);
+  if (!supported(c) || T < 1 || T > AWQ_MAX_CALIB_TOKENS || !good_nk(N, K)) return 0;
+  return search_layout(T, N, K, c.n_grid).total;
+}
+
+awq_status awq_search_scales(const void* X, int64_t T, const void* W, int64_t N, int64_t K,
+                             const awq_config* cfg, void* s_best, int32_t* best_idx,
+                             double* err, void* s_grid, void* workspace,
+                             size_t workspace_bytes, uint32_t* flags, void* stream) {
+  const awq_config c = resolve(cfg);
+  if (!X || !W || !s_best || !best_idx) return AWQ_ERR_NULL_POINTER;
+  if (!supported(c)) return AWQ_ERR_UNSUPPORTED;
+  if (T < 1 || T > AWQ_MAX_CALIB_TOKENS || !good_nk(N, K)) return AWQ_ERR_BAD_SHAPE;
+  const SearchLayout L = search_layout(T, N, K, c.n_grid);
+  if (!workspace || workspace_bytes < L.total) return AWQ_ERR_WORKSPACE;
+  if (!aligned16(X) || !aligned16(W) || !aligned16(s_best) || !aligned4(best_idx) ||
+      (err && !aligned16(err)) || (s_grid && !aligned16(s_grid)) || !aligned16(workspace) ||
+      (flags && !aligned4(flags)))
+    return AWQ_ERR_MISALIGNED;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  auto* u = (unsigned long long*)(ws + L.u);
+  auto* act = (double*)(ws + L.act);
+  auto* sg = s_grid ? (uint16_t*)s_grid : (uint16_t*)(ws + L.sgrid);
+  auto* partials = (double*)(ws + L.partials);
+  const auto* Xh = (const uint16_t*)X;
+  hipError_t e = awq::launch_zero_u64(u, K, st);
+  if (e == hipSuccess) e = awq::launch_act_sums(Xh, T, K, u, flags, st);
+  if (e == hipSuccess) e = awq::launch_act_finalize(u, T, K, act, st);
+  if (e == hipSuccess) e = awq::launch_scalegen(act, K, c.n_grid, sg, st);
+  if (e == hipSuccess)
+    e = awq::launch_search_err(Xh, T, (const uint16_t*)W, N, K, sg, c.n_grid, partials, flags, st);
+  if (e == hipSuccess)
+    e = awq::launch_search_reduce(partials, c.n_grid, L.n_partials, sg, K, (uint16_t*)s_best,
+                                  best_idx, err, st);
+  return hip_status(e);
+}
+
+awq_status awq_linear_w4a16_ex(const void* X, int64_t M, const uint32_t* qweight,
+                               const void* scales, const uint8_t* zeros, int64_t N, int64_t K,
+                               const awq_config* cfg, void* Y, uint32_t* flags,
+                               awq_linear_kernel kernel, void* stream) {
+  (void)flags;
+  const awq_config c = resolve(cfg);
+  if (!X || !qweight || !scales || !zeros || !Y) return AWQ_ERR_NULL_POINTER;
+  if (!supported(c)) return AWQ_ERR_UNSUPPORTED;
+  if (M < 1 || M >= kMaxDim || !good_nk(N, K)) return AWQ_ERR_BAD_SHAPE;
+  if (kernel != AWQ_LINEAR_AUTO && kernel != AWQ_LINEAR_GEMV && kernel != AWQ_LINEAR_GEMM)
+    return AWQ_ERR_UNSUPPORTED;
+  if (kernel == AWQ_LINEAR_GEMV && M > awq::kGemvMaxM) return AWQ_ERR_BAD_SHAPE;
+  if (!aligned16(X) || !aligned16(qweight) || !aligned16(scales) || !aligned16(zeros) ||
+      !aligned16(Y))
+    return AWQ_ERR_MISALIGNED;
+  const bool gemv = kernel == AWQ_LINEAR_GEMV || (kernel == AWQ_LINEAR_AUTO && M <= g_gemv_max_m);
+  hipStream_t st = (hipStream_t)stream;
+  const auto* Xh = (const uint16_t*)X;
+  const auto* sc = (const uint16_t*)scales;
+  auto* Yh = (uint16_t*)Y;
+  return hip_status(gemv ? awq::launch_gemv(Xh, M, qweight, sc, zeros, N, K, Yh, st)
+                         : awq::launch_gemm(Xh, M, qweight, sc, zeros, N, K, Yh, st));
+}
+
+awq_status awq_linear_w4a16(const void* X, int64_t M, const uint32_t* qweight,
+                            const void* scales, const uint8_t* zeros, int64_t N, int64_t K,
+                            const awq_config* cfg, void* Y, uint32_t* flags, void* stream) {
+  return awq_linear_w4a16_ex(X, M, qweight, scales, zeros, N, K, cfg, Y, flags, AWQ_LINEAR_AUTO,
+                             stream);
+}
+
+}  // extern "C"

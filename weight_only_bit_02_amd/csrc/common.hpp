@@ -1,0 +1,148 @@
+// Device helpers shared by the AWQ kernels (gfx950 / CDNA4, wave64).
+//
+// The group quantizer here is the only one on the GPU: the stand-alone quantize+pack
+// kernel and the grid-search kernel both call it, so the codes the search scores are
+// the codes the pack kernel writes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "awq.h"
+
+namespace awq {
+
+constexpr int kGroup = 128;   // input channels per quantization group
+constexpr int kQMax = 15;     // 4-bit unsigned codes 0..15 with a zero point
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float h2f(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+__device__ __forceinline__ uint16_t f2h_bits(float f) {  // v_cvt_f16_f32, round-to-nearest-even
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// ------------------------------------------------------------------ DPP reductions
+// Reductions inside one 16-lane DPP row: quad_perm butterflies, then row rotations.
+// Every lane of the row ends up with the result.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
+}
+constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kDppRowRor4 = 0x124;
+constexpr int kDppRowRor8 = 0x128;
+
+__device__ __forceinline__ void row16_minmax(float& mn, float& mx) {
+  mn = fminf(mn, dpp_f32<kDppQuadXor1>(mn));
+  mx = fmaxf(mx, dpp_f32<kDppQuadXor1>(mx));
+  mn = fminf(mn, dpp_f32<kDppQuadXor2>(mn));
+  mx = fmaxf(mx, dpp_f32<kDppQuadXor2>(mx));
+  mn = fminf(mn, dpp_f32<kDppRowRor4>(mn));
+  mx = fmaxf(mx, dpp_f32<kDppRowRor4>(mx));
+  mn = fminf(mn, dpp_f32<kDppRowRor8>(mn));
+  mx = fmaxf(mx, dpp_f32<kDppRowRor8>(mx));
+}
+
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f32<kDppQuadXor1>(v);
+  v += dpp_f32<kDppQuadXor2>(v);
+  v += dpp_f32<kDppRowRor4>(v);
+  v += dpp_f32<kDppRowRor8>(v);
+  return v;
+}
+
+// Sum over the whole wave; the result is valid in every lane. Fixed order, so the
+// result is deterministic.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+// ------------------------------------------------------------------ group quantizer
+// Per group of 128 values w' (= w * s, an exact fp32 product), in fp32 with
+// round-to-nearest-even and no contraction:
+//   sc = max((mx - mn) / 15, 2^-14), clamped at 65504; sc_h = fp16(sc);
+//   z = clamp(rint(-mn / sc_h), 0, 15);  q = clamp(rint(w' / sc_h) + z, 0, 15).
+struct GroupQ {
+  float scf;     // the stored scale as fp32
+  float rcp;     // fp32(1 / scf), only used to find the easy codes quickly
+  float z;       // zero point, 0..15
+  uint16_t sch;  // fp16 bits of the stored scale
+  bool clamped;  // sc exceeded 65504
+};
+
+__device__ __forceinline__ GroupQ group_params(float mn, float mx) {
+#pragma clang fp contract(off)
+  GroupQ g;
+  float sc = (mx - mn) / 15.0f;  // correctly rounded division (no fast-math)
+  sc = fmaxf(sc, 0x1p-14f);
+  g.clamped = sc > 65504.0f;
+  sc = fminf(sc, 65504.0f);
+  g.sch = f2h_bits(sc);
+  g.scf = h2f(g.sch);
+  g.z = fminf(fmaxf(__builtin_rintf(-mn / g.scf), 0.0f), 15.0f);
+  g.rcp = 1.0f / g.scf;
+  return g;
+}
+
+// rint(w / scf) exactly as the correctly rounded quotient would give it. The product
+// w * rcp is within 2^-23 (relative) of the real quotient; unless it sits within
+// |q| * 2^-21 of a half-integer, it lies on the same side of that half-integer as
+// the correctly rounded quotient and rint gives the same integer. The rare close
+// calls take the correctly rounded division.
+__device__ __forceinline__ float rint_quotient(float w, const GroupQ& g) {
+#pragma clang fp contract(off)
+  float qa = w * g.rcp;
+  float fl = __builtin_floorf(qa);
+  float d = __builtin_fabsf((qa - fl) - 0.5f);
+  if (!(d > __builtin_fabsf(qa) * 0x1p-21f + 0x1p-60f)) qa = w / g.scf;
+  return __builtin_rintf(qa);
+}
+
+__device__ __forceinline__ float quant_code(float w, const GroupQ& g) {
+#pragma clang fp contract(off)
+  return fminf(fmaxf(rint_quotient(w, g) + g.z, 0.0f), 15.0f);
+}
+
+// ------------------------------------------------------------------ fp64 -> fp16
+// Exact round-to-nearest-even conversion of a double to binary16 bits (one rounding;
+// a detour through fp32 would round twice).
+__device__ __forceinline__ uint16_t f64_to_f16_rne(double d) {
+  uint64_t b = __builtin_bit_cast(uint64_t, d);
+  uint16_t sign = (uint16_t)((b >> 48) & 0x8000u);
+  uint64_t mag = b & 0x7FFFFFFFFFFFFFFFull;
+  if (mag >= 0x7FF0000000000000ull) return sign | (mag > 0x7FF0000000000000ull ? 0x7E00 : 0x7C00);
+  int e = (int)(mag >> 52) - 1023;
+  if (e > 15) return sign | 0x7C00;
+  if (e < -40) return sign;  // far below half the smallest subnormal
+  uint64_t m = (mag & 0xFFFFFFFFFFFFFull) | (1ull << 52);
+  int shift = (e >= -14) ? 42 : 42 + (-14 - e);
+  uint64_t q = m >> shift;
+  uint64_t rem = m & ((1ull << shift) - 1);
+  uint64_t half = 1ull << (shift - 1);
+  if (rem > half || (rem == half && (q & 1))) ++q;
+  if (e >= -14) return sign | (uint16_t)(((uint32_t)(e + 15) << 10) + (uint32_t)(q - 1024));
+  return sign | (uint16_t)q;
+}
+
+// Magnitude of an fp16 value in units of 2^-24 (every finite fp16 is an integer
+// multiple of 2^-24 below 2^40 units); returns -1 for Inf/NaN.
+__device__ __forceinline__ int64_t f16_abs_units(uint16_t h) {
+  uint32_t e = (h >> 10) & 0x1F, m = h & 0x3FF;
+  if (e == 31) return -1;
+  if (e == 0) return (int64_t)m;
+  return (int64_t)(1024 + m) << (e - 1);
+}
+
+}  // namespace awq

@@ -1,0 +1,48 @@
+// Internal launchers: host functions that enqueue one kernel each on a stream.
+// The C ABI (awq_abi.hip) validates arguments and calls these; nothing here checks
+// arguments again.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace awq {
+
+// a3 + a4: quantize W * diag(s) per group of 128 and pack codes / scales / zeros.
+hipError_t launch_quant_pack(const uint16_t* W, int64_t N, int64_t K, const uint16_t* s,
+                             uint32_t* qweight, uint16_t* scales, uint8_t* zeros,
+                             uint32_t* flags, hipStream_t stream);
+
+// a1: u_k = sum_t |X_tk| in units of 2^-24 (int64, exact), then a_k = u_k 2^-24 / T.
+hipError_t launch_zero_u64(unsigned long long* p, int64_t n, hipStream_t stream);
+hipError_t launch_act_sums(const uint16_t* X, int64_t T, int64_t K, unsigned long long* u,
+                           uint32_t* flags, hipStream_t stream);
+hipError_t launch_act_finalize(const unsigned long long* u, int64_t T, int64_t K, double* act,
+                               hipStream_t stream);
+
+// a2: s_grid[i][k] = fp16_rne(pow(max(act_k, 2^-14), i / n_grid)).
+hipError_t launch_scalegen(const double* act, int64_t K, int n_grid, uint16_t* s_grid,
+                           hipStream_t stream);
+
+// a5: per (alpha, row tile, token chunk) partial sums of the squared output error.
+int search_row_tile();
+int search_token_chunk(int64_t T);
+hipError_t launch_search_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N,
+                             int64_t K, const uint16_t* s_grid, int n_grid, double* partials,
+                             uint32_t* flags, hipStream_t stream);
+// a6: fixed-order sums of the partials, first-minimum argmin, s_best copy.
+hipError_t launch_search_reduce(const double* partials, int n_grid, int64_t n_partials,
+                                const uint16_t* s_grid, int64_t K, uint16_t* s_best,
+                                int32_t* best_idx, double* err, hipStream_t stream);
+
+// a7 / a8: Y = X deq(W)^T.
+hipError_t launch_gemv(const uint16_t* X, int64_t M, const uint32_t* qweight,
+                       const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
+                       uint16_t* Y, hipStream_t stream);
+hipError_t launch_gemm(const uint16_t* X, int64_t M, const uint32_t* qweight,
+                       const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
+                       uint16_t* Y, hipStream_t stream);
+
+constexpr int kGemvMaxM = 8;
+
+}  // namespace awq

@@ -1,0 +1,93 @@
+// Quantize + pack (a3 + a4): one pass over W, HBM-bound.
+//
+// "AWQ量化实战" §2.3: 128 consecutive input channels share one quantization step;
+// "大模型量化部署实战：GPTQ与AWQ算法", "大模型量化的核心原理与位宽选择": a 4-bit integer with a
+// scale and a zero point. Layout of the packed result: see include/awq.h.
+//
+// Mapping: a wave owns one (row, run of 4 groups) unit = 512 input channels. Lane l
+// reads 8 consecutive weights (one 16-byte load) and writes the 32-bit word that packs
+// their 8 codes, so loads and stores are fully coalesced; the 16 lanes of a DPP row
+// form one group and find its min / max with row-local DPP.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace awq {
+
+__global__ void __launch_bounds__(256) k_quant_pack(const uint16_t* __restrict__ W, int64_t N,
+                                                    int64_t K, const uint16_t* __restrict__ s,
+                                                    uint32_t* __restrict__ qweight,
+                                                    uint16_t* __restrict__ scales,
+                                                    uint8_t* __restrict__ zeros,
+                                                    uint32_t* __restrict__ flags) {
+  const int lane = threadIdx.x & 63;
+  const int gi = lane >> 4;  // group within the unit
+  const int li = lane & 15;  // lane within the group
+  const int64_t G = K / kGroup;
+  const int64_t chunks = (G + 3) / 4;
+  const int64_t units = N * chunks;
+  const int64_t wave0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  const int64_t zbytes = (G + 1) / 2;
+
+  for (int64_t u = wave0; u < units; u += nwaves) {
+    const int64_t n = u / chunks;
+    const int64_t j = (u - n * chunks) * 4 + gi;  // group index
+    const bool valid = j < G;
+    const int64_t k0 = j * kGroup + li * 8;
+
+    uint4 wv = make_uint4(0, 0, 0, 0);
+    uint4 sv = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);  // s = 1
+    if (valid) {
+      wv = *reinterpret_cast<const uint4*>(W + n * K + k0);
+      if (s) sv = *reinterpret_cast<const uint4*>(s + k0);
+    }
+    const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
+    const uint32_t sd[4] = {sv.x, sv.y, sv.z, sv.w};
+    float w[8];
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      w[2 * i] = h2f((uint16_t)(wd[i] & 0xFFFF)) * h2f((uint16_t)(sd[i] & 0xFFFF));
+      w[2 * i + 1] = h2f((uint16_t)(wd[i] >> 16)) * h2f((uint16_t)(sd[i] >> 16));
+    }
+    float mn = w[0], mx = w[0];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      bad |= !__builtin_isfinite(w[i]);
+      mn = fminf(mn, w[i]);
+      mx = fmaxf(mx, w[i]);
+    }
+    row16_minmax(mn, mx);
+    const GroupQ g = group_params(mn, mx);
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) word |= (uint32_t)quant_code(w[i], g) << (4 * i);
+
+    const uint32_t zi = (uint32_t)g.z;
+    const uint32_t z_next = (uint32_t)__shfl_down((int)zi, 16);  // zero of group j + 1
+    if (valid) {
+      qweight[(n * K + k0) >> 3] = word;
+      if (li == 0) {
+        scales[n * G + j] = g.sch;
+        if ((j & 1) == 0) {
+          const uint32_t hi = (j + 1 < G) ? z_next : 0u;
+          zeros[n * zbytes + (j >> 1)] = (uint8_t)(zi | (hi << 4));
+        }
+        if (g.clamped && flags) atomicOr(flags, AWQ_FLAG_SCALE_CLAMPED);
+      }
+      if (bad && flags) atomicOr(flags, AWQ_FLAG_NONFINITE_INPUT);
+    }
+  }
+}
+
+hipError_t launch_quant_pack(const uint16_t* W, int64_t N, int64_t K, const uint16_t* s,
+                             uint32_t* qweight, uint16_t* scales, uint8_t* zeros,
+                             uint32_t* flags, hipStream_t stream) {
+  const int64_t units = N * ((K / kGroup + 3) / 4);
+  const int64_t blocks = units / 4 + 1 < 16384 ? units / 4 + 1 : 16384;
+  hipLaunchKernelGGL(k_quant_pack, dim3((unsigned)blocks), dim3(256), 0, stream, W, N, K, s,
+                     qweight, scales, zeros, flags);
+  return hipGetLastError();
+}
+
+}  // namespace awq
