@@ -1,0 +1,280 @@
+#!/usr/bin/env python3
+"""Benchmark of the AWQ W4A16 hot path on one MI355X.
+
+One step = one pass of the whole hot path over one Llama-2-7B decoder layer's linears
+(seeded synthetic fp16 weights ~ N(0, 0.02^2), activations ~ N(0, 1) with 1% of the
+channels x20, group 128, 4-bit + zero point):
+  1. scale search (statistic, 20-point alpha grid, error, argmin) for the four
+     shared-input groups q|k|v [12288x4096], o [4096x4096], gate|up [22016x4096],
+     down [4096x11008], calibration X = 512 tokens;
+  2. quantize + pack of the seven matrices with the chosen scales;
+  3. decode GEMV at M = 1 over 32 layer copies of the seven matrices (one token through
+     the 32 decoder layers of a 7B model: 3.37 GB of packed weights, far above the
+     256 MB last-level cache, so every launch streams from HBM);
+  4. prefill MFMA dequant-GEMM at M = 2048 over the seven matrices.
+Inputs are resident in HBM before the timed region. Each part is captured once in a
+HIP graph (so host launch overhead is not kernel time) and replayed; HIP events on
+the launch stream time each part. The headline value is the GEMV bandwidth; the GEMM
+rate is reported beside it.
+
+Prints ONE JSON line. `python bench.py --gpus N` with N > 1 exits: this build runs
+on one GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published
+CALIB_T = 512
+PREFILL_M = 2048
+DECODE_LAYERS = 32
+GROUP = 128
+
+MATRICES = [  # name, search group, row offset inside the group, N, K
+    ("q_proj", "qkv", 0, 4096, 4096), ("k_proj", "qkv", 4096, 4096, 4096),
+    ("v_proj", "qkv", 8192, 4096, 4096), ("o_proj", "o", 0, 4096, 4096),
+    ("gate_proj", "gate_up", 0, 11008, 4096), ("up_proj", "gate_up", 11008, 11008, 4096),
+    ("down_proj", "down", 0, 4096, 11008),
+]
+SEARCH_GROUPS = {"qkv": (12288, 4096), "o": (4096, 4096), "gate_up": (22016, 4096), "down": (4096, 11008)}
+
+
+def packed_bytes(N, K):
+    G = K // GROUP
+    return N * (K // 2) + N * G * 2 + N * ((G + 1) // 2)
+
+
+def linear_bytes(M, N, K):
+    return packed_bytes(N, K) + 2 * M * K + 2 * M * N
+
+
+def source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "weight_only_bit_02_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(budget_s: float = 15.0):
+    """The CPU oracle's W4A16 linear at M = 1 on the 7B matrices, bounded to ~budget_s."""
+    import numpy as np
+    import oracle
+    import synthetic_inputs as si
+    done_bytes, wall, cpu, names = 0, 0.0, 0.0, []
+    for i, (name, _, _, N, K) in enumerate(MATRICES):
+        W = si.weights(N, K, offset=500 + i)
+        qw, sc, zb, _ = oracle.quantize_pack(W)
+        x = si.activations(1, K, offset=600 + i)
+        t0, c0 = time.perf_counter(), time.process_time()
+        oracle.linear_reference(x, qw, sc, zb, K)
+        wall += time.perf_counter() - t0
+        cpu += time.process_time() - c0
+        done_bytes += linear_bytes(1, N, K)
+        names.append(name)
+        if wall > budget_s:
+            break
+    return {"value": round(done_bytes / wall / 1e9, 4), "unit": "GB/s",
+            "cores": max(1, round(cpu / wall)), "kind": "oracle",
+            "sample": f"oracle fp64 W4A16 linear, M=1, on {len(names)} of the 7 Llama-2-7B matrices "
+                      f"({', '.join(names)}); {done_bytes / 1e6:.1f} MB algorithmic in {wall:.2f} s"}
+
+
+def load_traffic(kernel_key):
+    """HBM bytes per launch measured with rocprofv3 counters (profiles/traffic.json), or None
+    when the kernels changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("source_hash") != source_hash():
+        return None
+    return d.get("kernels", {}).get(kernel_key)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--layers", type=int, default=DECODE_LAYERS)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying graphs")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU; --gpus N with N > 1 is not supported "
+              "(the multi-GPU sharding is a design note only).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synthetic_inputs as si
+    import weight_only_bit_02_amd as awq
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+
+    # ------------------------------------------------------------------ inputs (untimed)
+    log("bench: generating inputs")
+    Wg = {g: si.torch_weights(N, K, 100 + i, dev) for i, (g, (N, K)) in enumerate(SEARCH_GROUPS.items())}
+    Xcal = {g: si.torch_activations(CALIB_T, K, 200 + i, dev, channel_offset=K)
+            for i, (g, (N, K)) in enumerate(SEARCH_GROUPS.items())}
+    ws = {g: awq.SearchWorkspace(CALIB_T, N, K, dev) for g, (N, K) in SEARCH_GROUPS.items()}
+    sres = {g: awq.SearchResult(torch.empty(K, dtype=torch.float16, device=dev),
+                                torch.empty(1, dtype=torch.int32, device=dev),
+                                torch.empty(20, dtype=torch.float64, device=dev),
+                                torch.empty((20, K), dtype=torch.float16, device=dev))
+            for g, (N, K) in SEARCH_GROUPS.items()}
+    Wm = {name: Wg[g][off:off + N] for name, g, off, N, K in MATRICES}
+    packed = [{name: awq.alloc_packed(N, K, dev) for name, _, _, N, K in MATRICES} for _ in range(args.layers)]
+    log(f"bench: packing {args.layers} layer copies")
+    for c in range(1, args.layers):
+        for i, (name, _, _, N, K) in enumerate(MATRICES):
+            w = si.torch_weights(N, K, 1000 + 7 * c + i, dev)
+            awq.quantize_pack(w, out=packed[c][name])
+            del w
+    xdec = {4096: si.torch_activations(1, 4096, 300, dev, channel_offset=4096),
+            11008: si.torch_activations(1, 11008, 301, dev, channel_offset=11008)}
+    ydec = {name: torch.empty((1, N), dtype=torch.float16, device=dev) for name, _, _, N, K in MATRICES}
+    xpre = {4096: si.torch_activations(PREFILL_M, 4096, 400, dev, channel_offset=4096),
+            11008: si.torch_activations(PREFILL_M, 11008, 401, dev, channel_offset=11008)}
+    ypre = {name: torch.empty((PREFILL_M, N), dtype=torch.float16, device=dev) for name, _, _, N, K in MATRICES}
+    torch.cuda.synchronize()
+
+    # ------------------------------------------------------------------ the four parts
+    def part_search():
+        for g in SEARCH_GROUPS:
+            awq.search_scales(Xcal[g], Wg[g], workspace=ws[g], out=sres[g])
+
+    def part_pack():
+        for name, g, _, _, _ in MATRICES:
+            awq.quantize_pack(Wm[name], sres[g].s_best, out=packed[0][name])
+
+    def part_gemv():
+        for c in range(args.layers):
+            for name, _, _, N, K in MATRICES:
+                awq.linear_w4a16(xdec[K], packed[c][name], out=ydec[name])
+
+    def part_gemm():
+        for name, _, _, N, K in MATRICES:
+            awq.linear_w4a16(xpre[K], packed[0][name], out=ypre[name])
+
+    parts = [("search", part_search), ("quant_pack", part_pack), ("gemv", part_gemv), ("gemm", part_gemm)]
+    stream = torch.cuda.Stream()
+    runners = {}
+    with torch.cuda.stream(stream):
+        for _, fn in parts:  # eager warm-up (also loads the code objects)
+            fn()
+        torch.cuda.synchronize()
+        eager_ref = {"best": {g: sres[g].best_idx.clone() for g in SEARCH_GROUPS},
+                     "y": {n: ydec[n].clone() for n in ydec}, "Y": {n: ypre[n].clone() for n in ypre}}
+        for pname, fn in parts:
+            if args.no_graph:
+                runners[pname] = fn
+            else:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    fn()
+                runners[pname] = g.replay
+        torch.cuda.synchronize()
+
+        def step(evs=None):
+            for i, (pname, _) in enumerate(parts):
+                if evs is not None:
+                    evs[i].record(stream)
+                runners[pname]()
+            if evs is not None:
+                evs[len(parts)].record(stream)
+
+        log(f"bench: warmup {args.warmup} steps")
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in range(args.steps)]
+        log(f"bench: timing {args.steps} steps")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(args.steps):
+            step(ev[s])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        part_ms = {pname: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps
+                   for i, (pname, _) in enumerate(parts)}
+
+        # graph replays must reproduce the eager results bit for bit
+        for g in SEARCH_GROUPS:
+            assert torch.equal(sres[g].best_idx, eager_ref["best"][g]), "graph replay differs (search)"
+        for n in ydec:
+            assert torch.equal(ydec[n], eager_ref["y"][n]), "graph replay differs (gemv)"
+            assert torch.equal(ypre[n], eager_ref["Y"][n]), "graph replay differs (gemm)"
+
+    # ------------------------------------------------------------------ figures
+    n_gemv = args.layers * len(MATRICES)
+    gemv_bytes = args.layers * sum(linear_bytes(1, N, K) for _, _, _, N, K in MATRICES)
+    gemv_gbs = gemv_bytes / (part_ms["gemv"] * 1e-3) / 1e9
+    gemm_flops = sum(2 * PREFILL_M * N * K for _, _, _, N, K in MATRICES)
+    gemm_tflops = gemm_flops / (part_ms["gemm"] * 1e-3) / 1e12
+    search_flops = sum(2 * CALIB_T * N * K * 20 for N, K in SEARCH_GROUPS.values())
+    search_tflops = search_flops / (part_ms["search"] * 1e-3) / 1e12
+    pack_bytes = sum(N * K * 2 + packed_bytes(N, K) for _, _, _, N, K in MATRICES)
+    pack_gbs = pack_bytes / (part_ms["quant_pack"] * 1e-3) / 1e9
+    best = {g: int(sres[g].best_idx.item()) for g in SEARCH_GROUPS}
+
+    traffic = load_traffic("gemv_m1")
+    result = {
+        "metric": "W4A16 GEMV GB/s @M=1 and dequant-GEMM TFLOP/s @M=2048, 7B shapes",
+        "value": round(gemv_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 (int4 weights, fp32 accumulate)",
+        "data": "synthetic (seeded; W ~ N(0,0.02^2), X ~ N(0,1) with 1% channels x20)",
+        "config": {"workload": "Llama-2-7B decoder-layer linears: decode GEMV M=1 over "
+                               f"{args.layers} layer copies; prefill GEMM M={PREFILL_M}; "
+                               f"scale search T={CALIB_T}, 20 alpha, group 128; quantize+pack",
+                   "gemv_launches_per_step": n_gemv, "group_size": GROUP, "w_bit": 4,
+                   "graphs": not args.no_graph},
+        "roofline": {"bound": "hbm", "achieved": round(gemv_gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gemv_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": "k_gemv<1,4> (M=1)",
+                     "avg_launch_us": round(part_ms["gemv"] * 1e3 / n_gemv, 3),
+                     "algorithmic_bytes_per_launch": round(gemv_bytes / n_gemv)},
+        "gemm": {"tflops": round(gemm_tflops, 2), "ms": round(part_ms["gemm"], 4),
+                 "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2),
+                              "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                              "frac": round(gemm_tflops / FP16_MFMA_PEAK_TFLOPS, 4)}},
+        "search": {"tflops_algorithmic": round(search_tflops, 2), "ms": round(part_ms["search"], 4),
+                   "best_alpha_index": best,
+                   "roofline": {"bound": "mfma", "achieved": round(search_tflops, 2),
+                                "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                "frac": round(search_tflops / FP16_MFMA_PEAK_TFLOPS, 4)}},
+        "quant_pack": {"gbs": round(pack_gbs, 2), "ms": round(part_ms["quant_pack"], 4),
+                       "roofline": {"bound": "hbm", "achieved": round(pack_gbs, 2), "peak": HBM_PEAK_GBS,
+                                    "unit": "GB/s", "frac": round(pack_gbs / HBM_PEAK_GBS, 4)}},
+        "gemv_ms": round(part_ms["gemv"], 4),
+        "source_hash": source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle (bounded sample)")
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
