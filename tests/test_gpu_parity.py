@@ -227,3 +227,10 @@ def test_linear_auto_dispatch_and_determinism():
         assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
         y_ref, bound = oracle.linear_reference(Xm, *ref, 1024)
         assert oracle.linear_within_tolerance(a.astype(np.float64), y_ref, bound).all()
+
+
+@pytest.mark.parametrize("N,K", [(4097, 4096), (9000, 1152), (11008, 4096), (4096, 11008)])
+def test_gemv_m1_many_rows_per_wave(N, K):
+    """Enough rows that every wave of the persistent M = 1 grid walks several row groups."""
+    p, ref = _packed_case(N, K, off=N + K + 7)
+    _check_linear(si.activations(1, K, offset=N), p, ref, "gemv")

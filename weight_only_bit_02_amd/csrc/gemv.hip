@@ -97,6 +97,209 @@ __global__ void __launch_bounds__(256)
     }
 }
 
+// M = 1: the activation row is staged once per block in LDS, already re-paired, so
+// the inner loop reads it with ds_read_b128 and no permutes. A lane's code loads for
+// U chunks of each of its R rows are issued together, and the next batch is in flight
+// while the current one is multiplied (two register buffers), so a wave keeps
+// R * U * 16 bytes per lane of HBM reads outstanding.
+template <int R, int U>
+struct GemvBatch {
+  uint4 cw[R][U];
+  uint16_t sc[R][U];
+  uint8_t zb[R][U];
+};
+
+template <int R, int U>
+__device__ __forceinline__ void gemv1_load(GemvBatch<R, U>& bt, const uint32_t* qweight,
+                                           const uint16_t* scales, const uint8_t* zeros,
+                                           const int64_t (&rows)[R],
+                                           int64_t C, int64_t words, int64_t G, int64_t zbytes,
+                                           int64_t b, int lane) {
+  // Straight-line loads (chunk index clamped, results past the row end unused), so the
+  // compiler can keep them all in flight and wait for each one only where it is used.
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    int64_t c = (b * U + u) * 64 + lane;
+    c = c < C ? c : C - 1;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      bt.cw[r][u] = *reinterpret_cast<const uint4*>(qweight + rows[r] * words + c * 4);
+      bt.sc[r][u] = scales[rows[r] * G + (c >> 2)];
+      bt.zb[r][u] = zeros[rows[r] * zbytes + (c >> 3)];
+    }
+  }
+}
+
+// fp16 magic 1024.0 in both halves, held in a VGPR the optimizer cannot see through: the
+// widening then compiles to one v_and_or_b32 per pair (mask from an SGPR, magic from
+// this VGPR) instead of an AND and an OR with literal operands.
+__device__ __forceinline__ uint32_t magic_1024x2() {
+  uint32_t m;
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(m));
+  return m;
+}
+
+template <int R, int U>
+__device__ __forceinline__ void gemv1_compute(const GemvBatch<R, U>& bt, const uint4* __restrict__ xs,
+                                              float (&acc)[R], int64_t C, int64_t b, int lane,
+                                              uint32_t magic) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t c = (b * U + u) * 64 + lane;
+    if (c < C) {
+      half2v xq[16];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint4 v = xs[c * 4 + w];
+        xq[w * 4 + 0] = __builtin_bit_cast(half2v, v.x);
+        xq[w * 4 + 1] = __builtin_bit_cast(half2v, v.y);
+        xq[w * 4 + 2] = __builtin_bit_cast(half2v, v.z);
+        xq[w * 4 + 3] = __builtin_bit_cast(half2v, v.w);
+      }
+      const int nib = (int)((c >> 2) & 1) * 4;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const uint32_t z = (bt.zb[r][u] >> nib) & 0xF;
+        const uint32_t zbits = 0x6400u + z;
+        const half2v zz = -__builtin_bit_cast(half2v, zbits | (zbits << 16));
+        const uint32_t wd[4] = {bt.cw[r][u].x, bt.cw[r][u].y, bt.cw[r][u].z, bt.cw[r][u].w};
+        float part0 = 0.0f, part1 = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const uint32_t q = ((wd[w] >> (4 * p)) & 0x000F000Fu) | magic;
+            const half2v d = __builtin_bit_cast(half2v, q) + zz;  // exact (q - z)
+            if (p & 1) part1 = __builtin_amdgcn_fdot2(d, xq[w * 4 + p], part1, false);
+            else part0 = __builtin_amdgcn_fdot2(d, xq[w * 4 + p], part0, false);
+          }
+        acc[r] += h2f(bt.sc[r][u]) * (part0 + part1);
+      }
+    }
+  }
+}
+
+// Barrier for LDS data only: wait for this wave's LDS operations, then s_barrier. Unlike
+// __syncthreads() it does not wait for outstanding global loads, so the HBM reads
+// issued before it stay in flight. The memory clobber keeps the compiler from moving
+// those loads past it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Persistent grid: a few blocks per CU; each wave walks its row groups (R rows, all of K)
+// as a flat list of (row group, batch of U chunks per lane) items and always has the
+// next item's code loads in flight while it multiplies the current one. The block
+// stages the activation row once for all its rows.
+template <int R, int U, int XR>
+__global__ void __launch_bounds__(256)
+    k_gemv1(const uint16_t* X, const uint32_t* qweight, const uint16_t* scales,
+            const uint8_t* zeros, int64_t N, int64_t K, uint16_t* Y) {
+  // (no __restrict__: the code loads must stay ordered before the LDS barrier below)
+  // XR * 256 entries (>= K / 8): channels 8i..8i+7 as (0,4) (1,5) (2,6) (3,7)
+  extern __shared__ uint4 xs[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int64_t wave0 = (int64_t)blockIdx.x * 4 + (tid >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  const int64_t C = K / 32, G = K / kGroup, zbytes = (G + 1) / 2, words = K / 8;
+  const int64_t nb = (C + 64 * U - 1) / (64 * U);  // batches per row group
+  const int64_t ngroups = (N + R - 1) / R;
+  const int64_t my_groups = wave0 < ngroups ? (ngroups - wave0 + nwaves - 1) / nwaves : 0;
+  const int64_t items = my_groups * nb;
+  __builtin_assume(nb >= 1);
+
+  auto rows_of = [&](int64_t item, int64_t (&rows)[R]) {
+    const int64_t g = wave0 + (item / nb) * nwaves;
+#pragma unroll
+    for (int r = 0; r < R; ++r) rows[r] = (g * R + r < N) ? g * R + r : N - 1;
+  };
+
+  // Activation loads first, then the first item's code loads; the scheduler barriers
+  // keep that order, so waiting for the activations (in-order load counter) does not
+  // wait for the codes, and the LDS-only barrier leaves the HBM reads in flight.
+  uint4 v[XR];
+#pragma unroll
+  for (int j = 0; j < XR; ++j) {
+    const int64_t i = j * 256 + tid;
+    v[j] = *reinterpret_cast<const uint4*>(X + (i < words ? i : words - 1) * 8);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  GemvBatch<R, U> b0, b1;
+  int64_t rows[R];
+  rows_of(0, rows);
+  if (items > 0) gemv1_load(b0, qweight, scales, zeros, rows, C, words, G, zbytes, 0, lane);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < XR; ++j) {
+    const int64_t i = j * 256 + tid;
+    uint4 p;
+    p.x = __builtin_amdgcn_perm(v[j].z, v[j].x, 0x05040100u);
+    p.y = __builtin_amdgcn_perm(v[j].z, v[j].x, 0x07060302u);
+    p.z = __builtin_amdgcn_perm(v[j].w, v[j].y, 0x05040100u);
+    p.w = __builtin_amdgcn_perm(v[j].w, v[j].y, 0x07060302u);
+    xs[i] = p;  // the LDS row is padded to XR * 256 entries, so no store is predicated
+  }
+  lds_barrier();
+
+  const uint32_t magic = magic_1024x2();
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+
+  auto finish = [&](int64_t item) {  // after the last batch of a row group
+    if ((item % nb) != nb - 1) return;
+    const int64_t g = wave0 + (item / nb) * nwaves;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float sum = wave_sum(acc[r]);
+      if (lane == 0 && g * R + r < N) Y[g * R + r] = f2h_bits(sum);
+      acc[r] = 0.0f;
+    }
+  };
+
+  for (int64_t t = 0; t < items; t += 2) {
+    if (t + 1 < items) {
+      rows_of(t + 1, rows);
+      gemv1_load(b1, qweight, scales, zeros, rows, C, words, G, zbytes, (t + 1) % nb, lane);
+    }
+    gemv1_compute(b0, xs, acc, C, t % nb, lane, magic);
+    finish(t);
+    if (t + 2 < items) {
+      rows_of(t + 2, rows);
+      gemv1_load(b0, qweight, scales, zeros, rows, C, words, G, zbytes, (t + 2) % nb, lane);
+    }
+    if (t + 1 < items) {
+      gemv1_compute(b1, xs, acc, C, (t + 1) % nb, lane, magic);
+      finish(t + 1);
+    }
+  }
+}
+
+template <int R, int U, int XR>
+static hipError_t launch_gemv1_x(const uint16_t* X, const uint32_t* qw, const uint16_t* sc,
+                                 const uint8_t* z, int64_t N, int64_t K, uint16_t* Y,
+                                 int blocks_per_cu, hipStream_t stream) {
+  const int64_t want = (N + 4 * R - 1) / (4 * R);
+  const int64_t cap = (int64_t)256 * blocks_per_cu;
+  const int64_t blocks = want < cap ? want : cap;
+  hipLaunchKernelGGL((k_gemv1<R, U, XR>), dim3((unsigned)blocks), dim3(256), (size_t)XR * 256 * 16, stream,
+                     X, qw, sc, z, N, K, Y);
+  return hipGetLastError();
+}
+
+// K <= 32768 (the activation row fits the 64 KiB of LDS this kernel asks for).
+template <int R, int U>
+static hipError_t launch_gemv1(const uint16_t* X, const uint32_t* qw, const uint16_t* sc,
+                               const uint8_t* z, int64_t N, int64_t K, uint16_t* Y,
+                               int blocks_per_cu, hipStream_t stream) {
+  const int64_t per_thread = (K / 8 + 255) / 256;
+  if (per_thread <= 2) return launch_gemv1_x<R, U, 2>(X, qw, sc, z, N, K, Y, blocks_per_cu, stream);
+  if (per_thread <= 4) return launch_gemv1_x<R, U, 4>(X, qw, sc, z, N, K, Y, blocks_per_cu, stream);
+  if (per_thread <= 8) return launch_gemv1_x<R, U, 8>(X, qw, sc, z, N, K, Y, blocks_per_cu, stream);
+  return launch_gemv1_x<R, U, 16>(X, qw, sc, z, N, K, Y, blocks_per_cu, stream);
+}
+
 template <int M>
 static hipError_t launch_gemv_m(const uint16_t* X, const uint32_t* qw, const uint16_t* sc,
                                 const uint8_t* z, int64_t N, int64_t K, uint16_t* Y,
@@ -113,7 +316,12 @@ hipError_t launch_gemv(const uint16_t* X, int64_t M, const uint32_t* qweight,
                        const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
                        uint16_t* Y, hipStream_t stream) {
   switch (M) {
-    case 1: return launch_gemv_m<1>(X, qweight, scales, zeros, N, K, Y, stream);
+    case 1:
+      // Two rows per wave; one chunk batch per lane for K <= 4096, two above (measured best
+      // on the Llama-2 shapes). 16 blocks per CU caps the grid only for very tall matrices.
+      if (K <= 4096) return launch_gemv1<2, 1>(X, qweight, scales, zeros, N, K, Y, 16, stream);
+      if (K <= 32768) return launch_gemv1<2, 2>(X, qweight, scales, zeros, N, K, Y, 16, stream);
+      return launch_gemv_m<1>(X, qweight, scales, zeros, N, K, Y, stream);
     case 2: return launch_gemv_m<2>(X, qweight, scales, zeros, N, K, Y, stream);
     case 3: return launch_gemv_m<3>(X, qweight, scales, zeros, N, K, Y, stream);
     case 4: return launch_gemv_m<4>(X, qweight, scales, zeros, N, K, Y, stream);
