@@ -30,9 +30,10 @@ awq_status hip_status(hipError_t e) { return e == hipSuccess ? AWQ_OK : AWQ_ERR_
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Search workspace: [u: int64 K][act: fp64 K][s_grid: fp16 n_grid K][partials: fp64 ...]
+// Search workspace: [u: int64 K][act: fp64 K][s_grid: fp16 n_grid K][rowmax: f32 N]
+// [srange: f32 n_grid][partials: fp64 n_grid x row tiles x token chunks]
 struct SearchLayout {
-  size_t u, act, sgrid, partials, total;
+  size_t u, act, sgrid, rowmax, srange, partials, total;
   int64_t n_partials;  // per grid point
 };
 
@@ -44,7 +45,9 @@ SearchLayout search_layout(int64_t T, int64_t N, int64_t K, int n_grid) {
   L.u = 0;
   L.act = align256(L.u + (size_t)K * 8);
   L.sgrid = align256(L.act + (size_t)K * 8);
-  L.partials = align256(L.sgrid + (size_t)n_grid * K * 2);
+  L.rowmax = align256(L.sgrid + (size_t)n_grid * K * 2);
+  L.srange = align256(L.rowmax + (size_t)N * 4);
+  L.partials = align256(L.srange + (size_t)n_grid * 4);
   L.total = align256(L.partials + (size_t)n_grid * L.n_partials * 8);
   return L;
 }
@@ -159,7 +162,8 @@ awq_status awq_search_scales(const void* X, int64_t T, const void* W, int64_t N,
   if (e == hipSuccess) e = awq::launch_act_finalize(u, T, K, act, st);
   if (e == hipSuccess) e = awq::launch_scalegen(act, K, c.n_grid, sg, st);
   if (e == hipSuccess)
-    e = awq::launch_search_err(Xh, T, (const uint16_t*)W, N, K, sg, c.n_grid, partials, flags, st);
+    e = awq::launch_search_err(Xh, T, (const uint16_t*)W, N, K, sg, c.n_grid,
+                               (float*)(ws + L.rowmax), (float*)(ws + L.srange), partials, flags, st);
   if (e == hipSuccess)
     e = awq::launch_search_reduce(partials, c.n_grid, L.n_partials, sg, K, (uint16_t*)s_best,
                                   best_idx, err, st);

@@ -3,14 +3,21 @@
 // "AWQ量化技术Skill", "主要功能和特点": a GEMM kernel serves batch sizes above one;
 // "AWQ量化实战" §2.3 / §3.4: weights stay 4-bit in memory and are dequantized on the fly.
 //
-// Block tile 128 (tokens) x 128 (output channels), K step = one quantization group
-// (128 channels), four waves each owning a 64 x 64 sub-tile (2 x 2 tiles of
-// v_mfma_f32_32x32x16_f16). Per K step the block stages through LDS:
-//   - A: X[128][128] fp16, re-paired per 8 channels as (k, k+4) to match the codes;
-//   - B: the 128 x 128 codes, widened exactly to (q - z) in fp16 and multiplied by the
-//     group scale in fp16 (one rounding), in the same paired order.
-// Both operands then feed the MFMA in the same channel order, so the contraction is
-// the plain sum over K. fp32 accumulation, one fp16 rounding of the result.
+// Block tile 128 (tokens) x 256 (output channels), K step 128 (one group), four waves side by side
+// along N, each owning 128 x 64 = 4 x 2 tiles of v_mfma_f32_32x32x16_f16.
+//   - A (activations) is shared by the four waves: it goes global -> registers -> LDS,
+//     re-paired per 8 channels as (k, k+4) to match the code unpack, double-buffered
+//     with one barrier per K step; loads run two K steps ahead of the MFMAs.
+//   - B (codes) is private to a wave: each lane loads two 16-byte chunks (8 packed words,
+//     64 channels of one output column) straight into registers; word s is the lane's
+//     B operand for the wave's k16 step s. It is widened exactly to (q - z) with the
+//     0x6400 trick and a packed fp16 add, then multiplied by the group scale in fp16
+//     (one rounding), so no LDS round trip and no barrier are needed for B.
+// Within a K step the lane half h = lane / 32 covers channels [64 h, 64 h + 64) and k16
+// step s covers 8 of them; A is read from LDS with the same channel map, so the contraction
+// is the plain sum over K. fp32 accumulation, one fp16 rounding of the result.
+// The 128-row A panels are handed to the XCDs in contiguous runs of tiles, so the
+// blocks running together on one XCD share their A panel in that XCD's L2.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -21,121 +28,214 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBM = 128;
-constexpr int kBN = 128;
-constexpr int kLdsK = 128 + 8;  // halves per LDS row (16-byte pad)
+constexpr int kBN = 256;
+constexpr int kBK = 128;              // one quantization group per K step
+constexpr int kAStride = kBK + 8;     // halves per LDS row of A (16-byte pad)
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ uint32_t gemm_magic() {
+  uint32_t m;
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(m));
+  return m;
+}
+
+__device__ __forceinline__ uint4 pair_k_k4(uint4 v) {  // (0,1)(2,3)(4,5)(6,7) -> (0,4)(1,5)(2,6)(3,7)
+  uint4 p;
+  p.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
+  p.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);
+  p.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
+  p.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
+  return p;
+}
+
+// One packed word -> 8 dequantized fp16 channels (q - z) * sc in (k, k+4) pair order.
+__device__ __forceinline__ half8 dequant_word(uint32_t w, half2v zz, half2v s2, uint32_t magic) {
+  half2v d[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t u = ((w >> (4 * p)) & 0x000F000Fu) | magic;
+    d[p] = (__builtin_bit_cast(half2v, u) + zz) * s2;
+  }
+  return half8{d[0][0], d[0][1], d[1][0], d[1][1], d[2][0], d[2][1], d[3][0], d[3][1]};
+}
+
+// Per-step operands that travel through registers: this thread's share of the A tile
+// (8 x 16 bytes) and this lane's codes (2 columns x 32 bytes) with their scale and zero.
+struct GemmStage {
+  uint4 a[8];
+  uint4 b[2][2];
+  uint32_t zb[2], sc[2];
+};
 
 __global__ void __launch_bounds__(256)
-    k_gemm(const uint16_t* __restrict__ X, int64_t M, const uint32_t* __restrict__ qweight,
-           const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int64_t N,
-           int64_t K, uint16_t* __restrict__ Y) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[kBM * kLdsK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[kBN * kLdsK];
+    k_gemm(const uint16_t* X, int64_t M, const uint32_t* qweight, const uint16_t* scales,
+           const uint8_t* zeros, int64_t N, int64_t K, uint16_t* __restrict__ Y, int64_t mt,
+           int64_t nt, int64_t per_xcd) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kAStride];
+
+  // ---- XCD-aware tile order: XCD x (= blockIdx % 8) takes tiles [x * per_xcd, ...),
+  // consecutive tiles share an A panel (m tile) and walk N.
+  const int64_t t = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (t >= mt * nt) return;
+  const int64_t m0 = (t / nt) * kBM;
+  const int64_t n0 = (t % nt) * kBN;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int m32 = lane & 31, khalf = lane >> 5;
-  const int64_t m0 = (int64_t)blockIdx.y * kBM;
-  const int64_t n0 = (int64_t)blockIdx.x * kBN;
-  const int64_t G = K / kGroup;
-  const int64_t zb = (G + 1) / 2;
-  const int64_t words = K / 8;
+  const int m32 = lane & 31, kh = lane >> 5;
+  const int64_t G = K / kGroup, zb = (G + 1) / 2, words = K / 8;
+  const int64_t nsteps = G;
+  const uint32_t magic = gemm_magic();
 
-  f32x16 acc[2][2];
+  // A staging map: 128 rows x 128 channels = 2048 16-byte pieces, 8 per thread.
+  int64_t a_row[8];
+  int a_kc[8];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int i = 0; i < 8; ++i) {
+    const int id = i * 256 + tid;
+    const int64_t r = m0 + (id >> 4);
+    a_row[i] = (r < M ? r : M - 1) * K;
+    a_kc[i] = id & 15;
+  }
+  // B map: this lane's two output columns.
+  int64_t b_col[2];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+  for (int b = 0; b < 2; ++b) {
+    const int64_t n = n0 + wave * 64 + b * 32 + m32;
+    b_col[b] = n < N ? n : N - 1;
+  }
 
-  for (int64_t g = 0; g < G; ++g) {
-    // ---------------------------------------------------------------- stage A
+  // small loads first, then codes, then activations: waits for an older stage never
+  // cover a younger one (in-order load counter)
+  auto load = [&](GemmStage& st, int64_t step) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      st.zb[b] = zeros[b_col[b] * zb + (step >> 1)];
+      st.sc[b] = scales[b_col[b] * G + step];
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        st.b[b][h] = *reinterpret_cast<const uint4*>(qweight + b_col[b] * words + step * 16 + kh * 8 + h * 4);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      st.a[i] = *reinterpret_cast<const uint4*>(X + a_row[i] + step * kBK + a_kc[i] * 8);
+  };
+  auto store_a = [&](const GemmStage& st, int buf) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int id = i * 256 + tid;
-      const int row = id >> 4, kc = id & 15;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (m0 + row < M) v = *reinterpret_cast<const uint4*>(X + (m0 + row) * K + g * kGroup + kc * 8);
-      uint4 p;
-      p.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
-      p.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);
-      p.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
-      p.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
-      *reinterpret_cast<uint4*>(&As[row * kLdsK + kc * 8]) = p;
+      *reinterpret_cast<uint4*>(&As[buf][(id >> 4) * kAStride + a_kc[i] * 8]) = pair_k_k4(st.a[i]);
     }
-    // ---------------------------------------------------------------- stage B
+  };
+
+  f32x16 acc[4][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int id = i * 256 + tid;
-      const int n = id >> 2, wc = id & 3;
-      uint4 cw = make_uint4(0, 0, 0, 0);
-      half2v zz = {}, s2 = {};
-      if (n0 + n < N) {
-        const int64_t nn = n0 + n;
-        cw = *reinterpret_cast<const uint4*>(qweight + nn * words + g * 16 + wc * 4);
-        const uint32_t zbyte = zeros[nn * zb + (g >> 1)];
-        const uint32_t z = (g & 1) ? (zbyte >> 4) : (zbyte & 0xF);
-        const uint32_t zbits = 0x6400u + z;
-        zz = -__builtin_bit_cast(half2v, zbits | (zbits << 16));
-        const uint32_t sb = scales[nn * G + g];
-        s2 = __builtin_bit_cast(half2v, sb | (sb << 16));
-      } else {
-        cw = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
-        zz = -__builtin_bit_cast(half2v, 0x64086408u);  // q = z = 8 -> 0
-      }
-      const uint32_t wd[4] = {cw.x, cw.y, cw.z, cw.w};
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        uint32_t o[4];
+    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+
+  // Prefetch distance 2: stage `cur` is being multiplied, `nxt` (one step ahead) has its
+  // A in flight to LDS, `nn` (two steps ahead) is being loaded. The loop is unrolled by
+  // three with the stages' roles rotated, so no register copy (which would wait for the
+  // loads just issued) is ever needed.
+  GemmStage S0, S1, S2;
+  load(S0, 0);
+  load(S1, nsteps > 1 ? 1 : 0);
+  store_a(S0, 0);
+  __syncthreads();
+
+  auto body = [&](GemmStage& cur, GemmStage& nxt, GemmStage& nn, int64_t step) {
+    const int buf = (int)(step & 1);
+    // always issued (clamped to the last step) so the load counter is the same on every
+    // path and the waits below can be exact
+    load(nn, step + 2 < nsteps ? step + 2 : nsteps - 1);
+    half2v zz[2], s2[2];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const uint32_t u = ((wd[w] >> (4 * p)) & 0x000F000Fu) | 0x64006400u;
-          const half2v d = (__builtin_bit_cast(half2v, u) + zz) * s2;
-          o[p] = __builtin_bit_cast(uint32_t, d);
-        }
-        *reinterpret_cast<uint4*>(&Bs[n * kLdsK + wc * 32 + w * 8]) = make_uint4(o[0], o[1], o[2], o[3]);
-      }
+    for (int b = 0; b < 2; ++b) {
+      const uint32_t z = (step & 1) ? (cur.zb[b] >> 4) : (cur.zb[b] & 0xF);
+      const uint32_t zbits = 0x6400u + z;
+      zz[b] = -__builtin_bit_cast(half2v, zbits | (zbits << 16));
+      s2[b] = __builtin_bit_cast(half2v, cur.sc[b] | (cur.sc[b] << 16));
     }
-    __syncthreads();
-    // ---------------------------------------------------------------- MFMA
+    // lane half kh covers channels [64 kh, 64 kh + 64) of the step; k16 step s covers 8 of
+    // them. Operands of step s + 1 (A from LDS, B dequantized) are produced while the
+    // MFMAs of step s run.
+    auto load_frags = [&](int s, half8 (&A)[4], half8 (&B)[2]) {
 #pragma unroll
-    for (int st = 0; st < kGroup / 16; ++st) {
-      const int koff = st * 16 + khalf * 8;
-      half8 A[2], B[2];
+      for (int a = 0; a < 4; ++a)
+        A[a] = __builtin_bit_cast(
+            half8, *reinterpret_cast<const uint4*>(&As[buf][(a * 32 + m32) * kAStride + kh * 64 + s * 8]));
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
-        A[a] = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(&As[(wm * 64 + a * 32 + m32) * kLdsK + koff]));
+      for (int b = 0; b < 2; ++b) {
+        const uint4 q = cur.b[b][s >> 2];
+        const uint32_t w = (s & 3) == 0 ? q.x : (s & 3) == 1 ? q.y : (s & 3) == 2 ? q.z : q.w;
+        B[b] = dequant_word(w, zz[b], s2[b], magic);
+      }
+    };
+    half8 A0[4], B0[2], A1[4], B1[2];
+    load_frags(0, A0, B0);
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-        B[b] = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(&Bs[(wn * 64 + b * 32 + m32) * kLdsK + koff]));
+    for (int s = 0; s < kBK / 16; s += 2) {
+      load_frags(s + 1, A1, B1);
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+      for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[a], B[b], acc[a][b], 0, 0, 0);
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A0[a], B0[b], acc[a][b], 0, 0, 0);
+      if (s + 2 < kBK / 16) load_frags(s + 2, A0, B0);
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A1[a], B1[b], acc[a][b], 0, 0, 0);
+      // issue pattern for the 16 MFMAs above: each MFMA followed by a share of the next
+      // step's LDS reads and dequant VALU work, so the matrix pipe never waits for them
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);  // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);  // 1 LDS read
+        __builtin_amdgcn_sched_group_barrier(0x0002, 4, 0);  // 4 VALU
+      }
     }
+    if (step + 1 < nsteps) store_a(nxt, buf ^ 1);
     __syncthreads();
+  };
+
+  int64_t step = 0;
+  for (; step + 3 <= nsteps; step += 3) {  // straight-line triples: one path through the loop
+    body(S0, S1, S2, step);
+    body(S1, S2, S0, step + 1);
+    body(S2, S0, S1, step + 2);
   }
+  if (step < nsteps) body(S0, S1, S2, step);
+  if (step + 1 < nsteps) body(S1, S2, S0, step + 1);
 
   // ------------------------------------------------------------------ epilogue
   // 32x32 accumulator layout: element e of lane l is (row 8(e/4) + 4(l/32) + e%4, col l%32).
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 2; ++b) {
+      const int64_t col = n0 + wave * 64 + b * 32 + m32;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int64_t row = m0 + wm * 64 + a * 32 + 8 * (e >> 2) + 4 * khalf + (e & 3);
-        const int64_t col = n0 + wn * 64 + b * 32 + m32;
+        const int64_t row = m0 + a * 32 + 8 * (e >> 2) + 4 * kh + (e & 3);
         if (row < M && col < N) Y[row * N + col] = f2h_bits(acc[a][b][e]);
       }
+    }
 }
 
 hipError_t launch_gemm(const uint16_t* X, int64_t M, const uint32_t* qweight,
                        const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
                        uint16_t* Y, hipStream_t stream) {
-  dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM));
-  hipLaunchKernelGGL(k_gemm, grid, dim3(256), 0, stream, X, M, qweight, scales, zeros, N, K, Y);
+  const int64_t mt = (M + kBM - 1) / kBM;
+  const int64_t nt = (N + kBN - 1) / kBN;
+  const int64_t per_xcd = (mt * nt + kXcds - 1) / kXcds;
+  hipLaunchKernelGGL(k_gemm, dim3((unsigned)(per_xcd * kXcds)), dim3(256), 0, stream, X, M,
+                     qweight, scales, zeros, N, K, Y, mt, nt, per_xcd);
   return hipGetLastError();
 }
 

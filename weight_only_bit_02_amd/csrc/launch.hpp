@@ -27,9 +27,11 @@ hipError_t launch_scalegen(const double* act, int64_t K, int n_grid, uint16_t* s
 // a5: per (alpha, row tile, token chunk) partial sums of the squared output error.
 int search_row_tile();
 int search_token_chunk(int64_t T);
+// rowmax [N] and srange [n_grid] are scratch (per-row max |W|, per-grid-point max s / min s).
 hipError_t launch_search_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N,
-                             int64_t K, const uint16_t* s_grid, int n_grid, double* partials,
-                             uint32_t* flags, hipStream_t stream);
+                             int64_t K, const uint16_t* s_grid, int n_grid, float* rowmax,
+                             float* srange, double* partials, uint32_t* flags,
+                             hipStream_t stream);
 // a6: fixed-order sums of the partials, first-minimum argmin, s_best copy.
 hipError_t launch_search_reduce(const double* partials, int n_grid, int64_t n_partials,
                                 const uint16_t* s_grid, int64_t K, uint16_t* s_best,

@@ -28,154 +28,209 @@ namespace awq {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kRowTile = 64;         // rows of W per block
+constexpr int kRowTile = 128;        // rows of W per block
 constexpr int kTokPerWave = 64;      // tokens per wave (2 MFMA row tiles)
 constexpr int kLdsStride = 128 + 8;  // halves per LDS row (16-byte pad against bank conflicts)
+constexpr int kXcds = 8;
+
+// Per-row power-of-two scale of D. For every channel k of row n,
+//   |D_nk| = |w'_nk - deq_nk| / s_k <= (max|w'| + 15 sc_h) / s_k
+//          <= 3.01 * max_k |W_nk| * (max_k s_k / min_k s_k),
+// so P_n = 2^(14 - e) with that bound in [2^(e-1), 2^e) keeps |D P| < 2^14 and the fp16
+// hi part finite; hi + lo then carries 22 significant bits of D P.
+__device__ __forceinline__ float row_scale(float rowmax, float srange) {
+  const float bound = 3.01f * rowmax * srange;
+  int ex = 0;
+  (void)__builtin_frexpf(bound, &ex);
+  if (!(bound > 0.0f) || !__builtin_isfinite(bound)) ex = 0;
+  ex = ex < -100 ? -100 : (ex > 100 ? 100 : ex);
+  return __builtin_ldexpf(1.0f, 14 - ex);
+}
+
+// max |W| per row (fp16 magnitudes compared as integers: order-free, exact).
+__global__ void __launch_bounds__(256) k_row_absmax(const uint16_t* __restrict__ W, int64_t N,
+                                                    int64_t K, float* __restrict__ rowmax) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  if (row >= N) return;
+  uint32_t m = 0;
+  for (int64_t c = lane; c < K / 8; c += 64) {
+    const uint4 v = *reinterpret_cast<const uint4*>(W + row * K + c * 8);
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      m = max(m, d[i] & 0x7FFFu);
+      m = max(m, (d[i] >> 16) & 0x7FFFu);
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+  if (lane == 0) rowmax[row] = m >= 0x7C00u ? __builtin_inff() : h2f((uint16_t)m);
+}
+
+// max s / min s of every grid point (one block per grid point; min/max are order-free).
+__global__ void __launch_bounds__(256) k_scale_range(const uint16_t* __restrict__ s_grid, int64_t K,
+                                                     float* __restrict__ srange,
+                                                     uint32_t* __restrict__ flags) {
+  __shared__ float lmin[256], lmax[256];
+  const uint16_t* s = s_grid + (int64_t)blockIdx.x * K;
+  float mn = __builtin_inff(), mx = 0.0f;
+  for (int64_t k = threadIdx.x; k < K; k += 256) {
+    const float v = h2f(s[k]);
+    mn = fminf(mn, v);
+    mx = fmaxf(mx, v);
+  }
+  lmin[threadIdx.x] = mn;
+  lmax[threadIdx.x] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int i = 1; i < 256; ++i) {
+      mn = fminf(mn, lmin[i]);
+      mx = fmaxf(mx, lmax[i]);
+    }
+    const float r = mx / mn;
+    srange[blockIdx.x] = r;
+    // beyond 2^10 the per-row scale leaves fewer than 12 of the 22 bits for small terms
+    if (!(r <= 1024.0f) && flags) atomicOr(flags, AWQ_FLAG_SEARCH_RANGE);
+  }
+}
 
 template <int NW>
 __global__ void __launch_bounds__(NW * 64)
-    k_search_err(const uint16_t* __restrict__ X, int64_t T, const uint16_t* __restrict__ W,
-                 int64_t N, int64_t K, const uint16_t* __restrict__ s_grid,
-                 double* __restrict__ partials, uint32_t* __restrict__ flags) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds_hi[kRowTile * kLdsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_lo[kRowTile * kLdsStride];
-  __shared__ float lds_pinv[kRowTile];
+    k_search_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N, int64_t K,
+                 const uint16_t* s_grid, int n_grid, const float* rowmax, const float* srange,
+                 double* __restrict__ partials, uint32_t* __restrict__ flags, int64_t n_ntiles,
+                 int64_t per_xcd) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds_hi[2][kRowTile * kLdsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_lo[2][kRowTile * kLdsStride];
+  __shared__ float lds_p[kRowTile];
   __shared__ double lds_red[NW];
+
+  // XCD-aware order: consecutive blocks of one XCD share a row tile (different grid
+  // points), so the tile of W is read from HBM once per XCD.
+  const int64_t t = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (t >= n_ntiles * n_grid) return;
+  const int64_t ntile = t / n_grid;
+  const int alpha = (int)(t % n_grid);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int64_t ntile = blockIdx.x;
-  const int alpha = blockIdx.y;
   const int64_t n0 = ntile * kRowTile;
   const int64_t G = K / kGroup;
   const uint16_t* s = s_grid + (int64_t)alpha * K;
   const int64_t tchunk = (int64_t)NW * kTokPerWave;
   const int64_t n_tchunks = (T + tchunk - 1) / tchunk;
-  const int64_t n_ntiles = gridDim.x;
 
-  // quantize-phase mapping
   constexpr int kRowsPerPass = NW * 4;
   constexpr int kPasses = kRowTile / kRowsPerPass;
   const int q_row = tid >> 4;
   const int li = tid & 15;
-
-  // contract-phase mapping (32x32x16 operands: row/col = lane % 32, k-half = lane / 32)
   const int m32 = lane & 31;
   const int khalf = lane >> 5;
 
+  const float sr = srange[alpha];
+  for (int r = tid; r < kRowTile; r += NW * 64)
+    lds_p[r] = row_scale(n0 + r < N ? rowmax[n0 + r] : 0.0f, sr);
+  __syncthreads();
+
   bool bad = false;
+  // quantize group j of the tile into LDS buffer `buf` as (D P) split into fp16 hi + lo
+  auto quantize = [&](int64_t j, int buf) {
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+      const int r = p * kRowsPerPass + q_row;
+      const int64_t n = n0 + r;
+      const int64_t k0 = j * kGroup + li * 8;
+      const int64_t nc = n < N ? n : N - 1;
+      uint4 wv = *reinterpret_cast<const uint4*>(W + nc * K + k0);
+      if (n >= N) wv = make_uint4(0, 0, 0, 0);
+      const uint4 sv = *reinterpret_cast<const uint4*>(s + k0);
+      const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
+      const uint32_t sd[4] = {sv.x, sv.y, sv.z, sv.w};
+      float wf[8], wp[8], rs[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        wf[2 * i] = h2f((uint16_t)(wd[i] & 0xFFFF));
+        wf[2 * i + 1] = h2f((uint16_t)(wd[i] >> 16));
+        const float s0 = h2f((uint16_t)(sd[i] & 0xFFFF)), s1 = h2f((uint16_t)(sd[i] >> 16));
+        wp[2 * i] = wf[2 * i] * s0;
+        wp[2 * i + 1] = wf[2 * i + 1] * s1;
+        rs[2 * i] = __builtin_amdgcn_rcpf(s0);
+        rs[2 * i + 1] = __builtin_amdgcn_rcpf(s1);
+      }
+      float mn = wp[0], mx = wp[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) {
+        mn = fminf(mn, wp[i]);
+        mx = fmaxf(mx, wp[i]);
+      }
+      row16_minmax(mn, mx);
+      const GroupQ g = group_params(mn, mx);
+      const float P = lds_p[r];
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint16_t h2[2], l2[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int c = 2 * i + e;
+          const float q = quant_code(wp[c], g);
+          const float deq = (q - g.z) * g.scf;  // exact: small integer times an fp16
+          const float d = (wf[c] - deq * rs[c]) * P;
+          h2[e] = f2h_bits(d);
+          l2[e] = f2h_bits(d - h2f(h2[e]));
+        }
+        hi[i] = (uint32_t)h2[0] | ((uint32_t)h2[1] << 16);
+        lo[i] = (uint32_t)l2[0] | ((uint32_t)l2[1] << 16);
+      }
+      bad |= !__builtin_isfinite(mn) || !__builtin_isfinite(mx);
+      *reinterpret_cast<uint4*>(&lds_hi[buf][r * kLdsStride + li * 8]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      *reinterpret_cast<uint4*>(&lds_lo[buf][r * kLdsStride + li * 8]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    }
+  };
+
   for (int64_t tc = 0; tc < n_tchunks; ++tc) {
     const int64_t tw = tc * tchunk + (int64_t)wave * kTokPerWave;
     const bool active = tw < T;
-    f32x16 acc[2][2];
+    f32x16 acc[2][4];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+      for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
 
+    quantize(0, 0);
+    __syncthreads();
     for (int64_t j = 0; j < G; ++j) {
-      // ---------------------------------------------------------------- quantize
-#pragma unroll
-      for (int p = 0; p < kPasses; ++p) {
-        const int r = p * kRowsPerPass + q_row;
-        const int64_t n = n0 + r;
-        const int64_t k0 = j * kGroup + li * 8;
-        uint4 wv = make_uint4(0, 0, 0, 0);
-        if (n < N) wv = *reinterpret_cast<const uint4*>(W + n * K + k0);
-        const uint4 sv = *reinterpret_cast<const uint4*>(s + k0);
-        const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
-        const uint32_t sd[4] = {sv.x, sv.y, sv.z, sv.w};
-        float wf[8], sf[8], wp[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          wf[2 * i] = h2f((uint16_t)(wd[i] & 0xFFFF));
-          wf[2 * i + 1] = h2f((uint16_t)(wd[i] >> 16));
-          sf[2 * i] = h2f((uint16_t)(sd[i] & 0xFFFF));
-          sf[2 * i + 1] = h2f((uint16_t)(sd[i] >> 16));
-        }
-        float mn, mx, rsmax = 0.0f;
-        float rs[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          wp[i] = wf[i] * sf[i];
-          rs[i] = __builtin_amdgcn_rcpf(sf[i]);
-          bad |= !__builtin_isfinite(wp[i]);
-          mn = i ? fminf(mn, wp[i]) : wp[i];
-          mx = i ? fmaxf(mx, wp[i]) : wp[i];
-          rsmax = fmaxf(rsmax, rs[i]);
-        }
-        float dummy = -rsmax;
-        row16_minmax(mn, mx);
-        row16_minmax(dummy, rsmax);
-        const GroupQ g = group_params(mn, mx);
-        // |w' - deq| <= max|w'| + 15 sc_h, so |D| <= that / min s.
-        const float bound = (fmaxf(__builtin_fabsf(mx), __builtin_fabsf(mn)) + 15.0f * g.scf) * rsmax;
-        int ex = 0;
-        (void)__builtin_frexpf(bound, &ex);
-        ex = ex < -100 ? -100 : (ex > 100 ? 100 : ex);
-        const float P = __builtin_ldexpf(1.0f, 14 - ex);
-        uint32_t hi[4], lo[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          uint16_t h2[2], l2[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int c = 2 * i + e;
-            const float q = quant_code(wp[c], g);
-            const float deq = (q - g.z) * g.scf;  // exact: small integer times an fp16
-            const float d = (wf[c] - deq * rs[c]) * P;
-            h2[e] = f2h_bits(d);
-            l2[e] = f2h_bits(d - h2f(h2[e]));
-          }
-          hi[i] = (uint32_t)h2[0] | ((uint32_t)h2[1] << 16);
-          lo[i] = (uint32_t)l2[0] | ((uint32_t)l2[1] << 16);
-        }
-        *reinterpret_cast<uint4*>(&lds_hi[r * kLdsStride + li * 8]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-        *reinterpret_cast<uint4*>(&lds_lo[r * kLdsStride + li * 8]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-        if (li == 0) lds_pinv[r] = __builtin_ldexpf(1.0f, ex - 14);
-      }
-      __syncthreads();
-
-      // ---------------------------------------------------------------- contract
+      const int buf = (int)(j & 1);
+      // next group's quantization (unconditional, clamped: the last one is redundant and
+      // lands in the buffer nobody reads) overlaps this group's MFMAs
+      quantize(j + 1 < G ? j + 1 : G - 1, buf ^ 1);
       if (active) {
-        f32x16 tmp[2][2];
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-          for (int b = 0; b < 2; ++b) tmp[a][b] = f32x16{};
 #pragma unroll 2
         for (int st = 0; st < kGroup / 16; ++st) {
           const int koff = st * 16 + khalf * 8;
-          half8 A[2], Bh[2], Bl[2];
+          half8 A[2], Bh[4], Bl[4];
 #pragma unroll
           for (int a = 0; a < 2; ++a) {
-            const int64_t t = tw + a * 32 + m32;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (t < T) v = *reinterpret_cast<const uint4*>(X + t * K + j * kGroup + koff);
+            const int64_t tt = tw + a * 32 + m32;
+            uint4 v = *reinterpret_cast<const uint4*>(X + (tt < T ? tt : T - 1) * K + j * kGroup + koff);
+            if (tt >= T) v = make_uint4(0, 0, 0, 0);
             A[a] = __builtin_bit_cast(half8, v);
           }
 #pragma unroll
-          for (int b = 0; b < 2; ++b) {
+          for (int b = 0; b < 4; ++b) {
             const int r = b * 32 + m32;
-            Bh[b] = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(&lds_hi[r * kLdsStride + koff]));
-            Bl[b] = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(&lds_lo[r * kLdsStride + koff]));
+            Bh[b] = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(&lds_hi[buf][r * kLdsStride + koff]));
+            Bl[b] = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(&lds_lo[buf][r * kLdsStride + koff]));
           }
 #pragma unroll
           for (int a = 0; a < 2; ++a)
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
-              tmp[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[a], Bh[b], tmp[a][b], 0, 0, 0);
-              tmp[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[a], Bl[b], tmp[a][b], 0, 0, 0);
+            for (int b = 0; b < 4; ++b) {
+              acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[a], Bh[b], acc[a][b], 0, 0, 0);
+              acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[a], Bl[b], acc[a][b], 0, 0, 0);
             }
-        }
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const float pv = lds_pinv[b * 32 + m32];  // output column = lane % 32
-#pragma unroll
-          for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[a][b][e] += tmp[a][b][e] * pv;
         }
       }
       __syncthreads();
@@ -184,11 +239,16 @@ __global__ void __launch_bounds__(NW * 64)
     // ------------------------------------------------------------------ sum of squares
     double ss = 0.0;
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int b = 0; b < 4; ++b) {
+      const double pinv = 1.0 / (double)lds_p[b * 32 + m32];  // output column = lane % 32
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) ss += (double)acc[a][b][e] * (double)acc[a][b][e];
+        for (int e = 0; e < 16; ++e) {
+          const double v = (double)acc[a][b][e] * pinv;
+          ss += v * v;
+        }
+    }
     ss = wave_sum(ss);
     if (lane == 0) lds_red[wave] = ss;
     __syncthreads();
@@ -234,15 +294,24 @@ int search_row_tile() { return kRowTile; }
 int search_token_chunk(int64_t T) { return T <= 4 * kTokPerWave ? 4 * kTokPerWave : 8 * kTokPerWave; }
 
 hipError_t launch_search_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N,
-                             int64_t K, const uint16_t* s_grid, int n_grid, double* partials,
-                             uint32_t* flags, hipStream_t stream) {
-  dim3 grid((unsigned)((N + kRowTile - 1) / kRowTile), (unsigned)n_grid);
+                             int64_t K, const uint16_t* s_grid, int n_grid, float* rowmax,
+                             float* srange, double* partials, uint32_t* flags,
+                             hipStream_t stream) {
+  hipLaunchKernelGGL(k_row_absmax, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, stream, W, N, K, rowmax);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_scale_range, dim3((unsigned)n_grid), dim3(256), 0, stream, s_grid, K, srange, flags);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n_ntiles = (N + kRowTile - 1) / kRowTile;
+  const int64_t per_xcd = (n_ntiles * n_grid + kXcds - 1) / kXcds;
+  const dim3 grid((unsigned)(per_xcd * kXcds));
   if (T <= 4 * kTokPerWave)
-    hipLaunchKernelGGL(k_search_err<4>, grid, dim3(256), 0, stream, X, T, W, N, K, s_grid,
-                       partials, flags);
+    hipLaunchKernelGGL(k_search_err<4>, grid, dim3(256), 0, stream, X, T, W, N, K, s_grid, n_grid,
+                       rowmax, srange, partials, flags, n_ntiles, per_xcd);
   else
-    hipLaunchKernelGGL(k_search_err<8>, grid, dim3(512), 0, stream, X, T, W, N, K, s_grid,
-                       partials, flags);
+    hipLaunchKernelGGL(k_search_err<8>, grid, dim3(512), 0, stream, X, T, W, N, K, s_grid, n_grid,
+                       rowmax, srange, partials, flags, n_ntiles, per_xcd);
   return hipGetLastError();
 }
 
