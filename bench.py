@@ -7,11 +7,13 @@ channels x20, group 128, 4-bit + zero point):
   1. scale search (statistic, 20-point alpha grid, error, argmin) for the four
      shared-input groups q|k|v [12288x4096], o [4096x4096], gate|up [22016x4096],
      down [4096x11008], calibration X = 512 tokens;
-  2. quantize + pack of the seven matrices with the chosen scales;
-  3. decode GEMV at M = 1 over 32 layer copies of the seven matrices (one token through
-     the 32 decoder layers of a 7B model: 3.37 GB of packed weights, far above the
-     256 MB last-level cache, so every launch streams from HBM);
-  4. prefill MFMA dequant-GEMM at M = 2048 over the seven matrices.
+  2. quantize + pack of the four groups with their chosen scales (the seven matrices);
+  3. decode GEMV at M = 1 over 32 layer copies (one token through the 32 decoder layers
+     of a 7B model: 3.37 GB of packed weights, far above the 256 MB last-level cache, so
+     every launch streams from HBM), with q|k|v and gate|up launched as one GEMV each
+     (they share their input; the fused-module decode of the pages); the same sweep
+     with one launch per matrix is timed and reported beside it;
+  4. prefill MFMA dequant-GEMM at M = 2048 over the four groups.
 Inputs are resident in HBM before the timed region. Each part is captured once in a
 HIP graph (so host launch overhead is not kernel time) and replayed; HIP events on
 the launch stream time each part. The headline value is the GEMV bandwidth; the GEMM
@@ -125,6 +127,9 @@ def main():
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
 
     # ------------------------------------------------------------------ inputs (untimed)
+    # The linears sharing an input are one search group and one packed tensor (q|k|v and
+    # gate|up concatenated along N); a single matrix is a row slice of its group's
+    # packed tensor (the format is row-major per output channel).
     log("bench: generating inputs")
     Wg = {g: si.torch_weights(N, K, 100 + i, dev) for i, (g, (N, K)) in enumerate(SEARCH_GROUPS.items())}
     Xcal = {g: si.torch_activations(CALIB_T, K, 200 + i, dev, channel_offset=K)
@@ -135,41 +140,52 @@ def main():
                                 torch.empty(20, dtype=torch.float64, device=dev),
                                 torch.empty((20, K), dtype=torch.float16, device=dev))
             for g, (N, K) in SEARCH_GROUPS.items()}
-    Wm = {name: Wg[g][off:off + N] for name, g, off, N, K in MATRICES}
-    packed = [{name: awq.alloc_packed(N, K, dev) for name, _, _, N, K in MATRICES} for _ in range(args.layers)]
+    packed = [{g: awq.alloc_packed(N, K, dev) for g, (N, K) in SEARCH_GROUPS.items()} for _ in range(args.layers)]
+
+    def row_slice(p, off, n):
+        return awq.PackedLinear(p.qweight[off:off + n], p.scales[off:off + n], p.zeros[off:off + n], n, p.K)
+
+    views = [{name: row_slice(packed[c][g], off, N) for name, g, off, N, K in MATRICES} for c in range(args.layers)]
     log(f"bench: packing {args.layers} layer copies")
     for c in range(1, args.layers):
-        for i, (name, _, _, N, K) in enumerate(MATRICES):
+        for i, (g, (N, K)) in enumerate(SEARCH_GROUPS.items()):
             w = si.torch_weights(N, K, 1000 + 7 * c + i, dev)
-            awq.quantize_pack(w, out=packed[c][name])
+            awq.quantize_pack(w, out=packed[c][g])
             del w
     xdec = {4096: si.torch_activations(1, 4096, 300, dev, channel_offset=4096),
             11008: si.torch_activations(1, 11008, 301, dev, channel_offset=11008)}
     ydec = {name: torch.empty((1, N), dtype=torch.float16, device=dev) for name, _, _, N, K in MATRICES}
+    yfus = {g: torch.empty((1, N), dtype=torch.float16, device=dev) for g, (N, K) in SEARCH_GROUPS.items()}
     xpre = {4096: si.torch_activations(PREFILL_M, 4096, 400, dev, channel_offset=4096),
             11008: si.torch_activations(PREFILL_M, 11008, 401, dev, channel_offset=11008)}
-    ypre = {name: torch.empty((PREFILL_M, N), dtype=torch.float16, device=dev) for name, _, _, N, K in MATRICES}
+    ypre = {g: torch.empty((PREFILL_M, N), dtype=torch.float16, device=dev) for g, (N, K) in SEARCH_GROUPS.items()}
     torch.cuda.synchronize()
 
-    # ------------------------------------------------------------------ the four parts
+    # ------------------------------------------------------------------ the parts
     def part_search():
         for g in SEARCH_GROUPS:
             awq.search_scales(Xcal[g], Wg[g], workspace=ws[g], out=sres[g])
 
     def part_pack():
-        for name, g, _, _, _ in MATRICES:
-            awq.quantize_pack(Wm[name], sres[g].s_best, out=packed[0][name])
+        for g in SEARCH_GROUPS:
+            awq.quantize_pack(Wg[g], sres[g].s_best, out=packed[0][g])
 
-    def part_gemv():
+    def part_gemv():  # decode: q|k|v and gate|up as one launch each (shared input)
+        for c in range(args.layers):
+            for g, (N, K) in SEARCH_GROUPS.items():
+                awq.linear_w4a16(xdec[K], packed[c][g], out=yfus[g])
+
+    def part_gemv_unfused():  # decode: one launch per matrix
         for c in range(args.layers):
             for name, _, _, N, K in MATRICES:
-                awq.linear_w4a16(xdec[K], packed[c][name], out=ydec[name])
+                awq.linear_w4a16(xdec[K], views[c][name], out=ydec[name])
 
     def part_gemm():
-        for name, _, _, N, K in MATRICES:
-            awq.linear_w4a16(xpre[K], packed[0][name], out=ypre[name])
+        for g, (N, K) in SEARCH_GROUPS.items():
+            awq.linear_w4a16(xpre[K], packed[0][g], out=ypre[g])
 
-    parts = [("search", part_search), ("quant_pack", part_pack), ("gemv", part_gemv), ("gemm", part_gemm)]
+    parts = [("search", part_search), ("quant_pack", part_pack), ("gemv", part_gemv),
+             ("gemv_unfused", part_gemv_unfused), ("gemm", part_gemm)]
     stream = torch.cuda.Stream()
     runners = {}
     with torch.cuda.stream(stream):
@@ -177,7 +193,8 @@ def main():
             fn()
         torch.cuda.synchronize()
         eager_ref = {"best": {g: sres[g].best_idx.clone() for g in SEARCH_GROUPS},
-                     "y": {n: ydec[n].clone() for n in ydec}, "Y": {n: ypre[n].clone() for n in ypre}}
+                     "y": {n: ydec[n].clone() for n in ydec}, "yf": {g: yfus[g].clone() for g in yfus},
+                     "Y": {g: ypre[g].clone() for g in ypre}}
         for pname, fn in parts:
             if args.no_graph:
                 runners[pname] = fn
@@ -214,19 +231,23 @@ def main():
         # graph replays must reproduce the eager results bit for bit
         for g in SEARCH_GROUPS:
             assert torch.equal(sres[g].best_idx, eager_ref["best"][g]), "graph replay differs (search)"
+            assert torch.equal(yfus[g], eager_ref["yf"][g]), "graph replay differs (gemv)"
+            assert torch.equal(ypre[g], eager_ref["Y"][g]), "graph replay differs (gemm)"
         for n in ydec:
-            assert torch.equal(ydec[n], eager_ref["y"][n]), "graph replay differs (gemv)"
-            assert torch.equal(ypre[n], eager_ref["Y"][n]), "graph replay differs (gemm)"
+            assert torch.equal(ydec[n], eager_ref["y"][n]), "graph replay differs (gemv, per matrix)"
 
     # ------------------------------------------------------------------ figures
-    n_gemv = args.layers * len(MATRICES)
-    gemv_bytes = args.layers * sum(linear_bytes(1, N, K) for _, _, _, N, K in MATRICES)
+    n_gemv = args.layers * len(SEARCH_GROUPS)
+    gemv_bytes = args.layers * sum(linear_bytes(1, N, K) for N, K in SEARCH_GROUPS.values())
     gemv_gbs = gemv_bytes / (part_ms["gemv"] * 1e-3) / 1e9
-    gemm_flops = sum(2 * PREFILL_M * N * K for _, _, _, N, K in MATRICES)
+    n_gemv_u = args.layers * len(MATRICES)
+    gemv_bytes_u = args.layers * sum(linear_bytes(1, N, K) for _, _, _, N, K in MATRICES)
+    gemv_gbs_u = gemv_bytes_u / (part_ms["gemv_unfused"] * 1e-3) / 1e9
+    gemm_flops = sum(2 * PREFILL_M * N * K for N, K in SEARCH_GROUPS.values())
     gemm_tflops = gemm_flops / (part_ms["gemm"] * 1e-3) / 1e12
     search_flops = sum(2 * CALIB_T * N * K * 20 for N, K in SEARCH_GROUPS.values())
     search_tflops = search_flops / (part_ms["search"] * 1e-3) / 1e12
-    pack_bytes = sum(N * K * 2 + packed_bytes(N, K) for _, _, _, N, K in MATRICES)
+    pack_bytes = sum(N * K * 2 + packed_bytes(N, K) for N, K in SEARCH_GROUPS.values())
     pack_gbs = pack_bytes / (part_ms["quant_pack"] * 1e-3) / 1e9
     best = {g: int(sres[g].best_idx.item()) for g in SEARCH_GROUPS}
 
@@ -244,15 +265,17 @@ def main():
         "vs_baseline": None,
         "dtype": "f16 (int4 weights, fp32 accumulate)",
         "data": "synthetic (seeded; W ~ N(0,0.02^2), X ~ N(0,1) with 1% channels x20)",
-        "config": {"workload": "Llama-2-7B decoder-layer linears: decode GEMV M=1 over "
-                               f"{args.layers} layer copies; prefill GEMM M={PREFILL_M}; "
-                               f"scale search T={CALIB_T}, 20 alpha, group 128; quantize+pack",
+        "config": {"workload": "Llama-2-7B decoder-layer linears (q,k,v,o 4096x4096; gate,up 11008x4096; "
+                               "down 4096x11008): decode GEMV M=1 over "
+                               f"{args.layers} layer copies with q|k|v and gate|up launched together; "
+                               f"prefill GEMM M={PREFILL_M}; scale search T={CALIB_T}, 20 alpha, group 128; "
+                               "quantize+pack",
                    "gemv_launches_per_step": n_gemv, "group_size": GROUP, "w_bit": 4,
                    "graphs": not args.no_graph},
         "roofline": {"bound": "hbm", "achieved": round(gemv_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gemv_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "k_gemv<1,4> (M=1)",
+                     "kernel": "k_gemv1 (M=1)",
                      "avg_launch_us": round(part_ms["gemv"] * 1e3 / n_gemv, 3),
                      "algorithmic_bytes_per_launch": round(gemv_bytes / n_gemv)},
         "gemm": {"tflops": round(gemm_tflops, 2), "ms": round(part_ms["gemm"], 4),
@@ -268,6 +291,9 @@ def main():
                        "roofline": {"bound": "hbm", "achieved": round(pack_gbs, 2), "peak": HBM_PEAK_GBS,
                                     "unit": "GB/s", "frac": round(pack_gbs / HBM_PEAK_GBS, 4)}},
         "gemv_ms": round(part_ms["gemv"], 4),
+        "gemv_per_matrix": {"gbs": round(gemv_gbs_u, 2), "ms": round(part_ms["gemv_unfused"], 4),
+                            "launches_per_step": n_gemv_u, "frac": round(gemv_gbs_u / HBM_PEAK_GBS, 4),
+                            "avg_launch_us": round(part_ms["gemv_unfused"] * 1e3 / n_gemv_u, 3)},
         "source_hash": source_hash(),
     }
     if not args.no_cpu_baseline:

@@ -187,10 +187,13 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Persistent grid: a few blocks per CU; each wave walks its row groups (R rows, all of K)
-// as a flat list of (row group, batch of U chunks per lane) items and always has the
-// next item's code loads in flight while it multiplies the current one. The block
-// stages the activation row once for all its rows.
+// Each wave owns R rows. The activation loads go out first, then all of the wave's code
+// loads for its rows (U chunks per lane per row, covering all of K when the batch count
+// nb is 1); scheduler barriers keep that order, so the wait for the activations
+// (in-order load counter) leaves the codes in flight, and the LDS-only barrier shares
+// the activation row without waiting for them. For K above 64 * U * 32 the wave walks
+// nb batches with the next batch's loads in flight (unconditional, clamped prefetch, so
+// every path has the same loads outstanding and the waits stay exact).
 template <int R, int U, int XR>
 __global__ void __launch_bounds__(256)
     k_gemv1(const uint16_t* X, const uint32_t* qweight, const uint16_t* scales,
@@ -200,24 +203,14 @@ __global__ void __launch_bounds__(256)
   extern __shared__ uint4 xs[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int64_t wave0 = (int64_t)blockIdx.x * 4 + (tid >> 6);
-  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  const int64_t row0 = ((int64_t)blockIdx.x * 4 + (tid >> 6)) * R;
   const int64_t C = K / 32, G = K / kGroup, zbytes = (G + 1) / 2, words = K / 8;
-  const int64_t nb = (C + 64 * U - 1) / (64 * U);  // batches per row group
-  const int64_t ngroups = (N + R - 1) / R;
-  const int64_t my_groups = wave0 < ngroups ? (ngroups - wave0 + nwaves - 1) / nwaves : 0;
-  const int64_t items = my_groups * nb;
+  const int64_t nb = (C + 64 * U - 1) / (64 * U);
   __builtin_assume(nb >= 1);
-
-  auto rows_of = [&](int64_t item, int64_t (&rows)[R]) {
-    const int64_t g = wave0 + (item / nb) * nwaves;
+  int64_t rows[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) rows[r] = (g * R + r < N) ? g * R + r : N - 1;
-  };
+  for (int r = 0; r < R; ++r) rows[r] = (row0 + r < N) ? row0 + r : N - 1;
 
-  // Activation loads first, then the first item's code loads; the scheduler barriers
-  // keep that order, so waiting for the activations (in-order load counter) does not
-  // wait for the codes, and the LDS-only barrier leaves the HBM reads in flight.
   uint4 v[XR];
 #pragma unroll
   for (int j = 0; j < XR; ++j) {
@@ -226,9 +219,7 @@ __global__ void __launch_bounds__(256)
   }
   __builtin_amdgcn_sched_barrier(0);
   GemvBatch<R, U> b0, b1;
-  int64_t rows[R];
-  rows_of(0, rows);
-  if (items > 0) gemv1_load(b0, qweight, scales, zeros, rows, C, words, G, zbytes, 0, lane);
+  gemv1_load(b0, qweight, scales, zeros, rows, C, words, G, zbytes, 0, lane);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < XR; ++j) {
@@ -246,58 +237,63 @@ __global__ void __launch_bounds__(256)
   float acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = 0.0f;
-
-  auto finish = [&](int64_t item) {  // after the last batch of a row group
-    if ((item % nb) != nb - 1) return;
-    const int64_t g = wave0 + (item / nb) * nwaves;
+  if (nb == 1) {
+    gemv1_compute(b0, xs, acc, C, 0, lane, magic);
+  } else {
+    for (int64_t b = 0; b < nb; b += 2) {
+      const int64_t b1i = b + 1 < nb ? b + 1 : nb - 1;
+      gemv1_load(b1, qweight, scales, zeros, rows, C, words, G, zbytes, b1i, lane);
+      gemv1_compute(b0, xs, acc, C, b, lane, magic);
+      const int64_t b2i = b + 2 < nb ? b + 2 : nb - 1;
+      gemv1_load(b0, qweight, scales, zeros, rows, C, words, G, zbytes, b2i, lane);
+      if (b + 1 < nb) gemv1_compute(b1, xs, acc, C, b + 1, lane, magic);
+    }
+  }
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float sum = wave_sum(acc[r]);
-      if (lane == 0 && g * R + r < N) Y[g * R + r] = f2h_bits(sum);
-      acc[r] = 0.0f;
-    }
-  };
-
-  for (int64_t t = 0; t < items; t += 2) {
-    if (t + 1 < items) {
-      rows_of(t + 1, rows);
-      gemv1_load(b1, qweight, scales, zeros, rows, C, words, G, zbytes, (t + 1) % nb, lane);
-    }
-    gemv1_compute(b0, xs, acc, C, t % nb, lane, magic);
-    finish(t);
-    if (t + 2 < items) {
-      rows_of(t + 2, rows);
-      gemv1_load(b0, qweight, scales, zeros, rows, C, words, G, zbytes, (t + 2) % nb, lane);
-    }
-    if (t + 1 < items) {
-      gemv1_compute(b1, xs, acc, C, (t + 1) % nb, lane, magic);
-      finish(t + 1);
-    }
+  for (int r = 0; r < R; ++r) {
+    const float sum = wave_sum(acc[r]);
+    if (lane == 0 && row0 + r < N) Y[row0 + r] = f2h_bits(sum);
   }
 }
 
 template <int R, int U, int XR>
 static hipError_t launch_gemv1_x(const uint16_t* X, const uint32_t* qw, const uint16_t* sc,
                                  const uint8_t* z, int64_t N, int64_t K, uint16_t* Y,
-                                 int blocks_per_cu, hipStream_t stream) {
-  const int64_t want = (N + 4 * R - 1) / (4 * R);
-  const int64_t cap = (int64_t)256 * blocks_per_cu;
-  const int64_t blocks = want < cap ? want : cap;
-  hipLaunchKernelGGL((k_gemv1<R, U, XR>), dim3((unsigned)blocks), dim3(256), (size_t)XR * 256 * 16, stream,
-                     X, qw, sc, z, N, K, Y);
+                                 hipStream_t stream) {
+  const int64_t blocks = (N + 4 * R - 1) / (4 * R);
+  hipLaunchKernelGGL((k_gemv1<R, U, XR>), dim3((unsigned)blocks), dim3(256), (size_t)XR * 256 * 16,
+                     stream, X, qw, sc, z, N, K, Y);
   return hipGetLastError();
 }
 
-// K <= 32768 (the activation row fits the 64 KiB of LDS this kernel asks for).
 template <int R, int U>
 static hipError_t launch_gemv1(const uint16_t* X, const uint32_t* qw, const uint16_t* sc,
                                const uint8_t* z, int64_t N, int64_t K, uint16_t* Y,
-                               int blocks_per_cu, hipStream_t stream) {
+                               hipStream_t stream) {
   const int64_t per_thread = (K / 8 + 255) / 256;
-  if (per_thread <= 2) return launch_gemv1_x<R, U, 2>(X, qw, sc, z, N, K, Y, blocks_per_cu, stream);
-  if (per_thread <= 4) return launch_gemv1_x<R, U, 4>(X, qw, sc, z, N, K, Y, blocks_per_cu, stream);
-  if (per_thread <= 8) return launch_gemv1_x<R, U, 8>(X, qw, sc, z, N, K, Y, blocks_per_cu, stream);
-  return launch_gemv1_x<R, U, 16>(X, qw, sc, z, N, K, Y, blocks_per_cu, stream);
+  if (per_thread <= 2) return launch_gemv1_x<R, U, 2>(X, qw, sc, z, N, K, Y, stream);
+  if (per_thread <= 4) return launch_gemv1_x<R, U, 4>(X, qw, sc, z, N, K, Y, stream);
+  if (per_thread <= 8) return launch_gemv1_x<R, U, 8>(X, qw, sc, z, N, K, Y, stream);
+  return launch_gemv1_x<R, U, 16>(X, qw, sc, z, N, K, Y, stream);
+}
+
+// M = 1 dispatch (K <= 32768, so the activation row fits 64 KiB of LDS): one batch of
+// ceil(K / 2048) chunks per lane when that is at most 8, else batches of 4.
+static hipError_t launch_gemv_m1(const uint16_t* X, const uint32_t* qw, const uint16_t* sc,
+                                 const uint8_t* z, int64_t N, int64_t K, uint16_t* Y,
+                                 hipStream_t stream) {
+  const int64_t cpl = (K / 32 + 63) / 64;  // chunks per lane to cover K once
+  switch (cpl) {
+    case 1: return launch_gemv1<2, 1>(X, qw, sc, z, N, K, Y, stream);
+    case 2: return launch_gemv1<2, 2>(X, qw, sc, z, N, K, Y, stream);
+    case 3: return launch_gemv1<2, 3>(X, qw, sc, z, N, K, Y, stream);
+    case 4: return launch_gemv1<2, 4>(X, qw, sc, z, N, K, Y, stream);
+    case 5: return launch_gemv1<2, 5>(X, qw, sc, z, N, K, Y, stream);
+    case 6: return launch_gemv1<2, 6>(X, qw, sc, z, N, K, Y, stream);
+    case 7: return launch_gemv1<1, 7>(X, qw, sc, z, N, K, Y, stream);
+    case 8: return launch_gemv1<1, 8>(X, qw, sc, z, N, K, Y, stream);
+    default: return launch_gemv1<1, 4>(X, qw, sc, z, N, K, Y, stream);
+  }
 }
 
 template <int M>
@@ -317,10 +313,7 @@ hipError_t launch_gemv(const uint16_t* X, int64_t M, const uint32_t* qweight,
                        uint16_t* Y, hipStream_t stream) {
   switch (M) {
     case 1:
-      // Two rows per wave; one chunk batch per lane for K <= 4096, two above (measured best
-      // on the Llama-2 shapes). 16 blocks per CU caps the grid only for very tall matrices.
-      if (K <= 4096) return launch_gemv1<2, 1>(X, qweight, scales, zeros, N, K, Y, 16, stream);
-      if (K <= 32768) return launch_gemv1<2, 2>(X, qweight, scales, zeros, N, K, Y, 16, stream);
+      if (K <= 32768) return launch_gemv_m1(X, qweight, scales, zeros, N, K, Y, stream);
       return launch_gemv_m<1>(X, qweight, scales, zeros, N, K, Y, stream);
     case 2: return launch_gemv_m<2>(X, qweight, scales, zeros, N, K, Y, stream);
     case 3: return launch_gemv_m<3>(X, qweight, scales, zeros, N, K, Y, stream);
