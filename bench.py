@@ -112,6 +112,9 @@ def main():
     ap.add_argument("--layers", type=int, default=DECODE_LAYERS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying graphs")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="first run one plain device copy of BYTES (a known-size kernel for "
+                         "calibrating HBM traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU; --gpus N with N > 1 is not supported "
@@ -125,6 +128,13 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
+    if args.copy_probe:
+        src = torch.empty(args.copy_probe, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ------------------------------------------------------------------ inputs (untimed)
     # The linears sharing an input are one search group and one packed tensor (q|k|v and
