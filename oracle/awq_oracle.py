@@ -32,6 +32,7 @@ design notes of the repository):
 * scale floored at 2^-14, clamped to 65504 (flagged);
 * statistic = plain mean of |x| over all calibration tokens;
 * s = (max(mean|x|, 2^-14))^alpha, alpha_i = i / n_grid, i = 0..n_grid-1, s stored as fp16;
+* packed word: channels 0, 2, 4, 6 in the low nibbles of its bytes, 1, 3, 5, 7 in the high;
 * error = sum of squares of X * D^T with D = W - Q(W diag(s)) diag(1/s), ties -> smallest i.
 
 Every function spells out the steps in order; numpy supplies only elementwise IEEE
@@ -46,7 +47,7 @@ __all__ = [
     "GROUP", "QMAX", "N_GRID", "ACT_FLOOR", "SCALE_FLOOR", "SCALE_MAX",
     "FLAG_NONFINITE_INPUT", "FLAG_SCALE_CLAMPED",
     "activation_mean_abs", "candidate_scales", "quantize_groups", "pack", "unpack",
-    "quantize_pack", "dequantize", "search_errors", "search_scales", "linear_reference",
+    "quantize_pack", "dequantize", "NIBBLE_CHANNEL", "search_errors", "search_scales", "linear_reference",
     "linear_within_tolerance", "fp16_midpoint_distance", "relative_gap", "packed_bytes",
 ]
 
@@ -160,21 +161,28 @@ def quantize_groups(W16: np.ndarray, s16: np.ndarray | None = None) -> dict:
 
 
 # --------------------------------------------------------------------------- a4
+# Channel held by nibble j (bits 4j..4j+3) of a packed word, relative to the word's first
+# channel: the low halves of the word's four bytes hold channels 0, 2, 4, 6 and the high
+# halves 1, 3, 5, 7, so masking bits {4p..4p+3, 16+4p..19+4p} of the word (p = 0..3)
+# yields the adjacent channel pair (2p, 2p+1).
+NIBBLE_CHANNEL = (0, 2, 4, 6, 1, 3, 5, 7)
+
+
 def pack(q: np.ndarray, z: np.ndarray, scale: np.ndarray) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Nibble packing of codes and zero points.
 
-    The pages give no layout ([AWQ-WIKI] only names "platform-aware weight
-    packing"). Reading: qweight uint32 [N][K/8] where nibble j (bits 4j..4j+3) of
-    word w is the code of input channel k = 8 w + j; zeros uint8 [N][ceil(G/2)]
-    where the low nibble holds the even group and the high nibble the odd group;
-    scales fp16 [N][G].
+    The pages give no layout ([AWQ-WIKI] only names "platform-aware weight packing").
+    Reading: qweight uint32 [N][K/8]; word w covers input channels 8w..8w+7 and nibble j
+    (bits 4j..4j+3) holds the code of channel 8w + NIBBLE_CHANNEL[j]; zeros uint8
+    [N][ceil(G/2)] where the low nibble holds the even group and the high nibble the
+    odd group; scales fp16 [N][G].
     """
     q = np.asarray(q, dtype=np.uint8)
     N, K = q.shape
     G = K // GROUP
     qweight = np.zeros((N, K // 8), dtype=np.uint32)
     for j in range(8):
-        qweight |= q[:, j::8].astype(np.uint32) << np.uint32(4 * j)
+        qweight |= q[:, NIBBLE_CHANNEL[j]::8].astype(np.uint32) << np.uint32(4 * j)
     zeros = np.zeros((N, (G + 1) // 2), dtype=np.uint8)
     zeros |= z[:, 0::2].astype(np.uint8)
     zeros[:, : G // 2] |= (z[:, 1::2].astype(np.uint8) << np.uint8(4))
@@ -187,7 +195,7 @@ def unpack(qweight: np.ndarray, scales: np.ndarray, zeros: np.ndarray, K: int):
     G = K // GROUP
     q = np.empty((N, K), dtype=np.uint8)
     for j in range(8):
-        q[:, j::8] = ((qweight >> np.uint32(4 * j)) & np.uint32(0xF)).astype(np.uint8)
+        q[:, NIBBLE_CHANNEL[j]::8] = ((qweight >> np.uint32(4 * j)) & np.uint32(0xF)).astype(np.uint8)
     z = np.empty((N, G), dtype=np.uint8)
     z[:, 0::2] = zeros[:, : (G + 1) // 2] & np.uint8(0xF)
     z[:, 1::2] = zeros[:, : G // 2] >> np.uint8(4)

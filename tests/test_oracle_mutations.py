@@ -61,14 +61,14 @@ def test_unrounded_scale_mutant_caught_on_codes():
     assert not np.array_equal(q, ref["q"]) or not np.array_equal(z, ref["z"])
 
 
-def test_reversed_nibble_order_mutant_caught():
+def test_sequential_nibble_order_mutant_caught():
     q = np.arange(8 * 16, dtype=np.uint8).reshape(1, 128) % 16
     qw, _, _ = oracle.pack(q, np.zeros((1, 1), np.uint8), np.ones((1, 1), np.float16))
     word = 0
-    for j in range(8):                     # mutant: nibble j holds channel 7 - j
-        word |= int(q[0, 7 - j]) << (4 * j)
+    for j in range(8):                     # mutant: nibble j holds channel j
+        word |= int(q[0, j]) << (4 * j)
     assert word != int(qw[0, 0])
-    assert int(qw[0, 0]) == 0x76543210     # hand-derived: nibble j holds channel j
+    assert int(qw[0, 0]) == 0x75316420     # hand-derived: nibbles hold channels 0,2,4,6,1,3,5,7
 
 
 def test_dropped_inverse_scale_mutant_caught():

@@ -237,8 +237,9 @@ def test_one_hot_extracts_dequantized_column():
         X = np.zeros((1, 256), dtype=np.float16)
         X[0, k] = 1.0
         y, bound = oracle.linear_reference(X, qw, sc, zb, 256)
+        nibble = (0, 4, 1, 5, 2, 6, 3, 7)[k % 8]   # channel 8w + (0,2,4,6,1,3,5,7)[j] sits in nibble j
         for n in range(6):
-            code = (int(qw[n, k // 8]) >> (4 * (k % 8))) & 0xF
+            code = (int(qw[n, k // 8]) >> (4 * nibble)) & 0xF
             j = k // 128
             zero = (int(zb[n, j // 2]) >> (4 * (j % 2))) & 0xF
             assert y[0, n] == (code - zero) * float(sc[n, j])
