@@ -82,7 +82,9 @@ typedef enum awq_linear_kernel {
  *     q = clamp(rint(w' / sc_h) + z, 0, 15).
  *   W        fp16 [N][K]          input, K % 128 == 0
  *   s        fp16 [K]             per-input-channel scale; NULL means s = 1 (plain RTN)
- *   qweight  uint32 [N][K/8]      out: nibble j (bits 4j..4j+3) of word w = code of k = 8w + j
+ *   qweight  uint32 [N][K/8]      out: word w holds the codes of k = 8w..8w+7; nibble j (bits
+ *                                 4j..4j+3) holds k = 8w + (0,2,4,6,1,3,5,7)[j], so each byte
+ *                                 holds one channel pair (2p low nibble, 2p+1 high nibble)
  *   scales   fp16 [N][K/128]      out: sc_h
  *   zeros    uint8 [N][ceil(G/2)] out: G = K/128; low nibble = even group, high = odd group
  *   flags    uint32 [1] or NULL   NONFINITE_INPUT, SCALE_CLAMPED

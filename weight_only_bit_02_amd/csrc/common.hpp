@@ -16,6 +16,12 @@ constexpr int kGroup = 128;   // input channels per quantization group
 constexpr int kQMax = 15;     // 4-bit unsigned codes 0..15 with a zero point
 constexpr int kWave = 64;
 
+// Packed word layout: word w covers input channels 8w..8w+7; channel i sits in nibble
+// kNibbleOf[i] (bits 4n..4n+3). Channels 0, 2, 4, 6 fill the low nibbles of the four bytes
+// and 1, 3, 5, 7 the high ones, so (word >> 4p) & 0x000F000F holds the adjacent pair
+// (2p, 2p+1) in its two 16-bit halves.
+__device__ constexpr int kNibbleOf[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+
 __device__ __forceinline__ float h2f(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
 }
@@ -143,6 +149,17 @@ __device__ __forceinline__ int64_t f16_abs_units(uint16_t h) {
   if (e == 31) return -1;
   if (e == 0) return (int64_t)m;
   return (int64_t)(1024 + m) << (e - 1);
+}
+
+// Copy of a loaded vector through VGPRs the optimizer cannot see through. Storing a
+// loaded value straight to LDS can otherwise leave it in a stack slot (scratch memory),
+// whose reload waits, like any vector memory access, for every load still in flight.
+__device__ __forceinline__ uint4 vgpr_copy(uint4 v) {
+  uint4 r;
+  asm volatile("v_mov_b32 %0, %4\n\tv_mov_b32 %1, %5\n\tv_mov_b32 %2, %6\n\tv_mov_b32 %3, %7"
+               : "=v"(r.x), "=v"(r.y), "=v"(r.z), "=v"(r.w)
+               : "v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w));
+  return r;
 }
 
 }  // namespace awq

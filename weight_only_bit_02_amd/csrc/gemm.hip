@@ -6,11 +6,12 @@
 // Block tile 128 (tokens) x 256 (output channels), K step 128 (one group), four waves side by side
 // along N, each owning 128 x 64 = 4 x 2 tiles of v_mfma_f32_32x32x16_f16.
 //   - A (activations) is shared by the four waves: it goes global -> registers -> LDS,
-//     re-paired per 8 channels as (k, k+4) to match the code unpack, double-buffered
+//     double-buffered
 //     with one barrier per K step; loads run two K steps ahead of the MFMAs.
 //   - B (codes) is private to a wave: each lane loads two 16-byte chunks (8 packed words,
 //     64 channels of one output column) straight into registers; word s is the lane's
-//     B operand for the wave's k16 step s. It is widened exactly to (q - z) with the
+//     B operand for the wave's k16 step s. The packed layout puts channel pairs (2p, 2p+1)
+//     in nibbles p and p+4, so one mask per pair widens it, exactly, to (q - z) with the
 //     0x6400 trick and a packed fp16 add, then multiplied by the group scale in fp16
 //     (one rounding), so no LDS round trip and no barrier are needed for B.
 // Within a K step the lane half h = lane / 32 covers channels [64 h, 64 h + 64) and k16
@@ -39,16 +40,7 @@ __device__ __forceinline__ uint32_t gemm_magic() {
   return m;
 }
 
-__device__ __forceinline__ uint4 pair_k_k4(uint4 v) {  // (0,1)(2,3)(4,5)(6,7) -> (0,4)(1,5)(2,6)(3,7)
-  uint4 p;
-  p.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
-  p.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);
-  p.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
-  p.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
-  return p;
-}
-
-// One packed word -> 8 dequantized fp16 channels (q - z) * sc in (k, k+4) pair order.
+// One packed word -> its 8 dequantized fp16 channels (q - z) * sc, in channel order.
 __device__ __forceinline__ half8 dequant_word(uint32_t w, half2v zz, half2v s2, uint32_t magic) {
   half2v d[4];
 #pragma unroll
@@ -127,7 +119,7 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int id = i * 256 + tid;
-      *reinterpret_cast<uint4*>(&As[buf][(id >> 4) * kAStride + a_kc[i] * 8]) = pair_k_k4(st.a[i]);
+      *reinterpret_cast<uint4*>(&As[buf][(id >> 4) * kAStride + a_kc[i] * 8]) = vgpr_copy(st.a[i]);
     }
   };
 

@@ -11,9 +11,10 @@
 // 0x6400 exponent trick ((1024 + q) as fp16), the zero is removed with a packed fp16
 // add (exact: q - z is a small integer), and v_dot2_f32_f16 multiplies two channels
 // at a time into fp32. The group scale multiplies the 32-channel partial once. The
-// word's nibbles come out paired (k, k + 4), so the activations are re-paired the
-// same way with v_perm_b32 (once per chunk, shared by the R rows). Rows finish with
-// a DPP / shuffle reduction across the wave.
+// packed layout puts the channel pair (2p, 2p+1) of a word in nibbles p and p+4, so
+// one mask per pair yields two adjacent channels and the activations are used in
+// their natural order (each 32-bit word of x is one pair). Rows finish with a DPP /
+// shuffle reduction across the wave.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -62,7 +63,7 @@ __global__ void __launch_bounds__(256)
       for (int w = 0; w < 4; ++w)
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          const uint32_t u = ((wd[w] >> (4 * p)) & 0x000F000Fu) | 0x64006400u;  // (1024+q_p, 1024+q_{p+4})
+          const uint32_t u = ((wd[w] >> (4 * p)) & 0x000F000Fu) | 0x64006400u;  // (1024+q_2p, 1024+q_2p+1)
           qz[r][w * 4 + p] = __builtin_bit_cast(half2v, u) + zz;                // exact (q - z)
         }
     }
@@ -72,11 +73,11 @@ __global__ void __launch_bounds__(256)
       half2v xq[16];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const uint4 v = xp[w];  // channels 8w .. 8w+7 as (0,1) (2,3) (4,5) (6,7)
-        xq[w * 4 + 0] = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(v.z, v.x, 0x05040100u));
-        xq[w * 4 + 1] = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(v.z, v.x, 0x07060302u));
-        xq[w * 4 + 2] = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(v.w, v.y, 0x05040100u));
-        xq[w * 4 + 3] = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(v.w, v.y, 0x07060302u));
+        const uint4 v = xp[w];  // channels 8w .. 8w+7 as the pairs (0,1) (2,3) (4,5) (6,7)
+        xq[w * 4 + 0] = __builtin_bit_cast(half2v, v.x);
+        xq[w * 4 + 1] = __builtin_bit_cast(half2v, v.y);
+        xq[w * 4 + 2] = __builtin_bit_cast(half2v, v.z);
+        xq[w * 4 + 3] = __builtin_bit_cast(half2v, v.w);
       }
 #pragma unroll
       for (int r = 0; r < R; ++r) {
@@ -97,8 +98,8 @@ __global__ void __launch_bounds__(256)
     }
 }
 
-// M = 1: the activation row is staged once per block in LDS, already re-paired, so
-// the inner loop reads it with ds_read_b128 and no permutes. A lane's code loads for
+// M = 1: the activation row is staged once per block in LDS, so the inner loop reads
+// it with ds_read_b128 shared by the R rows of a wave. A lane's code loads for
 // U chunks of each of its R rows are issued together, and the next batch is in flight
 // while the current one is multiplied (two register buffers), so a wave keeps
 // R * U * 16 bytes per lane of HBM reads outstanding.
@@ -194,16 +195,16 @@ __device__ __forceinline__ void lds_barrier() {
 // the activation row without waiting for them. For K above 64 * U * 32 the wave walks
 // nb batches with the next batch's loads in flight (unconditional, clamped prefetch, so
 // every path has the same loads outstanding and the waits stay exact).
-template <int R, int U, int XR>
-__global__ void __launch_bounds__(256)
+template <int R, int U, int XR, int WPB>
+__global__ void __launch_bounds__(WPB * 64)
     k_gemv1(const uint16_t* X, const uint32_t* qweight, const uint16_t* scales,
             const uint8_t* zeros, int64_t N, int64_t K, uint16_t* Y) {
   // (no __restrict__: the code loads must stay ordered before the LDS barrier below)
-  // XR * 256 entries (>= K / 8): channels 8i..8i+7 as (0,4) (1,5) (2,6) (3,7)
+  // XR * WPB * 64 entries (>= K / 8): entry i holds channels 8i..8i+7
   extern __shared__ uint4 xs[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int64_t row0 = ((int64_t)blockIdx.x * 4 + (tid >> 6)) * R;
+  const int64_t row0 = ((int64_t)blockIdx.x * WPB + (tid >> 6)) * R;
   const int64_t C = K / 32, G = K / kGroup, zbytes = (G + 1) / 2, words = K / 8;
   const int64_t nb = (C + 64 * U - 1) / (64 * U);
   __builtin_assume(nb >= 1);
@@ -214,7 +215,7 @@ __global__ void __launch_bounds__(256)
   uint4 v[XR];
 #pragma unroll
   for (int j = 0; j < XR; ++j) {
-    const int64_t i = j * 256 + tid;
+    const int64_t i = j * WPB * 64 + tid;
     v[j] = *reinterpret_cast<const uint4*>(X + (i < words ? i : words - 1) * 8);
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -223,13 +224,8 @@ __global__ void __launch_bounds__(256)
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < XR; ++j) {
-    const int64_t i = j * 256 + tid;
-    uint4 p;
-    p.x = __builtin_amdgcn_perm(v[j].z, v[j].x, 0x05040100u);
-    p.y = __builtin_amdgcn_perm(v[j].z, v[j].x, 0x07060302u);
-    p.z = __builtin_amdgcn_perm(v[j].w, v[j].y, 0x05040100u);
-    p.w = __builtin_amdgcn_perm(v[j].w, v[j].y, 0x07060302u);
-    xs[i] = p;  // the LDS row is padded to XR * 256 entries, so no store is predicated
+    const int64_t i = j * WPB * 64 + tid;
+    xs[i] = vgpr_copy(v[j]);  // the LDS row is padded to XR * WPB * 64 entries: no predicate
   }
   lds_barrier();
 
@@ -256,40 +252,126 @@ __global__ void __launch_bounds__(256)
   }
 }
 
-template <int R, int U, int XR>
+template <int R, int U, int XR, int WPB>
 static hipError_t launch_gemv1_x(const uint16_t* X, const uint32_t* qw, const uint16_t* sc,
                                  const uint8_t* z, int64_t N, int64_t K, uint16_t* Y,
                                  hipStream_t stream) {
-  const int64_t blocks = (N + 4 * R - 1) / (4 * R);
-  hipLaunchKernelGGL((k_gemv1<R, U, XR>), dim3((unsigned)blocks), dim3(256), (size_t)XR * 256 * 16,
-                     stream, X, qw, sc, z, N, K, Y);
+  const int64_t blocks = (N + WPB * R - 1) / (WPB * R);
+  hipLaunchKernelGGL((k_gemv1<R, U, XR, WPB>), dim3((unsigned)blocks), dim3(WPB * 64),
+                     (size_t)XR * WPB * 64 * 16, stream, X, qw, sc, z, N, K, Y);
   return hipGetLastError();
 }
 
-template <int R, int U>
+// K <= 32768: the activation row (K / 8 16-byte entries) fits XR * WPB * 64 entries.
+template <int R, int U, int WPB = 4>
 static hipError_t launch_gemv1(const uint16_t* X, const uint32_t* qw, const uint16_t* sc,
                                const uint8_t* z, int64_t N, int64_t K, uint16_t* Y,
                                hipStream_t stream) {
-  const int64_t per_thread = (K / 8 + 255) / 256;
-  if (per_thread <= 2) return launch_gemv1_x<R, U, 2>(X, qw, sc, z, N, K, Y, stream);
-  if (per_thread <= 4) return launch_gemv1_x<R, U, 4>(X, qw, sc, z, N, K, Y, stream);
-  if (per_thread <= 8) return launch_gemv1_x<R, U, 8>(X, qw, sc, z, N, K, Y, stream);
-  return launch_gemv1_x<R, U, 16>(X, qw, sc, z, N, K, Y, stream);
+  const int64_t per_thread = (K / 8 + WPB * 64 - 1) / (WPB * 64);
+  if (per_thread <= 1) return launch_gemv1_x<R, U, 1, WPB>(X, qw, sc, z, N, K, Y, stream);
+  if (per_thread <= 2) return launch_gemv1_x<R, U, 2, WPB>(X, qw, sc, z, N, K, Y, stream);
+  if (per_thread <= 4) return launch_gemv1_x<R, U, 4, WPB>(X, qw, sc, z, N, K, Y, stream);
+  if (per_thread <= 8) return launch_gemv1_x<R, U, 8, WPB>(X, qw, sc, z, N, K, Y, stream);
+  return launch_gemv1_x<R, U, 16, WPB>(X, qw, sc, z, N, K, Y, stream);
 }
 
-// M = 1 dispatch (K <= 32768, so the activation row fits 64 KiB of LDS): one batch of
-// ceil(K / 2048) chunks per lane when that is at most 8, else batches of 4.
+// Persistent variant for tall matrices: a few blocks per CU, each wave walks rows
+// wave0, wave0 + nwaves, ... (one batch of U chunks per lane covers K) and always has
+// the next row's code loads in flight while it multiplies the current one. Prefetches
+// are unconditional (row index clamped to the last row, which then hits in L2), so the
+// waits stay exact; a wave with a single row takes a straight-line path instead.
+template <int U, int XR, int WPB>
+__global__ void __launch_bounds__(WPB * 64)
+    k_gemv1p(const uint16_t* X, const uint32_t* qweight, const uint16_t* scales,
+             const uint8_t* zeros, int64_t N, int64_t K, uint16_t* Y) {
+  extern __shared__ uint4 xs[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int64_t wave0 = (int64_t)blockIdx.x * WPB + (tid >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * WPB;
+  const int64_t C = K / 32, G = K / kGroup, zbytes = (G + 1) / 2, words = K / 8;
+  auto clamp_row = [&](int64_t r) { return r < N ? r : N - 1; };
+
+  uint4 v[XR];
+#pragma unroll
+  for (int j = 0; j < XR; ++j) {
+    const int64_t i = j * WPB * 64 + tid;
+    v[j] = *reinterpret_cast<const uint4*>(X + (i < words ? i : words - 1) * 8);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  GemvBatch<1, U> b0, b1;
+  int64_t rows[1] = {clamp_row(wave0)};
+  gemv1_load(b0, qweight, scales, zeros, rows, C, words, G, zbytes, 0, lane);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < XR; ++j) {
+    const int64_t i = j * WPB * 64 + tid;
+    xs[i] = vgpr_copy(v[j]);
+  }
+  lds_barrier();
+
+  const uint32_t magic = magic_1024x2();
+  auto finish = [&](float (&acc)[1], int64_t row) {
+    const float sum = wave_sum(acc[0]);
+    if (lane == 0 && row < N) Y[row] = f2h_bits(sum);
+  };
+  if (wave0 + nwaves >= N) {  // at most one row for this wave
+    float acc[1] = {0.0f};
+    gemv1_compute(b0, xs, acc, C, 0, lane, magic);
+    finish(acc, wave0);
+    return;
+  }
+  for (int64_t row = wave0; row < N; row += 2 * nwaves) {
+    rows[0] = clamp_row(row + nwaves);
+    gemv1_load(b1, qweight, scales, zeros, rows, C, words, G, zbytes, 0, lane);
+    float acc0[1] = {0.0f};
+    gemv1_compute(b0, xs, acc0, C, 0, lane, magic);
+    finish(acc0, row);
+    rows[0] = clamp_row(row + 2 * nwaves);
+    gemv1_load(b0, qweight, scales, zeros, rows, C, words, G, zbytes, 0, lane);
+    float acc1[1] = {0.0f};
+    gemv1_compute(b1, xs, acc1, C, 0, lane, magic);
+    finish(acc1, row + nwaves);
+  }
+}
+
+template <int U, int XR, int WPB>
+static hipError_t launch_gemv1p_x(const uint16_t* X, const uint32_t* qw, const uint16_t* sc,
+                                  const uint8_t* z, int64_t N, int64_t K, uint16_t* Y,
+                                  int blocks_per_cu, hipStream_t stream) {
+  const int64_t want = (N + WPB - 1) / WPB;
+  const int64_t cap = (int64_t)256 * blocks_per_cu;
+  hipLaunchKernelGGL((k_gemv1p<U, XR, WPB>), dim3((unsigned)(want < cap ? want : cap)),
+                     dim3(WPB * 64), (size_t)XR * WPB * 64 * 16, stream, X, qw, sc, z, N, K, Y);
+  return hipGetLastError();
+}
+
+template <int U, int WPB>
+static hipError_t launch_gemv1p(const uint16_t* X, const uint32_t* qw, const uint16_t* sc,
+                                const uint8_t* z, int64_t N, int64_t K, uint16_t* Y,
+                                int blocks_per_cu, hipStream_t stream) {
+  const int64_t per_thread = (K / 8 + WPB * 64 - 1) / (WPB * 64);
+  if (per_thread <= 1) return launch_gemv1p_x<U, 1, WPB>(X, qw, sc, z, N, K, Y, blocks_per_cu, stream);
+  if (per_thread <= 2) return launch_gemv1p_x<U, 2, WPB>(X, qw, sc, z, N, K, Y, blocks_per_cu, stream);
+  if (per_thread <= 4) return launch_gemv1p_x<U, 4, WPB>(X, qw, sc, z, N, K, Y, blocks_per_cu, stream);
+  if (per_thread <= 8) return launch_gemv1p_x<U, 8, WPB>(X, qw, sc, z, N, K, Y, blocks_per_cu, stream);
+  return launch_gemv1p_x<U, 16, WPB>(X, qw, sc, z, N, K, Y, blocks_per_cu, stream);
+}
+
+// M = 1 dispatch (K <= 32768, so the activation row fits 64 KiB of LDS): one row per
+// wave, four waves per block, one batch of ceil(K / 2048) chunks per lane when that is
+// at most 8 (measured best on the Llama-2 7B/70B shapes), else batches of 4.
 static hipError_t launch_gemv_m1(const uint16_t* X, const uint32_t* qw, const uint16_t* sc,
                                  const uint8_t* z, int64_t N, int64_t K, uint16_t* Y,
                                  hipStream_t stream) {
   const int64_t cpl = (K / 32 + 63) / 64;  // chunks per lane to cover K once
   switch (cpl) {
-    case 1: return launch_gemv1<2, 1>(X, qw, sc, z, N, K, Y, stream);
-    case 2: return launch_gemv1<2, 2>(X, qw, sc, z, N, K, Y, stream);
-    case 3: return launch_gemv1<2, 3>(X, qw, sc, z, N, K, Y, stream);
-    case 4: return launch_gemv1<2, 4>(X, qw, sc, z, N, K, Y, stream);
-    case 5: return launch_gemv1<2, 5>(X, qw, sc, z, N, K, Y, stream);
-    case 6: return launch_gemv1<2, 6>(X, qw, sc, z, N, K, Y, stream);
+    case 1: return launch_gemv1<1, 1>(X, qw, sc, z, N, K, Y, stream);
+    case 2: return launch_gemv1<1, 2>(X, qw, sc, z, N, K, Y, stream);
+    case 3: return launch_gemv1<1, 3>(X, qw, sc, z, N, K, Y, stream);
+    case 4: return launch_gemv1<1, 4>(X, qw, sc, z, N, K, Y, stream);
+    case 5: return launch_gemv1<1, 5>(X, qw, sc, z, N, K, Y, stream);
+    case 6: return launch_gemv1<1, 6>(X, qw, sc, z, N, K, Y, stream);
     case 7: return launch_gemv1<1, 7>(X, qw, sc, z, N, K, Y, stream);
     case 8: return launch_gemv1<1, 8>(X, qw, sc, z, N, K, Y, stream);
     default: return launch_gemv1<1, 4>(X, qw, sc, z, N, K, Y, stream);

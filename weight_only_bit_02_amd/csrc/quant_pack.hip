@@ -6,7 +6,7 @@
 //
 // Mapping: a wave owns one (row, run of 4 groups) unit = 512 input channels. Lane l
 // reads 8 consecutive weights (one 16-byte load) and writes the 32-bit word that packs
-// their 8 codes, so loads and stores are fully coalesced; the 16 lanes of a DPP row
+// their 8 codes (channel i of the word in nibble kNibbleOf[i]), so loads and stores are fully coalesced; the 16 lanes of a DPP row
 // form one group and find its min / max with row-local DPP.
 #include "common.hpp"
 #include "launch.hpp"
@@ -61,7 +61,7 @@ __global__ void __launch_bounds__(256) k_quant_pack(const uint16_t* __restrict__
     const GroupQ g = group_params(mn, mx);
     uint32_t word = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) word |= (uint32_t)quant_code(w[i], g) << (4 * i);
+    for (int i = 0; i < 8; ++i) word |= (uint32_t)quant_code(w[i], g) << (4 * kNibbleOf[i]);
 
     const uint32_t zi = (uint32_t)g.z;
     const uint32_t z_next = (uint32_t)__shfl_down((int)zi, 16);  // zero of group j + 1
