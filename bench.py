@@ -15,8 +15,10 @@ channels x20, group 128, 4-bit + zero point):
      with one launch per matrix is timed and reported beside it;
   4. prefill MFMA dequant-GEMM at M = 2048 over the four groups.
 Inputs are resident in HBM before the timed region. Each part is captured once in a
-HIP graph (so host launch overhead is not kernel time) and replayed; HIP events on
-the launch stream time each part. The headline value is the GEMV bandwidth; the GEMM
+HIP graph (so host launch overhead is not kernel time) and replayed. The K timed steps
+run in phases, part by part (K decode sweeps back to back, then K prefill GEMMs, and so
+on), so each part is measured in the steady state it has in service; HIP events on the
+launch stream bracket each phase. The headline value is the GEMV bandwidth; the GEMM
 rate is reported beside it.
 
 Prints ONE JSON line. `python bench.py --gpus N` with N > 1 exits: this build runs
@@ -215,28 +217,30 @@ def main():
                 runners[pname] = g.replay
         torch.cuda.synchronize()
 
-        def step(evs=None):
-            for i, (pname, _) in enumerate(parts):
-                if evs is not None:
-                    evs[i].record(stream)
-                runners[pname]()
-            if evs is not None:
-                evs[len(parts)].record(stream)
-
+        # Timed in phases: the K steps run part by part (K decode sweeps, then K prefill
+        # GEMMs, ...), each part back to back with itself, as it runs in service (a decode
+        # loop never follows an 11 ms quantization search, after which the VALU-bound decode
+        # kernel runs at a lower clock). Warm-up ends with the decode parts, so the first
+        # timed phase follows its own kind of work. One event pair brackets each phase.
+        order = ["gemv", "gemv_unfused", "gemm", "quant_pack", "search"]
         log(f"bench: warmup {args.warmup} steps")
-        for _ in range(args.warmup):
-            step()
+        for pname in reversed(order):
+            for _ in range(args.warmup):
+                runners[pname]()
         torch.cuda.synchronize()
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in range(args.steps)]
+        ev = {pname: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for pname in order}
         log(f"bench: timing {args.steps} steps")
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for s in range(args.steps):
-            step(ev[s])
+        for pname in order:
+            ev[pname][0].record(stream)
+            for _ in range(args.steps):
+                runners[pname]()
+            ev[pname][1].record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        part_ms = {pname: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps
-                   for i, (pname, _) in enumerate(parts)}
+        part_ms = {pname: ev[pname][0].elapsed_time(ev[pname][1]) / args.steps for pname in order}
 
         # graph replays must reproduce the eager results bit for bit
         for g in SEARCH_GROUPS:
@@ -281,7 +285,7 @@ def main():
                                f"prefill GEMM M={PREFILL_M}; scale search T={CALIB_T}, 20 alpha, group 128; "
                                "quantize+pack",
                    "gemv_launches_per_step": n_gemv, "group_size": GROUP, "w_bit": 4,
-                   "graphs": not args.no_graph},
+                   "graphs": not args.no_graph, "timing": "phased (each part K times back to back)"},
         "roofline": {"bound": "hbm", "achieved": round(gemv_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gemv_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic,

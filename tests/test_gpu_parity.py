@@ -229,8 +229,13 @@ def test_linear_auto_dispatch_and_determinism():
         assert oracle.linear_within_tolerance(a.astype(np.float64), y_ref, bound).all()
 
 
-@pytest.mark.parametrize("N,K", [(4097, 4096), (9000, 1152), (11008, 4096), (4096, 11008)])
-def test_gemv_m1_many_rows_per_wave(N, K):
-    """Enough rows that every wave of the persistent M = 1 grid walks several row groups."""
+@pytest.mark.parametrize("N,K", [
+    (4097, 4096), (9000, 1152), (11008, 4096), (4096, 11008),  # one row per wave
+    (16389, 4096), (16387, 2048),  # tall: two rows per wave, odd N (last row clamped)
+    (129, 18432),                  # more than 8 chunks per lane: batched kernel, 3 batches
+    (65, 33024),                   # activation row beyond 64 KiB of LDS: generic kernel
+])
+def test_gemv_m1_launch_shapes(N, K):
+    """Every M = 1 launch shape of the dispatch, ragged row counts included."""
     p, ref = _packed_case(N, K, off=N + K + 7)
     _check_linear(si.activations(1, K, offset=N), p, ref, "gemv")

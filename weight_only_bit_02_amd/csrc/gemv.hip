@@ -140,6 +140,12 @@ __device__ __forceinline__ uint32_t magic_1024x2() {
   return m;
 }
 
+// Per chunk (4 words = 32 channels) and row: exact (q - z) in fp16, two channels per dot.
+// Pairs p = 0, 2 of a word are masked at bits 0..3 of each half, pairs p = 1, 3 at bits
+// 4..7 (one shift by 8 serves p = 2, 3): with the 0x6400 magic the latter read 1024 + 16 q,
+// and subtracting 1024 + 16 z leaves 16 (q - z), still exact. They accumulate in part1,
+// whose factor 16 is removed at the end; a power-of-two factor commutes with every fp32
+// rounding, so the result is the same as with unscaled codes.
 template <int R, int U>
 __device__ __forceinline__ void gemv1_compute(const GemvBatch<R, U>& bt, const uint4* __restrict__ xs,
                                               float (&acc)[R], int64_t C, int64_t b, int lane,
@@ -151,7 +157,7 @@ __device__ __forceinline__ void gemv1_compute(const GemvBatch<R, U>& bt, const u
       half2v xq[16];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const uint4 v = xs[c * 4 + w];
+        const uint4 v = xs[c * 4 + w];  // channels 8w .. 8w+7 as the pairs (0,1) (2,3) (4,5) (6,7)
         xq[w * 4 + 0] = __builtin_bit_cast(half2v, v.x);
         xq[w * 4 + 1] = __builtin_bit_cast(half2v, v.y);
         xq[w * 4 + 2] = __builtin_bit_cast(half2v, v.z);
@@ -161,20 +167,24 @@ __device__ __forceinline__ void gemv1_compute(const GemvBatch<R, U>& bt, const u
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const uint32_t z = (bt.zb[r][u] >> nib) & 0xF;
-        const uint32_t zbits = 0x6400u + z;
-        const half2v zz = -__builtin_bit_cast(half2v, zbits | (zbits << 16));
+        const uint32_t z1 = 0x6400u + z, z16 = 0x6400u + 16 * z;  // fp16 1024 + z, 1024 + 16 z
+        const half2v zz1 = -__builtin_bit_cast(half2v, z1 | (z1 << 16));
+        const half2v zz16 = -__builtin_bit_cast(half2v, z16 | (z16 << 16));
         const uint32_t wd[4] = {bt.cw[r][u].x, bt.cw[r][u].y, bt.cw[r][u].z, bt.cw[r][u].w};
         float part0 = 0.0f, part1 = 0.0f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w)
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            const uint32_t q = ((wd[w] >> (4 * p)) & 0x000F000Fu) | magic;
-            const half2v d = __builtin_bit_cast(half2v, q) + zz;  // exact (q - z)
-            if (p & 1) part1 = __builtin_amdgcn_fdot2(d, xq[w * 4 + p], part1, false);
-            else part0 = __builtin_amdgcn_fdot2(d, xq[w * 4 + p], part0, false);
-          }
-        acc[r] += h2f(bt.sc[r][u]) * (part0 + part1);
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t hi = wd[w] >> 8;
+          const half2v d0 = __builtin_bit_cast(half2v, (wd[w] & 0x000F000Fu) | magic) + zz1;
+          const half2v d1 = __builtin_bit_cast(half2v, (wd[w] & 0x00F000F0u) | magic) + zz16;
+          const half2v d2 = __builtin_bit_cast(half2v, (hi & 0x000F000Fu) | magic) + zz1;
+          const half2v d3 = __builtin_bit_cast(half2v, (hi & 0x00F000F0u) | magic) + zz16;
+          part0 = __builtin_amdgcn_fdot2(d0, xq[w * 4 + 0], part0, false);
+          part1 = __builtin_amdgcn_fdot2(d1, xq[w * 4 + 1], part1, false);
+          part0 = __builtin_amdgcn_fdot2(d2, xq[w * 4 + 2], part0, false);
+          part1 = __builtin_amdgcn_fdot2(d3, xq[w * 4 + 3], part1, false);
+        }
+        acc[r] = __builtin_fmaf(h2f(bt.sc[r][u]), part0 + part1 * 0.0625f, acc[r]);
       }
     }
   }
@@ -275,22 +285,23 @@ static hipError_t launch_gemv1(const uint16_t* X, const uint32_t* qw, const uint
   return launch_gemv1_x<R, U, 16, WPB>(X, qw, sc, z, N, K, Y, stream);
 }
 
-// Persistent variant for tall matrices: a few blocks per CU, each wave walks rows
-// wave0, wave0 + nwaves, ... (one batch of U chunks per lane covers K) and always has
-// the next row's code loads in flight while it multiplies the current one. Prefetches
-// are unconditional (row index clamped to the last row, which then hits in L2), so the
-// waits stay exact; a wave with a single row takes a straight-line path instead.
-template <int U, int XR, int WPB>
+// One batch covers K (at most 8 chunks per lane, K <= 16384), so only that path is
+// compiled: half the registers of the batched kernel, eight waves per SIMD. Each wave
+// owns RPW consecutive rows; with RPW = 2 the second row's codes are in flight while
+// the first is multiplied (tall matrices, where waves otherwise load and then compute in
+// lockstep). Stores are made by every lane with lane 0's sum (no branch); a row index
+// past the matrix end is clamped to the wave's last row, whose value it rewrites.
+template <int U, int XR, int WPB, int RPW>
 __global__ void __launch_bounds__(WPB * 64)
-    k_gemv1p(const uint16_t* X, const uint32_t* qweight, const uint16_t* scales,
+    k_gemv1s(const uint16_t* X, const uint32_t* qweight, const uint16_t* scales,
              const uint8_t* zeros, int64_t N, int64_t K, uint16_t* Y) {
   extern __shared__ uint4 xs[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int64_t wave0 = (int64_t)blockIdx.x * WPB + (tid >> 6);
-  const int64_t nwaves = (int64_t)gridDim.x * WPB;
+  const int64_t row0 = ((int64_t)blockIdx.x * WPB + (tid >> 6)) * RPW;
   const int64_t C = K / 32, G = K / kGroup, zbytes = (G + 1) / 2, words = K / 8;
-  auto clamp_row = [&](int64_t r) { return r < N ? r : N - 1; };
+  const int64_t lastrow = row0 + RPW - 1 < N ? row0 + RPW - 1 : N - 1;
+  auto row_at = [&](int r) { const int64_t v = row0 + r; return v < lastrow ? v : lastrow; };
 
   uint4 v[XR];
 #pragma unroll
@@ -299,81 +310,68 @@ __global__ void __launch_bounds__(WPB * 64)
     v[j] = *reinterpret_cast<const uint4*>(X + (i < words ? i : words - 1) * 8);
   }
   __builtin_amdgcn_sched_barrier(0);
-  GemvBatch<1, U> b0, b1;
-  int64_t rows[1] = {clamp_row(wave0)};
-  gemv1_load(b0, qweight, scales, zeros, rows, C, words, G, zbytes, 0, lane);
+  GemvBatch<1, U> bt[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int64_t rows[1] = {row_at(r)};
+    gemv1_load(bt[r], qweight, scales, zeros, rows, C, words, G, zbytes, 0, lane);
+  }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < XR; ++j) {
     const int64_t i = j * WPB * 64 + tid;
-    xs[i] = vgpr_copy(v[j]);
+    xs[i] = vgpr_copy(v[j]);  // the LDS row is padded to XR * WPB * 64 entries: no predicate
   }
   lds_barrier();
 
   const uint32_t magic = magic_1024x2();
-  auto finish = [&](float (&acc)[1], int64_t row) {
-    const float sum = wave_sum(acc[0]);
-    if (lane == 0 && row < N) Y[row] = f2h_bits(sum);
-  };
-  if (wave0 + nwaves >= N) {  // at most one row for this wave
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
     float acc[1] = {0.0f};
-    gemv1_compute(b0, xs, acc, C, 0, lane, magic);
-    finish(acc, wave0);
-    return;
-  }
-  for (int64_t row = wave0; row < N; row += 2 * nwaves) {
-    rows[0] = clamp_row(row + nwaves);
-    gemv1_load(b1, qweight, scales, zeros, rows, C, words, G, zbytes, 0, lane);
-    float acc0[1] = {0.0f};
-    gemv1_compute(b0, xs, acc0, C, 0, lane, magic);
-    finish(acc0, row);
-    rows[0] = clamp_row(row + 2 * nwaves);
-    gemv1_load(b0, qweight, scales, zeros, rows, C, words, G, zbytes, 0, lane);
-    float acc1[1] = {0.0f};
-    gemv1_compute(b1, xs, acc1, C, 0, lane, magic);
-    finish(acc1, row + nwaves);
+    gemv1_compute(bt[r], xs, acc, C, 0, lane, magic);
+    const float sum = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_sum(acc[0])), 0));
+    Y[row_at(r)] = f2h_bits(sum);
   }
 }
 
-template <int U, int XR, int WPB>
-static hipError_t launch_gemv1p_x(const uint16_t* X, const uint32_t* qw, const uint16_t* sc,
+template <int U, int XR, int WPB, int RPW>
+static hipError_t launch_gemv1s_x(const uint16_t* X, const uint32_t* qw, const uint16_t* sc,
                                   const uint8_t* z, int64_t N, int64_t K, uint16_t* Y,
-                                  int blocks_per_cu, hipStream_t stream) {
-  const int64_t want = (N + WPB - 1) / WPB;
-  const int64_t cap = (int64_t)256 * blocks_per_cu;
-  hipLaunchKernelGGL((k_gemv1p<U, XR, WPB>), dim3((unsigned)(want < cap ? want : cap)),
-                     dim3(WPB * 64), (size_t)XR * WPB * 64 * 16, stream, X, qw, sc, z, N, K, Y);
+                                  hipStream_t stream) {
+  const int64_t blocks = (N + WPB * RPW - 1) / (WPB * RPW);
+  hipLaunchKernelGGL((k_gemv1s<U, XR, WPB, RPW>), dim3((unsigned)blocks), dim3(WPB * 64),
+                     (size_t)XR * WPB * 64 * 16, stream, X, qw, sc, z, N, K, Y);
   return hipGetLastError();
 }
 
-template <int U, int WPB>
-static hipError_t launch_gemv1p(const uint16_t* X, const uint32_t* qw, const uint16_t* sc,
+// XR = U: the activation row (K / 8 entries) fits U * 256 entries, as U = ceil(K / 2048).
+template <int U, int RPW>
+static hipError_t launch_gemv1s(const uint16_t* X, const uint32_t* qw, const uint16_t* sc,
                                 const uint8_t* z, int64_t N, int64_t K, uint16_t* Y,
-                                int blocks_per_cu, hipStream_t stream) {
-  const int64_t per_thread = (K / 8 + WPB * 64 - 1) / (WPB * 64);
-  if (per_thread <= 1) return launch_gemv1p_x<U, 1, WPB>(X, qw, sc, z, N, K, Y, blocks_per_cu, stream);
-  if (per_thread <= 2) return launch_gemv1p_x<U, 2, WPB>(X, qw, sc, z, N, K, Y, blocks_per_cu, stream);
-  if (per_thread <= 4) return launch_gemv1p_x<U, 4, WPB>(X, qw, sc, z, N, K, Y, blocks_per_cu, stream);
-  if (per_thread <= 8) return launch_gemv1p_x<U, 8, WPB>(X, qw, sc, z, N, K, Y, blocks_per_cu, stream);
-  return launch_gemv1p_x<U, 16, WPB>(X, qw, sc, z, N, K, Y, blocks_per_cu, stream);
+                                hipStream_t stream) {
+  return launch_gemv1s_x<U, U, 4, RPW>(X, qw, sc, z, N, K, Y, stream);
 }
 
-// M = 1 dispatch (K <= 32768, so the activation row fits 64 KiB of LDS): one row per
-// wave, four waves per block, one batch of ceil(K / 2048) chunks per lane when that is
-// at most 8 (measured best on the Llama-2 7B/70B shapes), else batches of 4.
+// M = 1 dispatch (K <= 32768, so the activation row fits 64 KiB of LDS). Up to eight
+// chunks per lane (K <= 16384): the single-batch kernel, two rows per wave for tall
+// matrices with at most two chunks per lane (measured on the Llama-2 7B shapes), else
+// one. Longer rows: the batched kernel, four chunks per lane per batch.
 static hipError_t launch_gemv_m1(const uint16_t* X, const uint32_t* qw, const uint16_t* sc,
                                  const uint8_t* z, int64_t N, int64_t K, uint16_t* Y,
                                  hipStream_t stream) {
   const int64_t cpl = (K / 32 + 63) / 64;  // chunks per lane to cover K once
+  const bool tall = N >= 16384;
   switch (cpl) {
-    case 1: return launch_gemv1<1, 1>(X, qw, sc, z, N, K, Y, stream);
-    case 2: return launch_gemv1<1, 2>(X, qw, sc, z, N, K, Y, stream);
-    case 3: return launch_gemv1<1, 3>(X, qw, sc, z, N, K, Y, stream);
-    case 4: return launch_gemv1<1, 4>(X, qw, sc, z, N, K, Y, stream);
-    case 5: return launch_gemv1<1, 5>(X, qw, sc, z, N, K, Y, stream);
-    case 6: return launch_gemv1<1, 6>(X, qw, sc, z, N, K, Y, stream);
-    case 7: return launch_gemv1<1, 7>(X, qw, sc, z, N, K, Y, stream);
-    case 8: return launch_gemv1<1, 8>(X, qw, sc, z, N, K, Y, stream);
+    case 1: return tall ? launch_gemv1s<1, 2>(X, qw, sc, z, N, K, Y, stream)
+                        : launch_gemv1s<1, 1>(X, qw, sc, z, N, K, Y, stream);
+    case 2: return tall ? launch_gemv1s<2, 2>(X, qw, sc, z, N, K, Y, stream)
+                        : launch_gemv1s<2, 1>(X, qw, sc, z, N, K, Y, stream);
+    case 3: return launch_gemv1s<3, 1>(X, qw, sc, z, N, K, Y, stream);
+    case 4: return launch_gemv1s<4, 1>(X, qw, sc, z, N, K, Y, stream);
+    case 5: return launch_gemv1s<5, 1>(X, qw, sc, z, N, K, Y, stream);
+    case 6: return launch_gemv1s<6, 1>(X, qw, sc, z, N, K, Y, stream);
+    case 7: return launch_gemv1s<7, 1>(X, qw, sc, z, N, K, Y, stream);
+    case 8: return launch_gemv1s<8, 1>(X, qw, sc, z, N, K, Y, stream);
     default: return launch_gemv1<1, 4>(X, qw, sc, z, N, K, Y, stream);
   }
 }
