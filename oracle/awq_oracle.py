@@ -33,7 +33,10 @@ design notes of the repository):
 * statistic = plain mean of |x| over all calibration tokens;
 * s = (max(mean|x|, 2^-14))^alpha, alpha_i = i / n_grid, i = 0..n_grid-1, s stored as fp16;
 * packed word: channels 0, 2, 4, 6 in the low nibbles of its bytes, 1, 3, 5, 7 in the high;
-* error = sum of squares of X * D^T with D = W - Q(W diag(s)) diag(1/s), ties -> smallest i.
+* error = sum of squares of X * D^T with D = W - Q(W diag(s)) diag(1/s), ties -> smallest i;
+* the fused MLP module ([AWQ-SKILL] "主要功能和特点", fused attention/MLP; [AWQ-WIKI]
+  TinyChat kernel fusion) is Llama's gated MLP: h = SiLU(x W_gate^T) * (x W_up^T) with
+  SiLU(v) = v / (1 + e^-v), gate and up stacked as one packed weight (gate rows first).
 
 Every function spells out the steps in order; numpy supplies only elementwise IEEE
 operations, reductions and (fp64) matrix products.
@@ -49,6 +52,7 @@ __all__ = [
     "activation_mean_abs", "candidate_scales", "quantize_groups", "pack", "unpack",
     "quantize_pack", "dequantize", "NIBBLE_CHANNEL", "search_errors", "search_scales", "linear_reference",
     "linear_within_tolerance", "fp16_midpoint_distance", "relative_gap", "packed_bytes",
+    "silu", "SILU_DMAX", "gated_silu_reference", "gated_silu_within_tolerance",
 ]
 
 GROUP = 128                       # [AWQ-PRACTICE] §2.3; [AWQ-SKILL] q_group_size
@@ -293,6 +297,47 @@ def linear_within_tolerance(y, y_ref, bound, rel: float = 2e-3) -> np.ndarray:
     """Per-element check |y - y_ref| <= rel * bound (returns a boolean mask)."""
     y = np.asarray(y, dtype=_F64)
     return np.abs(y - y_ref) <= rel * bound
+
+
+# --------------------------------------------------------------------------- fused MLP
+SILU_DMAX = 1.1  # bound on |SiLU'(v)| over all v (the maximum is about 1.0998, near v = 2.40)
+
+
+def silu(v: np.ndarray) -> np.ndarray:
+    """SiLU(v) = v / (1 + e^-v) in fp64 (large negative v: e^-v overflows to inf, SiLU -> -0)."""
+    v = np.asarray(v, dtype=_F64)
+    with np.errstate(over="ignore"):
+        return v / (1.0 + np.exp(-v))
+
+
+def gated_silu_reference(X16: np.ndarray, qweight: np.ndarray, scales: np.ndarray,
+                         zeros: np.ndarray, K: int):
+    """Fused MLP module of a packed gate|up weight: h = SiLU(g) * u, in fp64.
+
+    [AWQ-SKILL] "主要功能和特点": fused attention/MLP modules cut decode latency;
+    [AWQ-WIKI] TinyChat: kernel fusion. The packed weight holds the N/2 gate rows first,
+    then the N/2 up rows; g = x W_gate^T and u = x W_up^T are both W4A16 linears
+    (linear_reference). Returns (h, g, u, bound_g, bound_u), each [M][N/2].
+    """
+    y, bound = linear_reference(X16, qweight, scales, zeros, K)
+    nh = y.shape[1] // 2
+    g, u = y[:, :nh], y[:, nh:2 * nh]
+    return silu(g) * u, g, u, bound[:, :nh], bound[:, nh:2 * nh]
+
+
+def gated_silu_within_tolerance(h, g, u, bound_g, bound_u, rel: float = 2e-3) -> np.ndarray:
+    """Per-element check of a fused gate|up result against the fp64 reference.
+
+    With |g' - g| <= rel * bound_g and |u' - u| <= rel * bound_u (the linear tolerance),
+    |SiLU(g') u' - SiLU(g) u| <= SILU_DMAX |g' - g| |u| + |SiLU(g)| |u' - u|
+    + SILU_DMAX |g' - g| |u' - u|; one fp16 rounding of the result adds at most 2^-11 |h|
+    (2^-10 allowed, which also covers the fp32 evaluation of SiLU).
+    """
+    h = np.asarray(h, dtype=_F64)
+    h_ref = silu(g) * u
+    tol = (rel * (SILU_DMAX * bound_g * np.abs(u) + np.abs(silu(g)) * bound_u)
+           + SILU_DMAX * rel * rel * bound_g * bound_u + 2.0 ** -10 * np.abs(h_ref))
+    return np.abs(h - h_ref) <= tol
 
 
 # --------------------------------------------------------------------------- hazards

@@ -337,3 +337,65 @@ def test_format_size_matches_70b_figure():
     assert total == 68_451_041_280 * 133 // 256   # 0.51953125 B per weight = 35.56 GB
     assert 33e9 < total < 37e9
     assert oracle.packed_bytes(4096, 4096) * 8 == 4096 * 4096 * 4 + 4096 * 32 * 16 + 4096 * 16 * 8
+
+
+# ----------------------------------------------------------------- fused MLP (gate|up)
+def test_silu_matches_library_logistic():
+    """SiLU(v) = v * logistic(v), against scipy's expit over the fp16 range and beyond."""
+    from scipy.special import expit
+    v = np.concatenate([np.linspace(-60, 60, 20001), [-1000.0, -745.5, 0.0, 1e-30, 65504.0]])
+    ref = v * expit(v)
+    got = oracle.silu(v)
+    assert np.all(np.abs(got - ref) <= 4 * np.finfo(np.float64).eps * np.abs(ref) + 1e-300)
+
+
+def test_silu_odd_part_identity_and_derivative_bound():
+    """SiLU(-v) = SiLU(v) - v (logistic symmetry); max |SiLU'| is just below SILU_DMAX."""
+    v = np.linspace(0, 40, 4001)
+    assert np.allclose(oracle.silu(-v), oracle.silu(v) - v, rtol=0, atol=1e-13)
+    x = np.linspace(-30, 30, 600001)
+    d = np.diff(oracle.silu(x)) / np.diff(x)
+    assert 1.09 < np.max(np.abs(d)) <= oracle.SILU_DMAX
+
+
+def _gate_up_case(nh=6, K=256, off=90):
+    W = si.weights(2 * nh, K, offset=off)
+    qw, sc, zb, _ = oracle.quantize_pack(W)
+    q, z, scale = oracle.unpack(qw, sc, zb, K)
+    return qw, sc, zb, oracle.dequantize(q, z, scale)
+
+
+def test_gated_silu_gate_rows_first():
+    """One-hot x = e_k: h_n = SiLU(deq_gate[n, k]) * deq_up[n, k], gate rows first."""
+    import math
+    nh, K = 6, 256
+    qw, sc, zb, deq = _gate_up_case(nh, K)
+    ks = [0, 1, 127, 128, 255]
+    X = np.zeros((len(ks), K), dtype=np.float16)
+    for m, k in enumerate(ks):
+        X[m, k] = 1.0
+    h, g, u, bg, bu = oracle.gated_silu_reference(X, qw, sc, zb, K)
+    assert h.shape == (len(ks), nh)
+    for m, k in enumerate(ks):
+        for n in range(nh):
+            a, b = float(deq[n, k]), float(deq[nh + n, k])
+            assert h[m, n] == pytest.approx(a / (1.0 + math.exp(-a)) * b, rel=1e-15, abs=1e-300)
+            assert bg[m, n] == abs(a) and bu[m, n] == abs(b)
+    # mutant: up rows first
+    swapped = oracle.silu(u) * g
+    assert not np.allclose(swapped, h, rtol=1e-6, atol=0)
+
+
+def test_gated_silu_tolerance_covers_linear_errors():
+    """Any g', u' within the linear tolerance, with one fp16 rounding of SiLU(g') u', passes;
+    a result off by a few percent does not."""
+    rng = np.random.default_rng(5)
+    qw, sc, zb, _ = _gate_up_case(64, 512, off=91)
+    X = si.activations(8, 512, offset=91)
+    h, g, u, bg, bu = oracle.gated_silu_reference(X, qw, sc, zb, 512)
+    for _ in range(20):
+        g2 = g + rng.uniform(-1, 1, g.shape) * 2e-3 * bg
+        u2 = u + rng.uniform(-1, 1, u.shape) * 2e-3 * bu
+        h2 = (oracle.silu(g2) * u2).astype(np.float16).astype(np.float64)
+        assert oracle.gated_silu_within_tolerance(h2, g, u, bg, bu).all()
+    assert not oracle.gated_silu_within_tolerance(h * 1.05, g, u, bg, bu).all()
