@@ -11,9 +11,10 @@ channels x20, group 128, 4-bit + zero point):
   3. decode GEMV at M = 1 over 32 layer copies (one token through the 32 decoder layers
      of a 7B model: 3.37 GB of packed weights, far above the 256 MB last-level cache, so
      every launch streams from HBM), with q|k|v and gate|up launched as one GEMV each
-     (they share their input; the fused-module decode of the pages); the same sweep
-     with one launch per matrix is timed and reported beside it;
-  4. prefill MFMA dequant-GEMM at M = 2048 over the four groups.
+     (they share their input; the fused-module decode of the pages), gate|up with its
+     SiLU(gate) * up epilogue (the fused MLP module); the same sweep with one launch
+     per matrix (no epilogue) is timed and reported beside it;
+  4. prefill MFMA dequant-GEMM at M = 2048 over the four groups (gate|up fused as in 3).
 Inputs are resident in HBM before the timed region. Each part is captured once in a
 HIP graph (so host launch overhead is not kernel time) and replayed. The K timed steps
 run in phases, part by part (K decode sweeps back to back, then K prefill GEMMs, and so
@@ -58,8 +59,12 @@ def packed_bytes(N, K):
     return N * (K // 2) + N * G * 2 + N * ((G + 1) // 2)
 
 
-def linear_bytes(M, N, K):
-    return packed_bytes(N, K) + 2 * M * K + 2 * M * N
+def linear_bytes(M, N, K, gated=False):
+    """Algorithmic HBM bytes of one W4A16 linear: packed weight + X + Y (gated: Y is N/2 wide)."""
+    return packed_bytes(N, K) + 2 * M * K + 2 * M * (N // 2 if gated else N)
+
+
+GATED = {"gate_up"}  # the fused MLP module: SiLU(gate) * up in the launch's epilogue
 
 
 def source_hash():
@@ -167,10 +172,12 @@ def main():
     xdec = {4096: si.torch_activations(1, 4096, 300, dev, channel_offset=4096),
             11008: si.torch_activations(1, 11008, 301, dev, channel_offset=11008)}
     ydec = {name: torch.empty((1, N), dtype=torch.float16, device=dev) for name, _, _, N, K in MATRICES}
-    yfus = {g: torch.empty((1, N), dtype=torch.float16, device=dev) for g, (N, K) in SEARCH_GROUPS.items()}
+    yfus = {g: torch.empty((1, N // 2 if g in GATED else N), dtype=torch.float16, device=dev)
+            for g, (N, K) in SEARCH_GROUPS.items()}
     xpre = {4096: si.torch_activations(PREFILL_M, 4096, 400, dev, channel_offset=4096),
             11008: si.torch_activations(PREFILL_M, 11008, 401, dev, channel_offset=11008)}
-    ypre = {g: torch.empty((PREFILL_M, N), dtype=torch.float16, device=dev) for g, (N, K) in SEARCH_GROUPS.items()}
+    ypre = {g: torch.empty((PREFILL_M, N // 2 if g in GATED else N), dtype=torch.float16, device=dev)
+            for g, (N, K) in SEARCH_GROUPS.items()}
     torch.cuda.synchronize()
 
     # ------------------------------------------------------------------ the parts
@@ -182,10 +189,11 @@ def main():
         for g in SEARCH_GROUPS:
             awq.quantize_pack(Wg[g], sres[g].s_best, out=packed[0][g])
 
-    def part_gemv():  # decode: q|k|v and gate|up as one launch each (shared input)
+    def part_gemv():  # decode: q|k|v and gate|up as one launch each (shared input), SiLU * up
         for c in range(args.layers):
             for g, (N, K) in SEARCH_GROUPS.items():
-                awq.linear_w4a16(xdec[K], packed[c][g], out=yfus[g])
+                linear = awq.linear_w4a16_gated_silu if g in GATED else awq.linear_w4a16
+                linear(xdec[K], packed[c][g], out=yfus[g])
 
     def part_gemv_unfused():  # decode: one launch per matrix
         for c in range(args.layers):
@@ -194,7 +202,8 @@ def main():
 
     def part_gemm():
         for g, (N, K) in SEARCH_GROUPS.items():
-            awq.linear_w4a16(xpre[K], packed[0][g], out=ypre[g])
+            linear = awq.linear_w4a16_gated_silu if g in GATED else awq.linear_w4a16
+            linear(xpre[K], packed[0][g], out=ypre[g])
 
     parts = [("search", part_search), ("quant_pack", part_pack), ("gemv", part_gemv),
              ("gemv_unfused", part_gemv_unfused), ("gemm", part_gemm)]
@@ -252,7 +261,7 @@ def main():
 
     # ------------------------------------------------------------------ figures
     n_gemv = args.layers * len(SEARCH_GROUPS)
-    gemv_bytes = args.layers * sum(linear_bytes(1, N, K) for N, K in SEARCH_GROUPS.values())
+    gemv_bytes = args.layers * sum(linear_bytes(1, N, K, g in GATED) for g, (N, K) in SEARCH_GROUPS.items())
     gemv_gbs = gemv_bytes / (part_ms["gemv"] * 1e-3) / 1e9
     n_gemv_u = args.layers * len(MATRICES)
     gemv_bytes_u = args.layers * sum(linear_bytes(1, N, K) for _, _, _, N, K in MATRICES)
@@ -281,7 +290,7 @@ def main():
         "data": "synthetic (seeded; W ~ N(0,0.02^2), X ~ N(0,1) with 1% channels x20)",
         "config": {"workload": "Llama-2-7B decoder-layer linears (q,k,v,o 4096x4096; gate,up 11008x4096; "
                                "down 4096x11008): decode GEMV M=1 over "
-                               f"{args.layers} layer copies with q|k|v and gate|up launched together; "
+                               f"{args.layers} layer copies with q|k|v and gate|up (SiLU(gate)*up epilogue) launched together; "
                                f"prefill GEMM M={PREFILL_M}; scale search T={CALIB_T}, 20 alpha, group 128; "
                                "quantize+pack",
                    "gemv_launches_per_step": n_gemv, "group_size": GROUP, "w_bit": 4,

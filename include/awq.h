@@ -162,6 +162,29 @@ awq_status awq_linear_w4a16_ex(const void* X, int64_t M, const uint32_t* qweight
                                const awq_config* cfg, void* Y, uint32_t* flags,
                                awq_linear_kernel kernel, void* stream);
 
+/*
+ * awq_linear_w4a16_gated_silu -- fused MLP module of a packed gate|up weight:
+ *   Y = SiLU(X * deq(W_gate)^T) * (X * deq(W_up)^T), SiLU(v) = v / (1 + e^-v).
+ *   [SKILL] "主要功能和特点" (fused attention/MLP modules lower decode latency); [WIKI]
+ *   TinyChat (kernel fusion). Reading: Llama's gated MLP, with gate and up packed as one
+ *   weight so one launch streams both.
+ *   qweight/scales/zeros: one packed weight of N rows (awq_quantize_pack of the stacked
+ *   [W_gate; W_up]): rows [0, N/2) are the gate projection, rows [N/2, N) the up
+ *   projection. N must be even (else AWQ_ERR_BAD_SHAPE). X fp16 [M][K]; Y fp16 [M][N/2].
+ *   g and u are accumulated in fp32 exactly as in awq_linear_w4a16, SiLU(g) * u is formed
+ *   in fp32 and rounded once to fp16. Kernel choice, errors and alignment as for
+ *   awq_linear_w4a16 / awq_linear_w4a16_ex.
+ */
+awq_status awq_linear_w4a16_gated_silu(const void* X, int64_t M, const uint32_t* qweight,
+                                       const void* scales, const uint8_t* zeros, int64_t N,
+                                       int64_t K, const awq_config* cfg, void* Y,
+                                       uint32_t* flags, void* stream);
+awq_status awq_linear_w4a16_gated_silu_ex(const void* X, int64_t M, const uint32_t* qweight,
+                                          const void* scales, const uint8_t* zeros, int64_t N,
+                                          int64_t K, const awq_config* cfg, void* Y,
+                                          uint32_t* flags, awq_linear_kernel kernel,
+                                          void* stream);
+
 /* Largest M served by the GEMV kernel under AWQ_LINEAR_AUTO. */
 int32_t awq_gemv_max_m(void);
 

@@ -105,3 +105,18 @@ def test_linear_validation(lib):
     assert call(kern=7) == 3
     assert call(Y=FAKE_ODD) == 4
     assert lib.awq_linear_w4a16(None, 1, FAKE, FAKE, FAKE, 64, 256, None, FAKE, None, None) == 1
+
+
+def test_gated_linear_validation(lib):
+    def call(X=FAKE, M=1, N=64, K=256, Y=FAKE, kern=0):
+        return lib.awq_linear_w4a16_gated_silu_ex(X, M, FAKE, FAKE, FAKE, N, K, None, Y, None, kern,
+                                                  None)
+    assert call(X=None) == 1
+    assert call(N=63) == 2              # gate|up needs an even row count
+    assert call(N=1) == 2
+    assert call(K=130) == 2
+    assert call(M=9, kern=1) == 2
+    assert call(kern=7) == 3
+    assert call(Y=FAKE_ODD) == 4
+    assert lib.awq_linear_w4a16_gated_silu(FAKE, 1, FAKE, FAKE, FAKE, 65, 256, None, FAKE, None,
+                                           None) == 2

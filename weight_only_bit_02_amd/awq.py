@@ -181,5 +181,27 @@ def linear_w4a16(X: torch.Tensor, w: PackedLinear, kernel: str = "auto",
     return Y
 
 
+def linear_w4a16_gated_silu(X: torch.Tensor, w: PackedLinear, kernel: str = "auto",
+                            out: torch.Tensor | None = None) -> torch.Tensor:
+    """awq_linear_w4a16_gated_silu: Y[M][N/2] = SiLU(X deq(W_gate)^T) * (X deq(W_up)^T),
+    where w packs the gate rows [0, N/2) and the up rows [N/2, N) (fused MLP module)."""
+    lib = _abi.load()
+    _need(X, torch.float16, "X")
+    M, K = X.shape
+    if K != w.K:
+        raise ValueError("X and the packed weight disagree on K")
+    if w.N % 2:
+        raise ValueError("a gate|up weight has an even number of rows")
+    Y = out if out is not None else torch.empty((M, w.N // 2), dtype=torch.float16, device=X.device)
+    _need(Y, torch.float16, "Y")
+    if Y.shape != (M, w.N // 2):
+        raise ValueError("Y has the wrong shape")
+    cfg = _abi.config()
+    _abi.check("awq_linear_w4a16_gated_silu_ex", lib.awq_linear_w4a16_gated_silu_ex(
+        _ptr(X), M, _ptr(w.qweight), _ptr(w.scales), _ptr(w.zeros), w.N, K, C.byref(cfg),
+        _ptr(Y), None, _KERNELS[kernel], _stream()))
+    return Y
+
+
 def gemv_max_m() -> int:
     return int(_abi.load().awq_gemv_max_m())

@@ -170,15 +170,15 @@ awq_status awq_search_scales(const void* X, int64_t T, const void* W, int64_t N,
   return hip_status(e);
 }
 
-awq_status awq_linear_w4a16_ex(const void* X, int64_t M, const uint32_t* qweight,
-                               const void* scales, const uint8_t* zeros, int64_t N, int64_t K,
-                               const awq_config* cfg, void* Y, uint32_t* flags,
-                               awq_linear_kernel kernel, void* stream) {
-  (void)flags;
+static awq_status linear_common(const void* X, int64_t M, const uint32_t* qweight,
+                                const void* scales, const uint8_t* zeros, int64_t N, int64_t K,
+                                const awq_config* cfg, void* Y, awq_linear_kernel kernel,
+                                bool gated, void* stream) {
   const awq_config c = resolve(cfg);
   if (!X || !qweight || !scales || !zeros || !Y) return AWQ_ERR_NULL_POINTER;
   if (!supported(c)) return AWQ_ERR_UNSUPPORTED;
   if (M < 1 || M >= kMaxDim || !good_nk(N, K)) return AWQ_ERR_BAD_SHAPE;
+  if (gated && (N < 2 || N % 2 != 0)) return AWQ_ERR_BAD_SHAPE;
   if (kernel != AWQ_LINEAR_AUTO && kernel != AWQ_LINEAR_GEMV && kernel != AWQ_LINEAR_GEMM)
     return AWQ_ERR_UNSUPPORTED;
   if (kernel == AWQ_LINEAR_GEMV && M > awq::kGemvMaxM) return AWQ_ERR_BAD_SHAPE;
@@ -190,8 +190,16 @@ awq_status awq_linear_w4a16_ex(const void* X, int64_t M, const uint32_t* qweight
   const auto* Xh = (const uint16_t*)X;
   const auto* sc = (const uint16_t*)scales;
   auto* Yh = (uint16_t*)Y;
-  return hip_status(gemv ? awq::launch_gemv(Xh, M, qweight, sc, zeros, N, K, Yh, st)
-                         : awq::launch_gemm(Xh, M, qweight, sc, zeros, N, K, Yh, st));
+  return hip_status(gemv ? awq::launch_gemv(Xh, M, qweight, sc, zeros, N, K, Yh, gated, st)
+                         : awq::launch_gemm(Xh, M, qweight, sc, zeros, N, K, Yh, gated, st));
+}
+
+awq_status awq_linear_w4a16_ex(const void* X, int64_t M, const uint32_t* qweight,
+                               const void* scales, const uint8_t* zeros, int64_t N, int64_t K,
+                               const awq_config* cfg, void* Y, uint32_t* flags,
+                               awq_linear_kernel kernel, void* stream) {
+  (void)flags;
+  return linear_common(X, M, qweight, scales, zeros, N, K, cfg, Y, kernel, false, stream);
 }
 
 awq_status awq_linear_w4a16(const void* X, int64_t M, const uint32_t* qweight,
@@ -199,6 +207,23 @@ awq_status awq_linear_w4a16(const void* X, int64_t M, const uint32_t* qweight,
                             const awq_config* cfg, void* Y, uint32_t* flags, void* stream) {
   return awq_linear_w4a16_ex(X, M, qweight, scales, zeros, N, K, cfg, Y, flags, AWQ_LINEAR_AUTO,
                              stream);
+}
+
+awq_status awq_linear_w4a16_gated_silu_ex(const void* X, int64_t M, const uint32_t* qweight,
+                                          const void* scales, const uint8_t* zeros, int64_t N,
+                                          int64_t K, const awq_config* cfg, void* Y,
+                                          uint32_t* flags, awq_linear_kernel kernel,
+                                          void* stream) {
+  (void)flags;
+  return linear_common(X, M, qweight, scales, zeros, N, K, cfg, Y, kernel, true, stream);
+}
+
+awq_status awq_linear_w4a16_gated_silu(const void* X, int64_t M, const uint32_t* qweight,
+                                       const void* scales, const uint8_t* zeros, int64_t N,
+                                       int64_t K, const awq_config* cfg, void* Y,
+                                       uint32_t* flags, void* stream) {
+  return awq_linear_w4a16_gated_silu_ex(X, M, qweight, scales, zeros, N, K, cfg, Y, flags,
+                                        AWQ_LINEAR_AUTO, stream);
 }
 
 }  // extern "C"

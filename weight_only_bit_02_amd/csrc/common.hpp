@@ -151,6 +151,13 @@ __device__ __forceinline__ int64_t f16_abs_units(uint16_t h) {
   return (int64_t)(1024 + m) << (e - 1);
 }
 
+// SiLU(v) = v / (1 + e^-v) in fp32, the activation of the fused gate|up epilogue, with
+// the hardware exponential and reciprocal (relative error about 1e-6 for |v| <= 20, far
+// below the result's fp16 rounding); large negative v: e^-v = inf, rcp(inf) = 0, -0.
+__device__ __forceinline__ float silu_f32(float v) {
+  return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v));
+}
+
 // Copy of a loaded vector through VGPRs the optimizer cannot see through. Storing a
 // loaded value straight to LDS can otherwise leave it in a stack slot (scratch memory),
 // whose reload waits, like any vector memory access, for every load still in flight.

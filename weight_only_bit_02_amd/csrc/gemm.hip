@@ -19,6 +19,12 @@
 // is the plain sum over K. fp32 accumulation, one fp16 rounding of the result.
 // The 128-row A panels are handed to the XCDs in contiguous runs of tiles, so the
 // blocks running together on one XCD share their A panel in that XCD's L2.
+//
+// Fused gate|up (GATED; "AWQ量化技术Skill", "主要功能和特点": fused MLP modules): the
+// packed weight holds N/2 gate rows, then N/2 up rows. A block covers 128 outputs; a
+// wave's first 32-column MFMA tile is gate column n, its second the up column n + N/2,
+// so each lane holds g and u of the same output element and the epilogue stores
+// SiLU(g) * u (fp32, one fp16 rounding) into Y[M][N/2] without any data exchange.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -59,6 +65,7 @@ struct GemmStage {
   uint32_t zb[2], sc[2];
 };
 
+template <bool GATED>
 __global__ void __launch_bounds__(256)
     k_gemm(const uint16_t* X, int64_t M, const uint32_t* qweight, const uint16_t* scales,
            const uint8_t* zeros, int64_t N, int64_t K, uint16_t* __restrict__ Y, int64_t mt,
@@ -70,7 +77,8 @@ __global__ void __launch_bounds__(256)
   const int64_t t = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
   if (t >= mt * nt) return;
   const int64_t m0 = (t / nt) * kBM;
-  const int64_t n0 = (t % nt) * kBN;
+  const int64_t n0 = (t % nt) * (GATED ? kBN / 2 : kBN);  // first output column of the tile
+  const int64_t nh = N / 2;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -90,12 +98,18 @@ __global__ void __launch_bounds__(256)
     a_row[i] = (r < M ? r : M - 1) * K;
     a_kc[i] = id & 15;
   }
-  // B map: this lane's two output columns.
+  // B map: this lane's two weight rows (gated: gate row n and up row n + N/2).
   int64_t b_col[2];
+  if constexpr (GATED) {
+    const int64_t n = n0 + wave * 32 + m32;
+    b_col[0] = n < nh ? n : nh - 1;
+    b_col[1] = b_col[0] + nh;
+  } else {
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int64_t n = n0 + wave * 64 + b * 32 + m32;
-    b_col[b] = n < N ? n : N - 1;
+    for (int b = 0; b < 2; ++b) {
+      const int64_t n = n0 + wave * 64 + b * 32 + m32;
+      b_col[b] = n < N ? n : N - 1;
+    }
   }
 
   // small loads first, then codes, then activations: waits for an older stage never
@@ -207,27 +221,42 @@ __global__ void __launch_bounds__(256)
 
   // ------------------------------------------------------------------ epilogue
   // 32x32 accumulator layout: element e of lane l is (row 8(e/4) + 4(l/32) + e%4, col l%32).
+  if constexpr (GATED) {
+    const int64_t col = n0 + wave * 32 + m32;
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int64_t col = n0 + wave * 64 + b * 32 + m32;
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int64_t row = m0 + a * 32 + 8 * (e >> 2) + 4 * kh + (e & 3);
-        if (row < M && col < N) Y[row * N + col] = f2h_bits(acc[a][b][e]);
+        if (row < M && col < nh) Y[row * nh + col] = f2h_bits(silu_f32(acc[a][0][e]) * acc[a][1][e]);
       }
-    }
+  } else {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int64_t col = n0 + wave * 64 + b * 32 + m32;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int64_t row = m0 + a * 32 + 8 * (e >> 2) + 4 * kh + (e & 3);
+          if (row < M && col < N) Y[row * N + col] = f2h_bits(acc[a][b][e]);
+        }
+      }
+  }
 }
 
 hipError_t launch_gemm(const uint16_t* X, int64_t M, const uint32_t* qweight,
                        const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
-                       uint16_t* Y, hipStream_t stream) {
+                       uint16_t* Y, bool gated, hipStream_t stream) {
   const int64_t mt = (M + kBM - 1) / kBM;
-  const int64_t nt = (N + kBN - 1) / kBN;
+  const int64_t nt = gated ? (N / 2 + kBN / 2 - 1) / (kBN / 2) : (N + kBN - 1) / kBN;
   const int64_t per_xcd = (mt * nt + kXcds - 1) / kXcds;
-  hipLaunchKernelGGL(k_gemm, dim3((unsigned)(per_xcd * kXcds)), dim3(256), 0, stream, X, M,
-                     qweight, scales, zeros, N, K, Y, mt, nt, per_xcd);
+  if (gated)
+    hipLaunchKernelGGL(k_gemm<true>, dim3((unsigned)(per_xcd * kXcds)), dim3(256), 0, stream, X,
+                       M, qweight, scales, zeros, N, K, Y, mt, nt, per_xcd);
+  else
+    hipLaunchKernelGGL(k_gemm<false>, dim3((unsigned)(per_xcd * kXcds)), dim3(256), 0, stream, X,
+                       M, qweight, scales, zeros, N, K, Y, mt, nt, per_xcd);
   return hipGetLastError();
 }
 

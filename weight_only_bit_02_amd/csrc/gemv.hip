@@ -15,6 +15,11 @@
 // one mask per pair yields two adjacent channels and the activations are used in
 // their natural order (each 32-bit word of x is one pair). Rows finish with a DPP /
 // shuffle reduction across the wave.
+//
+// Fused gate|up (GATED): the packed weight holds N/2 gate rows, then N/2 up rows
+// ("AWQ量化技术Skill", "主要功能和特点": fused MLP modules). A wave computes gate row n
+// and up row n + N/2 together and stores h_n = SiLU(g_n) * u_n (fp32, one fp16
+// rounding) into Y[M][N/2].
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -22,15 +27,17 @@ namespace awq {
 
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
-template <int M, int R>
+template <int M, int R, bool GATED>
 __global__ void __launch_bounds__(256)
     k_gemv(const uint16_t* __restrict__ X, const uint32_t* __restrict__ qweight,
            const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int64_t N,
            int64_t K, uint16_t* __restrict__ Y) {
+  static_assert(!GATED || R == 2, "a gated wave owns one gate row and one up row");
   const int lane = threadIdx.x & 63;
   const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-  const int64_t row0 = wave * R;
-  if (row0 >= N) return;  // whole wave leaves together
+  const int64_t nh = N / 2;
+  const int64_t row0 = GATED ? wave : wave * R;
+  if (row0 >= (GATED ? nh : N)) return;  // whole wave leaves together
   const int64_t C = K / 32;  // chunks per row
   const int64_t G = K / kGroup;
   const int64_t zb = (G + 1) / 2;
@@ -38,7 +45,8 @@ __global__ void __launch_bounds__(256)
 
   int64_t rows[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) rows[r] = (row0 + r < N) ? row0 + r : N - 1;
+  for (int r = 0; r < R; ++r)
+    rows[r] = GATED ? row0 + r * nh : ((row0 + r < N) ? row0 + r : N - 1);
 
   float acc[R][M];
 #pragma unroll
@@ -89,13 +97,21 @@ __global__ void __launch_bounds__(256)
     }
   }
 
-#pragma unroll
-  for (int r = 0; r < R; ++r)
+  if constexpr (GATED) {
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-      const float v = wave_sum(acc[r][m]);
-      if (lane == 0 && row0 + r < N) Y[(int64_t)m * N + row0 + r] = f2h_bits(v);
+      const float g = wave_sum(acc[0][m]), u = wave_sum(acc[R - 1][m]);
+      if (lane == 0) Y[(int64_t)m * nh + row0] = f2h_bits(silu_f32(g) * u);
     }
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const float v = wave_sum(acc[r][m]);
+        if (lane == 0 && row0 + r < N) Y[(int64_t)m * N + row0 + r] = f2h_bits(v);
+      }
+  }
 }
 
 // M = 1: the activation row is staged once per block in LDS, so the inner loop reads
@@ -205,22 +221,26 @@ __device__ __forceinline__ void lds_barrier() {
 // the activation row without waiting for them. For K above 64 * U * 32 the wave walks
 // nb batches with the next batch's loads in flight (unconditional, clamped prefetch, so
 // every path has the same loads outstanding and the waits stay exact).
-template <int R, int U, int XR, int WPB>
+template <int R, int U, int XR, int WPB, bool GATED>
 __global__ void __launch_bounds__(WPB * 64)
     k_gemv1(const uint16_t* X, const uint32_t* qweight, const uint16_t* scales,
             const uint8_t* zeros, int64_t N, int64_t K, uint16_t* Y) {
+  static_assert(!GATED || R == 2, "a gated wave owns one gate row and one up row");
   // (no __restrict__: the code loads must stay ordered before the LDS barrier below)
   // XR * WPB * 64 entries (>= K / 8): entry i holds channels 8i..8i+7
   extern __shared__ uint4 xs[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int64_t row0 = ((int64_t)blockIdx.x * WPB + (tid >> 6)) * R;
+  const int64_t nh = N / 2;
+  const int64_t wave_id = (int64_t)blockIdx.x * WPB + (tid >> 6);
+  const int64_t row0 = GATED ? (wave_id < nh ? wave_id : nh - 1) : wave_id * R;
   const int64_t C = K / 32, G = K / kGroup, zbytes = (G + 1) / 2, words = K / 8;
   const int64_t nb = (C + 64 * U - 1) / (64 * U);
   __builtin_assume(nb >= 1);
   int64_t rows[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) rows[r] = (row0 + r < N) ? row0 + r : N - 1;
+  for (int r = 0; r < R; ++r)
+    rows[r] = GATED ? row0 + r * nh : ((row0 + r < N) ? row0 + r : N - 1);
 
   uint4 v[XR];
 #pragma unroll
@@ -255,34 +275,40 @@ __global__ void __launch_bounds__(WPB * 64)
       if (b + 1 < nb) gemv1_compute(b1, xs, acc, C, b + 1, lane, magic);
     }
   }
+  if constexpr (GATED) {
+    const float g = wave_sum(acc[0]), u = wave_sum(acc[R - 1]);
+    if (lane == 0 && wave_id < nh) Y[wave_id] = f2h_bits(silu_f32(g) * u);
+  } else {
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const float sum = wave_sum(acc[r]);
-    if (lane == 0 && row0 + r < N) Y[row0 + r] = f2h_bits(sum);
+    for (int r = 0; r < R; ++r) {
+      const float sum = wave_sum(acc[r]);
+      if (lane == 0 && row0 + r < N) Y[row0 + r] = f2h_bits(sum);
+    }
   }
 }
 
-template <int R, int U, int XR, int WPB>
+template <int R, int U, int XR, int WPB, bool GATED>
 static hipError_t launch_gemv1_x(const uint16_t* X, const uint32_t* qw, const uint16_t* sc,
                                  const uint8_t* z, int64_t N, int64_t K, uint16_t* Y,
                                  hipStream_t stream) {
-  const int64_t blocks = (N + WPB * R - 1) / (WPB * R);
-  hipLaunchKernelGGL((k_gemv1<R, U, XR, WPB>), dim3((unsigned)blocks), dim3(WPB * 64),
+  const int64_t waves = GATED ? N / 2 : (N + R - 1) / R;
+  const int64_t blocks = (waves + WPB - 1) / WPB;
+  hipLaunchKernelGGL((k_gemv1<R, U, XR, WPB, GATED>), dim3((unsigned)blocks), dim3(WPB * 64),
                      (size_t)XR * WPB * 64 * 16, stream, X, qw, sc, z, N, K, Y);
   return hipGetLastError();
 }
 
 // K <= 32768: the activation row (K / 8 16-byte entries) fits XR * WPB * 64 entries.
-template <int R, int U, int WPB = 4>
+template <int R, int U, bool GATED, int WPB = 4>
 static hipError_t launch_gemv1(const uint16_t* X, const uint32_t* qw, const uint16_t* sc,
                                const uint8_t* z, int64_t N, int64_t K, uint16_t* Y,
                                hipStream_t stream) {
   const int64_t per_thread = (K / 8 + WPB * 64 - 1) / (WPB * 64);
-  if (per_thread <= 1) return launch_gemv1_x<R, U, 1, WPB>(X, qw, sc, z, N, K, Y, stream);
-  if (per_thread <= 2) return launch_gemv1_x<R, U, 2, WPB>(X, qw, sc, z, N, K, Y, stream);
-  if (per_thread <= 4) return launch_gemv1_x<R, U, 4, WPB>(X, qw, sc, z, N, K, Y, stream);
-  if (per_thread <= 8) return launch_gemv1_x<R, U, 8, WPB>(X, qw, sc, z, N, K, Y, stream);
-  return launch_gemv1_x<R, U, 16, WPB>(X, qw, sc, z, N, K, Y, stream);
+  if (per_thread <= 1) return launch_gemv1_x<R, U, 1, WPB, GATED>(X, qw, sc, z, N, K, Y, stream);
+  if (per_thread <= 2) return launch_gemv1_x<R, U, 2, WPB, GATED>(X, qw, sc, z, N, K, Y, stream);
+  if (per_thread <= 4) return launch_gemv1_x<R, U, 4, WPB, GATED>(X, qw, sc, z, N, K, Y, stream);
+  if (per_thread <= 8) return launch_gemv1_x<R, U, 8, WPB, GATED>(X, qw, sc, z, N, K, Y, stream);
+  return launch_gemv1_x<R, U, 16, WPB, GATED>(X, qw, sc, z, N, K, Y, stream);
 }
 
 // One batch covers K (at most 8 chunks per lane, K <= 16384), so only that path is
@@ -291,17 +317,27 @@ static hipError_t launch_gemv1(const uint16_t* X, const uint32_t* qw, const uint
 // the first is multiplied (tall matrices, where waves otherwise load and then compute in
 // lockstep). Stores are made by every lane with lane 0's sum (no branch); a row index
 // past the matrix end is clamped to the wave's last row, whose value it rewrites.
-template <int U, int XR, int WPB, int RPW>
+template <int U, int XR, int WPB, int RPW, bool GATED>
 __global__ void __launch_bounds__(WPB * 64)
     k_gemv1s(const uint16_t* X, const uint32_t* qweight, const uint16_t* scales,
              const uint8_t* zeros, int64_t N, int64_t K, uint16_t* Y) {
+  static_assert(!GATED || RPW == 2, "a gated wave owns one gate row and one up row");
   extern __shared__ uint4 xs[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int64_t row0 = ((int64_t)blockIdx.x * WPB + (tid >> 6)) * RPW;
+  const int64_t wave_id = (int64_t)blockIdx.x * WPB + (tid >> 6);
   const int64_t C = K / 32, G = K / kGroup, zbytes = (G + 1) / 2, words = K / 8;
+  // plain: rows wave_id * RPW + r, clamped to the wave's last row; gated: gate row n and
+  // up row n + N/2, n clamped to the last output (its store rewrites the same value)
+  const int64_t nh = N / 2;
+  const int64_t n_out = wave_id < nh ? wave_id : nh - 1;
+  const int64_t row0 = GATED ? n_out : wave_id * RPW;
   const int64_t lastrow = row0 + RPW - 1 < N ? row0 + RPW - 1 : N - 1;
-  auto row_at = [&](int r) { const int64_t v = row0 + r; return v < lastrow ? v : lastrow; };
+  auto row_at = [&](int r) -> int64_t {
+    if constexpr (GATED) return n_out + r * nh;
+    const int64_t v = row0 + r;
+    return v < lastrow ? v : lastrow;
+  };
 
   uint4 v[XR];
 #pragma unroll
@@ -325,85 +361,105 @@ __global__ void __launch_bounds__(WPB * 64)
   lds_barrier();
 
   const uint32_t magic = magic_1024x2();
+  float sums[RPW];
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
     float acc[1] = {0.0f};
     gemv1_compute(bt[r], xs, acc, C, 0, lane, magic);
-    const float sum = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_sum(acc[0])), 0));
-    Y[row_at(r)] = f2h_bits(sum);
+    sums[r] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_sum(acc[0])), 0));
+    if constexpr (!GATED) Y[row_at(r)] = f2h_bits(sums[r]);
   }
+  if constexpr (GATED) Y[n_out] = f2h_bits(silu_f32(sums[0]) * sums[RPW - 1]);
 }
 
-template <int U, int XR, int WPB, int RPW>
+template <int U, int XR, int WPB, int RPW, bool GATED>
 static hipError_t launch_gemv1s_x(const uint16_t* X, const uint32_t* qw, const uint16_t* sc,
                                   const uint8_t* z, int64_t N, int64_t K, uint16_t* Y,
                                   hipStream_t stream) {
-  const int64_t blocks = (N + WPB * RPW - 1) / (WPB * RPW);
-  hipLaunchKernelGGL((k_gemv1s<U, XR, WPB, RPW>), dim3((unsigned)blocks), dim3(WPB * 64),
+  const int64_t waves = GATED ? N / 2 : (N + RPW - 1) / RPW;
+  const int64_t blocks = (waves + WPB - 1) / WPB;
+  hipLaunchKernelGGL((k_gemv1s<U, XR, WPB, RPW, GATED>), dim3((unsigned)blocks), dim3(WPB * 64),
                      (size_t)XR * WPB * 64 * 16, stream, X, qw, sc, z, N, K, Y);
   return hipGetLastError();
 }
 
 // XR = U: the activation row (K / 8 entries) fits U * 256 entries, as U = ceil(K / 2048).
-template <int U, int RPW>
+template <int U, int RPW, bool GATED>
 static hipError_t launch_gemv1s(const uint16_t* X, const uint32_t* qw, const uint16_t* sc,
                                 const uint8_t* z, int64_t N, int64_t K, uint16_t* Y,
                                 hipStream_t stream) {
-  return launch_gemv1s_x<U, U, 4, RPW>(X, qw, sc, z, N, K, Y, stream);
+  return launch_gemv1s_x<U, U, 4, RPW, GATED>(X, qw, sc, z, N, K, Y, stream);
 }
 
 // M = 1 dispatch (K <= 32768, so the activation row fits 64 KiB of LDS). Up to eight
 // chunks per lane (K <= 16384): the single-batch kernel, two rows per wave for tall
 // matrices with at most two chunks per lane (measured on the Llama-2 7B shapes), else
-// one. Longer rows: the batched kernel, four chunks per lane per batch.
+// one; gated, always the gate row and the up row. Longer rows: the batched kernel, four
+// chunks per lane per batch.
+template <bool GATED>
 static hipError_t launch_gemv_m1(const uint16_t* X, const uint32_t* qw, const uint16_t* sc,
                                  const uint8_t* z, int64_t N, int64_t K, uint16_t* Y,
                                  hipStream_t stream) {
   const int64_t cpl = (K / 32 + 63) / 64;  // chunks per lane to cover K once
-  const bool tall = N >= 16384;
+  const bool two = GATED || N >= 16384;
   switch (cpl) {
-    case 1: return tall ? launch_gemv1s<1, 2>(X, qw, sc, z, N, K, Y, stream)
-                        : launch_gemv1s<1, 1>(X, qw, sc, z, N, K, Y, stream);
-    case 2: return tall ? launch_gemv1s<2, 2>(X, qw, sc, z, N, K, Y, stream)
-                        : launch_gemv1s<2, 1>(X, qw, sc, z, N, K, Y, stream);
-    case 3: return launch_gemv1s<3, 1>(X, qw, sc, z, N, K, Y, stream);
-    case 4: return launch_gemv1s<4, 1>(X, qw, sc, z, N, K, Y, stream);
-    case 5: return launch_gemv1s<5, 1>(X, qw, sc, z, N, K, Y, stream);
-    case 6: return launch_gemv1s<6, 1>(X, qw, sc, z, N, K, Y, stream);
-    case 7: return launch_gemv1s<7, 1>(X, qw, sc, z, N, K, Y, stream);
-    case 8: return launch_gemv1s<8, 1>(X, qw, sc, z, N, K, Y, stream);
-    default: return launch_gemv1<1, 4>(X, qw, sc, z, N, K, Y, stream);
+    case 1: return two ? launch_gemv1s<1, 2, GATED>(X, qw, sc, z, N, K, Y, stream)
+                       : launch_gemv1s<1, 1, false>(X, qw, sc, z, N, K, Y, stream);
+    case 2: return two ? launch_gemv1s<2, 2, GATED>(X, qw, sc, z, N, K, Y, stream)
+                       : launch_gemv1s<2, 1, false>(X, qw, sc, z, N, K, Y, stream);
+    case 3: return GATED ? launch_gemv1s<3, 2, GATED>(X, qw, sc, z, N, K, Y, stream)
+                         : launch_gemv1s<3, 1, false>(X, qw, sc, z, N, K, Y, stream);
+    case 4: return GATED ? launch_gemv1s<4, 2, GATED>(X, qw, sc, z, N, K, Y, stream)
+                         : launch_gemv1s<4, 1, false>(X, qw, sc, z, N, K, Y, stream);
+    case 5: return GATED ? launch_gemv1s<5, 2, GATED>(X, qw, sc, z, N, K, Y, stream)
+                         : launch_gemv1s<5, 1, false>(X, qw, sc, z, N, K, Y, stream);
+    case 6: return GATED ? launch_gemv1s<6, 2, GATED>(X, qw, sc, z, N, K, Y, stream)
+                         : launch_gemv1s<6, 1, false>(X, qw, sc, z, N, K, Y, stream);
+    case 7: return GATED ? launch_gemv1s<7, 2, GATED>(X, qw, sc, z, N, K, Y, stream)
+                         : launch_gemv1s<7, 1, false>(X, qw, sc, z, N, K, Y, stream);
+    case 8: return GATED ? launch_gemv1s<8, 2, GATED>(X, qw, sc, z, N, K, Y, stream)
+                         : launch_gemv1s<8, 1, false>(X, qw, sc, z, N, K, Y, stream);
+    default: return GATED ? launch_gemv1<2, 4, GATED>(X, qw, sc, z, N, K, Y, stream)
+                          : launch_gemv1<1, 4, false>(X, qw, sc, z, N, K, Y, stream);
   }
 }
 
-template <int M>
+template <int M, bool GATED>
 static hipError_t launch_gemv_m(const uint16_t* X, const uint32_t* qw, const uint16_t* sc,
                                 const uint8_t* z, int64_t N, int64_t K, uint16_t* Y,
                                 hipStream_t stream) {
-  constexpr int R = 4;
-  const int64_t waves = (N + R - 1) / R;
+  constexpr int R = GATED ? 2 : 4;
+  const int64_t waves = GATED ? N / 2 : (N + R - 1) / R;
   const int64_t blocks = (waves + 3) / 4;
-  hipLaunchKernelGGL((k_gemv<M, R>), dim3((unsigned)blocks), dim3(256), 0, stream, X, qw, sc, z,
-                     N, K, Y);
+  hipLaunchKernelGGL((k_gemv<M, R, GATED>), dim3((unsigned)blocks), dim3(256), 0, stream, X, qw,
+                     sc, z, N, K, Y);
   return hipGetLastError();
+}
+
+template <bool GATED>
+static hipError_t launch_gemv_t(const uint16_t* X, int64_t M, const uint32_t* qweight,
+                                const uint16_t* scales, const uint8_t* zeros, int64_t N,
+                                int64_t K, uint16_t* Y, hipStream_t stream) {
+  switch (M) {
+    case 1:
+      if (K <= 32768) return launch_gemv_m1<GATED>(X, qweight, scales, zeros, N, K, Y, stream);
+      return launch_gemv_m<1, GATED>(X, qweight, scales, zeros, N, K, Y, stream);
+    case 2: return launch_gemv_m<2, GATED>(X, qweight, scales, zeros, N, K, Y, stream);
+    case 3: return launch_gemv_m<3, GATED>(X, qweight, scales, zeros, N, K, Y, stream);
+    case 4: return launch_gemv_m<4, GATED>(X, qweight, scales, zeros, N, K, Y, stream);
+    case 5: return launch_gemv_m<5, GATED>(X, qweight, scales, zeros, N, K, Y, stream);
+    case 6: return launch_gemv_m<6, GATED>(X, qweight, scales, zeros, N, K, Y, stream);
+    case 7: return launch_gemv_m<7, GATED>(X, qweight, scales, zeros, N, K, Y, stream);
+    case 8: return launch_gemv_m<8, GATED>(X, qweight, scales, zeros, N, K, Y, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_gemv(const uint16_t* X, int64_t M, const uint32_t* qweight,
                        const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
-                       uint16_t* Y, hipStream_t stream) {
-  switch (M) {
-    case 1:
-      if (K <= 32768) return launch_gemv_m1(X, qweight, scales, zeros, N, K, Y, stream);
-      return launch_gemv_m<1>(X, qweight, scales, zeros, N, K, Y, stream);
-    case 2: return launch_gemv_m<2>(X, qweight, scales, zeros, N, K, Y, stream);
-    case 3: return launch_gemv_m<3>(X, qweight, scales, zeros, N, K, Y, stream);
-    case 4: return launch_gemv_m<4>(X, qweight, scales, zeros, N, K, Y, stream);
-    case 5: return launch_gemv_m<5>(X, qweight, scales, zeros, N, K, Y, stream);
-    case 6: return launch_gemv_m<6>(X, qweight, scales, zeros, N, K, Y, stream);
-    case 7: return launch_gemv_m<7>(X, qweight, scales, zeros, N, K, Y, stream);
-    case 8: return launch_gemv_m<8>(X, qweight, scales, zeros, N, K, Y, stream);
-    default: return hipErrorInvalidValue;
-  }
+                       uint16_t* Y, bool gated, hipStream_t stream) {
+  return gated ? launch_gemv_t<true>(X, M, qweight, scales, zeros, N, K, Y, stream)
+               : launch_gemv_t<false>(X, M, qweight, scales, zeros, N, K, Y, stream);
 }
 
 }  // namespace awq

@@ -37,13 +37,14 @@ hipError_t launch_search_reduce(const double* partials, int n_grid, int64_t n_pa
                                 const uint16_t* s_grid, int64_t K, uint16_t* s_best,
                                 int32_t* best_idx, double* err, hipStream_t stream);
 
-// a7 / a8: Y = X deq(W)^T.
+// a7 / a8: Y = X deq(W)^T. gated (f1): W is gate|up stacked (N/2 rows each) and
+// Y[M][N/2] = SiLU(X deq(W_gate)^T) * (X deq(W_up)^T); N is even.
 hipError_t launch_gemv(const uint16_t* X, int64_t M, const uint32_t* qweight,
                        const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
-                       uint16_t* Y, hipStream_t stream);
+                       uint16_t* Y, bool gated, hipStream_t stream);
 hipError_t launch_gemm(const uint16_t* X, int64_t M, const uint32_t* qweight,
                        const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
-                       uint16_t* Y, hipStream_t stream);
+                       uint16_t* Y, bool gated, hipStream_t stream);
 
 constexpr int kGemvMaxM = 8;
 
