@@ -34,6 +34,8 @@ design notes of the repository):
 * s = (max(mean|x|, 2^-14))^alpha, alpha_i = i / n_grid, i = 0..n_grid-1, s stored as fp16;
 * packed word: channels 0, 2, 4, 6 in the low nibbles of its bytes, 1, 3, 5, 7 in the high;
 * error = sum of squares of X * D^T with D = W - Q(W diag(s)) diag(1/s), ties -> smallest i;
+* the equivalent transform divides the producer of X by s (activations or a norm weight
+  along columns, a previous linear's weight along rows), fp16 correctly rounded;
 * the fused MLP module ([AWQ-SKILL] "主要功能和特点", fused attention/MLP; [AWQ-WIKI]
   TinyChat kernel fusion) is Llama's gated MLP: h = SiLU(x W_gate^T) * (x W_up^T) with
   SiLU(v) = v / (1 + e^-v), gate and up stacked as one packed weight (gate rows first).
@@ -53,6 +55,7 @@ __all__ = [
     "quantize_pack", "dequantize", "NIBBLE_CHANNEL", "search_errors", "search_scales", "linear_reference",
     "linear_within_tolerance", "fp16_midpoint_distance", "relative_gap", "packed_bytes",
     "silu", "SILU_DMAX", "gated_silu_reference", "gated_silu_within_tolerance",
+    "apply_inverse_scale", "FLAG_OVERFLOW",
 ]
 
 GROUP = 128                       # [AWQ-PRACTICE] §2.3; [AWQ-SKILL] q_group_size
@@ -65,6 +68,7 @@ MAX_CALIB_TOKENS = 8192           # keeps the |x| column sums exact in fp64
 
 FLAG_NONFINITE_INPUT = 1
 FLAG_SCALE_CLAMPED = 2
+FLAG_OVERFLOW = 8                 # a finite input whose folded fp16 value is infinite
 
 _F32 = np.float32
 _F64 = np.float64
@@ -297,6 +301,32 @@ def linear_within_tolerance(y, y_ref, bound, rel: float = 2e-3) -> np.ndarray:
     """Per-element check |y - y_ref| <= rel * bound (returns a boolean mask)."""
     y = np.asarray(y, dtype=_F64)
     return np.abs(y - y_ref) <= rel * bound
+
+
+# --------------------------------------------------------------------------- equivalent transform
+def apply_inverse_scale(A16: np.ndarray, s16: np.ndarray, axis: int) -> tuple[np.ndarray, int]:
+    """Fold 1/s into the producer of a linear's input: fp16(A / s), correctly rounded.
+
+    [AWQ-PRACTICE] §2.2: the salient input channels of W are multiplied by s before
+    quantization and the other side is divided by s; [AWQ-WIKI] "工作机制": an equivalent
+    transformation, X W^T = (X diag(1/s)) (W diag(s))^T. The division goes where X is
+    made: the activations themselves or a norm weight (axis 1: A[r][k] / s_k, len(s) =
+    columns), or the rows of the previous linear's weight (axis 0: A[k][j] / s_k,
+    len(s) = rows). Returns (fp16 array, flags); FLAG_OVERFLOW when a finite input
+    becomes infinite, FLAG_NONFINITE_INPUT when A or s holds NaN or inf.
+    """
+    A = np.asarray(A16, dtype=np.float16)
+    s = np.asarray(s16, dtype=np.float16).astype(_F64)
+    sb = s[None, :] if axis == 1 else s[:, None]
+    with np.errstate(over="ignore", divide="ignore", invalid="ignore"):
+        q = A.astype(_F64) / sb      # exact operands; fp64 quotient, then one rounding to fp16
+        out = q.astype(np.float16)
+    flags = 0
+    if not (np.isfinite(A).all() and np.isfinite(s).all()):
+        flags |= FLAG_NONFINITE_INPUT
+    if np.any(np.isfinite(A) & np.isfinite(sb) & ~np.isfinite(out)):
+        flags |= FLAG_OVERFLOW
+    return out, flags
 
 
 # --------------------------------------------------------------------------- fused MLP

@@ -399,3 +399,49 @@ def test_gated_silu_tolerance_covers_linear_errors():
         h2 = (oracle.silu(g2) * u2).astype(np.float16).astype(np.float64)
         assert oracle.gated_silu_within_tolerance(h2, g, u, bg, bu).all()
     assert not oracle.gated_silu_within_tolerance(h * 1.05, g, u, bg, bu).all()
+
+
+# ----------------------------------------------------------------- equivalent transform
+def test_inverse_scale_hand_worked_and_axes():
+    """fp16(A / s): hand-worked quotients (exact, and correctly rounded), both axes."""
+    A = np.array([[1.0, 3.0, -0.5], [6.0, 1.0, 65504.0]], dtype=np.float16)
+    s_cols = np.array([2.0, 3.0, 0.25], dtype=np.float16)
+    out, flags = oracle.apply_inverse_scale(A, s_cols, axis=1)
+    # 1/2 = 0.5, 3/3 = 1, -0.5/0.25 = -2; 6/2 = 3, 1/3 -> fp16 0x3555 (0.333251953125),
+    # 65504/0.25 = 262016 > 65504 -> inf (overflow flagged)
+    assert out[0].tolist() == [0.5, 1.0, -2.0]
+    assert out[1, 0] == 3.0 and out[1, 1].view(np.uint16) == 0x3555 and np.isinf(out[1, 2])
+    assert flags == oracle.FLAG_OVERFLOW
+    s_rows = np.array([4.0, 0.5], dtype=np.float16)
+    out0, f0 = oracle.apply_inverse_scale(A[:, :2], s_rows, axis=0)
+    assert out0.tolist() == [[0.25, 0.75], [12.0, 2.0]] and f0 == 0
+
+
+def test_inverse_scale_is_correctly_rounded():
+    """Against exact rational arithmetic: |fp16 result - a/s| <= half an fp16 ulp, ties even."""
+    rng = np.random.default_rng(3)
+    A = (rng.standard_normal((64, 256)) * 3).astype(np.float16)
+    s = np.exp(rng.uniform(-3, 3, 256)).astype(np.float16)
+    out, _ = oracle.apply_inverse_scale(A, s, axis=1)
+    for r in range(0, 64, 7):
+        for k in range(0, 256, 5):
+            exact = Fraction(float(A[r, k])) / Fraction(float(s[k]))
+            got = Fraction(float(out[r, k]))
+            h = np.float16(out[r, k])
+            ulp = Fraction(float(np.spacing(np.abs(h)))) if h != 0 else Fraction(2) ** -24
+            assert abs(got - exact) <= ulp / 2
+
+
+def test_equivalent_transform_identity_without_quantization():
+    """X W^T = (X diag(1/s)) (W diag(s))^T exactly when s are powers of two."""
+    X = si.activations(4, 256, offset=95)
+    W = si.weights(8, 256, offset=95)
+    s = (2.0 ** np.random.default_rng(4).integers(0, 4, 256)).astype(np.float16)
+    Xs, _ = oracle.apply_inverse_scale(X, s, axis=1)
+    Ws = (W.astype(np.float64) * s.astype(np.float64)).astype(np.float16)
+    lhs = X.astype(np.float64) @ W.astype(np.float64).T
+    rhs = Xs.astype(np.float64) @ Ws.astype(np.float64).T
+    # both sides exact (no fp16 underflow of X / s, W * s stays in range)
+    assert np.all(Xs.astype(np.float64) * s == X.astype(np.float64))
+    assert np.all(Ws.astype(np.float64) / s == W.astype(np.float64))
+    assert np.array_equal(lhs, rhs)
