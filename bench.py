@@ -14,7 +14,10 @@ channels x20, group 128, 4-bit + zero point):
      (they share their input; the fused-module decode of the pages), gate|up with its
      SiLU(gate) * up epilogue (the fused MLP module); the same sweep with one launch
      per matrix (no epilogue) is timed and reported beside it;
-  4. prefill MFMA dequant-GEMM at M = 2048 over the four groups (gate|up fused as in 3).
+  4. prefill MFMA dequant-GEMM at M = 2048 over the four groups (gate|up fused as in 3);
+  5. the equivalent transform's other half: each group's 1/s folded into the producer
+     of its input (norm weights for q|k|v and gate|up, v_proj rows for o, up_proj rows
+     for down).
 Inputs are resident in HBM before the timed region. Each part is captured once in a
 HIP graph (so host launch overhead is not kernel time) and replayed. The K timed steps
 run in phases, part by part (K decode sweeps back to back, then K prefill GEMMs, and so
@@ -200,12 +203,25 @@ def main():
             for name, _, _, N, K in MATRICES:
                 awq.linear_w4a16(xdec[K], views[c][name], out=ydec[name])
 
+    # The equivalent transform's other half: each group's 1/s folded into what produces its
+    # input -- the two norm weights (q|k|v, gate|up), the v_proj rows (o), the up_proj rows
+    # (down) -- out of place, so the search inputs are untouched.
+    norm_w = {g: si.torch_activations(1, 4096, 500 + i, dev) for i, g in enumerate(("qkv", "gate_up"))}
+    fold_jobs = [(norm_w["qkv"], "qkv", 1), (norm_w["gate_up"], "gate_up", 1),
+                 (Wg["qkv"][8192:12288], "o", 0), (Wg["gate_up"][11008:22016], "down", 0)]
+    fold_out = [torch.empty_like(a) for a, _, _ in fold_jobs]
+    fold_bytes = sum(4 * a.numel() + 2 * (a.shape[1] if axis == 1 else a.shape[0]) for a, _, axis in fold_jobs)
+
+    def part_fold():
+        for (a, g, axis), o in zip(fold_jobs, fold_out):
+            awq.apply_inverse_scale(a, sres[g].s_best, axis, out=o)
+
     def part_gemm():
         for g, (N, K) in SEARCH_GROUPS.items():
             linear = awq.linear_w4a16_gated_silu if g in GATED else awq.linear_w4a16
             linear(xpre[K], packed[0][g], out=ypre[g])
 
-    parts = [("search", part_search), ("quant_pack", part_pack), ("gemv", part_gemv),
+    parts = [("search", part_search), ("quant_pack", part_pack), ("fold", part_fold), ("gemv", part_gemv),
              ("gemv_unfused", part_gemv_unfused), ("gemm", part_gemm)]
     stream = torch.cuda.Stream()
     runners = {}
@@ -215,7 +231,7 @@ def main():
         torch.cuda.synchronize()
         eager_ref = {"best": {g: sres[g].best_idx.clone() for g in SEARCH_GROUPS},
                      "y": {n: ydec[n].clone() for n in ydec}, "yf": {g: yfus[g].clone() for g in yfus},
-                     "Y": {g: ypre[g].clone() for g in ypre}}
+                     "Y": {g: ypre[g].clone() for g in ypre}, "fold": [o.clone() for o in fold_out]}
         for pname, fn in parts:
             if args.no_graph:
                 runners[pname] = fn
@@ -231,7 +247,7 @@ def main():
         # loop never follows an 11 ms quantization search, after which the VALU-bound decode
         # kernel runs at a lower clock). Warm-up ends with the decode parts, so the first
         # timed phase follows its own kind of work. One event pair brackets each phase.
-        order = ["gemv", "gemv_unfused", "gemm", "quant_pack", "search"]
+        order = ["gemv", "gemv_unfused", "gemm", "fold", "quant_pack", "search"]
         log(f"bench: warmup {args.warmup} steps")
         for pname in reversed(order):
             for _ in range(args.warmup):
@@ -258,6 +274,8 @@ def main():
             assert torch.equal(ypre[g], eager_ref["Y"][g]), "graph replay differs (gemm)"
         for n in ydec:
             assert torch.equal(ydec[n], eager_ref["y"][n]), "graph replay differs (gemv, per matrix)"
+        for o, e in zip(fold_out, eager_ref["fold"]):
+            assert torch.equal(o, e), "graph replay differs (fold)"
 
     # ------------------------------------------------------------------ figures
     n_gemv = args.layers * len(SEARCH_GROUPS)
@@ -272,6 +290,7 @@ def main():
     search_tflops = search_flops / (part_ms["search"] * 1e-3) / 1e12
     pack_bytes = sum(N * K * 2 + packed_bytes(N, K) for N, K in SEARCH_GROUPS.values())
     pack_gbs = pack_bytes / (part_ms["quant_pack"] * 1e-3) / 1e9
+    fold_gbs = fold_bytes / (part_ms["fold"] * 1e-3) / 1e9
     best = {g: int(sres[g].best_idx.item()) for g in SEARCH_GROUPS}
 
     traffic = load_traffic("gemv_m1")
@@ -310,6 +329,11 @@ def main():
                    "roofline": {"bound": "mfma", "achieved": round(search_tflops, 2),
                                 "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                                 "frac": round(search_tflops / FP16_MFMA_PEAK_TFLOPS, 4)}},
+        "fold_inverse_scale": {"gbs": round(fold_gbs, 2), "ms": round(part_ms["fold"], 4),
+                               "bytes": fold_bytes,
+                               "roofline": {"bound": "hbm", "achieved": round(fold_gbs, 2),
+                                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                            "frac": round(fold_gbs / HBM_PEAK_GBS, 4)}},
         "quant_pack": {"gbs": round(pack_gbs, 2), "ms": round(part_ms["quant_pack"], 4),
                        "roofline": {"bound": "hbm", "achieved": round(pack_gbs, 2), "peak": HBM_PEAK_GBS,
                                     "unit": "GB/s", "frac": round(pack_gbs / HBM_PEAK_GBS, 4)}},

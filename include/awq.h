@@ -62,6 +62,7 @@ typedef struct awq_config {
 #define AWQ_FLAG_NONFINITE_INPUT 1u /* NaN or Inf met in W, s or X (outputs unspecified) */
 #define AWQ_FLAG_SCALE_CLAMPED 2u   /* a group scale above 65504 was clamped to 65504   */
 #define AWQ_FLAG_SEARCH_RANGE 4u    /* a search error term left the fp16 split's range  */
+#define AWQ_FLAG_OVERFLOW 8u        /* a finite value folded by 1/s overflowed fp16      */
 
 #define AWQ_MAX_CALIB_TOKENS 8192
 
@@ -184,6 +185,23 @@ awq_status awq_linear_w4a16_gated_silu_ex(const void* X, int64_t M, const uint32
                                           int64_t K, const awq_config* cfg, void* Y,
                                           uint32_t* flags, awq_linear_kernel kernel,
                                           void* stream);
+
+/*
+ * awq_apply_inverse_scale -- fold 1/s into the producer of a linear's input (the other
+ *   half of the equivalent transform): out = fp16(A / s), correctly rounded.
+ *   [PRACTICE] §2.2 (W's salient channels are multiplied by s, the other side divided by
+ *   s); [WIKI] "工作机制" (equivalent transformation: X W^T = (X diag(1/s)) (W diag(s))^T).
+ *   A, out: fp16 [rows][cols], cols % 8 == 0 (else AWQ_ERR_BAD_SHAPE); out may equal A
+ *   (in place). s: fp16, the scales awq_search_scales chose.
+ *   axis = 1: out[r][k] = A[r][k] / s_k, len(s) = cols -- the activations themselves or
+ *     a norm weight (rows = 1) that produces them;
+ *   axis = 0: out[k][j] = A[k][j] / s_k, len(s) = rows -- the previous linear's weight,
+ *     whose output row k feeds input channel k.
+ *   Any other axis: AWQ_ERR_UNSUPPORTED. flags: AWQ_FLAG_OVERFLOW (a finite value became
+ *   infinite), AWQ_FLAG_NONFINITE_INPUT (NaN or Inf in A or s).
+ */
+awq_status awq_apply_inverse_scale(const void* A, int64_t rows, int64_t cols, const void* s,
+                                   int32_t axis, void* out, uint32_t* flags, void* stream);
 
 /* Largest M served by the GEMV kernel under AWQ_LINEAR_AUTO. */
 int32_t awq_gemv_max_m(void);

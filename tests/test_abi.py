@@ -120,3 +120,12 @@ def test_gated_linear_validation(lib):
     assert call(Y=FAKE_ODD) == 4
     assert lib.awq_linear_w4a16_gated_silu(FAKE, 1, FAKE, FAKE, FAKE, 65, 256, None, FAKE, None,
                                            None) == 2
+
+
+def test_inverse_scale_validation(lib):
+    def call(A=FAKE, rows=4, cols=64, s=FAKE, axis=1, out=FAKE):
+        return lib.awq_apply_inverse_scale(A, rows, cols, s, axis, out, None, None)
+    assert call(A=None) == 1 and call(s=None) == 1 and call(out=None) == 1
+    assert call(axis=2) == 3
+    assert call(cols=12) == 2 and call(rows=0) == 2 and call(cols=0) == 2
+    assert call(out=FAKE_ODD) == 4

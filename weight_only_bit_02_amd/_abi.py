@@ -43,6 +43,7 @@ SIGNATURES = {
     "awq_linear_w4a16_ex": (C.c_int, [P, I64, P, P, P, I64, I64, CFG, P, P, C.c_int, P]),
     "awq_linear_w4a16_gated_silu": (C.c_int, [P, I64, P, P, P, I64, I64, CFG, P, P, P]),
     "awq_linear_w4a16_gated_silu_ex": (C.c_int, [P, I64, P, P, P, I64, I64, CFG, P, P, C.c_int, P]),
+    "awq_apply_inverse_scale": (C.c_int, [P, I64, I64, P, C.c_int32, P, P, P]),
     "awq_gemv_max_m": (C.c_int32, []),
     "awq_status_string": (C.c_char_p, [C.c_int]),
 }

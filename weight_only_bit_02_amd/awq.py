@@ -203,5 +203,28 @@ def linear_w4a16_gated_silu(X: torch.Tensor, w: PackedLinear, kernel: str = "aut
     return Y
 
 
+def apply_inverse_scale(A: torch.Tensor, s: torch.Tensor, axis: int, out: torch.Tensor | None = None,
+                        flags: torch.Tensor | None = None) -> torch.Tensor:
+    """awq_apply_inverse_scale: fp16(A / s) along columns (axis 1, activations or a norm
+    weight) or rows (axis 0, the previous linear's weight); out may be A (in place)."""
+    lib = _abi.load()
+    _need(A, torch.float16, "A")
+    _need(s, torch.float16, "s")
+    A2 = A.reshape(1, -1) if A.dim() == 1 else A
+    if A2.dim() != 2:
+        raise ValueError("A must be 1-D or 2-D")
+    rows, cols = A2.shape
+    if s.numel() != (cols if axis == 1 else rows):
+        raise ValueError("s has the wrong length for this axis")
+    Y = out if out is not None else torch.empty_like(A)
+    _need(Y, torch.float16, "out")
+    if Y.shape != A.shape:
+        raise ValueError("out has the wrong shape")
+    _abi.check("awq_apply_inverse_scale", lib.awq_apply_inverse_scale(
+        _ptr(A), rows, cols, _ptr(s), axis, _ptr(Y), _ptr(flags) if flags is not None else None,
+        _stream()))
+    return Y
+
+
 def gemv_max_m() -> int:
     return int(_abi.load().awq_gemv_max_m())

@@ -226,4 +226,16 @@ awq_status awq_linear_w4a16_gated_silu(const void* X, int64_t M, const uint32_t*
                                         AWQ_LINEAR_AUTO, stream);
 }
 
+awq_status awq_apply_inverse_scale(const void* A, int64_t rows, int64_t cols, const void* s,
+                                   int32_t axis, void* out, uint32_t* flags, void* stream) {
+  if (!A || !s || !out) return AWQ_ERR_NULL_POINTER;
+  if (axis != 0 && axis != 1) return AWQ_ERR_UNSUPPORTED;
+  if (rows < 1 || cols < 8 || cols % 8 != 0 || rows >= kMaxDim || cols >= kMaxDim)
+    return AWQ_ERR_BAD_SHAPE;
+  if (!aligned16(A) || !aligned16(s) || !aligned16(out) || (flags && !aligned4(flags)))
+    return AWQ_ERR_MISALIGNED;
+  return hip_status(awq::launch_inverse_scale((const uint16_t*)A, rows, cols, (const uint16_t*)s,
+                                              axis, (uint16_t*)out, flags, (hipStream_t)stream));
+}
+
 }  // extern "C"

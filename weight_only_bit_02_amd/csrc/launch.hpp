@@ -46,6 +46,11 @@ hipError_t launch_gemm(const uint16_t* X, int64_t M, const uint32_t* qweight,
                        const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
                        uint16_t* Y, bool gated, hipStream_t stream);
 
+// f2: out = fp16(A / s) along columns (axis 1, len(s) = cols) or rows (axis 0,
+// len(s) = rows); cols % 8 == 0; out may alias A.
+hipError_t launch_inverse_scale(const uint16_t* A, int64_t rows, int64_t cols, const uint16_t* s,
+                                int axis, uint16_t* out, uint32_t* flags, hipStream_t stream);
+
 constexpr int kGemvMaxM = 8;
 
 }  // namespace awq
