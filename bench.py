@@ -78,6 +78,32 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
+def crossover(awq, packed, dev, stream, ms=(1, 2, 4, 8, 16, 32, 64), reps=20):
+    """GEMV vs GEMM time (us) over the four 7B groups per M (one launch per group, events
+    around `reps` back-to-back sweeps): the data behind the M <= awq_gemv_max_m dispatch."""
+    import torch
+    out = {"M": list(ms), "gemv_us": [], "skinny_us": [], "gemm_us": [], "gemv_max_m": awq.gemv_max_m()}
+    for M in ms:
+        X = {K: torch.randn((M, K), device=dev).half() for K in (4096, 11008)}
+        for kern, key in (("gemv", "gemv_us"), ("skinny", "skinny_us"), ("gemm", "gemm_us")):
+            if (kern == "gemv" and M > 8) or (kern == "skinny" and M > 32):
+                out[key].append(None)
+                continue
+            with torch.cuda.stream(stream):
+                def sweep():
+                    for g, p in packed.items():
+                        awq.linear_w4a16(X[p.K], p, kernel=kern)
+                sweep()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for _ in range(reps):
+                    sweep()
+                b.record(stream)
+            b.synchronize()
+            out[key].append(round(a.elapsed_time(b) * 1e3 / reps, 2))
+    return out
+
+
 def cpu_baseline(budget_s: float = 15.0):
     """The CPU oracle's W4A16 linear at M = 1 on the 7B matrices, bounded to ~budget_s."""
     import numpy as np
@@ -343,6 +369,7 @@ def main():
                             "avg_launch_us": round(part_ms["gemv_unfused"] * 1e3 / n_gemv_u, 3)},
         "source_hash": source_hash(),
     }
+    result["crossover"] = crossover(awq, packed[0], dev, stream)
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle (bounded sample)")
         result["cpu_baseline"] = cpu_baseline()

@@ -51,6 +51,13 @@ def test_gated_gemv_long_rows_and_tall(nh, K):
     _check(si.activations(1, K, offset=nh), p, ref, "gemv")
 
 
+@pytest.mark.parametrize("M", [1, 5, 8, 16, 17, 32])
+@pytest.mark.parametrize("nh,K", [(1, 128), (67, 384), (200, 1152), (40, 11008)])
+def test_gated_skinny_matches_oracle(M, nh, K):
+    p, ref = _gated_case(nh, K, off=nh + 17 * K)
+    _check(si.activations(M, K, offset=M + 500), p, ref, "skinny")
+
+
 @pytest.mark.parametrize("M", [1, 9, 64, 130, 257])
 @pytest.mark.parametrize("nh,K", [(1, 128), (67, 384), (200, 1152)])
 def test_gated_gemm_matches_oracle(M, nh, K):

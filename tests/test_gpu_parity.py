@@ -189,6 +189,15 @@ def test_gemv_matches_oracle(M, N, K):
     _check_linear(si.activations(M, K, offset=M), p, ref, "gemv")
 
 
+@pytest.mark.parametrize("M", [1, 2, 3, 7, 8, 9, 16, 17, 31, 32])
+@pytest.mark.parametrize("N,K", [(1, 128), (67, 384), (256, 4096), (130, 11008), (33, 1152)])
+def test_skinny_matches_oracle(M, N, K):
+    """Small-batch MFMA GEMV: every accumulator bucket (M <= 8, 16, 32), ragged N, K
+    splits that leave some waves without a group (K = 128) or uneven (K = 1152)."""
+    p, ref = _packed_case(N, K, off=N + 13 * K)
+    _check_linear(si.activations(M, K, offset=M + 400), p, ref, "skinny")
+
+
 @pytest.mark.parametrize("M", [1, 8, 9, 16, 63, 64, 65, 130, 257])
 @pytest.mark.parametrize("N,K", [(1, 128), (67, 384), (256, 4096), (130, 1152)])
 def test_gemm_matches_oracle(M, N, K):
@@ -218,13 +227,19 @@ def test_linear_zero_input(kernel):
 
 
 def test_linear_auto_dispatch_and_determinism():
+    """AUTO picks the vector GEMV up to M = 3, the skinny MFMA GEMV up to 32, the GEMM above
+    (each result equals its explicit kernel's bit for bit), deterministically."""
     p, ref = _packed_case(300, 1024, off=63)
-    X = si.activations(24, 1024, offset=63)
-    for M in (1, 8, 9, 24):
+    X = si.activations(40, 1024, offset=63)
+    assert awq.gemv_max_m() == 32
+    for M, kern in ((1, "gemv"), (3, "gemv"), (4, "skinny"), (8, "skinny"), (32, "skinny"),
+                    (33, "gemm"), (40, "gemm")):
         Xm = X[:M]
         a = host(awq.linear_w4a16(to_dev(Xm), p))
         b = host(awq.linear_w4a16(to_dev(Xm), p))
+        e = host(awq.linear_w4a16(to_dev(Xm), p, kernel=kern))
         assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+        assert np.array_equal(a.view(np.uint16), e.view(np.uint16)), (M, kern)
         y_ref, bound = oracle.linear_reference(Xm, *ref, 1024)
         assert oracle.linear_within_tolerance(a.astype(np.float64), y_ref, bound).all()
 

@@ -19,7 +19,7 @@ FLAG_NONFINITE_INPUT = 1
 FLAG_SCALE_CLAMPED = 2
 FLAG_SEARCH_RANGE = 4
 
-KERNEL_AUTO, KERNEL_GEMV, KERNEL_GEMM = 0, 1, 2
+KERNEL_AUTO, KERNEL_GEMV, KERNEL_GEMM, KERNEL_SKINNY = 0, 1, 2, 3
 
 
 class AwqConfig(C.Structure):

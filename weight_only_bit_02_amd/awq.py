@@ -159,7 +159,8 @@ def search_scales(X: torch.Tensor, W: torch.Tensor, n_grid: int = 20,
     return out
 
 
-_KERNELS = {"auto": _abi.KERNEL_AUTO, "gemv": _abi.KERNEL_GEMV, "gemm": _abi.KERNEL_GEMM}
+_KERNELS = {"auto": _abi.KERNEL_AUTO, "gemv": _abi.KERNEL_GEMV, "gemm": _abi.KERNEL_GEMM,
+            "skinny": _abi.KERNEL_SKINNY}
 
 
 def linear_w4a16(X: torch.Tensor, w: PackedLinear, kernel: str = "auto",

@@ -19,7 +19,7 @@ LIB_DIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIB_DIR, "libawq_mi355x.so")
 
 SOURCES = ["awq_abi.hip", "quant_pack.hip", "stats.hip", "search.hip", "gemv.hip", "gemm.hip",
-           "fold.hip"]
+           "fold.hip", "gemv_mfma.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -52,15 +52,16 @@ SearchLayout search_layout(int64_t T, int64_t N, int64_t K, int n_grid) {
   return L;
 }
 
+// Largest M that AWQ_LINEAR_AUTO serves with a GEMV-class kernel (above it, the MFMA
+// GEMM); AWQ_GEMV_MAX_M overrides it (0 .. 32) to measure the crossover.
 int gemv_max_m_from_env() {
   const char* e = getenv("AWQ_GEMV_MAX_M");
-  if (!e) return awq::kGemvMaxM;
+  if (!e) return awq::kSkinnyMaxM;
   int v = atoi(e);
   if (v < 0) v = 0;
-  if (v > awq::kGemvMaxM) v = awq::kGemvMaxM;
+  if (v > awq::kSkinnyMaxM) v = awq::kSkinnyMaxM;
   return v;
 }
-
 const int g_gemv_max_m = gemv_max_m_from_env();
 
 }  // namespace
@@ -179,19 +180,32 @@ static awq_status linear_common(const void* X, int64_t M, const uint32_t* qweigh
   if (!supported(c)) return AWQ_ERR_UNSUPPORTED;
   if (M < 1 || M >= kMaxDim || !good_nk(N, K)) return AWQ_ERR_BAD_SHAPE;
   if (gated && (N < 2 || N % 2 != 0)) return AWQ_ERR_BAD_SHAPE;
-  if (kernel != AWQ_LINEAR_AUTO && kernel != AWQ_LINEAR_GEMV && kernel != AWQ_LINEAR_GEMM)
+  if (kernel != AWQ_LINEAR_AUTO && kernel != AWQ_LINEAR_GEMV && kernel != AWQ_LINEAR_GEMM &&
+      kernel != AWQ_LINEAR_SKINNY)
     return AWQ_ERR_UNSUPPORTED;
   if (kernel == AWQ_LINEAR_GEMV && M > awq::kGemvMaxM) return AWQ_ERR_BAD_SHAPE;
+  if (kernel == AWQ_LINEAR_SKINNY && M > awq::kSkinnyMaxM) return AWQ_ERR_BAD_SHAPE;
   if (!aligned16(X) || !aligned16(qweight) || !aligned16(scales) || !aligned16(zeros) ||
       !aligned16(Y))
     return AWQ_ERR_MISALIGNED;
-  const bool gemv = kernel == AWQ_LINEAR_GEMV || (kernel == AWQ_LINEAR_AUTO && M <= g_gemv_max_m);
+  // AUTO, measured on the Llama-2-7B layer: the vector-ALU GEMV up to M = 3 (its dot cost
+  // grows with M), the MFMA skinny GEMV up to g_gemv_max_m, the MFMA GEMM above.
+  if (kernel == AWQ_LINEAR_AUTO)
+    kernel = M <= awq::kVgemvAutoMaxM && M <= g_gemv_max_m ? AWQ_LINEAR_GEMV
+             : M <= g_gemv_max_m                            ? AWQ_LINEAR_SKINNY
+                                                            : AWQ_LINEAR_GEMM;
   hipStream_t st = (hipStream_t)stream;
   const auto* Xh = (const uint16_t*)X;
   const auto* sc = (const uint16_t*)scales;
   auto* Yh = (uint16_t*)Y;
-  return hip_status(gemv ? awq::launch_gemv(Xh, M, qweight, sc, zeros, N, K, Yh, gated, st)
-                         : awq::launch_gemm(Xh, M, qweight, sc, zeros, N, K, Yh, gated, st));
+  switch (kernel) {
+    case AWQ_LINEAR_GEMV:
+      return hip_status(awq::launch_gemv(Xh, M, qweight, sc, zeros, N, K, Yh, gated, st));
+    case AWQ_LINEAR_SKINNY:
+      return hip_status(awq::launch_gemv_mfma(Xh, M, qweight, sc, zeros, N, K, Yh, gated, st));
+    default:
+      return hip_status(awq::launch_gemm(Xh, M, qweight, sc, zeros, N, K, Yh, gated, st));
+  }
 }
 
 awq_status awq_linear_w4a16_ex(const void* X, int64_t M, const uint32_t* qweight,

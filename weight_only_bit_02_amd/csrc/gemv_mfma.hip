@@ -1,0 +1,192 @@
+// Skinny MFMA GEMV for small batches (a7 / a9): Y[M][N] = X[M][K] deq(W)^T for M <= 32.
+//
+// "AWQ量化实战" §3.4: decode is memory-bound, so the packed weights are streamed once and
+// dequantized on the fly; "AWQ量化技术Skill", "主要功能和特点": a GEMV kernel serves the
+// small batches of token generation.
+//
+// With more than one token, dot products on the vector ALU cost one v_dot2 per channel
+// pair per token; here they go to the matrix cores instead, so the vector work per byte
+// of codes (the exact widening to q - z) does not grow with M:
+//   - a wave owns 32 weight rows (the 32 columns of a v_mfma_f32_32x32x16_f16 tile) and
+//     a slice of the K groups; lane l works on row l % 32 and, h = l / 32, on channels
+//     [32 h, 32 h + 32) and [64 + 32 h, 96 + 32 h) of each group (two 16-byte code loads
+//     per group; lanes l and l + 32 read 32 contiguous bytes of the row together);
+//   - word s of those 64 channels is the lane's B operand of k16 step s, widened exactly
+//     to (q - z) in fp16 (0x6400 trick, packed fp16 add); the A operand is the 16 bytes
+//     of X at the same channels for token l % 32 (rows past M repeat row M - 1 and are
+//     never stored), read straight from global memory (X is tiny and stays in cache);
+//   - the 8 MFMAs of a group start from zero, and the group scale multiplies that partial
+//     tile in fp32 (one FMA per element), as in the M = 1 kernel;
+//   - the S waves of a block split K and meet in LDS at the end, where wave 0 adds the S
+//     partial tiles in a fixed order: results do not depend on scheduling.
+// Loads of group g + 1 are in flight while group g is multiplied (two register stages
+// used alternately in a loop unrolled by two, so no register copy waits for them).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace awq {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+namespace {
+
+struct SkinnyStage {
+  uint4 b[2];     // 8 packed words: channels 32 h + [0, 32) and 64 + 32 h + [0, 32), row l % 32
+  uint4 a[8];     // X[token][same channels], one 16-byte piece per k16 step
+  uint32_t sc, zb;
+};
+
+__device__ __forceinline__ uint32_t skinny_magic() {
+  uint32_t m;
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(m));
+  return m;
+}
+
+// One packed word -> its 8 channels as exact fp16 (q - z), in channel order.
+__device__ __forceinline__ half8 widen_word(uint32_t w, half2v zz, uint32_t magic) {
+  half2v d[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p)
+    d[p] = __builtin_bit_cast(half2v, ((w >> (4 * p)) & 0x000F000Fu) | magic) + zz;
+  return half8{d[0][0], d[0][1], d[1][0], d[1][1], d[2][0], d[2][1], d[3][0], d[3][1]};
+}
+
+}  // namespace
+
+// E = accumulator elements kept per lane: rows 8 (e / 4) + 4 h + e % 4 of the 32 x 32 tile;
+// E = 4 serves M <= 8, 8 serves M <= 16, 16 serves M <= 32.
+template <int S, int E, bool GATED>
+__global__ void __launch_bounds__(S * 64)
+    k_gemv_mfma(const uint16_t* X, int64_t M, const uint32_t* qweight, const uint16_t* scales,
+                const uint8_t* zeros, int64_t N, int64_t K, uint16_t* Y) {
+  __shared__ float red[S][E][64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int j = lane & 31, h = lane >> 5;
+  const int64_t G = K / kGroup, zbytes = (G + 1) / 2, words = K / 8;
+  // rows of this tile: plain, 32 consecutive rows; gated, 16 gate rows then their 16 up
+  // rows (tile columns j and j + 16 hold g and u of output n0 + j)
+  const int64_t nh = N / 2;
+  int64_t n;
+  if constexpr (GATED) {
+    const int64_t o = (int64_t)blockIdx.x * 16 + (j & 15);
+    n = (o < nh ? o : nh - 1) + (j >> 4) * nh;
+  } else {
+    const int64_t o = (int64_t)blockIdx.x * 32 + j;
+    n = o < N ? o : N - 1;
+  }
+  const int64_t xrow = (j < M ? j : M - 1) * K;
+  // this wave's groups: an even split of the G groups over the S waves
+  const int64_t g0 = G * wave / S, g1 = G * (wave + 1) / S;
+  const uint32_t magic = skinny_magic();
+
+  auto load = [&](SkinnyStage& st, int64_t g) {
+    st.zb = zeros[n * zbytes + (g >> 1)];
+    st.sc = scales[n * G + g];
+    const uint32_t* cp = qweight + n * words + g * 16 + h * 4;
+    st.b[0] = *reinterpret_cast<const uint4*>(cp);
+    st.b[1] = *reinterpret_cast<const uint4*>(cp + 8);
+    // word s (k16 step s) covers channels 8 s' + 32 h + 64 (s / 4), s' = s % 4
+    const uint16_t* xp = X + xrow + g * kGroup + h * 32;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) st.a[s] = *reinterpret_cast<const uint4*>(xp + (s & 3) * 8 + (s >> 2) * 64);
+  };
+
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.0f;
+
+  auto body = [&](const SkinnyStage& st, int64_t g) {
+    const uint32_t z = (g & 1) ? (st.zb >> 4) & 0xF : st.zb & 0xF;
+    const uint32_t zbits = 0x6400u + z;
+    const half2v zz = -__builtin_bit_cast(half2v, zbits | (zbits << 16));
+    const uint32_t wd[8] = {st.b[0].x, st.b[0].y, st.b[0].z, st.b[0].w,
+                            st.b[1].x, st.b[1].y, st.b[1].z, st.b[1].w};
+    f32x16 d = f32x16{};
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      d = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, st.a[s]),
+                                                 widen_word(wd[s], zz, magic), d, 0, 0, 0);
+    const float scf = h2f((uint16_t)st.sc);
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(scf, d[e], acc[e]);
+  };
+
+  if (g1 > g0) {
+    SkinnyStage s0, s1;
+    load(s0, g0);
+    int64_t g = g0;
+    for (; g + 2 <= g1; g += 2) {
+      load(s1, g + 1);
+      body(s0, g);
+      load(s0, g + 2 < g1 ? g + 2 : g1 - 1);  // always issued: exact waits on every path
+      body(s1, g + 1);
+    }
+    if (g < g1) body(s0, g);
+  }
+
+  // fixed-order reduction of the S partial tiles
+#pragma unroll
+  for (int e = 0; e < E; ++e) red[wave][e][lane] = acc[e];
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    float v = red[0][e][lane];
+#pragma unroll
+    for (int w = 1; w < S; ++w) v += red[w][e][lane];
+    acc[e] = v;
+  }
+  // 32x32 accumulator layout: element e of lane l is (row 8(e/4) + 4(l/32) + e%4, col l%32)
+  if constexpr (GATED) {
+    // up partner of column j (< 16) is column j + 16, held by lane + 16 for the same rows
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float u = __shfl_down(acc[e], 16, 32);
+      const int64_t o = (int64_t)blockIdx.x * 16 + j;
+      const int64_t i = 8 * (e >> 2) + 4 * h + (e & 3);
+      if (j < 16 && o < nh && i < M) Y[i * nh + o] = f2h_bits(silu_f32(acc[e]) * u);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int64_t o = (int64_t)blockIdx.x * 32 + j;
+      const int64_t i = 8 * (e >> 2) + 4 * h + (e & 3);
+      if (o < N && i < M) Y[i * N + o] = f2h_bits(acc[e]);
+    }
+  }
+}
+
+template <int S, int E, bool GATED>
+static hipError_t launch_skinny_x(const uint16_t* X, int64_t M, const uint32_t* qw,
+                                  const uint16_t* sc, const uint8_t* z, int64_t N, int64_t K,
+                                  uint16_t* Y, hipStream_t stream) {
+  const int64_t outs = GATED ? N / 2 : N;
+  const int64_t per = GATED ? 16 : 32;
+  const int64_t blocks = (outs + per - 1) / per;
+  hipLaunchKernelGGL((k_gemv_mfma<S, E, GATED>), dim3((unsigned)blocks), dim3(S * 64), 0, stream,
+                     X, M, qw, sc, z, N, K, Y);
+  return hipGetLastError();
+}
+
+template <bool GATED>
+static hipError_t launch_skinny_t(const uint16_t* X, int64_t M, const uint32_t* qw,
+                                  const uint16_t* sc, const uint8_t* z, int64_t N, int64_t K,
+                                  uint16_t* Y, hipStream_t stream) {
+  if (M <= 8) return launch_skinny_x<8, 4, GATED>(X, M, qw, sc, z, N, K, Y, stream);
+  if (M <= 16) return launch_skinny_x<8, 8, GATED>(X, M, qw, sc, z, N, K, Y, stream);
+  return launch_skinny_x<8, 16, GATED>(X, M, qw, sc, z, N, K, Y, stream);
+}
+
+hipError_t launch_gemv_mfma(const uint16_t* X, int64_t M, const uint32_t* qweight,
+                            const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
+                            uint16_t* Y, bool gated, hipStream_t stream) {
+  if (M < 1 || M > kSkinnyMaxM) return hipErrorInvalidValue;
+  return gated ? launch_skinny_t<true>(X, M, qweight, scales, zeros, N, K, Y, stream)
+               : launch_skinny_t<false>(X, M, qweight, scales, zeros, N, K, Y, stream);
+}
+
+}  // namespace awq

@@ -51,6 +51,13 @@ hipError_t launch_gemm(const uint16_t* X, int64_t M, const uint32_t* qweight,
 hipError_t launch_inverse_scale(const uint16_t* A, int64_t rows, int64_t cols, const uint16_t* s,
                                 int axis, uint16_t* out, uint32_t* flags, hipStream_t stream);
 
-constexpr int kGemvMaxM = 8;
+// a7 / a9 for small batches: 32-row MFMA tiles, K split over the waves of a block.
+constexpr int kSkinnyMaxM = 32;
+hipError_t launch_gemv_mfma(const uint16_t* X, int64_t M, const uint32_t* qweight,
+                            const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
+                            uint16_t* Y, bool gated, hipStream_t stream);
+
+constexpr int kGemvMaxM = 8;       // the vector-ALU GEMV serves M <= 8 when asked for
+constexpr int kVgemvAutoMaxM = 3;  // and is the automatic choice up to M = 3
 
 }  // namespace awq
