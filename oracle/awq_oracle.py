@@ -34,6 +34,9 @@ design notes of the repository):
 * s = (max(mean|x|, 2^-14))^alpha, alpha_i = i / n_grid, i = 0..n_grid-1, s stored as fp16;
 * packed word: channels 0, 2, 4, 6 in the low nibbles of its bytes, 1, 3, 5, 7 in the high;
 * error = sum of squares of X * D^T with D = W - Q(W diag(s)) diag(1/s), ties -> smallest i;
+* weight clipping: per group, ratios r_i = (clip_steps - i) / clip_steps, i < n_shrink
+  (default 200 and 100), shrink the group's min/max; score = the group's own output
+  contribution error; first minimum;
 * the equivalent transform divides the producer of X by s (activations or a norm weight
   along columns, a previous linear's weight along rows), fp16 correctly rounded;
 * the fused MLP module ([AWQ-SKILL] "主要功能和特点", fused attention/MLP; [AWQ-WIKI]
@@ -56,6 +59,7 @@ __all__ = [
     "linear_within_tolerance", "fp16_midpoint_distance", "relative_gap", "packed_bytes",
     "silu", "SILU_DMAX", "gated_silu_reference", "gated_silu_within_tolerance",
     "apply_inverse_scale", "FLAG_OVERFLOW",
+    "CLIP_STEPS", "clip_ratios", "clip_errors", "clip_search",
 ]
 
 GROUP = 128                       # [AWQ-PRACTICE] §2.3; [AWQ-SKILL] q_group_size
@@ -119,7 +123,7 @@ def candidate_scales(a: np.ndarray, n_grid: int = N_GRID) -> tuple[np.ndarray, n
 
 
 # --------------------------------------------------------------------------- a3
-def quantize_groups(W16: np.ndarray, s16: np.ndarray | None = None) -> dict:
+def quantize_groups(W16: np.ndarray, s16: np.ndarray | None = None, clip_ratio: np.ndarray | None = None) -> dict:
     """Group-wise asymmetric 4-bit quantization of W * diag(s).
 
     [AWQ-PRACTICE] §2.3 (128 consecutive input channels share one step) and §2.1
@@ -135,6 +139,9 @@ def quantize_groups(W16: np.ndarray, s16: np.ndarray | None = None) -> dict:
       5. sc_h = fp16(sc)                        (the stored scale)
       6. z = clamp(rint(-mn / f32(sc_h)), 0, 15)
       7. q = clamp(rint(w' / f32(sc_h)) + z, 0, 15)
+    With ``clip_ratio`` (fp32 [N][G], the weight-clipping search), step 2 is followed by
+    mx = f32(r mx), mn = f32(r mn): the group's range shrinks toward 0 by r and the
+    weights beyond it take the end codes through the clamp of step 7.
     Returns dict(q uint8 [N][K], z uint8 [N][G], scale fp16 [N][G], flags int).
     """
     W16 = np.asarray(W16)
@@ -153,6 +160,11 @@ def quantize_groups(W16: np.ndarray, s16: np.ndarray | None = None) -> dict:
     wg = w.reshape(N, G, GROUP)
     mx = wg.max(axis=2)
     mn = wg.min(axis=2)
+    if clip_ratio is not None:
+        r = np.asarray(clip_ratio, dtype=_F32)
+        assert r.shape == (N, G)
+        mx = (r * mx).astype(_F32)
+        mn = (r * mn).astype(_F32)
     sc = (mx - mn) / _F32(QMAX)
     sc = np.maximum(sc, SCALE_FLOOR)
     if np.any(sc > SCALE_MAX):
@@ -210,9 +222,9 @@ def unpack(qweight: np.ndarray, scales: np.ndarray, zeros: np.ndarray, K: int):
     return q, z, np.asarray(scales, dtype=np.float16)
 
 
-def quantize_pack(W16: np.ndarray, s16: np.ndarray | None = None):
+def quantize_pack(W16: np.ndarray, s16: np.ndarray | None = None, clip_ratio: np.ndarray | None = None):
     """a3 + a4: returns (qweight, scales, zeros, flags)."""
-    r = quantize_groups(W16, s16)
+    r = quantize_groups(W16, s16, clip_ratio)
     qweight, scales, zeros = pack(r["q"], r["z"], r["scale"])
     return qweight, scales, zeros, r["flags"]
 
@@ -281,6 +293,61 @@ def search_scales(X16: np.ndarray, W16: np.ndarray, n_grid: int = N_GRID) -> dic
     r.update(best_idx=best, s_best=s_best, qweight=qweight, scales=scales, zeros=zeros,
              gap=relative_gap(err), flags=r["flags"] | f)
     return r
+
+
+# --------------------------------------------------------------------------- weight clipping
+CLIP_STEPS = 200  # the clip_steps value the nxmr.cn page suggests
+
+
+def clip_ratios(clip_steps: int = CLIP_STEPS, n_shrink: int = CLIP_STEPS // 2) -> np.ndarray:
+    """Shrink ratios of the clipping grid: r_i = f32((clip_steps - i) / clip_steps),
+    i = 0 .. n_shrink - 1 (r_0 = 1 is plain min/max quantization)."""
+    assert 1 <= n_shrink <= clip_steps
+    return np.array([(clip_steps - i) / clip_steps for i in range(n_shrink)], dtype=_F64).astype(_F32)
+
+
+def clip_errors(X16: np.ndarray, W16: np.ndarray, s16: np.ndarray | None = None,
+                clip_steps: int = CLIP_STEPS, n_shrink: int = CLIP_STEPS // 2) -> np.ndarray:
+    """Per-group output error of every shrink ratio, fp64 [n_shrink][N][G].
+
+    Weight-clipping search ("AWQ量化实战 ... nxmr.cn" §5.1: tune clip_steps, 200
+    suggested, against accuracy loss). Reading: after the scale search, every group
+    (row n, group g) of W diag(s) tries the ratios r_i of clip_ratios(), quantized with its
+    range shrunk by r_i (quantize_groups' clip_ratio); the score is that group's own
+    contribution to the calibration outputs,
+        err[i, n, g] = sum_t ( sum_{k in g} X_tk D_nk )^2,  D = W - Q_r(W diag(s)) diag(1/s).
+    """
+    N, K = W16.shape
+    G = K // GROUP
+    Xd = X16.astype(_F64)
+    Wd = W16.astype(_F64)
+    ratios = clip_ratios(clip_steps, n_shrink)
+    err = np.empty((n_shrink, N, G), dtype=_F64)
+    for i, r in enumerate(ratios):
+        qz = quantize_groups(W16, s16, np.full((N, G), r, dtype=_F32))
+        D = Wd - dequantize(qz["q"], qz["z"], qz["scale"], s16)
+        for g in range(G):
+            E = Xd[:, g * GROUP:(g + 1) * GROUP] @ D[:, g * GROUP:(g + 1) * GROUP].T
+            err[i, :, g] = np.sum(E * E, axis=0)
+    return err
+
+
+def clip_search(X16: np.ndarray, W16: np.ndarray, s16: np.ndarray | None = None,
+                clip_steps: int = CLIP_STEPS, n_shrink: int = CLIP_STEPS // 2) -> dict:
+    """Per group, the first ratio index with the smallest error, and the weight packed
+    with those ratios. Returns dict(idx uint8 [N][G], ratio fp32 [N][G], err fp64
+    [n_shrink][N][G], qweight, scales, zeros, flags)."""
+    err = clip_errors(X16, W16, s16, clip_steps, n_shrink)
+    idx = np.zeros(err.shape[1:], dtype=np.int64)
+    best = err[0].copy()
+    for i in range(1, n_shrink):
+        better = err[i] < best
+        idx[better] = i
+        best[better] = err[i][better]
+    ratio = clip_ratios(clip_steps, n_shrink)[idx]
+    qweight, scales, zeros, flags = quantize_pack(W16, s16, ratio)
+    return {"idx": idx.astype(np.uint8), "ratio": ratio, "err": err, "qweight": qweight,
+            "scales": scales, "zeros": zeros, "flags": flags}
 
 
 # --------------------------------------------------------------------------- a7/a8

@@ -70,12 +70,13 @@ def check_codes_nearest(w_scaled: np.ndarray, q: np.ndarray, z: np.ndarray, scal
     return bad
 
 
-def check_scale_zero(w_scaled: np.ndarray, z: np.ndarray, scale: np.ndarray) -> list:
+def check_scale_zero(w_scaled: np.ndarray, z: np.ndarray, scale: np.ndarray, ratio=None) -> list:
     """P2: closed form of the scale and the zero point from the group's extremes.
 
     sc_h must be the fp16 rounding of (mx - mn)/15 up to the fp32 roundings on the
-    way (a relative 2^-23 window), floored at 2^-14; z in [0, 15]; when the zero is
-    not clamped, -z*sc_h lies within sc_h/2 of mn.
+    way (a relative 2^-22 window), floored at 2^-14; z in [0, 15]; when the zero is
+    not clamped, -z*sc_h lies within sc_h/2 of mn. With ``ratio`` ([N][G], weight
+    clipping) the extremes are r mx and r mn.
     """
     bad = []
     N, K = w_scaled.shape
@@ -83,6 +84,9 @@ def check_scale_zero(w_scaled: np.ndarray, z: np.ndarray, scale: np.ndarray) -> 
         for j in range(K // GROUP):
             g = w_scaled[n, j * GROUP:(j + 1) * GROUP]
             mx, mn = frac(g.max()), frac(g.min())
+            if ratio is not None:
+                r = frac(ratio[n, j])
+                mx, mn = r * mx, r * mn
             exact = max((mx - mn) / 15, Fraction(2) ** -14)
             lo_ = rne_fp16(exact * (1 - Fraction(1, 2 ** 22)))
             hi_ = rne_fp16(exact * (1 + Fraction(1, 2 ** 22)))
@@ -115,3 +119,26 @@ def exact_search_error(X16: np.ndarray, W16: np.ndarray, s16: np.ndarray, q, z, 
             e = sum((frac(X16[t, k]) * D[k] for k in range(K)), Fraction(0))
             total += e * e
     return total
+
+
+def exact_group_errors(X16: np.ndarray, W16: np.ndarray, s16, q, z, scale) -> list:
+    """Weight clipping: err[n][g] = sum_t (sum_{k in g} X_tk D_nk)^2, D = W - (q - z) sc / s,
+    exactly (s16 None means s = 1)."""
+    T, K = X16.shape
+    N = W16.shape[0]
+    out = []
+    for n in range(N):
+        row = []
+        for j in range(K // GROUP):
+            ks = range(j * GROUP, (j + 1) * GROUP)
+            D = {}
+            for k in ks:
+                sk = frac(s16[k]) if s16 is not None else Fraction(1)
+                D[k] = frac(W16[n, k]) - (int(q[n, k]) - int(z[n, j])) * frac(scale[n, j]) / sk
+            tot = Fraction(0)
+            for t in range(T):
+                e = sum((frac(X16[t, k]) * D[k] for k in ks), Fraction(0))
+                tot += e * e
+            row.append(tot)
+        out.append(row)
+    return out

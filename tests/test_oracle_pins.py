@@ -445,3 +445,80 @@ def test_equivalent_transform_identity_without_quantization():
     assert np.all(Xs.astype(np.float64) * s == X.astype(np.float64))
     assert np.all(Ws.astype(np.float64) / s == W.astype(np.float64))
     assert np.array_equal(lhs, rhs)
+
+
+# ----------------------------------------------------------------- weight clipping
+def test_clip_grid_and_ratio_one_is_plain_quantization():
+    """r_i = (200 - i) / 200 in fp32; a one-point grid (r = 1) packs exactly as without clipping."""
+    r = oracle.clip_ratios(200, 100)
+    assert r[0] == 1.0 and r[1] == np.float32(0.995) and r[-1] == np.float32(0.505)
+    assert np.all(np.diff(r.astype(np.float64)) < 0)
+    X = si.activations(16, 256, offset=110)
+    W = si.weights(6, 256, offset=110)
+    a, _ = oracle.activation_mean_abs(X)
+    s = oracle.candidate_scales(a, 20)[1][7]
+    c = oracle.clip_search(X, W, s, 200, 1)
+    qw, sc, zb, _ = oracle.quantize_pack(W, s)
+    assert np.all(c["idx"] == 0)
+    assert np.array_equal(c["qweight"], qw) and np.array_equal(c["zeros"], zb)
+    assert np.array_equal(c["scales"].view(np.uint16), sc.view(np.uint16))
+
+
+def test_clipped_codes_nearest_and_ranges():
+    """Shrunk ranges: codes are the nearest in the clipped grid (weights beyond it take the
+    end codes), and scale / zero follow the closed form on r mx, r mn."""
+    W = si.weights(4, 256, offset=111)
+    s = np.exp(np.random.default_rng(6).uniform(-1, 1, 256)).astype(np.float16)
+    ratio = oracle.clip_ratios(200, 100)[np.random.default_rng(7).integers(0, 100, (4, 2))]
+    qz = oracle.quantize_groups(W, s, ratio)
+    w = W.astype(np.float32) * s.astype(np.float32)
+    assert not pins.check_codes_nearest(w, qz["q"], qz["z"], qz["scale"])
+    assert not pins.check_scale_zero(w, qz["z"], qz["scale"], ratio)
+    # mutant: the range shrunk from the top only
+    mx_only = oracle.quantize_groups(W, s, None)
+    assert pins.check_scale_zero(w, mx_only["z"], mx_only["scale"], ratio)
+
+
+def test_clip_errors_exact_and_separable():
+    """Per-group errors against exact rational arithmetic; a change in one group leaves the
+    other group's errors untouched; the choice is the first minimum."""
+    X = si.activations(3, 256, offset=112)
+    W = si.weights(2, 256, offset=112)
+    s = np.exp(np.random.default_rng(8).uniform(-0.5, 0.5, 256)).astype(np.float16)
+    err = oracle.clip_errors(X, W, s, 200, 5)
+    for i, r in enumerate(oracle.clip_ratios(200, 5)):
+        qz = oracle.quantize_groups(W, s, np.full((2, 2), r, dtype=np.float32))
+        ex = pins.exact_group_errors(X, W, s, qz["q"], qz["z"], qz["scale"])
+        for n in range(2):
+            for g in range(2):
+                assert abs(err[i, n, g] - float(ex[n][g])) <= 1e-12 * float(ex[n][g])
+    W2 = W.copy()
+    W2[:, 128:] = si.weights(2, 128, offset=113)
+    err2 = oracle.clip_errors(X, W2, s, 200, 5)
+    assert np.array_equal(err2[:, :, 0], err[:, :, 0]) and not np.array_equal(err2[:, :, 1], err[:, :, 1])
+    c = oracle.clip_search(X, W, s, 200, 5)
+    for n in range(2):
+        for g in range(2):
+            e = err[:, n, g]
+            assert c["idx"][n, g] == int(np.flatnonzero(e == e.min())[0])
+
+
+def test_clipping_an_outlier_the_tokens_never_see():
+    """Worked case: weights spread over [0.0024, 0.3] plus one outlier at 1.5 on a channel the
+    calibration tokens leave at zero. Min/max puts the step at (1.5 - 0.0024)/15 ~ 0.1; at the
+    grid's smallest ratio 0.505 the range is both ends times 0.505 and the step half as large,
+    so the weights the tokens use are rounded about twice as finely (squared error about a
+    quarter) while the clipped outlier costs nothing; the search keeps the smallest error."""
+    W = (np.arange(128) * (0.3 / 127)).astype(np.float16)[None, :]
+    W[0, 0] = 1.5
+    X = si.activations(4, 128, offset=114)
+    X[:, 0] = 0
+    err = oracle.clip_errors(X, W, None, 200, 100)[:, 0, 0]
+    w1 = float(W[0, 1])
+    qz0 = oracle.quantize_groups(W, None, np.ones((1, 1), np.float32))
+    qz1 = oracle.quantize_groups(W, None, np.full((1, 1), 0.505, np.float32))
+    assert float(qz0["scale"][0, 0]) == pytest.approx((1.5 - w1) / 15, rel=2 ** -10)  # fp16 step
+    assert float(qz1["scale"][0, 0]) == pytest.approx(0.505 * (1.5 - w1) / 15, rel=2 ** -10)
+    assert qz0["z"][0, 0] == 0 and qz1["z"][0, 0] == 0 and qz1["q"][0, 0] == 15
+    assert err[-1] < err[0] / 3
+    assert oracle.clip_search(X, W, None, 200, 100)["idx"][0, 0] == int(np.argmin(err))
