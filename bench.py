@@ -15,7 +15,9 @@ channels x20, group 128, 4-bit + zero point):
      SiLU(gate) * up epilogue (the fused MLP module); the same sweep with one launch
      per matrix (no epilogue) is timed and reported beside it;
   4. prefill MFMA dequant-GEMM at M = 2048 over the four groups (gate|up fused as in 3);
-  5. the equivalent transform's other half: each group's 1/s folded into the producer
+  5. weight clipping after the scale search: 20 shrink ratios per group (r = 1 .. 0.905
+     on the clip_steps = 200 grid) of each group's W diag(s);
+  6. the equivalent transform's other half: each group's 1/s folded into the producer
      of its input (norm weights for q|k|v and gate|up, v_proj rows for o, up_proj rows
      for down).
 Inputs are resident in HBM before the timed region. Each part is captured once in a
@@ -238,6 +240,18 @@ def main():
     fold_out = [torch.empty_like(a) for a, _, _ in fold_jobs]
     fold_bytes = sum(4 * a.numel() + 2 * (a.shape[1] if axis == 1 else a.shape[0]) for a, _, axis in fold_jobs)
 
+    # Weight clipping after the scale search: 20 shrink ratios (r = 1 .. 0.905 on the
+    # clip_steps = 200 grid) per group of each group's W diag(s).
+    CLIP_SHRINK = 20
+    clip_ws = {g: torch.empty(awq.load_library().awq_clip_search_workspace_size(CALIB_T, N, K, CLIP_SHRINK),
+                              dtype=torch.uint8, device=dev) for g, (N, K) in SEARCH_GROUPS.items()}
+    clip_out = {}
+
+    def part_clip():
+        for g in SEARCH_GROUPS:
+            clip_out[g] = awq.clip_search(Xcal[g], Wg[g], sres[g].s_best, 200, CLIP_SHRINK,
+                                          workspace=clip_ws[g])
+
     def part_fold():
         for (a, g, axis), o in zip(fold_jobs, fold_out):
             awq.apply_inverse_scale(a, sres[g].s_best, axis, out=o)
@@ -247,7 +261,8 @@ def main():
             linear = awq.linear_w4a16_gated_silu if g in GATED else awq.linear_w4a16
             linear(xpre[K], packed[0][g], out=ypre[g])
 
-    parts = [("search", part_search), ("quant_pack", part_pack), ("fold", part_fold), ("gemv", part_gemv),
+    parts = [("search", part_search), ("clip", part_clip), ("quant_pack", part_pack), ("fold", part_fold),
+             ("gemv", part_gemv),
              ("gemv_unfused", part_gemv_unfused), ("gemm", part_gemm)]
     stream = torch.cuda.Stream()
     runners = {}
@@ -273,7 +288,7 @@ def main():
         # loop never follows an 11 ms quantization search, after which the VALU-bound decode
         # kernel runs at a lower clock). Warm-up ends with the decode parts, so the first
         # timed phase follows its own kind of work. One event pair brackets each phase.
-        order = ["gemv", "gemv_unfused", "gemm", "fold", "quant_pack", "search"]
+        order = ["gemv", "gemv_unfused", "gemm", "fold", "quant_pack", "search", "clip"]
         log(f"bench: warmup {args.warmup} steps")
         for pname in reversed(order):
             for _ in range(args.warmup):
@@ -317,6 +332,8 @@ def main():
     pack_bytes = sum(N * K * 2 + packed_bytes(N, K) for N, K in SEARCH_GROUPS.values())
     pack_gbs = pack_bytes / (part_ms["quant_pack"] * 1e-3) / 1e9
     fold_gbs = fold_bytes / (part_ms["fold"] * 1e-3) / 1e9
+    clip_flops = sum(2 * CALIB_T * N * K * CLIP_SHRINK for N, K in SEARCH_GROUPS.values())
+    clip_tflops = clip_flops / (part_ms["clip"] * 1e-3) / 1e12
     best = {g: int(sres[g].best_idx.item()) for g in SEARCH_GROUPS}
 
     traffic = load_traffic("gemv_m1")
@@ -355,6 +372,11 @@ def main():
                    "roofline": {"bound": "mfma", "achieved": round(search_tflops, 2),
                                 "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                                 "frac": round(search_tflops / FP16_MFMA_PEAK_TFLOPS, 4)}},
+        "clip_search": {"tflops_algorithmic": round(clip_tflops, 2), "ms": round(part_ms["clip"], 4),
+                        "ratios": CLIP_SHRINK, "clip_steps": 200,
+                        "roofline": {"bound": "mfma", "achieved": round(clip_tflops, 2),
+                                     "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                     "frac": round(clip_tflops / FP16_MFMA_PEAK_TFLOPS, 4)}},
         "fold_inverse_scale": {"gbs": round(fold_gbs, 2), "ms": round(part_ms["fold"], 4),
                                "bytes": fold_bytes,
                                "roofline": {"bound": "hbm", "achieved": round(fold_gbs, 2),

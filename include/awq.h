@@ -12,6 +12,7 @@
  *   "AWQ量化技术Skill" (skillsbot.cn, awq-quantization usage page)  -- [SKILL]
  *   "大模型量化部署实战：GPTQ与AWQ算法" (yunthe.com)                 -- [GPTQ-AWQ]
  *   "什么是激活感知权重量化（AWQ）" (aiboss88.com)                   -- [WIKI]
+ *   "AWQ技术概述：重新定义大语言模型量化" (nxmr.cn, untitled; its first heading) -- [NXMR]
  *
  * Conventions shared by every entry point
  *   - Every tensor pointer is a DEVICE pointer owned by the caller. The library never
@@ -190,6 +191,39 @@ awq_status awq_linear_w4a16_gated_silu_ex(const void* X, int64_t M, const uint32
                                           int64_t K, const awq_config* cfg, void* Y,
                                           uint32_t* flags, awq_linear_kernel kernel,
                                           void* stream);
+
+/*
+ * awq_clip_search -- weight clipping: per group, the shrink of its quantization range
+ *   that best preserves its share of the calibration outputs.
+ *   [NXMR] §5.1 "精度下降严重" (tune clip_steps, 200 suggested, when accuracy drops).
+ *   Reading: with s fixed (the scale search's choice; NULL = 1), group (n, g) of W diag(s)
+ *   tries r_i = (clip_steps - i) / clip_steps, i = 0 .. n_shrink - 1 (r_0 = 1: plain
+ *   min/max), quantized from the extremes r_i max and r_i min (fp32), scored by
+ *     err_i(n, g) = sum_t ( sum_{k in g} X_tk D_nk )^2,  D = W - Q_{r_i}(W diag(s)) diag(1/s),
+ *   and keeps the first minimum. Contraction and its accuracy as in awq_search_scales.
+ *   X fp16 [T][K], 1 <= T <= 512 (else AWQ_ERR_BAD_SHAPE: one block scores all tokens);
+ *   W fp16 [N][K]; s fp16 [K] or NULL; 1 <= n_shrink <= min(clip_steps, 256).
+ *   clip_idx uint8 [N][K/128] out (pass to awq_quantize_pack_clipped); err fp64 [N][K/128]
+ *   out, the chosen error, or NULL. workspace: device, awq_clip_search_workspace_size
+ *   bytes (n_shrink N K/128 doubles plus N + 1 floats), 16-byte aligned.
+ */
+size_t awq_clip_search_workspace_size(int64_t T, int64_t N, int64_t K, int32_t n_shrink);
+awq_status awq_clip_search(const void* X, int64_t T, const void* W, int64_t N, int64_t K,
+                           const void* s, int32_t clip_steps, int32_t n_shrink,
+                           const awq_config* cfg, uint8_t* clip_idx, double* err,
+                           void* workspace, size_t workspace_bytes, uint32_t* flags,
+                           void* stream);
+
+/*
+ * awq_quantize_pack_clipped -- awq_quantize_pack with per-group clipping: group (n, g)
+ *   quantizes from its extremes times r = (clip_steps - clip_idx[n][g]) / clip_steps
+ *   (fp32); weights beyond the shrunk range take the end codes. clip_idx uint8 [N][K/128]
+ *   (awq_clip_search's output) or NULL (plain awq_quantize_pack); 1 <= clip_steps <= 65535.
+ */
+awq_status awq_quantize_pack_clipped(const void* W, int64_t N, int64_t K, const void* s,
+                                     const uint8_t* clip_idx, int32_t clip_steps,
+                                     const awq_config* cfg, uint32_t* qweight, void* scales,
+                                     uint8_t* zeros, uint32_t* flags, void* stream);
 
 /*
  * awq_apply_inverse_scale -- fold 1/s into the producer of a linear's input (the other

@@ -19,6 +19,8 @@ Sources (web pages; cited by title and section):
 * [GPTQ-VS-AWQ] "大模型量化部署实战：GPTQ与AWQ算法" (yunthe.com), section
   "大模型量化的核心原理与位宽选择": a 4-bit integer plus a scale and a zero point
   for dequantization; per-group (128) quantization.
+* [NXMR] the nxmr.cn article (no title; first heading "AWQ技术概述：重新定义大语言模型
+  量化"), §5.1 "精度下降严重": tune clip_steps (200 suggested) against accuracy loss.
 * [AWQ-WIKI] "什么是激活感知权重量化（AWQ）" (aiboss88.com), section "工作机制":
   the protection is an equivalent transformation whose scale comes from offline
   activation statistics; no backpropagation or reconstruction.
@@ -296,7 +298,7 @@ def search_scales(X16: np.ndarray, W16: np.ndarray, n_grid: int = N_GRID) -> dic
 
 
 # --------------------------------------------------------------------------- weight clipping
-CLIP_STEPS = 200  # the clip_steps value the nxmr.cn page suggests
+CLIP_STEPS = 200  # [NXMR] §5.1: the suggested clip_steps
 
 
 def clip_ratios(clip_steps: int = CLIP_STEPS, n_shrink: int = CLIP_STEPS // 2) -> np.ndarray:
@@ -310,8 +312,8 @@ def clip_errors(X16: np.ndarray, W16: np.ndarray, s16: np.ndarray | None = None,
                 clip_steps: int = CLIP_STEPS, n_shrink: int = CLIP_STEPS // 2) -> np.ndarray:
     """Per-group output error of every shrink ratio, fp64 [n_shrink][N][G].
 
-    Weight-clipping search ("AWQ量化实战 ... nxmr.cn" §5.1: tune clip_steps, 200
-    suggested, against accuracy loss). Reading: after the scale search, every group
+    Weight-clipping search ([NXMR] §5.1 "精度下降严重": tune clip_steps, 200 suggested,
+    against accuracy loss). Reading: after the scale search, every group
     (row n, group g) of W diag(s) tries the ratios r_i of clip_ratios(), quantized with its
     range shrunk by r_i (quantize_groups' clip_ratio); the score is that group's own
     contribution to the calibration outputs,

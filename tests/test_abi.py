@@ -130,3 +130,19 @@ def test_inverse_scale_validation(lib):
     assert call(axis=2) == 3
     assert call(cols=12) == 2 and call(rows=0) == 2 and call(cols=0) == 2
     assert call(out=FAKE_ODD) == 4
+
+
+def test_clip_validation(lib):
+    WS = C.c_size_t(1 << 20)
+
+    def call(X=FAKE, T=64, N=64, K=256, steps=200, ns=20, idx=FAKE, ws=FAKE, wsb=WS):
+        return lib.awq_clip_search(X, T, FAKE, N, K, None, steps, ns, None, idx, None, ws, wsb,
+                                   None, None)
+    assert call(X=None) == 1 and call(idx=None) == 1
+    assert call(T=513) == 2 and call(T=0) == 2 and call(K=130) == 2
+    assert call(ns=201) == 2 and call(ns=257, steps=300) == 2 and call(ns=0) == 2
+    assert call(ws=None) == 5 and call(wsb=C.c_size_t(16)) == 5
+    need = lib.awq_clip_search_workspace_size(64, 64, 256, 20)
+    assert need >= 20 * 64 * 2 * 8
+    assert lib.awq_quantize_pack_clipped(FAKE, 64, 256, None, FAKE, 0, None, FAKE, FAKE, FAKE,
+                                         None, None) == 2

@@ -5,6 +5,6 @@ search, and the W4A16 linear, as hand-written HIP kernels behind a small C ABI
 from ._abi import AwqError, load as load_library  # noqa: F401
 from .awq import (  # noqa: F401
     PackedLinear, SearchResult, SearchWorkspace, activation_stats, alloc_packed, apply_inverse_scale,
-    candidate_scales, gemv_max_m, linear_w4a16, linear_w4a16_gated_silu, quantize_pack,
+    candidate_scales, clip_search, gemv_max_m, linear_w4a16, linear_w4a16_gated_silu, quantize_pack,
     search_scales,
 )

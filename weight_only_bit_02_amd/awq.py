@@ -59,8 +59,10 @@ def alloc_packed(N: int, K: int, device) -> PackedLinear:
 
 
 def quantize_pack(W: torch.Tensor, s: torch.Tensor | None = None, flags: torch.Tensor | None = None,
-                  out: PackedLinear | None = None) -> PackedLinear:
-    """awq_quantize_pack: 4-bit group-128 quantization of W * diag(s) (s = None: plain RTN)."""
+                  out: PackedLinear | None = None, clip_idx: torch.Tensor | None = None,
+                  clip_steps: int = 200) -> PackedLinear:
+    """awq_quantize_pack: 4-bit group-128 quantization of W * diag(s) (s = None: plain RTN);
+    with clip_idx (uint8 [N][K/128], clip_search's output), awq_quantize_pack_clipped."""
     lib = _abi.load()
     _need(W, torch.float16, "W")
     if W.dim() != 2:
@@ -79,10 +81,40 @@ def quantize_pack(W: torch.Tensor, s: torch.Tensor | None = None, flags: torch.T
     if p.N != N or p.K != K:
         raise ValueError("output packed buffers have the wrong shape")
     cfg = _abi.config()
-    _abi.check("awq_quantize_pack", lib.awq_quantize_pack(
-        _ptr(W), N, K, _ptr(s), C.byref(cfg), _ptr(p.qweight), _ptr(p.scales), _ptr(p.zeros),
-        _ptr(flags), _stream()))
+    if clip_idx is not None:
+        _need(clip_idx, torch.uint8, "clip_idx")
+        if clip_idx.shape != (N, K // 128):
+            raise ValueError("clip_idx must be [N][K/128]")
+    _abi.check("awq_quantize_pack_clipped", lib.awq_quantize_pack_clipped(
+        _ptr(W), N, K, _ptr(s), _ptr(clip_idx), clip_steps, C.byref(cfg), _ptr(p.qweight),
+        _ptr(p.scales), _ptr(p.zeros), _ptr(flags), _stream()))
     return p
+
+
+def clip_search(X: torch.Tensor, W: torch.Tensor, s: torch.Tensor | None = None,
+                clip_steps: int = 200, n_shrink: int = 100, flags: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None):
+    """awq_clip_search: per group, the index of the best shrink ratio (uint8 [N][K/128]) and
+    its error (fp64 [N][K/128]); ratio r_i = (clip_steps - i) / clip_steps, i < n_shrink."""
+    lib = _abi.load()
+    _need(X, torch.float16, "X")
+    _need(W, torch.float16, "W")
+    T, K = X.shape
+    N = W.shape[0]
+    if W.shape[1] != K:
+        raise ValueError("X and W disagree on K")
+    if s is not None:
+        _need(s, torch.float16, "s")
+    nbytes = int(lib.awq_clip_search_workspace_size(T, N, K, n_shrink))
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=X.device)
+    idx = torch.empty((N, K // 128), dtype=torch.uint8, device=X.device)
+    err = torch.empty((N, K // 128), dtype=torch.float64, device=X.device)
+    cfg = _abi.config()
+    _abi.check("awq_clip_search", lib.awq_clip_search(
+        _ptr(X), T, _ptr(W), N, K, _ptr(s), clip_steps, n_shrink, C.byref(cfg), _ptr(idx),
+        _ptr(err), _ptr(workspace), workspace.numel(), _ptr(flags), _stream()))
+    return idx, err
 
 
 def activation_stats(X: torch.Tensor, flags: torch.Tensor | None = None) -> torch.Tensor:

@@ -52,6 +52,20 @@ SearchLayout search_layout(int64_t T, int64_t N, int64_t K, int n_grid) {
   return L;
 }
 
+// Clip-search workspace: [rowmax: f32 N][srange: f32 1][err: fp64 n_shrink x N x G]
+struct ClipLayout {
+  size_t rowmax, srange, err, total;
+};
+
+ClipLayout clip_layout(int64_t N, int64_t K, int n_shrink) {
+  ClipLayout L;
+  L.rowmax = 0;
+  L.srange = align256((size_t)N * 4);
+  L.err = align256(L.srange + 4);
+  L.total = align256(L.err + (size_t)n_shrink * N * (K / 128) * 8);
+  return L;
+}
+
 // Largest M that AWQ_LINEAR_AUTO serves with a GEMV-class kernel (above it, the MFMA
 // GEMM); AWQ_GEMV_MAX_M overrides it (0 .. 32) to measure the crossover.
 int gemv_max_m_from_env() {
@@ -86,15 +100,25 @@ int32_t awq_gemv_max_m(void) { return g_gemv_max_m; }
 awq_status awq_quantize_pack(const void* W, int64_t N, int64_t K, const void* s,
                              const awq_config* cfg, uint32_t* qweight, void* scales,
                              uint8_t* zeros, uint32_t* flags, void* stream) {
+  return awq_quantize_pack_clipped(W, N, K, s, nullptr, 0, cfg, qweight, scales, zeros, flags,
+                                   stream);
+}
+
+awq_status awq_quantize_pack_clipped(const void* W, int64_t N, int64_t K, const void* s,
+                                     const uint8_t* clip_idx, int32_t clip_steps,
+                                     const awq_config* cfg, uint32_t* qweight, void* scales,
+                                     uint8_t* zeros, uint32_t* flags, void* stream) {
   const awq_config c = resolve(cfg);
   if (!W || !qweight || !scales || !zeros) return AWQ_ERR_NULL_POINTER;
   if (!supported(c)) return AWQ_ERR_UNSUPPORTED;
   if (!good_nk(N, K)) return AWQ_ERR_BAD_SHAPE;
+  if (clip_idx && (clip_steps < 1 || clip_steps > 65535)) return AWQ_ERR_BAD_SHAPE;
   if (!aligned16(W) || !aligned16(qweight) || !aligned16(scales) || !aligned16(zeros) ||
       (s && !aligned16(s)) || (flags && !aligned4(flags)))
     return AWQ_ERR_MISALIGNED;
   return hip_status(awq::launch_quant_pack((const uint16_t*)W, N, K, (const uint16_t*)s, qweight,
-                                           (uint16_t*)scales, zeros, flags, (hipStream_t)stream));
+                                           (uint16_t*)scales, zeros, clip_idx, clip_steps, flags,
+                                           (hipStream_t)stream));
 }
 
 size_t awq_activation_stats_workspace_size(int64_t T, int64_t K) {
@@ -238,6 +262,40 @@ awq_status awq_linear_w4a16_gated_silu(const void* X, int64_t M, const uint32_t*
                                        uint32_t* flags, void* stream) {
   return awq_linear_w4a16_gated_silu_ex(X, M, qweight, scales, zeros, N, K, cfg, Y, flags,
                                         AWQ_LINEAR_AUTO, stream);
+}
+
+size_t awq_clip_search_workspace_size(int64_t T, int64_t N, int64_t K, int32_t n_shrink) {
+  (void)T;
+  if (!good_nk(N, K) || n_shrink < 1) return 0;
+  return clip_layout(N, K, n_shrink).total;
+}
+
+awq_status awq_clip_search(const void* X, int64_t T, const void* W, int64_t N, int64_t K,
+                           const void* s, int32_t clip_steps, int32_t n_shrink,
+                           const awq_config* cfg, uint8_t* clip_idx, double* err,
+                           void* workspace, size_t workspace_bytes, uint32_t* flags,
+                           void* stream) {
+  const awq_config c = resolve(cfg);
+  if (!X || !W || !clip_idx) return AWQ_ERR_NULL_POINTER;
+  if (!supported(c)) return AWQ_ERR_UNSUPPORTED;
+  if (T < 1 || T > awq::kClipMaxTokens || !good_nk(N, K)) return AWQ_ERR_BAD_SHAPE;
+  if (clip_steps < 1 || clip_steps > 65535 || n_shrink < 1 || n_shrink > clip_steps ||
+      n_shrink > awq::kClipMaxShrink)
+    return AWQ_ERR_BAD_SHAPE;
+  if (!aligned16(X) || !aligned16(W) || (s && !aligned16(s)) || (err && !aligned16(err)) ||
+      (flags && !aligned4(flags)))
+    return AWQ_ERR_MISALIGNED;
+  const ClipLayout L = clip_layout(N, K, n_shrink);
+  if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return AWQ_ERR_WORKSPACE;
+  char* ws = (char*)workspace;
+  hipStream_t st = (hipStream_t)stream;
+  double* errs = (double*)(ws + L.err);
+  hipError_t e = awq::launch_clip_err((const uint16_t*)X, T, (const uint16_t*)W, N, K,
+                                      (const uint16_t*)s, clip_steps, n_shrink,
+                                      (float*)(ws + L.rowmax), (float*)(ws + L.srange), errs, flags, st);
+  if (e == hipSuccess)
+    e = awq::launch_clip_reduce(errs, n_shrink, N, K / 128, clip_idx, err, st);
+  return hip_status(e);
 }
 
 awq_status awq_apply_inverse_scale(const void* A, int64_t rows, int64_t cols, const void* s,

@@ -151,6 +151,12 @@ __device__ __forceinline__ int64_t f16_abs_units(uint16_t h) {
   return (int64_t)(1024 + m) << (e - 1);
 }
 
+// Shrink ratio of the weight-clipping grid: r_i = (steps - i) / steps, the correctly
+// rounded fp32 quotient of two exact integers.
+__device__ __forceinline__ float clip_ratio(int i, int steps) {
+  return (float)(steps - i) / (float)steps;
+}
+
 // SiLU(v) = v / (1 + e^-v) in fp32, the activation of the fused gate|up epilogue, with
 // the hardware exponential and reciprocal (relative error about 1e-6 for |v| <= 20, far
 // below the result's fp16 rounding); large negative v: e^-v = inf, rcp(inf) = 0, -0.

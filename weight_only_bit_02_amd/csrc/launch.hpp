@@ -9,9 +9,22 @@
 namespace awq {
 
 // a3 + a4: quantize W * diag(s) per group of 128 and pack codes / scales / zeros.
+// clip_idx (nullable, [N][G]): group (n, j) shrinks its range by (steps - idx) / steps.
 hipError_t launch_quant_pack(const uint16_t* W, int64_t N, int64_t K, const uint16_t* s,
                              uint32_t* qweight, uint16_t* scales, uint8_t* zeros,
-                             uint32_t* flags, hipStream_t stream);
+                             const uint8_t* clip_idx, int clip_steps, uint32_t* flags,
+                             hipStream_t stream);
+
+// f3: err[i][n][g] = sum_t (sum_{k in g} X_tk D_nk)^2 for the clip ratios i < n_shrink
+// (T <= 512), then the first minimum per (n, g).
+hipError_t launch_clip_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N,
+                           int64_t K, const uint16_t* s, int clip_steps, int n_shrink,
+                           float* rowmax, float* srange, double* err, uint32_t* flags,
+                           hipStream_t stream);
+hipError_t launch_clip_reduce(const double* err, int n_shrink, int64_t N, int64_t G,
+                              uint8_t* clip_idx, double* err_best, hipStream_t stream);
+constexpr int kClipMaxTokens = 512;
+constexpr int kClipMaxShrink = 256;
 
 // a1: u_k = sum_t |X_tk| in units of 2^-24 (int64, exact), then a_k = u_k 2^-24 / T.
 hipError_t launch_zero_u64(unsigned long long* p, int64_t n, hipStream_t stream);

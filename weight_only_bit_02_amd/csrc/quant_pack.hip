@@ -7,7 +7,9 @@
 // Mapping: a wave owns one (row, run of 4 groups) unit = 512 input channels. Lane l
 // reads 8 consecutive weights (one 16-byte load) and writes the 32-bit word that packs
 // their 8 codes (channel i of the word in nibble kNibbleOf[i]), so loads and stores are fully coalesced; the 16 lanes of a DPP row
-// form one group and find its min / max with row-local DPP.
+// form one group and find its min / max with row-local DPP. With clip indices (the
+// weight-clipping search), group (n, j) shrinks its extremes by r = clip_ratio(idx, steps)
+// before the quantizer sees them.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -18,6 +20,8 @@ __global__ void __launch_bounds__(256) k_quant_pack(const uint16_t* __restrict__
                                                     uint32_t* __restrict__ qweight,
                                                     uint16_t* __restrict__ scales,
                                                     uint8_t* __restrict__ zeros,
+                                                    const uint8_t* __restrict__ clip_idx,
+                                                    int clip_steps,
                                                     uint32_t* __restrict__ flags) {
   const int lane = threadIdx.x & 63;
   const int gi = lane >> 4;  // group within the unit
@@ -58,6 +62,11 @@ __global__ void __launch_bounds__(256) k_quant_pack(const uint16_t* __restrict__
       mx = fmaxf(mx, w[i]);
     }
     row16_minmax(mn, mx);
+    if (clip_idx && valid) {
+      const float r = clip_ratio(clip_idx[n * G + j], clip_steps);
+      mn = r * mn;
+      mx = r * mx;
+    }
     const GroupQ g = group_params(mn, mx);
     uint32_t word = 0;
 #pragma unroll
@@ -82,11 +91,12 @@ __global__ void __launch_bounds__(256) k_quant_pack(const uint16_t* __restrict__
 
 hipError_t launch_quant_pack(const uint16_t* W, int64_t N, int64_t K, const uint16_t* s,
                              uint32_t* qweight, uint16_t* scales, uint8_t* zeros,
-                             uint32_t* flags, hipStream_t stream) {
+                             const uint8_t* clip_idx, int clip_steps, uint32_t* flags,
+                             hipStream_t stream) {
   const int64_t units = N * ((K / kGroup + 3) / 4);
   const int64_t blocks = units / 4 + 1 < 16384 ? units / 4 + 1 : 16384;
   hipLaunchKernelGGL(k_quant_pack, dim3((unsigned)blocks), dim3(256), 0, stream, W, N, K, s,
-                     qweight, scales, zeros, flags);
+                     qweight, scales, zeros, clip_idx, clip_steps, flags);
   return hipGetLastError();
 }
 

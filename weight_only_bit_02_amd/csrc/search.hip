@@ -20,6 +20,14 @@
 // partial; a second kernel adds the partials of each grid point in a fixed order and
 // takes the first minimum. No floating-point atomics: results are bitwise
 // reproducible.
+//
+// Weight clipping (f3; the nxmr.cn article "AWQ技术概述：重新定义大语言模型量化", §5.1
+// "精度下降严重", names clip_steps, 200 suggested): with s fixed, every
+// group tries the shrink ratios r_i = (steps - i) / steps of its range, scored by its own
+// output contribution err[i][n][g] = sum_t (sum_{k in g} X_tk D_nk)^2. A block owns
+// (ratio i, 128 rows, all T <= 512 tokens); the same tile quantizer (extremes times r)
+// feeds the same MFMA contraction, but each group's accumulator starts from zero and is
+// squared on its own, and the waves' per-row partials meet in LDS every group.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -95,6 +103,79 @@ __global__ void __launch_bounds__(256) k_scale_range(const uint16_t* __restrict_
   }
 }
 
+// Quantizes group j of the 128-row tile starting at row n0 into LDS as (D P) split into
+// fp16 hi + lo, D = W - Q(W diag(s)) diag(1/s) (s == nullptr: s = 1). With CLIP the
+// group's extremes are shrunk by r before the quantizer sees them (weight clipping).
+// 16 lanes per (row, group), 8 weights each; returns whether a non-finite value was met.
+template <int NW, bool CLIP>
+__device__ __forceinline__ bool quantize_tile_group(const uint16_t* W, int64_t N, int64_t K,
+                                                    const uint16_t* s, float r, int64_t n0,
+                                                    int64_t j, const float* lds_p, uint16_t* hi_buf,
+                                                    uint16_t* lo_buf, int tid) {
+  constexpr int kRowsPerPass = NW * 4;
+  constexpr int kPasses = kRowTile / kRowsPerPass;
+  const int q_row = tid >> 4;
+  const int li = tid & 15;
+  bool bad = false;
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    const int row = p * kRowsPerPass + q_row;
+    const int64_t n = n0 + row;
+    const int64_t k0 = j * kGroup + li * 8;
+    const int64_t nc = n < N ? n : N - 1;
+    uint4 wv = *reinterpret_cast<const uint4*>(W + nc * K + k0);
+    if (n >= N) wv = make_uint4(0, 0, 0, 0);
+    uint4 sv = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);  // s = 1
+    if (!CLIP || s) sv = *reinterpret_cast<const uint4*>(s + k0);
+    const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
+    const uint32_t sd[4] = {sv.x, sv.y, sv.z, sv.w};
+    float wf[8], wp[8], rs[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      wf[2 * i] = h2f((uint16_t)(wd[i] & 0xFFFF));
+      wf[2 * i + 1] = h2f((uint16_t)(wd[i] >> 16));
+      const float s0 = h2f((uint16_t)(sd[i] & 0xFFFF)), s1 = h2f((uint16_t)(sd[i] >> 16));
+      wp[2 * i] = wf[2 * i] * s0;
+      wp[2 * i + 1] = wf[2 * i + 1] * s1;
+      rs[2 * i] = __builtin_amdgcn_rcpf(s0);
+      rs[2 * i + 1] = __builtin_amdgcn_rcpf(s1);
+    }
+    float mn = wp[0], mx = wp[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) {
+      mn = fminf(mn, wp[i]);
+      mx = fmaxf(mx, wp[i]);
+    }
+    row16_minmax(mn, mx);
+    bad |= !__builtin_isfinite(mn) || !__builtin_isfinite(mx);
+    if (CLIP) {
+      mn = r * mn;
+      mx = r * mx;
+    }
+    const GroupQ g = group_params(mn, mx);
+    const float P = lds_p[row];
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint16_t h2[2], l2[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int c = 2 * i + e;
+        const float q = quant_code(wp[c], g);
+        const float deq = (q - g.z) * g.scf;  // exact: small integer times an fp16
+        const float d = (wf[c] - deq * rs[c]) * P;
+        h2[e] = f2h_bits(d);
+        l2[e] = f2h_bits(d - h2f(h2[e]));
+      }
+      hi[i] = (uint32_t)h2[0] | ((uint32_t)h2[1] << 16);
+      lo[i] = (uint32_t)l2[0] | ((uint32_t)l2[1] << 16);
+    }
+    *reinterpret_cast<uint4*>(&hi_buf[row * kLdsStride + li * 8]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    *reinterpret_cast<uint4*>(&lo_buf[row * kLdsStride + li * 8]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+  }
+  return bad;
+}
+
 template <int NW>
 __global__ void __launch_bounds__(NW * 64)
     k_search_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N, int64_t K,
@@ -122,10 +203,6 @@ __global__ void __launch_bounds__(NW * 64)
   const int64_t tchunk = (int64_t)NW * kTokPerWave;
   const int64_t n_tchunks = (T + tchunk - 1) / tchunk;
 
-  constexpr int kRowsPerPass = NW * 4;
-  constexpr int kPasses = kRowTile / kRowsPerPass;
-  const int q_row = tid >> 4;
-  const int li = tid & 15;
   const int m32 = lane & 31;
   const int khalf = lane >> 5;
 
@@ -135,59 +212,8 @@ __global__ void __launch_bounds__(NW * 64)
   __syncthreads();
 
   bool bad = false;
-  // quantize group j of the tile into LDS buffer `buf` as (D P) split into fp16 hi + lo
   auto quantize = [&](int64_t j, int buf) {
-#pragma unroll
-    for (int p = 0; p < kPasses; ++p) {
-      const int r = p * kRowsPerPass + q_row;
-      const int64_t n = n0 + r;
-      const int64_t k0 = j * kGroup + li * 8;
-      const int64_t nc = n < N ? n : N - 1;
-      uint4 wv = *reinterpret_cast<const uint4*>(W + nc * K + k0);
-      if (n >= N) wv = make_uint4(0, 0, 0, 0);
-      const uint4 sv = *reinterpret_cast<const uint4*>(s + k0);
-      const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
-      const uint32_t sd[4] = {sv.x, sv.y, sv.z, sv.w};
-      float wf[8], wp[8], rs[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        wf[2 * i] = h2f((uint16_t)(wd[i] & 0xFFFF));
-        wf[2 * i + 1] = h2f((uint16_t)(wd[i] >> 16));
-        const float s0 = h2f((uint16_t)(sd[i] & 0xFFFF)), s1 = h2f((uint16_t)(sd[i] >> 16));
-        wp[2 * i] = wf[2 * i] * s0;
-        wp[2 * i + 1] = wf[2 * i + 1] * s1;
-        rs[2 * i] = __builtin_amdgcn_rcpf(s0);
-        rs[2 * i + 1] = __builtin_amdgcn_rcpf(s1);
-      }
-      float mn = wp[0], mx = wp[0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) {
-        mn = fminf(mn, wp[i]);
-        mx = fmaxf(mx, wp[i]);
-      }
-      row16_minmax(mn, mx);
-      const GroupQ g = group_params(mn, mx);
-      const float P = lds_p[r];
-      uint32_t hi[4], lo[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint16_t h2[2], l2[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int c = 2 * i + e;
-          const float q = quant_code(wp[c], g);
-          const float deq = (q - g.z) * g.scf;  // exact: small integer times an fp16
-          const float d = (wf[c] - deq * rs[c]) * P;
-          h2[e] = f2h_bits(d);
-          l2[e] = f2h_bits(d - h2f(h2[e]));
-        }
-        hi[i] = (uint32_t)h2[0] | ((uint32_t)h2[1] << 16);
-        lo[i] = (uint32_t)l2[0] | ((uint32_t)l2[1] << 16);
-      }
-      bad |= !__builtin_isfinite(mn) || !__builtin_isfinite(mx);
-      *reinterpret_cast<uint4*>(&lds_hi[buf][r * kLdsStride + li * 8]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-      *reinterpret_cast<uint4*>(&lds_lo[buf][r * kLdsStride + li * 8]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-    }
+    bad |= quantize_tile_group<NW, false>(W, N, K, s, 1.0f, n0, j, lds_p, lds_hi[buf], lds_lo[buf], tid);
   };
 
   for (int64_t tc = 0; tc < n_tchunks; ++tc) {
@@ -260,6 +286,154 @@ __global__ void __launch_bounds__(NW * 64)
     __syncthreads();
   }
   if (bad && flags && alpha == 0) atomicOr(flags, AWQ_FLAG_NONFINITE_INPUT);
+}
+
+template <int NW>
+__global__ void __launch_bounds__(NW * 64)
+    k_clip_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N, int64_t K,
+               const uint16_t* s, int clip_steps, int n_shrink, const float* rowmax,
+               const float* srange, double* __restrict__ err, uint32_t* __restrict__ flags,
+               int64_t n_ntiles, int64_t per_xcd) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds_hi[2][kRowTile * kLdsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_lo[2][kRowTile * kLdsStride];
+  __shared__ float lds_p[kRowTile];
+  __shared__ double lds_red[2][NW][kRowTile];
+
+  const int64_t t = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (t >= n_ntiles * n_shrink) return;
+  const int64_t ntile = t / n_shrink;
+  const int ci = (int)(t % n_shrink);
+  const float r = clip_ratio(ci, clip_steps);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t n0 = ntile * kRowTile;
+  const int64_t G = K / kGroup;
+  const int m32 = lane & 31;
+  const int khalf = lane >> 5;
+  const int64_t tw = (int64_t)wave * kTokPerWave;
+  const bool active = tw < T;
+
+  const float sr = s ? srange[0] : 1.0f;
+  for (int i = tid; i < kRowTile; i += NW * 64)
+    lds_p[i] = row_scale(n0 + i < N ? rowmax[n0 + i] : 0.0f, sr);
+  __syncthreads();
+
+  bool bad = false;
+  bad |= quantize_tile_group<NW, true>(W, N, K, s, r, n0, 0, lds_p, lds_hi[0], lds_lo[0], tid);
+  __syncthreads();
+  for (int64_t j = 0; j < G; ++j) {
+    const int buf = (int)(j & 1);
+    bad |= quantize_tile_group<NW, true>(W, N, K, s, r, n0, j + 1 < G ? j + 1 : G - 1, lds_p,
+                                         lds_hi[buf ^ 1], lds_lo[buf ^ 1], tid);
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
+    if (active) {
+#pragma unroll 2
+      for (int st = 0; st < kGroup / 16; ++st) {
+        const int koff = st * 16 + khalf * 8;
+        half8 A[2], Bh[4], Bl[4];
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+          const int64_t tt = tw + a * 32 + m32;
+          uint4 v = *reinterpret_cast<const uint4*>(X + (tt < T ? tt : T - 1) * K + j * kGroup + koff);
+          if (tt >= T) v = make_uint4(0, 0, 0, 0);
+          A[a] = __builtin_bit_cast(half8, v);
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int row = b * 32 + m32;
+          Bh[b] = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(&lds_hi[buf][row * kLdsStride + koff]));
+          Bl[b] = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(&lds_lo[buf][row * kLdsStride + koff]));
+        }
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[a], Bh[b], acc[a][b], 0, 0, 0);
+            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[a], Bl[b], acc[a][b], 0, 0, 0);
+          }
+      }
+    }
+    // this group's squares per row (output column = lane % 32; lanes l and l + 32 hold
+    // the same column for different tokens)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const double pinv = 1.0 / (double)lds_p[b * 32 + m32];
+      double ss = 0.0;
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const double v = (double)acc[a][b][e] * pinv;
+          ss += v * v;
+        }
+      ss += __shfl_xor(ss, 32);
+      if (khalf == 0) lds_red[buf][wave][b * 32 + m32] = ss;
+    }
+    __syncthreads();
+    if (tid < kRowTile && n0 + tid < N) {
+      double tot = lds_red[buf][0][tid];
+      for (int w = 1; w < NW; ++w) tot += lds_red[buf][w][tid];
+      err[((int64_t)ci * N + n0 + tid) * G + j] = tot;
+    }
+  }
+  if (bad && flags && ci == 0) atomicOr(flags, AWQ_FLAG_NONFINITE_INPUT);
+}
+
+// One thread per (row, group): the first ratio index with the smallest error.
+__global__ void __launch_bounds__(256)
+    k_clip_reduce(const double* __restrict__ err, int n_shrink, int64_t NG,
+                  uint8_t* __restrict__ clip_idx, double* __restrict__ err_best) {
+  const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (u >= NG) return;
+  double best = err[u];
+  int bi = 0;
+  for (int i = 1; i < n_shrink; ++i) {
+    const double v = err[(int64_t)i * NG + u];
+    if (v < best) {
+      best = v;
+      bi = i;
+    }
+  }
+  clip_idx[u] = (uint8_t)bi;
+  if (err_best) err_best[u] = best;
+}
+
+hipError_t launch_clip_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N,
+                           int64_t K, const uint16_t* s, int clip_steps, int n_shrink,
+                           float* rowmax, float* srange, double* err, uint32_t* flags,
+                           hipStream_t stream) {
+  hipLaunchKernelGGL(k_row_absmax, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, stream, W, N, K, rowmax);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (s) {
+    hipLaunchKernelGGL(k_scale_range, dim3(1), dim3(256), 0, stream, s, K, srange, flags);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t n_ntiles = (N + kRowTile - 1) / kRowTile;
+  const int64_t per_xcd = (n_ntiles * n_shrink + kXcds - 1) / kXcds;
+  const dim3 grid((unsigned)(per_xcd * kXcds));
+  if (T <= 4 * kTokPerWave)
+    hipLaunchKernelGGL(k_clip_err<4>, grid, dim3(256), 0, stream, X, T, W, N, K, s, clip_steps,
+                       n_shrink, rowmax, srange, err, flags, n_ntiles, per_xcd);
+  else
+    hipLaunchKernelGGL(k_clip_err<8>, grid, dim3(512), 0, stream, X, T, W, N, K, s, clip_steps,
+                       n_shrink, rowmax, srange, err, flags, n_ntiles, per_xcd);
+  return hipGetLastError();
+}
+
+hipError_t launch_clip_reduce(const double* err, int n_shrink, int64_t N, int64_t G,
+                              uint8_t* clip_idx, double* err_best, hipStream_t stream) {
+  const int64_t NG = N * G;
+  hipLaunchKernelGGL(k_clip_reduce, dim3((unsigned)((NG + 255) / 256)), dim3(256), 0, stream, err,
+                     n_shrink, NG, clip_idx, err_best);
+  return hipGetLastError();
 }
 
 // One block: err_i = sum of partials of grid point i in index order; first minimum.
