@@ -29,6 +29,7 @@ Readings taken where the pages are silent (each is listed with its reason in the
 design notes of the repository):
 
 * codes are unsigned 0..15 with a zero point (asymmetric), dequant = (q - z) * scale;
+  the symmetric variant (zero_point False) uses sc = max|w'| / 7 and z = 8;
 * min/max affine group quantizer, computed in fp32 with IEEE round-to-nearest-even;
   the codes are rounded against the stored fp16 scale;
 * scale floored at 2^-14, clamped to 65504 (flagged);
@@ -125,7 +126,8 @@ def candidate_scales(a: np.ndarray, n_grid: int = N_GRID) -> tuple[np.ndarray, n
 
 
 # --------------------------------------------------------------------------- a3
-def quantize_groups(W16: np.ndarray, s16: np.ndarray | None = None, clip_ratio: np.ndarray | None = None) -> dict:
+def quantize_groups(W16: np.ndarray, s16: np.ndarray | None = None, clip_ratio: np.ndarray | None = None,
+                    zero_point: bool = True) -> dict:
     """Group-wise asymmetric 4-bit quantization of W * diag(s).
 
     [AWQ-PRACTICE] §2.3 (128 consecutive input channels share one step) and §2.1
@@ -144,6 +146,11 @@ def quantize_groups(W16: np.ndarray, s16: np.ndarray | None = None, clip_ratio: 
     With ``clip_ratio`` (fp32 [N][G], the weight-clipping search), step 2 is followed by
     mx = f32(r mx), mn = f32(r mn): the group's range shrinks toward 0 by r and the
     weights beyond it take the end codes through the clamp of step 7.
+    Symmetric (zero_point=False; [AWQ-PRACTICE] §3.3 advises zero_point False,
+    [GPTQ-VS-AWQ] gives the signed range -8..7): steps 3 and 6 become
+      3'. sc = max(|mx|, |mn|) / 7             6'. z = 8
+    so q - 8 = clamp(rint(w' / sc_h), -8, 7) is the signed code, stored offset by 8 in the
+    same format (every zero nibble 8).
     Returns dict(q uint8 [N][K], z uint8 [N][G], scale fp16 [N][G], flags int).
     """
     W16 = np.asarray(W16)
@@ -167,7 +174,10 @@ def quantize_groups(W16: np.ndarray, s16: np.ndarray | None = None, clip_ratio: 
         assert r.shape == (N, G)
         mx = (r * mx).astype(_F32)
         mn = (r * mn).astype(_F32)
-    sc = (mx - mn) / _F32(QMAX)
+    if zero_point:
+        sc = (mx - mn) / _F32(QMAX)
+    else:
+        sc = np.maximum(np.abs(mx), np.abs(mn)) / _F32(7)
     sc = np.maximum(sc, SCALE_FLOOR)
     if np.any(sc > SCALE_MAX):
         flags |= FLAG_SCALE_CLAMPED
@@ -175,7 +185,10 @@ def quantize_groups(W16: np.ndarray, s16: np.ndarray | None = None, clip_ratio: 
     sc_h = sc.astype(np.float16)
     sc_f = sc_h.astype(_F32)
     with np.errstate(invalid="ignore"):
-        z = np.clip(np.rint(-mn / sc_f), _F32(0), _F32(QMAX))
+        if zero_point:
+            z = np.clip(np.rint(-mn / sc_f), _F32(0), _F32(QMAX))
+        else:
+            z = np.full(sc_f.shape, _F32(8))
         q = np.clip(np.rint(wg / sc_f[:, :, None]) + z[:, :, None], _F32(0), _F32(QMAX))
     q = np.nan_to_num(q, nan=0.0).astype(np.uint8).reshape(N, K)
     z = np.nan_to_num(z, nan=0.0).astype(np.uint8)
@@ -224,9 +237,10 @@ def unpack(qweight: np.ndarray, scales: np.ndarray, zeros: np.ndarray, K: int):
     return q, z, np.asarray(scales, dtype=np.float16)
 
 
-def quantize_pack(W16: np.ndarray, s16: np.ndarray | None = None, clip_ratio: np.ndarray | None = None):
+def quantize_pack(W16: np.ndarray, s16: np.ndarray | None = None, clip_ratio: np.ndarray | None = None,
+                  zero_point: bool = True):
     """a3 + a4: returns (qweight, scales, zeros, flags)."""
-    r = quantize_groups(W16, s16, clip_ratio)
+    r = quantize_groups(W16, s16, clip_ratio, zero_point)
     qweight, scales, zeros = pack(r["q"], r["z"], r["scale"])
     return qweight, scales, zeros, r["flags"]
 
@@ -246,7 +260,8 @@ def dequantize(q: np.ndarray, z: np.ndarray, scale: np.ndarray, s16: np.ndarray 
 
 
 # --------------------------------------------------------------------------- a5/a6
-def search_errors(X16: np.ndarray, W16: np.ndarray, n_grid: int = N_GRID, grid_points=None) -> dict:
+def search_errors(X16: np.ndarray, W16: np.ndarray, n_grid: int = N_GRID, grid_points=None,
+                  zero_point: bool = True) -> dict:
     """Output error of every candidate scale.
 
     [AWQ-PRACTICE] §2.2 and §3.3 step 4: grid search over a candidate interval so
@@ -268,7 +283,7 @@ def search_errors(X16: np.ndarray, W16: np.ndarray, n_grid: int = N_GRID, grid_p
     err = np.full(n_grid, np.nan, dtype=_F64)
     points = range(n_grid) if grid_points is None else grid_points
     for i in points:
-        r = quantize_groups(W16, s16[i])
+        r = quantize_groups(W16, s16[i], zero_point=zero_point)
         flags |= r["flags"]
         What = dequantize(r["q"], r["z"], r["scale"], s16[i])
         D = Wd - What
@@ -277,21 +292,21 @@ def search_errors(X16: np.ndarray, W16: np.ndarray, n_grid: int = N_GRID, grid_p
     return {"alpha": alpha, "a": a, "s16": s16, "s64": s64, "err": err, "flags": flags}
 
 
-def search_scales(X16: np.ndarray, W16: np.ndarray, n_grid: int = N_GRID) -> dict:
+def search_scales(X16: np.ndarray, W16: np.ndarray, n_grid: int = N_GRID, zero_point: bool = True) -> dict:
     """a1..a6: the chosen grid index (first minimum), its scale and its packed weights.
 
     [AWQ-PRACTICE] §3.3 steps 4-5: pick the s with the smallest error, then
     quantize with it and keep the scale. Ties go to the smallest index (closest to
     plain RTN).
     """
-    r = search_errors(X16, W16, n_grid)
+    r = search_errors(X16, W16, n_grid, zero_point=zero_point)
     err = r["err"]
     best = 0
     for i in range(1, n_grid):
         if err[i] < err[best]:
             best = i
     s_best = r["s16"][best].copy()
-    qweight, scales, zeros, f = quantize_pack(W16, s_best)
+    qweight, scales, zeros, f = quantize_pack(W16, s_best, zero_point=zero_point)
     r.update(best_idx=best, s_best=s_best, qweight=qweight, scales=scales, zeros=zeros,
              gap=relative_gap(err), flags=r["flags"] | f)
     return r
@@ -309,7 +324,8 @@ def clip_ratios(clip_steps: int = CLIP_STEPS, n_shrink: int = CLIP_STEPS // 2) -
 
 
 def clip_errors(X16: np.ndarray, W16: np.ndarray, s16: np.ndarray | None = None,
-                clip_steps: int = CLIP_STEPS, n_shrink: int = CLIP_STEPS // 2) -> np.ndarray:
+                clip_steps: int = CLIP_STEPS, n_shrink: int = CLIP_STEPS // 2,
+                zero_point: bool = True) -> np.ndarray:
     """Per-group output error of every shrink ratio, fp64 [n_shrink][N][G].
 
     Weight-clipping search ([NXMR] §5.1 "精度下降严重": tune clip_steps, 200 suggested,
@@ -326,7 +342,7 @@ def clip_errors(X16: np.ndarray, W16: np.ndarray, s16: np.ndarray | None = None,
     ratios = clip_ratios(clip_steps, n_shrink)
     err = np.empty((n_shrink, N, G), dtype=_F64)
     for i, r in enumerate(ratios):
-        qz = quantize_groups(W16, s16, np.full((N, G), r, dtype=_F32))
+        qz = quantize_groups(W16, s16, np.full((N, G), r, dtype=_F32), zero_point)
         D = Wd - dequantize(qz["q"], qz["z"], qz["scale"], s16)
         for g in range(G):
             E = Xd[:, g * GROUP:(g + 1) * GROUP] @ D[:, g * GROUP:(g + 1) * GROUP].T
@@ -335,11 +351,12 @@ def clip_errors(X16: np.ndarray, W16: np.ndarray, s16: np.ndarray | None = None,
 
 
 def clip_search(X16: np.ndarray, W16: np.ndarray, s16: np.ndarray | None = None,
-                clip_steps: int = CLIP_STEPS, n_shrink: int = CLIP_STEPS // 2) -> dict:
+                clip_steps: int = CLIP_STEPS, n_shrink: int = CLIP_STEPS // 2,
+                zero_point: bool = True) -> dict:
     """Per group, the first ratio index with the smallest error, and the weight packed
     with those ratios. Returns dict(idx uint8 [N][G], ratio fp32 [N][G], err fp64
     [n_shrink][N][G], qweight, scales, zeros, flags)."""
-    err = clip_errors(X16, W16, s16, clip_steps, n_shrink)
+    err = clip_errors(X16, W16, s16, clip_steps, n_shrink, zero_point)
     idx = np.zeros(err.shape[1:], dtype=np.int64)
     best = err[0].copy()
     for i in range(1, n_shrink):
@@ -347,7 +364,7 @@ def clip_search(X16: np.ndarray, W16: np.ndarray, s16: np.ndarray | None = None,
         idx[better] = i
         best[better] = err[i][better]
     ratio = clip_ratios(clip_steps, n_shrink)[idx]
-    qweight, scales, zeros, flags = quantize_pack(W16, s16, ratio)
+    qweight, scales, zeros, flags = quantize_pack(W16, s16, ratio, zero_point)
     return {"idx": idx.astype(np.uint8), "ratio": ratio, "err": err, "qweight": qweight,
             "scales": scales, "zeros": zeros, "flags": flags}
 

@@ -522,3 +522,60 @@ def test_clipping_an_outlier_the_tokens_never_see():
     assert qz0["z"][0, 0] == 0 and qz1["z"][0, 0] == 0 and qz1["q"][0, 0] == 15
     assert err[-1] < err[0] / 3
     assert oracle.clip_search(X, W, None, 200, 100)["idx"][0, 0] == int(np.argmin(err))
+
+
+# ----------------------------------------------------------------- symmetric codes
+def test_symmetric_hand_worked_group():
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")))["symmetric_group"]
+    W = np.full((1, 128), g["fill"], dtype=np.float16)
+    for k, v in g["values"].items():
+        W[0, int(k)] = v
+    r = oracle.quantize_groups(W, zero_point=False)
+    assert hex(int(r["scale"].view(np.uint16)[0, 0])) == g["scale_bits"]
+    assert int(r["z"][0, 0]) == g["zero"]
+    for k, c in g["codes"].items():
+        assert int(r["q"][0, int(k)]) == c
+    assert int(r["q"][0, 100]) == g["fill_code"]
+
+
+def _check_symmetric_scale(w, z, scale):
+    """sc_h = fp16(max |w'| / 7) up to the fp32 division's rounding, floored at 2^-14; z = 8."""
+    bad = []
+    for n in range(w.shape[0]):
+        for j in range(w.shape[1] // 128):
+            grp = w[n, j * 128:(j + 1) * 128]
+            amax = max(Fraction(float(abs(grp.max()))), Fraction(float(abs(grp.min()))))
+            exact = max(amax / 7, Fraction(2) ** -14)
+            lo_ = pins.rne_fp16(exact * (1 - Fraction(1, 2 ** 22)))
+            hi_ = pins.rne_fp16(exact * (1 + Fraction(1, 2 ** 22)))
+            if not (lo_ <= Fraction(float(scale[n, j])) <= hi_) or int(z[n, j]) != 8:
+                bad.append((n, j))
+    return bad
+
+
+def test_symmetric_codes_nearest_and_scale():
+    """Codes nearest for the stored scale with the fixed zero 8 (brute force over 16 codes),
+    scale = fp16(max|w'| / 7); a /8 scale (the other common symmetric form) is caught."""
+    W = si.weights(4, 256, offset=115)
+    s = np.exp(np.random.default_rng(10).uniform(-1, 1, 256)).astype(np.float16)
+    r = oracle.quantize_groups(W, s, zero_point=False)
+    w = W.astype(np.float32) * s.astype(np.float32)
+    assert not pins.check_codes_nearest(w, r["q"], r["z"], r["scale"])
+    assert not _check_symmetric_scale(w, r["z"], r["scale"])
+    amax = np.maximum(np.abs(w.reshape(4, 2, 128)).max(axis=2), 2.0 ** -14)
+    mutant = (amax / np.float32(8)).astype(np.float16)
+    assert _check_symmetric_scale(w, r["z"], mutant)
+    # dequantized weights of the signed code: (q - 8) * sc with q - 8 in -8..7
+    qz = r["q"].astype(np.int64) - 8
+    assert qz.min() >= -8 and qz.max() <= 7
+
+
+def test_symmetric_search_errors_exact():
+    """The scale search with symmetric codes: errors against exact rational arithmetic."""
+    X = si.activations(2, 128, offset=116)
+    W = si.weights(2, 128, offset=116)
+    r = oracle.search_errors(X, W, n_grid=4, zero_point=False)
+    for i in range(4):
+        qz = oracle.quantize_groups(W, r["s16"][i], zero_point=False)
+        exact = pins.exact_search_error(X, W, r["s16"][i], qz["q"], qz["z"], qz["scale"])
+        assert abs(r["err"][i] - float(exact)) <= 1e-12 * float(exact)
