@@ -51,8 +51,12 @@ typedef enum awq_status {
 
 /* Quantization config ([SKILL] "如何使用该技能 / 步骤 2": quant_config zero_point, q_group_size,
  * w_bit; the page's "version" GEMM/GEMV switch becomes dispatch on M inside
- * awq_linear_w4a16). Supported: w_bit = 4, group_size = 128, zero_point = 1,
- * 1 <= n_grid <= 64. NULL config pointers mean {4, 128, 1, 20}. */
+ * awq_linear_w4a16). Supported: w_bit = 4, group_size = 128, zero_point = 1 or 0,
+ * 1 <= n_grid <= 64. NULL config pointers mean {4, 128, 1, 20}.
+ * zero_point = 0 ([PRACTICE] §3.3 advises it; [GPTQ-AWQ] gives the signed range -8..7):
+ * sc = max|w'| / 7, q - 8 = clamp(rint(w'/sc_h), -8, 7), stored offset by 8 with every
+ * zero nibble 8 -- the same packed format, so the linear entry points are unchanged;
+ * quantize, search and clip search honour the mode. */
 typedef struct awq_config {
   int32_t w_bit;
   int32_t group_size;

@@ -59,7 +59,7 @@ def test_quantize_pack_validation(lib):
     assert _qp(lib, cfg=C.byref(bad)) == 3
     bad = _abi.config(group_size=64)
     assert _qp(lib, cfg=C.byref(bad)) == 3
-    bad = _abi.config(zero_point=0)
+    bad = _abi.config(zero_point=2)
     assert _qp(lib, cfg=C.byref(bad)) == 3
 
 

@@ -91,3 +91,44 @@ def test_clip_7b_o_proj_sampled_rows():
     rows = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(9).choice(N, 46, replace=False)]))
     ref_err = oracle.clip_errors(X, W[rows], s, 200, 20)
     _check_choice(host(idx)[rows].astype(np.int64), host(err)[rows], ref_err)
+
+
+# ----------------------------------------------------------------- symmetric codes (f4)
+@pytest.mark.parametrize("N,K", [(67, 384), (256, 4096), (130, 11008)])
+def test_symmetric_pack_bit_exact_and_linear(N, K):
+    W = si.weights(N, K, offset=N + K + 1)
+    a, _ = oracle.activation_mean_abs(si.activations(32, K, offset=N))
+    s = oracle.candidate_scales(a, 20)[1][6]
+    qw, sc, zb, _ = oracle.quantize_pack(W, s, zero_point=False)
+    p = awq.quantize_pack(to_dev(W), to_dev(s), zero_point=False)
+    gq, gs, gz = packed_host(p)
+    assert np.array_equal(gq, qw) and np.array_equal(gz, zb)
+    assert np.all(oracle.unpack(qw, sc, zb, K)[1] == 8)   # every group's zero is 8
+    assert np.array_equal(gs.view(np.uint16), sc.view(np.uint16))
+    for M, kern in ((1, "gemv"), (8, "skinny"), (40, "gemm")):
+        X = si.activations(M, K, offset=M + 3)
+        Y = host(awq.linear_w4a16(to_dev(X), p, kernel=kern))
+        y_ref, bound = oracle.linear_reference(X, qw, sc, zb, K)
+        assert oracle.linear_within_tolerance(Y.astype(np.float64), y_ref, bound).all(), kern
+
+
+@pytest.mark.parametrize("T,N,K", [(96, 192, 512), (512, 130, 1152)])
+def test_symmetric_search_and_clip(T, N, K):
+    X = si.activations(T, K, offset=T + 5)
+    W = si.weights(N, K, offset=T + 5)
+    ref = oracle.search_errors(X, W, zero_point=False)
+    r = awq.search_scales(to_dev(X), to_dev(W), zero_point=False)
+    err = host(r.err)
+    assert np.all(np.abs(err - ref["err"]) <= 1e-5 * ref["err"])
+    if oracle.relative_gap(ref["err"]) >= 1e-5:
+        assert int(host(r.best_idx)[0]) == int(np.argmin(ref["err"]))
+    s = host(r.s_best)
+    ref_err = oracle.clip_errors(X, W, s, 200, 8, zero_point=False)
+    idx, cerr = awq.clip_search(to_dev(X), to_dev(W), r.s_best, 200, 8, zero_point=False)
+    ref_idx = _check_choice(host(idx).astype(np.int64), host(cerr), ref_err)
+    qw, sc, zb, _ = oracle.quantize_pack(W, s, oracle.clip_ratios(200, 8)[ref_idx], zero_point=False)
+    p = awq.quantize_pack(to_dev(W), r.s_best, clip_idx=to_dev(ref_idx.astype(np.uint8)),
+                          zero_point=False)
+    gq, gs, gz = packed_host(p)
+    assert np.array_equal(gq, qw) and np.array_equal(gz, zb)
+    assert np.array_equal(gs.view(np.uint16), sc.view(np.uint16))

@@ -60,9 +60,10 @@ def alloc_packed(N: int, K: int, device) -> PackedLinear:
 
 def quantize_pack(W: torch.Tensor, s: torch.Tensor | None = None, flags: torch.Tensor | None = None,
                   out: PackedLinear | None = None, clip_idx: torch.Tensor | None = None,
-                  clip_steps: int = 200) -> PackedLinear:
+                  clip_steps: int = 200, zero_point: bool = True) -> PackedLinear:
     """awq_quantize_pack: 4-bit group-128 quantization of W * diag(s) (s = None: plain RTN);
-    with clip_idx (uint8 [N][K/128], clip_search's output), awq_quantize_pack_clipped."""
+    with clip_idx (uint8 [N][K/128], clip_search's output), awq_quantize_pack_clipped;
+    zero_point=False: symmetric codes (same packed format, every zero 8)."""
     lib = _abi.load()
     _need(W, torch.float16, "W")
     if W.dim() != 2:
@@ -80,7 +81,7 @@ def quantize_pack(W: torch.Tensor, s: torch.Tensor | None = None, flags: torch.T
         _need(t, dt, name)
     if p.N != N or p.K != K:
         raise ValueError("output packed buffers have the wrong shape")
-    cfg = _abi.config()
+    cfg = _abi.config(zero_point=int(zero_point))
     if clip_idx is not None:
         _need(clip_idx, torch.uint8, "clip_idx")
         if clip_idx.shape != (N, K // 128):
@@ -93,7 +94,7 @@ def quantize_pack(W: torch.Tensor, s: torch.Tensor | None = None, flags: torch.T
 
 def clip_search(X: torch.Tensor, W: torch.Tensor, s: torch.Tensor | None = None,
                 clip_steps: int = 200, n_shrink: int = 100, flags: torch.Tensor | None = None,
-                workspace: torch.Tensor | None = None):
+                workspace: torch.Tensor | None = None, zero_point: bool = True):
     """awq_clip_search: per group, the index of the best shrink ratio (uint8 [N][K/128]) and
     its error (fp64 [N][K/128]); ratio r_i = (clip_steps - i) / clip_steps, i < n_shrink."""
     lib = _abi.load()
@@ -110,7 +111,7 @@ def clip_search(X: torch.Tensor, W: torch.Tensor, s: torch.Tensor | None = None,
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=X.device)
     idx = torch.empty((N, K // 128), dtype=torch.uint8, device=X.device)
     err = torch.empty((N, K // 128), dtype=torch.float64, device=X.device)
-    cfg = _abi.config()
+    cfg = _abi.config(zero_point=int(zero_point))
     _abi.check("awq_clip_search", lib.awq_clip_search(
         _ptr(X), T, _ptr(W), N, K, _ptr(s), clip_steps, n_shrink, C.byref(cfg), _ptr(idx),
         _ptr(err), _ptr(workspace), workspace.numel(), _ptr(flags), _stream()))
@@ -166,7 +167,7 @@ class SearchWorkspace:
 
 def search_scales(X: torch.Tensor, W: torch.Tensor, n_grid: int = 20,
                   workspace: SearchWorkspace | None = None, flags: torch.Tensor | None = None,
-                  out: SearchResult | None = None) -> SearchResult:
+                  out: SearchResult | None = None, zero_point: bool = True) -> SearchResult:
     """awq_search_scales: grid search of s = mean|x|^alpha minimizing the output error."""
     lib = _abi.load()
     _need(X, torch.float16, "X")
@@ -184,7 +185,7 @@ def search_scales(X: torch.Tensor, W: torch.Tensor, n_grid: int = 20,
     ws = workspace if workspace is not None else SearchWorkspace(T, N, K, dev, n_grid)
     if flags is not None:
         _need(flags, torch.int32, "flags")
-    cfg = _abi.config(n_grid)
+    cfg = _abi.config(n_grid, zero_point=int(zero_point))
     _abi.check("awq_search_scales", lib.awq_search_scales(
         _ptr(X), T, _ptr(W), N, K, C.byref(cfg), _ptr(out.s_best), _ptr(out.best_idx),
         _ptr(out.err), _ptr(out.s_grid), _ptr(ws.buf), ws.nbytes, _ptr(flags), _stream()))

@@ -15,8 +15,8 @@ awq_config resolve(const awq_config* cfg) {
 }
 
 bool supported(const awq_config& c) {
-  return c.w_bit == 4 && c.group_size == 128 && c.zero_point == 1 && c.n_grid >= 1 &&
-         c.n_grid <= 64;
+  return c.w_bit == 4 && c.group_size == 128 && (c.zero_point == 0 || c.zero_point == 1) &&
+         c.n_grid >= 1 && c.n_grid <= 64;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -117,8 +117,8 @@ awq_status awq_quantize_pack_clipped(const void* W, int64_t N, int64_t K, const 
       (s && !aligned16(s)) || (flags && !aligned4(flags)))
     return AWQ_ERR_MISALIGNED;
   return hip_status(awq::launch_quant_pack((const uint16_t*)W, N, K, (const uint16_t*)s, qweight,
-                                           (uint16_t*)scales, zeros, clip_idx, clip_steps, flags,
-                                           (hipStream_t)stream));
+                                           (uint16_t*)scales, zeros, clip_idx, clip_steps,
+                                           c.zero_point == 0, flags, (hipStream_t)stream));
 }
 
 size_t awq_activation_stats_workspace_size(int64_t T, int64_t K) {
@@ -187,7 +187,7 @@ awq_status awq_search_scales(const void* X, int64_t T, const void* W, int64_t N,
   if (e == hipSuccess) e = awq::launch_act_finalize(u, T, K, act, st);
   if (e == hipSuccess) e = awq::launch_scalegen(act, K, c.n_grid, sg, st);
   if (e == hipSuccess)
-    e = awq::launch_search_err(Xh, T, (const uint16_t*)W, N, K, sg, c.n_grid,
+    e = awq::launch_search_err(Xh, T, (const uint16_t*)W, N, K, sg, c.n_grid, c.zero_point == 0,
                                (float*)(ws + L.rowmax), (float*)(ws + L.srange), partials, flags, st);
   if (e == hipSuccess)
     e = awq::launch_search_reduce(partials, c.n_grid, L.n_partials, sg, K, (uint16_t*)s_best,
@@ -291,7 +291,7 @@ awq_status awq_clip_search(const void* X, int64_t T, const void* W, int64_t N, i
   hipStream_t st = (hipStream_t)stream;
   double* errs = (double*)(ws + L.err);
   hipError_t e = awq::launch_clip_err((const uint16_t*)X, T, (const uint16_t*)W, N, K,
-                                      (const uint16_t*)s, clip_steps, n_shrink,
+                                      (const uint16_t*)s, clip_steps, n_shrink, c.zero_point == 0,
                                       (float*)(ws + L.rowmax), (float*)(ws + L.srange), errs, flags, st);
   if (e == hipSuccess)
     e = awq::launch_clip_reduce(errs, n_shrink, N, K / 128, clip_idx, err, st);

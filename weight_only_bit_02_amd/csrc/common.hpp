@@ -102,6 +102,23 @@ __device__ __forceinline__ GroupQ group_params(float mn, float mx) {
   return g;
 }
 
+// Symmetric variant (zero point off): sc = max(|mx|, |mn|) / 7 with the same floor and
+// clamp, and the fixed zero 8, so q - 8 = clamp(rint(w / sc_h), -8, 7) is the signed code
+// and the stored format (and its dequantization (q - z) sc) is unchanged.
+__device__ __forceinline__ GroupQ group_params_sym(float mn, float mx) {
+#pragma clang fp contract(off)
+  GroupQ g;
+  float sc = fmaxf(__builtin_fabsf(mx), __builtin_fabsf(mn)) / 7.0f;
+  sc = fmaxf(sc, 0x1p-14f);
+  g.clamped = sc > 65504.0f;
+  sc = fminf(sc, 65504.0f);
+  g.sch = f2h_bits(sc);
+  g.scf = h2f(g.sch);
+  g.z = 8.0f;
+  g.rcp = 1.0f / g.scf;
+  return g;
+}
+
 // rint(w / scf) exactly as the correctly rounded quotient would give it. The product
 // w * rcp is within 2^-23 (relative) of the real quotient; unless it sits within
 // |q| * 2^-21 of a half-integer, it lies on the same side of that half-integer as

@@ -10,15 +10,16 @@ namespace awq {
 
 // a3 + a4: quantize W * diag(s) per group of 128 and pack codes / scales / zeros.
 // clip_idx (nullable, [N][G]): group (n, j) shrinks its range by (steps - idx) / steps.
+// sym: zero point off (sc = max|w'| / 7, zero fixed at 8, same stored format).
 hipError_t launch_quant_pack(const uint16_t* W, int64_t N, int64_t K, const uint16_t* s,
                              uint32_t* qweight, uint16_t* scales, uint8_t* zeros,
-                             const uint8_t* clip_idx, int clip_steps, uint32_t* flags,
+                             const uint8_t* clip_idx, int clip_steps, bool sym, uint32_t* flags,
                              hipStream_t stream);
 
 // f3: err[i][n][g] = sum_t (sum_{k in g} X_tk D_nk)^2 for the clip ratios i < n_shrink
 // (T <= 512), then the first minimum per (n, g).
 hipError_t launch_clip_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N,
-                           int64_t K, const uint16_t* s, int clip_steps, int n_shrink,
+                           int64_t K, const uint16_t* s, int clip_steps, int n_shrink, bool sym,
                            float* rowmax, float* srange, double* err, uint32_t* flags,
                            hipStream_t stream);
 hipError_t launch_clip_reduce(const double* err, int n_shrink, int64_t N, int64_t G,
@@ -42,7 +43,7 @@ int search_row_tile();
 int search_token_chunk(int64_t T);
 // rowmax [N] and srange [n_grid] are scratch (per-row max |W|, per-grid-point max s / min s).
 hipError_t launch_search_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N,
-                             int64_t K, const uint16_t* s_grid, int n_grid, float* rowmax,
+                             int64_t K, const uint16_t* s_grid, int n_grid, bool sym, float* rowmax,
                              float* srange, double* partials, uint32_t* flags,
                              hipStream_t stream);
 // a6: fixed-order sums of the partials, first-minimum argmin, s_best copy.

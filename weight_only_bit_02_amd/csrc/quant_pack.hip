@@ -7,7 +7,8 @@
 // Mapping: a wave owns one (row, run of 4 groups) unit = 512 input channels. Lane l
 // reads 8 consecutive weights (one 16-byte load) and writes the 32-bit word that packs
 // their 8 codes (channel i of the word in nibble kNibbleOf[i]), so loads and stores are fully coalesced; the 16 lanes of a DPP row
-// form one group and find its min / max with row-local DPP. With clip indices (the
+// form one group and find its min / max with row-local DPP (symmetric mode: the larger
+// magnitude sets the scale, zero fixed at 8). With clip indices (the
 // weight-clipping search), group (n, j) shrinks its extremes by r = clip_ratio(idx, steps)
 // before the quantizer sees them.
 #include "common.hpp"
@@ -21,7 +22,7 @@ __global__ void __launch_bounds__(256) k_quant_pack(const uint16_t* __restrict__
                                                     uint16_t* __restrict__ scales,
                                                     uint8_t* __restrict__ zeros,
                                                     const uint8_t* __restrict__ clip_idx,
-                                                    int clip_steps,
+                                                    int clip_steps, int sym,
                                                     uint32_t* __restrict__ flags) {
   const int lane = threadIdx.x & 63;
   const int gi = lane >> 4;  // group within the unit
@@ -67,7 +68,7 @@ __global__ void __launch_bounds__(256) k_quant_pack(const uint16_t* __restrict__
       mn = r * mn;
       mx = r * mx;
     }
-    const GroupQ g = group_params(mn, mx);
+    const GroupQ g = sym ? group_params_sym(mn, mx) : group_params(mn, mx);
     uint32_t word = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) word |= (uint32_t)quant_code(w[i], g) << (4 * kNibbleOf[i]);
@@ -91,12 +92,12 @@ __global__ void __launch_bounds__(256) k_quant_pack(const uint16_t* __restrict__
 
 hipError_t launch_quant_pack(const uint16_t* W, int64_t N, int64_t K, const uint16_t* s,
                              uint32_t* qweight, uint16_t* scales, uint8_t* zeros,
-                             const uint8_t* clip_idx, int clip_steps, uint32_t* flags,
+                             const uint8_t* clip_idx, int clip_steps, bool sym, uint32_t* flags,
                              hipStream_t stream) {
   const int64_t units = N * ((K / kGroup + 3) / 4);
   const int64_t blocks = units / 4 + 1 < 16384 ? units / 4 + 1 : 16384;
   hipLaunchKernelGGL(k_quant_pack, dim3((unsigned)blocks), dim3(256), 0, stream, W, N, K, s,
-                     qweight, scales, zeros, clip_idx, clip_steps, flags);
+                     qweight, scales, zeros, clip_idx, clip_steps, (int)sym, flags);
   return hipGetLastError();
 }
 

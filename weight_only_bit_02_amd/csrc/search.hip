@@ -109,9 +109,9 @@ __global__ void __launch_bounds__(256) k_scale_range(const uint16_t* __restrict_
 // 16 lanes per (row, group), 8 weights each; returns whether a non-finite value was met.
 template <int NW, bool CLIP>
 __device__ __forceinline__ bool quantize_tile_group(const uint16_t* W, int64_t N, int64_t K,
-                                                    const uint16_t* s, float r, int64_t n0,
-                                                    int64_t j, const float* lds_p, uint16_t* hi_buf,
-                                                    uint16_t* lo_buf, int tid) {
+                                                    const uint16_t* s, float r, bool sym,
+                                                    int64_t n0, int64_t j, const float* lds_p,
+                                                    uint16_t* hi_buf, uint16_t* lo_buf, int tid) {
   constexpr int kRowsPerPass = NW * 4;
   constexpr int kPasses = kRowTile / kRowsPerPass;
   const int q_row = tid >> 4;
@@ -152,7 +152,7 @@ __device__ __forceinline__ bool quantize_tile_group(const uint16_t* W, int64_t N
       mn = r * mn;
       mx = r * mx;
     }
-    const GroupQ g = group_params(mn, mx);
+    const GroupQ g = sym ? group_params_sym(mn, mx) : group_params(mn, mx);
     const float P = lds_p[row];
     uint32_t hi[4], lo[4];
 #pragma unroll
@@ -179,7 +179,7 @@ __device__ __forceinline__ bool quantize_tile_group(const uint16_t* W, int64_t N
 template <int NW>
 __global__ void __launch_bounds__(NW * 64)
     k_search_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N, int64_t K,
-                 const uint16_t* s_grid, int n_grid, const float* rowmax, const float* srange,
+                 const uint16_t* s_grid, int n_grid, int sym, const float* rowmax, const float* srange,
                  double* __restrict__ partials, uint32_t* __restrict__ flags, int64_t n_ntiles,
                  int64_t per_xcd) {
   __shared__ __attribute__((aligned(16))) uint16_t lds_hi[2][kRowTile * kLdsStride];
@@ -213,7 +213,7 @@ __global__ void __launch_bounds__(NW * 64)
 
   bool bad = false;
   auto quantize = [&](int64_t j, int buf) {
-    bad |= quantize_tile_group<NW, false>(W, N, K, s, 1.0f, n0, j, lds_p, lds_hi[buf], lds_lo[buf], tid);
+    bad |= quantize_tile_group<NW, false>(W, N, K, s, 1.0f, sym, n0, j, lds_p, lds_hi[buf], lds_lo[buf], tid);
   };
 
   for (int64_t tc = 0; tc < n_tchunks; ++tc) {
@@ -291,7 +291,7 @@ __global__ void __launch_bounds__(NW * 64)
 template <int NW>
 __global__ void __launch_bounds__(NW * 64)
     k_clip_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N, int64_t K,
-               const uint16_t* s, int clip_steps, int n_shrink, const float* rowmax,
+               const uint16_t* s, int clip_steps, int n_shrink, int sym, const float* rowmax,
                const float* srange, double* __restrict__ err, uint32_t* __restrict__ flags,
                int64_t n_ntiles, int64_t per_xcd) {
   __shared__ __attribute__((aligned(16))) uint16_t lds_hi[2][kRowTile * kLdsStride];
@@ -321,11 +321,11 @@ __global__ void __launch_bounds__(NW * 64)
   __syncthreads();
 
   bool bad = false;
-  bad |= quantize_tile_group<NW, true>(W, N, K, s, r, n0, 0, lds_p, lds_hi[0], lds_lo[0], tid);
+  bad |= quantize_tile_group<NW, true>(W, N, K, s, r, sym, n0, 0, lds_p, lds_hi[0], lds_lo[0], tid);
   __syncthreads();
   for (int64_t j = 0; j < G; ++j) {
     const int buf = (int)(j & 1);
-    bad |= quantize_tile_group<NW, true>(W, N, K, s, r, n0, j + 1 < G ? j + 1 : G - 1, lds_p,
+    bad |= quantize_tile_group<NW, true>(W, N, K, s, r, sym, n0, j + 1 < G ? j + 1 : G - 1, lds_p,
                                          lds_hi[buf ^ 1], lds_lo[buf ^ 1], tid);
     f32x16 acc[2][4];
 #pragma unroll
@@ -405,7 +405,7 @@ __global__ void __launch_bounds__(256)
 }
 
 hipError_t launch_clip_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N,
-                           int64_t K, const uint16_t* s, int clip_steps, int n_shrink,
+                           int64_t K, const uint16_t* s, int clip_steps, int n_shrink, bool sym,
                            float* rowmax, float* srange, double* err, uint32_t* flags,
                            hipStream_t stream) {
   hipLaunchKernelGGL(k_row_absmax, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, stream, W, N, K, rowmax);
@@ -421,10 +421,10 @@ hipError_t launch_clip_err(const uint16_t* X, int64_t T, const uint16_t* W, int6
   const dim3 grid((unsigned)(per_xcd * kXcds));
   if (T <= 4 * kTokPerWave)
     hipLaunchKernelGGL(k_clip_err<4>, grid, dim3(256), 0, stream, X, T, W, N, K, s, clip_steps,
-                       n_shrink, rowmax, srange, err, flags, n_ntiles, per_xcd);
+                       n_shrink, (int)sym, rowmax, srange, err, flags, n_ntiles, per_xcd);
   else
     hipLaunchKernelGGL(k_clip_err<8>, grid, dim3(512), 0, stream, X, T, W, N, K, s, clip_steps,
-                       n_shrink, rowmax, srange, err, flags, n_ntiles, per_xcd);
+                       n_shrink, (int)sym, rowmax, srange, err, flags, n_ntiles, per_xcd);
   return hipGetLastError();
 }
 
@@ -468,7 +468,7 @@ int search_row_tile() { return kRowTile; }
 int search_token_chunk(int64_t T) { return T <= 4 * kTokPerWave ? 4 * kTokPerWave : 8 * kTokPerWave; }
 
 hipError_t launch_search_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N,
-                             int64_t K, const uint16_t* s_grid, int n_grid, float* rowmax,
+                             int64_t K, const uint16_t* s_grid, int n_grid, bool sym, float* rowmax,
                              float* srange, double* partials, uint32_t* flags,
                              hipStream_t stream) {
   hipLaunchKernelGGL(k_row_absmax, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, stream, W, N, K, rowmax);
@@ -482,10 +482,10 @@ hipError_t launch_search_err(const uint16_t* X, int64_t T, const uint16_t* W, in
   const dim3 grid((unsigned)(per_xcd * kXcds));
   if (T <= 4 * kTokPerWave)
     hipLaunchKernelGGL(k_search_err<4>, grid, dim3(256), 0, stream, X, T, W, N, K, s_grid, n_grid,
-                       rowmax, srange, partials, flags, n_ntiles, per_xcd);
+                       (int)sym, rowmax, srange, partials, flags, n_ntiles, per_xcd);
   else
     hipLaunchKernelGGL(k_search_err<8>, grid, dim3(512), 0, stream, X, T, W, N, K, s_grid, n_grid,
-                       rowmax, srange, partials, flags, n_ntiles, per_xcd);
+                       (int)sym, rowmax, srange, partials, flags, n_ntiles, per_xcd);
   return hipGetLastError();
 }
 
