@@ -33,6 +33,7 @@ design notes of the repository):
 * min/max affine group quantizer, computed in fp32 with IEEE round-to-nearest-even;
   the codes are rounded against the stored fp16 scale;
 * scale floored at 2^-14, clamped to 65504 (flagged);
+* group size 128 by default, 64 as the smaller size the practice page names;
 * statistic = plain mean of |x| over all calibration tokens;
 * s = (max(mean|x|, 2^-14))^alpha, alpha_i = i / n_grid, i = 0..n_grid-1, s stored as fp16;
 * packed word: channels 0, 2, 4, 6 in the low nibbles of its bytes, 1, 3, 5, 7 in the high;
@@ -127,7 +128,7 @@ def candidate_scales(a: np.ndarray, n_grid: int = N_GRID) -> tuple[np.ndarray, n
 
 # --------------------------------------------------------------------------- a3
 def quantize_groups(W16: np.ndarray, s16: np.ndarray | None = None, clip_ratio: np.ndarray | None = None,
-                    zero_point: bool = True) -> dict:
+                    zero_point: bool = True, group: int = GROUP) -> dict:
     """Group-wise asymmetric 4-bit quantization of W * diag(s).
 
     [AWQ-PRACTICE] §2.3 (128 consecutive input channels share one step) and §2.1
@@ -135,7 +136,8 @@ def quantize_groups(W16: np.ndarray, s16: np.ndarray | None = None, clip_ratio: 
     integer with a scale and a zero point, dequant = (q - z) * scale);
     [AWQ-SKILL] step 2 (w_bit 4, q_group_size 128, zero_point True).
 
-    Steps per row n and group j (k in [128 j, 128 j + 128)), all in fp32, RNE:
+    Steps per row n and group j (k in [g j, g j + g), g = group: 128, or 64 as
+    [AWQ-PRACTICE] §2.3 also names), all in fp32, RNE:
       1. w' = f32(w) * f32(s)                  (exact: 11 + 11 significant bits)
       2. mx, mn = max / min of the 128 values w'
       3. sc = (mx - mn) / 15
@@ -156,8 +158,8 @@ def quantize_groups(W16: np.ndarray, s16: np.ndarray | None = None, clip_ratio: 
     W16 = np.asarray(W16)
     assert W16.dtype == np.float16 and W16.ndim == 2
     N, K = W16.shape
-    assert K % GROUP == 0
-    G = K // GROUP
+    assert group in (GROUP, 64) and K % group == 0
+    G = K // group
     w = W16.astype(_F32)
     if s16 is not None:
         s16 = np.asarray(s16)
@@ -166,7 +168,7 @@ def quantize_groups(W16: np.ndarray, s16: np.ndarray | None = None, clip_ratio: 
     flags = 0
     if not np.all(np.isfinite(w)):
         flags |= FLAG_NONFINITE_INPUT
-    wg = w.reshape(N, G, GROUP)
+    wg = w.reshape(N, G, group)
     mx = wg.max(axis=2)
     mn = wg.min(axis=2)
     if clip_ratio is not None:
@@ -214,7 +216,7 @@ def pack(q: np.ndarray, z: np.ndarray, scale: np.ndarray) -> tuple[np.ndarray, n
     """
     q = np.asarray(q, dtype=np.uint8)
     N, K = q.shape
-    G = K // GROUP
+    G = np.asarray(z).shape[1]                  # groups per row (128 or 64 channels each)
     qweight = np.zeros((N, K // 8), dtype=np.uint32)
     for j in range(8):
         qweight |= q[:, NIBBLE_CHANNEL[j]::8].astype(np.uint32) << np.uint32(4 * j)
@@ -227,7 +229,7 @@ def pack(q: np.ndarray, z: np.ndarray, scale: np.ndarray) -> tuple[np.ndarray, n
 def unpack(qweight: np.ndarray, scales: np.ndarray, zeros: np.ndarray, K: int):
     """Inverse of :func:`pack`: returns (q uint8 [N][K], z uint8 [N][G], scale fp16 [N][G])."""
     N = qweight.shape[0]
-    G = K // GROUP
+    G = np.asarray(scales).shape[1]             # groups per row (128 or 64 channels each)
     q = np.empty((N, K), dtype=np.uint8)
     for j in range(8):
         q[:, NIBBLE_CHANNEL[j]::8] = ((qweight >> np.uint32(4 * j)) & np.uint32(0xF)).astype(np.uint8)
@@ -238,9 +240,9 @@ def unpack(qweight: np.ndarray, scales: np.ndarray, zeros: np.ndarray, K: int):
 
 
 def quantize_pack(W16: np.ndarray, s16: np.ndarray | None = None, clip_ratio: np.ndarray | None = None,
-                  zero_point: bool = True):
+                  zero_point: bool = True, group: int = GROUP):
     """a3 + a4: returns (qweight, scales, zeros, flags)."""
-    r = quantize_groups(W16, s16, clip_ratio, zero_point)
+    r = quantize_groups(W16, s16, clip_ratio, zero_point, group)
     qweight, scales, zeros = pack(r["q"], r["z"], r["scale"])
     return qweight, scales, zeros, r["flags"]
 
@@ -251,8 +253,9 @@ def dequantize(q: np.ndarray, z: np.ndarray, scale: np.ndarray, s16: np.ndarray 
     [GPTQ-VS-AWQ]: dequant = (q - z) * scale; [AWQ-PRACTICE] §2.2: the 1/s is undone.
     """
     N, K = q.shape
-    zz = np.repeat(z.astype(_F64), GROUP, axis=1)
-    ss = np.repeat(scale.astype(_F64), GROUP, axis=1)
+    group = K // z.shape[1]
+    zz = np.repeat(z.astype(_F64), group, axis=1)
+    ss = np.repeat(scale.astype(_F64), group, axis=1)
     w = (q.astype(_F64) - zz) * ss
     if s16 is not None:
         w = w / s16.astype(_F64)[None, :]
@@ -261,7 +264,7 @@ def dequantize(q: np.ndarray, z: np.ndarray, scale: np.ndarray, s16: np.ndarray 
 
 # --------------------------------------------------------------------------- a5/a6
 def search_errors(X16: np.ndarray, W16: np.ndarray, n_grid: int = N_GRID, grid_points=None,
-                  zero_point: bool = True) -> dict:
+                  zero_point: bool = True, group: int = GROUP) -> dict:
     """Output error of every candidate scale.
 
     [AWQ-PRACTICE] §2.2 and §3.3 step 4: grid search over a candidate interval so
@@ -283,7 +286,7 @@ def search_errors(X16: np.ndarray, W16: np.ndarray, n_grid: int = N_GRID, grid_p
     err = np.full(n_grid, np.nan, dtype=_F64)
     points = range(n_grid) if grid_points is None else grid_points
     for i in points:
-        r = quantize_groups(W16, s16[i], zero_point=zero_point)
+        r = quantize_groups(W16, s16[i], zero_point=zero_point, group=group)
         flags |= r["flags"]
         What = dequantize(r["q"], r["z"], r["scale"], s16[i])
         D = Wd - What
@@ -292,21 +295,22 @@ def search_errors(X16: np.ndarray, W16: np.ndarray, n_grid: int = N_GRID, grid_p
     return {"alpha": alpha, "a": a, "s16": s16, "s64": s64, "err": err, "flags": flags}
 
 
-def search_scales(X16: np.ndarray, W16: np.ndarray, n_grid: int = N_GRID, zero_point: bool = True) -> dict:
+def search_scales(X16: np.ndarray, W16: np.ndarray, n_grid: int = N_GRID, zero_point: bool = True,
+                  group: int = GROUP) -> dict:
     """a1..a6: the chosen grid index (first minimum), its scale and its packed weights.
 
     [AWQ-PRACTICE] §3.3 steps 4-5: pick the s with the smallest error, then
     quantize with it and keep the scale. Ties go to the smallest index (closest to
     plain RTN).
     """
-    r = search_errors(X16, W16, n_grid, zero_point=zero_point)
+    r = search_errors(X16, W16, n_grid, zero_point=zero_point, group=group)
     err = r["err"]
     best = 0
     for i in range(1, n_grid):
         if err[i] < err[best]:
             best = i
     s_best = r["s16"][best].copy()
-    qweight, scales, zeros, f = quantize_pack(W16, s_best, zero_point=zero_point)
+    qweight, scales, zeros, f = quantize_pack(W16, s_best, zero_point=zero_point, group=group)
     r.update(best_idx=best, s_best=s_best, qweight=qweight, scales=scales, zeros=zeros,
              gap=relative_gap(err), flags=r["flags"] | f)
     return r
@@ -325,7 +329,7 @@ def clip_ratios(clip_steps: int = CLIP_STEPS, n_shrink: int = CLIP_STEPS // 2) -
 
 def clip_errors(X16: np.ndarray, W16: np.ndarray, s16: np.ndarray | None = None,
                 clip_steps: int = CLIP_STEPS, n_shrink: int = CLIP_STEPS // 2,
-                zero_point: bool = True) -> np.ndarray:
+                zero_point: bool = True, group: int = GROUP) -> np.ndarray:
     """Per-group output error of every shrink ratio, fp64 [n_shrink][N][G].
 
     Weight-clipping search ([NXMR] §5.1 "精度下降严重": tune clip_steps, 200 suggested,
@@ -336,27 +340,27 @@ def clip_errors(X16: np.ndarray, W16: np.ndarray, s16: np.ndarray | None = None,
         err[i, n, g] = sum_t ( sum_{k in g} X_tk D_nk )^2,  D = W - Q_r(W diag(s)) diag(1/s).
     """
     N, K = W16.shape
-    G = K // GROUP
+    G = K // group
     Xd = X16.astype(_F64)
     Wd = W16.astype(_F64)
     ratios = clip_ratios(clip_steps, n_shrink)
     err = np.empty((n_shrink, N, G), dtype=_F64)
     for i, r in enumerate(ratios):
-        qz = quantize_groups(W16, s16, np.full((N, G), r, dtype=_F32), zero_point)
+        qz = quantize_groups(W16, s16, np.full((N, G), r, dtype=_F32), zero_point, group)
         D = Wd - dequantize(qz["q"], qz["z"], qz["scale"], s16)
         for g in range(G):
-            E = Xd[:, g * GROUP:(g + 1) * GROUP] @ D[:, g * GROUP:(g + 1) * GROUP].T
+            E = Xd[:, g * group:(g + 1) * group] @ D[:, g * group:(g + 1) * group].T
             err[i, :, g] = np.sum(E * E, axis=0)
     return err
 
 
 def clip_search(X16: np.ndarray, W16: np.ndarray, s16: np.ndarray | None = None,
                 clip_steps: int = CLIP_STEPS, n_shrink: int = CLIP_STEPS // 2,
-                zero_point: bool = True) -> dict:
+                zero_point: bool = True, group: int = GROUP) -> dict:
     """Per group, the first ratio index with the smallest error, and the weight packed
     with those ratios. Returns dict(idx uint8 [N][G], ratio fp32 [N][G], err fp64
     [n_shrink][N][G], qweight, scales, zeros, flags)."""
-    err = clip_errors(X16, W16, s16, clip_steps, n_shrink, zero_point)
+    err = clip_errors(X16, W16, s16, clip_steps, n_shrink, zero_point, group)
     idx = np.zeros(err.shape[1:], dtype=np.int64)
     best = err[0].copy()
     for i in range(1, n_shrink):
@@ -364,7 +368,7 @@ def clip_search(X16: np.ndarray, W16: np.ndarray, s16: np.ndarray | None = None,
         idx[better] = i
         best[better] = err[i][better]
     ratio = clip_ratios(clip_steps, n_shrink)[idx]
-    qweight, scales, zeros, flags = quantize_pack(W16, s16, ratio, zero_point)
+    qweight, scales, zeros, flags = quantize_pack(W16, s16, ratio, zero_point, group)
     return {"idx": idx.astype(np.uint8), "ratio": ratio, "err": err, "qweight": qweight,
             "scales": scales, "zeros": zeros, "flags": flags}
 
@@ -485,7 +489,7 @@ def relative_gap(err: np.ndarray) -> float:
     return float((e[1] - e[0]) / e[0])
 
 
-def packed_bytes(N: int, K: int) -> int:
+def packed_bytes(N: int, K: int, group: int = GROUP) -> int:
     """Bytes of the packed format for one [N][K] weight: codes + fp16 scales + zero nibbles."""
-    G = K // GROUP
+    G = K // group
     return N * (K // 2) + N * G * 2 + N * ((G + 1) // 2)

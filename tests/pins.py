@@ -49,9 +49,10 @@ def check_codes_nearest(w_scaled: np.ndarray, q: np.ndarray, z: np.ndarray, scal
     """
     bad = []
     N, K = q.shape
+    group = K // np.asarray(scale).shape[1]
     for n in range(N):
         for k in range(K):
-            j = k // GROUP
+            j = k // group
             sc = frac(scale[n, j])
             zz = int(z[n, j])
             wv = frac(w_scaled[n, k])
@@ -80,9 +81,11 @@ def check_scale_zero(w_scaled: np.ndarray, z: np.ndarray, scale: np.ndarray, rat
     """
     bad = []
     N, K = w_scaled.shape
+    G = np.asarray(scale).shape[1]
+    group = K // G
     for n in range(N):
-        for j in range(K // GROUP):
-            g = w_scaled[n, j * GROUP:(j + 1) * GROUP]
+        for j in range(G):
+            g = w_scaled[n, j * group:(j + 1) * group]
             mx, mn = frac(g.max()), frac(g.min())
             if ratio is not None:
                 r = frac(ratio[n, j])
@@ -108,11 +111,12 @@ def exact_search_error(X16: np.ndarray, W16: np.ndarray, s16: np.ndarray, q, z, 
     """P7: err = sum_t sum_n (sum_k X_tk D_nk)^2 with D = W - (q - z) sc / s, exactly."""
     T, K = X16.shape
     N = W16.shape[0]
+    group = K // np.asarray(scale).shape[1]
     total = Fraction(0)
     for n in range(N):
         D = []
         for k in range(K):
-            j = k // GROUP
+            j = k // group
             what = (int(q[n, k]) - int(z[n, j])) * frac(scale[n, j]) / frac(s16[k])
             D.append(frac(W16[n, k]) - what)
         for t in range(T):
@@ -126,11 +130,13 @@ def exact_group_errors(X16: np.ndarray, W16: np.ndarray, s16, q, z, scale) -> li
     exactly (s16 None means s = 1)."""
     T, K = X16.shape
     N = W16.shape[0]
+    G = np.asarray(scale).shape[1]
+    group = K // G
     out = []
     for n in range(N):
         row = []
-        for j in range(K // GROUP):
-            ks = range(j * GROUP, (j + 1) * GROUP)
+        for j in range(G):
+            ks = range(j * group, (j + 1) * group)
             D = {}
             for k in ks:
                 sk = frac(s16[k]) if s16 is not None else Fraction(1)
