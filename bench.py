@@ -243,7 +243,7 @@ def main():
     # Weight clipping after the scale search: 20 shrink ratios (r = 1 .. 0.905 on the
     # clip_steps = 200 grid) per group of each group's W diag(s).
     CLIP_SHRINK = 20
-    clip_ws = {g: torch.empty(awq.load_library().awq_clip_search_workspace_size(CALIB_T, N, K, CLIP_SHRINK),
+    clip_ws = {g: torch.empty(awq.load_library().awq_clip_search_workspace_size(CALIB_T, N, K, CLIP_SHRINK, None),
                               dtype=torch.uint8, device=dev) for g, (N, K) in SEARCH_GROUPS.items()}
     clip_out = {}
 

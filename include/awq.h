@@ -3,7 +3,7 @@
  *
  * AWQ (activation-aware weight quantization) keeps activations in 16-bit and stores
  * weights as 4-bit integers, one fp16 scale and one 4-bit zero point per group of
- * 128 consecutive input channels; before quantizing, input channel k of the weight is
+ * 128 (or 64) consecutive input channels; before quantizing, input channel k of the weight is
  * multiplied by a scale s_k picked from offline activation magnitudes, and the
  * activation side carries 1/s_k (an equivalent transform).
  *
@@ -43,7 +43,7 @@ typedef enum awq_status {
   AWQ_OK = 0,
   AWQ_ERR_NULL_POINTER = 1,  /* a required pointer is NULL                          */
   AWQ_ERR_BAD_SHAPE = 2,     /* a size < 1, K % 128 != 0, T above 8192, ...          */
-  AWQ_ERR_UNSUPPORTED = 3,   /* config other than w_bit 4 / group 128 / zero point on */
+  AWQ_ERR_UNSUPPORTED = 3,   /* config outside w_bit 4 / group 128 or 64 / zp 0 or 1  */
   AWQ_ERR_MISALIGNED = 4,    /* a base pointer is not 16-byte aligned                */
   AWQ_ERR_WORKSPACE = 5,     /* workspace missing or smaller than the query returns  */
   AWQ_ERR_HIP = 6            /* the HIP runtime reported an error on launch          */
@@ -51,8 +51,11 @@ typedef enum awq_status {
 
 /* Quantization config ([SKILL] "如何使用该技能 / 步骤 2": quant_config zero_point, q_group_size,
  * w_bit; the page's "version" GEMM/GEMV switch becomes dispatch on M inside
- * awq_linear_w4a16). Supported: w_bit = 4, group_size = 128, zero_point = 1 or 0,
- * 1 <= n_grid <= 64. NULL config pointers mean {4, 128, 1, 20}.
+ * awq_linear_w4a16). Supported: w_bit = 4, group_size = 128 or 64 ([PRACTICE] §2.3:
+ * 128 is the usual group, 64 also in use), zero_point = 1 or 0, 1 <= n_grid <= 64.
+ * NULL config pointers mean {4, 128, 1, 20}. Every entry point takes the group size from
+ * the config; K stays a multiple of 128 in both cases, so a 64-channel group never
+ * straddles a 128-channel step of the kernels.
  * zero_point = 0 ([PRACTICE] §3.3 advises it; [GPTQ-AWQ] gives the signed range -8..7):
  * sc = max|w'| / 7, q - 8 = clamp(rint(w'/sc_h), -8, 7), stored offset by 8 with every
  * zero nibble 8 -- the same packed format, so the linear entry points are unchanged;
@@ -84,7 +87,8 @@ typedef enum awq_linear_kernel {
  * awq_quantize_pack -- group-wise asymmetric 4-bit quantization of W * diag(s), packed.
  *   [PRACTICE] §2.3 (128 consecutive input channels share one step), §3.3 step 5;
  *   [GPTQ-AWQ] "大模型量化的核心原理与位宽选择" (4-bit integer + scale + zero point).
- *   Per row n and group j, in fp32 with round-to-nearest-even:
+ *   Per row n and group j (g = group_size consecutive channels), in fp32 with
+ *   round-to-nearest-even:
  *     w' = w * s_k;  sc = max((max w' - min w') / 15, 2^-14) (clamped at 65504);
  *     sc_h = fp16(sc);  z = clamp(rint(-min w' / sc_h), 0, 15);
  *     q = clamp(rint(w' / sc_h) + z, 0, 15).
@@ -93,8 +97,8 @@ typedef enum awq_linear_kernel {
  *   qweight  uint32 [N][K/8]      out: word w holds the codes of k = 8w..8w+7; nibble j (bits
  *                                 4j..4j+3) holds k = 8w + (0,2,4,6,1,3,5,7)[j], so each byte
  *                                 holds one channel pair (2p low nibble, 2p+1 high nibble)
- *   scales   fp16 [N][K/128]      out: sc_h
- *   zeros    uint8 [N][ceil(G/2)] out: G = K/128; low nibble = even group, high = odd group
+ *   scales   fp16 [N][G]          out: sc_h, G = K/g
+ *   zeros    uint8 [N][ceil(G/2)] out: low nibble = even group, high = odd group
  *   flags    uint32 [1] or NULL   NONFINITE_INPUT, SCALE_CLAMPED
  */
 awq_status awq_quantize_pack(const void* W, int64_t N, int64_t K, const void* s,
@@ -207,11 +211,13 @@ awq_status awq_linear_w4a16_gated_silu_ex(const void* X, int64_t M, const uint32
  *   and keeps the first minimum. Contraction and its accuracy as in awq_search_scales.
  *   X fp16 [T][K], 1 <= T <= 512 (else AWQ_ERR_BAD_SHAPE: one block scores all tokens);
  *   W fp16 [N][K]; s fp16 [K] or NULL; 1 <= n_shrink <= min(clip_steps, 256).
- *   clip_idx uint8 [N][K/128] out (pass to awq_quantize_pack_clipped); err fp64 [N][K/128]
- *   out, the chosen error, or NULL. workspace: device, awq_clip_search_workspace_size
- *   bytes (n_shrink N K/128 doubles plus N + 1 floats), 16-byte aligned.
+ *   clip_idx uint8 [N][G] out (pass to awq_quantize_pack_clipped); err fp64 [N][G]
+ *   out, the chosen error, or NULL; G = K / group_size. workspace: device,
+ *   awq_clip_search_workspace_size bytes (n_shrink N G doubles plus N + 1 floats; 0 for an
+ *   unsupported config or shape), 16-byte aligned.
  */
-size_t awq_clip_search_workspace_size(int64_t T, int64_t N, int64_t K, int32_t n_shrink);
+size_t awq_clip_search_workspace_size(int64_t T, int64_t N, int64_t K, int32_t n_shrink,
+                                      const awq_config* cfg);
 awq_status awq_clip_search(const void* X, int64_t T, const void* W, int64_t N, int64_t K,
                            const void* s, int32_t clip_steps, int32_t n_shrink,
                            const awq_config* cfg, uint8_t* clip_idx, double* err,
@@ -221,7 +227,7 @@ awq_status awq_clip_search(const void* X, int64_t T, const void* W, int64_t N, i
 /*
  * awq_quantize_pack_clipped -- awq_quantize_pack with per-group clipping: group (n, g)
  *   quantizes from its extremes times r = (clip_steps - clip_idx[n][g]) / clip_steps
- *   (fp32); weights beyond the shrunk range take the end codes. clip_idx uint8 [N][K/128]
+ *   (fp32); weights beyond the shrunk range take the end codes. clip_idx uint8 [N][K/g]
  *   (awq_clip_search's output) or NULL (plain awq_quantize_pack); 1 <= clip_steps <= 65535.
  */
 awq_status awq_quantize_pack_clipped(const void* W, int64_t N, int64_t K, const void* s,

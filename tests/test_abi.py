@@ -57,7 +57,9 @@ def test_quantize_pack_validation(lib):
     assert _qp(lib, cfg=C.byref(bad)) == 3
     bad = _abi.config(n_grid=0)
     assert _qp(lib, cfg=C.byref(bad)) == 3
-    bad = _abi.config(group_size=64)
+    bad = _abi.config(group_size=32)
+    assert _qp(lib, cfg=C.byref(bad)) == 3
+    bad = _abi.config(group_size=256)
     assert _qp(lib, cfg=C.byref(bad)) == 3
     bad = _abi.config(zero_point=2)
     assert _qp(lib, cfg=C.byref(bad)) == 3
@@ -142,7 +144,11 @@ def test_clip_validation(lib):
     assert call(T=513) == 2 and call(T=0) == 2 and call(K=130) == 2
     assert call(ns=201) == 2 and call(ns=257, steps=300) == 2 and call(ns=0) == 2
     assert call(ws=None) == 5 and call(wsb=C.c_size_t(16)) == 5
-    need = lib.awq_clip_search_workspace_size(64, 64, 256, 20)
+    need = lib.awq_clip_search_workspace_size(64, 64, 256, 20, None)
     assert need >= 20 * 64 * 2 * 8
+    g64 = _abi.config(group_size=64)
+    assert lib.awq_clip_search_workspace_size(64, 64, 256, 20, C.byref(g64)) >= 20 * 64 * 4 * 8
+    bad = _abi.config(group_size=32)
+    assert lib.awq_clip_search_workspace_size(64, 64, 256, 20, C.byref(bad)) == 0
     assert lib.awq_quantize_pack_clipped(FAKE, 64, 256, None, FAKE, 0, None, FAKE, FAKE, FAKE,
                                          None, None) == 2

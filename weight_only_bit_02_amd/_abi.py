@@ -35,7 +35,7 @@ CFG = C.POINTER(AwqConfig)
 SIGNATURES = {
     "awq_quantize_pack": (C.c_int, [P, I64, I64, P, CFG, P, P, P, P, P]),
     "awq_quantize_pack_clipped": (C.c_int, [P, I64, I64, P, P, C.c_int32, CFG, P, P, P, P, P]),
-    "awq_clip_search_workspace_size": (C.c_size_t, [I64, I64, I64, C.c_int32]),
+    "awq_clip_search_workspace_size": (C.c_size_t, [I64, I64, I64, C.c_int32, CFG]),
     "awq_clip_search": (C.c_int, [P, I64, P, I64, I64, P, C.c_int32, C.c_int32, CFG, P, P, P,
                                   C.c_size_t, P, P]),
     "awq_activation_stats_workspace_size": (C.c_size_t, [I64, I64]),

@@ -15,8 +15,8 @@ awq_config resolve(const awq_config* cfg) {
 }
 
 bool supported(const awq_config& c) {
-  return c.w_bit == 4 && c.group_size == 128 && (c.zero_point == 0 || c.zero_point == 1) &&
-         c.n_grid >= 1 && c.n_grid <= 64;
+  return c.w_bit == 4 && (c.group_size == 128 || c.group_size == 64) &&
+         (c.zero_point == 0 || c.zero_point == 1) && c.n_grid >= 1 && c.n_grid <= 64;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -57,12 +57,12 @@ struct ClipLayout {
   size_t rowmax, srange, err, total;
 };
 
-ClipLayout clip_layout(int64_t N, int64_t K, int n_shrink) {
+ClipLayout clip_layout(int64_t N, int64_t K, int n_shrink, int group) {
   ClipLayout L;
   L.rowmax = 0;
   L.srange = align256((size_t)N * 4);
   L.err = align256(L.srange + 4);
-  L.total = align256(L.err + (size_t)n_shrink * N * (K / 128) * 8);
+  L.total = align256(L.err + (size_t)n_shrink * N * (K / group) * 8);
   return L;
 }
 
@@ -87,7 +87,7 @@ const char* awq_status_string(awq_status s) {
     case AWQ_OK: return "ok";
     case AWQ_ERR_NULL_POINTER: return "a required pointer is NULL";
     case AWQ_ERR_BAD_SHAPE: return "bad shape (sizes must be >= 1, K a multiple of 128, T <= 8192)";
-    case AWQ_ERR_UNSUPPORTED: return "unsupported config (w_bit 4, group_size 128, zero_point 1, 1 <= n_grid <= 64)";
+    case AWQ_ERR_UNSUPPORTED: return "unsupported config (w_bit 4, group_size 128 or 64, zero_point 0 or 1, 1 <= n_grid <= 64)";
     case AWQ_ERR_MISALIGNED: return "a base pointer is not 16-byte aligned";
     case AWQ_ERR_WORKSPACE: return "workspace missing or too small";
     case AWQ_ERR_HIP: return "HIP launch error";
@@ -118,7 +118,8 @@ awq_status awq_quantize_pack_clipped(const void* W, int64_t N, int64_t K, const 
     return AWQ_ERR_MISALIGNED;
   return hip_status(awq::launch_quant_pack((const uint16_t*)W, N, K, (const uint16_t*)s, qweight,
                                            (uint16_t*)scales, zeros, clip_idx, clip_steps,
-                                           c.zero_point == 0, flags, (hipStream_t)stream));
+                                           c.zero_point == 0, c.group_size, flags,
+                                           (hipStream_t)stream));
 }
 
 size_t awq_activation_stats_workspace_size(int64_t T, int64_t K) {
@@ -188,7 +189,7 @@ awq_status awq_search_scales(const void* X, int64_t T, const void* W, int64_t N,
   if (e == hipSuccess) e = awq::launch_scalegen(act, K, c.n_grid, sg, st);
   if (e == hipSuccess)
     e = awq::launch_search_err(Xh, T, (const uint16_t*)W, N, K, sg, c.n_grid, c.zero_point == 0,
-                               (float*)(ws + L.rowmax), (float*)(ws + L.srange), partials, flags, st);
+                               c.group_size, (float*)(ws + L.rowmax), (float*)(ws + L.srange), partials, flags, st);
   if (e == hipSuccess)
     e = awq::launch_search_reduce(partials, c.n_grid, L.n_partials, sg, K, (uint16_t*)s_best,
                                   best_idx, err, st);
@@ -224,11 +225,14 @@ static awq_status linear_common(const void* X, int64_t M, const uint32_t* qweigh
   auto* Yh = (uint16_t*)Y;
   switch (kernel) {
     case AWQ_LINEAR_GEMV:
-      return hip_status(awq::launch_gemv(Xh, M, qweight, sc, zeros, N, K, Yh, gated, st));
+      return hip_status(
+          awq::launch_gemv(Xh, M, qweight, sc, zeros, N, K, c.group_size, Yh, gated, st));
     case AWQ_LINEAR_SKINNY:
-      return hip_status(awq::launch_gemv_mfma(Xh, M, qweight, sc, zeros, N, K, Yh, gated, st));
+      return hip_status(
+          awq::launch_gemv_mfma(Xh, M, qweight, sc, zeros, N, K, c.group_size, Yh, gated, st));
     default:
-      return hip_status(awq::launch_gemm(Xh, M, qweight, sc, zeros, N, K, Yh, gated, st));
+      return hip_status(
+          awq::launch_gemm(Xh, M, qweight, sc, zeros, N, K, c.group_size, Yh, gated, st));
   }
 }
 
@@ -264,10 +268,12 @@ awq_status awq_linear_w4a16_gated_silu(const void* X, int64_t M, const uint32_t*
                                         AWQ_LINEAR_AUTO, stream);
 }
 
-size_t awq_clip_search_workspace_size(int64_t T, int64_t N, int64_t K, int32_t n_shrink) {
+size_t awq_clip_search_workspace_size(int64_t T, int64_t N, int64_t K, int32_t n_shrink,
+                                      const awq_config* cfg) {
   (void)T;
-  if (!good_nk(N, K) || n_shrink < 1) return 0;
-  return clip_layout(N, K, n_shrink).total;
+  const awq_config c = resolve(cfg);
+  if (!supported(c) || !good_nk(N, K) || n_shrink < 1) return 0;
+  return clip_layout(N, K, n_shrink, c.group_size).total;
 }
 
 awq_status awq_clip_search(const void* X, int64_t T, const void* W, int64_t N, int64_t K,
@@ -285,16 +291,16 @@ awq_status awq_clip_search(const void* X, int64_t T, const void* W, int64_t N, i
   if (!aligned16(X) || !aligned16(W) || (s && !aligned16(s)) || (err && !aligned16(err)) ||
       (flags && !aligned4(flags)))
     return AWQ_ERR_MISALIGNED;
-  const ClipLayout L = clip_layout(N, K, n_shrink);
+  const ClipLayout L = clip_layout(N, K, n_shrink, c.group_size);
   if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return AWQ_ERR_WORKSPACE;
   char* ws = (char*)workspace;
   hipStream_t st = (hipStream_t)stream;
   double* errs = (double*)(ws + L.err);
   hipError_t e = awq::launch_clip_err((const uint16_t*)X, T, (const uint16_t*)W, N, K,
                                       (const uint16_t*)s, clip_steps, n_shrink, c.zero_point == 0,
-                                      (float*)(ws + L.rowmax), (float*)(ws + L.srange), errs, flags, st);
+                                      c.group_size, (float*)(ws + L.rowmax), (float*)(ws + L.srange), errs, flags, st);
   if (e == hipSuccess)
-    e = awq::launch_clip_reduce(errs, n_shrink, N, K / 128, clip_idx, err, st);
+    e = awq::launch_clip_reduce(errs, n_shrink, N, K / c.group_size, clip_idx, err, st);
   return hip_status(e);
 }
 

@@ -53,6 +53,24 @@ __device__ __forceinline__ void row16_minmax(float& mn, float& mx) {
   mx = fmaxf(mx, dpp_f32<kDppRowRor8>(mx));
 }
 
+// Min / max over the 8-lane halves of each DPP row (64-channel groups): quad butterflies,
+// then row_half_mirror, which pairs lane i of a half with lane 7 - i (the other quad).
+constexpr int kDppRowHalfMirror = 0x141;
+__device__ __forceinline__ void row8_minmax(float& mn, float& mx) {
+  mn = fminf(mn, dpp_f32<kDppQuadXor1>(mn));
+  mx = fmaxf(mx, dpp_f32<kDppQuadXor1>(mx));
+  mn = fminf(mn, dpp_f32<kDppQuadXor2>(mn));
+  mx = fmaxf(mx, dpp_f32<kDppQuadXor2>(mx));
+  mn = fminf(mn, dpp_f32<kDppRowHalfMirror>(mn));
+  mx = fmaxf(mx, dpp_f32<kDppRowHalfMirror>(mx));
+}
+
+// Group min / max for groups of 16 lanes x 8 channels (g = 128) or 8 lanes (g = 64).
+__device__ __forceinline__ void group_minmax(float& mn, float& mx, bool g64) {
+  if (g64) row8_minmax(mn, mx);
+  else row16_minmax(mn, mx);
+}
+
 __device__ __forceinline__ float row16_sum(float v) {
   v += dpp_f32<kDppQuadXor1>(v);
   v += dpp_f32<kDppQuadXor2>(v);

@@ -3,7 +3,8 @@
 // "AWQ量化技术Skill", "主要功能和特点": a GEMM kernel serves batch sizes above one;
 // "AWQ量化实战" §2.3 / §3.4: weights stay 4-bit in memory and are dequantized on the fly.
 //
-// Block tile 128 (tokens) x 256 (output channels), K step 128 (one group), four waves side by side
+// Block tile 128 (tokens) x 256 (output channels), K step 128 (one group of 128, or two of
+// 64: the lane half's 64 channels are then one group), four waves side by side
 // along N, each owning 128 x 64 = 4 x 2 tiles of v_mfma_f32_32x32x16_f16.
 //   - A (activations) is shared by the four waves: it goes global -> registers -> LDS,
 //     double-buffered
@@ -36,7 +37,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBM = 128;
 constexpr int kBN = 256;
-constexpr int kBK = 128;              // one quantization group per K step
+constexpr int kBK = 128;              // channels per K step: one group of 128 or two of 64
 constexpr int kAStride = kBK + 8;     // halves per LDS row of A (16-byte pad)
 constexpr int kXcds = 8;
 
@@ -68,7 +69,7 @@ struct GemmStage {
 template <bool GATED>
 __global__ void __launch_bounds__(256)
     k_gemm(const uint16_t* X, int64_t M, const uint32_t* qweight, const uint16_t* scales,
-           const uint8_t* zeros, int64_t N, int64_t K, uint16_t* __restrict__ Y, int64_t mt,
+           const uint8_t* zeros, int64_t N, int64_t K, int group, uint16_t* __restrict__ Y, int64_t mt,
            int64_t nt, int64_t per_xcd) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kAStride];
 
@@ -84,8 +85,11 @@ __global__ void __launch_bounds__(256)
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int m32 = lane & 31, kh = lane >> 5;
-  const int64_t G = K / kGroup, zb = (G + 1) / 2, words = K / 8;
-  const int64_t nsteps = G;
+  // 64-channel groups: lane half kh of step `step` lies in group 2 step + kh, whose zero
+  // is nibble kh of byte `step`; 128-channel groups: group `step`, nibble step & 1
+  const int g64 = group == 64;
+  const int64_t Gs = K / group, zb = (Gs + 1) / 2, words = K / 8;
+  const int64_t nsteps = K / kBK;
   const uint32_t magic = gemm_magic();
 
   // A staging map: 128 rows x 128 channels = 2048 16-byte pieces, 8 per thread.
@@ -117,8 +121,8 @@ __global__ void __launch_bounds__(256)
   auto load = [&](GemmStage& st, int64_t step) {
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      st.zb[b] = zeros[b_col[b] * zb + (step >> 1)];
-      st.sc[b] = scales[b_col[b] * G + step];
+      st.zb[b] = zeros[b_col[b] * zb + (step >> (1 - g64))];
+      st.sc[b] = scales[b_col[b] * Gs + (step << g64) + (g64 & kh)];
     }
 #pragma unroll
     for (int b = 0; b < 2; ++b)
@@ -159,9 +163,10 @@ __global__ void __launch_bounds__(256)
     // path and the waits below can be exact
     load(nn, step + 2 < nsteps ? step + 2 : nsteps - 1);
     half2v zz[2], s2[2];
+    const int hi = g64 ? kh : (int)(step & 1);
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      const uint32_t z = (step & 1) ? (cur.zb[b] >> 4) : (cur.zb[b] & 0xF);
+      const uint32_t z = hi ? (cur.zb[b] >> 4) : (cur.zb[b] & 0xF);
       const uint32_t zbits = 0x6400u + z;
       zz[b] = -__builtin_bit_cast(half2v, zbits | (zbits << 16));
       s2[b] = __builtin_bit_cast(half2v, cur.sc[b] | (cur.sc[b] << 16));
@@ -247,16 +252,16 @@ __global__ void __launch_bounds__(256)
 
 hipError_t launch_gemm(const uint16_t* X, int64_t M, const uint32_t* qweight,
                        const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
-                       uint16_t* Y, bool gated, hipStream_t stream) {
+                       int group, uint16_t* Y, bool gated, hipStream_t stream) {
   const int64_t mt = (M + kBM - 1) / kBM;
   const int64_t nt = gated ? (N / 2 + kBN / 2 - 1) / (kBN / 2) : (N + kBN - 1) / kBN;
   const int64_t per_xcd = (mt * nt + kXcds - 1) / kXcds;
   if (gated)
     hipLaunchKernelGGL(k_gemm<true>, dim3((unsigned)(per_xcd * kXcds)), dim3(256), 0, stream, X,
-                       M, qweight, scales, zeros, N, K, Y, mt, nt, per_xcd);
+                       M, qweight, scales, zeros, N, K, group, Y, mt, nt, per_xcd);
   else
     hipLaunchKernelGGL(k_gemm<false>, dim3((unsigned)(per_xcd * kXcds)), dim3(256), 0, stream, X,
-                       M, qweight, scales, zeros, N, K, Y, mt, nt, per_xcd);
+                       M, qweight, scales, zeros, N, K, group, Y, mt, nt, per_xcd);
   return hipGetLastError();
 }
 

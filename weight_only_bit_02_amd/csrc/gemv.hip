@@ -31,7 +31,7 @@ template <int M, int R, bool GATED>
 __global__ void __launch_bounds__(256)
     k_gemv(const uint16_t* __restrict__ X, const uint32_t* __restrict__ qweight,
            const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int64_t N,
-           int64_t K, uint16_t* __restrict__ Y) {
+           int64_t K, int gsh, uint16_t* __restrict__ Y) {
   static_assert(!GATED || R == 2, "a gated wave owns one gate row and one up row");
   const int lane = threadIdx.x & 63;
   const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
@@ -39,7 +39,7 @@ __global__ void __launch_bounds__(256)
   const int64_t row0 = GATED ? wave : wave * R;
   if (row0 >= (GATED ? nh : N)) return;  // whole wave leaves together
   const int64_t C = K / 32;  // chunks per row
-  const int64_t G = K / kGroup;
+  const int64_t G = (K >> (gsh + 5));
   const int64_t zb = (G + 1) / 2;
   const int64_t words = K / 8;
 
@@ -55,7 +55,7 @@ __global__ void __launch_bounds__(256)
     for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
 
   for (int64_t c = lane; c < C; c += 64) {
-    const int64_t g = c >> 2;
+    const int64_t g = c >> gsh;  // group of this 32-channel chunk
     half2v qz[R][16];
     float sc[R];
 #pragma unroll
@@ -131,7 +131,7 @@ __device__ __forceinline__ void gemv1_load(GemvBatch<R, U>& bt, const uint32_t* 
                                            const uint16_t* scales, const uint8_t* zeros,
                                            const int64_t (&rows)[R],
                                            int64_t C, int64_t words, int64_t G, int64_t zbytes,
-                                           int64_t b, int lane) {
+                                           int64_t b, int lane, int gsh) {
   // Straight-line loads (chunk index clamped, results past the row end unused), so the
   // compiler can keep them all in flight and wait for each one only where it is used.
 #pragma unroll
@@ -141,8 +141,8 @@ __device__ __forceinline__ void gemv1_load(GemvBatch<R, U>& bt, const uint32_t* 
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       bt.cw[r][u] = *reinterpret_cast<const uint4*>(qweight + rows[r] * words + c * 4);
-      bt.sc[r][u] = scales[rows[r] * G + (c >> 2)];
-      bt.zb[r][u] = zeros[rows[r] * zbytes + (c >> 3)];
+      bt.sc[r][u] = scales[rows[r] * G + (c >> gsh)];
+      bt.zb[r][u] = zeros[rows[r] * zbytes + (c >> (gsh + 1))];
     }
   }
 }
@@ -165,7 +165,7 @@ __device__ __forceinline__ uint32_t magic_1024x2() {
 template <int R, int U>
 __device__ __forceinline__ void gemv1_compute(const GemvBatch<R, U>& bt, const uint4* __restrict__ xs,
                                               float (&acc)[R], int64_t C, int64_t b, int lane,
-                                              uint32_t magic) {
+                                              uint32_t magic, int gsh) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t c = (b * U + u) * 64 + lane;
@@ -179,7 +179,7 @@ __device__ __forceinline__ void gemv1_compute(const GemvBatch<R, U>& bt, const u
         xq[w * 4 + 2] = __builtin_bit_cast(half2v, v.z);
         xq[w * 4 + 3] = __builtin_bit_cast(half2v, v.w);
       }
-      const int nib = (int)((c >> 2) & 1) * 4;
+      const int nib = (int)((c >> gsh) & 1) * 4;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const uint32_t z = (bt.zb[r][u] >> nib) & 0xF;
@@ -224,7 +224,7 @@ __device__ __forceinline__ void lds_barrier() {
 template <int R, int U, int XR, int WPB, bool GATED>
 __global__ void __launch_bounds__(WPB * 64)
     k_gemv1(const uint16_t* X, const uint32_t* qweight, const uint16_t* scales,
-            const uint8_t* zeros, int64_t N, int64_t K, uint16_t* Y) {
+            const uint8_t* zeros, int64_t N, int64_t K, int gsh, uint16_t* Y) {
   static_assert(!GATED || R == 2, "a gated wave owns one gate row and one up row");
   // (no __restrict__: the code loads must stay ordered before the LDS barrier below)
   // XR * WPB * 64 entries (>= K / 8): entry i holds channels 8i..8i+7
@@ -234,7 +234,7 @@ __global__ void __launch_bounds__(WPB * 64)
   const int64_t nh = N / 2;
   const int64_t wave_id = (int64_t)blockIdx.x * WPB + (tid >> 6);
   const int64_t row0 = GATED ? (wave_id < nh ? wave_id : nh - 1) : wave_id * R;
-  const int64_t C = K / 32, G = K / kGroup, zbytes = (G + 1) / 2, words = K / 8;
+  const int64_t C = K / 32, G = (K >> (gsh + 5)), zbytes = (G + 1) / 2, words = K / 8;
   const int64_t nb = (C + 64 * U - 1) / (64 * U);
   __builtin_assume(nb >= 1);
   int64_t rows[R];
@@ -250,7 +250,7 @@ __global__ void __launch_bounds__(WPB * 64)
   }
   __builtin_amdgcn_sched_barrier(0);
   GemvBatch<R, U> b0, b1;
-  gemv1_load(b0, qweight, scales, zeros, rows, C, words, G, zbytes, 0, lane);
+  gemv1_load(b0, qweight, scales, zeros, rows, C, words, G, zbytes, 0, lane, gsh);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < XR; ++j) {
@@ -264,15 +264,15 @@ __global__ void __launch_bounds__(WPB * 64)
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = 0.0f;
   if (nb == 1) {
-    gemv1_compute(b0, xs, acc, C, 0, lane, magic);
+    gemv1_compute(b0, xs, acc, C, 0, lane, magic, gsh);
   } else {
     for (int64_t b = 0; b < nb; b += 2) {
       const int64_t b1i = b + 1 < nb ? b + 1 : nb - 1;
-      gemv1_load(b1, qweight, scales, zeros, rows, C, words, G, zbytes, b1i, lane);
-      gemv1_compute(b0, xs, acc, C, b, lane, magic);
+      gemv1_load(b1, qweight, scales, zeros, rows, C, words, G, zbytes, b1i, lane, gsh);
+      gemv1_compute(b0, xs, acc, C, b, lane, magic, gsh);
       const int64_t b2i = b + 2 < nb ? b + 2 : nb - 1;
-      gemv1_load(b0, qweight, scales, zeros, rows, C, words, G, zbytes, b2i, lane);
-      if (b + 1 < nb) gemv1_compute(b1, xs, acc, C, b + 1, lane, magic);
+      gemv1_load(b0, qweight, scales, zeros, rows, C, words, G, zbytes, b2i, lane, gsh);
+      if (b + 1 < nb) gemv1_compute(b1, xs, acc, C, b + 1, lane, magic, gsh);
     }
   }
   if constexpr (GATED) {
@@ -289,26 +289,26 @@ __global__ void __launch_bounds__(WPB * 64)
 
 template <int R, int U, int XR, int WPB, bool GATED>
 static hipError_t launch_gemv1_x(const uint16_t* X, const uint32_t* qw, const uint16_t* sc,
-                                 const uint8_t* z, int64_t N, int64_t K, uint16_t* Y,
+                                 const uint8_t* z, int64_t N, int64_t K, int gsh, uint16_t* Y,
                                  hipStream_t stream) {
   const int64_t waves = GATED ? N / 2 : (N + R - 1) / R;
   const int64_t blocks = (waves + WPB - 1) / WPB;
   hipLaunchKernelGGL((k_gemv1<R, U, XR, WPB, GATED>), dim3((unsigned)blocks), dim3(WPB * 64),
-                     (size_t)XR * WPB * 64 * 16, stream, X, qw, sc, z, N, K, Y);
+                     (size_t)XR * WPB * 64 * 16, stream, X, qw, sc, z, N, K, gsh, Y);
   return hipGetLastError();
 }
 
 // K <= 32768: the activation row (K / 8 16-byte entries) fits XR * WPB * 64 entries.
 template <int R, int U, bool GATED, int WPB = 4>
 static hipError_t launch_gemv1(const uint16_t* X, const uint32_t* qw, const uint16_t* sc,
-                               const uint8_t* z, int64_t N, int64_t K, uint16_t* Y,
+                               const uint8_t* z, int64_t N, int64_t K, int gsh, uint16_t* Y,
                                hipStream_t stream) {
   const int64_t per_thread = (K / 8 + WPB * 64 - 1) / (WPB * 64);
-  if (per_thread <= 1) return launch_gemv1_x<R, U, 1, WPB, GATED>(X, qw, sc, z, N, K, Y, stream);
-  if (per_thread <= 2) return launch_gemv1_x<R, U, 2, WPB, GATED>(X, qw, sc, z, N, K, Y, stream);
-  if (per_thread <= 4) return launch_gemv1_x<R, U, 4, WPB, GATED>(X, qw, sc, z, N, K, Y, stream);
-  if (per_thread <= 8) return launch_gemv1_x<R, U, 8, WPB, GATED>(X, qw, sc, z, N, K, Y, stream);
-  return launch_gemv1_x<R, U, 16, WPB, GATED>(X, qw, sc, z, N, K, Y, stream);
+  if (per_thread <= 1) return launch_gemv1_x<R, U, 1, WPB, GATED>(X, qw, sc, z, N, K, gsh, Y, stream);
+  if (per_thread <= 2) return launch_gemv1_x<R, U, 2, WPB, GATED>(X, qw, sc, z, N, K, gsh, Y, stream);
+  if (per_thread <= 4) return launch_gemv1_x<R, U, 4, WPB, GATED>(X, qw, sc, z, N, K, gsh, Y, stream);
+  if (per_thread <= 8) return launch_gemv1_x<R, U, 8, WPB, GATED>(X, qw, sc, z, N, K, gsh, Y, stream);
+  return launch_gemv1_x<R, U, 16, WPB, GATED>(X, qw, sc, z, N, K, gsh, Y, stream);
 }
 
 // One batch covers K (at most 8 chunks per lane, K <= 16384), so only that path is
@@ -320,13 +320,13 @@ static hipError_t launch_gemv1(const uint16_t* X, const uint32_t* qw, const uint
 template <int U, int XR, int WPB, int RPW, bool GATED>
 __global__ void __launch_bounds__(WPB * 64)
     k_gemv1s(const uint16_t* X, const uint32_t* qweight, const uint16_t* scales,
-             const uint8_t* zeros, int64_t N, int64_t K, uint16_t* Y) {
+             const uint8_t* zeros, int64_t N, int64_t K, int gsh, uint16_t* Y) {
   static_assert(!GATED || RPW == 2, "a gated wave owns one gate row and one up row");
   extern __shared__ uint4 xs[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int64_t wave_id = (int64_t)blockIdx.x * WPB + (tid >> 6);
-  const int64_t C = K / 32, G = K / kGroup, zbytes = (G + 1) / 2, words = K / 8;
+  const int64_t C = K / 32, G = (K >> (gsh + 5)), zbytes = (G + 1) / 2, words = K / 8;
   // plain: rows wave_id * RPW + r, clamped to the wave's last row; gated: gate row n and
   // up row n + N/2, n clamped to the last output (its store rewrites the same value)
   const int64_t nh = N / 2;
@@ -350,7 +350,7 @@ __global__ void __launch_bounds__(WPB * 64)
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
     const int64_t rows[1] = {row_at(r)};
-    gemv1_load(bt[r], qweight, scales, zeros, rows, C, words, G, zbytes, 0, lane);
+    gemv1_load(bt[r], qweight, scales, zeros, rows, C, words, G, zbytes, 0, lane, gsh);
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -365,7 +365,7 @@ __global__ void __launch_bounds__(WPB * 64)
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
     float acc[1] = {0.0f};
-    gemv1_compute(bt[r], xs, acc, C, 0, lane, magic);
+    gemv1_compute(bt[r], xs, acc, C, 0, lane, magic, gsh);
     sums[r] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_sum(acc[0])), 0));
     if constexpr (!GATED) Y[row_at(r)] = f2h_bits(sums[r]);
   }
@@ -374,21 +374,21 @@ __global__ void __launch_bounds__(WPB * 64)
 
 template <int U, int XR, int WPB, int RPW, bool GATED>
 static hipError_t launch_gemv1s_x(const uint16_t* X, const uint32_t* qw, const uint16_t* sc,
-                                  const uint8_t* z, int64_t N, int64_t K, uint16_t* Y,
+                                  const uint8_t* z, int64_t N, int64_t K, int gsh, uint16_t* Y,
                                   hipStream_t stream) {
   const int64_t waves = GATED ? N / 2 : (N + RPW - 1) / RPW;
   const int64_t blocks = (waves + WPB - 1) / WPB;
   hipLaunchKernelGGL((k_gemv1s<U, XR, WPB, RPW, GATED>), dim3((unsigned)blocks), dim3(WPB * 64),
-                     (size_t)XR * WPB * 64 * 16, stream, X, qw, sc, z, N, K, Y);
+                     (size_t)XR * WPB * 64 * 16, stream, X, qw, sc, z, N, K, gsh, Y);
   return hipGetLastError();
 }
 
 // XR = U: the activation row (K / 8 entries) fits U * 256 entries, as U = ceil(K / 2048).
 template <int U, int RPW, bool GATED>
 static hipError_t launch_gemv1s(const uint16_t* X, const uint32_t* qw, const uint16_t* sc,
-                                const uint8_t* z, int64_t N, int64_t K, uint16_t* Y,
+                                const uint8_t* z, int64_t N, int64_t K, int gsh, uint16_t* Y,
                                 hipStream_t stream) {
-  return launch_gemv1s_x<U, U, 4, RPW, GATED>(X, qw, sc, z, N, K, Y, stream);
+  return launch_gemv1s_x<U, U, 4, RPW, GATED>(X, qw, sc, z, N, K, gsh, Y, stream);
 }
 
 // M = 1 dispatch (K <= 32768, so the activation row fits 64 KiB of LDS). Up to eight
@@ -398,68 +398,69 @@ static hipError_t launch_gemv1s(const uint16_t* X, const uint32_t* qw, const uin
 // chunks per lane per batch.
 template <bool GATED>
 static hipError_t launch_gemv_m1(const uint16_t* X, const uint32_t* qw, const uint16_t* sc,
-                                 const uint8_t* z, int64_t N, int64_t K, uint16_t* Y,
+                                 const uint8_t* z, int64_t N, int64_t K, int gsh, uint16_t* Y,
                                  hipStream_t stream) {
   const int64_t cpl = (K / 32 + 63) / 64;  // chunks per lane to cover K once
   const bool two = GATED || N >= 16384;
   switch (cpl) {
-    case 1: return two ? launch_gemv1s<1, 2, GATED>(X, qw, sc, z, N, K, Y, stream)
-                       : launch_gemv1s<1, 1, false>(X, qw, sc, z, N, K, Y, stream);
-    case 2: return two ? launch_gemv1s<2, 2, GATED>(X, qw, sc, z, N, K, Y, stream)
-                       : launch_gemv1s<2, 1, false>(X, qw, sc, z, N, K, Y, stream);
-    case 3: return GATED ? launch_gemv1s<3, 2, GATED>(X, qw, sc, z, N, K, Y, stream)
-                         : launch_gemv1s<3, 1, false>(X, qw, sc, z, N, K, Y, stream);
-    case 4: return GATED ? launch_gemv1s<4, 2, GATED>(X, qw, sc, z, N, K, Y, stream)
-                         : launch_gemv1s<4, 1, false>(X, qw, sc, z, N, K, Y, stream);
-    case 5: return GATED ? launch_gemv1s<5, 2, GATED>(X, qw, sc, z, N, K, Y, stream)
-                         : launch_gemv1s<5, 1, false>(X, qw, sc, z, N, K, Y, stream);
-    case 6: return GATED ? launch_gemv1s<6, 2, GATED>(X, qw, sc, z, N, K, Y, stream)
-                         : launch_gemv1s<6, 1, false>(X, qw, sc, z, N, K, Y, stream);
-    case 7: return GATED ? launch_gemv1s<7, 2, GATED>(X, qw, sc, z, N, K, Y, stream)
-                         : launch_gemv1s<7, 1, false>(X, qw, sc, z, N, K, Y, stream);
-    case 8: return GATED ? launch_gemv1s<8, 2, GATED>(X, qw, sc, z, N, K, Y, stream)
-                         : launch_gemv1s<8, 1, false>(X, qw, sc, z, N, K, Y, stream);
-    default: return GATED ? launch_gemv1<2, 4, GATED>(X, qw, sc, z, N, K, Y, stream)
-                          : launch_gemv1<1, 4, false>(X, qw, sc, z, N, K, Y, stream);
+    case 1: return two ? launch_gemv1s<1, 2, GATED>(X, qw, sc, z, N, K, gsh, Y, stream)
+                       : launch_gemv1s<1, 1, false>(X, qw, sc, z, N, K, gsh, Y, stream);
+    case 2: return two ? launch_gemv1s<2, 2, GATED>(X, qw, sc, z, N, K, gsh, Y, stream)
+                       : launch_gemv1s<2, 1, false>(X, qw, sc, z, N, K, gsh, Y, stream);
+    case 3: return GATED ? launch_gemv1s<3, 2, GATED>(X, qw, sc, z, N, K, gsh, Y, stream)
+                         : launch_gemv1s<3, 1, false>(X, qw, sc, z, N, K, gsh, Y, stream);
+    case 4: return GATED ? launch_gemv1s<4, 2, GATED>(X, qw, sc, z, N, K, gsh, Y, stream)
+                         : launch_gemv1s<4, 1, false>(X, qw, sc, z, N, K, gsh, Y, stream);
+    case 5: return GATED ? launch_gemv1s<5, 2, GATED>(X, qw, sc, z, N, K, gsh, Y, stream)
+                         : launch_gemv1s<5, 1, false>(X, qw, sc, z, N, K, gsh, Y, stream);
+    case 6: return GATED ? launch_gemv1s<6, 2, GATED>(X, qw, sc, z, N, K, gsh, Y, stream)
+                         : launch_gemv1s<6, 1, false>(X, qw, sc, z, N, K, gsh, Y, stream);
+    case 7: return GATED ? launch_gemv1s<7, 2, GATED>(X, qw, sc, z, N, K, gsh, Y, stream)
+                         : launch_gemv1s<7, 1, false>(X, qw, sc, z, N, K, gsh, Y, stream);
+    case 8: return GATED ? launch_gemv1s<8, 2, GATED>(X, qw, sc, z, N, K, gsh, Y, stream)
+                         : launch_gemv1s<8, 1, false>(X, qw, sc, z, N, K, gsh, Y, stream);
+    default: return GATED ? launch_gemv1<2, 4, GATED>(X, qw, sc, z, N, K, gsh, Y, stream)
+                          : launch_gemv1<1, 4, false>(X, qw, sc, z, N, K, gsh, Y, stream);
   }
 }
 
 template <int M, bool GATED>
 static hipError_t launch_gemv_m(const uint16_t* X, const uint32_t* qw, const uint16_t* sc,
-                                const uint8_t* z, int64_t N, int64_t K, uint16_t* Y,
+                                const uint8_t* z, int64_t N, int64_t K, int gsh, uint16_t* Y,
                                 hipStream_t stream) {
   constexpr int R = GATED ? 2 : 4;
   const int64_t waves = GATED ? N / 2 : (N + R - 1) / R;
   const int64_t blocks = (waves + 3) / 4;
   hipLaunchKernelGGL((k_gemv<M, R, GATED>), dim3((unsigned)blocks), dim3(256), 0, stream, X, qw,
-                     sc, z, N, K, Y);
+                     sc, z, N, K, gsh, Y);
   return hipGetLastError();
 }
 
 template <bool GATED>
 static hipError_t launch_gemv_t(const uint16_t* X, int64_t M, const uint32_t* qweight,
                                 const uint16_t* scales, const uint8_t* zeros, int64_t N,
-                                int64_t K, uint16_t* Y, hipStream_t stream) {
+                                int64_t K, int gsh, uint16_t* Y, hipStream_t stream) {
   switch (M) {
     case 1:
-      if (K <= 32768) return launch_gemv_m1<GATED>(X, qweight, scales, zeros, N, K, Y, stream);
-      return launch_gemv_m<1, GATED>(X, qweight, scales, zeros, N, K, Y, stream);
-    case 2: return launch_gemv_m<2, GATED>(X, qweight, scales, zeros, N, K, Y, stream);
-    case 3: return launch_gemv_m<3, GATED>(X, qweight, scales, zeros, N, K, Y, stream);
-    case 4: return launch_gemv_m<4, GATED>(X, qweight, scales, zeros, N, K, Y, stream);
-    case 5: return launch_gemv_m<5, GATED>(X, qweight, scales, zeros, N, K, Y, stream);
-    case 6: return launch_gemv_m<6, GATED>(X, qweight, scales, zeros, N, K, Y, stream);
-    case 7: return launch_gemv_m<7, GATED>(X, qweight, scales, zeros, N, K, Y, stream);
-    case 8: return launch_gemv_m<8, GATED>(X, qweight, scales, zeros, N, K, Y, stream);
+      if (K <= 32768) return launch_gemv_m1<GATED>(X, qweight, scales, zeros, N, K, gsh, Y, stream);
+      return launch_gemv_m<1, GATED>(X, qweight, scales, zeros, N, K, gsh, Y, stream);
+    case 2: return launch_gemv_m<2, GATED>(X, qweight, scales, zeros, N, K, gsh, Y, stream);
+    case 3: return launch_gemv_m<3, GATED>(X, qweight, scales, zeros, N, K, gsh, Y, stream);
+    case 4: return launch_gemv_m<4, GATED>(X, qweight, scales, zeros, N, K, gsh, Y, stream);
+    case 5: return launch_gemv_m<5, GATED>(X, qweight, scales, zeros, N, K, gsh, Y, stream);
+    case 6: return launch_gemv_m<6, GATED>(X, qweight, scales, zeros, N, K, gsh, Y, stream);
+    case 7: return launch_gemv_m<7, GATED>(X, qweight, scales, zeros, N, K, gsh, Y, stream);
+    case 8: return launch_gemv_m<8, GATED>(X, qweight, scales, zeros, N, K, gsh, Y, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_gemv(const uint16_t* X, int64_t M, const uint32_t* qweight,
                        const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
-                       uint16_t* Y, bool gated, hipStream_t stream) {
-  return gated ? launch_gemv_t<true>(X, M, qweight, scales, zeros, N, K, Y, stream)
-               : launch_gemv_t<false>(X, M, qweight, scales, zeros, N, K, Y, stream);
+                       int group, uint16_t* Y, bool gated, hipStream_t stream) {
+  const int gsh = group == 64 ? 1 : 2;  // 32-channel chunk c belongs to group c >> gsh
+  return gated ? launch_gemv_t<true>(X, M, qweight, scales, zeros, N, K, gsh, Y, stream)
+               : launch_gemv_t<false>(X, M, qweight, scales, zeros, N, K, gsh, Y, stream);
 }
 
 }  // namespace awq

@@ -16,7 +16,9 @@
 //     of X at the same channels for token l % 32 (rows past M repeat row M - 1 and are
 //     never stored), read straight from global memory (X is tiny and stays in cache);
 //   - the 8 MFMAs of a group start from zero, and the group scale multiplies that partial
-//     tile in fp32 (one FMA per element), as in the M = 1 kernel;
+//     tile in fp32 (one FMA per element), as in the M = 1 kernel; with 64-channel groups
+//     the lane's first four words are one group and the last four the next, so the 8
+//     MFMAs form two partial tiles of four, each with its own scale;
 //   - the S waves of a block split K and meet in LDS at the end, where wave 0 adds the S
 //     partial tiles in a fixed order: results do not depend on scheduling.
 // Loads of group g + 1 are in flight while group g is multiplied (two register stages
@@ -35,7 +37,7 @@ namespace {
 struct SkinnyStage {
   uint4 b[2];     // 8 packed words: channels 32 h + [0, 32) and 64 + 32 h + [0, 32), row l % 32
   uint4 a[8];     // X[token][same channels], one 16-byte piece per k16 step
-  uint32_t sc, zb;
+  uint32_t sc[2], zb;  // scale(s) and zero byte of the 128-channel step (two groups of 64)
 };
 
 __device__ __forceinline__ uint32_t skinny_magic() {
@@ -60,13 +62,15 @@ __device__ __forceinline__ half8 widen_word(uint32_t w, half2v zz, uint32_t magi
 template <int S, int E, bool GATED>
 __global__ void __launch_bounds__(S * 64)
     k_gemv_mfma(const uint16_t* X, int64_t M, const uint32_t* qweight, const uint16_t* scales,
-                const uint8_t* zeros, int64_t N, int64_t K, uint16_t* Y) {
+                const uint8_t* zeros, int64_t N, int64_t K, int group, uint16_t* Y) {
   __shared__ float red[S][E][64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int j = lane & 31, h = lane >> 5;
-  const int64_t G = K / kGroup, zbytes = (G + 1) / 2, words = K / 8;
+  const bool g64 = group == 64;
+  const int64_t G = K / kGroup;                 // 128-channel steps
+  const int64_t Gs = K / group, zbytes = (Gs + 1) / 2, words = K / 8;  // scale groups
   // rows of this tile: plain, 32 consecutive rows; gated, 16 gate rows then their 16 up
   // rows (tile columns j and j + 16 hold g and u of output n0 + j)
   const int64_t nh = N / 2;
@@ -84,8 +88,14 @@ __global__ void __launch_bounds__(S * 64)
   const uint32_t magic = skinny_magic();
 
   auto load = [&](SkinnyStage& st, int64_t g) {
-    st.zb = zeros[n * zbytes + (g >> 1)];
-    st.sc = scales[n * G + g];
+    if (g64) {
+      st.zb = zeros[n * zbytes + g];  // groups 2g (low nibble) and 2g + 1 (high)
+      st.sc[0] = scales[n * Gs + 2 * g];
+      st.sc[1] = scales[n * Gs + 2 * g + 1];
+    } else {
+      st.zb = zeros[n * zbytes + (g >> 1)];
+      st.sc[0] = st.sc[1] = scales[n * Gs + g];
+    }
     const uint32_t* cp = qweight + n * words + g * 16 + h * 4;
     st.b[0] = *reinterpret_cast<const uint4*>(cp);
     st.b[1] = *reinterpret_cast<const uint4*>(cp + 8);
@@ -100,19 +110,36 @@ __global__ void __launch_bounds__(S * 64)
   for (int e = 0; e < E; ++e) acc[e] = 0.0f;
 
   auto body = [&](const SkinnyStage& st, int64_t g) {
-    const uint32_t z = (g & 1) ? (st.zb >> 4) & 0xF : st.zb & 0xF;
-    const uint32_t zbits = 0x6400u + z;
-    const half2v zz = -__builtin_bit_cast(half2v, zbits | (zbits << 16));
     const uint32_t wd[8] = {st.b[0].x, st.b[0].y, st.b[0].z, st.b[0].w,
                             st.b[1].x, st.b[1].y, st.b[1].z, st.b[1].w};
-    f32x16 d = f32x16{};
+    auto zz_of = [](uint32_t z) {
+      const uint32_t zbits = 0x6400u + z;
+      return -__builtin_bit_cast(half2v, zbits | (zbits << 16));
+    };
+    if (g64) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-      d = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, st.a[s]),
-                                                 widen_word(wd[s], zz, magic), d, 0, 0, 0);
-    const float scf = h2f((uint16_t)st.sc);
+      for (int half = 0; half < 2; ++half) {
+        const half2v zz = zz_of((st.zb >> (4 * half)) & 0xF);
+        f32x16 d = f32x16{};
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(scf, d[e], acc[e]);
+        for (int s = 4 * half; s < 4 * half + 4; ++s)
+          d = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, st.a[s]),
+                                                     widen_word(wd[s], zz, magic), d, 0, 0, 0);
+        const float scf = h2f((uint16_t)st.sc[half]);
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(scf, d[e], acc[e]);
+      }
+    } else {
+      const half2v zz = zz_of((g & 1) ? (st.zb >> 4) & 0xF : st.zb & 0xF);
+      f32x16 d = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        d = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, st.a[s]),
+                                                   widen_word(wd[s], zz, magic), d, 0, 0, 0);
+      const float scf = h2f((uint16_t)st.sc[0]);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(scf, d[e], acc[e]);
+    }
   };
 
   if (g1 > g0) {
@@ -163,30 +190,30 @@ __global__ void __launch_bounds__(S * 64)
 template <int S, int E, bool GATED>
 static hipError_t launch_skinny_x(const uint16_t* X, int64_t M, const uint32_t* qw,
                                   const uint16_t* sc, const uint8_t* z, int64_t N, int64_t K,
-                                  uint16_t* Y, hipStream_t stream) {
+                                  int group, uint16_t* Y, hipStream_t stream) {
   const int64_t outs = GATED ? N / 2 : N;
   const int64_t per = GATED ? 16 : 32;
   const int64_t blocks = (outs + per - 1) / per;
   hipLaunchKernelGGL((k_gemv_mfma<S, E, GATED>), dim3((unsigned)blocks), dim3(S * 64), 0, stream,
-                     X, M, qw, sc, z, N, K, Y);
+                     X, M, qw, sc, z, N, K, group, Y);
   return hipGetLastError();
 }
 
 template <bool GATED>
 static hipError_t launch_skinny_t(const uint16_t* X, int64_t M, const uint32_t* qw,
                                   const uint16_t* sc, const uint8_t* z, int64_t N, int64_t K,
-                                  uint16_t* Y, hipStream_t stream) {
-  if (M <= 8) return launch_skinny_x<8, 4, GATED>(X, M, qw, sc, z, N, K, Y, stream);
-  if (M <= 16) return launch_skinny_x<8, 8, GATED>(X, M, qw, sc, z, N, K, Y, stream);
-  return launch_skinny_x<8, 16, GATED>(X, M, qw, sc, z, N, K, Y, stream);
+                                  int group, uint16_t* Y, hipStream_t stream) {
+  if (M <= 8) return launch_skinny_x<8, 4, GATED>(X, M, qw, sc, z, N, K, group, Y, stream);
+  if (M <= 16) return launch_skinny_x<8, 8, GATED>(X, M, qw, sc, z, N, K, group, Y, stream);
+  return launch_skinny_x<8, 16, GATED>(X, M, qw, sc, z, N, K, group, Y, stream);
 }
 
 hipError_t launch_gemv_mfma(const uint16_t* X, int64_t M, const uint32_t* qweight,
                             const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
-                            uint16_t* Y, bool gated, hipStream_t stream) {
+                            int group, uint16_t* Y, bool gated, hipStream_t stream) {
   if (M < 1 || M > kSkinnyMaxM) return hipErrorInvalidValue;
-  return gated ? launch_skinny_t<true>(X, M, qweight, scales, zeros, N, K, Y, stream)
-               : launch_skinny_t<false>(X, M, qweight, scales, zeros, N, K, Y, stream);
+  return gated ? launch_skinny_t<true>(X, M, qweight, scales, zeros, N, K, group, Y, stream)
+               : launch_skinny_t<false>(X, M, qweight, scales, zeros, N, K, group, Y, stream);
 }
 
 }  // namespace awq

@@ -11,16 +11,17 @@ namespace awq {
 // a3 + a4: quantize W * diag(s) per group of 128 and pack codes / scales / zeros.
 // clip_idx (nullable, [N][G]): group (n, j) shrinks its range by (steps - idx) / steps.
 // sym: zero point off (sc = max|w'| / 7, zero fixed at 8, same stored format).
+// group: 128 or 64 input channels per scale / zero.
 hipError_t launch_quant_pack(const uint16_t* W, int64_t N, int64_t K, const uint16_t* s,
                              uint32_t* qweight, uint16_t* scales, uint8_t* zeros,
-                             const uint8_t* clip_idx, int clip_steps, bool sym, uint32_t* flags,
-                             hipStream_t stream);
+                             const uint8_t* clip_idx, int clip_steps, bool sym, int group,
+                             uint32_t* flags, hipStream_t stream);
 
 // f3: err[i][n][g] = sum_t (sum_{k in g} X_tk D_nk)^2 for the clip ratios i < n_shrink
 // (T <= 512), then the first minimum per (n, g).
 hipError_t launch_clip_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N,
                            int64_t K, const uint16_t* s, int clip_steps, int n_shrink, bool sym,
-                           float* rowmax, float* srange, double* err, uint32_t* flags,
+                           int group, float* rowmax, float* srange, double* err, uint32_t* flags,
                            hipStream_t stream);
 hipError_t launch_clip_reduce(const double* err, int n_shrink, int64_t N, int64_t G,
                               uint8_t* clip_idx, double* err_best, hipStream_t stream);
@@ -43,7 +44,8 @@ int search_row_tile();
 int search_token_chunk(int64_t T);
 // rowmax [N] and srange [n_grid] are scratch (per-row max |W|, per-grid-point max s / min s).
 hipError_t launch_search_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N,
-                             int64_t K, const uint16_t* s_grid, int n_grid, bool sym, float* rowmax,
+                             int64_t K, const uint16_t* s_grid, int n_grid, bool sym, int group,
+                             float* rowmax,
                              float* srange, double* partials, uint32_t* flags,
                              hipStream_t stream);
 // a6: fixed-order sums of the partials, first-minimum argmin, s_best copy.
@@ -53,12 +55,13 @@ hipError_t launch_search_reduce(const double* partials, int n_grid, int64_t n_pa
 
 // a7 / a8: Y = X deq(W)^T. gated (f1): W is gate|up stacked (N/2 rows each) and
 // Y[M][N/2] = SiLU(X deq(W_gate)^T) * (X deq(W_up)^T); N is even.
+// group: 128 or 64 (the layout of scales / zeros).
 hipError_t launch_gemv(const uint16_t* X, int64_t M, const uint32_t* qweight,
                        const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
-                       uint16_t* Y, bool gated, hipStream_t stream);
+                       int group, uint16_t* Y, bool gated, hipStream_t stream);
 hipError_t launch_gemm(const uint16_t* X, int64_t M, const uint32_t* qweight,
                        const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
-                       uint16_t* Y, bool gated, hipStream_t stream);
+                       int group, uint16_t* Y, bool gated, hipStream_t stream);
 
 // f2: out = fp16(A / s) along columns (axis 1, len(s) = cols) or rows (axis 0,
 // len(s) = rows); cols % 8 == 0; out may alias A.
@@ -69,7 +72,7 @@ hipError_t launch_inverse_scale(const uint16_t* A, int64_t rows, int64_t cols, c
 constexpr int kSkinnyMaxM = 32;
 hipError_t launch_gemv_mfma(const uint16_t* X, int64_t M, const uint32_t* qweight,
                             const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
-                            uint16_t* Y, bool gated, hipStream_t stream);
+                            int group, uint16_t* Y, bool gated, hipStream_t stream);
 
 constexpr int kGemvMaxM = 8;       // the vector-ALU GEMV serves M <= 8 when asked for
 constexpr int kVgemvAutoMaxM = 3;  // and is the automatic choice up to M = 3

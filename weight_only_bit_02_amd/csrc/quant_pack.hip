@@ -4,10 +4,12 @@
 // "大模型量化部署实战：GPTQ与AWQ算法", "大模型量化的核心原理与位宽选择": a 4-bit integer with a
 // scale and a zero point. Layout of the packed result: see include/awq.h.
 //
-// Mapping: a wave owns one (row, run of 4 groups) unit = 512 input channels. Lane l
+// Mapping: a wave owns one (row, 512 input channels) unit: 4 groups of 128 or 8 groups of
+// 64 ("AWQ量化实战" §2.3 also names 64). Lane l
 // reads 8 consecutive weights (one 16-byte load) and writes the 32-bit word that packs
 // their 8 codes (channel i of the word in nibble kNibbleOf[i]), so loads and stores are fully coalesced; the 16 lanes of a DPP row
-// form one group and find its min / max with row-local DPP (symmetric mode: the larger
+// (8 lanes for 64-channel groups) form one group and find its min / max with row-local
+// DPP (symmetric mode: the larger
 // magnitude sets the scale, zero fixed at 8). With clip indices (the
 // weight-clipping search), group (n, j) shrinks its extremes by r = clip_ratio(idx, steps)
 // before the quantizer sees them.
@@ -22,13 +24,16 @@ __global__ void __launch_bounds__(256) k_quant_pack(const uint16_t* __restrict__
                                                     uint16_t* __restrict__ scales,
                                                     uint8_t* __restrict__ zeros,
                                                     const uint8_t* __restrict__ clip_idx,
-                                                    int clip_steps, int sym,
+                                                    int clip_steps, int sym, int group,
                                                     uint32_t* __restrict__ flags) {
   const int lane = threadIdx.x & 63;
-  const int gi = lane >> 4;  // group within the unit
-  const int li = lane & 15;  // lane within the group
-  const int64_t G = K / kGroup;
-  const int64_t chunks = (G + 3) / 4;
+  const bool g64 = group == 64;
+  const int gl = g64 ? 8 : 16;        // lanes per group
+  const int gpu = 64 / gl;            // groups per unit
+  const int gi = lane / gl;           // group within the unit
+  const int li = lane % gl;           // lane within the group
+  const int64_t G = K / group;
+  const int64_t chunks = (G + gpu - 1) / gpu;
   const int64_t units = N * chunks;
   const int64_t wave0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
@@ -36,9 +41,9 @@ __global__ void __launch_bounds__(256) k_quant_pack(const uint16_t* __restrict__
 
   for (int64_t u = wave0; u < units; u += nwaves) {
     const int64_t n = u / chunks;
-    const int64_t j = (u - n * chunks) * 4 + gi;  // group index
+    const int64_t j = (u - n * chunks) * gpu + gi;  // group index
     const bool valid = j < G;
-    const int64_t k0 = j * kGroup + li * 8;
+    const int64_t k0 = j * group + li * 8;
 
     uint4 wv = make_uint4(0, 0, 0, 0);
     uint4 sv = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);  // s = 1
@@ -62,7 +67,7 @@ __global__ void __launch_bounds__(256) k_quant_pack(const uint16_t* __restrict__
       mn = fminf(mn, w[i]);
       mx = fmaxf(mx, w[i]);
     }
-    row16_minmax(mn, mx);
+    group_minmax(mn, mx, g64);
     if (clip_idx && valid) {
       const float r = clip_ratio(clip_idx[n * G + j], clip_steps);
       mn = r * mn;
@@ -74,7 +79,7 @@ __global__ void __launch_bounds__(256) k_quant_pack(const uint16_t* __restrict__
     for (int i = 0; i < 8; ++i) word |= (uint32_t)quant_code(w[i], g) << (4 * kNibbleOf[i]);
 
     const uint32_t zi = (uint32_t)g.z;
-    const uint32_t z_next = (uint32_t)__shfl_down((int)zi, 16);  // zero of group j + 1
+    const uint32_t z_next = (uint32_t)__shfl_down((int)zi, gl);  // zero of group j + 1
     if (valid) {
       qweight[(n * K + k0) >> 3] = word;
       if (li == 0) {
@@ -92,12 +97,12 @@ __global__ void __launch_bounds__(256) k_quant_pack(const uint16_t* __restrict__
 
 hipError_t launch_quant_pack(const uint16_t* W, int64_t N, int64_t K, const uint16_t* s,
                              uint32_t* qweight, uint16_t* scales, uint8_t* zeros,
-                             const uint8_t* clip_idx, int clip_steps, bool sym, uint32_t* flags,
-                             hipStream_t stream) {
-  const int64_t units = N * ((K / kGroup + 3) / 4);
+                             const uint8_t* clip_idx, int clip_steps, bool sym, int group,
+                             uint32_t* flags, hipStream_t stream) {
+  const int64_t units = N * ((K / 512 + (K % 512 ? 1 : 0)));
   const int64_t blocks = units / 4 + 1 < 16384 ? units / 4 + 1 : 16384;
   hipLaunchKernelGGL(k_quant_pack, dim3((unsigned)blocks), dim3(256), 0, stream, W, N, K, s,
-                     qweight, scales, zeros, clip_idx, clip_steps, (int)sym, flags);
+                     qweight, scales, zeros, clip_idx, clip_steps, (int)sym, group, flags);
   return hipGetLastError();
 }
 

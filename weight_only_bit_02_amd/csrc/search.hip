@@ -110,8 +110,9 @@ __global__ void __launch_bounds__(256) k_scale_range(const uint16_t* __restrict_
 template <int NW, bool CLIP>
 __device__ __forceinline__ bool quantize_tile_group(const uint16_t* W, int64_t N, int64_t K,
                                                     const uint16_t* s, float r, bool sym,
-                                                    int64_t n0, int64_t j, const float* lds_p,
-                                                    uint16_t* hi_buf, uint16_t* lo_buf, int tid) {
+                                                    bool g64, int64_t n0, int64_t j,
+                                                    const float* lds_p, uint16_t* hi_buf,
+                                                    uint16_t* lo_buf, int tid) {
   constexpr int kRowsPerPass = NW * 4;
   constexpr int kPasses = kRowTile / kRowsPerPass;
   const int q_row = tid >> 4;
@@ -146,7 +147,7 @@ __device__ __forceinline__ bool quantize_tile_group(const uint16_t* W, int64_t N
       mn = fminf(mn, wp[i]);
       mx = fmaxf(mx, wp[i]);
     }
-    row16_minmax(mn, mx);
+    group_minmax(mn, mx, g64);  // 16 lanes = one 128-channel group, or two of 64
     bad |= !__builtin_isfinite(mn) || !__builtin_isfinite(mx);
     if (CLIP) {
       mn = r * mn;
@@ -179,7 +180,8 @@ __device__ __forceinline__ bool quantize_tile_group(const uint16_t* W, int64_t N
 template <int NW>
 __global__ void __launch_bounds__(NW * 64)
     k_search_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N, int64_t K,
-                 const uint16_t* s_grid, int n_grid, int sym, const float* rowmax, const float* srange,
+                 const uint16_t* s_grid, int n_grid, int sym, int group, const float* rowmax,
+                 const float* srange,
                  double* __restrict__ partials, uint32_t* __restrict__ flags, int64_t n_ntiles,
                  int64_t per_xcd) {
   __shared__ __attribute__((aligned(16))) uint16_t lds_hi[2][kRowTile * kLdsStride];
@@ -212,8 +214,10 @@ __global__ void __launch_bounds__(NW * 64)
   __syncthreads();
 
   bool bad = false;
+  const bool g64 = group == 64;
   auto quantize = [&](int64_t j, int buf) {
-    bad |= quantize_tile_group<NW, false>(W, N, K, s, 1.0f, sym, n0, j, lds_p, lds_hi[buf], lds_lo[buf], tid);
+    bad |= quantize_tile_group<NW, false>(W, N, K, s, 1.0f, sym, g64, n0, j, lds_p, lds_hi[buf],
+                                          lds_lo[buf], tid);
   };
 
   for (int64_t tc = 0; tc < n_tchunks; ++tc) {
@@ -291,12 +295,15 @@ __global__ void __launch_bounds__(NW * 64)
 template <int NW>
 __global__ void __launch_bounds__(NW * 64)
     k_clip_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N, int64_t K,
-               const uint16_t* s, int clip_steps, int n_shrink, int sym, const float* rowmax,
-               const float* srange, double* __restrict__ err, uint32_t* __restrict__ flags,
-               int64_t n_ntiles, int64_t per_xcd) {
+               const uint16_t* s, int clip_steps, int n_shrink, int sym, int group,
+               const float* rowmax, const float* srange, double* __restrict__ err,
+               uint32_t* __restrict__ flags, int64_t n_ntiles, int64_t per_xcd) {
   __shared__ __attribute__((aligned(16))) uint16_t lds_hi[2][kRowTile * kLdsStride];
   __shared__ __attribute__((aligned(16))) uint16_t lds_lo[2][kRowTile * kLdsStride];
   __shared__ float lds_p[kRowTile];
+  // per-row partial errors of each wave: slot = step parity (128-channel groups; one
+  // barrier per step suffices) or the half of the step (64-channel groups: both slots are
+  // written every step, so a second barrier guards their reuse)
   __shared__ double lds_red[2][NW][kRowTile];
 
   const int64_t t = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
@@ -309,7 +316,9 @@ __global__ void __launch_bounds__(NW * 64)
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int64_t n0 = ntile * kRowTile;
-  const int64_t G = K / kGroup;
+  const bool g64 = group == 64;
+  const int64_t G = K / kGroup;    // 128-channel steps
+  const int64_t Gs = K / group;    // groups
   const int m32 = lane & 31;
   const int khalf = lane >> 5;
   const int64_t tw = (int64_t)wave * kTokPerWave;
@@ -321,66 +330,86 @@ __global__ void __launch_bounds__(NW * 64)
   __syncthreads();
 
   bool bad = false;
-  bad |= quantize_tile_group<NW, true>(W, N, K, s, r, sym, n0, 0, lds_p, lds_hi[0], lds_lo[0], tid);
+  bad |= quantize_tile_group<NW, true>(W, N, K, s, r, sym, g64, n0, 0, lds_p, lds_hi[0], lds_lo[0], tid);
   __syncthreads();
   for (int64_t j = 0; j < G; ++j) {
     const int buf = (int)(j & 1);
-    bad |= quantize_tile_group<NW, true>(W, N, K, s, r, sym, n0, j + 1 < G ? j + 1 : G - 1, lds_p,
-                                         lds_hi[buf ^ 1], lds_lo[buf ^ 1], tid);
+    bad |= quantize_tile_group<NW, true>(W, N, K, s, r, sym, g64, n0, j + 1 < G ? j + 1 : G - 1,
+                                         lds_p, lds_hi[buf ^ 1], lds_lo[buf ^ 1], tid);
     f32x16 acc[2][4];
+    // the step's 8 k16 slices in two halves of 4 (channels [0, 64) and [64, 128)); with
+    // 64-channel groups each half is a group and its error is taken on its own
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
-    if (active) {
-#pragma unroll 2
-      for (int st = 0; st < kGroup / 16; ++st) {
-        const int koff = st * 16 + khalf * 8;
-        half8 A[2], Bh[4], Bl[4];
-#pragma unroll
-        for (int a = 0; a < 2; ++a) {
-          const int64_t tt = tw + a * 32 + m32;
-          uint4 v = *reinterpret_cast<const uint4*>(X + (tt < T ? tt : T - 1) * K + j * kGroup + koff);
-          if (tt >= T) v = make_uint4(0, 0, 0, 0);
-          A[a] = __builtin_bit_cast(half8, v);
-        }
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int row = b * 32 + m32;
-          Bh[b] = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(&lds_hi[buf][row * kLdsStride + koff]));
-          Bl[b] = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(&lds_lo[buf][row * kLdsStride + koff]));
-        }
+    for (int hh = 0; hh < 2; ++hh) {
+      if (hh == 0 || g64) {
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[a], Bh[b], acc[a][b], 0, 0, 0);
-            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[a], Bl[b], acc[a][b], 0, 0, 0);
-          }
+          for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
       }
-    }
-    // this group's squares per row (output column = lane % 32; lanes l and l + 32 hold
-    // the same column for different tokens)
+      if (active) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const double pinv = 1.0 / (double)lds_p[b * 32 + m32];
-      double ss = 0.0;
+        for (int st = 4 * hh; st < 4 * hh + 4; ++st) {
+          const int koff = st * 16 + khalf * 8;
+          half8 A[2], Bh[4], Bl[4];
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+          for (int a = 0; a < 2; ++a) {
+            const int64_t tt = tw + a * 32 + m32;
+            uint4 v = *reinterpret_cast<const uint4*>(X + (tt < T ? tt : T - 1) * K + j * kGroup + koff);
+            if (tt >= T) v = make_uint4(0, 0, 0, 0);
+            A[a] = __builtin_bit_cast(half8, v);
+          }
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const double v = (double)acc[a][b][e] * pinv;
-          ss += v * v;
+          for (int b = 0; b < 4; ++b) {
+            const int row = b * 32 + m32;
+            Bh[b] = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(&lds_hi[buf][row * kLdsStride + koff]));
+            Bl[b] = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(&lds_lo[buf][row * kLdsStride + koff]));
+          }
+#pragma unroll
+          for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+              acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[a], Bh[b], acc[a][b], 0, 0, 0);
+              acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[a], Bl[b], acc[a][b], 0, 0, 0);
+            }
         }
-      ss += __shfl_xor(ss, 32);
-      if (khalf == 0) lds_red[buf][wave][b * 32 + m32] = ss;
+      }
+      if (hh == 1 || g64) {
+        // the group's squares per row (output column = lane % 32; lanes l and l + 32 hold
+        // the same column for different tokens)
+        const int slot = g64 ? hh : buf;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const double pinv = 1.0 / (double)lds_p[b * 32 + m32];
+          double ss = 0.0;
+#pragma unroll
+          for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const double v = (double)acc[a][b][e] * pinv;
+              ss += v * v;
+            }
+          ss += __shfl_xor(ss, 32);
+          if (khalf == 0) lds_red[slot][wave][b * 32 + m32] = ss;
+        }
+      }
     }
     __syncthreads();
     if (tid < kRowTile && n0 + tid < N) {
-      double tot = lds_red[buf][0][tid];
-      for (int w = 1; w < NW; ++w) tot += lds_red[buf][w][tid];
-      err[((int64_t)ci * N + n0 + tid) * G + j] = tot;
+      if (g64) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          double tot = lds_red[hh][0][tid];
+          for (int w = 1; w < NW; ++w) tot += lds_red[hh][w][tid];
+          err[((int64_t)ci * N + n0 + tid) * Gs + 2 * j + hh] = tot;
+        }
+      } else {
+        double tot = lds_red[buf][0][tid];
+        for (int w = 1; w < NW; ++w) tot += lds_red[buf][w][tid];
+        err[((int64_t)ci * N + n0 + tid) * Gs + j] = tot;
+      }
     }
+    if (g64) __syncthreads();
   }
   if (bad && flags && ci == 0) atomicOr(flags, AWQ_FLAG_NONFINITE_INPUT);
 }
@@ -406,7 +435,7 @@ __global__ void __launch_bounds__(256)
 
 hipError_t launch_clip_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N,
                            int64_t K, const uint16_t* s, int clip_steps, int n_shrink, bool sym,
-                           float* rowmax, float* srange, double* err, uint32_t* flags,
+                           int group, float* rowmax, float* srange, double* err, uint32_t* flags,
                            hipStream_t stream) {
   hipLaunchKernelGGL(k_row_absmax, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, stream, W, N, K, rowmax);
   hipError_t e = hipGetLastError();
@@ -421,10 +450,10 @@ hipError_t launch_clip_err(const uint16_t* X, int64_t T, const uint16_t* W, int6
   const dim3 grid((unsigned)(per_xcd * kXcds));
   if (T <= 4 * kTokPerWave)
     hipLaunchKernelGGL(k_clip_err<4>, grid, dim3(256), 0, stream, X, T, W, N, K, s, clip_steps,
-                       n_shrink, (int)sym, rowmax, srange, err, flags, n_ntiles, per_xcd);
+                       n_shrink, (int)sym, group, rowmax, srange, err, flags, n_ntiles, per_xcd);
   else
     hipLaunchKernelGGL(k_clip_err<8>, grid, dim3(512), 0, stream, X, T, W, N, K, s, clip_steps,
-                       n_shrink, (int)sym, rowmax, srange, err, flags, n_ntiles, per_xcd);
+                       n_shrink, (int)sym, group, rowmax, srange, err, flags, n_ntiles, per_xcd);
   return hipGetLastError();
 }
 
@@ -468,7 +497,8 @@ int search_row_tile() { return kRowTile; }
 int search_token_chunk(int64_t T) { return T <= 4 * kTokPerWave ? 4 * kTokPerWave : 8 * kTokPerWave; }
 
 hipError_t launch_search_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N,
-                             int64_t K, const uint16_t* s_grid, int n_grid, bool sym, float* rowmax,
+                             int64_t K, const uint16_t* s_grid, int n_grid, bool sym, int group,
+                             float* rowmax,
                              float* srange, double* partials, uint32_t* flags,
                              hipStream_t stream) {
   hipLaunchKernelGGL(k_row_absmax, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, stream, W, N, K, rowmax);
@@ -482,10 +512,10 @@ hipError_t launch_search_err(const uint16_t* X, int64_t T, const uint16_t* W, in
   const dim3 grid((unsigned)(per_xcd * kXcds));
   if (T <= 4 * kTokPerWave)
     hipLaunchKernelGGL(k_search_err<4>, grid, dim3(256), 0, stream, X, T, W, N, K, s_grid, n_grid,
-                       (int)sym, rowmax, srange, partials, flags, n_ntiles, per_xcd);
+                       (int)sym, group, rowmax, srange, partials, flags, n_ntiles, per_xcd);
   else
     hipLaunchKernelGGL(k_search_err<8>, grid, dim3(512), 0, stream, X, T, W, N, K, s_grid, n_grid,
-                       (int)sym, rowmax, srange, partials, flags, n_ntiles, per_xcd);
+                       (int)sym, group, rowmax, srange, partials, flags, n_ntiles, per_xcd);
   return hipGetLastError();
 }
 
