@@ -136,10 +136,10 @@ def quantize_groups(W16: np.ndarray, s16: np.ndarray | None = None, clip_ratio: 
     integer with a scale and a zero point, dequant = (q - z) * scale);
     [AWQ-SKILL] step 2 (w_bit 4, q_group_size 128, zero_point True).
 
-    Steps per row n and group j (k in [g j, g j + g), g = group: 128, or 64 as
+    Steps per row n and group j (k in [g j, g j + g), g = group: 128, or 64 or 32 as
     [AWQ-PRACTICE] §2.3 also names), all in fp32, RNE:
       1. w' = f32(w) * f32(s)                  (exact: 11 + 11 significant bits)
-      2. mx, mn = max / min of the 128 values w'
+      2. mx, mn = max / min of the g values w'
       3. sc = (mx - mn) / 15
       4. sc = max(sc, 2^-14); if sc > 65504 then sc = 65504 (flag SCALE_CLAMPED)
       5. sc_h = fp16(sc)                        (the stored scale)
@@ -158,7 +158,7 @@ def quantize_groups(W16: np.ndarray, s16: np.ndarray | None = None, clip_ratio: 
     W16 = np.asarray(W16)
     assert W16.dtype == np.float16 and W16.ndim == 2
     N, K = W16.shape
-    assert group in (GROUP, 64) and K % group == 0
+    assert group in (GROUP, 64, 32) and K % group == 0
     G = K // group
     w = W16.astype(_F32)
     if s16 is not None:

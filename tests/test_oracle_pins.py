@@ -582,23 +582,57 @@ def test_symmetric_search_errors_exact():
 
 
 # ----------------------------------------------------------------- group size 64
-def test_group64_codes_scales_and_layout():
-    """64-channel groups: codes nearest, scale / zero closed form per 64 channels, packed
+@pytest.mark.parametrize("group", [64, 32])
+def test_small_group_codes_scales_and_layout(group):
+    """64- and 32-channel groups: codes nearest, scale / zero closed form per group, packed
     zeros two groups per byte, byte count; symmetric codes too."""
     W = si.weights(3, 384, offset=117)
     s = np.exp(np.random.default_rng(11).uniform(-1, 1, 384)).astype(np.float16)
     w = W.astype(np.float32) * s.astype(np.float32)
+    G = 384 // group
     for zp in (True, False):
-        r = oracle.quantize_groups(W, s, zero_point=zp, group=64)
-        assert r["scale"].shape == (3, 6) and r["z"].shape == (3, 6)
+        r = oracle.quantize_groups(W, s, zero_point=zp, group=group)
+        assert r["scale"].shape == (3, G) and r["z"].shape == (3, G)
         assert not pins.check_codes_nearest(w, r["q"], r["z"], r["scale"])
         if zp:
             assert not pins.check_scale_zero(w, r["z"], r["scale"])
         qw, sc, zb = oracle.pack(r["q"], r["z"], r["scale"])
-        assert zb.shape == (3, 3)
+        assert zb.shape == (3, G // 2)
         q2, z2, s2 = oracle.unpack(qw, sc, zb, 384)
         assert np.array_equal(q2, r["q"]) and np.array_equal(z2, r["z"])
     assert oracle.packed_bytes(4096, 4096, 64) == 4096 * 2048 + 4096 * 64 * 2 + 4096 * 32
+    assert oracle.packed_bytes(4096, 4096, 32) == 4096 * 2048 + 4096 * 128 * 2 + 4096 * 64
+
+
+def test_group32_matches_group64_when_quarters_share_the_range():
+    """If each 32-channel quarter of every 64-channel block holds that block's min and max,
+    the two group sizes give the same codes and each 64-group's scale and zero twice."""
+    rng = np.random.default_rng(13)
+    W = (rng.uniform(-0.05, 0.05, (2, 256))).astype(np.float16)
+    for b in range(4):
+        for half in range(2):
+            W[:, b * 64 + half * 32 + 3] = np.float16(-0.06)
+            W[:, b * 64 + half * 32 + 30] = np.float16(0.08)
+    r64 = oracle.quantize_groups(W, group=64)
+    r32 = oracle.quantize_groups(W, group=32)
+    assert np.array_equal(r32["q"], r64["q"])
+    assert np.array_equal(r32["scale"].view(np.uint16), np.repeat(r64["scale"], 2, axis=1).view(np.uint16))
+    assert np.array_equal(r32["z"], np.repeat(r64["z"], 2, axis=1))
+
+
+def test_group32_search_and_clip_errors_exact():
+    X = si.activations(2, 128, offset=119)
+    W = si.weights(2, 128, offset=119)
+    r = oracle.search_errors(X, W, n_grid=3, group=32)
+    for i in range(3):
+        qz = oracle.quantize_groups(W, r["s16"][i], group=32)
+        exact = pins.exact_search_error(X, W, r["s16"][i], qz["q"], qz["z"], qz["scale"])
+        assert abs(r["err"][i] - float(exact)) <= 1e-12 * float(exact)
+    e = oracle.clip_errors(X, W, r["s16"][2], 200, 3, group=32)
+    assert e.shape == (3, 2, 4)
+    qz = oracle.quantize_groups(W, r["s16"][2], np.full((2, 4), oracle.clip_ratios(200, 3)[1], np.float32), group=32)
+    ex = pins.exact_group_errors(X, W, r["s16"][2], qz["q"], qz["z"], qz["scale"])
+    assert all(abs(e[1, n, g] - float(ex[n][g])) <= 1e-12 * float(ex[n][g]) for n in range(2) for g in range(4))
 
 
 def test_group64_matches_group128_when_halves_share_the_range():
