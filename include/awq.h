@@ -3,7 +3,7 @@
  *
  * AWQ (activation-aware weight quantization) keeps activations in 16-bit and stores
  * weights as 4-bit integers, one fp16 scale and one 4-bit zero point per group of
- * 128 (or 64) consecutive input channels; before quantizing, input channel k of the weight is
+ * 128 (or 64 or 32) consecutive input channels; before quantizing, input channel k of the weight is
  * multiplied by a scale s_k picked from offline activation magnitudes, and the
  * activation side carries 1/s_k (an equivalent transform).
  *
@@ -43,7 +43,7 @@ typedef enum awq_status {
   AWQ_OK = 0,
   AWQ_ERR_NULL_POINTER = 1,  /* a required pointer is NULL                          */
   AWQ_ERR_BAD_SHAPE = 2,     /* a size < 1, K % 128 != 0, T above 8192, ...          */
-  AWQ_ERR_UNSUPPORTED = 3,   /* config outside w_bit 4 / group 128 or 64 / zp 0 or 1  */
+  AWQ_ERR_UNSUPPORTED = 3,   /* config outside w_bit 4 / group 128, 64, 32 / zp 0, 1  */
   AWQ_ERR_MISALIGNED = 4,    /* a base pointer is not 16-byte aligned                */
   AWQ_ERR_WORKSPACE = 5,     /* workspace missing or smaller than the query returns  */
   AWQ_ERR_HIP = 6            /* the HIP runtime reported an error on launch          */
@@ -51,11 +51,12 @@ typedef enum awq_status {
 
 /* Quantization config ([SKILL] "如何使用该技能 / 步骤 2": quant_config zero_point, q_group_size,
  * w_bit; the page's "version" GEMM/GEMV switch becomes dispatch on M inside
- * awq_linear_w4a16). Supported: w_bit = 4, group_size = 128 or 64 ([PRACTICE] §2.3:
- * 128 is the usual group, 64 also in use), zero_point = 1 or 0, 1 <= n_grid <= 64.
+ * awq_linear_w4a16). Supported: w_bit = 4, group_size = 128, 64 or 32 ([PRACTICE] §2.3:
+ * 128 is the usual group, 64 and 32 also in use), zero_point = 1 or 0, 1 <= n_grid <= 64.
  * NULL config pointers mean {4, 128, 1, 20}. Every entry point takes the group size from
- * the config; K stays a multiple of 128 in both cases, so a 64-channel group never
- * straddles a 128-channel step of the kernels.
+ * the config; K stays a multiple of 128 in every case, so a smaller group never straddles
+ * a 128-channel step of the kernels. With 32-channel groups the skinny MFMA GEMV and the
+ * GEMM round (q - z) sc to fp16 before the multiply (within the linear tolerance).
  * zero_point = 0 ([PRACTICE] §3.3 advises it; [GPTQ-AWQ] gives the signed range -8..7):
  * sc = max|w'| / 7, q - 8 = clamp(rint(w'/sc_h), -8, 7), stored offset by 8 with every
  * zero nibble 8 -- the same packed format, so the linear entry points are unchanged;

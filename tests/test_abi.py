@@ -57,7 +57,9 @@ def test_quantize_pack_validation(lib):
     assert _qp(lib, cfg=C.byref(bad)) == 3
     bad = _abi.config(n_grid=0)
     assert _qp(lib, cfg=C.byref(bad)) == 3
-    bad = _abi.config(group_size=32)
+    bad = _abi.config(group_size=16)
+    assert _qp(lib, cfg=C.byref(bad)) == 3
+    bad = _abi.config(group_size=96)
     assert _qp(lib, cfg=C.byref(bad)) == 3
     bad = _abi.config(group_size=256)
     assert _qp(lib, cfg=C.byref(bad)) == 3
@@ -148,7 +150,9 @@ def test_clip_validation(lib):
     assert need >= 20 * 64 * 2 * 8
     g64 = _abi.config(group_size=64)
     assert lib.awq_clip_search_workspace_size(64, 64, 256, 20, C.byref(g64)) >= 20 * 64 * 4 * 8
-    bad = _abi.config(group_size=32)
+    g32 = _abi.config(group_size=32)
+    assert lib.awq_clip_search_workspace_size(64, 64, 256, 20, C.byref(g32)) >= 20 * 64 * 8 * 8
+    bad = _abi.config(group_size=16)
     assert lib.awq_clip_search_workspace_size(64, 64, 256, 20, C.byref(bad)) == 0
     assert lib.awq_quantize_pack_clipped(FAKE, 64, 256, None, FAKE, 0, None, FAKE, FAKE, FAKE,
                                          None, None) == 2

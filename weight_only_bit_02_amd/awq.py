@@ -15,7 +15,7 @@ import torch
 
 from . import _abi
 
-GROUP = 128          # default group size; 64 is the other supported one
+GROUP = 128          # default group size; 64 and 32 are also supported
 
 
 def _ptr(t):

@@ -15,7 +15,7 @@ awq_config resolve(const awq_config* cfg) {
 }
 
 bool supported(const awq_config& c) {
-  return c.w_bit == 4 && (c.group_size == 128 || c.group_size == 64) &&
+  return c.w_bit == 4 && (c.group_size == 128 || c.group_size == 64 || c.group_size == 32) &&
          (c.zero_point == 0 || c.zero_point == 1) && c.n_grid >= 1 && c.n_grid <= 64;
 }
 
@@ -87,7 +87,7 @@ const char* awq_status_string(awq_status s) {
     case AWQ_OK: return "ok";
     case AWQ_ERR_NULL_POINTER: return "a required pointer is NULL";
     case AWQ_ERR_BAD_SHAPE: return "bad shape (sizes must be >= 1, K a multiple of 128, T <= 8192)";
-    case AWQ_ERR_UNSUPPORTED: return "unsupported config (w_bit 4, group_size 128 or 64, zero_point 0 or 1, 1 <= n_grid <= 64)";
+    case AWQ_ERR_UNSUPPORTED: return "unsupported config (w_bit 4, group_size 128, 64 or 32, zero_point 0 or 1, 1 <= n_grid <= 64)";
     case AWQ_ERR_MISALIGNED: return "a base pointer is not 16-byte aligned";
     case AWQ_ERR_WORKSPACE: return "workspace missing or too small";
     case AWQ_ERR_HIP: return "HIP launch error";

@@ -65,10 +65,20 @@ __device__ __forceinline__ void row8_minmax(float& mn, float& mx) {
   mx = fmaxf(mx, dpp_f32<kDppRowHalfMirror>(mx));
 }
 
-// Group min / max for groups of 16 lanes x 8 channels (g = 128) or 8 lanes (g = 64).
-__device__ __forceinline__ void group_minmax(float& mn, float& mx, bool g64) {
-  if (g64) row8_minmax(mn, mx);
-  else row16_minmax(mn, mx);
+// Min / max over each quad of lanes (32-channel groups): the two quad_perm butterflies.
+__device__ __forceinline__ void quad_minmax(float& mn, float& mx) {
+  mn = fminf(mn, dpp_f32<kDppQuadXor1>(mn));
+  mx = fmaxf(mx, dpp_f32<kDppQuadXor1>(mx));
+  mn = fminf(mn, dpp_f32<kDppQuadXor2>(mn));
+  mx = fmaxf(mx, dpp_f32<kDppQuadXor2>(mx));
+}
+
+// Group min / max when each lane holds 8 consecutive channels: a group of g channels is
+// g / 8 adjacent lanes (16 for g = 128, 8 for g = 64, 4 for g = 32).
+__device__ __forceinline__ void group_minmax(float& mn, float& mx, int group) {
+  if (group == 128) row16_minmax(mn, mx);
+  else if (group == 64) row8_minmax(mn, mx);
+  else quad_minmax(mn, mx);
 }
 
 __device__ __forceinline__ float row16_sum(float v) {

@@ -3,8 +3,9 @@
 // "AWQ量化技术Skill", "主要功能和特点": a GEMM kernel serves batch sizes above one;
 // "AWQ量化实战" §2.3 / §3.4: weights stay 4-bit in memory and are dequantized on the fly.
 //
-// Block tile 128 (tokens) x 256 (output channels), K step 128 (one group of 128, or two of
-// 64: the lane half's 64 channels are then one group), four waves side by side
+// Block tile 128 (tokens) x 256 (output channels), K step 128 (one group of 128, two of 64
+// -- the lane half's 64 channels are then one group -- or four of 32, the lane half's
+// words 0-3 one group and words 4-7 the next), four waves side by side
 // along N, each owning 128 x 64 = 4 x 2 tiles of v_mfma_f32_32x32x16_f16.
 //   - A (activations) is shared by the four waves: it goes global -> registers -> LDS,
 //     double-buffered
@@ -63,10 +64,12 @@ __device__ __forceinline__ half8 dequant_word(uint32_t w, half2v zz, half2v s2, 
 struct GemmStage {
   uint4 a[8];
   uint4 b[2][2];
-  uint32_t zb[2], sc[2];
+  uint32_t zb[2], sc[2][2];  // per column: zero byte; scales of the lane's words 0-3, 4-7
+                             // (the second only with 32-channel groups)
 };
 
-template <bool GATED>
+// SPLIT: 32-channel groups (two scales per lane half); otherwise 128 or 64, one scale.
+template <bool GATED, bool SPLIT>
 __global__ void __launch_bounds__(256)
     k_gemm(const uint16_t* X, int64_t M, const uint32_t* qweight, const uint16_t* scales,
            const uint8_t* zeros, int64_t N, int64_t K, int group, uint16_t* __restrict__ Y, int64_t mt,
@@ -85,8 +88,10 @@ __global__ void __launch_bounds__(256)
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int m32 = lane & 31, kh = lane >> 5;
-  // 64-channel groups: lane half kh of step `step` lies in group 2 step + kh, whose zero
-  // is nibble kh of byte `step`; 128-channel groups: group `step`, nibble step & 1
+  // Lane half kh covers channels [64 kh, 64 kh + 64) of step `step`: group `step` with
+  // zero nibble step & 1 (g = 128); group 2 step + kh, nibble kh (g = 64); groups
+  // 4 step + 2 kh and 4 step + 2 kh + 1 for words 0-3 and 4-7, the low and high nibble of
+  // byte 2 step + kh (g = 32)
   const int g64 = group == 64;
   const int64_t Gs = K / group, zb = (Gs + 1) / 2, words = K / 8;
   const int64_t nsteps = K / kBK;
@@ -121,8 +126,14 @@ __global__ void __launch_bounds__(256)
   auto load = [&](GemmStage& st, int64_t step) {
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      st.zb[b] = zeros[b_col[b] * zb + (step >> (1 - g64))];
-      st.sc[b] = scales[b_col[b] * Gs + (step << g64) + (g64 & kh)];
+      if constexpr (SPLIT) {
+        st.zb[b] = zeros[b_col[b] * zb + 2 * step + kh];
+        st.sc[b][0] = scales[b_col[b] * Gs + 4 * step + 2 * kh];
+        st.sc[b][1] = scales[b_col[b] * Gs + 4 * step + 2 * kh + 1];
+      } else {
+        st.zb[b] = zeros[b_col[b] * zb + (step >> (1 - g64))];
+        st.sc[b][0] = scales[b_col[b] * Gs + (step << g64) + (g64 & kh)];
+      }
     }
 #pragma unroll
     for (int b = 0; b < 2; ++b)
@@ -162,14 +173,17 @@ __global__ void __launch_bounds__(256)
     // always issued (clamped to the last step) so the load counter is the same on every
     // path and the waits below can be exact
     load(nn, step + 2 < nsteps ? step + 2 : nsteps - 1);
-    half2v zz[2], s2[2];
-    const int hi = g64 ? kh : (int)(step & 1);
+    half2v zz[2][2], s2[2][2];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const uint32_t z = hi ? (cur.zb[b] >> 4) : (cur.zb[b] & 0xF);
-      const uint32_t zbits = 0x6400u + z;
-      zz[b] = -__builtin_bit_cast(half2v, zbits | (zbits << 16));
-      s2[b] = __builtin_bit_cast(half2v, cur.sc[b] | (cur.sc[b] << 16));
+    for (int i = 0; i < (SPLIT ? 2 : 1); ++i) {
+      const int hi = SPLIT ? i : g64 ? kh : (int)(step & 1);  // zero nibble
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const uint32_t z = hi ? (cur.zb[b] >> 4) : (cur.zb[b] & 0xF);
+        const uint32_t zbits = 0x6400u + z;
+        zz[b][i] = -__builtin_bit_cast(half2v, zbits | (zbits << 16));
+        s2[b][i] = __builtin_bit_cast(half2v, cur.sc[b][i] | (cur.sc[b][i] << 16));
+      }
     }
     // lane half kh covers channels [64 kh, 64 kh + 64) of the step; k16 step s covers 8 of
     // them. Operands of step s + 1 (A from LDS, B dequantized) are produced while the
@@ -183,7 +197,8 @@ __global__ void __launch_bounds__(256)
       for (int b = 0; b < 2; ++b) {
         const uint4 q = cur.b[b][s >> 2];
         const uint32_t w = (s & 3) == 0 ? q.x : (s & 3) == 1 ? q.y : (s & 3) == 2 ? q.z : q.w;
-        B[b] = dequant_word(w, zz[b], s2[b], magic);
+        const int i = SPLIT ? (s >> 2) : 0;
+        B[b] = dequant_word(w, zz[b][i], s2[b][i], magic);
       }
     };
     half8 A0[4], B0[2], A1[4], B1[2];
@@ -256,12 +271,20 @@ hipError_t launch_gemm(const uint16_t* X, int64_t M, const uint32_t* qweight,
   const int64_t mt = (M + kBM - 1) / kBM;
   const int64_t nt = gated ? (N / 2 + kBN / 2 - 1) / (kBN / 2) : (N + kBN - 1) / kBN;
   const int64_t per_xcd = (mt * nt + kXcds - 1) / kXcds;
-  if (gated)
-    hipLaunchKernelGGL(k_gemm<true>, dim3((unsigned)(per_xcd * kXcds)), dim3(256), 0, stream, X,
-                       M, qweight, scales, zeros, N, K, group, Y, mt, nt, per_xcd);
+  const dim3 grid((unsigned)(per_xcd * kXcds));
+  const bool split = group == 32;
+  if (gated && split)
+    hipLaunchKernelGGL((k_gemm<true, true>), grid, dim3(256), 0, stream, X, M, qweight, scales,
+                       zeros, N, K, group, Y, mt, nt, per_xcd);
+  else if (gated)
+    hipLaunchKernelGGL((k_gemm<true, false>), grid, dim3(256), 0, stream, X, M, qweight, scales,
+                       zeros, N, K, group, Y, mt, nt, per_xcd);
+  else if (split)
+    hipLaunchKernelGGL((k_gemm<false, true>), grid, dim3(256), 0, stream, X, M, qweight, scales,
+                       zeros, N, K, group, Y, mt, nt, per_xcd);
   else
-    hipLaunchKernelGGL(k_gemm<false>, dim3((unsigned)(per_xcd * kXcds)), dim3(256), 0, stream, X,
-                       M, qweight, scales, zeros, N, K, group, Y, mt, nt, per_xcd);
+    hipLaunchKernelGGL((k_gemm<false, false>), grid, dim3(256), 0, stream, X, M, qweight, scales,
+                       zeros, N, K, group, Y, mt, nt, per_xcd);
   return hipGetLastError();
 }
 

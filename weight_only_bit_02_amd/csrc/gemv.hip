@@ -458,7 +458,7 @@ static hipError_t launch_gemv_t(const uint16_t* X, int64_t M, const uint32_t* qw
 hipError_t launch_gemv(const uint16_t* X, int64_t M, const uint32_t* qweight,
                        const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
                        int group, uint16_t* Y, bool gated, hipStream_t stream) {
-  const int gsh = group == 64 ? 1 : 2;  // 32-channel chunk c belongs to group c >> gsh
+  const int gsh = group == 128 ? 2 : group == 64 ? 1 : 0;  // chunk c (32 channels) is in group c >> gsh
   return gated ? launch_gemv_t<true>(X, M, qweight, scales, zeros, N, K, gsh, Y, stream)
                : launch_gemv_t<false>(X, M, qweight, scales, zeros, N, K, gsh, Y, stream);
 }

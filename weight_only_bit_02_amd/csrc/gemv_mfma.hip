@@ -18,7 +18,9 @@
 //   - the 8 MFMAs of a group start from zero, and the group scale multiplies that partial
 //     tile in fp32 (one FMA per element), as in the M = 1 kernel; with 64-channel groups
 //     the lane's first four words are one group and the last four the next, so the 8
-//     MFMAs form two partial tiles of four, each with its own scale;
+//     MFMAs form two partial tiles of four, each with its own scale; with 32-channel
+//     groups the two lane halves of one k16 slice lie in different groups, so there the
+//     operand itself carries the scale ((q - z) sc in fp16, one rounding, as in the GEMM);
 //   - the S waves of a block split K and meet in LDS at the end, where wave 0 adds the S
 //     partial tiles in a fixed order: results do not depend on scheduling.
 // Loads of group g + 1 are in flight while group g is multiplied (two register stages
@@ -37,7 +39,7 @@ namespace {
 struct SkinnyStage {
   uint4 b[2];     // 8 packed words: channels 32 h + [0, 32) and 64 + 32 h + [0, 32), row l % 32
   uint4 a[8];     // X[token][same channels], one 16-byte piece per k16 step
-  uint32_t sc[2], zb;  // scale(s) and zero byte of the 128-channel step (two groups of 64)
+  uint32_t sc[2], zb;  // the lane's scales of words 0-3 and 4-7; the step's zero byte(s)
 };
 
 __device__ __forceinline__ uint32_t skinny_magic() {
@@ -68,7 +70,7 @@ __global__ void __launch_bounds__(S * 64)
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int j = lane & 31, h = lane >> 5;
-  const bool g64 = group == 64;
+  const bool g64 = group == 64, g32 = group == 32;
   const int64_t G = K / kGroup;                 // 128-channel steps
   const int64_t Gs = K / group, zbytes = (Gs + 1) / 2, words = K / 8;  // scale groups
   // rows of this tile: plain, 32 consecutive rows; gated, 16 gate rows then their 16 up
@@ -88,7 +90,12 @@ __global__ void __launch_bounds__(S * 64)
   const uint32_t magic = skinny_magic();
 
   auto load = [&](SkinnyStage& st, int64_t g) {
-    if (g64) {
+    if (g32) {
+      // words 0-3 of lane half h: group 4g + h; words 4-7: group 4g + 2 + h
+      st.zb = (uint32_t)zeros[n * zbytes + 2 * g] | ((uint32_t)zeros[n * zbytes + 2 * g + 1] << 8);
+      st.sc[0] = scales[n * Gs + 4 * g + h];
+      st.sc[1] = scales[n * Gs + 4 * g + 2 + h];
+    } else if (g64) {
       st.zb = zeros[n * zbytes + g];  // groups 2g (low nibble) and 2g + 1 (high)
       st.sc[0] = scales[n * Gs + 2 * g];
       st.sc[1] = scales[n * Gs + 2 * g + 1];
@@ -116,7 +123,20 @@ __global__ void __launch_bounds__(S * 64)
       const uint32_t zbits = 0x6400u + z;
       return -__builtin_bit_cast(half2v, zbits | (zbits << 16));
     };
-    if (g64) {
+    if (g32) {
+      f32x16 d = f32x16{};
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const half2v zz = zz_of((st.zb >> (8 * half + 4 * h)) & 0xF);
+        const half2v s2 = __builtin_bit_cast(half2v, st.sc[half] | (st.sc[half] << 16));
+#pragma unroll
+        for (int s = 4 * half; s < 4 * half + 4; ++s)
+          d = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+              __builtin_bit_cast(half8, st.a[s]), widen_word(wd[s], zz, magic) * half8{s2[0], s2[1], s2[0], s2[1], s2[0], s2[1], s2[0], s2[1]}, d, 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] += d[e];
+    } else if (g64) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const half2v zz = zz_of((st.zb >> (4 * half)) & 0xF);

@@ -4,12 +4,12 @@
 // "大模型量化部署实战：GPTQ与AWQ算法", "大模型量化的核心原理与位宽选择": a 4-bit integer with a
 // scale and a zero point. Layout of the packed result: see include/awq.h.
 //
-// Mapping: a wave owns one (row, 512 input channels) unit: 4 groups of 128 or 8 groups of
-// 64 ("AWQ量化实战" §2.3 also names 64). Lane l
+// Mapping: a wave owns one (row, 512 input channels) unit: 4 groups of 128, 8 of 64 or 16
+// of 32 ("AWQ量化实战" §2.3 also names 64 and 32). Lane l
 // reads 8 consecutive weights (one 16-byte load) and writes the 32-bit word that packs
-// their 8 codes (channel i of the word in nibble kNibbleOf[i]), so loads and stores are fully coalesced; the 16 lanes of a DPP row
-// (8 lanes for 64-channel groups) form one group and find its min / max with row-local
-// DPP (symmetric mode: the larger
+// their 8 codes (channel i of the word in nibble kNibbleOf[i]), so loads and stores are
+// fully coalesced; the 16 lanes of a DPP row (8 lanes for 64-channel groups, a quad for
+// 32) form one group and find its min / max with row-local DPP (symmetric mode: the larger
 // magnitude sets the scale, zero fixed at 8). With clip indices (the
 // weight-clipping search), group (n, j) shrinks its extremes by r = clip_ratio(idx, steps)
 // before the quantizer sees them.
@@ -27,8 +27,7 @@ __global__ void __launch_bounds__(256) k_quant_pack(const uint16_t* __restrict__
                                                     int clip_steps, int sym, int group,
                                                     uint32_t* __restrict__ flags) {
   const int lane = threadIdx.x & 63;
-  const bool g64 = group == 64;
-  const int gl = g64 ? 8 : 16;        // lanes per group
+  const int gl = group / 8;          // lanes per group
   const int gpu = 64 / gl;            // groups per unit
   const int gi = lane / gl;           // group within the unit
   const int li = lane % gl;           // lane within the group
@@ -67,7 +66,7 @@ __global__ void __launch_bounds__(256) k_quant_pack(const uint16_t* __restrict__
       mn = fminf(mn, w[i]);
       mx = fmaxf(mx, w[i]);
     }
-    group_minmax(mn, mx, g64);
+    group_minmax(mn, mx, group);
     if (clip_idx && valid) {
       const float r = clip_ratio(clip_idx[n * G + j], clip_steps);
       mn = r * mn;

@@ -110,7 +110,7 @@ __global__ void __launch_bounds__(256) k_scale_range(const uint16_t* __restrict_
 template <int NW, bool CLIP>
 __device__ __forceinline__ bool quantize_tile_group(const uint16_t* W, int64_t N, int64_t K,
                                                     const uint16_t* s, float r, bool sym,
-                                                    bool g64, int64_t n0, int64_t j,
+                                                    int group, int64_t n0, int64_t j,
                                                     const float* lds_p, uint16_t* hi_buf,
                                                     uint16_t* lo_buf, int tid) {
   constexpr int kRowsPerPass = NW * 4;
@@ -147,7 +147,7 @@ __device__ __forceinline__ bool quantize_tile_group(const uint16_t* W, int64_t N
       mn = fminf(mn, wp[i]);
       mx = fmaxf(mx, wp[i]);
     }
-    group_minmax(mn, mx, g64);  // 16 lanes = one 128-channel group, or two of 64
+    group_minmax(mn, mx, group);  // 16 lanes = one 128-channel group, two of 64, four of 32
     bad |= !__builtin_isfinite(mn) || !__builtin_isfinite(mx);
     if (CLIP) {
       mn = r * mn;
@@ -214,9 +214,8 @@ __global__ void __launch_bounds__(NW * 64)
   __syncthreads();
 
   bool bad = false;
-  const bool g64 = group == 64;
   auto quantize = [&](int64_t j, int buf) {
-    bad |= quantize_tile_group<NW, false>(W, N, K, s, 1.0f, sym, g64, n0, j, lds_p, lds_hi[buf],
+    bad |= quantize_tile_group<NW, false>(W, N, K, s, 1.0f, sym, group, n0, j, lds_p, lds_hi[buf],
                                           lds_lo[buf], tid);
   };
 
@@ -302,8 +301,8 @@ __global__ void __launch_bounds__(NW * 64)
   __shared__ __attribute__((aligned(16))) uint16_t lds_lo[2][kRowTile * kLdsStride];
   __shared__ float lds_p[kRowTile];
   // per-row partial errors of each wave: slot = step parity (128-channel groups; one
-  // barrier per step suffices) or the half of the step (64-channel groups: both slots are
-  // written every step, so a second barrier guards their reuse)
+  // barrier per step suffices) or the group's place in a pair (64- and 32-channel groups:
+  // both slots are filled, then stored and freed between two barriers)
   __shared__ double lds_red[2][NW][kRowTile];
 
   const int64_t t = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
@@ -316,7 +315,8 @@ __global__ void __launch_bounds__(NW * 64)
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int64_t n0 = ntile * kRowTile;
-  const bool g64 = group == 64;
+  const int gps = kGroup / group;  // groups per 128-channel step: 1, 2 or 4
+  const int per = 8 / gps;         // k16 slices per group: 8, 4 or 2
   const int64_t G = K / kGroup;    // 128-channel steps
   const int64_t Gs = K / group;    // groups
   const int m32 = lane & 31;
@@ -330,18 +330,21 @@ __global__ void __launch_bounds__(NW * 64)
   __syncthreads();
 
   bool bad = false;
-  bad |= quantize_tile_group<NW, true>(W, N, K, s, r, sym, g64, n0, 0, lds_p, lds_hi[0], lds_lo[0], tid);
+  bad |= quantize_tile_group<NW, true>(W, N, K, s, r, sym, group, n0, 0, lds_p, lds_hi[0], lds_lo[0], tid);
   __syncthreads();
   for (int64_t j = 0; j < G; ++j) {
     const int buf = (int)(j & 1);
-    bad |= quantize_tile_group<NW, true>(W, N, K, s, r, sym, g64, n0, j + 1 < G ? j + 1 : G - 1,
+    bad |= quantize_tile_group<NW, true>(W, N, K, s, r, sym, group, n0, j + 1 < G ? j + 1 : G - 1,
                                          lds_p, lds_hi[buf ^ 1], lds_lo[buf ^ 1], tid);
     f32x16 acc[2][4];
-    // the step's 8 k16 slices in two halves of 4 (channels [0, 64) and [64, 128)); with
-    // 64-channel groups each half is a group and its error is taken on its own
+    // the step's 8 k16 slices in quarters of two; a group spans per = 8, 4 or 2 slices and
+    // its error is taken when its last slice is done. Groups go through the two LDS slots:
+    // one group per step uses the slot of the step's parity (one barrier per step); two or
+    // four groups per step fill both slots, store them and free them (two barriers per pair)
+    int nred = 0, gdone = 0;
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      if (hh == 0 || g64) {
+    for (int c = 0; c < 4; ++c) {
+      if ((2 * c) % per == 0) {
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -349,7 +352,7 @@ __global__ void __launch_bounds__(NW * 64)
       }
       if (active) {
 #pragma unroll
-        for (int st = 4 * hh; st < 4 * hh + 4; ++st) {
+        for (int st = 2 * c; st < 2 * c + 2; ++st) {
           const int koff = st * 16 + khalf * 8;
           half8 A[2], Bh[4], Bl[4];
 #pragma unroll
@@ -374,10 +377,10 @@ __global__ void __launch_bounds__(NW * 64)
             }
         }
       }
-      if (hh == 1 || g64) {
+      if ((2 * c + 2) % per == 0) {
         // the group's squares per row (output column = lane % 32; lanes l and l + 32 hold
         // the same column for different tokens)
-        const int slot = g64 ? hh : buf;
+        const int slot = gps == 1 ? buf : nred;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const double pinv = 1.0 / (double)lds_p[b * 32 + m32];
@@ -392,24 +395,31 @@ __global__ void __launch_bounds__(NW * 64)
           ss += __shfl_xor(ss, 32);
           if (khalf == 0) lds_red[slot][wave][b * 32 + m32] = ss;
         }
+        ++nred;
+        if (gps > 1 && nred == 2) {
+          __syncthreads();
+          if (tid < kRowTile && n0 + tid < N) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              double tot = lds_red[q][0][tid];
+              for (int w = 1; w < NW; ++w) tot += lds_red[q][w][tid];
+              err[((int64_t)ci * N + n0 + tid) * Gs + j * gps + gdone + q] = tot;
+            }
+          }
+          __syncthreads();
+          nred = 0;
+          gdone += 2;
+        }
       }
     }
-    __syncthreads();
-    if (tid < kRowTile && n0 + tid < N) {
-      if (g64) {
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          double tot = lds_red[hh][0][tid];
-          for (int w = 1; w < NW; ++w) tot += lds_red[hh][w][tid];
-          err[((int64_t)ci * N + n0 + tid) * Gs + 2 * j + hh] = tot;
-        }
-      } else {
+    if (gps == 1) {
+      __syncthreads();
+      if (tid < kRowTile && n0 + tid < N) {
         double tot = lds_red[buf][0][tid];
         for (int w = 1; w < NW; ++w) tot += lds_red[buf][w][tid];
         err[((int64_t)ci * N + n0 + tid) * Gs + j] = tot;
       }
     }
-    if (g64) __syncthreads();
   }
   if (bad && flags && ci == 0) atomicOr(flags, AWQ_FLAG_NONFINITE_INPUT);
 }
