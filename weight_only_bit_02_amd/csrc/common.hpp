@@ -104,17 +104,47 @@ __device__ __forceinline__ double wave_sum(double v) {
 }
 
 // ------------------------------------------------------------------ group quantizer
-// Per group of 128 values w' (= w * s, an exact fp32 product), in fp32 with
+// Per group of g values w' (= w * s, an exact fp32 product), in fp32 with
 // round-to-nearest-even and no contraction:
 //   sc = max((mx - mn) / 15, 2^-14), clamped at 65504; sc_h = fp16(sc);
 //   z = clamp(rint(-mn / sc_h), 0, 15);  q = clamp(rint(w' / sc_h) + z, 0, 15).
 struct GroupQ {
   float scf;     // the stored scale as fp32
-  float rcp;     // fp32(1 / scf), only used to find the easy codes quickly
+  float rcp;     // hardware reciprocal of scf (within 1 ulp), only to guess quotients
   float z;       // zero point, 0..15
   uint16_t sch;  // fp16 bits of the stored scale
   bool clamped;  // sc exceeded 65504
 };
+
+// rint(w_i / scf) for NV values, equal to rint of the correctly rounded quotient. The
+// product w * rcp is within 1.5 * 2^-23 (relative) of the real quotient; unless it sits
+// within |q| * 2^-21 of a half-integer, it lies on the same side of that half-integer as
+// the correctly rounded quotient and rint gives the same integer. Close calls are rare
+// (about 2^-17 per value): the wave takes the correctly rounded division for them in a
+// branch it skips unless one of its lanes has one, so the common path has no division.
+template <int NV>
+__device__ __forceinline__ void rint_quotients(const float (&w)[NV], float scf, float rcp,
+                                               float (&q)[NV]) {
+#pragma clang fp contract(off)
+  bool close[NV];
+  bool any = false;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const float qa = w[i] * rcp;
+    const float fl = __builtin_floorf(qa);
+    const float d = __builtin_fabsf((qa - fl) - 0.5f);
+    close[i] = !(d > __builtin_fabsf(qa) * 0x1p-21f + 0x1p-60f);
+    any |= close[i];
+    q[i] = qa;
+  }
+  if (__builtin_amdgcn_ballot_w64(any)) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (close[i]) q[i] = w[i] / scf;  // correctly rounded division
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) q[i] = __builtin_rintf(q[i]);
+}
 
 __device__ __forceinline__ GroupQ group_params(float mn, float mx) {
 #pragma clang fp contract(off)
@@ -125,8 +155,11 @@ __device__ __forceinline__ GroupQ group_params(float mn, float mx) {
   sc = fminf(sc, 65504.0f);
   g.sch = f2h_bits(sc);
   g.scf = h2f(g.sch);
-  g.z = fminf(fmaxf(__builtin_rintf(-mn / g.scf), 0.0f), 15.0f);
-  g.rcp = 1.0f / g.scf;
+  g.rcp = __builtin_amdgcn_rcpf(g.scf);
+  const float nmn[1] = {-mn};
+  float zq[1];
+  rint_quotients(nmn, g.scf, g.rcp, zq);
+  g.z = fminf(fmaxf(zq[0], 0.0f), 15.0f);
   return g;
 }
 
@@ -143,27 +176,17 @@ __device__ __forceinline__ GroupQ group_params_sym(float mn, float mx) {
   g.sch = f2h_bits(sc);
   g.scf = h2f(g.sch);
   g.z = 8.0f;
-  g.rcp = 1.0f / g.scf;
+  g.rcp = __builtin_amdgcn_rcpf(g.scf);
   return g;
 }
 
-// rint(w / scf) exactly as the correctly rounded quotient would give it. The product
-// w * rcp is within 2^-23 (relative) of the real quotient; unless it sits within
-// |q| * 2^-21 of a half-integer, it lies on the same side of that half-integer as
-// the correctly rounded quotient and rint gives the same integer. The rare close
-// calls take the correctly rounded division.
-__device__ __forceinline__ float rint_quotient(float w, const GroupQ& g) {
+// Codes q = clamp(rint(w / sc_h) + z, 0, 15) of NV values of one group.
+template <int NV>
+__device__ __forceinline__ void quant_codes(const float (&w)[NV], const GroupQ& g, float (&q)[NV]) {
 #pragma clang fp contract(off)
-  float qa = w * g.rcp;
-  float fl = __builtin_floorf(qa);
-  float d = __builtin_fabsf((qa - fl) - 0.5f);
-  if (!(d > __builtin_fabsf(qa) * 0x1p-21f + 0x1p-60f)) qa = w / g.scf;
-  return __builtin_rintf(qa);
-}
-
-__device__ __forceinline__ float quant_code(float w, const GroupQ& g) {
-#pragma clang fp contract(off)
-  return fminf(fmaxf(rint_quotient(w, g) + g.z, 0.0f), 15.0f);
+  rint_quotients(w, g.scf, g.rcp, q);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) q[i] = fminf(fmaxf(q[i] + g.z, 0.0f), 15.0f);
 }
 
 // ------------------------------------------------------------------ fp64 -> fp16

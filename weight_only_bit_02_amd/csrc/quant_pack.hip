@@ -27,10 +27,11 @@ __global__ void __launch_bounds__(256) k_quant_pack(const uint16_t* __restrict__
                                                     int clip_steps, int sym, int group,
                                                     uint32_t* __restrict__ flags) {
   const int lane = threadIdx.x & 63;
-  const int gl = group / 8;          // lanes per group
-  const int gpu = 64 / gl;            // groups per unit
-  const int gi = lane / gl;           // group within the unit
-  const int li = lane % gl;           // lane within the group
+  const int lgl = group == 128 ? 4 : group == 64 ? 3 : 2;
+  const int gl = 1 << lgl;            // lanes per group (8 channels per lane)
+  const int gpu = 64 >> lgl;          // groups per unit
+  const int gi = lane >> lgl;         // group within the unit
+  const int li = lane & (gl - 1);     // lane within the group
   const int64_t G = K / group;
   const int64_t chunks = (G + gpu - 1) / gpu;
   const int64_t units = N * chunks;
@@ -73,9 +74,11 @@ __global__ void __launch_bounds__(256) k_quant_pack(const uint16_t* __restrict__
       mx = r * mx;
     }
     const GroupQ g = sym ? group_params_sym(mn, mx) : group_params(mn, mx);
+    float qc[8];
+    quant_codes(w, g, qc);
     uint32_t word = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) word |= (uint32_t)quant_code(w[i], g) << (4 * kNibbleOf[i]);
+    for (int i = 0; i < 8; ++i) word |= (uint32_t)qc[i] << (4 * kNibbleOf[i]);
 
     const uint32_t zi = (uint32_t)g.z;
     const uint32_t z_next = (uint32_t)__shfl_down((int)zi, gl);  // zero of group j + 1

@@ -155,6 +155,8 @@ __device__ __forceinline__ bool quantize_tile_group(const uint16_t* W, int64_t N
     }
     const GroupQ g = sym ? group_params_sym(mn, mx) : group_params(mn, mx);
     const float P = lds_p[row];
+    float qc[8];
+    quant_codes(wp, g, qc);
     uint32_t hi[4], lo[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -162,8 +164,7 @@ __device__ __forceinline__ bool quantize_tile_group(const uint16_t* W, int64_t N
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int c = 2 * i + e;
-        const float q = quant_code(wp[c], g);
-        const float deq = (q - g.z) * g.scf;  // exact: small integer times an fp16
+        const float deq = (qc[c] - g.z) * g.scf;  // exact: small integer times an fp16
         const float d = (wf[c] - deq * rs[c]) * P;
         h2[e] = f2h_bits(d);
         l2[e] = f2h_bits(d - h2f(h2[e]));
