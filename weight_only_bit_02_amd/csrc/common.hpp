@@ -180,13 +180,50 @@ __device__ __forceinline__ GroupQ group_params_sym(float mn, float mx) {
   return g;
 }
 
-// Codes q = clamp(rint(w / sc_h) + z, 0, 15) of NV values of one group.
+// Codes q = clamp(rint(w / sc_h) + z, 0, 15) of NV values w of one group, each the
+// exact fp32 product of two fp16 numbers (at most 22 significant bits).
+// q0 = rint(w * rcp) is taken when the residual e = w - q0 sc_h, formed by one fma, has
+// |e| < sc_h / 2. For |q0| < 2^12, q0 sc_h is exact (at most 23 bits) and so is e: when
+// q0 is within 1 of the quotient, |e| < 1.5 sc_h, and e is a multiple of the finer of
+// ulp(w) and ulp(sc_h), at least 2^-23 |e| when q0 != 0 (then |w| >= sc_h / 2), so e fits
+// 24 bits; q0 = 0 gives e = w. The test is therefore exact, and q0 is then the rint of
+// the real quotient. For larger
+// |q0| the guess is still within 1 of it and q0 + z lies far outside [0, 15], so the
+// clamp gives the same code either way. Everything else (|e| >= sc_h / 2: a wrong guess
+// or an exact tie; NaN; Inf) takes the correctly rounded division in a branch the wave
+// enters only when one of its lanes needs it.
 template <int NV>
 __device__ __forceinline__ void quant_codes(const float (&w)[NV], const GroupQ& g, float (&q)[NV]) {
 #pragma clang fp contract(off)
-  rint_quotients(w, g.scf, g.rcp, q);
+  const float half_sc = 0.5f * g.scf;  // exact
+  bool close[NV];
+  bool any = false;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    q[i] = __builtin_rintf(w[i] * g.rcp);
+    const float e = __builtin_fmaf(-q[i], g.scf, w[i]);
+    close[i] = !(__builtin_fabsf(e) < half_sc) && !(__builtin_fabsf(q[i]) >= 4096.0f);
+    any |= close[i];
+  }
+  if (__builtin_amdgcn_ballot_w64(any)) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (close[i]) q[i] = __builtin_rintf(w[i] / g.scf);  // correctly rounded division
+  }
 #pragma unroll
   for (int i = 0; i < NV; ++i) q[i] = fminf(fmaxf(q[i] + g.z, 0.0f), 15.0f);
+}
+
+// The packed word of 8 codes of channels 8w .. 8w + 7 (channel i in nibble kNibbleOf[i]):
+// byte b holds one channel pair, (0, 2), (4, 6), (1, 3), (5, 7) for b = 0 .. 3, so each
+// byte is qa + 16 qb (exact) written with one v_cvt_pk_u8_f32.
+__device__ __forceinline__ uint32_t pack_codes8(const float (&q)[8]) {
+  uint32_t word = 0;
+  word = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(q[2], 16.0f, q[0]), 0, word);
+  word = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(q[6], 16.0f, q[4]), 1, word);
+  word = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(q[3], 16.0f, q[1]), 2, word);
+  word = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(q[7], 16.0f, q[5]), 3, word);
+  return word;
 }
 
 // ------------------------------------------------------------------ fp64 -> fp16

@@ -34,14 +34,21 @@ __global__ void __launch_bounds__(256) k_quant_pack(const uint16_t* __restrict__
   const int li = lane & (gl - 1);     // lane within the group
   const int64_t G = K / group;
   const int64_t chunks = (G + gpu - 1) / gpu;
-  const int64_t units = N * chunks;
-  const int64_t wave0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-  const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
   const int64_t zbytes = (G + 1) / 2;
+  // unit u = (row n, chunk ch) = n * chunks + ch; the wave walks u = wave0, wave0 + nwaves,
+  // ... with (n, ch) stepped incrementally (wave-uniform, no division in the loop)
+  const int64_t wave0 = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)));
+  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+  const int64_t dn = nwaves / chunks, dc = nwaves - dn * chunks;
+  int64_t n = wave0 / chunks, ch = wave0 - n * chunks;
 
-  for (int64_t u = wave0; u < units; u += nwaves) {
-    const int64_t n = u / chunks;
-    const int64_t j = (u - n * chunks) * gpu + gi;  // group index
+  for (; n < N; n += dn, ch += dc) {
+    if (ch >= chunks) {
+      ch -= chunks;
+      ++n;
+      if (n >= N) break;
+    }
+    const int64_t j = ch * gpu + gi;  // group index
     const bool valid = j < G;
     const int64_t k0 = j * group + li * 8;
 
@@ -76,9 +83,7 @@ __global__ void __launch_bounds__(256) k_quant_pack(const uint16_t* __restrict__
     const GroupQ g = sym ? group_params_sym(mn, mx) : group_params(mn, mx);
     float qc[8];
     quant_codes(w, g, qc);
-    uint32_t word = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) word |= (uint32_t)qc[i] << (4 * kNibbleOf[i]);
+    const uint32_t word = pack_codes8(qc);
 
     const uint32_t zi = (uint32_t)g.z;
     const uint32_t z_next = (uint32_t)__shfl_down((int)zi, gl);  // zero of group j + 1
