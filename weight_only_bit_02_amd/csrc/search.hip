@@ -103,19 +103,22 @@ __global__ void __launch_bounds__(256) k_scale_range(const uint16_t* __restrict_
   }
 }
 
-// Quantizes group j of the 128-row tile starting at row n0 into LDS as (D P) split into
-// fp16 hi + lo, D = W - Q(W diag(s)) diag(1/s) (s == nullptr: s = 1). With CLIP the
-// group's extremes are shrunk by r before the quantizer sees them (weight clipping).
-// 16 lanes per (row, group), 8 weights each; returns whether a non-finite value was met.
-template <int NW, bool CLIP>
+// Quantizes 128-channel step j of rows [row_base, row_base + NROWS) of the 128-row tile
+// starting at row n0 into LDS as (D P) split into fp16 hi + lo,
+// D = W - Q(W diag(s)) diag(1/s) (s == nullptr: s = 1), with NW waves (tid counts their
+// threads from 0). With CLIP the group's extremes are shrunk by r before the quantizer
+// sees them (weight clipping). 16 lanes per (row, 128 channels), 8 weights each; returns
+// whether a non-finite value was met.
+template <int NW, bool CLIP, int NROWS>
 __device__ __forceinline__ bool quantize_tile_group(const uint16_t* W, int64_t N, int64_t K,
                                                     const uint16_t* s, float r, bool sym,
                                                     int group, int64_t n0, int64_t j,
                                                     const float* lds_p, uint16_t* hi_buf,
-                                                    uint16_t* lo_buf, int tid) {
+                                                    uint16_t* lo_buf, int tid, int row_base) {
   constexpr int kRowsPerPass = NW * 4;
-  constexpr int kPasses = kRowTile / kRowsPerPass;
-  const int q_row = tid >> 4;
+  constexpr int kPasses = NROWS / kRowsPerPass;
+  static_assert(kPasses * kRowsPerPass == NROWS, "whole passes");
+  const int q_row = row_base + (tid >> 4);
   const int li = tid & 15;
   bool bad = false;
 #pragma unroll
@@ -214,10 +217,20 @@ __global__ void __launch_bounds__(NW * 64)
     lds_p[r] = row_scale(n0 + r < N ? rowmax[n0 + r] : 0.0f, sr);
   __syncthreads();
 
+  // The waves form two sets of NW / 2 (one wave of each per SIMD), each quantizing half
+  // of the tile's rows. Per step, set A multiplies the current group and then quantizes
+  // its half of the next one, set B does the same in the opposite order, so on each SIMD
+  // one wave keeps the matrix core busy while the other runs the vector quantizer. The
+  // one barrier per step still orders both buffers: a step reads the buffer written in
+  // the step before and writes the one read there.
+  constexpr int NH = NW / 2;
+  const bool set_b = wave >= NH;
+  const int tid_set = set_b ? tid - NH * 64 : tid;
   bool bad = false;
   auto quantize = [&](int64_t j, int buf) {
-    bad |= quantize_tile_group<NW, false>(W, N, K, s, 1.0f, sym, group, n0, j, lds_p, lds_hi[buf],
-                                          lds_lo[buf], tid);
+    bad |= quantize_tile_group<NH, false, kRowTile / 2>(W, N, K, s, 1.0f, sym, group, n0, j, lds_p,
+                                                       lds_hi[buf], lds_lo[buf], tid_set,
+                                                       set_b ? kRowTile / 2 : 0);
   };
 
   for (int64_t tc = 0; tc < n_tchunks; ++tc) {
@@ -229,39 +242,48 @@ __global__ void __launch_bounds__(NW * 64)
 #pragma unroll
       for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
 
+    auto multiply = [&](int64_t j, int buf) {
+      if (!active) return;
+#pragma unroll 2
+      for (int st = 0; st < kGroup / 16; ++st) {
+        const int koff = st * 16 + khalf * 8;
+        half8 A[2], Bh[4], Bl[4];
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+          const int64_t tt = tw + a * 32 + m32;
+          uint4 v = *reinterpret_cast<const uint4*>(X + (tt < T ? tt : T - 1) * K + j * kGroup + koff);
+          if (tt >= T) v = make_uint4(0, 0, 0, 0);
+          A[a] = __builtin_bit_cast(half8, v);
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int r = b * 32 + m32;
+          Bh[b] = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(&lds_hi[buf][r * kLdsStride + koff]));
+          Bl[b] = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(&lds_lo[buf][r * kLdsStride + koff]));
+        }
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[a], Bh[b], acc[a][b], 0, 0, 0);
+            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[a], Bl[b], acc[a][b], 0, 0, 0);
+          }
+      }
+    };
+
     quantize(0, 0);
     __syncthreads();
     for (int64_t j = 0; j < G; ++j) {
       const int buf = (int)(j & 1);
       // next group's quantization (unconditional, clamped: the last one is redundant and
-      // lands in the buffer nobody reads) overlaps this group's MFMAs
-      quantize(j + 1 < G ? j + 1 : G - 1, buf ^ 1);
-      if (active) {
-#pragma unroll 2
-        for (int st = 0; st < kGroup / 16; ++st) {
-          const int koff = st * 16 + khalf * 8;
-          half8 A[2], Bh[4], Bl[4];
-#pragma unroll
-          for (int a = 0; a < 2; ++a) {
-            const int64_t tt = tw + a * 32 + m32;
-            uint4 v = *reinterpret_cast<const uint4*>(X + (tt < T ? tt : T - 1) * K + j * kGroup + koff);
-            if (tt >= T) v = make_uint4(0, 0, 0, 0);
-            A[a] = __builtin_bit_cast(half8, v);
-          }
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const int r = b * 32 + m32;
-            Bh[b] = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(&lds_hi[buf][r * kLdsStride + koff]));
-            Bl[b] = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(&lds_lo[buf][r * kLdsStride + koff]));
-          }
-#pragma unroll
-          for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-              acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[a], Bh[b], acc[a][b], 0, 0, 0);
-              acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[a], Bl[b], acc[a][b], 0, 0, 0);
-            }
-        }
+      // lands in the buffer nobody reads)
+      const int64_t jn = j + 1 < G ? j + 1 : G - 1;
+      if (!set_b) {
+        multiply(j, buf);
+        quantize(jn, buf ^ 1);
+      } else {
+        quantize(jn, buf ^ 1);
+        multiply(j, buf);
       }
       __syncthreads();
     }
@@ -330,13 +352,25 @@ __global__ void __launch_bounds__(NW * 64)
     lds_p[i] = row_scale(n0 + i < N ? rowmax[n0 + i] : 0.0f, sr);
   __syncthreads();
 
+  // two sets of waves in opposite phase, as in the scale search: set A multiplies then
+  // quantizes its half of the next step's rows, set B the reverse. Every wave runs the
+  // same barriers in the same order (the pair stores of small groups included), so the
+  // sets only drift apart between barriers.
+  constexpr int NH = NW / 2;
+  const bool set_b = wave >= NH;
+  const int tid_set = set_b ? tid - NH * 64 : tid;
   bool bad = false;
-  bad |= quantize_tile_group<NW, true>(W, N, K, s, r, sym, group, n0, 0, lds_p, lds_hi[0], lds_lo[0], tid);
+  auto quantize = [&](int64_t jq, int qbuf) {
+    bad |= quantize_tile_group<NH, true, kRowTile / 2>(W, N, K, s, r, sym, group, n0, jq, lds_p,
+                                                      lds_hi[qbuf], lds_lo[qbuf], tid_set,
+                                                      set_b ? kRowTile / 2 : 0);
+  };
+  quantize(0, 0);
   __syncthreads();
   for (int64_t j = 0; j < G; ++j) {
     const int buf = (int)(j & 1);
-    bad |= quantize_tile_group<NW, true>(W, N, K, s, r, sym, group, n0, j + 1 < G ? j + 1 : G - 1,
-                                         lds_p, lds_hi[buf ^ 1], lds_lo[buf ^ 1], tid);
+    const int64_t jn = j + 1 < G ? j + 1 : G - 1;
+    if (set_b) quantize(jn, buf ^ 1);
     f32x16 acc[2][4];
     // the step's 8 k16 slices in quarters of two; a group spans per = 8, 4 or 2 slices and
     // its error is taken when its last slice is done. Groups go through the two LDS slots:
@@ -413,8 +447,11 @@ __global__ void __launch_bounds__(NW * 64)
         }
       }
     }
+    if (!set_b) quantize(jn, buf ^ 1);
+    // end of step: the next one reads the buffer just written (by both sets) and, with one
+    // group per step, this step's errors are complete in their slot
+    __syncthreads();
     if (gps == 1) {
-      __syncthreads();
       if (tid < kRowTile && n0 + tid < N) {
         double tot = lds_red[buf][0][tid];
         for (int w = 1; w < NW; ++w) tot += lds_red[buf][w][tid];
