@@ -216,6 +216,7 @@ awq_status awq_linear_w4a16_gated_silu_ex(const void* X, int64_t M, const uint32
  *   out, the chosen error, or NULL; G = K / group_size. workspace: device,
  *   awq_clip_search_workspace_size bytes (n_shrink N G doubles plus N + 1 floats; 0 for an
  *   unsupported config or shape), 16-byte aligned.
+ *   flags: NONFINITE_INPUT (a NaN or Inf in W or s, or in X through a non-finite error).
  */
 size_t awq_clip_search_workspace_size(int64_t T, int64_t N, int64_t K, int32_t n_shrink,
                                       const awq_config* cfg);

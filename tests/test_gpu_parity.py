@@ -58,6 +58,24 @@ def test_quantize_pack_degenerate_groups():
     _assert_pack_equal(packed_host(p), oracle.quantize_pack(W))
 
 
+@pytest.mark.parametrize("bad", [np.inf, -np.inf, np.nan])
+def test_nonfinite_weight_flags(bad):
+    """A NaN or Inf weight raises NONFINITE_INPUT in the pack, the scale search and the
+    clip search (a NaN hides from min / max, so the searches also check their errors)."""
+    W = si.weights(64, 256, offset=5)
+    W[1, 3] = bad
+    X = si.activations(64, 256, offset=5)
+    f = flags_tensor()
+    awq.quantize_pack(to_dev(W), flags=f)
+    assert int(host(f)[0]) & oracle.FLAG_NONFINITE_INPUT
+    f = flags_tensor()
+    awq.search_scales(to_dev(X), to_dev(W), flags=f)
+    assert int(host(f)[0]) & oracle.FLAG_NONFINITE_INPUT
+    f = flags_tensor()
+    awq.clip_search(to_dev(X), to_dev(W), None, 200, 4, flags=f)
+    assert int(host(f)[0]) & oracle.FLAG_NONFINITE_INPUT
+
+
 def test_quantize_pack_flags():
     W = si.weights(2, 256, offset=5)
     W[1, 3] = np.inf

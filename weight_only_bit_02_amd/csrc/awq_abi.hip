@@ -192,7 +192,7 @@ awq_status awq_search_scales(const void* X, int64_t T, const void* W, int64_t N,
                                c.group_size, (float*)(ws + L.rowmax), (float*)(ws + L.srange), partials, flags, st);
   if (e == hipSuccess)
     e = awq::launch_search_reduce(partials, c.n_grid, L.n_partials, sg, K, (uint16_t*)s_best,
-                                  best_idx, err, st);
+                                  best_idx, err, flags, st);
   return hip_status(e);
 }
 
@@ -300,7 +300,7 @@ awq_status awq_clip_search(const void* X, int64_t T, const void* W, int64_t N, i
                                       (const uint16_t*)s, clip_steps, n_shrink, c.zero_point == 0,
                                       c.group_size, (float*)(ws + L.rowmax), (float*)(ws + L.srange), errs, flags, st);
   if (e == hipSuccess)
-    e = awq::launch_clip_reduce(errs, n_shrink, N, K / c.group_size, clip_idx, err, st);
+    e = awq::launch_clip_reduce(errs, n_shrink, N, K / c.group_size, clip_idx, err, flags, st);
   return hip_status(e);
 }
 

@@ -42,35 +42,48 @@ constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
 constexpr int kDppRowRor4 = 0x124;
 constexpr int kDppRowRor8 = 0x128;
 
+// min / max of a value and the value of the lane a DPP control selects, as one
+// DPP-modified instruction each (through the compiler, a DPP move plus a canonicalizing
+// max plus the min / max). s_nop 1 covers the two wait states a VALU write needs before a
+// DPP read of the same register.
+#define AWQ_DPP_MINMAX(NAME, CTRL)                                                        \
+  __device__ __forceinline__ void NAME(float& mn, float& mx) {                            \
+    float a, b;                                                                           \
+    asm("s_nop 1\n\tv_min_f32_dpp %0, %2, %2 " CTRL " row_mask:0xf bank_mask:0xf\n\t"     \
+        "v_max_f32_dpp %1, %3, %3 " CTRL " row_mask:0xf bank_mask:0xf"                     \
+        : "=&v"(a), "=&v"(b)                                                              \
+        : "v"(mn), "v"(mx));                                                              \
+    mn = a;                                                                               \
+    mx = b;                                                                               \
+  }
+AWQ_DPP_MINMAX(minmax_quad_xor1, "quad_perm:[1,0,3,2]")
+AWQ_DPP_MINMAX(minmax_quad_xor2, "quad_perm:[2,3,0,1]")
+AWQ_DPP_MINMAX(minmax_row_ror4, "row_ror:4")
+AWQ_DPP_MINMAX(minmax_row_ror8, "row_ror:8")
+AWQ_DPP_MINMAX(minmax_row_half_mirror, "row_half_mirror")
+#undef AWQ_DPP_MINMAX
+
+// Min / max over each 16-lane DPP row (128-channel groups): quad butterflies, then row
+// rotations; every lane of the row ends up with the result.
 __device__ __forceinline__ void row16_minmax(float& mn, float& mx) {
-  mn = fminf(mn, dpp_f32<kDppQuadXor1>(mn));
-  mx = fmaxf(mx, dpp_f32<kDppQuadXor1>(mx));
-  mn = fminf(mn, dpp_f32<kDppQuadXor2>(mn));
-  mx = fmaxf(mx, dpp_f32<kDppQuadXor2>(mx));
-  mn = fminf(mn, dpp_f32<kDppRowRor4>(mn));
-  mx = fmaxf(mx, dpp_f32<kDppRowRor4>(mx));
-  mn = fminf(mn, dpp_f32<kDppRowRor8>(mn));
-  mx = fmaxf(mx, dpp_f32<kDppRowRor8>(mx));
+  minmax_quad_xor1(mn, mx);
+  minmax_quad_xor2(mn, mx);
+  minmax_row_ror4(mn, mx);
+  minmax_row_ror8(mn, mx);
 }
 
 // Min / max over the 8-lane halves of each DPP row (64-channel groups): quad butterflies,
 // then row_half_mirror, which pairs lane i of a half with lane 7 - i (the other quad).
-constexpr int kDppRowHalfMirror = 0x141;
 __device__ __forceinline__ void row8_minmax(float& mn, float& mx) {
-  mn = fminf(mn, dpp_f32<kDppQuadXor1>(mn));
-  mx = fmaxf(mx, dpp_f32<kDppQuadXor1>(mx));
-  mn = fminf(mn, dpp_f32<kDppQuadXor2>(mn));
-  mx = fmaxf(mx, dpp_f32<kDppQuadXor2>(mx));
-  mn = fminf(mn, dpp_f32<kDppRowHalfMirror>(mn));
-  mx = fmaxf(mx, dpp_f32<kDppRowHalfMirror>(mx));
+  minmax_quad_xor1(mn, mx);
+  minmax_quad_xor2(mn, mx);
+  minmax_row_half_mirror(mn, mx);
 }
 
 // Min / max over each quad of lanes (32-channel groups): the two quad_perm butterflies.
 __device__ __forceinline__ void quad_minmax(float& mn, float& mx) {
-  mn = fminf(mn, dpp_f32<kDppQuadXor1>(mn));
-  mx = fmaxf(mx, dpp_f32<kDppQuadXor1>(mx));
-  mn = fminf(mn, dpp_f32<kDppQuadXor2>(mn));
-  mx = fmaxf(mx, dpp_f32<kDppQuadXor2>(mx));
+  minmax_quad_xor1(mn, mx);
+  minmax_quad_xor2(mn, mx);
 }
 
 // Group min / max when each lane holds 8 consecutive channels: a group of g channels is

@@ -24,7 +24,8 @@ hipError_t launch_clip_err(const uint16_t* X, int64_t T, const uint16_t* W, int6
                            int group, float* rowmax, float* srange, double* err, uint32_t* flags,
                            hipStream_t stream);
 hipError_t launch_clip_reduce(const double* err, int n_shrink, int64_t N, int64_t G,
-                              uint8_t* clip_idx, double* err_best, hipStream_t stream);
+                              uint8_t* clip_idx, double* err_best, uint32_t* flags,
+                              hipStream_t stream);
 constexpr int kClipMaxTokens = 512;
 constexpr int kClipMaxShrink = 256;
 
@@ -51,7 +52,8 @@ hipError_t launch_search_err(const uint16_t* X, int64_t T, const uint16_t* W, in
 // a6: fixed-order sums of the partials, first-minimum argmin, s_best copy.
 hipError_t launch_search_reduce(const double* partials, int n_grid, int64_t n_partials,
                                 const uint16_t* s_grid, int64_t K, uint16_t* s_best,
-                                int32_t* best_idx, double* err, hipStream_t stream);
+                                int32_t* best_idx, double* err, uint32_t* flags,
+                                hipStream_t stream);
 
 // a7 / a8: Y = X deq(W)^T. gated (f1): W is gate|up stacked (N/2 rows each) and
 // Y[M][N/2] = SiLU(X deq(W_gate)^T) * (X deq(W_up)^T); N is even.

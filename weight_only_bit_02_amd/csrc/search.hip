@@ -120,29 +120,37 @@ __device__ __forceinline__ bool quantize_tile_group(const uint16_t* W, int64_t N
   static_assert(kPasses * kRowsPerPass == NROWS, "whole passes");
   const int q_row = row_base + (tid >> 4);
   const int li = tid & 15;
+  const int64_t k0 = j * kGroup + li * 8;
+  // the thread's 8 channels are the same in every pass: s and 1/s once
+  uint4 sv = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);  // s = 1
+  if (!CLIP || s) sv = *reinterpret_cast<const uint4*>(s + k0);
+  float sf[8], rs[8];
+  {
+    const uint32_t sd[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sf[2 * i] = h2f((uint16_t)(sd[i] & 0xFFFF));
+      sf[2 * i + 1] = h2f((uint16_t)(sd[i] >> 16));
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) rs[i] = __builtin_amdgcn_rcpf(sf[i]);
+  }
   bool bad = false;
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) {
     const int row = p * kRowsPerPass + q_row;
     const int64_t n = n0 + row;
-    const int64_t k0 = j * kGroup + li * 8;
     const int64_t nc = n < N ? n : N - 1;
     uint4 wv = *reinterpret_cast<const uint4*>(W + nc * K + k0);
     if (n >= N) wv = make_uint4(0, 0, 0, 0);
-    uint4 sv = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);  // s = 1
-    if (!CLIP || s) sv = *reinterpret_cast<const uint4*>(s + k0);
     const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
-    const uint32_t sd[4] = {sv.x, sv.y, sv.z, sv.w};
-    float wf[8], wp[8], rs[8];
+    float wf[8], wp[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       wf[2 * i] = h2f((uint16_t)(wd[i] & 0xFFFF));
       wf[2 * i + 1] = h2f((uint16_t)(wd[i] >> 16));
-      const float s0 = h2f((uint16_t)(sd[i] & 0xFFFF)), s1 = h2f((uint16_t)(sd[i] >> 16));
-      wp[2 * i] = wf[2 * i] * s0;
-      wp[2 * i + 1] = wf[2 * i + 1] * s1;
-      rs[2 * i] = __builtin_amdgcn_rcpf(s0);
-      rs[2 * i + 1] = __builtin_amdgcn_rcpf(s1);
+      wp[2 * i] = wf[2 * i] * sf[2 * i];
+      wp[2 * i + 1] = wf[2 * i + 1] * sf[2 * i + 1];
     }
     float mn = wp[0], mx = wp[0];
 #pragma unroll
@@ -462,16 +470,21 @@ __global__ void __launch_bounds__(NW * 64)
   if (bad && flags && ci == 0) atomicOr(flags, AWQ_FLAG_NONFINITE_INPUT);
 }
 
-// One thread per (row, group): the first ratio index with the smallest error.
+// One thread per (row, group): the first ratio index with the smallest error. A
+// non-finite error can only come from a NaN or Inf weight or activation (the tile's
+// min / max drop a NaN), so it raises NONFINITE_INPUT.
 __global__ void __launch_bounds__(256)
     k_clip_reduce(const double* __restrict__ err, int n_shrink, int64_t NG,
-                  uint8_t* __restrict__ clip_idx, double* __restrict__ err_best) {
+                  uint8_t* __restrict__ clip_idx, double* __restrict__ err_best,
+                  uint32_t* __restrict__ flags) {
   const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (u >= NG) return;
   double best = err[u];
   int bi = 0;
+  bool bad = !__builtin_isfinite(best);
   for (int i = 1; i < n_shrink; ++i) {
     const double v = err[(int64_t)i * NG + u];
+    bad |= !__builtin_isfinite(v);
     if (v < best) {
       best = v;
       bi = i;
@@ -479,6 +492,7 @@ __global__ void __launch_bounds__(256)
   }
   clip_idx[u] = (uint8_t)bi;
   if (err_best) err_best[u] = best;
+  if (bad && flags) atomicOr(flags, AWQ_FLAG_NONFINITE_INPUT);
 }
 
 hipError_t launch_clip_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N,
@@ -506,18 +520,22 @@ hipError_t launch_clip_err(const uint16_t* X, int64_t T, const uint16_t* W, int6
 }
 
 hipError_t launch_clip_reduce(const double* err, int n_shrink, int64_t N, int64_t G,
-                              uint8_t* clip_idx, double* err_best, hipStream_t stream) {
+                              uint8_t* clip_idx, double* err_best, uint32_t* flags,
+                              hipStream_t stream) {
   const int64_t NG = N * G;
   hipLaunchKernelGGL(k_clip_reduce, dim3((unsigned)((NG + 255) / 256)), dim3(256), 0, stream, err,
-                     n_shrink, NG, clip_idx, err_best);
+                     n_shrink, NG, clip_idx, err_best, flags);
   return hipGetLastError();
 }
 
-// One block: err_i = sum of partials of grid point i in index order; first minimum.
+// One block: err_i = sum of partials of grid point i in index order; first minimum. A
+// non-finite error can only come from a NaN or Inf weight or activation (the tile's
+// min / max drop a NaN), so it raises NONFINITE_INPUT.
 __global__ void __launch_bounds__(256)
     k_search_reduce(const double* __restrict__ partials, int n_grid, int64_t n_partials,
                     const uint16_t* __restrict__ s_grid, int64_t K, uint16_t* __restrict__ s_best,
-                    int32_t* __restrict__ best_idx, double* __restrict__ err) {
+                    int32_t* __restrict__ best_idx, double* __restrict__ err,
+                    uint32_t* __restrict__ flags) {
   __shared__ double lds_err[64];
   __shared__ int lds_best;
   const int tid = threadIdx.x;
@@ -526,6 +544,7 @@ __global__ void __launch_bounds__(256)
     const double* p = partials + (int64_t)tid * n_partials;
     for (int64_t i = 0; i < n_partials; ++i) tot += p[i];
     lds_err[tid] = tot;
+    if (!__builtin_isfinite(tot) && flags) atomicOr(flags, AWQ_FLAG_NONFINITE_INPUT);
   }
   __syncthreads();
   if (tid == 0) {
@@ -569,9 +588,10 @@ hipError_t launch_search_err(const uint16_t* X, int64_t T, const uint16_t* W, in
 
 hipError_t launch_search_reduce(const double* partials, int n_grid, int64_t n_partials,
                                 const uint16_t* s_grid, int64_t K, uint16_t* s_best,
-                                int32_t* best_idx, double* err, hipStream_t stream) {
+                                int32_t* best_idx, double* err, uint32_t* flags,
+                                hipStream_t stream) {
   hipLaunchKernelGGL(k_search_reduce, dim3(1), dim3(256), 0, stream, partials, n_grid,
-                     n_partials, s_grid, K, s_best, best_idx, err);
+                     n_partials, s_grid, K, s_best, best_idx, err, flags);
   return hipGetLastError();
 }
 
