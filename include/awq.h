@@ -147,7 +147,8 @@ awq_status awq_candidate_scales(const double* act_mean, int64_t K, const awq_con
  *   best_idx  int32 [1]         out: best
  *   err       fp64 [n_grid]     out (may be NULL)
  *   s_grid    fp16 [n_grid][K]  out (may be NULL): every candidate scale
- *   workspace device scratch of awq_search_workspace_size(T, N, K, cfg) bytes
+ *   workspace device scratch of awq_search_workspace_size(T, N, K, cfg) bytes (statistics,
+ *             candidate scales, partial errors and a copy of X in MFMA operand order)
  *   flags     NONFINITE_INPUT, SCALE_CLAMPED, SEARCH_RANGE
  *   Follow with awq_quantize_pack(W, s_best) to obtain the packed weights.
  */
@@ -214,8 +215,9 @@ awq_status awq_linear_w4a16_gated_silu_ex(const void* X, int64_t M, const uint32
  *   W fp16 [N][K]; s fp16 [K] or NULL; 1 <= n_shrink <= min(clip_steps, 256).
  *   clip_idx uint8 [N][G] out (pass to awq_quantize_pack_clipped); err fp64 [N][G]
  *   out, the chosen error, or NULL; G = K / group_size. workspace: device,
- *   awq_clip_search_workspace_size bytes (n_shrink N G doubles plus N + 1 floats; 0 for an
- *   unsupported config or shape), 16-byte aligned.
+ *   awq_clip_search_workspace_size bytes (n_shrink N G doubles, N + 1 floats and a copy of
+ *   X in MFMA operand order, T rounded up to 64 tokens; 0 for an unsupported config or
+ *   shape, T included), 16-byte aligned.
  *   flags: NONFINITE_INPUT (a NaN or Inf in W or s, or in X through a non-finite error).
  */
 size_t awq_clip_search_workspace_size(int64_t T, int64_t N, int64_t K, int32_t n_shrink,

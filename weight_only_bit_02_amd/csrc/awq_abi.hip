@@ -32,8 +32,9 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Search workspace: [u: int64 K][act: fp64 K][s_grid: fp16 n_grid K][rowmax: f32 N]
 // [srange: f32 n_grid][partials: fp64 n_grid x row tiles x token chunks]
+// [xp: X in MFMA operand order, T rounded up to 64 tokens]
 struct SearchLayout {
-  size_t u, act, sgrid, rowmax, srange, partials, total;
+  size_t u, act, sgrid, rowmax, srange, partials, xp, total;
   int64_t n_partials;  // per grid point
 };
 
@@ -48,21 +49,24 @@ SearchLayout search_layout(int64_t T, int64_t N, int64_t K, int n_grid) {
   L.rowmax = align256(L.sgrid + (size_t)n_grid * K * 2);
   L.srange = align256(L.rowmax + (size_t)N * 4);
   L.partials = align256(L.srange + (size_t)n_grid * 4);
-  L.total = align256(L.partials + (size_t)n_grid * L.n_partials * 8);
+  L.xp = align256(L.partials + (size_t)n_grid * L.n_partials * 8);
+  L.total = align256(L.xp + awq::packed_x_bytes(T, K));
   return L;
 }
 
 // Clip-search workspace: [rowmax: f32 N][srange: f32 1][err: fp64 n_shrink x N x G]
+// [xp: X in MFMA operand order, T rounded up to 64 tokens]
 struct ClipLayout {
-  size_t rowmax, srange, err, total;
+  size_t rowmax, srange, err, xp, total;
 };
 
-ClipLayout clip_layout(int64_t N, int64_t K, int n_shrink, int group) {
+ClipLayout clip_layout(int64_t T, int64_t N, int64_t K, int n_shrink, int group) {
   ClipLayout L;
   L.rowmax = 0;
   L.srange = align256((size_t)N * 4);
   L.err = align256(L.srange + 4);
-  L.total = align256(L.err + (size_t)n_shrink * N * (K / group) * 8);
+  L.xp = align256(L.err + (size_t)n_shrink * N * (K / group) * 8);
+  L.total = align256(L.xp + awq::packed_x_bytes(T, K));
   return L;
 }
 
@@ -189,7 +193,8 @@ awq_status awq_search_scales(const void* X, int64_t T, const void* W, int64_t N,
   if (e == hipSuccess) e = awq::launch_scalegen(act, K, c.n_grid, sg, st);
   if (e == hipSuccess)
     e = awq::launch_search_err(Xh, T, (const uint16_t*)W, N, K, sg, c.n_grid, c.zero_point == 0,
-                               c.group_size, (float*)(ws + L.rowmax), (float*)(ws + L.srange), partials, flags, st);
+                               c.group_size, (float*)(ws + L.rowmax), (float*)(ws + L.srange),
+                               (uint4*)(ws + L.xp), partials, flags, st);
   if (e == hipSuccess)
     e = awq::launch_search_reduce(partials, c.n_grid, L.n_partials, sg, K, (uint16_t*)s_best,
                                   best_idx, err, flags, st);
@@ -270,10 +275,10 @@ awq_status awq_linear_w4a16_gated_silu(const void* X, int64_t M, const uint32_t*
 
 size_t awq_clip_search_workspace_size(int64_t T, int64_t N, int64_t K, int32_t n_shrink,
                                       const awq_config* cfg) {
-  (void)T;
   const awq_config c = resolve(cfg);
   if (!supported(c) || !good_nk(N, K) || n_shrink < 1) return 0;
-  return clip_layout(N, K, n_shrink, c.group_size).total;
+  if (T < 1 || T > awq::kClipMaxTokens) return 0;
+  return clip_layout(T, N, K, n_shrink, c.group_size).total;
 }
 
 awq_status awq_clip_search(const void* X, int64_t T, const void* W, int64_t N, int64_t K,
@@ -291,14 +296,15 @@ awq_status awq_clip_search(const void* X, int64_t T, const void* W, int64_t N, i
   if (!aligned16(X) || !aligned16(W) || (s && !aligned16(s)) || (err && !aligned16(err)) ||
       (flags && !aligned4(flags)))
     return AWQ_ERR_MISALIGNED;
-  const ClipLayout L = clip_layout(N, K, n_shrink, c.group_size);
+  const ClipLayout L = clip_layout(T, N, K, n_shrink, c.group_size);
   if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return AWQ_ERR_WORKSPACE;
   char* ws = (char*)workspace;
   hipStream_t st = (hipStream_t)stream;
   double* errs = (double*)(ws + L.err);
   hipError_t e = awq::launch_clip_err((const uint16_t*)X, T, (const uint16_t*)W, N, K,
                                       (const uint16_t*)s, clip_steps, n_shrink, c.zero_point == 0,
-                                      c.group_size, (float*)(ws + L.rowmax), (float*)(ws + L.srange), errs, flags, st);
+                                      c.group_size, (float*)(ws + L.rowmax), (float*)(ws + L.srange),
+                                      (uint4*)(ws + L.xp), errs, flags, st);
   if (e == hipSuccess)
     e = awq::launch_clip_reduce(errs, n_shrink, N, K / c.group_size, clip_idx, err, flags, st);
   return hip_status(e);

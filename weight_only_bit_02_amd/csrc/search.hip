@@ -103,6 +103,39 @@ __global__ void __launch_bounds__(256) k_scale_range(const uint16_t* __restrict_
   }
 }
 
+// X in the order the MFMA A operand reads it. For 64-token tile t (tokens 64 t .. 64 t + 63,
+// zeros past T), 128-channel step j, k16 slice st and token half a, lane l's 16 bytes are
+// X[64 t + 32 a + l % 32][128 j + 16 st + 8 (l / 32) .. + 8], so one wave's load of a slice
+// is 1 KiB contiguous (X as stored puts each lane 8 KiB apart, and the lines a step needs
+// do not stay in the L1 between the slices that share them).
+__global__ void __launch_bounds__(256)
+    k_pack_x(const uint16_t* __restrict__ X, int64_t T, int64_t K, int64_t tiles,
+             uint4* __restrict__ xp) {
+  const int64_t G = K / kGroup;
+  const int64_t total = tiles * G * 8 * 2 * 64;  // 16-byte entries
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(i & 63);
+    int64_t r = i >> 6;
+    const int a = (int)(r & 1);
+    r >>= 1;
+    const int st = (int)(r & 7);
+    r >>= 3;
+    const int64_t j = r % G, t = r / G;
+    const int64_t tok = t * 64 + a * 32 + (lane & 31);
+    const int64_t ch = j * kGroup + st * 16 + (lane >> 5) * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (tok < T) v = *reinterpret_cast<const uint4*>(X + tok * K + ch);
+    xp[i] = v;
+  }
+}
+
+// Entry (tile, j, st, a) of the packed X: the wave's 64 consecutive 16-byte pieces.
+__device__ __forceinline__ const uint4* packed_x(const uint4* xp, int64_t G, int64_t tile,
+                                                 int64_t j, int st, int a) {
+  return xp + (((tile * G + j) * 8 + st) * 2 + a) * 64;
+}
+
 // Quantizes 128-channel step j of rows [row_base, row_base + NROWS) of the 128-row tile
 // starting at row n0 into LDS as (D P) split into fp16 hi + lo,
 // D = W - Q(W diag(s)) diag(1/s) (s == nullptr: s = 1), with NW waves (tid counts their
@@ -191,7 +224,7 @@ __device__ __forceinline__ bool quantize_tile_group(const uint16_t* W, int64_t N
 
 template <int NW>
 __global__ void __launch_bounds__(NW * 64)
-    k_search_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N, int64_t K,
+    k_search_err(const uint4* xp, int64_t T, const uint16_t* W, int64_t N, int64_t K,
                  const uint16_t* s_grid, int n_grid, int sym, int group, const float* rowmax,
                  const float* srange,
                  double* __restrict__ partials, uint32_t* __restrict__ flags, int64_t n_ntiles,
@@ -250,6 +283,7 @@ __global__ void __launch_bounds__(NW * 64)
 #pragma unroll
       for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
 
+    const int64_t tile = tw / kTokPerWave;  // the wave's 64-token tile of the packed X
     auto multiply = [&](int64_t j, int buf) {
       if (!active) return;
 #pragma unroll 2
@@ -257,12 +291,8 @@ __global__ void __launch_bounds__(NW * 64)
         const int koff = st * 16 + khalf * 8;
         half8 A[2], Bh[4], Bl[4];
 #pragma unroll
-        for (int a = 0; a < 2; ++a) {
-          const int64_t tt = tw + a * 32 + m32;
-          uint4 v = *reinterpret_cast<const uint4*>(X + (tt < T ? tt : T - 1) * K + j * kGroup + koff);
-          if (tt >= T) v = make_uint4(0, 0, 0, 0);
-          A[a] = __builtin_bit_cast(half8, v);
-        }
+        for (int a = 0; a < 2; ++a)
+          A[a] = __builtin_bit_cast(half8, packed_x(xp, G, tile, j, st, a)[lane]);
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const int r = b * 32 + m32;
@@ -324,7 +354,7 @@ __global__ void __launch_bounds__(NW * 64)
 
 template <int NW>
 __global__ void __launch_bounds__(NW * 64)
-    k_clip_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N, int64_t K,
+    k_clip_err(const uint4* xp, int64_t T, const uint16_t* W, int64_t N, int64_t K,
                const uint16_t* s, int clip_steps, int n_shrink, int sym, int group,
                const float* rowmax, const float* srange, double* __restrict__ err,
                uint32_t* __restrict__ flags, int64_t n_ntiles, int64_t per_xcd) {
@@ -399,12 +429,8 @@ __global__ void __launch_bounds__(NW * 64)
           const int koff = st * 16 + khalf * 8;
           half8 A[2], Bh[4], Bl[4];
 #pragma unroll
-          for (int a = 0; a < 2; ++a) {
-            const int64_t tt = tw + a * 32 + m32;
-            uint4 v = *reinterpret_cast<const uint4*>(X + (tt < T ? tt : T - 1) * K + j * kGroup + koff);
-            if (tt >= T) v = make_uint4(0, 0, 0, 0);
-            A[a] = __builtin_bit_cast(half8, v);
-          }
+          for (int a = 0; a < 2; ++a)
+            A[a] = __builtin_bit_cast(half8, packed_x(xp, G, wave, j, st, a)[lane]);
 #pragma unroll
           for (int b = 0; b < 4; ++b) {
             const int row = b * 32 + m32;
@@ -495,12 +521,27 @@ __global__ void __launch_bounds__(256)
   if (bad && flags) atomicOr(flags, AWQ_FLAG_NONFINITE_INPUT);
 }
 
+static hipError_t launch_pack_x(const uint16_t* X, int64_t T, int64_t K, uint4* xp,
+                                hipStream_t stream) {
+  const int64_t tiles = (T + kTokPerWave - 1) / kTokPerWave;
+  const int64_t total = tiles * (K / kGroup) * 8 * 2 * 64;
+  const int64_t blocks = (total + 255) / 256 < 8192 ? (total + 255) / 256 : 8192;
+  hipLaunchKernelGGL(k_pack_x, dim3((unsigned)blocks), dim3(256), 0, stream, X, T, K, tiles, xp);
+  return hipGetLastError();
+}
+
+size_t packed_x_bytes(int64_t T, int64_t K) {
+  return (size_t)((T + kTokPerWave - 1) / kTokPerWave) * kTokPerWave * K * 2;
+}
+
 hipError_t launch_clip_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N,
                            int64_t K, const uint16_t* s, int clip_steps, int n_shrink, bool sym,
-                           int group, float* rowmax, float* srange, double* err, uint32_t* flags,
-                           hipStream_t stream) {
+                           int group, float* rowmax, float* srange, uint4* xp, double* err,
+                           uint32_t* flags, hipStream_t stream) {
   hipLaunchKernelGGL(k_row_absmax, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, stream, W, N, K, rowmax);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_pack_x(X, T, K, xp, stream);
   if (e != hipSuccess) return e;
   if (s) {
     hipLaunchKernelGGL(k_scale_range, dim3(1), dim3(256), 0, stream, s, K, srange, flags);
@@ -511,10 +552,10 @@ hipError_t launch_clip_err(const uint16_t* X, int64_t T, const uint16_t* W, int6
   const int64_t per_xcd = (n_ntiles * n_shrink + kXcds - 1) / kXcds;
   const dim3 grid((unsigned)(per_xcd * kXcds));
   if (T <= 4 * kTokPerWave)
-    hipLaunchKernelGGL(k_clip_err<4>, grid, dim3(256), 0, stream, X, T, W, N, K, s, clip_steps,
+    hipLaunchKernelGGL(k_clip_err<4>, grid, dim3(256), 0, stream, xp, T, W, N, K, s, clip_steps,
                        n_shrink, (int)sym, group, rowmax, srange, err, flags, n_ntiles, per_xcd);
   else
-    hipLaunchKernelGGL(k_clip_err<8>, grid, dim3(512), 0, stream, X, T, W, N, K, s, clip_steps,
+    hipLaunchKernelGGL(k_clip_err<8>, grid, dim3(512), 0, stream, xp, T, W, N, K, s, clip_steps,
                        n_shrink, (int)sym, group, rowmax, srange, err, flags, n_ntiles, per_xcd);
   return hipGetLastError();
 }
@@ -565,11 +606,12 @@ int search_token_chunk(int64_t T) { return T <= 4 * kTokPerWave ? 4 * kTokPerWav
 
 hipError_t launch_search_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N,
                              int64_t K, const uint16_t* s_grid, int n_grid, bool sym, int group,
-                             float* rowmax,
-                             float* srange, double* partials, uint32_t* flags,
-                             hipStream_t stream) {
+                             float* rowmax, float* srange, uint4* xp, double* partials,
+                             uint32_t* flags, hipStream_t stream) {
   hipLaunchKernelGGL(k_row_absmax, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, stream, W, N, K, rowmax);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_pack_x(X, T, K, xp, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_scale_range, dim3((unsigned)n_grid), dim3(256), 0, stream, s_grid, K, srange, flags);
   e = hipGetLastError();
@@ -578,10 +620,10 @@ hipError_t launch_search_err(const uint16_t* X, int64_t T, const uint16_t* W, in
   const int64_t per_xcd = (n_ntiles * n_grid + kXcds - 1) / kXcds;
   const dim3 grid((unsigned)(per_xcd * kXcds));
   if (T <= 4 * kTokPerWave)
-    hipLaunchKernelGGL(k_search_err<4>, grid, dim3(256), 0, stream, X, T, W, N, K, s_grid, n_grid,
+    hipLaunchKernelGGL(k_search_err<4>, grid, dim3(256), 0, stream, xp, T, W, N, K, s_grid, n_grid,
                        (int)sym, group, rowmax, srange, partials, flags, n_ntiles, per_xcd);
   else
-    hipLaunchKernelGGL(k_search_err<8>, grid, dim3(512), 0, stream, X, T, W, N, K, s_grid, n_grid,
+    hipLaunchKernelGGL(k_search_err<8>, grid, dim3(512), 0, stream, xp, T, W, N, K, s_grid, n_grid,
                        (int)sym, group, rowmax, srange, partials, flags, n_ntiles, per_xcd);
   return hipGetLastError();
 }
