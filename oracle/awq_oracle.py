@@ -63,11 +63,12 @@ __all__ = [
     "linear_within_tolerance", "fp16_midpoint_distance", "relative_gap", "packed_bytes",
     "silu", "SILU_DMAX", "gated_silu_reference", "gated_silu_within_tolerance",
     "apply_inverse_scale", "FLAG_OVERFLOW",
-    "CLIP_STEPS", "clip_ratios", "clip_errors", "clip_search",
+    "CLIP_STEPS", "clip_ratios", "clip_errors", "clip_search", "W_BITS",
 ]
 
 GROUP = 128                       # [AWQ-PRACTICE] §2.3; [AWQ-SKILL] q_group_size
 QMAX = 15                         # 4-bit unsigned codes 0..15 with a zero point
+W_BITS = (4, 8)                   # code widths: 4 (the format measured) and 8 ([AWQ-PRACTICE] §5.1)
 N_GRID = 20                       # alpha grid: 20 points in [0, 1)
 ACT_FLOOR = 2.0 ** -14            # floor of the activation statistic (smallest normal fp16)
 SCALE_FLOOR = np.float32(2.0 ** -14)
@@ -128,7 +129,7 @@ def candidate_scales(a: np.ndarray, n_grid: int = N_GRID) -> tuple[np.ndarray, n
 
 # --------------------------------------------------------------------------- a3
 def quantize_groups(W16: np.ndarray, s16: np.ndarray | None = None, clip_ratio: np.ndarray | None = None,
-                    zero_point: bool = True, group: int = GROUP) -> dict:
+                    zero_point: bool = True, group: int = GROUP, w_bit: int = 4) -> dict:
     """Group-wise asymmetric 4-bit quantization of W * diag(s).
 
     [AWQ-PRACTICE] §2.3 (128 consecutive input channels share one step) and §2.1
@@ -153,12 +154,16 @@ def quantize_groups(W16: np.ndarray, s16: np.ndarray | None = None, clip_ratio: 
       3'. sc = max(|mx|, |mn|) / 7             6'. z = 8
     so q - 8 = clamp(rint(w' / sc_h), -8, 7) is the signed code, stored offset by 8 in the
     same format (every zero nibble 8).
+    8-bit codes (w_bit = 8; [AWQ-PRACTICE] §5.1 raises w_bit when accuracy drops): the same
+    steps with 15 -> 255 (codes 0..255) and, symmetric, 7 -> 127 and z = 128.
     Returns dict(q uint8 [N][K], z uint8 [N][G], scale fp16 [N][G], flags int).
     """
     W16 = np.asarray(W16)
     assert W16.dtype == np.float16 and W16.ndim == 2
     N, K = W16.shape
-    assert group in (GROUP, 64, 32) and K % group == 0
+    assert group in (GROUP, 64, 32) and K % group == 0 and w_bit in W_BITS
+    qmax = _F32(2 ** w_bit - 1)
+    half = _F32(2 ** (w_bit - 1))
     G = K // group
     w = W16.astype(_F32)
     if s16 is not None:
@@ -177,9 +182,9 @@ def quantize_groups(W16: np.ndarray, s16: np.ndarray | None = None, clip_ratio: 
         mx = (r * mx).astype(_F32)
         mn = (r * mn).astype(_F32)
     if zero_point:
-        sc = (mx - mn) / _F32(QMAX)
+        sc = (mx - mn) / qmax
     else:
-        sc = np.maximum(np.abs(mx), np.abs(mn)) / _F32(7)
+        sc = np.maximum(np.abs(mx), np.abs(mn)) / (half - _F32(1))
     sc = np.maximum(sc, SCALE_FLOOR)
     if np.any(sc > SCALE_MAX):
         flags |= FLAG_SCALE_CLAMPED
@@ -188,10 +193,10 @@ def quantize_groups(W16: np.ndarray, s16: np.ndarray | None = None, clip_ratio: 
     sc_f = sc_h.astype(_F32)
     with np.errstate(invalid="ignore"):
         if zero_point:
-            z = np.clip(np.rint(-mn / sc_f), _F32(0), _F32(QMAX))
+            z = np.clip(np.rint(-mn / sc_f), _F32(0), qmax)
         else:
-            z = np.full(sc_f.shape, _F32(8))
-        q = np.clip(np.rint(wg / sc_f[:, :, None]) + z[:, :, None], _F32(0), _F32(QMAX))
+            z = np.full(sc_f.shape, half)
+        q = np.clip(np.rint(wg / sc_f[:, :, None]) + z[:, :, None], _F32(0), qmax)
     q = np.nan_to_num(q, nan=0.0).astype(np.uint8).reshape(N, K)
     z = np.nan_to_num(z, nan=0.0).astype(np.uint8)
     return {"q": q, "z": z, "scale": sc_h, "flags": flags}
@@ -205,18 +210,26 @@ def quantize_groups(W16: np.ndarray, s16: np.ndarray | None = None, clip_ratio: 
 NIBBLE_CHANNEL = (0, 2, 4, 6, 1, 3, 5, 7)
 
 
-def pack(q: np.ndarray, z: np.ndarray, scale: np.ndarray) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
-    """Nibble packing of codes and zero points.
+def pack(q: np.ndarray, z: np.ndarray, scale: np.ndarray, w_bit: int = 4) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Packing of codes and zero points.
 
     The pages give no layout ([AWQ-WIKI] only names "platform-aware weight packing").
-    Reading: qweight uint32 [N][K/8]; word w covers input channels 8w..8w+7 and nibble j
-    (bits 4j..4j+3) holds the code of channel 8w + NIBBLE_CHANNEL[j]; zeros uint8
+    Reading, 4-bit: qweight uint32 [N][K/8]; word w covers input channels 8w..8w+7 and
+    nibble j (bits 4j..4j+3) holds the code of channel 8w + NIBBLE_CHANNEL[j]; zeros uint8
     [N][ceil(G/2)] where the low nibble holds the even group and the high nibble the
     odd group; scales fp16 [N][G].
+    8-bit: qweight uint32 [N][K/4]; byte j of word w holds the code of channel 4w + j;
+    zeros uint8 [N][G], one byte per group; scales fp16 [N][G].
     """
     q = np.asarray(q, dtype=np.uint8)
     N, K = q.shape
-    G = np.asarray(z).shape[1]                  # groups per row (128 or 64 channels each)
+    G = np.asarray(z).shape[1]                  # groups per row (128, 64 or 32 channels each)
+    if w_bit == 8:
+        qweight = np.zeros((N, K // 4), dtype=np.uint32)
+        for j in range(4):
+            qweight |= q[:, j::4].astype(np.uint32) << np.uint32(8 * j)
+        return qweight, np.asarray(scale, dtype=np.float16).copy(), np.asarray(z, dtype=np.uint8).copy()
+    assert w_bit == 4
     qweight = np.zeros((N, K // 8), dtype=np.uint32)
     for j in range(8):
         qweight |= q[:, NIBBLE_CHANNEL[j]::8].astype(np.uint32) << np.uint32(4 * j)
@@ -227,10 +240,16 @@ def pack(q: np.ndarray, z: np.ndarray, scale: np.ndarray) -> tuple[np.ndarray, n
 
 
 def unpack(qweight: np.ndarray, scales: np.ndarray, zeros: np.ndarray, K: int):
-    """Inverse of :func:`pack`: returns (q uint8 [N][K], z uint8 [N][G], scale fp16 [N][G])."""
+    """Inverse of :func:`pack` (the code width follows from qweight's shape): returns
+    (q uint8 [N][K], z uint8 [N][G], scale fp16 [N][G])."""
     N = qweight.shape[0]
-    G = np.asarray(scales).shape[1]             # groups per row (128 or 64 channels each)
+    G = np.asarray(scales).shape[1]             # groups per row (128, 64 or 32 channels each)
     q = np.empty((N, K), dtype=np.uint8)
+    if qweight.shape[1] == K // 4:              # 8-bit
+        for j in range(4):
+            q[:, j::4] = ((qweight >> np.uint32(8 * j)) & np.uint32(0xFF)).astype(np.uint8)
+        return q, np.asarray(zeros, dtype=np.uint8)[:, :G].copy(), np.asarray(scales, dtype=np.float16)
+    assert qweight.shape[1] == K // 8
     for j in range(8):
         q[:, NIBBLE_CHANNEL[j]::8] = ((qweight >> np.uint32(4 * j)) & np.uint32(0xF)).astype(np.uint8)
     z = np.empty((N, G), dtype=np.uint8)
@@ -240,10 +259,10 @@ def unpack(qweight: np.ndarray, scales: np.ndarray, zeros: np.ndarray, K: int):
 
 
 def quantize_pack(W16: np.ndarray, s16: np.ndarray | None = None, clip_ratio: np.ndarray | None = None,
-                  zero_point: bool = True, group: int = GROUP):
+                  zero_point: bool = True, group: int = GROUP, w_bit: int = 4):
     """a3 + a4: returns (qweight, scales, zeros, flags)."""
-    r = quantize_groups(W16, s16, clip_ratio, zero_point, group)
-    qweight, scales, zeros = pack(r["q"], r["z"], r["scale"])
+    r = quantize_groups(W16, s16, clip_ratio, zero_point, group, w_bit)
+    qweight, scales, zeros = pack(r["q"], r["z"], r["scale"], w_bit)
     return qweight, scales, zeros, r["flags"]
 
 
@@ -264,7 +283,7 @@ def dequantize(q: np.ndarray, z: np.ndarray, scale: np.ndarray, s16: np.ndarray 
 
 # --------------------------------------------------------------------------- a5/a6
 def search_errors(X16: np.ndarray, W16: np.ndarray, n_grid: int = N_GRID, grid_points=None,
-                  zero_point: bool = True, group: int = GROUP) -> dict:
+                  zero_point: bool = True, group: int = GROUP, w_bit: int = 4) -> dict:
     """Output error of every candidate scale.
 
     [AWQ-PRACTICE] §2.2 and §3.3 step 4: grid search over a candidate interval so
@@ -286,7 +305,7 @@ def search_errors(X16: np.ndarray, W16: np.ndarray, n_grid: int = N_GRID, grid_p
     err = np.full(n_grid, np.nan, dtype=_F64)
     points = range(n_grid) if grid_points is None else grid_points
     for i in points:
-        r = quantize_groups(W16, s16[i], zero_point=zero_point, group=group)
+        r = quantize_groups(W16, s16[i], zero_point=zero_point, group=group, w_bit=w_bit)
         flags |= r["flags"]
         What = dequantize(r["q"], r["z"], r["scale"], s16[i])
         D = Wd - What
@@ -296,21 +315,21 @@ def search_errors(X16: np.ndarray, W16: np.ndarray, n_grid: int = N_GRID, grid_p
 
 
 def search_scales(X16: np.ndarray, W16: np.ndarray, n_grid: int = N_GRID, zero_point: bool = True,
-                  group: int = GROUP) -> dict:
+                  group: int = GROUP, w_bit: int = 4) -> dict:
     """a1..a6: the chosen grid index (first minimum), its scale and its packed weights.
 
     [AWQ-PRACTICE] §3.3 steps 4-5: pick the s with the smallest error, then
     quantize with it and keep the scale. Ties go to the smallest index (closest to
     plain RTN).
     """
-    r = search_errors(X16, W16, n_grid, zero_point=zero_point, group=group)
+    r = search_errors(X16, W16, n_grid, zero_point=zero_point, group=group, w_bit=w_bit)
     err = r["err"]
     best = 0
     for i in range(1, n_grid):
         if err[i] < err[best]:
             best = i
     s_best = r["s16"][best].copy()
-    qweight, scales, zeros, f = quantize_pack(W16, s_best, zero_point=zero_point, group=group)
+    qweight, scales, zeros, f = quantize_pack(W16, s_best, zero_point=zero_point, group=group, w_bit=w_bit)
     r.update(best_idx=best, s_best=s_best, qweight=qweight, scales=scales, zeros=zeros,
              gap=relative_gap(err), flags=r["flags"] | f)
     return r
@@ -329,7 +348,7 @@ def clip_ratios(clip_steps: int = CLIP_STEPS, n_shrink: int = CLIP_STEPS // 2) -
 
 def clip_errors(X16: np.ndarray, W16: np.ndarray, s16: np.ndarray | None = None,
                 clip_steps: int = CLIP_STEPS, n_shrink: int = CLIP_STEPS // 2,
-                zero_point: bool = True, group: int = GROUP) -> np.ndarray:
+                zero_point: bool = True, group: int = GROUP, w_bit: int = 4) -> np.ndarray:
     """Per-group output error of every shrink ratio, fp64 [n_shrink][N][G].
 
     Weight-clipping search ([NXMR] §5.1 "精度下降严重": tune clip_steps, 200 suggested,
@@ -346,7 +365,7 @@ def clip_errors(X16: np.ndarray, W16: np.ndarray, s16: np.ndarray | None = None,
     ratios = clip_ratios(clip_steps, n_shrink)
     err = np.empty((n_shrink, N, G), dtype=_F64)
     for i, r in enumerate(ratios):
-        qz = quantize_groups(W16, s16, np.full((N, G), r, dtype=_F32), zero_point, group)
+        qz = quantize_groups(W16, s16, np.full((N, G), r, dtype=_F32), zero_point, group, w_bit)
         D = Wd - dequantize(qz["q"], qz["z"], qz["scale"], s16)
         for g in range(G):
             E = Xd[:, g * group:(g + 1) * group] @ D[:, g * group:(g + 1) * group].T
@@ -356,11 +375,11 @@ def clip_errors(X16: np.ndarray, W16: np.ndarray, s16: np.ndarray | None = None,
 
 def clip_search(X16: np.ndarray, W16: np.ndarray, s16: np.ndarray | None = None,
                 clip_steps: int = CLIP_STEPS, n_shrink: int = CLIP_STEPS // 2,
-                zero_point: bool = True, group: int = GROUP) -> dict:
+                zero_point: bool = True, group: int = GROUP, w_bit: int = 4) -> dict:
     """Per group, the first ratio index with the smallest error, and the weight packed
     with those ratios. Returns dict(idx uint8 [N][G], ratio fp32 [N][G], err fp64
     [n_shrink][N][G], qweight, scales, zeros, flags)."""
-    err = clip_errors(X16, W16, s16, clip_steps, n_shrink, zero_point, group)
+    err = clip_errors(X16, W16, s16, clip_steps, n_shrink, zero_point, group, w_bit)
     idx = np.zeros(err.shape[1:], dtype=np.int64)
     best = err[0].copy()
     for i in range(1, n_shrink):
@@ -368,7 +387,7 @@ def clip_search(X16: np.ndarray, W16: np.ndarray, s16: np.ndarray | None = None,
         idx[better] = i
         best[better] = err[i][better]
     ratio = clip_ratios(clip_steps, n_shrink)[idx]
-    qweight, scales, zeros, flags = quantize_pack(W16, s16, ratio, zero_point, group)
+    qweight, scales, zeros, flags = quantize_pack(W16, s16, ratio, zero_point, group, w_bit)
     return {"idx": idx.astype(np.uint8), "ratio": ratio, "err": err, "qweight": qweight,
             "scales": scales, "zeros": zeros, "flags": flags}
 
@@ -489,7 +508,9 @@ def relative_gap(err: np.ndarray) -> float:
     return float((e[1] - e[0]) / e[0])
 
 
-def packed_bytes(N: int, K: int, group: int = GROUP) -> int:
-    """Bytes of the packed format for one [N][K] weight: codes + fp16 scales + zero nibbles."""
+def packed_bytes(N: int, K: int, group: int = GROUP, w_bit: int = 4) -> int:
+    """Bytes of the packed format for one [N][K] weight: codes + fp16 scales + zero points."""
     G = K // group
+    if w_bit == 8:
+        return N * K + N * G * 2 + N * G
     return N * (K // 2) + N * G * 2 + N * ((G + 1) // 2)

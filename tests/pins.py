@@ -39,13 +39,14 @@ def rne_fp16(v: Fraction) -> Fraction:
     return sign * lo * ulp
 
 
-def check_codes_nearest(w_scaled: np.ndarray, q: np.ndarray, z: np.ndarray, scale: np.ndarray) -> list:
+def check_codes_nearest(w_scaled: np.ndarray, q: np.ndarray, z: np.ndarray, scale: np.ndarray,
+                        qmax: int = 15) -> list:
     """P1: every unclamped code is the nearest one for the stored scale, in exact arithmetic.
 
     w_scaled: fp32 [N][K] values W*s (exact products); q uint8 [N][K]; z uint8 [N][G];
     scale fp16 [N][G]. A code may differ from the exact nearest only when the fp32
     quotient w'/sc lies within 2 fp32 ulps of a half-integer (then either neighbour
-    is accepted) or when the nearest code falls outside 0..15 (then the clamp).
+    is accepted) or when the nearest code falls outside 0..qmax (then the clamp).
     """
     bad = []
     N, K = q.shape
@@ -56,9 +57,9 @@ def check_codes_nearest(w_scaled: np.ndarray, q: np.ndarray, z: np.ndarray, scal
             sc = frac(scale[n, j])
             zz = int(z[n, j])
             wv = frac(w_scaled[n, k])
-            errs = [abs(wv - (c - zz) * sc) for c in range(16)]
+            errs = [abs(wv - (c - zz) * sc) for c in range(qmax + 1)]
             best = min(errs)
-            cands = {c for c in range(16) if errs[c] == best}
+            cands = {c for c in range(qmax + 1) if errs[c] == best}
             got = int(q[n, k])
             if got in cands:
                 continue
@@ -71,11 +72,12 @@ def check_codes_nearest(w_scaled: np.ndarray, q: np.ndarray, z: np.ndarray, scal
     return bad
 
 
-def check_scale_zero(w_scaled: np.ndarray, z: np.ndarray, scale: np.ndarray, ratio=None) -> list:
+def check_scale_zero(w_scaled: np.ndarray, z: np.ndarray, scale: np.ndarray, ratio=None,
+                     qmax: int = 15) -> list:
     """P2: closed form of the scale and the zero point from the group's extremes.
 
-    sc_h must be the fp16 rounding of (mx - mn)/15 up to the fp32 roundings on the
-    way (a relative 2^-22 window), floored at 2^-14; z in [0, 15]; when the zero is
+    sc_h must be the fp16 rounding of (mx - mn)/qmax up to the fp32 roundings on the
+    way (a relative 2^-22 window), floored at 2^-14; z in [0, qmax]; when the zero is
     not clamped, -z*sc_h lies within sc_h/2 of mn. With ``ratio`` ([N][G], weight
     clipping) the extremes are r mx and r mn.
     """
@@ -90,7 +92,7 @@ def check_scale_zero(w_scaled: np.ndarray, z: np.ndarray, scale: np.ndarray, rat
             if ratio is not None:
                 r = frac(ratio[n, j])
                 mx, mn = r * mx, r * mn
-            exact = max((mx - mn) / 15, Fraction(2) ** -14)
+            exact = max((mx - mn) / qmax, Fraction(2) ** -14)
             lo_ = rne_fp16(exact * (1 - Fraction(1, 2 ** 22)))
             hi_ = rne_fp16(exact * (1 + Fraction(1, 2 ** 22)))
             sc = frac(scale[n, j])
@@ -98,11 +100,11 @@ def check_scale_zero(w_scaled: np.ndarray, z: np.ndarray, scale: np.ndarray, rat
                 bad.append(("scale", n, j, float(sc), float(exact)))
                 continue
             zz = int(z[n, j])
-            if not (0 <= zz <= 15):
+            if not (0 <= zz <= qmax):
                 bad.append(("zero-range", n, j, zz))
                 continue
             ideal = -mn / sc
-            if 0 <= ideal <= 15 and abs(-zz * sc - mn) > sc / 2 + sc * Fraction(1, 2 ** 20):
+            if 0 <= ideal <= qmax and abs(-zz * sc - mn) > sc / 2 + sc * Fraction(1, 2 ** 20):
                 bad.append(("zero", n, j, zz, float(ideal)))
     return bad
 

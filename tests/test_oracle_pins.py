@@ -663,3 +663,86 @@ def test_group64_search_errors_exact():
     qz = oracle.quantize_groups(W, r["s16"][1], np.full((2, 2), oracle.clip_ratios(200, 3)[2], np.float32), group=64)
     ex = pins.exact_group_errors(X, W, r["s16"][1], qz["q"], qz["z"], qz["scale"])
     assert all(abs(e[2, n, g] - float(ex[n][g])) <= 1e-12 * float(ex[n][g]) for n in range(2) for g in range(2))
+
+
+# ----------------------------------------------------------------- 8-bit codes
+@pytest.mark.parametrize("group", [128, 32])
+def test_8bit_codes_nearest_scale_and_zero(group):
+    """8-bit codes: nearest of 0..255 for the stored scale (brute force), scale / zero from
+    the closed form with 255 levels; a 15-level scale is caught by the same check."""
+    W = si.weights(3, 256, offset=130)
+    s = np.exp(np.random.default_rng(14).uniform(-1, 1, 256)).astype(np.float16)
+    w = W.astype(np.float32) * s.astype(np.float32)
+    r = oracle.quantize_groups(W, s, group=group, w_bit=8)
+    assert not pins.check_codes_nearest(w, r["q"], r["z"], r["scale"], qmax=255)
+    assert not pins.check_scale_zero(w, r["z"], r["scale"], qmax=255)
+    r4 = oracle.quantize_groups(W, s, group=group, w_bit=4)
+    assert pins.check_scale_zero(w, r4["z"], r4["scale"], qmax=255)
+    assert r["q"].max() > 15                      # the codes use the wider range
+
+
+def test_8bit_symmetric_codes():
+    """Symmetric 8-bit: sc = max|w'| / 127, zero 128, q - 128 in -128..127, codes nearest."""
+    W = si.weights(2, 256, offset=131)
+    r = oracle.quantize_groups(W, zero_point=False, w_bit=8)
+    w = W.astype(np.float32)
+    assert np.all(r["z"] == 128)
+    assert not pins.check_codes_nearest(w, r["q"], r["z"], r["scale"], qmax=255)
+    for n in range(2):
+        for j in range(2):
+            amax = np.abs(w[n, j * 128:(j + 1) * 128]).max()
+            assert r["scale"][n, j] == np.float16(np.float32(amax) / np.float32(127))
+    # the largest magnitude maps to code 128 +- 127
+    n, k = np.unravel_index(np.argmax(np.abs(w[:, :128])), (2, 128))
+    assert abs(int(r["q"][n, k]) - 128) == 127
+
+
+def test_8bit_pack_layout_by_hand():
+    """Byte j of word w holds channel 4w + j; one zero byte per group; the byte count."""
+    q = np.zeros((1, 128), dtype=np.uint8)
+    q[0, :8] = [1, 2, 3, 4, 0xA0, 0xB0, 0xC0, 0xD0]
+    z = np.array([[0x7F]], dtype=np.uint8)
+    sc = np.array([[1.0]], dtype=np.float16)
+    qw, scp, zp = oracle.pack(q, z, sc, w_bit=8)
+    assert qw.shape == (1, 32) and zp.shape == (1, 1)
+    assert qw[0, 0] == 0x04030201 and qw[0, 1] == 0xD0C0B0A0
+    assert zp[0, 0] == 0x7F
+    q2, z2, s2 = oracle.unpack(qw, scp, zp, 128)
+    assert np.array_equal(q2, q) and np.array_equal(z2, z)
+    W = si.weights(5, 384, offset=132)
+    r = oracle.quantize_groups(W, group=64, w_bit=8)
+    qw, scp, zp = oracle.pack(r["q"], r["z"], r["scale"], w_bit=8)
+    q2, z2, _ = oracle.unpack(qw, scp, zp, 384)
+    assert np.array_equal(q2, r["q"]) and np.array_equal(z2, r["z"])
+    assert oracle.packed_bytes(4096, 4096, 128, w_bit=8) == 4096 * 4096 + 4096 * 32 * 2 + 4096 * 32
+
+
+def test_8bit_search_and_clip_errors_exact():
+    X = si.activations(2, 128, offset=133)
+    W = si.weights(2, 128, offset=133)
+    r = oracle.search_errors(X, W, n_grid=3, w_bit=8)
+    for i in range(3):
+        qz = oracle.quantize_groups(W, r["s16"][i], w_bit=8)
+        exact = pins.exact_search_error(X, W, r["s16"][i], qz["q"], qz["z"], qz["scale"])
+        assert abs(r["err"][i] - float(exact)) <= 1e-12 * float(exact)
+    e = oracle.clip_errors(X, W, r["s16"][1], 200, 3, w_bit=8)
+    qz = oracle.quantize_groups(W, r["s16"][1], np.full((2, 1), oracle.clip_ratios(200, 3)[2], np.float32), w_bit=8)
+    ex = pins.exact_group_errors(X, W, r["s16"][1], qz["q"], qz["z"], qz["scale"])
+    assert all(abs(e[2, n, 0] - float(ex[n][0])) <= 1e-12 * float(ex[n][0]) for n in range(2))
+    # 8-bit codes quantize more finely: the RTN error falls well below the 4-bit one
+    r4 = oracle.search_errors(X, W, n_grid=1)
+    assert r["err"][0] < r4["err"][0] / 50
+
+
+def test_8bit_linear_reference_one_hot():
+    """x = e_k reads (q - z) sc of channel k straight from the 8-bit packed words."""
+    W = si.weights(3, 256, offset=134)
+    qw, sc, zp, _ = oracle.quantize_pack(W, group=64, w_bit=8)
+    for k in (0, 5, 63, 64, 255):
+        X = np.zeros((1, 256), dtype=np.float16)
+        X[0, k] = 1.0
+        y, _ = oracle.linear_reference(X, qw, sc, zp, 256)
+        for n in range(3):
+            code = (int(qw[n, k // 4]) >> (8 * (k % 4))) & 0xFF
+            want = (code - int(zp[n, k // 64])) * float(sc[n, k // 64])
+            assert y[0, n] == want
