@@ -210,14 +210,17 @@ awq_status awq_linear_w4a16_gated_silu_ex(const void* X, int64_t M, const uint32
  *   tries r_i = (clip_steps - i) / clip_steps, i = 0 .. n_shrink - 1 (r_0 = 1: plain
  *   min/max), quantized from the extremes r_i max and r_i min (fp32), scored by
  *     err_i(n, g) = sum_t ( sum_{k in g} X_tk D_nk )^2,  D = W - Q_{r_i}(W diag(s)) diag(1/s),
- *   and keeps the first minimum. Contraction and its accuracy as in awq_search_scales.
+ *   and keeps the first minimum. Contraction as in awq_search_scales (D as fp16 hi + lo
+ *   against fp16 X on the matrix cores, fp32 accumulation, fp64 reduction).
  *   X fp16 [T][K], 1 <= T <= 512 (else AWQ_ERR_BAD_SHAPE: one block scores all tokens);
  *   W fp16 [N][K]; s fp16 [K] or NULL; 1 <= n_shrink <= min(clip_steps, 256).
  *   clip_idx uint8 [N][G] out (pass to awq_quantize_pack_clipped); err fp64 [N][G]
  *   out, the chosen error, or NULL; G = K / group_size. workspace: device,
- *   awq_clip_search_workspace_size bytes (n_shrink N G doubles, N + 1 floats and a copy of
- *   X in MFMA operand order, T rounded up to 64 tokens; 0 for an unsupported config or
- *   shape, T included), 16-byte aligned.
+ *   awq_clip_search_workspace_size bytes (n_shrink N G doubles and a copy of X in MFMA
+ *   operand order, T rounded up to 64 tokens; 0 for an unsupported config or shape, T
+ *   included), 16-byte aligned. Accuracy: each group's D is scaled by a power of two
+ *   from its own largest |D| before the fp16 hi + lo split, so every group keeps 22
+ *   significant bits whatever its magnitude or the code width.
  *   flags: NONFINITE_INPUT (a NaN or Inf in W or s, or in X through a non-finite error).
  */
 size_t awq_clip_search_workspace_size(int64_t T, int64_t N, int64_t K, int32_t n_shrink,

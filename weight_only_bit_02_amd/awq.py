@@ -40,33 +40,36 @@ def _need(t, dtype, name):
 @dataclass
 class PackedLinear:
     """Packed 4-bit weight of one [N][K] linear: codes, fp16 group scales, zero nibbles."""
-    qweight: torch.Tensor  # int32 [N][K/8] (the bits of uint32 words)
+    qweight: torch.Tensor  # int32 [N][K/8] (4-bit) or [N][K/4] (8-bit): the bits of uint32 words
     scales: torch.Tensor   # fp16 [N][G], G = K / group
-    zeros: torch.Tensor    # uint8 [N][ceil(G/2)]
+    zeros: torch.Tensor    # uint8 [N][ceil(G/2)] (4-bit: two per byte) or [N][G] (8-bit)
     N: int
     K: int
     group: int = GROUP
+    w_bit: int = 4
 
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size() for t in (self.qweight, self.scales, self.zeros))
 
 
-def alloc_packed(N: int, K: int, device, group: int = GROUP) -> PackedLinear:
+def alloc_packed(N: int, K: int, device, group: int = GROUP, w_bit: int = 4) -> PackedLinear:
     G = K // group
+    per_word = 32 // w_bit
+    zcols = G if w_bit == 8 else (G + 1) // 2
     return PackedLinear(
-        torch.empty((N, K // 8), dtype=torch.int32, device=device),
+        torch.empty((N, K // per_word), dtype=torch.int32, device=device),
         torch.empty((N, G), dtype=torch.float16, device=device),
-        torch.empty((N, (G + 1) // 2), dtype=torch.uint8, device=device), N, K, group)
+        torch.empty((N, zcols), dtype=torch.uint8, device=device), N, K, group, w_bit)
 
 
 def quantize_pack(W: torch.Tensor, s: torch.Tensor | None = None, flags: torch.Tensor | None = None,
                   out: PackedLinear | None = None, clip_idx: torch.Tensor | None = None,
                   clip_steps: int = 200, zero_point: bool = True,
-                  group_size: int = GROUP) -> PackedLinear:
+                  group_size: int = GROUP, w_bit: int = 4) -> PackedLinear:
     """awq_quantize_pack: 4-bit group-wise quantization of W * diag(s) (s = None: plain
     RTN; groups of group_size = 128 or 64 channels); with clip_idx (uint8 [N][K/group],
     clip_search's output), awq_quantize_pack_clipped; zero_point=False: symmetric codes
-    (same packed format, every zero 8)."""
+    (same packed format, every zero 8); w_bit=8: 8-bit codes."""
     lib = _abi.load()
     _need(W, torch.float16, "W")
     if W.dim() != 2:
@@ -78,13 +81,13 @@ def quantize_pack(W: torch.Tensor, s: torch.Tensor | None = None, flags: torch.T
             raise ValueError("s must be [K]")
     if flags is not None:
         _need(flags, torch.int32, "flags")
-    p = out if out is not None else alloc_packed(N, K, W.device, group_size)
+    p = out if out is not None else alloc_packed(N, K, W.device, group_size, w_bit)
     for name, t, dt in (("qweight", p.qweight, torch.int32), ("scales", p.scales, torch.float16),
                         ("zeros", p.zeros, torch.uint8)):
         _need(t, dt, name)
-    if p.N != N or p.K != K or p.group != group_size:
-        raise ValueError("output packed buffers have the wrong shape or group size")
-    cfg = _abi.config(zero_point=int(zero_point), group_size=group_size)
+    if p.N != N or p.K != K or p.group != group_size or p.w_bit != w_bit:
+        raise ValueError("output packed buffers have the wrong shape, group size or width")
+    cfg = _abi.config(zero_point=int(zero_point), group_size=group_size, w_bit=w_bit)
     if clip_idx is not None:
         _need(clip_idx, torch.uint8, "clip_idx")
         if clip_idx.shape != (N, K // group_size):
@@ -98,7 +101,7 @@ def quantize_pack(W: torch.Tensor, s: torch.Tensor | None = None, flags: torch.T
 def clip_search(X: torch.Tensor, W: torch.Tensor, s: torch.Tensor | None = None,
                 clip_steps: int = 200, n_shrink: int = 100, flags: torch.Tensor | None = None,
                 workspace: torch.Tensor | None = None, zero_point: bool = True,
-                group_size: int = GROUP):
+                group_size: int = GROUP, w_bit: int = 4):
     """awq_clip_search: per group, the index of the best shrink ratio (uint8 [N][K/group])
     and its error (fp64 [N][K/group]); ratio r_i = (clip_steps - i) / clip_steps, i < n_shrink."""
     lib = _abi.load()
@@ -110,7 +113,7 @@ def clip_search(X: torch.Tensor, W: torch.Tensor, s: torch.Tensor | None = None,
         raise ValueError("X and W disagree on K")
     if s is not None:
         _need(s, torch.float16, "s")
-    cfg = _abi.config(zero_point=int(zero_point), group_size=group_size)
+    cfg = _abi.config(zero_point=int(zero_point), group_size=group_size, w_bit=w_bit)
     nbytes = int(lib.awq_clip_search_workspace_size(T, N, K, n_shrink, C.byref(cfg)))
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=X.device)
@@ -173,7 +176,7 @@ class SearchWorkspace:
 def search_scales(X: torch.Tensor, W: torch.Tensor, n_grid: int = 20,
                   workspace: SearchWorkspace | None = None, flags: torch.Tensor | None = None,
                   out: SearchResult | None = None, zero_point: bool = True,
-                  group_size: int = GROUP) -> SearchResult:
+                  group_size: int = GROUP, w_bit: int = 4) -> SearchResult:
     """awq_search_scales: grid search of s = mean|x|^alpha minimizing the output error."""
     lib = _abi.load()
     _need(X, torch.float16, "X")
@@ -191,7 +194,7 @@ def search_scales(X: torch.Tensor, W: torch.Tensor, n_grid: int = 20,
     ws = workspace if workspace is not None else SearchWorkspace(T, N, K, dev, n_grid)
     if flags is not None:
         _need(flags, torch.int32, "flags")
-    cfg = _abi.config(n_grid, zero_point=int(zero_point), group_size=group_size)
+    cfg = _abi.config(n_grid, zero_point=int(zero_point), group_size=group_size, w_bit=w_bit)
     _abi.check("awq_search_scales", lib.awq_search_scales(
         _ptr(X), T, _ptr(W), N, K, C.byref(cfg), _ptr(out.s_best), _ptr(out.best_idx),
         _ptr(out.err), _ptr(out.s_grid), _ptr(ws.buf), ws.nbytes, _ptr(flags), _stream()))
@@ -214,7 +217,7 @@ def linear_w4a16(X: torch.Tensor, w: PackedLinear, kernel: str = "auto",
     _need(Y, torch.float16, "Y")
     if Y.shape != (M, w.N):
         raise ValueError("Y has the wrong shape")
-    cfg = _abi.config(group_size=w.group)
+    cfg = _abi.config(group_size=w.group, w_bit=w.w_bit)
     _abi.check("awq_linear_w4a16_ex", lib.awq_linear_w4a16_ex(
         _ptr(X), M, _ptr(w.qweight), _ptr(w.scales), _ptr(w.zeros), w.N, K, C.byref(cfg),
         _ptr(Y), None, _KERNELS[kernel], _stream()))
@@ -236,7 +239,7 @@ def linear_w4a16_gated_silu(X: torch.Tensor, w: PackedLinear, kernel: str = "aut
     _need(Y, torch.float16, "Y")
     if Y.shape != (M, w.N // 2):
         raise ValueError("Y has the wrong shape")
-    cfg = _abi.config(group_size=w.group)
+    cfg = _abi.config(group_size=w.group, w_bit=w.w_bit)
     _abi.check("awq_linear_w4a16_gated_silu_ex", lib.awq_linear_w4a16_gated_silu_ex(
         _ptr(X), M, _ptr(w.qweight), _ptr(w.scales), _ptr(w.zeros), w.N, K, C.byref(cfg),
         _ptr(Y), None, _KERNELS[kernel], _stream()))

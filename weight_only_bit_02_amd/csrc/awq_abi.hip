@@ -15,7 +15,8 @@ awq_config resolve(const awq_config* cfg) {
 }
 
 bool supported(const awq_config& c) {
-  return c.w_bit == 4 && (c.group_size == 128 || c.group_size == 64 || c.group_size == 32) &&
+  return (c.w_bit == 4 || c.w_bit == 8) &&
+         (c.group_size == 128 || c.group_size == 64 || c.group_size == 32) &&
          (c.zero_point == 0 || c.zero_point == 1) && c.n_grid >= 1 && c.n_grid <= 64;
 }
 
@@ -54,17 +55,15 @@ SearchLayout search_layout(int64_t T, int64_t N, int64_t K, int n_grid) {
   return L;
 }
 
-// Clip-search workspace: [rowmax: f32 N][srange: f32 1][err: fp64 n_shrink x N x G]
+// Clip-search workspace: [err: fp64 n_shrink x N x G]
 // [xp: X in MFMA operand order, T rounded up to 64 tokens]
 struct ClipLayout {
-  size_t rowmax, srange, err, xp, total;
+  size_t err, xp, total;
 };
 
 ClipLayout clip_layout(int64_t T, int64_t N, int64_t K, int n_shrink, int group) {
   ClipLayout L;
-  L.rowmax = 0;
-  L.srange = align256((size_t)N * 4);
-  L.err = align256(L.srange + 4);
+  L.err = 0;
   L.xp = align256(L.err + (size_t)n_shrink * N * (K / group) * 8);
   L.total = align256(L.xp + awq::packed_x_bytes(T, K));
   return L;
@@ -91,7 +90,7 @@ const char* awq_status_string(awq_status s) {
     case AWQ_OK: return "ok";
     case AWQ_ERR_NULL_POINTER: return "a required pointer is NULL";
     case AWQ_ERR_BAD_SHAPE: return "bad shape (sizes must be >= 1, K a multiple of 128, T <= 8192)";
-    case AWQ_ERR_UNSUPPORTED: return "unsupported config (w_bit 4, group_size 128, 64 or 32, zero_point 0 or 1, 1 <= n_grid <= 64)";
+    case AWQ_ERR_UNSUPPORTED: return "unsupported config (w_bit 4 or 8, group_size 128, 64 or 32, zero_point 0 or 1, 1 <= n_grid <= 64)";
     case AWQ_ERR_MISALIGNED: return "a base pointer is not 16-byte aligned";
     case AWQ_ERR_WORKSPACE: return "workspace missing or too small";
     case AWQ_ERR_HIP: return "HIP launch error";
@@ -122,7 +121,7 @@ awq_status awq_quantize_pack_clipped(const void* W, int64_t N, int64_t K, const 
     return AWQ_ERR_MISALIGNED;
   return hip_status(awq::launch_quant_pack((const uint16_t*)W, N, K, (const uint16_t*)s, qweight,
                                            (uint16_t*)scales, zeros, clip_idx, clip_steps,
-                                           c.zero_point == 0, c.group_size, flags,
+                                           c.zero_point == 0, c.group_size, c.w_bit, flags,
                                            (hipStream_t)stream));
 }
 
@@ -193,7 +192,7 @@ awq_status awq_search_scales(const void* X, int64_t T, const void* W, int64_t N,
   if (e == hipSuccess) e = awq::launch_scalegen(act, K, c.n_grid, sg, st);
   if (e == hipSuccess)
     e = awq::launch_search_err(Xh, T, (const uint16_t*)W, N, K, sg, c.n_grid, c.zero_point == 0,
-                               c.group_size, (float*)(ws + L.rowmax), (float*)(ws + L.srange),
+                               c.group_size, c.w_bit, (float*)(ws + L.rowmax), (float*)(ws + L.srange),
                                (uint4*)(ws + L.xp), partials, flags, st);
   if (e == hipSuccess)
     e = awq::launch_search_reduce(partials, c.n_grid, L.n_partials, sg, K, (uint16_t*)s_best,
@@ -207,7 +206,7 @@ static awq_status linear_common(const void* X, int64_t M, const uint32_t* qweigh
                                 bool gated, void* stream) {
   const awq_config c = resolve(cfg);
   if (!X || !qweight || !scales || !zeros || !Y) return AWQ_ERR_NULL_POINTER;
-  if (!supported(c)) return AWQ_ERR_UNSUPPORTED;
+  if (!supported(c) || c.w_bit != 4) return AWQ_ERR_UNSUPPORTED;
   if (M < 1 || M >= kMaxDim || !good_nk(N, K)) return AWQ_ERR_BAD_SHAPE;
   if (gated && (N < 2 || N % 2 != 0)) return AWQ_ERR_BAD_SHAPE;
   if (kernel != AWQ_LINEAR_AUTO && kernel != AWQ_LINEAR_GEMV && kernel != AWQ_LINEAR_GEMM &&
@@ -303,8 +302,7 @@ awq_status awq_clip_search(const void* X, int64_t T, const void* W, int64_t N, i
   double* errs = (double*)(ws + L.err);
   hipError_t e = awq::launch_clip_err((const uint16_t*)X, T, (const uint16_t*)W, N, K,
                                       (const uint16_t*)s, clip_steps, n_shrink, c.zero_point == 0,
-                                      c.group_size, (float*)(ws + L.rowmax), (float*)(ws + L.srange),
-                                      (uint4*)(ws + L.xp), errs, flags, st);
+                                      c.group_size, c.w_bit, (uint4*)(ws + L.xp), errs, flags, st);
   if (e == hipSuccess)
     e = awq::launch_clip_reduce(errs, n_shrink, N, K / c.group_size, clip_idx, err, flags, st);
   return hip_status(e);

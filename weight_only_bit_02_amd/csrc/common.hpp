@@ -13,7 +13,7 @@
 namespace awq {
 
 constexpr int kGroup = 128;   // input channels per quantization group
-constexpr int kQMax = 15;     // 4-bit unsigned codes 0..15 with a zero point
+constexpr int kQMax = 15;     // 4-bit unsigned codes 0..15 with a zero point (8-bit: 0..255)
 constexpr int kWave = 64;
 
 // Packed word layout: word w covers input channels 8w..8w+7; channel i sits in nibble
@@ -122,6 +122,7 @@ __device__ __forceinline__ double wave_sum(double v) {
 //   sc = max((mx - mn) / 15, 2^-14), clamped at 65504; sc_h = fp16(sc);
 //   z = clamp(rint(-mn / sc_h), 0, 15);  q = clamp(rint(w' / sc_h) + z, 0, 15).
 struct GroupQ {
+  float qmax;    // largest code: 15 (4-bit) or 255 (8-bit)
   float scf;     // the stored scale as fp32
   float rcp;     // hardware reciprocal of scf (within 1 ulp), only to guess quotients
   float z;       // zero point, 0..15
@@ -159,10 +160,12 @@ __device__ __forceinline__ void rint_quotients(const float (&w)[NV], float scf, 
   for (int i = 0; i < NV; ++i) q[i] = __builtin_rintf(q[i]);
 }
 
-__device__ __forceinline__ GroupQ group_params(float mn, float mx) {
+// Asymmetric group parameters for codes 0..qmax (qmax = 2^w_bit - 1).
+__device__ __forceinline__ GroupQ group_params(float mn, float mx, float qmax) {
 #pragma clang fp contract(off)
   GroupQ g;
-  float sc = (mx - mn) / 15.0f;  // correctly rounded division (no fast-math)
+  g.qmax = qmax;
+  float sc = (mx - mn) / qmax;  // correctly rounded division (no fast-math)
   sc = fmaxf(sc, 0x1p-14f);
   g.clamped = sc > 65504.0f;
   sc = fminf(sc, 65504.0f);
@@ -172,28 +175,31 @@ __device__ __forceinline__ GroupQ group_params(float mn, float mx) {
   const float nmn[1] = {-mn};
   float zq[1];
   rint_quotients(nmn, g.scf, g.rcp, zq);
-  g.z = fminf(fmaxf(zq[0], 0.0f), 15.0f);
+  g.z = fminf(fmaxf(zq[0], 0.0f), qmax);
   return g;
 }
 
-// Symmetric variant (zero point off): sc = max(|mx|, |mn|) / 7 with the same floor and
-// clamp, and the fixed zero 8, so q - 8 = clamp(rint(w / sc_h), -8, 7) is the signed code
-// and the stored format (and its dequantization (q - z) sc) is unchanged.
-__device__ __forceinline__ GroupQ group_params_sym(float mn, float mx) {
+// Symmetric variant (zero point off): sc = max(|mx|, |mn|) / (h - 1) with the same floor
+// and clamp, and the fixed zero h = 2^(w_bit - 1) (8 or 128), so q - h = clamp(rint(w /
+// sc_h), -h, h - 1) is the signed code and the stored format (and its dequantization
+// (q - z) sc) is unchanged.
+__device__ __forceinline__ GroupQ group_params_sym(float mn, float mx, float qmax) {
 #pragma clang fp contract(off)
   GroupQ g;
-  float sc = fmaxf(__builtin_fabsf(mx), __builtin_fabsf(mn)) / 7.0f;
+  g.qmax = qmax;
+  const float h = 0.5f * (qmax + 1.0f);  // exact
+  float sc = fmaxf(__builtin_fabsf(mx), __builtin_fabsf(mn)) / (h - 1.0f);
   sc = fmaxf(sc, 0x1p-14f);
   g.clamped = sc > 65504.0f;
   sc = fminf(sc, 65504.0f);
   g.sch = f2h_bits(sc);
   g.scf = h2f(g.sch);
-  g.z = 8.0f;
+  g.z = h;
   g.rcp = __builtin_amdgcn_rcpf(g.scf);
   return g;
 }
 
-// Codes q = clamp(rint(w / sc_h) + z, 0, 15) of NV values w of one group, each the
+// Codes q = clamp(rint(w / sc_h) + z, 0, qmax) of NV values w of one group, each the
 // exact fp32 product of two fp16 numbers (at most 22 significant bits).
 // q0 = rint(w * rcp) is taken when the residual e = w - q0 sc_h, formed by one fma, has
 // |e| < sc_h / 2. For |q0| < 2^12, q0 sc_h is exact (at most 23 bits) and so is e: when
@@ -201,7 +207,7 @@ __device__ __forceinline__ GroupQ group_params_sym(float mn, float mx) {
 // ulp(w) and ulp(sc_h), at least 2^-23 |e| when q0 != 0 (then |w| >= sc_h / 2), so e fits
 // 24 bits; q0 = 0 gives e = w. The test is therefore exact, and q0 is then the rint of
 // the real quotient. For larger
-// |q0| the guess is still within 1 of it and q0 + z lies far outside [0, 15], so the
+// |q0| the guess is still within 1 of it and q0 + z lies far outside [0, qmax], so the
 // clamp gives the same code either way. Everything else (|e| >= sc_h / 2: a wrong guess
 // or an exact tie; NaN; Inf) takes the correctly rounded division in a branch the wave
 // enters only when one of its lanes needs it.
@@ -224,7 +230,7 @@ __device__ __forceinline__ void quant_codes(const float (&w)[NV], const GroupQ& 
       if (close[i]) q[i] = __builtin_rintf(w[i] / g.scf);  // correctly rounded division
   }
 #pragma unroll
-  for (int i = 0; i < NV; ++i) q[i] = fminf(fmaxf(q[i] + g.z, 0.0f), 15.0f);
+  for (int i = 0; i < NV; ++i) q[i] = fminf(fmaxf(q[i] + g.z, 0.0f), g.qmax);
 }
 
 // The packed word of 8 codes of channels 8w .. 8w + 7 (channel i in nibble kNibbleOf[i]):
@@ -236,6 +242,16 @@ __device__ __forceinline__ uint32_t pack_codes8(const float (&q)[8]) {
   word = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(q[6], 16.0f, q[4]), 1, word);
   word = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(q[3], 16.0f, q[1]), 2, word);
   word = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(q[7], 16.0f, q[5]), 3, word);
+  return word;
+}
+
+// One word of four 8-bit codes, byte i = code i.
+__device__ __forceinline__ uint32_t pack_bytes4(float q0, float q1, float q2, float q3) {
+  uint32_t word = 0;
+  word = __builtin_amdgcn_cvt_pk_u8_f32(q0, 0, word);
+  word = __builtin_amdgcn_cvt_pk_u8_f32(q1, 1, word);
+  word = __builtin_amdgcn_cvt_pk_u8_f32(q2, 2, word);
+  word = __builtin_amdgcn_cvt_pk_u8_f32(q3, 3, word);
   return word;
 }
 

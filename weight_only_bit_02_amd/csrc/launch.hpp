@@ -15,14 +15,14 @@ namespace awq {
 hipError_t launch_quant_pack(const uint16_t* W, int64_t N, int64_t K, const uint16_t* s,
                              uint32_t* qweight, uint16_t* scales, uint8_t* zeros,
                              const uint8_t* clip_idx, int clip_steps, bool sym, int group,
-                             uint32_t* flags, hipStream_t stream);
+                             int w_bit, uint32_t* flags, hipStream_t stream);
 
 // f3: err[i][n][g] = sum_t (sum_{k in g} X_tk D_nk)^2 for the clip ratios i < n_shrink
 // (T <= 512), then the first minimum per (n, g).
 hipError_t launch_clip_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N,
                            int64_t K, const uint16_t* s, int clip_steps, int n_shrink, bool sym,
-                           int group, float* rowmax, float* srange, uint4* xp, double* err,
-                           uint32_t* flags, hipStream_t stream);
+                           int group, int w_bit, uint4* xp, double* err, uint32_t* flags,
+                           hipStream_t stream);
 // Bytes of the MFMA-ordered copy of X (T tokens rounded up to 64, K channels) that the
 // scale and clip searches read their activations from.
 size_t packed_x_bytes(int64_t T, int64_t K);
@@ -49,7 +49,7 @@ int search_token_chunk(int64_t T);
 // rowmax [N] and srange [n_grid] are scratch (per-row max |W|, per-grid-point max s / min s).
 hipError_t launch_search_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N,
                              int64_t K, const uint16_t* s_grid, int n_grid, bool sym, int group,
-                             float* rowmax, float* srange, uint4* xp, double* partials,
+                             int w_bit, float* rowmax, float* srange, uint4* xp, double* partials,
                              uint32_t* flags, hipStream_t stream);
 // a6: fixed-order sums of the partials, first-minimum argmin, s_best copy.
 hipError_t launch_search_reduce(const double* partials, int n_grid, int64_t n_partials,

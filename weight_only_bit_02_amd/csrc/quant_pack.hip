@@ -1,4 +1,5 @@
-// Quantize + pack (a3 + a4): one pass over W, HBM-bound.
+// Quantize + pack (a3 + a4): one pass over W, HBM-bound. 4-bit codes (the format measured)
+// or 8-bit ones (same quantizer with 255 levels, two natural-order words per lane).
 //
 // "AWQ量化实战" §2.3: 128 consecutive input channels share one quantization step;
 // "大模型量化部署实战：GPTQ与AWQ算法", "大模型量化的核心原理与位宽选择": a 4-bit integer with a
@@ -25,7 +26,7 @@ __global__ void __launch_bounds__(256) k_quant_pack(const uint16_t* __restrict__
                                                     uint8_t* __restrict__ zeros,
                                                     const uint8_t* __restrict__ clip_idx,
                                                     int clip_steps, int sym, int group,
-                                                    uint32_t* __restrict__ flags) {
+                                                    int w_bit, uint32_t* __restrict__ flags) {
   const int lane = threadIdx.x & 63;
   const int lgl = group == 128 ? 4 : group == 64 ? 3 : 2;
   const int gl = 1 << lgl;            // lanes per group (8 channels per lane)
@@ -34,7 +35,9 @@ __global__ void __launch_bounds__(256) k_quant_pack(const uint16_t* __restrict__
   const int li = lane & (gl - 1);     // lane within the group
   const int64_t G = K / group;
   const int64_t chunks = (G + gpu - 1) / gpu;
-  const int64_t zbytes = (G + 1) / 2;
+  const bool w8 = w_bit == 8;
+  const float qmax = w8 ? 255.0f : 15.0f;
+  const int64_t zbytes = w8 ? G : (G + 1) / 2;  // 8-bit: one zero byte per group
   // unit u = (row n, chunk ch) = n * chunks + ch; the wave walks u = wave0, wave0 + nwaves,
   // ... with (n, ch) stepped incrementally (wave-uniform, no division in the loop)
   const int64_t wave0 = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)));
@@ -80,18 +83,27 @@ __global__ void __launch_bounds__(256) k_quant_pack(const uint16_t* __restrict__
       mn = r * mn;
       mx = r * mx;
     }
-    const GroupQ g = sym ? group_params_sym(mn, mx) : group_params(mn, mx);
+    const GroupQ g = sym ? group_params_sym(mn, mx, qmax) : group_params(mn, mx, qmax);
     float qc[8];
     quant_codes(w, g, qc);
-    const uint32_t word = pack_codes8(qc);
 
     const uint32_t zi = (uint32_t)g.z;
     const uint32_t z_next = (uint32_t)__shfl_down((int)zi, gl);  // zero of group j + 1
     if (valid) {
-      qweight[(n * K + k0) >> 3] = word;
+      if (w8) {
+        // two words, byte i of word h = code of channel k0 + 4 h + i
+        uint2 wd8;
+        wd8.x = pack_bytes4(qc[0], qc[1], qc[2], qc[3]);
+        wd8.y = pack_bytes4(qc[4], qc[5], qc[6], qc[7]);
+        reinterpret_cast<uint2*>(qweight)[(n * K + k0) >> 3] = wd8;
+      } else {
+        qweight[(n * K + k0) >> 3] = pack_codes8(qc);
+      }
       if (li == 0) {
         scales[n * G + j] = g.sch;
-        if ((j & 1) == 0) {
+        if (w8) {
+          zeros[n * zbytes + j] = (uint8_t)zi;
+        } else if ((j & 1) == 0) {
           const uint32_t hi = (j + 1 < G) ? z_next : 0u;
           zeros[n * zbytes + (j >> 1)] = (uint8_t)(zi | (hi << 4));
         }
@@ -105,11 +117,11 @@ __global__ void __launch_bounds__(256) k_quant_pack(const uint16_t* __restrict__
 hipError_t launch_quant_pack(const uint16_t* W, int64_t N, int64_t K, const uint16_t* s,
                              uint32_t* qweight, uint16_t* scales, uint8_t* zeros,
                              const uint8_t* clip_idx, int clip_steps, bool sym, int group,
-                             uint32_t* flags, hipStream_t stream) {
+                             int w_bit, uint32_t* flags, hipStream_t stream) {
   const int64_t units = N * ((K / 512 + (K % 512 ? 1 : 0)));
   const int64_t blocks = units / 4 + 1 < 16384 ? units / 4 + 1 : 16384;
   hipLaunchKernelGGL(k_quant_pack, dim3((unsigned)blocks), dim3(256), 0, stream, W, N, K, s,
-                     qweight, scales, zeros, clip_idx, clip_steps, (int)sym, group, flags);
+                     qweight, scales, zeros, clip_idx, clip_steps, (int)sym, group, w_bit, flags);
   return hipGetLastError();
 }
 

@@ -145,9 +145,10 @@ __device__ __forceinline__ const uint4* packed_x(const uint4* xp, int64_t G, int
 template <int NW, bool CLIP, int NROWS>
 __device__ __forceinline__ bool quantize_tile_group(const uint16_t* W, int64_t N, int64_t K,
                                                     const uint16_t* s, float r, bool sym,
-                                                    int group, int64_t n0, int64_t j,
+                                                    int group, float qmax, int64_t n0, int64_t j,
                                                     const float* lds_p, uint16_t* hi_buf,
-                                                    uint16_t* lo_buf, int tid, int row_base) {
+                                                    uint16_t* lo_buf, int tid, int row_base,
+                                                    float* pg_out) {
   constexpr int kRowsPerPass = NW * 4;
   constexpr int kPasses = NROWS / kRowsPerPass;
   static_assert(kPasses * kRowsPerPass == NROWS, "whole passes");
@@ -197,10 +198,39 @@ __device__ __forceinline__ bool quantize_tile_group(const uint16_t* W, int64_t N
       mn = r * mn;
       mx = r * mx;
     }
-    const GroupQ g = sym ? group_params_sym(mn, mx) : group_params(mn, mx);
-    const float P = lds_p[row];
+    const GroupQ g = sym ? group_params_sym(mn, mx, qmax) : group_params(mn, mx, qmax);
     float qc[8];
     quant_codes(wp, g, qc);
+    // D = (w' - deq) / s: w' = w s and deq = (q - z) sc_h are exact, and so is their
+    // difference (both are multiples of the finer ulp and close in magnitude), so the
+    // reciprocal's error (1 ulp) is relative to D itself; w - deq / s would carry it
+    // relative to w, which is 30 (4-bit) to 500 (8-bit) times larger than D
+    float dg[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float deq = (qc[c] - g.z) * g.scf;  // exact: small integer times an fp16
+      dg[c] = (wp[c] - deq) * rs[c];
+    }
+    float P;
+    if constexpr (CLIP) {
+      // each group is scored on its own, so its scale comes from its own largest |D|:
+      // P = 2^(14 - e) with that maximum in [2^(e-1), 2^e), so |D P| < 2^14 and hi + lo
+      // keep 22 significant bits of every group, whatever the code width
+      float dmx = 0.0f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) dmx = fmaxf(dmx, __builtin_fabsf(dg[c]));
+      float dmn = dmx;
+      group_minmax(dmn, dmx, group);
+      int ex = 0;
+      (void)__builtin_frexpf(dmx, &ex);
+      if (!(dmx > 0.0f) || !__builtin_isfinite(dmx)) ex = 0;
+      ex = ex < -100 ? -100 : (ex > 100 ? 100 : ex);
+      P = __builtin_ldexpf(1.0f, 14 - ex);
+      const int gl = group >> 3;  // lanes per group
+      if ((li & (gl - 1)) == 0) pg_out[row * 4 + li / gl] = P;
+    } else {
+      P = lds_p[row];
+    }
     uint32_t hi[4], lo[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -208,8 +238,7 @@ __device__ __forceinline__ bool quantize_tile_group(const uint16_t* W, int64_t N
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int c = 2 * i + e;
-        const float deq = (qc[c] - g.z) * g.scf;  // exact: small integer times an fp16
-        const float d = (wf[c] - deq * rs[c]) * P;
+        const float d = dg[c] * P;
         h2[e] = f2h_bits(d);
         l2[e] = f2h_bits(d - h2f(h2[e]));
       }
@@ -225,7 +254,8 @@ __device__ __forceinline__ bool quantize_tile_group(const uint16_t* W, int64_t N
 template <int NW>
 __global__ void __launch_bounds__(NW * 64)
     k_search_err(const uint4* xp, int64_t T, const uint16_t* W, int64_t N, int64_t K,
-                 const uint16_t* s_grid, int n_grid, int sym, int group, const float* rowmax,
+                 const uint16_t* s_grid, int n_grid, int sym, int group, int w_bit,
+                 const float* rowmax,
                  const float* srange,
                  double* __restrict__ partials, uint32_t* __restrict__ flags, int64_t n_ntiles,
                  int64_t per_xcd) {
@@ -245,6 +275,7 @@ __global__ void __launch_bounds__(NW * 64)
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int64_t n0 = ntile * kRowTile;
+  const float qmax = w_bit == 8 ? 255.0f : 15.0f;
   const int64_t G = K / kGroup;
   const uint16_t* s = s_grid + (int64_t)alpha * K;
   const int64_t tchunk = (int64_t)NW * kTokPerWave;
@@ -269,9 +300,9 @@ __global__ void __launch_bounds__(NW * 64)
   const int tid_set = set_b ? tid - NH * 64 : tid;
   bool bad = false;
   auto quantize = [&](int64_t j, int buf) {
-    bad |= quantize_tile_group<NH, false, kRowTile / 2>(W, N, K, s, 1.0f, sym, group, n0, j, lds_p,
+    bad |= quantize_tile_group<NH, false, kRowTile / 2>(W, N, K, s, 1.0f, sym, group, qmax, n0, j, lds_p,
                                                        lds_hi[buf], lds_lo[buf], tid_set,
-                                                       set_b ? kRowTile / 2 : 0);
+                                                       set_b ? kRowTile / 2 : 0, nullptr);
   };
 
   for (int64_t tc = 0; tc < n_tchunks; ++tc) {
@@ -355,12 +386,13 @@ __global__ void __launch_bounds__(NW * 64)
 template <int NW>
 __global__ void __launch_bounds__(NW * 64)
     k_clip_err(const uint4* xp, int64_t T, const uint16_t* W, int64_t N, int64_t K,
-               const uint16_t* s, int clip_steps, int n_shrink, int sym, int group,
-               const float* rowmax, const float* srange, double* __restrict__ err,
-               uint32_t* __restrict__ flags, int64_t n_ntiles, int64_t per_xcd) {
+               const uint16_t* s, int clip_steps, int n_shrink, int sym, int group, int w_bit,
+               double* __restrict__ err, uint32_t* __restrict__ flags, int64_t n_ntiles,
+               int64_t per_xcd) {
   __shared__ __attribute__((aligned(16))) uint16_t lds_hi[2][kRowTile * kLdsStride];
   __shared__ __attribute__((aligned(16))) uint16_t lds_lo[2][kRowTile * kLdsStride];
-  __shared__ float lds_p[kRowTile];
+  // power-of-two scale of each (row, group of the step), double-buffered with hi / lo
+  __shared__ float lds_pg[2][kRowTile * 4];
   // per-row partial errors of each wave: slot = step parity (128-channel groups; one
   // barrier per step suffices) or the group's place in a pair (64- and 32-channel groups:
   // both slots are filled, then stored and freed between two barriers)
@@ -376,6 +408,7 @@ __global__ void __launch_bounds__(NW * 64)
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int64_t n0 = ntile * kRowTile;
+  const float qmax = w_bit == 8 ? 255.0f : 15.0f;
   const int gps = kGroup / group;  // groups per 128-channel step: 1, 2 or 4
   const int per = 8 / gps;         // k16 slices per group: 8, 4 or 2
   const int64_t G = K / kGroup;    // 128-channel steps
@@ -384,11 +417,6 @@ __global__ void __launch_bounds__(NW * 64)
   const int khalf = lane >> 5;
   const int64_t tw = (int64_t)wave * kTokPerWave;
   const bool active = tw < T;
-
-  const float sr = s ? srange[0] : 1.0f;
-  for (int i = tid; i < kRowTile; i += NW * 64)
-    lds_p[i] = row_scale(n0 + i < N ? rowmax[n0 + i] : 0.0f, sr);
-  __syncthreads();
 
   // two sets of waves in opposite phase, as in the scale search: set A multiplies then
   // quantizes its half of the next step's rows, set B the reverse. Every wave runs the
@@ -399,9 +427,9 @@ __global__ void __launch_bounds__(NW * 64)
   const int tid_set = set_b ? tid - NH * 64 : tid;
   bool bad = false;
   auto quantize = [&](int64_t jq, int qbuf) {
-    bad |= quantize_tile_group<NH, true, kRowTile / 2>(W, N, K, s, r, sym, group, n0, jq, lds_p,
-                                                      lds_hi[qbuf], lds_lo[qbuf], tid_set,
-                                                      set_b ? kRowTile / 2 : 0);
+    bad |= quantize_tile_group<NH, true, kRowTile / 2>(W, N, K, s, r, sym, group, qmax, n0, jq,
+                                                      nullptr, lds_hi[qbuf], lds_lo[qbuf], tid_set,
+                                                      set_b ? kRowTile / 2 : 0, lds_pg[qbuf]);
   };
   quantize(0, 0);
   __syncthreads();
@@ -455,7 +483,7 @@ __global__ void __launch_bounds__(NW * 64)
         const int slot = gps == 1 ? buf : nred;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          const double pinv = 1.0 / (double)lds_p[b * 32 + m32];
+          const double pinv = 1.0 / (double)lds_pg[buf][(b * 32 + m32) * 4 + (2 * c + 2) / per - 1];
           float s32 = 0.0f;
 #pragma unroll
           for (int a = 0; a < 2; ++a)
@@ -537,27 +565,19 @@ size_t packed_x_bytes(int64_t T, int64_t K) {
 
 hipError_t launch_clip_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N,
                            int64_t K, const uint16_t* s, int clip_steps, int n_shrink, bool sym,
-                           int group, float* rowmax, float* srange, uint4* xp, double* err,
-                           uint32_t* flags, hipStream_t stream) {
-  hipLaunchKernelGGL(k_row_absmax, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, stream, W, N, K, rowmax);
-  hipError_t e = hipGetLastError();
+                           int group, int w_bit, uint4* xp, double* err, uint32_t* flags,
+                           hipStream_t stream) {
+  hipError_t e = launch_pack_x(X, T, K, xp, stream);
   if (e != hipSuccess) return e;
-  e = launch_pack_x(X, T, K, xp, stream);
-  if (e != hipSuccess) return e;
-  if (s) {
-    hipLaunchKernelGGL(k_scale_range, dim3(1), dim3(256), 0, stream, s, K, srange, flags);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   const int64_t n_ntiles = (N + kRowTile - 1) / kRowTile;
   const int64_t per_xcd = (n_ntiles * n_shrink + kXcds - 1) / kXcds;
   const dim3 grid((unsigned)(per_xcd * kXcds));
   if (T <= 4 * kTokPerWave)
     hipLaunchKernelGGL(k_clip_err<4>, grid, dim3(256), 0, stream, xp, T, W, N, K, s, clip_steps,
-                       n_shrink, (int)sym, group, rowmax, srange, err, flags, n_ntiles, per_xcd);
+                       n_shrink, (int)sym, group, w_bit, err, flags, n_ntiles, per_xcd);
   else
     hipLaunchKernelGGL(k_clip_err<8>, grid, dim3(512), 0, stream, xp, T, W, N, K, s, clip_steps,
-                       n_shrink, (int)sym, group, rowmax, srange, err, flags, n_ntiles, per_xcd);
+                       n_shrink, (int)sym, group, w_bit, err, flags, n_ntiles, per_xcd);
   return hipGetLastError();
 }
 
@@ -607,7 +627,7 @@ int search_token_chunk(int64_t T) { return T <= 4 * kTokPerWave ? 4 * kTokPerWav
 
 hipError_t launch_search_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N,
                              int64_t K, const uint16_t* s_grid, int n_grid, bool sym, int group,
-                             float* rowmax, float* srange, uint4* xp, double* partials,
+                             int w_bit, float* rowmax, float* srange, uint4* xp, double* partials,
                              uint32_t* flags, hipStream_t stream) {
   hipLaunchKernelGGL(k_row_absmax, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, stream, W, N, K, rowmax);
   hipError_t e = hipGetLastError();
@@ -622,10 +642,10 @@ hipError_t launch_search_err(const uint16_t* X, int64_t T, const uint16_t* W, in
   const dim3 grid((unsigned)(per_xcd * kXcds));
   if (T <= 4 * kTokPerWave)
     hipLaunchKernelGGL(k_search_err<4>, grid, dim3(256), 0, stream, xp, T, W, N, K, s_grid, n_grid,
-                       (int)sym, group, rowmax, srange, partials, flags, n_ntiles, per_xcd);
+                       (int)sym, group, w_bit, rowmax, srange, partials, flags, n_ntiles, per_xcd);
   else
     hipLaunchKernelGGL(k_search_err<8>, grid, dim3(512), 0, stream, xp, T, W, N, K, s_grid, n_grid,
-                       (int)sym, group, rowmax, srange, partials, flags, n_ntiles, per_xcd);
+                       (int)sym, group, w_bit, rowmax, srange, partials, flags, n_ntiles, per_xcd);
   return hipGetLastError();
 }
 
