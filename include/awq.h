@@ -51,7 +51,8 @@ typedef enum awq_status {
 
 /* Quantization config ([SKILL] "如何使用该技能 / 步骤 2": quant_config zero_point, q_group_size,
  * w_bit; the page's "version" GEMM/GEMV switch becomes dispatch on M inside
- * awq_linear_w4a16). Supported: w_bit = 4, group_size = 128, 64 or 32 ([PRACTICE] §2.3:
+ * awq_linear_w4a16). Supported: w_bit = 4 or 8 ([PRACTICE] §5.1 raises w_bit when 4-bit
+ * accuracy falls short), group_size = 128, 64 or 32 ([PRACTICE] §2.3:
  * 128 is the usual group, 64 and 32 also in use), zero_point = 1 or 0, 1 <= n_grid <= 64.
  * NULL config pointers mean {4, 128, 1, 20}. Every entry point takes the group size from
  * the config; K stays a multiple of 128 in every case, so a smaller group never straddles
@@ -60,7 +61,10 @@ typedef enum awq_status {
  * zero_point = 0 ([PRACTICE] §3.3 advises it; [GPTQ-AWQ] gives the signed range -8..7):
  * sc = max|w'| / 7, q - 8 = clamp(rint(w'/sc_h), -8, 7), stored offset by 8 with every
  * zero nibble 8 -- the same packed format, so the linear entry points are unchanged;
- * quantize, search and clip search honour the mode. */
+ * quantize, search and clip search honour the mode (8-bit: /127 and zero 128).
+ * w_bit = 8: the same quantizer with 255 levels and its own packed layout (see
+ * awq_quantize_pack); every entry point, linear kernels included, takes it from the config.
+ * The linear entry points need the config the weight was packed with. */
 typedef struct awq_config {
   int32_t w_bit;
   int32_t group_size;
@@ -78,7 +82,8 @@ typedef struct awq_config {
 /* Which linear kernel awq_linear_w4a16_ex runs. */
 typedef enum awq_linear_kernel {
   AWQ_LINEAR_AUTO = 0, /* vector GEMV for M <= 3, skinny MFMA GEMV up to
-                          awq_gemv_max_m(), MFMA GEMM above                   */
+                          awq_gemv_max_m(), MFMA GEMM above (8-bit codes:
+                          vector GEMV up to 8, skinny up to 32)               */
   AWQ_LINEAR_GEMV = 1, /* wave-per-rows dequant-fused GEMV (any M <= 8)       */
   AWQ_LINEAR_GEMM = 2, /* MFMA dequant-GEMM (any M)                           */
   AWQ_LINEAR_SKINNY = 3 /* MFMA GEMV for small batches, split K (M <= 32)     */
@@ -101,6 +106,8 @@ typedef enum awq_linear_kernel {
  *   scales   fp16 [N][G]          out: sc_h, G = K/g
  *   zeros    uint8 [N][ceil(G/2)] out: low nibble = even group, high = odd group
  *   flags    uint32 [1] or NULL   NONFINITE_INPUT, SCALE_CLAMPED
+ *   w_bit = 8: 15 -> 255 above (codes 0..255); qweight uint32 [N][K/4], byte j of word w
+ *   holds k = 4w + j; zeros uint8 [N][G], one byte per group; scales as above.
  */
 awq_status awq_quantize_pack(const void* W, int64_t N, int64_t K, const void* s,
                              const awq_config* cfg, uint32_t* qweight, void* scales,

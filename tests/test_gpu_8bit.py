@@ -90,3 +90,69 @@ def test_clip_search_and_clipped_pack(T, N, K, n_shrink, group):
     ratio = oracle.clip_ratios(200, n_shrink)[ref_idx]
     ref, p = _pack_both(W, group, s, True, clip_ratio=ratio, clip_idx=ref_idx.astype(np.uint8))
     _assert_same_pack(ref, p)
+
+
+# ----------------------------------------------------------------- linear kernels
+@pytest.mark.parametrize("M,N,K,kernel,group", [
+    (1, 96, 384, "gemv", 128),
+    (1, 200, 4096, "gemv", 64),
+    (1, 77, 11008, "gemv", 32),
+    (3, 130, 4096, "gemv", 128),
+    (8, 67, 1152, "gemv", 64),
+    (1, 100, 4096, "skinny", 128),
+    (7, 130, 1152, "skinny", 64),
+    (16, 64, 4096, "skinny", 32),
+    (32, 96, 11008, "skinny", 128),
+    (40, 300, 1152, "gemm", 128),
+    (129, 256, 4096, "gemm", 64),
+    (70, 96, 1152, "gemm", 32),
+    (5, 1000, 384, "auto", 128),
+    (20, 300, 512, "auto", 128),
+    (50, 300, 512, "auto", 128),
+])
+def test_linear_kernels(M, N, K, kernel, group):
+    W = si.weights(N, K, offset=M + N + K + 8)
+    ref, p = _pack_both(W, group, _s(K, M + 1))
+    X = si.activations(M, K, offset=M + 6)
+    Y = host(awq.linear_w4a16(to_dev(X), p, kernel=kernel)).astype(np.float64)
+    y_ref, bound = oracle.linear_reference(X, *ref, K)
+    ok = oracle.linear_within_tolerance(Y, y_ref, bound)
+    assert ok.all(), (kernel, np.argwhere(~ok)[:4])
+
+
+@pytest.mark.parametrize("M,nh,K,kernel,group", [
+    (1, 96, 4096, "gemv", 128),
+    (4, 67, 1152, "gemv", 32),
+    (12, 80, 4096, "skinny", 64),
+    (70, 130, 1152, "gemm", 128),
+    (40, 64, 512, "gemm", 32),
+])
+def test_gated_kernels(M, nh, K, kernel, group):
+    W = si.weights(2 * nh, K, offset=M + nh + 8)
+    ref, p = _pack_both(W, group, _s(K, M + 2))
+    X = si.activations(M, K, offset=M + 10)
+    H = host(awq.linear_w4a16_gated_silu(to_dev(X), p, kernel=kernel))
+    h, g, u, bg, bu = oracle.gated_silu_reference(X, *ref, K)
+    assert oracle.gated_silu_within_tolerance(H, g, u, bg, bu).all(), kernel
+
+
+@pytest.mark.parametrize("group", [128, 64, 32])
+def test_dequant_identity_rows(group):
+    """x = e_k returns fp16((q - z) sc) of channel k bit-exactly through every kernel: pins the
+    byte order, the group index and the zero byte of every group of a 128-channel step."""
+    N, K = 40, 512
+    W = si.weights(N, K, offset=79)
+    ref, p = _pack_both(W, group, _s(K, 80), zero_point=group != 64)
+    q, z, sc = oracle.unpack(*ref, K)
+    ks = [0, 1, 2, 3, 4, 31, 32, 63, 64, 95, 96, 127, 128, 200, 511]
+    X = np.zeros((len(ks), K), dtype=np.float16)
+    for i, k in enumerate(ks):
+        X[i, k] = 1.0
+    want = np.stack([((q[:, k].astype(np.float64) - z[:, k // group]) * sc[:, k // group].astype(np.float64))
+                     for k in ks]).astype(np.float16)
+    for kernel in ("skinny", "gemm"):
+        Y = host(awq.linear_w4a16(to_dev(X), p, kernel=kernel))
+        assert np.array_equal(Y.view(np.uint16), want.view(np.uint16)), kernel
+    for i0 in range(0, len(ks), 8):
+        Y = host(awq.linear_w4a16(to_dev(X[i0:i0 + 8]), p, kernel="gemv"))
+        assert np.array_equal(Y.view(np.uint16), want[i0:i0 + 8].view(np.uint16))

@@ -206,7 +206,7 @@ static awq_status linear_common(const void* X, int64_t M, const uint32_t* qweigh
                                 bool gated, void* stream) {
   const awq_config c = resolve(cfg);
   if (!X || !qweight || !scales || !zeros || !Y) return AWQ_ERR_NULL_POINTER;
-  if (!supported(c) || c.w_bit != 4) return AWQ_ERR_UNSUPPORTED;
+  if (!supported(c)) return AWQ_ERR_UNSUPPORTED;
   if (M < 1 || M >= kMaxDim || !good_nk(N, K)) return AWQ_ERR_BAD_SHAPE;
   if (gated && (N < 2 || N % 2 != 0)) return AWQ_ERR_BAD_SHAPE;
   if (kernel != AWQ_LINEAR_AUTO && kernel != AWQ_LINEAR_GEMV && kernel != AWQ_LINEAR_GEMM &&
@@ -219,6 +219,9 @@ static awq_status linear_common(const void* X, int64_t M, const uint32_t* qweigh
     return AWQ_ERR_MISALIGNED;
   // AUTO, measured on the Llama-2-7B layer: the vector-ALU GEMV up to M = 3 (its dot cost
   // grows with M), the MFMA skinny GEMV up to g_gemv_max_m, the MFMA GEMM above.
+  if (kernel == AWQ_LINEAR_AUTO && c.w_bit == 8)
+    kernel = M <= awq::kGemvMaxM ? AWQ_LINEAR_GEMV
+             : M <= awq::kSkinnyMaxM ? AWQ_LINEAR_SKINNY : AWQ_LINEAR_GEMM;
   if (kernel == AWQ_LINEAR_AUTO)
     kernel = M <= awq::kVgemvAutoMaxM && M <= g_gemv_max_m ? AWQ_LINEAR_GEMV
              : M <= g_gemv_max_m                            ? AWQ_LINEAR_SKINNY
@@ -227,6 +230,17 @@ static awq_status linear_common(const void* X, int64_t M, const uint32_t* qweigh
   const auto* Xh = (const uint16_t*)X;
   const auto* sc = (const uint16_t*)scales;
   auto* Yh = (uint16_t*)Y;
+  if (c.w_bit == 8) {
+    // 8-bit codes: the vector GEMV (M <= 8), the skinny MFMA GEMV (M <= 32), the GEMM
+    if (kernel == AWQ_LINEAR_GEMV)
+      return hip_status(
+          awq::launch_gemv8(Xh, M, qweight, sc, zeros, N, K, c.group_size, Yh, gated, st));
+    if (kernel == AWQ_LINEAR_SKINNY)
+      return hip_status(
+          awq::launch_gemv_mfma8(Xh, M, qweight, sc, zeros, N, K, c.group_size, Yh, gated, st));
+    return hip_status(
+        awq::launch_gemm(Xh, M, qweight, sc, zeros, N, K, c.group_size, 8, Yh, gated, st));
+  }
   switch (kernel) {
     case AWQ_LINEAR_GEMV:
       return hip_status(
@@ -236,7 +250,7 @@ static awq_status linear_common(const void* X, int64_t M, const uint32_t* qweigh
           awq::launch_gemv_mfma(Xh, M, qweight, sc, zeros, N, K, c.group_size, Yh, gated, st));
     default:
       return hip_status(
-          awq::launch_gemm(Xh, M, qweight, sc, zeros, N, K, c.group_size, Yh, gated, st));
+          awq::launch_gemm(Xh, M, qweight, sc, zeros, N, K, c.group_size, 4, Yh, gated, st));
   }
 }
 

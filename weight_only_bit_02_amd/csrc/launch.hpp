@@ -60,12 +60,21 @@ hipError_t launch_search_reduce(const double* partials, int n_grid, int64_t n_pa
 // a7 / a8: Y = X deq(W)^T. gated (f1): W is gate|up stacked (N/2 rows each) and
 // Y[M][N/2] = SiLU(X deq(W_gate)^T) * (X deq(W_up)^T); N is even.
 // group: 128 or 64 (the layout of scales / zeros).
+// 8-bit codes (qweight uint32 [N][K/4], byte j of word w = channel 4w + j; zeros uint8
+// [N][G]): the vector GEMV for M <= 8, plain or gated.
+hipError_t launch_gemv8(const uint16_t* X, int64_t M, const uint32_t* qweight,
+                        const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
+                        int group, uint16_t* Y, bool gated, hipStream_t stream);
+// 8-bit codes: the skinny MFMA GEMV (M <= kSkinnyMaxM), plain or gated.
+hipError_t launch_gemv_mfma8(const uint16_t* X, int64_t M, const uint32_t* qweight,
+                             const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
+                             int group, uint16_t* Y, bool gated, hipStream_t stream);
 hipError_t launch_gemv(const uint16_t* X, int64_t M, const uint32_t* qweight,
                        const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
                        int group, uint16_t* Y, bool gated, hipStream_t stream);
 hipError_t launch_gemm(const uint16_t* X, int64_t M, const uint32_t* qweight,
                        const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
-                       int group, uint16_t* Y, bool gated, hipStream_t stream);
+                       int group, int w_bit, uint16_t* Y, bool gated, hipStream_t stream);
 
 // f2: out = fp16(A / s) along columns (axis 1, len(s) = cols) or rows (axis 0,
 // len(s) = rows); cols % 8 == 0; out may alias A.
