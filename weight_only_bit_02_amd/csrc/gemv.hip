@@ -401,7 +401,7 @@ static hipError_t launch_gemv_m1(const uint16_t* X, const uint32_t* qw, const ui
                                  const uint8_t* z, int64_t N, int64_t K, int gsh, uint16_t* Y,
                                  hipStream_t stream) {
   const int64_t cpl = (K / 32 + 63) / 64;  // chunks per lane to cover K once
-  const bool two = GATED || N >= 16384;
+  const bool two = GATED || N >= 8192;
   switch (cpl) {
     case 1: return two ? launch_gemv1s<1, 2, GATED>(X, qw, sc, z, N, K, gsh, Y, stream)
                        : launch_gemv1s<1, 1, false>(X, qw, sc, z, N, K, gsh, Y, stream);
