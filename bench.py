@@ -59,14 +59,15 @@ MATRICES = [  # name, search group, row offset inside the group, N, K
 SEARCH_GROUPS = {"qkv": (12288, 4096), "o": (4096, 4096), "gate_up": (22016, 4096), "down": (4096, 11008)}
 
 
-def packed_bytes(N, K):
-    G = K // GROUP
-    return N * (K // 2) + N * G * 2 + N * ((G + 1) // 2)
+def packed_bytes(N, K, group=GROUP, w_bit=4):
+    """Bytes of one packed [N][K] weight: codes, fp16 scales, zeros (4-bit: two per byte)."""
+    G = K // group
+    return N * K * w_bit // 8 + N * G * 2 + N * (G if w_bit == 8 else (G + 1) // 2)
 
 
-def linear_bytes(M, N, K, gated=False):
+def linear_bytes(M, N, K, gated=False, group=GROUP, w_bit=4):
     """Algorithmic HBM bytes of one W4A16 linear: packed weight + X + Y (gated: Y is N/2 wide)."""
-    return packed_bytes(N, K) + 2 * M * K + 2 * M * (N // 2 if gated else N)
+    return packed_bytes(N, K, group, w_bit) + 2 * M * K + 2 * M * (N // 2 if gated else N)
 
 
 GATED = {"gate_up"}  # the fused MLP module: SiLU(gate) * up in the launch's epilogue
@@ -103,6 +104,114 @@ def crossover(awq, packed, dev, stream, ms=(1, 2, 4, 8, 16, 32, 64), reps=20):
                 b.record(stream)
             b.synchronize()
             out[key].append(round(a.elapsed_time(b) * 1e3 / reps, 2))
+    return out
+
+
+# Format variants measured beside the headline (4-bit, asymmetric, 128-channel groups):
+# the same parts on the same inputs with one config field changed each.
+VARIANTS = {"group64": {"group_size": 64}, "group32": {"group_size": 32},
+            "symmetric": {"zero_point": False}, "int8": {"w_bit": 8}}
+VARIANT_LAYERS = 16  # decode layer copies per variant: 1.6-3.3 GB, far beyond the on-chip caches
+
+
+def time_variants(awq, si, dev, stream, Xcal, Wg, s_best, xdec, xpre, steps, warmup, log):
+    """Decode sweep, prefill GEMM, quantize+pack, scale search and clip search per format
+    variant, each part captured in a graph and timed like the headline parts (warm-up
+    replays, then `steps` replays between two events on the launch stream)."""
+    import torch
+    out = {}
+    for vname, kw in VARIANTS.items():
+        group, w_bit = kw.get("group_size", GROUP), kw.get("w_bit", 4)
+        log(f"bench: variant {vname}: packing {VARIANT_LAYERS} layer copies")
+        packed = []
+        with torch.cuda.stream(stream):
+            for c in range(VARIANT_LAYERS):
+                layer = {}
+                for i, (g, (N, K)) in enumerate(SEARCH_GROUPS.items()):
+                    w = Wg[g] if c == 0 else si.torch_weights(N, K, 1000 + 7 * c + i, dev)
+                    layer[g] = awq.quantize_pack(w, s_best[g] if c == 0 else None,
+                                                 out=awq.alloc_packed(N, K, dev, group, w_bit), **kw)
+                    del w
+                packed.append(layer)
+        yfus = {g: torch.empty((1, N // 2 if g in GATED else N), dtype=torch.float16, device=dev)
+                for g, (N, K) in SEARCH_GROUPS.items()}
+        ypre = {g: torch.empty((PREFILL_M, N // 2 if g in GATED else N), dtype=torch.float16, device=dev)
+                for g, (N, K) in SEARCH_GROUPS.items()}
+        ws = {g: awq.SearchWorkspace(CALIB_T, N, K, dev) for g, (N, K) in SEARCH_GROUPS.items()}
+        sres = {g: awq.search_scales(Xcal[g], Wg[g], workspace=ws[g], **kw) for g in SEARCH_GROUPS}
+
+        def gemv():
+            for layer in packed:
+                for g, (N, K) in SEARCH_GROUPS.items():
+                    linear = awq.linear_w4a16_gated_silu if g in GATED else awq.linear_w4a16
+                    linear(xdec[K], layer[g], out=yfus[g])
+
+        def gemm():
+            for g, (N, K) in SEARCH_GROUPS.items():
+                linear = awq.linear_w4a16_gated_silu if g in GATED else awq.linear_w4a16
+                linear(xpre[K], packed[0][g], out=ypre[g])
+
+        def pack():
+            for g in SEARCH_GROUPS:
+                awq.quantize_pack(Wg[g], s_best[g], out=packed[0][g], **kw)
+
+        def search():
+            for g in SEARCH_GROUPS:
+                awq.search_scales(Xcal[g], Wg[g], workspace=ws[g], out=sres[g], **kw)
+
+        def clip():
+            for g in SEARCH_GROUPS:
+                awq.clip_search(Xcal[g], Wg[g], s_best[g], 200, 20, **kw)
+
+        parts = {"gemv": gemv, "gemm": gemm, "quant_pack": pack, "search": search, "clip": clip}
+        ms = {}
+        with torch.cuda.stream(stream):
+            for fn in parts.values():
+                fn()
+            torch.cuda.synchronize()
+            y_eager = {g: yfus[g].clone() for g in yfus}
+            for pname, fn in parts.items():
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph, stream=stream):
+                    fn()
+                for _ in range(warmup):
+                    graph.replay()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for _ in range(steps):
+                    graph.replay()
+                b.record(stream)
+                b.synchronize()
+                ms[pname] = a.elapsed_time(b) / steps
+                del graph
+            for g in yfus:
+                assert torch.equal(yfus[g], y_eager[g]), f"graph replay differs ({vname} gemv)"
+
+        dec_bytes = VARIANT_LAYERS * sum(linear_bytes(1, N, K, g in GATED, group, w_bit)
+                                         for g, (N, K) in SEARCH_GROUPS.items())
+        dec_gbs = dec_bytes / (ms["gemv"] * 1e-3) / 1e9
+        gemm_tf = sum(2 * PREFILL_M * N * K for N, K in SEARCH_GROUPS.values()) / (ms["gemm"] * 1e-3) / 1e12
+        pack_gbs = sum(N * K * 2 + packed_bytes(N, K, group, w_bit)
+                       for N, K in SEARCH_GROUPS.values()) / (ms["quant_pack"] * 1e-3) / 1e9
+        search_tf = sum(2 * CALIB_T * N * K * 20 for N, K in SEARCH_GROUPS.values()) / (ms["search"] * 1e-3) / 1e12
+        clip_tf = sum(2 * CALIB_T * N * K * 20 for N, K in SEARCH_GROUPS.values()) / (ms["clip"] * 1e-3) / 1e12
+        out[vname] = {
+            "config": {"group_size": group, "w_bit": w_bit, "zero_point": kw.get("zero_point", True)},
+            "decode": {"gbs": round(dec_gbs, 2), "ms": round(ms["gemv"], 4),
+                       "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "layers": VARIANT_LAYERS,
+                       "launches": VARIANT_LAYERS * len(SEARCH_GROUPS)},
+            "gemm": {"tflops": round(gemm_tf, 2), "ms": round(ms["gemm"], 4),
+                     "frac": round(gemm_tf / FP16_MFMA_PEAK_TFLOPS, 4)},
+            "quant_pack": {"gbs": round(pack_gbs, 2), "ms": round(ms["quant_pack"], 4),
+                           "frac": round(pack_gbs / HBM_PEAK_GBS, 4)},
+            "search": {"tflops_algorithmic": round(search_tf, 2), "ms": round(ms["search"], 4),
+                       "best_alpha_index": {g: int(sres[g].best_idx.item()) for g in SEARCH_GROUPS}},
+            "clip_search": {"tflops_algorithmic": round(clip_tf, 2), "ms": round(ms["clip"], 4)},
+        }
+        log(f"bench: variant {vname}: decode {dec_gbs:.0f} GB/s, gemm {gemm_tf:.0f} TF, "
+            f"search {ms['search']:.2f} ms, clip {ms['clip']:.2f} ms")
+        del packed, yfus, ypre, ws, sres
+        torch.cuda.empty_cache()
     return out
 
 
@@ -149,6 +258,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=DECODE_LAYERS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the format variants (64/32-channel groups, symmetric, 8-bit)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying graphs")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="first run one plain device copy of BYTES (a known-size kernel for "
@@ -392,6 +503,12 @@ def main():
         "source_hash": source_hash(),
     }
     result["crossover"] = crossover(awq, packed[0], dev, stream)
+    if not args.no_variants:
+        del packed, views
+        torch.cuda.empty_cache()
+        result["variants"] = time_variants(awq, si, dev, stream, Xcal, Wg,
+                                           {g: sres[g].s_best for g in SEARCH_GROUPS},
+                                           xdec, xpre, args.steps, args.warmup, log)
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle (bounded sample)")
         result["cpu_baseline"] = cpu_baseline()
