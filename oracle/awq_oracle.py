@@ -29,7 +29,8 @@ Readings taken where the pages are silent (each is listed with its reason in the
 design notes of the repository):
 
 * codes are unsigned 0..15 with a zero point (asymmetric), dequant = (q - z) * scale;
-  the symmetric variant (zero_point False) uses sc = max|w'| / 7 and z = 8;
+  the symmetric variant (zero_point False) uses sc = max|w'| / 7 and z = 8; 8- and 3-bit
+  codes take the same steps with 255 / 7 levels;
 * min/max affine group quantizer, computed in fp32 with IEEE round-to-nearest-even;
   the codes are rounded against the stored fp16 scale;
 * scale floored at 2^-14, clamped to 65504 (flagged);
@@ -37,6 +38,7 @@ design notes of the repository):
 * statistic = plain mean of |x| over all calibration tokens;
 * s = (max(mean|x|, 2^-14))^alpha, alpha_i = i / n_grid, i = 0..n_grid-1, s stored as fp16;
 * packed word: channels 0, 2, 4, 6 in the low nibbles of its bytes, 1, 3, 5, 7 in the high;
+  3-bit codes in two bit planes per 128-channel block (see :func:`pack`);
 * error = sum of squares of X * D^T with D = W - Q(W diag(s)) diag(1/s), ties -> smallest i;
 * weight clipping: per group, ratios r_i = (clip_steps - i) / clip_steps, i < n_shrink
   (default 200 and 100), shrink the group's min/max; score = the group's own output
@@ -68,7 +70,7 @@ __all__ = [
 
 GROUP = 128                       # [AWQ-PRACTICE] §2.3; [AWQ-SKILL] q_group_size
 QMAX = 15                         # 4-bit unsigned codes 0..15 with a zero point
-W_BITS = (4, 8)                   # code widths: 4 (the format measured) and 8 ([AWQ-PRACTICE] §5.1)
+W_BITS = (3, 4, 8)                # code widths: 4 (the format measured), 3 and 8 ([AWQ-PRACTICE] §5.1, §4.3)
 N_GRID = 20                       # alpha grid: 20 points in [0, 1)
 ACT_FLOOR = 2.0 ** -14            # floor of the activation statistic (smallest normal fp16)
 SCALE_FLOOR = np.float32(2.0 ** -14)
@@ -155,7 +157,9 @@ def quantize_groups(W16: np.ndarray, s16: np.ndarray | None = None, clip_ratio: 
     so q - 8 = clamp(rint(w' / sc_h), -8, 7) is the signed code, stored offset by 8 in the
     same format (every zero nibble 8).
     8-bit codes (w_bit = 8; [AWQ-PRACTICE] §5.1 raises w_bit when accuracy drops): the same
-    steps with 15 -> 255 (codes 0..255) and, symmetric, 7 -> 127 and z = 128.
+    steps with 15 -> 255 (codes 0..255) and, symmetric, 7 -> 127 and z = 128. 3-bit codes
+    (w_bit = 3, the extreme low width [AWQ-PRACTICE] §4.3 names): 15 -> 7 (codes 0..7) and,
+    symmetric, 7 -> 3 and z = 4 (signed range -4..3).
     Returns dict(q uint8 [N][K], z uint8 [N][G], scale fp16 [N][G], flags int).
     """
     W16 = np.asarray(W16)
@@ -220,6 +224,12 @@ def pack(q: np.ndarray, z: np.ndarray, scale: np.ndarray, w_bit: int = 4) -> tup
     odd group; scales fp16 [N][G].
     8-bit: qweight uint32 [N][K/4]; byte j of word w holds the code of channel 4w + j;
     zeros uint8 [N][G], one byte per group; scales fp16 [N][G].
+    3-bit: qweight uint32 [N][3K/32], 12 words per 128-channel block b (words 12b ..
+    12b + 11), split into bit planes: low-plane word i (i < 8) holds bits 0-1 of the codes
+    of channels 16i + 2f (bits 2f, 2f + 1 of the word) and 16i + 2f + 1 (bits 16 + 2f,
+    17 + 2f), f = 0..7; high-plane word 8 + j (j < 4) holds bit 2 of the codes of channels
+    32j + 2p (bit p) and 32j + 2p + 1 (bit 16 + p), p = 0..15 (channels relative to the
+    block). Zeros and scales as for 4-bit.
     """
     q = np.asarray(q, dtype=np.uint8)
     N, K = q.shape
@@ -229,10 +239,23 @@ def pack(q: np.ndarray, z: np.ndarray, scale: np.ndarray, w_bit: int = 4) -> tup
         for j in range(4):
             qweight |= q[:, j::4].astype(np.uint32) << np.uint32(8 * j)
         return qweight, np.asarray(scale, dtype=np.float16).copy(), np.asarray(z, dtype=np.uint8).copy()
-    assert w_bit == 4
-    qweight = np.zeros((N, K // 8), dtype=np.uint32)
-    for j in range(8):
-        qweight |= q[:, NIBBLE_CHANNEL[j]::8].astype(np.uint32) << np.uint32(4 * j)
+    if w_bit == 3:
+        assert K % 128 == 0
+        qweight = np.zeros((N, 3 * K // 32), dtype=np.uint32)
+        for k in range(K):
+            b, c = divmod(k, 128)                 # block, channel within the block
+            code = q[:, k].astype(np.uint32)
+            lo_word = 12 * b + c // 16
+            lo_shift = 2 * ((c % 16) // 2) + 16 * (c % 2)
+            qweight[:, lo_word] |= (code & np.uint32(3)) << np.uint32(lo_shift)
+            hi_word = 12 * b + 8 + c // 32
+            hi_shift = (c % 32) // 2 + 16 * (c % 2)
+            qweight[:, hi_word] |= (code >> np.uint32(2)) << np.uint32(hi_shift)
+    else:
+        assert w_bit == 4
+        qweight = np.zeros((N, K // 8), dtype=np.uint32)
+        for j in range(8):
+            qweight |= q[:, NIBBLE_CHANNEL[j]::8].astype(np.uint32) << np.uint32(4 * j)
     zeros = np.zeros((N, (G + 1) // 2), dtype=np.uint8)
     zeros |= z[:, 0::2].astype(np.uint8)
     zeros[:, : G // 2] |= (z[:, 1::2].astype(np.uint8) << np.uint8(4))
@@ -249,9 +272,16 @@ def unpack(qweight: np.ndarray, scales: np.ndarray, zeros: np.ndarray, K: int):
         for j in range(4):
             q[:, j::4] = ((qweight >> np.uint32(8 * j)) & np.uint32(0xFF)).astype(np.uint8)
         return q, np.asarray(zeros, dtype=np.uint8)[:, :G].copy(), np.asarray(scales, dtype=np.float16)
-    assert qweight.shape[1] == K // 8
-    for j in range(8):
-        q[:, NIBBLE_CHANNEL[j]::8] = ((qweight >> np.uint32(4 * j)) & np.uint32(0xF)).astype(np.uint8)
+    if qweight.shape[1] == 3 * K // 32:         # 3-bit bit planes
+        for k in range(K):
+            b, c = divmod(k, 128)
+            lo = (qweight[:, 12 * b + c // 16] >> np.uint32(2 * ((c % 16) // 2) + 16 * (c % 2))) & np.uint32(3)
+            hi = (qweight[:, 12 * b + 8 + c // 32] >> np.uint32((c % 32) // 2 + 16 * (c % 2))) & np.uint32(1)
+            q[:, k] = (lo | (hi << np.uint32(2))).astype(np.uint8)
+    else:
+        assert qweight.shape[1] == K // 8
+        for j in range(8):
+            q[:, NIBBLE_CHANNEL[j]::8] = ((qweight >> np.uint32(4 * j)) & np.uint32(0xF)).astype(np.uint8)
     z = np.empty((N, G), dtype=np.uint8)
     z[:, 0::2] = zeros[:, : (G + 1) // 2] & np.uint8(0xF)
     z[:, 1::2] = zeros[:, : G // 2] >> np.uint8(4)
@@ -513,4 +543,4 @@ def packed_bytes(N: int, K: int, group: int = GROUP, w_bit: int = 4) -> int:
     G = K // group
     if w_bit == 8:
         return N * K + N * G * 2 + N * G
-    return N * (K // 2) + N * G * 2 + N * ((G + 1) // 2)
+    return N * K * w_bit // 8 + N * G * 2 + N * ((G + 1) // 2)

@@ -746,3 +746,104 @@ def test_8bit_linear_reference_one_hot():
             code = (int(qw[n, k // 4]) >> (8 * (k % 4))) & 0xFF
             want = (code - int(zp[n, k // 64])) * float(sc[n, k // 64])
             assert y[0, n] == want
+
+
+# ----------------------------------------------------------------- 3-bit codes
+@pytest.mark.parametrize("group", [128, 32])
+def test_3bit_codes_nearest_scale_and_zero(group):
+    """3-bit codes: nearest of 0..7 for the stored scale (brute force), scale / zero from the
+    closed form with 7 levels; the 15-level scale of 4-bit codes fails the same check."""
+    W = si.weights(3, 256, offset=140)
+    s = np.exp(np.random.default_rng(15).uniform(-1, 1, 256)).astype(np.float16)
+    w = W.astype(np.float32) * s.astype(np.float32)
+    r = oracle.quantize_groups(W, s, group=group, w_bit=3)
+    assert not pins.check_codes_nearest(w, r["q"], r["z"], r["scale"], qmax=7)
+    assert not pins.check_scale_zero(w, r["z"], r["scale"], qmax=7)
+    r4 = oracle.quantize_groups(W, s, group=group, w_bit=4)
+    assert pins.check_scale_zero(w, r4["z"], r4["scale"], qmax=7)
+    assert r["q"].max() == 7 and r["q"].min() == 0   # min and max of each group hit the ends
+
+
+def test_3bit_symmetric_codes():
+    """Symmetric 3-bit: sc = max|w'| / 3, zero 4, q - 4 in -4..3, codes nearest."""
+    W = si.weights(2, 256, offset=141)
+    r = oracle.quantize_groups(W, zero_point=False, w_bit=3)
+    w = W.astype(np.float32)
+    assert np.all(r["z"] == 4)
+    assert not pins.check_codes_nearest(w, r["q"], r["z"], r["scale"], qmax=7)
+    for n in range(2):
+        for j in range(2):
+            amax = np.abs(w[n, j * 128:(j + 1) * 128]).max()
+            assert r["scale"][n, j] == np.float16(np.float32(amax) / np.float32(3))
+    n, k = np.unravel_index(np.argmax(np.abs(w[:, :128])), (2, 128))
+    assert abs(int(r["q"][n, k]) - 4) == 3
+
+
+def test_3bit_pack_layout_by_hand():
+    """Bit planes per 128-channel block: words 0-7 carry bits 0-1 (pair (2f, 2f+1) of word i
+    at bits 2f and 16 + 2f), words 8-11 bit 2 (pair p of word 8 + j at bits p and 16 + p);
+    zeros in nibbles as for 4-bit; the byte count."""
+    q = np.zeros((1, 256), dtype=np.uint8)
+    q[0, 0] = 5      # 0b101: word 0 bits 0-1 = 01, word 8 bit 0
+    q[0, 1] = 6      # 0b110: word 0 bits 16-17 = 10, word 8 bit 16
+    q[0, 17] = 3     # channel 16 + 1: word 1 bits 16-17 = 11
+    q[0, 33] = 4     # channel 32 + 1: word 2 bits 16-17 = 00, word 9 bit 16
+    q[0, 127] = 7    # channel 112 + 15: word 7 bits 30-31; channel 96 + 31: word 11 bit 31
+    q[0, 130] = 1    # block 1, channel 2: word 12 bits 2-3
+    z = np.array([[3, 5]], dtype=np.uint8)
+    sc = np.array([[1.0, 2.0]], dtype=np.float16)
+    qw, scp, zp = oracle.pack(q, z, sc, w_bit=3)
+    assert qw.shape == (1, 24) and zp.shape == (1, 1)
+    want = [0] * 24
+    want[0] = 0x1 | (0x2 << 16)
+    want[8] = 0x1 | (0x1 << 16)
+    want[1] = 0x3 << 16
+    want[9] = 0x1 << 16
+    want[7] = 0x3 << 30
+    want[11] = 0x1 << 31
+    want[12] = 0x1 << 2
+    assert [int(v) for v in qw[0]] == want
+    assert zp[0, 0] == 0x53
+    q2, z2, _ = oracle.unpack(qw, scp, zp, 256)
+    assert np.array_equal(q2, q) and np.array_equal(z2, z)
+    W = si.weights(5, 384, offset=142)
+    r = oracle.quantize_groups(W, group=32, w_bit=3)
+    qw, scp, zp = oracle.pack(r["q"], r["z"], r["scale"], w_bit=3)
+    q2, z2, _ = oracle.unpack(qw, scp, zp, 384)
+    assert np.array_equal(q2, r["q"]) and np.array_equal(z2, r["z"])
+    assert oracle.packed_bytes(4096, 4096, 128, w_bit=3) == 4096 * 1536 + 4096 * 32 * 2 + 4096 * 16
+
+
+def test_3bit_search_and_clip_errors_exact():
+    X = si.activations(2, 128, offset=143)
+    W = si.weights(2, 128, offset=143)
+    r = oracle.search_errors(X, W, n_grid=3, w_bit=3)
+    for i in range(3):
+        qz = oracle.quantize_groups(W, r["s16"][i], w_bit=3)
+        exact = pins.exact_search_error(X, W, r["s16"][i], qz["q"], qz["z"], qz["scale"])
+        assert abs(r["err"][i] - float(exact)) <= 1e-12 * float(exact)
+    e = oracle.clip_errors(X, W, r["s16"][1], 200, 3, w_bit=3)
+    qz = oracle.quantize_groups(W, r["s16"][1], np.full((2, 1), oracle.clip_ratios(200, 3)[2], np.float32), w_bit=3)
+    ex = pins.exact_group_errors(X, W, r["s16"][1], qz["q"], qz["z"], qz["scale"])
+    assert all(abs(e[2, n, 0] - float(ex[n][0])) <= 1e-12 * float(ex[n][0]) for n in range(2))
+    # 3-bit codes quantize more coarsely: about twice the step, four times the error
+    r4 = oracle.search_errors(X, W, n_grid=1)
+    assert r["err"][0] > 2 * r4["err"][0]
+
+
+def test_3bit_linear_reference_one_hot():
+    """x = e_k reads (q - z) sc of channel k from the bit planes (bits located by the
+    layout's own formula, written out here)."""
+    W = si.weights(3, 256, offset=144)
+    qw, sc, zp, _ = oracle.quantize_pack(W, group=64, w_bit=3)
+    for k in (0, 1, 17, 63, 64, 127, 128, 255):
+        X = np.zeros((1, 256), dtype=np.float16)
+        X[0, k] = 1.0
+        y, _ = oracle.linear_reference(X, qw, sc, zp, 256)
+        b, c = divmod(k, 128)
+        for n in range(3):
+            lo = (int(qw[n, 12 * b + c // 16]) >> (2 * ((c % 16) // 2) + 16 * (c % 2))) & 3
+            hi = (int(qw[n, 12 * b + 8 + c // 32]) >> ((c % 32) // 2 + 16 * (c % 2))) & 1
+            g = k // 64
+            zz = (int(zp[n, g // 2]) >> (4 * (g % 2))) & 0xF
+            assert y[0, n] == (lo + 4 * hi - zz) * float(sc[n, g])
