@@ -60,7 +60,7 @@ SEARCH_GROUPS = {"qkv": (12288, 4096), "o": (4096, 4096), "gate_up": (22016, 409
 
 
 def packed_bytes(N, K, group=GROUP, w_bit=4):
-    """Bytes of one packed [N][K] weight: codes, fp16 scales, zeros (4-bit: two per byte)."""
+    """Bytes of one packed [N][K] weight: codes, fp16 scales, zeros (3/4-bit: two per byte)."""
     G = K // group
     return N * K * w_bit // 8 + N * G * 2 + N * (G if w_bit == 8 else (G + 1) // 2)
 
@@ -110,7 +110,7 @@ def crossover(awq, packed, dev, stream, ms=(1, 2, 4, 8, 16, 32, 64), reps=20):
 # Format variants measured beside the headline (4-bit, asymmetric, 128-channel groups):
 # the same parts on the same inputs with one config field changed each.
 VARIANTS = {"group64": {"group_size": 64}, "group32": {"group_size": 32},
-            "symmetric": {"zero_point": False}, "int8": {"w_bit": 8}}
+            "symmetric": {"zero_point": False}, "int8": {"w_bit": 8}, "int3": {"w_bit": 3}}
 VARIANT_LAYERS = 16  # decode layer copies per variant: 1.6-3.3 GB, far beyond the on-chip caches
 
 
@@ -259,7 +259,7 @@ def main():
     ap.add_argument("--layers", type=int, default=DECODE_LAYERS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
-                    help="skip the format variants (64/32-channel groups, symmetric, 8-bit)")
+                    help="skip the format variants (64/32-channel groups, symmetric, 8- and 3-bit)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying graphs")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="first run one plain device copy of BYTES (a known-size kernel for "

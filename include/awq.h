@@ -43,7 +43,7 @@ typedef enum awq_status {
   AWQ_OK = 0,
   AWQ_ERR_NULL_POINTER = 1,  /* a required pointer is NULL                          */
   AWQ_ERR_BAD_SHAPE = 2,     /* a size < 1, K % 128 != 0, T above 8192, ...          */
-  AWQ_ERR_UNSUPPORTED = 3,   /* config outside w_bit 4 / group 128, 64, 32 / zp 0, 1  */
+  AWQ_ERR_UNSUPPORTED = 3,   /* config outside w_bit 3,4,8 / group 128,64,32 / zp 0,1 */
   AWQ_ERR_MISALIGNED = 4,    /* a base pointer is not 16-byte aligned                */
   AWQ_ERR_WORKSPACE = 5,     /* workspace missing or smaller than the query returns  */
   AWQ_ERR_HIP = 6            /* the HIP runtime reported an error on launch          */
@@ -51,8 +51,9 @@ typedef enum awq_status {
 
 /* Quantization config ([SKILL] "如何使用该技能 / 步骤 2": quant_config zero_point, q_group_size,
  * w_bit; the page's "version" GEMM/GEMV switch becomes dispatch on M inside
- * awq_linear_w4a16). Supported: w_bit = 4 or 8 ([PRACTICE] §5.1 raises w_bit when 4-bit
- * accuracy falls short), group_size = 128, 64 or 32 ([PRACTICE] §2.3:
+ * awq_linear_w4a16). Supported: w_bit = 4, 8 ([PRACTICE] §5.1 raises w_bit when 4-bit
+ * accuracy falls short) or 3 ([PRACTICE] §4.3 names 3-bit weights as the extreme low
+ * width), group_size = 128, 64 or 32 ([PRACTICE] §2.3:
  * 128 is the usual group, 64 and 32 also in use), zero_point = 1 or 0, 1 <= n_grid <= 64.
  * NULL config pointers mean {4, 128, 1, 20}. Every entry point takes the group size from
  * the config; K stays a multiple of 128 in every case, so a smaller group never straddles
@@ -61,9 +62,10 @@ typedef enum awq_status {
  * zero_point = 0 ([PRACTICE] §3.3 advises it; [GPTQ-AWQ] gives the signed range -8..7):
  * sc = max|w'| / 7, q - 8 = clamp(rint(w'/sc_h), -8, 7), stored offset by 8 with every
  * zero nibble 8 -- the same packed format, so the linear entry points are unchanged;
- * quantize, search and clip search honour the mode (8-bit: /127 and zero 128).
- * w_bit = 8: the same quantizer with 255 levels and its own packed layout (see
- * awq_quantize_pack); every entry point, linear kernels included, takes it from the config.
+ * quantize, search and clip search honour the mode (8-bit: /127 and zero 128; 3-bit: /3
+ * and zero 4). w_bit = 8 or 3: the same quantizer with 255 or 7 levels and its own packed
+ * layout (see awq_quantize_pack); every entry point, linear kernels included, takes it
+ * from the config.
  * The linear entry points need the config the weight was packed with. */
 typedef struct awq_config {
   int32_t w_bit;
@@ -82,8 +84,8 @@ typedef struct awq_config {
 /* Which linear kernel awq_linear_w4a16_ex runs. */
 typedef enum awq_linear_kernel {
   AWQ_LINEAR_AUTO = 0, /* vector GEMV for M <= 3, skinny MFMA GEMV up to
-                          awq_gemv_max_m(), MFMA GEMM above (8-bit codes:
-                          vector GEMV up to 8, skinny up to 32)               */
+                          awq_gemv_max_m(), MFMA GEMM above (8- and 3-bit
+                          codes: vector GEMV up to 8, skinny up to 32)         */
   AWQ_LINEAR_GEMV = 1, /* wave-per-rows dequant-fused GEMV (any M <= 8)       */
   AWQ_LINEAR_GEMM = 2, /* MFMA dequant-GEMM (any M)                           */
   AWQ_LINEAR_SKINNY = 3 /* MFMA GEMV for small batches, split K (M <= 32)     */
@@ -108,6 +110,12 @@ typedef enum awq_linear_kernel {
  *   flags    uint32 [1] or NULL   NONFINITE_INPUT, SCALE_CLAMPED
  *   w_bit = 8: 15 -> 255 above (codes 0..255); qweight uint32 [N][K/4], byte j of word w
  *   holds k = 4w + j; zeros uint8 [N][G], one byte per group; scales as above.
+ *   w_bit = 3: 15 -> 7 above (codes 0..7); qweight uint32 [N][3K/32] in bit planes, 12
+ *   words per 128-channel block b (words 12b .. 12b + 11): word 12b + i (i < 8) holds bits
+ *   0-1 of the codes of k = 128b + 16i + 2f at bits 2f, 2f + 1 and of k + 1 at bits
+ *   16 + 2f, 17 + 2f (f = 0..7); word 12b + 8 + j (j < 4) holds bit 2 of the codes of
+ *   k = 128b + 32j + 2p at bit p and of k + 1 at bit 16 + p (p = 0..15); zeros and scales
+ *   as for 4-bit.
  */
 awq_status awq_quantize_pack(const void* W, int64_t N, int64_t K, const void* s,
                              const awq_config* cfg, uint32_t* qweight, void* scales,

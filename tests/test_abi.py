@@ -53,8 +53,9 @@ def test_quantize_pack_validation(lib):
     assert _qp(lib, N=0) == 2
     assert _qp(lib, W=FAKE_ODD) == 4
     assert _qp(lib, s=FAKE_ODD) == 4
-    bad = _abi.config(w_bit=3)
-    assert _qp(lib, cfg=C.byref(bad)) == 3
+    for w_bit in (2, 5, 6, 16):
+        bad = _abi.config(w_bit=w_bit)
+        assert _qp(lib, cfg=C.byref(bad)) == 3
     bad = _abi.config(n_grid=0)
     assert _qp(lib, cfg=C.byref(bad)) == 3
     bad = _abi.config(group_size=16)

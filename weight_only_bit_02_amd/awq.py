@@ -40,9 +40,9 @@ def _need(t, dtype, name):
 @dataclass
 class PackedLinear:
     """Packed 4-bit weight of one [N][K] linear: codes, fp16 group scales, zero nibbles."""
-    qweight: torch.Tensor  # int32 [N][K/8] (4-bit) or [N][K/4] (8-bit): the bits of uint32 words
+    qweight: torch.Tensor  # int32 [N][K w_bit / 32] (3, 4 or 8-bit codes): the bits of uint32 words
     scales: torch.Tensor   # fp16 [N][G], G = K / group
-    zeros: torch.Tensor    # uint8 [N][ceil(G/2)] (4-bit: two per byte) or [N][G] (8-bit)
+    zeros: torch.Tensor    # uint8 [N][ceil(G/2)] (3/4-bit: two per byte) or [N][G] (8-bit)
     N: int
     K: int
     group: int = GROUP
@@ -54,10 +54,9 @@ class PackedLinear:
 
 def alloc_packed(N: int, K: int, device, group: int = GROUP, w_bit: int = 4) -> PackedLinear:
     G = K // group
-    per_word = 32 // w_bit
     zcols = G if w_bit == 8 else (G + 1) // 2
     return PackedLinear(
-        torch.empty((N, K // per_word), dtype=torch.int32, device=device),
+        torch.empty((N, K * w_bit // 32), dtype=torch.int32, device=device),
         torch.empty((N, G), dtype=torch.float16, device=device),
         torch.empty((N, zcols), dtype=torch.uint8, device=device), N, K, group, w_bit)
 
@@ -69,7 +68,7 @@ def quantize_pack(W: torch.Tensor, s: torch.Tensor | None = None, flags: torch.T
     """awq_quantize_pack: 4-bit group-wise quantization of W * diag(s) (s = None: plain
     RTN; groups of group_size = 128 or 64 channels); with clip_idx (uint8 [N][K/group],
     clip_search's output), awq_quantize_pack_clipped; zero_point=False: symmetric codes
-    (same packed format, every zero 8); w_bit=8: 8-bit codes."""
+    (same packed format, every zero 8); w_bit=8 or 3: 8- or 3-bit codes."""
     lib = _abi.load()
     _need(W, torch.float16, "W")
     if W.dim() != 2:

@@ -20,7 +20,8 @@ LIB = os.path.join(LIB_DIR, "libawq_mi355x.so")
 
 SOURCES = ["awq_abi.hip", "quant_pack.hip", "stats.hip", "search.hip", "gemv.hip", "gemm.hip",
            "fold.hip", "gemv_mfma.hip", "gemv8.hip", "gemm_i4_plain.hip", "gemm_i4_gated.hip",
-           "gemm_i4_plain_g32.hip", "gemm_i4_gated_g32.hip"]
+           "gemm_i4_plain_g32.hip", "gemm_i4_gated_g32.hip", "gemv3.hip", "gemm_i3_plain.hip",
+           "gemm_i3_gated.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -15,7 +15,7 @@ awq_config resolve(const awq_config* cfg) {
 }
 
 bool supported(const awq_config& c) {
-  return (c.w_bit == 4 || c.w_bit == 8) &&
+  return (c.w_bit == 3 || c.w_bit == 4 || c.w_bit == 8) &&
          (c.group_size == 128 || c.group_size == 64 || c.group_size == 32) &&
          (c.zero_point == 0 || c.zero_point == 1) && c.n_grid >= 1 && c.n_grid <= 64;
 }
@@ -90,7 +90,7 @@ const char* awq_status_string(awq_status s) {
     case AWQ_OK: return "ok";
     case AWQ_ERR_NULL_POINTER: return "a required pointer is NULL";
     case AWQ_ERR_BAD_SHAPE: return "bad shape (sizes must be >= 1, K a multiple of 128, T <= 8192)";
-    case AWQ_ERR_UNSUPPORTED: return "unsupported config (w_bit 4 or 8, group_size 128, 64 or 32, zero_point 0 or 1, 1 <= n_grid <= 64)";
+    case AWQ_ERR_UNSUPPORTED: return "unsupported config (w_bit 3, 4 or 8, group_size 128, 64 or 32, zero_point 0 or 1, 1 <= n_grid <= 64)";
     case AWQ_ERR_MISALIGNED: return "a base pointer is not 16-byte aligned";
     case AWQ_ERR_WORKSPACE: return "workspace missing or too small";
     case AWQ_ERR_HIP: return "HIP launch error";
@@ -219,7 +219,7 @@ static awq_status linear_common(const void* X, int64_t M, const uint32_t* qweigh
     return AWQ_ERR_MISALIGNED;
   // AUTO, measured on the Llama-2-7B layer: the vector-ALU GEMV up to M = 3 (its dot cost
   // grows with M), the MFMA skinny GEMV up to g_gemv_max_m, the MFMA GEMM above.
-  if (kernel == AWQ_LINEAR_AUTO && c.w_bit == 8)
+  if (kernel == AWQ_LINEAR_AUTO && c.w_bit != 4)
     kernel = M <= awq::kGemvMaxM ? AWQ_LINEAR_GEMV
              : M <= awq::kSkinnyMaxM ? AWQ_LINEAR_SKINNY : AWQ_LINEAR_GEMM;
   if (kernel == AWQ_LINEAR_AUTO)
@@ -240,6 +240,17 @@ static awq_status linear_common(const void* X, int64_t M, const uint32_t* qweigh
           awq::launch_gemv_mfma8(Xh, M, qweight, sc, zeros, N, K, c.group_size, Yh, gated, st));
     return hip_status(
         awq::launch_gemm(Xh, M, qweight, sc, zeros, N, K, c.group_size, 8, Yh, gated, st));
+  }
+  if (c.w_bit == 3) {
+    // 3-bit codes: the same three kernels' 3-bit forms, with the same thresholds
+    if (kernel == AWQ_LINEAR_GEMV)
+      return hip_status(
+          awq::launch_gemv3(Xh, M, qweight, sc, zeros, N, K, c.group_size, Yh, gated, st));
+    if (kernel == AWQ_LINEAR_SKINNY)
+      return hip_status(
+          awq::launch_gemv_mfma3(Xh, M, qweight, sc, zeros, N, K, c.group_size, Yh, gated, st));
+    return hip_status(
+        awq::launch_gemm(Xh, M, qweight, sc, zeros, N, K, c.group_size, 3, Yh, gated, st));
   }
   switch (kernel) {
     case AWQ_LINEAR_GEMV:

@@ -245,6 +245,21 @@ __device__ __forceinline__ uint32_t pack_codes8(const float (&q)[8]) {
   return word;
 }
 
+// 3-bit codes of 8 consecutive channels 0..7 (values 0..7 as floats) as their shares of
+// the two bit planes: lo = bits 0-1 of channel 2i + e at bits 2i + 16e, hi = bit 2 of
+// channel 2i + e at bit i + 16e (i = 0..3, e = 0..1), both for a lane whose channels start
+// a plane word; the caller shifts them to the lane's place in the word.
+__device__ __forceinline__ void planes3(const float (&q)[8], uint32_t& lo, uint32_t& hi) {
+  lo = 0;
+  hi = 0;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const uint32_t c = (uint32_t)q[t];
+    lo |= (c & 3u) << (2 * (t >> 1) + 16 * (t & 1));
+    hi |= (c >> 2) << ((t >> 1) + 16 * (t & 1));
+  }
+}
+
 // One word of four 8-bit codes, byte i = code i.
 __device__ __forceinline__ uint32_t pack_bytes4(float q0, float q1, float q2, float q3) {
   uint32_t word = 0;

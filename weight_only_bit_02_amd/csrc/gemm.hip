@@ -1,6 +1,6 @@
 // MFMA dequant-GEMM launcher: picks the instantiation for the code width, the group size
-// and the gated epilogue (the kernel is in gemm_kernel.hpp; the 4-bit instantiations are
-// compiled in gemm_i4_*.hip, the 8-bit ones here).
+// and the gated epilogue (the kernel is in gemm_kernel.hpp; the 4- and 3-bit instantiations
+// are compiled in gemm_i4_*.hip and gemm_i3_*.hip, the 8-bit ones here).
 #include "gemm_kernel.hpp"
 
 namespace awq {
@@ -18,6 +18,13 @@ void launch_gemm4_gated_g32(dim3 grid, const uint16_t* X, int64_t M, const uint3
                 const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K, int group,
                 uint16_t* Y, int64_t mt, int64_t nt, int64_t per_xcd, hipStream_t stream);
 
+void launch_gemm3_plain(dim3 grid, const uint16_t* X, int64_t M, const uint32_t* qweight,
+                const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K, int group,
+                uint16_t* Y, int64_t mt, int64_t nt, int64_t per_xcd, hipStream_t stream);
+void launch_gemm3_gated(dim3 grid, const uint16_t* X, int64_t M, const uint32_t* qweight,
+                const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K, int group,
+                uint16_t* Y, int64_t mt, int64_t nt, int64_t per_xcd, hipStream_t stream);
+
 hipError_t launch_gemm(const uint16_t* X, int64_t M, const uint32_t* qweight,
                        const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
                        int group, int w_bit, uint16_t* Y, bool gated, hipStream_t stream) {
@@ -32,6 +39,11 @@ hipError_t launch_gemm(const uint16_t* X, int64_t M, const uint32_t* qweight,
     else
       hipLaunchKernelGGL((k_gemm<false, false, 8>), grid, dim3(256), 0, stream, X, M, qweight,
                          scales, zeros, N, K, group, Y, mt, nt, per_xcd);
+  } else if (w_bit == 3) {
+    if (gated)
+      launch_gemm3_gated(grid, X, M, qweight, scales, zeros, N, K, group, Y, mt, nt, per_xcd, stream);
+    else
+      launch_gemm3_plain(grid, X, M, qweight, scales, zeros, N, K, group, Y, mt, nt, per_xcd, stream);
   } else if (group == 32) {  // two scales per lane half
     if (gated)
       launch_gemm4_gated_g32(grid, X, M, qweight, scales, zeros, N, K, group, Y, mt, nt, per_xcd, stream);

@@ -77,20 +77,42 @@ __device__ __forceinline__ half8 dequant_word8(uint32_t w0, uint32_t w1, half2v 
   return half8{d[0][0], d[0][1], d[1][0], d[1][1], d[2][0], d[2][1], d[3][0], d[3][1]};
 }
 
+// 4 channel pairs of 3-bit codes -> 8 dequantized fp16 channels (q - z) * sc, in channel
+// order. Pair t (t = 0..3) has bits 0-1 in field F + t of the low-plane word `lo` (bits
+// 2 (F + t) and 16 + 2 (F + t)) and bit 2 at bit P + t and 16 + P + t of the high-plane
+// word `hi`; both land in place below the 0x6400 exponent, so the fp16 pair is exactly
+// (1024 + q_even, 1024 + q_odd).
+template <int F, int P>
+__device__ __forceinline__ half8 dequant_word3(uint32_t lo, uint32_t hi, half2v zz, half2v s2,
+                                               uint32_t magic) {
+  half2v d[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int f = F + t, p = P + t;
+    const uint32_t h = p >= 2 ? (hi >> (p - 2)) : (hi << (2 - p));
+    const uint32_t u = ((lo >> (2 * f)) & 0x00030003u) | (h & 0x00040004u) | magic;
+    d[t] = (__builtin_bit_cast(half2v, u) + zz) * s2;
+  }
+  return half8{d[0][0], d[0][1], d[1][0], d[1][1], d[2][0], d[2][1], d[3][0], d[3][1]};
+}
+
 // Per-step operands that travel through registers: this thread's share of the A tile
 // (8 x 16 bytes) and this lane's codes (2 columns x 32 bytes, or 64 with 8-bit codes)
 // with their scales and zeros.
 template <int BITS>
 struct GemmStage {
   uint4 a[8];
-  uint4 b[2][BITS / 2];
+  uint4 b[2][BITS / 2];       // 3-bit: the lane half's 4 low-plane words
+  uint2 bh[2];                // 3-bit: the lane half's 2 high-plane words (unused otherwise)
   uint32_t zb[2], sc[2][2];  // per column: zero byte(s); scales of the lane's two 32-channel
                              // halves (the second only with 32-channel groups or 8-bit codes)
 };
 
 // SPLIT: 32-channel groups (two scales per lane half); otherwise 128 or 64, one scale.
 // BITS = 8: 8-bit codes (16 words per lane half and step; both halves' scales and zero
-// bytes always loaded).
+// bytes always loaded). BITS = 3: 3-bit codes, 12 words per step (words 0-7 the low bit
+// plane, 16 channels each; 8-11 the high plane, 32 channels each): lane half kh takes low
+// words 4 kh .. 4 kh + 3 and high words 8 + 2 kh, 9 + 2 kh; zeros and scales as for 4-bit.
 template <bool GATED, bool SPLIT, int BITS>
 __global__ void __launch_bounds__(256)
     k_gemm(const uint16_t* X, int64_t M, const uint32_t* qweight, const uint16_t* scales,
@@ -166,11 +188,18 @@ __global__ void __launch_bounds__(256)
       }
     }
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 2; ++b) {
+      if constexpr (BITS == 3) {
+        const uint32_t* wp = qweight + b_col[b] * words + step * 12;
+        st.b[b][0] = *reinterpret_cast<const uint4*>(wp + 4 * kh);
+        st.bh[b] = *reinterpret_cast<const uint2*>(wp + 8 + 2 * kh);
+      } else {
 #pragma unroll
-      for (int h = 0; h < BITS / 2; ++h)
-        st.b[b][h] = *reinterpret_cast<const uint4*>(qweight + b_col[b] * words + step * (4 * BITS) +
-                                                     kh * (2 * BITS) + h * 4);
+        for (int h = 0; h < BITS / 2; ++h)
+          st.b[b][h] = *reinterpret_cast<const uint4*>(qweight + b_col[b] * words + step * (4 * BITS) +
+                                                       kh * (2 * BITS) + h * 4);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       st.a[i] = *reinterpret_cast<const uint4*>(X + a_row[i] + step * kBK + a_kc[i] * 8);
@@ -193,9 +222,10 @@ __global__ void __launch_bounds__(256)
   // ahead) has its A in flight to LDS, `nn` (two steps ahead) is being loaded. The loop is
   // unrolled by three with the stages' roles rotated, so no register copy (which would
   // wait for the loads just issued) is ever needed. 8-bit codes double a stage's B
-  // registers, so there the distance is 1 with two stages (the next step's loads are in
-  // flight for a whole step of MFMAs): `nn` is `nxt`.
-  constexpr int PF = BITS == 8 ? 1 : 2;
+  // registers and the 3-bit widening needs more temporaries, so for those the distance is 1
+  // with two stages (the next step's loads are in flight for a whole step of MFMAs): `nn`
+  // is `nxt`.
+  constexpr int PF = BITS == 4 ? 2 : 1;
   GemmStage<BITS> S0, S1, S2;
   load(S0, 0);
   if constexpr (PF == 2) load(S1, nsteps > 1 ? 1 : 0);
@@ -238,6 +268,16 @@ __global__ void __launch_bounds__(256)
           const uint4 q = cur.b[b][s >> 1];
           B[b] = (s & 1) ? dequant_word8(q.z, q.w, zz[b][i], s2[b][i], magic8)
                          : dequant_word8(q.x, q.y, zz[b][i], s2[b][i], magic8);
+        } else if constexpr (BITS == 3) {
+          // slice s = channels 8 s .. 8 s + 7 of the half: pairs 4 s .. 4 s + 3, i.e. low
+          // word s / 2 (fields 4 (s % 2) ..) and high word s / 4 (bits 4 (s % 4) ..)
+          const uint4 q = cur.b[b][0];
+          const uint32_t lo = (s >> 1) == 0 ? q.x : (s >> 1) == 1 ? q.y : (s >> 1) == 2 ? q.z : q.w;
+          const uint32_t hi = (s >> 2) ? cur.bh[b].y : cur.bh[b].x;
+          B[b] = (s & 1) ? ((s & 2) ? dequant_word3<4, 12>(lo, hi, zz[b][i], s2[b][i], magic)
+                                    : dequant_word3<4, 4>(lo, hi, zz[b][i], s2[b][i], magic))
+                         : ((s & 2) ? dequant_word3<0, 8>(lo, hi, zz[b][i], s2[b][i], magic)
+                                    : dequant_word3<0, 0>(lo, hi, zz[b][i], s2[b][i], magic));
         } else {
           const uint4 q = cur.b[b][s >> 2];
           const uint32_t w = (s & 3) == 0 ? q.x : (s & 3) == 1 ? q.y : (s & 3) == 2 ? q.z : q.w;

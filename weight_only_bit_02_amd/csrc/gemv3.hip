@@ -1,0 +1,363 @@
+// Vector and skinny-MFMA GEMV for 3-bit codes (a7 with w_bit = 3): Y[M][N] = X[M][K] deq(W)^T.
+//
+// "AWQ量化实战" §4.3 names 3-bit weights as the extreme low width; the decode GEMV then
+// streams 3/8 of a byte per weight.
+//
+// Packed layout: 12 words per 128-channel block, in two bit planes. Low-plane word i
+// (i < 8) holds bits 0-1 of channel pair (16 i + 2 f, 16 i + 2 f + 1) at bits 2 f and
+// 16 + 2 f; high-plane word 8 + j (j < 4) holds bit 2 of pair (32 j + 2 p, 32 j + 2 p + 1)
+// at bits p and 16 + p. Masking both planes for one pair leaves the two 3-bit codes at bits
+// 0-2 of each 16-bit half, below the 0x6400 exponent: the fp16 pair (1024 + a, 1024 + b),
+// exactly, and a packed add of -(1024 + z) gives (q - z). Zeros are nibbles as for 4-bit.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace awq {
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+namespace {
+
+__device__ __forceinline__ uint32_t magic_6400() {
+  uint32_t m;
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(m));
+  return m;
+}
+
+// Pair p (0..15) of a 32-channel chunk: low-plane word `lo` (the chunk's word p / 8), field
+// p % 8; high-plane word hi, bit p. Returns the fp16 pair (1024 + q_2p, 1024 + q_2p+1) as
+// bits. Callers unroll over p, so every shift is a constant.
+__device__ __forceinline__ uint32_t widen3(uint32_t lo, uint32_t hi, int p, uint32_t magic) {
+  const uint32_t h = p >= 2 ? (hi >> (p - 2)) : (hi << (2 - p));
+  return ((lo >> (2 * (p & 7))) & 0x00030003u) | (h & 0x00040004u) | magic;
+}
+
+__device__ __forceinline__ uint32_t zero_nibble(const uint8_t* zrow, int64_t g) {
+  return ((uint32_t)zrow[g >> 1] >> (4 * (g & 1))) & 0xFu;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ vector GEMV, M <= 8
+// The 8-bit kernel's mapping: a wave owns R rows (gated: gate row n and up row n + N/2),
+// lane l walks 32-channel chunks c = l, l + 64, ...; chunk c's codes are low-plane words
+// 12 (c / 4) + 2 (c % 4) and + 1 (one 8-byte load) and high-plane word 12 (c / 4) + 8 + c % 4.
+// v_dot2 with the activation pair accumulates in fp32; the group scale multiplies each
+// chunk's partial in fp32.
+template <int M, int R, bool GATED>
+__global__ void __launch_bounds__(256)
+    k_gemv3(const uint16_t* __restrict__ X, const uint32_t* __restrict__ qweight,
+            const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zeros, int64_t N,
+            int64_t K, int gsh, uint16_t* __restrict__ Y) {
+  static_assert(!GATED || R == 2, "a gated wave owns one gate row and one up row");
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nh = N / 2;
+  const int64_t row0 = GATED ? wave : wave * R;
+  if (row0 >= (GATED ? nh : N)) return;  // whole wave leaves together
+  const int64_t C = K / 32;              // chunks per row
+  const int64_t G = K >> (gsh + 5);      // groups per row
+  const int64_t zb = (G + 1) / 2;        // zero bytes per row
+  const int64_t words = K * 3 / 32;
+  const uint32_t magic = magic_6400();
+
+  int64_t rows[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    rows[r] = GATED ? row0 + r * nh : ((row0 + r < N) ? row0 + r : N - 1);
+
+  float acc[R][M];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+
+  for (int64_t c = lane; c < C; c += 64) {
+    const int64_t g = c >> gsh;  // group of this 32-channel chunk
+    half2v qz[R][16];            // pair p = channels (2p, 2p + 1) of the chunk, as q - z
+    float sc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t* wp = qweight + rows[r] * words + (c >> 2) * 12;
+      const uint2 lo = *reinterpret_cast<const uint2*>(wp + 2 * (c & 3));
+      const uint32_t hi = wp[8 + (c & 3)];
+      sc[r] = h2f(scales[rows[r] * G + g]);
+      const uint32_t zbits = 0x6400u + zero_nibble(zeros + rows[r] * zb, g);  // fp16 of 1024 + z
+      const half2v zz = -__builtin_bit_cast(half2v, zbits | (zbits << 16));
+#pragma unroll
+      for (int p = 0; p < 16; ++p)
+        qz[r][p] = __builtin_bit_cast(half2v, widen3(p < 8 ? lo.x : lo.y, hi, p, magic)) + zz;
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const uint4* xp = reinterpret_cast<const uint4*>(X + (int64_t)m * K + c * 32);
+      half2v xq[16];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint4 v = xp[w];  // channels 8w .. 8w + 7 as the pairs (0,1) (2,3) (4,5) (6,7)
+        xq[w * 4 + 0] = __builtin_bit_cast(half2v, v.x);
+        xq[w * 4 + 1] = __builtin_bit_cast(half2v, v.y);
+        xq[w * 4 + 2] = __builtin_bit_cast(half2v, v.z);
+        xq[w * 4 + 3] = __builtin_bit_cast(half2v, v.w);
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float part = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) part = __builtin_amdgcn_fdot2(qz[r][i], xq[i], part, false);
+        acc[r][m] = __builtin_fmaf(sc[r], part, acc[r][m]);
+      }
+    }
+  }
+
+  if constexpr (GATED) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const float g = wave_sum(acc[0][m]), u = wave_sum(acc[R - 1][m]);
+      if (lane == 0) Y[(int64_t)m * nh + row0] = f2h_bits(silu_f32(g) * u);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const float v = wave_sum(acc[r][m]);
+        if (lane == 0 && row0 + r < N) Y[(int64_t)m * N + row0 + r] = f2h_bits(v);
+      }
+  }
+}
+
+// ------------------------------------------------------------------ skinny MFMA, M <= 32
+// The 4-bit skinny kernel's mapping: a wave owns 32 weight rows and a slice of the
+// 128-channel steps; lane l takes row l % 32 and, with h = l / 32, the 32-channel chunks h
+// and 2 + h of each step (channels [32 h, 32 h + 32) and [64 + 32 h, 96 + 32 h)). Chunk ch
+// is low-plane words 2 ch, 2 ch + 1 and high-plane word 8 + ch of the step. k16 slice s
+// takes 8 channels of chunk h + 2 (s / 4): pairs 4 (s % 4) .. 4 (s % 4) + 3. Scales as in
+// the 4-bit kernel: a fresh partial tile per group (one per step for 128-channel groups, one
+// per half for 64), and for 32-channel groups, where the two lane halves of a slice lie in
+// different groups, the fp16 operand carries the scale.
+namespace {
+
+struct SkinnyStage3 {
+  uint2 lo[2];         // low-plane words of chunks h and 2 + h
+  uint32_t hi[2];      // their high-plane words
+  uint4 a[8];          // X[token][same channels], one 16-byte piece per k16 step
+  uint32_t sc[2], zb;  // scales and zero nibbles of the lane's two chunks
+};
+
+// Slice s: pairs 4 (s % 4) .. 4 (s % 4) + 3 of chunk half = s / 4.
+__device__ __forceinline__ half8 operand3(const SkinnyStage3& st, int s, half2v zz, uint32_t magic) {
+  const int half = s >> 2, p0 = 4 * (s & 3);
+  const uint32_t lo = (p0 < 8) ? st.lo[half].x : st.lo[half].y;
+  const half2v d0 = __builtin_bit_cast(half2v, widen3(lo, st.hi[half], p0 + 0, magic)) + zz;
+  const half2v d1 = __builtin_bit_cast(half2v, widen3(lo, st.hi[half], p0 + 1, magic)) + zz;
+  const half2v d2 = __builtin_bit_cast(half2v, widen3(lo, st.hi[half], p0 + 2, magic)) + zz;
+  const half2v d3 = __builtin_bit_cast(half2v, widen3(lo, st.hi[half], p0 + 3, magic)) + zz;
+  return half8{d0[0], d0[1], d1[0], d1[1], d2[0], d2[1], d3[0], d3[1]};
+}
+
+}  // namespace
+
+template <int S, int E, bool GATED>
+__global__ void __launch_bounds__(S * 64)
+    k_gemv_mfma3(const uint16_t* X, int64_t M, const uint32_t* qweight, const uint16_t* scales,
+                 const uint8_t* zeros, int64_t N, int64_t K, int group, uint16_t* Y) {
+  __shared__ float red[S][E][64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int j = lane & 31, h = lane >> 5;
+  const int lg = group == 128 ? 7 : group == 64 ? 6 : 5;
+  const bool g128 = group == 128, g32 = group == 32;
+  const int64_t G = K / kGroup;                          // 128-channel steps
+  const int64_t Gs = K / group, zbr = (Gs + 1) / 2;      // groups, zero bytes per row
+  const int64_t words = K * 3 / 32;
+  const int64_t nh = N / 2;
+  int64_t n;
+  if constexpr (GATED) {
+    const int64_t o = (int64_t)blockIdx.x * 16 + (j & 15);
+    n = (o < nh ? o : nh - 1) + (j >> 4) * nh;
+  } else {
+    const int64_t o = (int64_t)blockIdx.x * 32 + j;
+    n = o < N ? o : N - 1;
+  }
+  const int64_t xrow = (j < M ? j : M - 1) * K;
+  const int64_t g0 = G * wave / S, g1 = G * (wave + 1) / S;
+  const uint32_t magic = magic_6400();
+  const uint8_t* zrow = zeros + n * zbr;
+
+  auto load = [&](SkinnyStage3& st, int64_t g) {
+    const int64_t q0 = (g * kGroup + 32 * h) >> lg, q1 = (g * kGroup + 64 + 32 * h) >> lg;
+    st.zb = zero_nibble(zrow, q0) | (zero_nibble(zrow, q1) << 8);
+    st.sc[0] = scales[n * Gs + q0];
+    st.sc[1] = scales[n * Gs + q1];
+    const uint32_t* wp = qweight + n * words + g * 12;
+    st.lo[0] = *reinterpret_cast<const uint2*>(wp + 2 * h);
+    st.lo[1] = *reinterpret_cast<const uint2*>(wp + 4 + 2 * h);
+    st.hi[0] = wp[8 + h];
+    st.hi[1] = wp[10 + h];
+    const uint16_t* xp = X + xrow + g * kGroup + h * 32;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) st.a[s] = *reinterpret_cast<const uint4*>(xp + (s & 3) * 8 + (s >> 2) * 64);
+  };
+
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.0f;
+
+  auto body = [&](const SkinnyStage3& st) {
+    half2v zz[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const uint32_t zbits = 0x6400u + ((st.zb >> (8 * half)) & 0xFF);
+      zz[half] = -__builtin_bit_cast(half2v, zbits | (zbits << 16));
+    }
+    if (g32) {
+      f32x16 d = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const uint32_t sb = st.sc[s >> 2];
+        const half2v s2 = __builtin_bit_cast(half2v, sb | (sb << 16));
+        d = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+            __builtin_bit_cast(half8, st.a[s]),
+            operand3(st, s, zz[s >> 2], magic) * half8{s2[0], s2[1], s2[0], s2[1], s2[0], s2[1], s2[0], s2[1]},
+            d, 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] += d[e];
+    } else if (g128) {
+      f32x16 d = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        d = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, st.a[s]),
+                                                   operand3(st, s, zz[s >> 2], magic), d, 0, 0, 0);
+      const float scf = h2f((uint16_t)st.sc[0]);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(scf, d[e], acc[e]);
+    } else {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        f32x16 d = f32x16{};
+#pragma unroll
+        for (int s = 4 * half; s < 4 * half + 4; ++s)
+          d = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, st.a[s]),
+                                                     operand3(st, s, zz[half], magic), d, 0, 0, 0);
+        const float scf = h2f((uint16_t)st.sc[half]);
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(scf, d[e], acc[e]);
+      }
+    }
+  };
+
+  if (g1 > g0) {
+    SkinnyStage3 s0, s1;
+    load(s0, g0);
+    int64_t g = g0;
+    for (; g + 2 <= g1; g += 2) {
+      load(s1, g + 1);
+      body(s0);
+      load(s0, g + 2 < g1 ? g + 2 : g1 - 1);  // always issued: exact waits on every path
+      body(s1);
+    }
+    if (g < g1) body(s0);
+  }
+
+#pragma unroll
+  for (int e = 0; e < E; ++e) red[wave][e][lane] = acc[e];
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    float v = red[0][e][lane];
+#pragma unroll
+    for (int w = 1; w < S; ++w) v += red[w][e][lane];
+    acc[e] = v;
+  }
+  // 32x32 accumulator layout: element e of lane l is (row 8(e/4) + 4(l/32) + e%4, col l%32)
+  if constexpr (GATED) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float u = __shfl_down(acc[e], 16, 32);
+      const int64_t o = (int64_t)blockIdx.x * 16 + j;
+      const int64_t i = 8 * (e >> 2) + 4 * h + (e & 3);
+      if (j < 16 && o < nh && i < M) Y[i * nh + o] = f2h_bits(silu_f32(acc[e]) * u);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int64_t o = (int64_t)blockIdx.x * 32 + j;
+      const int64_t i = 8 * (e >> 2) + 4 * h + (e & 3);
+      if (o < N && i < M) Y[i * N + o] = f2h_bits(acc[e]);
+    }
+  }
+}
+
+template <int S, int E, bool GATED>
+static hipError_t launch_skinny3_x(const uint16_t* X, int64_t M, const uint32_t* qw,
+                                   const uint16_t* sc, const uint8_t* z, int64_t N, int64_t K,
+                                   int group, uint16_t* Y, hipStream_t stream) {
+  const int64_t outs = GATED ? N / 2 : N;
+  const int64_t per = GATED ? 16 : 32;
+  const int64_t blocks = (outs + per - 1) / per;
+  hipLaunchKernelGGL((k_gemv_mfma3<S, E, GATED>), dim3((unsigned)blocks), dim3(S * 64), 0, stream,
+                     X, M, qw, sc, z, N, K, group, Y);
+  return hipGetLastError();
+}
+
+template <bool GATED>
+static hipError_t launch_skinny3_t(const uint16_t* X, int64_t M, const uint32_t* qw,
+                                   const uint16_t* sc, const uint8_t* z, int64_t N, int64_t K,
+                                   int group, uint16_t* Y, hipStream_t stream) {
+  if (M <= 8) return launch_skinny3_x<8, 4, GATED>(X, M, qw, sc, z, N, K, group, Y, stream);
+  if (M <= 16) return launch_skinny3_x<8, 8, GATED>(X, M, qw, sc, z, N, K, group, Y, stream);
+  return launch_skinny3_x<8, 16, GATED>(X, M, qw, sc, z, N, K, group, Y, stream);
+}
+
+hipError_t launch_gemv_mfma3(const uint16_t* X, int64_t M, const uint32_t* qweight,
+                             const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
+                             int group, uint16_t* Y, bool gated, hipStream_t stream) {
+  if (M < 1 || M > kSkinnyMaxM) return hipErrorInvalidValue;
+  return gated ? launch_skinny3_t<true>(X, M, qweight, scales, zeros, N, K, group, Y, stream)
+               : launch_skinny3_t<false>(X, M, qweight, scales, zeros, N, K, group, Y, stream);
+}
+
+template <int M, bool GATED>
+static hipError_t launch_gemv3_m(const uint16_t* X, const uint32_t* qw, const uint16_t* sc,
+                                 const uint8_t* z, int64_t N, int64_t K, int gsh, uint16_t* Y,
+                                 hipStream_t stream) {
+  constexpr int R = GATED ? 2 : (M <= 2 ? 2 : 4);
+  const int64_t waves = GATED ? N / 2 : (N + R - 1) / R;
+  const int64_t blocks = (waves + 3) / 4;
+  hipLaunchKernelGGL((k_gemv3<M, R, GATED>), dim3((unsigned)blocks), dim3(256), 0, stream, X, qw,
+                     sc, z, N, K, gsh, Y);
+  return hipGetLastError();
+}
+
+template <bool GATED>
+static hipError_t launch_gemv3_t(const uint16_t* X, int64_t M, const uint32_t* qw,
+                                 const uint16_t* sc, const uint8_t* z, int64_t N, int64_t K,
+                                 int gsh, uint16_t* Y, hipStream_t stream) {
+  switch (M) {
+    case 1: return launch_gemv3_m<1, GATED>(X, qw, sc, z, N, K, gsh, Y, stream);
+    case 2: return launch_gemv3_m<2, GATED>(X, qw, sc, z, N, K, gsh, Y, stream);
+    case 3: return launch_gemv3_m<3, GATED>(X, qw, sc, z, N, K, gsh, Y, stream);
+    case 4: return launch_gemv3_m<4, GATED>(X, qw, sc, z, N, K, gsh, Y, stream);
+    case 5: return launch_gemv3_m<5, GATED>(X, qw, sc, z, N, K, gsh, Y, stream);
+    case 6: return launch_gemv3_m<6, GATED>(X, qw, sc, z, N, K, gsh, Y, stream);
+    case 7: return launch_gemv3_m<7, GATED>(X, qw, sc, z, N, K, gsh, Y, stream);
+    case 8: return launch_gemv3_m<8, GATED>(X, qw, sc, z, N, K, gsh, Y, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_gemv3(const uint16_t* X, int64_t M, const uint32_t* qweight,
+                        const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
+                        int group, uint16_t* Y, bool gated, hipStream_t stream) {
+  const int gsh = group == 128 ? 2 : group == 64 ? 1 : 0;  // chunk c (32 channels) is in group c >> gsh
+  return gated ? launch_gemv3_t<true>(X, M, qweight, scales, zeros, N, K, gsh, Y, stream)
+               : launch_gemv3_t<false>(X, M, qweight, scales, zeros, N, K, gsh, Y, stream);
+}
+
+}  // namespace awq

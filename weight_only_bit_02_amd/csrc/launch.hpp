@@ -69,6 +69,14 @@ hipError_t launch_gemv8(const uint16_t* X, int64_t M, const uint32_t* qweight,
 hipError_t launch_gemv_mfma8(const uint16_t* X, int64_t M, const uint32_t* qweight,
                              const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
                              int group, uint16_t* Y, bool gated, hipStream_t stream);
+// 3-bit codes (two bit planes per 128-channel block): the vector GEMV (M <= 8) and the
+// skinny MFMA GEMV (M <= kSkinnyMaxM), plain or gated.
+hipError_t launch_gemv3(const uint16_t* X, int64_t M, const uint32_t* qweight,
+                        const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
+                        int group, uint16_t* Y, bool gated, hipStream_t stream);
+hipError_t launch_gemv_mfma3(const uint16_t* X, int64_t M, const uint32_t* qweight,
+                             const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
+                             int group, uint16_t* Y, bool gated, hipStream_t stream);
 hipError_t launch_gemv(const uint16_t* X, int64_t M, const uint32_t* qweight,
                        const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
                        int group, uint16_t* Y, bool gated, hipStream_t stream);

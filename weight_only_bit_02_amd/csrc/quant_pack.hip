@@ -1,5 +1,7 @@
-// Quantize + pack (a3 + a4): one pass over W, HBM-bound. 4-bit codes (the format measured)
-// or 8-bit ones (same quantizer with 255 levels, two natural-order words per lane).
+// Quantize + pack (a3 + a4): one pass over W, HBM-bound. 4-bit codes (the format measured),
+// 8-bit ones (same quantizer with 255 levels, two natural-order words per lane) or 3-bit
+// ones (7 levels; a lane pair ORs its shares into one low-plane word, a lane quad into one
+// high-plane word).
 //
 // "AWQ量化实战" §2.3: 128 consecutive input channels share one quantization step;
 // "大模型量化部署实战：GPTQ与AWQ算法", "大模型量化的核心原理与位宽选择": a 4-bit integer with a
@@ -35,8 +37,9 @@ __global__ void __launch_bounds__(256) k_quant_pack(const uint16_t* __restrict__
   const int li = lane & (gl - 1);     // lane within the group
   const int64_t G = K / group;
   const int64_t chunks = (G + gpu - 1) / gpu;
-  const bool w8 = w_bit == 8;
-  const float qmax = w8 ? 255.0f : 15.0f;
+  const bool w8 = w_bit == 8, w3 = w_bit == 3;
+  const float qmax = (float)((1 << w_bit) - 1);
+  const int64_t words = K * w_bit / 32;  // packed words per row
   const int64_t zbytes = w8 ? G : (G + 1) / 2;  // 8-bit: one zero byte per group
   // unit u = (row n, chunk ch) = n * chunks + ch; the wave walks u = wave0, wave0 + nwaves,
   // ... with (n, ch) stepped incrementally (wave-uniform, no division in the loop)
@@ -87,6 +90,17 @@ __global__ void __launch_bounds__(256) k_quant_pack(const uint16_t* __restrict__
     float qc[8];
     quant_codes(w, g, qc);
 
+    // 3-bit: this lane's 8 channels are half of a low-plane word (16 channels) and a
+    // quarter of a high-plane word (32 channels); the OR across lanes completes both
+    uint32_t lo3 = 0, hi3 = 0;
+    if (w3) {
+      planes3(qc, lo3, hi3);
+      lo3 <<= 8 * (lane & 1);
+      hi3 <<= 4 * (lane & 3);
+      lo3 |= (uint32_t)__shfl_xor((int)lo3, 1);
+      hi3 |= (uint32_t)__shfl_xor((int)hi3, 1);
+      hi3 |= (uint32_t)__shfl_xor((int)hi3, 2);
+    }
     const uint32_t zi = (uint32_t)g.z;
     const uint32_t z_next = (uint32_t)__shfl_down((int)zi, gl);  // zero of group j + 1
     if (valid) {
@@ -96,6 +110,12 @@ __global__ void __launch_bounds__(256) k_quant_pack(const uint16_t* __restrict__
         wd8.x = pack_bytes4(qc[0], qc[1], qc[2], qc[3]);
         wd8.y = pack_bytes4(qc[4], qc[5], qc[6], qc[7]);
         reinterpret_cast<uint2*>(qweight)[(n * K + k0) >> 3] = wd8;
+      } else if (w3) {
+        // block k0 / 128 holds words 12 b .. 12 b + 11: 8 low-plane words, then 4 high
+        const int64_t wb = n * words + (k0 >> 7) * 12;
+        const int c0 = (int)(k0 & 127);
+        if ((lane & 1) == 0) qweight[wb + (c0 >> 4)] = lo3;
+        if ((lane & 3) == 0) qweight[wb + 8 + (c0 >> 5)] = hi3;
       } else {
         qweight[(n * K + k0) >> 3] = pack_codes8(qc);
       }

@@ -275,7 +275,7 @@ __global__ void __launch_bounds__(NW * 64)
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int64_t n0 = ntile * kRowTile;
-  const float qmax = w_bit == 8 ? 255.0f : 15.0f;
+  const float qmax = (float)((1 << w_bit) - 1);
   const int64_t G = K / kGroup;
   const uint16_t* s = s_grid + (int64_t)alpha * K;
   const int64_t tchunk = (int64_t)NW * kTokPerWave;
@@ -408,7 +408,7 @@ __global__ void __launch_bounds__(NW * 64)
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int64_t n0 = ntile * kRowTile;
-  const float qmax = w_bit == 8 ? 255.0f : 15.0f;
+  const float qmax = (float)((1 << w_bit) - 1);
   const int gps = kGroup / group;  // groups per 128-channel step: 1, 2 or 4
   const int per = 8 / gps;         // k16 slices per group: 8, 4 or 2
   const int64_t G = K / kGroup;    // 128-channel steps
