@@ -98,6 +98,9 @@ def test_clip_search_and_clipped_pack(T, N, K, n_shrink, group):
     (1, 96, 384, "gemv", 128),
     (1, 200, 4096, "gemv", 64),
     (1, 77, 11008, "gemv", 32),
+    (1, 8193, 512, "gemv", 64),        # two rows per wave, ragged last wave
+    (1, 130, 16384, "gemv", 128),      # eight chunks per lane
+    (1, 33, 16512, "gemv", 32),        # K above the single-token kernel's range
     (3, 130, 4096, "gemv", 128),
     (8, 67, 1152, "gemv", 64),
     (1, 100, 4096, "skinny", 128),
@@ -123,6 +126,7 @@ def test_linear_kernels(M, N, K, kernel, group):
 
 @pytest.mark.parametrize("M,nh,K,kernel,group", [
     (1, 96, 4096, "gemv", 128),
+    (1, 4100, 11008, "gemv", 64),
     (4, 67, 1152, "gemv", 32),
     (12, 80, 4096, "skinny", 64),
     (70, 130, 1152, "gemm", 128),
@@ -157,3 +161,6 @@ def test_dequant_identity_rows(group):
     for i0 in range(0, len(ks), 8):
         Y = host(awq.linear_w4a16(to_dev(X[i0:i0 + 8]), p, kernel="gemv"))
         assert np.array_equal(Y.view(np.uint16), want[i0:i0 + 8].view(np.uint16))
+    for i in range(len(ks)):  # one token: the single-token kernel
+        Y = host(awq.linear_w4a16(to_dev(X[i:i + 1]), p, kernel="gemv"))
+        assert np.array_equal(Y.view(np.uint16), want[i:i + 1].view(np.uint16))

@@ -34,6 +34,38 @@ __device__ __forceinline__ uint32_t widen3(uint32_t lo, uint32_t hi, int p, uint
   return ((lo >> (2 * (p & 7))) & 0x00030003u) | (h & 0x00040004u) | magic;
 }
 
+// Sum over the 16 pairs of a chunk of x * (q - z), with the low-plane field masked in place:
+// pair p = 4 a + e (e = p % 4) reads its 2 low bits at bits 2e, 2e + 1 of low word a / 2,
+// shifted right by 8 for odd a (one shift per 4 pairs), and its high bit moved to bit 2e + 2
+// (one shift) and merged by a bit-field insert, so the fp16 half is 1024 + 4^e q, exactly
+// (4^3 * 7 < 1024). Subtracting 1024 + 4^e z leaves 4^e (q - z), exact; the pairs of each e
+// accumulate in their own fp32 partial, whose power-of-two factor is removed at the end (it
+// commutes with every rounding, so each partial equals its unscaled sum).
+__device__ __forceinline__ float chunk_dot3(uint2 lo, uint32_t hi, uint32_t z, const half2v (&xq)[16],
+                                            uint32_t magic) {
+  const uint32_t lw[4] = {lo.x, lo.x >> 8, lo.y, lo.y >> 8};
+  half2v zz[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t zb = 0x6400u + (z << (2 * e));  // fp16 of 1024 + 4^e z
+    zz[e] = -__builtin_bit_cast(half2v, zb | (zb << 16));
+  }
+  float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    const int e = p & 3, sh = p - 2 * e - 2;  // high bit p -> bit 2e + 2
+    const uint32_t hm = 0x00040004u << (2 * e);
+    const uint32_t hs = sh > 0 ? (hi >> sh) : sh < 0 ? (hi << -sh) : hi;
+    // (low word & field mask) | magic, then the high bit inserted: one VALU op each (the
+    // compiler otherwise spends an AND on each operand and an OR3)
+    uint32_t lm, u;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(lm) : "v"(lw[p >> 2]), "s"(0x00030003u << (2 * e)), "v"(magic));
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(u) : "s"(hm), "v"(hs), "v"(lm));
+    part[e] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, u) + zz[e], xq[p], part[e], false);
+  }
+  return part[0] + part[1] * 0.25f + part[2] * 0.0625f + part[3] * 0.015625f;
+}
+
 __device__ __forceinline__ uint32_t zero_nibble(const uint8_t* zrow, int64_t g) {
   return ((uint32_t)zrow[g >> 1] >> (4 * (g & 1))) & 0xFu;
 }
@@ -127,6 +159,94 @@ __global__ void __launch_bounds__(256)
         if (lane == 0 && row0 + r < N) Y[(int64_t)m * N + row0 + r] = f2h_bits(v);
       }
   }
+}
+
+// ------------------------------------------------------------------ M = 1, K <= 16384
+// The single-token structure of the 4-bit decode kernel: 4 waves per block share the
+// activation row through LDS; each wave owns RPW rows (gated: gate row n and up row
+// n + N/2) and issues every code load of its rows (U chunks per lane, covering K) before
+// any arithmetic, so a lane keeps U * RPW * 12 bytes in flight. Scheduler barriers keep
+// the activation loads first: the wait for them (in-order load counter) leaves the codes in
+// flight, and the LDS-only barrier shares the row without waiting for the codes. Every lane
+// stores lane 0's sum; a row index past the matrix end is clamped to the wave's last row,
+// whose value it rewrites.
+template <int U, int RPW, bool GATED>
+__global__ void __launch_bounds__(256)
+    k_gemv3_1(const uint16_t* X, const uint32_t* qweight, const uint16_t* scales,
+              const uint8_t* zeros, int64_t N, int64_t K, int gsh, uint16_t* Y) {
+  static_assert(!GATED || RPW == 2, "a gated wave owns one gate row and one up row");
+  extern __shared__ uint4 xs[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int64_t wave_id = (int64_t)blockIdx.x * 4 + (tid >> 6);
+  const int64_t C = K / 32, G = K >> (gsh + 5), zbytes = (G + 1) / 2, words = K * 3 / 32;
+  const int64_t xw = K / 8;  // 16-byte pieces of the activation row
+  const int64_t nh = N / 2;
+  const int64_t n_out = wave_id < nh ? wave_id : nh - 1;
+  const int64_t row0 = GATED ? n_out : wave_id * RPW;
+  const int64_t lastrow = row0 + RPW - 1 < N ? row0 + RPW - 1 : N - 1;
+  auto row_at = [&](int r) -> int64_t {
+    if constexpr (GATED) return n_out + r * nh;
+    const int64_t v = row0 + r;
+    return v < lastrow ? v : lastrow;
+  };
+
+  uint4 v[U];
+#pragma unroll
+  for (int j = 0; j < U; ++j) {
+    const int64_t i = j * 256 + tid;
+    v[j] = *reinterpret_cast<const uint4*>(X + (i < xw ? i : xw - 1) * 8);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  uint2 lo[RPW][U];
+  uint32_t hi[RPW][U];
+  uint16_t sc[RPW][U];
+  uint8_t zb[RPW][U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    int64_t c = u * 64 + lane;
+    c = c < C ? c : C - 1;  // results past the row end are loaded but unused
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int64_t row = row_at(r);
+      const uint32_t* wp = qweight + row * words + (c >> 2) * 12;
+      lo[r][u] = *reinterpret_cast<const uint2*>(wp + 2 * (c & 3));
+      hi[r][u] = wp[8 + (c & 3)];
+      sc[r][u] = scales[row * G + (c >> gsh)];
+      zb[r][u] = zeros[row * zbytes + (c >> (gsh + 1))];
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < U; ++j) xs[j * 256 + tid] = vgpr_copy(v[j]);  // U * 256 >= K / 8 entries
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // LDS only: codes stay in flight
+
+  const uint32_t magic = magic_6400();
+  float sums[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = u * 64 + lane;
+      if (c < C) {
+        half2v xq[16];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint4 xv = xs[c * 4 + w];  // channels 8w .. 8w + 7 as pairs
+          xq[w * 4 + 0] = __builtin_bit_cast(half2v, xv.x);
+          xq[w * 4 + 1] = __builtin_bit_cast(half2v, xv.y);
+          xq[w * 4 + 2] = __builtin_bit_cast(half2v, xv.z);
+          xq[w * 4 + 3] = __builtin_bit_cast(half2v, xv.w);
+        }
+        const uint32_t z = ((uint32_t)zb[r][u] >> (4 * ((c >> gsh) & 1))) & 0xFu;
+        acc = __builtin_fmaf(h2f(sc[r][u]), chunk_dot3(lo[r][u], hi[r][u], z, xq, magic), acc);
+      }
+    }
+    sums[r] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_sum(acc)), 0));
+    if constexpr (!GATED) Y[row_at(r)] = f2h_bits(sums[r]);
+  }
+  if constexpr (GATED) Y[n_out] = f2h_bits(silu_f32(sums[0]) * sums[RPW - 1]);
 }
 
 // ------------------------------------------------------------------ skinny MFMA, M <= 32
@@ -352,10 +472,50 @@ static hipError_t launch_gemv3_t(const uint16_t* X, int64_t M, const uint32_t* q
   }
 }
 
+template <int U, int RPW, bool GATED>
+static hipError_t launch_gemv3_1x(const uint16_t* X, const uint32_t* qw, const uint16_t* sc,
+                                  const uint8_t* z, int64_t N, int64_t K, int gsh, uint16_t* Y,
+                                  hipStream_t stream) {
+  const int64_t waves = GATED ? N / 2 : (N + RPW - 1) / RPW;
+  const int64_t blocks = (waves + 3) / 4;
+  hipLaunchKernelGGL((k_gemv3_1<U, RPW, GATED>), dim3((unsigned)blocks), dim3(256),
+                     (size_t)U * 256 * 16, stream, X, qw, sc, z, N, K, gsh, Y);
+  return hipGetLastError();
+}
+
+// M = 1 with U = ceil(K / 2048) <= 8 chunks per lane: two rows per wave for tall matrices
+// (and always when gated), else one.
+template <bool GATED>
+static hipError_t launch_gemv3_1(const uint16_t* X, const uint32_t* qw, const uint16_t* sc,
+                                 const uint8_t* z, int64_t N, int64_t K, int gsh, uint16_t* Y,
+                                 hipStream_t stream) {
+  const int64_t U = (K / 32 + 63) / 64;
+  const bool two = GATED || N >= 8192;
+#define AWQ_GEMV3_1(u)                                                                   \
+  case u:                                                                                \
+    return two ? launch_gemv3_1x<u, 2, GATED>(X, qw, sc, z, N, K, gsh, Y, stream)        \
+               : launch_gemv3_1x<u, 1, false>(X, qw, sc, z, N, K, gsh, Y, stream);
+  switch (U) {
+    AWQ_GEMV3_1(1)
+    AWQ_GEMV3_1(2)
+    AWQ_GEMV3_1(3)
+    AWQ_GEMV3_1(4)
+    AWQ_GEMV3_1(5)
+    AWQ_GEMV3_1(6)
+    AWQ_GEMV3_1(7)
+    AWQ_GEMV3_1(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef AWQ_GEMV3_1
+}
+
 hipError_t launch_gemv3(const uint16_t* X, int64_t M, const uint32_t* qweight,
                         const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
                         int group, uint16_t* Y, bool gated, hipStream_t stream) {
   const int gsh = group == 128 ? 2 : group == 64 ? 1 : 0;  // chunk c (32 channels) is in group c >> gsh
+  if (M == 1 && K <= 16384)
+    return gated ? launch_gemv3_1<true>(X, qweight, scales, zeros, N, K, gsh, Y, stream)
+                 : launch_gemv3_1<false>(X, qweight, scales, zeros, N, K, gsh, Y, stream);
   return gated ? launch_gemv3_t<true>(X, M, qweight, scales, zeros, N, K, gsh, Y, stream)
                : launch_gemv3_t<false>(X, M, qweight, scales, zeros, N, K, gsh, Y, stream);
 }
