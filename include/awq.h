@@ -231,9 +231,10 @@ awq_status awq_linear_w4a16_gated_silu_ex(const void* X, int64_t M, const uint32
  *   W fp16 [N][K]; s fp16 [K] or NULL; 1 <= n_shrink <= min(clip_steps, 256).
  *   clip_idx uint8 [N][G] out (pass to awq_quantize_pack_clipped); err fp64 [N][G]
  *   out, the chosen error, or NULL; G = K / group_size. workspace: device,
- *   awq_clip_search_workspace_size bytes (n_shrink N G doubles and a copy of X in MFMA
- *   operand order, T rounded up to 64 tokens; 0 for an unsupported config or shape, T
- *   included), 16-byte aligned. Accuracy: each group's D is scaled by a power of two
+ *   awq_clip_search_workspace_size bytes (the errors: n_shrink N G doubles for
+ *   128-channel groups, n_shrink N G w floats for smaller ones, w = 4 per-wave partials
+ *   for T <= 256, else 8; and a copy of X in MFMA operand order, T rounded up to 64
+ *   tokens; 0 for an unsupported config or shape, T included), 16-byte aligned. Accuracy: each group's D is scaled by a power of two
  *   from its own largest |D| before the fp16 hi + lo split, so every group keeps 22
  *   significant bits whatever its magnitude or the code width.
  *   flags: NONFINITE_INPUT (a NaN or Inf in W or s, or in X through a non-finite error).

@@ -153,6 +153,8 @@ def test_clip_validation(lib):
     assert lib.awq_clip_search_workspace_size(64, 64, 256, 20, C.byref(g64)) >= 20 * 64 * 4 * 8
     g32 = _abi.config(group_size=32)
     assert lib.awq_clip_search_workspace_size(64, 64, 256, 20, C.byref(g32)) >= 20 * 64 * 8 * 8
+    # 32-channel groups at T > 256: eight per-wave fp32 partials per error
+    assert lib.awq_clip_search_workspace_size(512, 64, 256, 20, C.byref(g32)) >= 20 * 64 * 8 * 4 * 8
     bad = _abi.config(group_size=16)
     assert lib.awq_clip_search_workspace_size(64, 64, 256, 20, C.byref(bad)) == 0
     assert lib.awq_quantize_pack_clipped(FAKE, 64, 256, None, FAKE, 0, None, FAKE, FAKE, FAKE,

@@ -170,6 +170,7 @@ def _check_choice(idx, err_best, ref_err):
     (64, 130, 256, 20, True, True),     # ragged row tile
     (37, 67, 384, 5, False, True),      # ragged tokens
     (512, 128, 1152, 10, True, False),  # eight waves of tokens, symmetric
+    (300, 96, 512, 7, True, True),      # eight waves, the last three without tokens
 ])
 def test_clip_search_and_clipped_pack(T, N, K, n_shrink, with_s, zp, group):
     X = si.activations(T, K, offset=T + N + 1)

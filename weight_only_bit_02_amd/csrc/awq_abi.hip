@@ -64,7 +64,7 @@ struct ClipLayout {
 ClipLayout clip_layout(int64_t T, int64_t N, int64_t K, int n_shrink, int group) {
   ClipLayout L;
   L.err = 0;
-  L.xp = align256(L.err + (size_t)n_shrink * N * (K / group) * 8);
+  L.xp = align256(L.err + awq::clip_err_bytes(T, N, K, n_shrink, group));
   L.total = align256(L.xp + awq::packed_x_bytes(T, K));
   return L;
 }
@@ -324,12 +324,12 @@ awq_status awq_clip_search(const void* X, int64_t T, const void* W, int64_t N, i
   if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return AWQ_ERR_WORKSPACE;
   char* ws = (char*)workspace;
   hipStream_t st = (hipStream_t)stream;
-  double* errs = (double*)(ws + L.err);
+  void* errs = ws + L.err;
   hipError_t e = awq::launch_clip_err((const uint16_t*)X, T, (const uint16_t*)W, N, K,
                                       (const uint16_t*)s, clip_steps, n_shrink, c.zero_point == 0,
                                       c.group_size, c.w_bit, (uint4*)(ws + L.xp), errs, flags, st);
   if (e == hipSuccess)
-    e = awq::launch_clip_reduce(errs, n_shrink, N, K / c.group_size, clip_idx, err, flags, st);
+    e = awq::launch_clip_reduce(errs, T, n_shrink, N, K, c.group_size, clip_idx, err, flags, st);
   return hip_status(e);
 }
 

@@ -21,13 +21,16 @@ hipError_t launch_quant_pack(const uint16_t* W, int64_t N, int64_t K, const uint
 // (T <= 512), then the first minimum per (n, g).
 hipError_t launch_clip_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N,
                            int64_t K, const uint16_t* s, int clip_steps, int n_shrink, bool sym,
-                           int group, int w_bit, uint4* xp, double* err, uint32_t* flags,
+                           int group, int w_bit, uint4* xp, void* err, uint32_t* flags,
                            hipStream_t stream);
+// Bytes of the clip search's error array: fp64 [n_shrink][N][G] for 128-channel groups;
+// for smaller ones the per-wave fp32 partials [n_shrink][G][waves][N] (4 or 8 waves by T).
+size_t clip_err_bytes(int64_t T, int64_t N, int64_t K, int n_shrink, int group);
 // Bytes of the MFMA-ordered copy of X (T tokens rounded up to 64, K channels) that the
 // scale and clip searches read their activations from.
 size_t packed_x_bytes(int64_t T, int64_t K);
-hipError_t launch_clip_reduce(const double* err, int n_shrink, int64_t N, int64_t G,
-                              uint8_t* clip_idx, double* err_best, uint32_t* flags,
+hipError_t launch_clip_reduce(const void* err, int64_t T, int n_shrink, int64_t N, int64_t K,
+                              int group, uint8_t* clip_idx, double* err_best, uint32_t* flags,
                               hipStream_t stream);
 constexpr int kClipMaxTokens = 512;
 constexpr int kClipMaxShrink = 256;

@@ -387,15 +387,17 @@ template <int NW>
 __global__ void __launch_bounds__(NW * 64)
     k_clip_err(const uint4* xp, int64_t T, const uint16_t* W, int64_t N, int64_t K,
                const uint16_t* s, int clip_steps, int n_shrink, int sym, int group, int w_bit,
-               double* __restrict__ err, uint32_t* __restrict__ flags, int64_t n_ntiles,
-               int64_t per_xcd) {
+               double* __restrict__ err, float* __restrict__ part, uint32_t* __restrict__ flags,
+               int64_t n_ntiles, int64_t per_xcd) {
   __shared__ __attribute__((aligned(16))) uint16_t lds_hi[2][kRowTile * kLdsStride];
   __shared__ __attribute__((aligned(16))) uint16_t lds_lo[2][kRowTile * kLdsStride];
   // power-of-two scale of each (row, group of the step), double-buffered with hi / lo
   __shared__ float lds_pg[2][kRowTile * 4];
-  // per-row partial errors of each wave: slot = step parity (128-channel groups; one
-  // barrier per step suffices) or the group's place in a pair (64- and 32-channel groups:
-  // both slots are filled, then stored and freed between two barriers)
+  // 128-channel groups: per-row partial errors of each wave, slot = step parity, summed
+  // over the waves after the end-of-step barrier (the one barrier per step). Smaller groups
+  // (two or four per step) would need 2 x 4 slots, more than the LDS left: each wave stores
+  // its partials of those groups to `part` instead, with no barrier, and the reduction
+  // kernel sums the waves.
   __shared__ double lds_red[2][NW][kRowTile];
 
   const int64_t t = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
@@ -439,10 +441,7 @@ __global__ void __launch_bounds__(NW * 64)
     if (set_b) quantize(jn, buf ^ 1);
     f32x16 acc[2][4];
     // the step's 8 k16 slices in quarters of two; a group spans per = 8, 4 or 2 slices and
-    // its error is taken when its last slice is done. Groups go through the two LDS slots:
-    // one group per step uses the slot of the step's parity (one barrier per step); two or
-    // four groups per step fill both slots, store them and free them (two barriers per pair)
-    int nred = 0, gdone = 0;
+    // its error is taken when its last slice is done
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       if ((2 * c) % per == 0) {
@@ -479,34 +478,28 @@ __global__ void __launch_bounds__(NW * 64)
         // the same column for different tokens). The lane's 32 squares are summed in fp32
         // (|acc| <= 65504 * 2^14 * 128, so no square overflows; the sum is within 32 * 2^-24
         // of exact), scaled by the exact power of two 1 / P^2 in fp64, and added across
-        // lanes and waves in fp64.
-        const int slot = gps == 1 ? buf : nred;
+        // the lane halves in fp64; across waves in fp64 too (LDS here, or the reduction
+        // kernel from fp32 partials, each within 2^-24 of its fp64 value).
+        const int gq = (2 * c + 2) / per - 1;  // group of the step
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          const double pinv = 1.0 / (double)lds_pg[buf][(b * 32 + m32) * 4 + (2 * c + 2) / per - 1];
+          // P = 2^(pe - 1) exactly, so the scaling by 1 / P^2 is an exponent change
+          int pe = 0;
+          (void)__builtin_frexpf(lds_pg[buf][(b * 32 + m32) * 4 + gq], &pe);
           float s32 = 0.0f;
 #pragma unroll
           for (int a = 0; a < 2; ++a)
 #pragma unroll
             for (int e = 0; e < 16; ++e) s32 = __builtin_fmaf(acc[a][b][e], acc[a][b][e], s32);
-          double ss = (double)s32 * (pinv * pinv);
+          double ss = __builtin_ldexp((double)s32, -2 * (pe - 1));
           ss += __shfl_xor(ss, 32);
-          if (khalf == 0) lds_red[slot][wave][b * 32 + m32] = ss;
-        }
-        ++nred;
-        if (gps > 1 && nred == 2) {
-          __syncthreads();
-          if (tid < kRowTile && n0 + tid < N) {
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-              double tot = lds_red[q][0][tid];
-              for (int w = 1; w < NW; ++w) tot += lds_red[q][w][tid];
-              err[((int64_t)ci * N + n0 + tid) * Gs + j * gps + gdone + q] = tot;
-            }
+          const int64_t row = n0 + b * 32 + m32;
+          if (gps == 1) {
+            if (khalf == 0) lds_red[buf][wave][b * 32 + m32] = ss;
+          } else if (khalf == 0 && row < N) {
+            // [ratio][group][wave][row]: a wave's 32 lanes store 128 consecutive bytes
+            part[(((int64_t)ci * Gs + j * gps + gq) * NW + wave) * N + row] = (float)ss;
           }
-          __syncthreads();
-          nred = 0;
-          gdone += 2;
         }
       }
     }
@@ -550,6 +543,38 @@ __global__ void __launch_bounds__(256)
   if (bad && flags) atomicOr(flags, AWQ_FLAG_NONFINITE_INPUT);
 }
 
+// Smaller groups: one thread per (group, row) (consecutive threads, consecutive rows: the
+// partial reads coalesce). err_i = sum of the nw wave partials in wave order, in fp64; then
+// the first minimum over the ratios, as above.
+__global__ void __launch_bounds__(256)
+    k_clip_reduce_waves(const float* __restrict__ part, int n_shrink, int64_t N, int64_t G,
+                        int nw, uint8_t* __restrict__ clip_idx, double* __restrict__ err_best,
+                        uint32_t* __restrict__ flags) {
+  const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (u >= N * G) return;
+  const int64_t g = u / N, row = u - g * N;
+  auto error = [&](int i) {
+    const float* p = part + ((int64_t)i * G + g) * nw * N + row;
+    double v = 0.0;
+    for (int w = 0; w < nw; ++w) v += (double)p[(int64_t)w * N];
+    return v;
+  };
+  double best = error(0);
+  int bi = 0;
+  bool bad = !__builtin_isfinite(best);
+  for (int i = 1; i < n_shrink; ++i) {
+    const double v = error(i);
+    bad |= !__builtin_isfinite(v);
+    if (v < best) {
+      best = v;
+      bi = i;
+    }
+  }
+  clip_idx[row * G + g] = (uint8_t)bi;
+  if (err_best) err_best[row * G + g] = best;
+  if (bad && flags) atomicOr(flags, AWQ_FLAG_NONFINITE_INPUT);
+}
+
 static hipError_t launch_pack_x(const uint16_t* X, int64_t T, int64_t K, uint4* xp,
                                 hipStream_t stream) {
   const int64_t tiles = (T + kTokPerWave - 1) / kTokPerWave;
@@ -563,30 +588,44 @@ size_t packed_x_bytes(int64_t T, int64_t K) {
   return (size_t)((T + kTokPerWave - 1) / kTokPerWave) * kTokPerWave * K * 2;
 }
 
+static int clip_waves(int64_t T) { return T <= 4 * kTokPerWave ? 4 : 8; }
+
+size_t clip_err_bytes(int64_t T, int64_t N, int64_t K, int n_shrink, int group) {
+  const size_t per = group == kGroup ? 8 : 4 * (size_t)clip_waves(T);  // fp64, or nw fp32 partials
+  return (size_t)n_shrink * N * (K / group) * per;
+}
+
 hipError_t launch_clip_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N,
                            int64_t K, const uint16_t* s, int clip_steps, int n_shrink, bool sym,
-                           int group, int w_bit, uint4* xp, double* err, uint32_t* flags,
+                           int group, int w_bit, uint4* xp, void* err, uint32_t* flags,
                            hipStream_t stream) {
   hipError_t e = launch_pack_x(X, T, K, xp, stream);
   if (e != hipSuccess) return e;
   const int64_t n_ntiles = (N + kRowTile - 1) / kRowTile;
   const int64_t per_xcd = (n_ntiles * n_shrink + kXcds - 1) / kXcds;
   const dim3 grid((unsigned)(per_xcd * kXcds));
-  if (T <= 4 * kTokPerWave)
+  double* e64 = (double*)err;
+  float* e32 = (float*)err;
+  if (clip_waves(T) == 4)
     hipLaunchKernelGGL(k_clip_err<4>, grid, dim3(256), 0, stream, xp, T, W, N, K, s, clip_steps,
-                       n_shrink, (int)sym, group, w_bit, err, flags, n_ntiles, per_xcd);
+                       n_shrink, (int)sym, group, w_bit, e64, e32, flags, n_ntiles, per_xcd);
   else
     hipLaunchKernelGGL(k_clip_err<8>, grid, dim3(512), 0, stream, xp, T, W, N, K, s, clip_steps,
-                       n_shrink, (int)sym, group, w_bit, err, flags, n_ntiles, per_xcd);
+                       n_shrink, (int)sym, group, w_bit, e64, e32, flags, n_ntiles, per_xcd);
   return hipGetLastError();
 }
 
-hipError_t launch_clip_reduce(const double* err, int n_shrink, int64_t N, int64_t G,
-                              uint8_t* clip_idx, double* err_best, uint32_t* flags,
+hipError_t launch_clip_reduce(const void* err, int64_t T, int n_shrink, int64_t N, int64_t K,
+                              int group, uint8_t* clip_idx, double* err_best, uint32_t* flags,
                               hipStream_t stream) {
-  const int64_t NG = N * G;
-  hipLaunchKernelGGL(k_clip_reduce, dim3((unsigned)((NG + 255) / 256)), dim3(256), 0, stream, err,
-                     n_shrink, NG, clip_idx, err_best, flags);
+  const int64_t G = K / group, NG = N * G;
+  const dim3 grid((unsigned)((NG + 255) / 256));
+  if (group == kGroup)
+    hipLaunchKernelGGL(k_clip_reduce, grid, dim3(256), 0, stream, (const double*)err, n_shrink, NG,
+                       clip_idx, err_best, flags);
+  else
+    hipLaunchKernelGGL(k_clip_reduce_waves, grid, dim3(256), 0, stream, (const float*)err, n_shrink,
+                       N, G, clip_waves(T), clip_idx, err_best, flags);
   return hipGetLastError();
 }
 
