@@ -103,8 +103,49 @@ def test_linear_7b_group(group, M):
     X = si.activations(M, K, offset=M, channel_offset=K)
     Y = host(awq.linear_w4a16(to_dev(X), p))
     rows = _rows_sample(N, 96 if M >= 64 else 256, seed=M)
+    ref = oracle.quantize_pack(W[rows])[:3]      # the oracle packs the sampled rows itself
     qw, sc, zb = packed_host(p)
-    _check_sampled_linear(X, p, (qw[rows], sc[rows], zb[rows]), rows, Y)
+    assert np.array_equal(qw[rows], ref[0]) and np.array_equal(zb[rows], ref[2])
+    assert np.array_equal(sc[rows].view(np.uint16), ref[1].view(np.uint16))
+    _check_sampled_linear(X, p, ref, rows, Y)
+
+
+# ----------------------------------------------------------------- format variants
+# Each variant as the benchmark times it (every variant packs the same weights with one
+# config field changed): pack bit-exact on sampled rows, and the decode (M = 1: fused
+# gate|up, down) and prefill (M = 2048: q|k|v) outputs of those rows against the oracle.
+VARIANTS = {"group64": {"group_size": 64}, "group32": {"group_size": 32},
+            "symmetric": {"zero_point": False}, "int8": {"w_bit": 8}, "int3": {"w_bit": 3}}
+
+
+@pytest.mark.parametrize("gname,M", [("gate_up", 1), ("down", 1), ("qkv", 2048)])
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_variant_7b_pack_and_linear(variant, gname, M):
+    kw = VARIANTS[variant]
+    group, w_bit, zp = kw.get("group_size", 128), kw.get("w_bit", 4), kw.get("zero_point", True)
+    N, K = GROUPS_7B[gname]
+    W = _weights(N, K, 7)
+    a, _ = oracle.activation_mean_abs(si.activations(64, K, offset=3))
+    s = oracle.candidate_scales(a, 20)[1][9]
+    p = awq.quantize_pack(to_dev(W), to_dev(s), zero_point=zp, group_size=group, w_bit=w_bit)
+    X = si.activations(M, K, offset=M + 1, channel_offset=K)
+    qw, sc, zb = packed_host(p)
+    if gname == "gate_up":  # fused module: output j reads gate row j and up row j + N/2
+        nh = N // 2
+        outs = _rows_sample(nh, 96, seed=5)
+        rows = np.concatenate([outs, outs + nh])
+    else:
+        outs = rows = _rows_sample(N, 64 if M > 1 else 128, seed=6)
+    ref = oracle.quantize_pack(W[rows], s, None, zp, group, w_bit)[:3]
+    assert np.array_equal(qw[rows], ref[0]) and np.array_equal(zb[rows], ref[2])
+    assert np.array_equal(sc[rows].view(np.uint16), ref[1].view(np.uint16))
+    if gname == "gate_up":
+        H = host(awq.linear_w4a16_gated_silu(to_dev(X), p))
+        h, g, u, bg, bu = oracle.gated_silu_reference(X, *ref, K)
+        assert oracle.gated_silu_within_tolerance(H[:, outs], g, u, bg, bu).all()
+    else:
+        Y = host(awq.linear_w4a16(to_dev(X), p))
+        _check_sampled_linear(X, p, ref, rows, Y)
 
 
 def test_linear_7b_per_matrix_row_slices():

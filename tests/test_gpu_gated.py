@@ -89,6 +89,9 @@ def test_gated_7b_gate_up_sampled(M):
     cols = np.unique(np.concatenate([[0, nh - 1], np.random.default_rng(M).choice(nh, 96, replace=False)]))
     qw, sc, zb = packed_host(p)
     rows = np.concatenate([cols, nh + cols])
-    h, g, u, bg, bu = oracle.gated_silu_reference(X, qw[rows], sc[rows], zb[rows], K)
+    ref = oracle.quantize_pack(W[rows])[:3]      # the oracle packs the sampled rows itself
+    assert np.array_equal(qw[rows], ref[0]) and np.array_equal(zb[rows], ref[2])
+    assert np.array_equal(sc[rows].view(np.uint16), ref[1].view(np.uint16))
+    h, g, u, bg, bu = oracle.gated_silu_reference(X, *ref, K)
     ok = oracle.gated_silu_within_tolerance(H[:, cols].astype(np.float64), g, u, bg, bu)
     assert ok.all(), np.argwhere(~ok)[:5]
