@@ -260,6 +260,20 @@ __device__ __forceinline__ void planes3(const float (&q)[8], uint32_t& lo, uint3
   }
 }
 
+// 3-bit channel pair -> fp16 bits (1024 + q_a, 1024 + q_b), exactly: the pair's 2-bit field f
+// of the low-plane word (bits 2f and 16 + 2f) shifted to bits 0-1 and OR-ed under the
+// exponent (v_and_or_b32), its high-plane bit p (bits p and 16 + p) shifted to bit 2 and
+// inserted (v_bfi_b32); `magic` holds 0x64006400. Callers unroll, so f and p are constants.
+__device__ __forceinline__ uint32_t widen3_pair(uint32_t lo, uint32_t hi, int f, int p,
+                                                uint32_t magic) {
+  const uint32_t ls = lo >> (2 * f);
+  const uint32_t hs = p >= 2 ? (hi >> (p - 2)) : (hi << (2 - p));
+  uint32_t lm, u;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(lm) : "v"(ls), "s"(0x00030003u), "v"(magic));
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(u) : "s"(0x00040004u), "v"(hs), "v"(lm));
+  return u;
+}
+
 // One word of four 8-bit codes, byte i = code i.
 __device__ __forceinline__ uint32_t pack_bytes4(float q0, float q1, float q2, float q3) {
   uint32_t word = 0;

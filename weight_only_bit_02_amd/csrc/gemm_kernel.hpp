@@ -87,12 +87,8 @@ __device__ __forceinline__ half8 dequant_word3(uint32_t lo, uint32_t hi, half2v 
                                                uint32_t magic) {
   half2v d[4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int f = F + t, p = P + t;
-    const uint32_t h = p >= 2 ? (hi >> (p - 2)) : (hi << (2 - p));
-    const uint32_t u = ((lo >> (2 * f)) & 0x00030003u) | (h & 0x00040004u) | magic;
-    d[t] = (__builtin_bit_cast(half2v, u) + zz) * s2;
-  }
+  for (int t = 0; t < 4; ++t)
+    d[t] = (__builtin_bit_cast(half2v, widen3_pair(lo, hi, F + t, P + t, magic)) + zz) * s2;
   return half8{d[0][0], d[0][1], d[1][0], d[1][1], d[2][0], d[2][1], d[3][0], d[3][1]};
 }
 

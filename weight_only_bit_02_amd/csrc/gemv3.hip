@@ -26,14 +26,6 @@ __device__ __forceinline__ uint32_t magic_6400() {
   return m;
 }
 
-// Pair p (0..15) of a 32-channel chunk: low-plane word `lo` (the chunk's word p / 8), field
-// p % 8; high-plane word hi, bit p. Returns the fp16 pair (1024 + q_2p, 1024 + q_2p+1) as
-// bits. Callers unroll over p, so every shift is a constant.
-__device__ __forceinline__ uint32_t widen3(uint32_t lo, uint32_t hi, int p, uint32_t magic) {
-  const uint32_t h = p >= 2 ? (hi >> (p - 2)) : (hi << (2 - p));
-  return ((lo >> (2 * (p & 7))) & 0x00030003u) | (h & 0x00040004u) | magic;
-}
-
 // Sum over the 16 pairs of a chunk of x * (q - z), with the low-plane field masked in place:
 // pair p = 4 a + e (e = p % 4) reads its 2 low bits at bits 2e, 2e + 1 of low word a / 2,
 // shifted right by 8 for odd a (one shift per 4 pairs), and its high bit moved to bit 2e + 2
@@ -120,7 +112,7 @@ __global__ void __launch_bounds__(256)
       const half2v zz = -__builtin_bit_cast(half2v, zbits | (zbits << 16));
 #pragma unroll
       for (int p = 0; p < 16; ++p)
-        qz[r][p] = __builtin_bit_cast(half2v, widen3(p < 8 ? lo.x : lo.y, hi, p, magic)) + zz;
+        qz[r][p] = __builtin_bit_cast(half2v, widen3_pair(p < 8 ? lo.x : lo.y, hi, p & 7, p, magic)) + zz;
     }
 #pragma unroll
     for (int m = 0; m < M; ++m) {
@@ -271,10 +263,10 @@ struct SkinnyStage3 {
 __device__ __forceinline__ half8 operand3(const SkinnyStage3& st, int s, half2v zz, uint32_t magic) {
   const int half = s >> 2, p0 = 4 * (s & 3);
   const uint32_t lo = (p0 < 8) ? st.lo[half].x : st.lo[half].y;
-  const half2v d0 = __builtin_bit_cast(half2v, widen3(lo, st.hi[half], p0 + 0, magic)) + zz;
-  const half2v d1 = __builtin_bit_cast(half2v, widen3(lo, st.hi[half], p0 + 1, magic)) + zz;
-  const half2v d2 = __builtin_bit_cast(half2v, widen3(lo, st.hi[half], p0 + 2, magic)) + zz;
-  const half2v d3 = __builtin_bit_cast(half2v, widen3(lo, st.hi[half], p0 + 3, magic)) + zz;
+  const half2v d0 = __builtin_bit_cast(half2v, widen3_pair(lo, st.hi[half], (p0 + 0) & 7, p0 + 0, magic)) + zz;
+  const half2v d1 = __builtin_bit_cast(half2v, widen3_pair(lo, st.hi[half], (p0 + 1) & 7, p0 + 1, magic)) + zz;
+  const half2v d2 = __builtin_bit_cast(half2v, widen3_pair(lo, st.hi[half], (p0 + 2) & 7, p0 + 2, magic)) + zz;
+  const half2v d3 = __builtin_bit_cast(half2v, widen3_pair(lo, st.hi[half], (p0 + 3) & 7, p0 + 3, magic)) + zz;
   return half8{d0[0], d0[1], d1[0], d1[1], d2[0], d2[1], d3[0], d3[1]};
 }
 
