@@ -18,10 +18,11 @@ BUILD = os.path.join(ROOT, "_build")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIB_DIR, "libawq_mi355x.so")
 
-SOURCES = ["awq_abi.hip", "quant_pack.hip", "stats.hip", "search.hip", "gemv.hip", "gemm.hip",
-           "fold.hip", "gemv_mfma.hip", "gemv8.hip", "gemm_i4_plain.hip", "gemm_i4_gated.hip",
-           "gemm_i4_plain_g32.hip", "gemm_i4_gated_g32.hip", "gemv3.hip", "gemm_i3_plain.hip",
-           "gemm_i3_gated.hip"]
+SOURCES = [  # the slowest units (GEMM instantiations, the searches) first: they bound the build
+    "gemm_i3_plain.hip", "gemm_i3_gated.hip", "gemm_i3_plain_g32.hip", "gemm_i3_gated_g32.hip",
+    "gemm_i8_plain.hip", "gemm_i8_gated.hip", "gemm_i4_plain.hip", "gemm_i4_gated.hip",
+    "gemm_i4_plain_g32.hip", "gemm_i4_gated_g32.hip", "search.hip", "gemv.hip", "gemv_mfma.hip",
+    "gemv8.hip", "gemv3.hip", "quant_pack.hip", "stats.hip", "fold.hip", "gemm.hip", "awq_abi.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -1,6 +1,6 @@
 // MFMA dequant-GEMM launcher: picks the instantiation for the code width, the group size
-// and the gated epilogue (the kernel is in gemm_kernel.hpp; the 4- and 3-bit instantiations
-// are compiled in gemm_i4_*.hip and gemm_i3_*.hip, the 8-bit ones here).
+// and the gated epilogue (the kernel is in gemm_kernel.hpp; each instantiation is compiled
+// in its own gemm_i<bits>_*.hip, so the build compiles them in parallel).
 #include "gemm_kernel.hpp"
 
 namespace awq {
@@ -17,11 +17,22 @@ void launch_gemm4_plain_g32(dim3 grid, const uint16_t* X, int64_t M, const uint3
 void launch_gemm4_gated_g32(dim3 grid, const uint16_t* X, int64_t M, const uint32_t* qweight,
                 const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K, int group,
                 uint16_t* Y, int64_t mt, int64_t nt, int64_t per_xcd, hipStream_t stream);
-
+void launch_gemm8_plain(dim3 grid, const uint16_t* X, int64_t M, const uint32_t* qweight,
+                const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K, int group,
+                uint16_t* Y, int64_t mt, int64_t nt, int64_t per_xcd, hipStream_t stream);
+void launch_gemm8_gated(dim3 grid, const uint16_t* X, int64_t M, const uint32_t* qweight,
+                const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K, int group,
+                uint16_t* Y, int64_t mt, int64_t nt, int64_t per_xcd, hipStream_t stream);
 void launch_gemm3_plain(dim3 grid, const uint16_t* X, int64_t M, const uint32_t* qweight,
                 const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K, int group,
                 uint16_t* Y, int64_t mt, int64_t nt, int64_t per_xcd, hipStream_t stream);
 void launch_gemm3_gated(dim3 grid, const uint16_t* X, int64_t M, const uint32_t* qweight,
+                const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K, int group,
+                uint16_t* Y, int64_t mt, int64_t nt, int64_t per_xcd, hipStream_t stream);
+void launch_gemm3_plain_g32(dim3 grid, const uint16_t* X, int64_t M, const uint32_t* qweight,
+                const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K, int group,
+                uint16_t* Y, int64_t mt, int64_t nt, int64_t per_xcd, hipStream_t stream);
+void launch_gemm3_gated_g32(dim3 grid, const uint16_t* X, int64_t M, const uint32_t* qweight,
                 const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K, int group,
                 uint16_t* Y, int64_t mt, int64_t nt, int64_t per_xcd, hipStream_t stream);
 
@@ -32,29 +43,14 @@ hipError_t launch_gemm(const uint16_t* X, int64_t M, const uint32_t* qweight,
   const int64_t nt = gated ? (N / 2 + kBN / 2 - 1) / (kBN / 2) : (N + kBN - 1) / kBN;
   const int64_t per_xcd = (mt * nt + kXcds - 1) / kXcds;
   const dim3 grid((unsigned)(per_xcd * kXcds));
-  if (w_bit == 8) {
-    if (gated)
-      hipLaunchKernelGGL((k_gemm<true, false, 8>), grid, dim3(256), 0, stream, X, M, qweight,
-                         scales, zeros, N, K, group, Y, mt, nt, per_xcd);
-    else
-      hipLaunchKernelGGL((k_gemm<false, false, 8>), grid, dim3(256), 0, stream, X, M, qweight,
-                         scales, zeros, N, K, group, Y, mt, nt, per_xcd);
-  } else if (w_bit == 3) {
-    if (gated)
-      launch_gemm3_gated(grid, X, M, qweight, scales, zeros, N, K, group, Y, mt, nt, per_xcd, stream);
-    else
-      launch_gemm3_plain(grid, X, M, qweight, scales, zeros, N, K, group, Y, mt, nt, per_xcd, stream);
-  } else if (group == 32) {  // two scales per lane half
-    if (gated)
-      launch_gemm4_gated_g32(grid, X, M, qweight, scales, zeros, N, K, group, Y, mt, nt, per_xcd, stream);
-    else
-      launch_gemm4_plain_g32(grid, X, M, qweight, scales, zeros, N, K, group, Y, mt, nt, per_xcd, stream);
-  } else {
-    if (gated)
-      launch_gemm4_gated(grid, X, M, qweight, scales, zeros, N, K, group, Y, mt, nt, per_xcd, stream);
-    else
-      launch_gemm4_plain(grid, X, M, qweight, scales, zeros, N, K, group, Y, mt, nt, per_xcd, stream);
-  }
+  // 8-bit: one form for every group size (both lane halves' scales are loaded); 4- and
+  // 3-bit: 32-channel groups (two scales per lane half) take the SPLIT form
+  auto* f = w_bit == 8   ? (gated ? launch_gemm8_gated : launch_gemm8_plain)
+            : w_bit == 3 ? (group == 32 ? (gated ? launch_gemm3_gated_g32 : launch_gemm3_plain_g32)
+                                        : (gated ? launch_gemm3_gated : launch_gemm3_plain))
+                         : (group == 32 ? (gated ? launch_gemm4_gated_g32 : launch_gemm4_plain_g32)
+                                        : (gated ? launch_gemm4_gated : launch_gemm4_plain));
+  f(grid, X, M, qweight, scales, zeros, N, K, group, Y, mt, nt, per_xcd, stream);
   return hipGetLastError();
 }
 

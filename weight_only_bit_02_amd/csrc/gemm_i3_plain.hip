@@ -1,5 +1,5 @@
-// The 3-bit instantiations of the MFMA dequant-GEMM with GATED = false (SPLIT for 32-channel
-// groups), in a file of their own so that the build compiles the GEMM variants in parallel.
+// One 3-bit instantiation of the MFMA dequant-GEMM (GATED = false, SPLIT = false: 128- or 64-channel groups),
+// in a file of its own so that the build compiles the GEMM variants in parallel.
 #include "gemm_kernel.hpp"
 
 namespace awq {
@@ -7,12 +7,8 @@ namespace awq {
 void launch_gemm3_plain(dim3 grid, const uint16_t* X, int64_t M, const uint32_t* qweight,
                 const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K, int group,
                 uint16_t* Y, int64_t mt, int64_t nt, int64_t per_xcd, hipStream_t stream) {
-  if (group == 32)
-    hipLaunchKernelGGL((k_gemm<false, true, 3>), grid, dim3(256), 0, stream, X, M, qweight, scales,
-                       zeros, N, K, group, Y, mt, nt, per_xcd);
-  else
-    hipLaunchKernelGGL((k_gemm<false, false, 3>), grid, dim3(256), 0, stream, X, M, qweight, scales,
-                       zeros, N, K, group, Y, mt, nt, per_xcd);
+  hipLaunchKernelGGL((k_gemm<false, false, 3>), grid, dim3(256), 0, stream, X, M, qweight, scales,
+                     zeros, N, K, group, Y, mt, nt, per_xcd);
 }
 
 }  // namespace awq

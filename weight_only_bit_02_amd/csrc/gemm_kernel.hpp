@@ -214,17 +214,17 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
 
-  // Prefetch distance 2 (4-bit codes): stage `cur` is being multiplied, `nxt` (one step
-  // ahead) has its A in flight to LDS, `nn` (two steps ahead) is being loaded. The loop is
-  // unrolled by three with the stages' roles rotated, so no register copy (which would
-  // wait for the loads just issued) is ever needed. 8-bit codes double a stage's B
-  // registers and the 3-bit widening needs more temporaries, so for those the distance is 1
-  // with two stages (the next step's loads are in flight for a whole step of MFMAs): `nn`
-  // is `nxt`.
-  constexpr int PF = BITS == 4 ? 2 : 1;
+  // Prefetch distance 2: stage `cur` is being multiplied, `nxt` (one step ahead) has its A
+  // in flight to LDS, `nn` (two steps ahead) is being loaded. The loop is unrolled by three
+  // with the stages' roles rotated, so no register copy (which would wait for the loads
+  // just issued) is ever needed. With 8- and 3-bit codes the three stages exceed the 256
+  // architectural VGPRs and the compiler parks values in AGPRs; measured on the 7B shapes
+  // at M = 2048 that still beats distance 1 (two stages, no spill): 530 -> 730 TFLOP/s
+  // (8-bit), 725 -> 790 (3-bit).
+  constexpr int PF = 2;
   GemmStage<BITS> S0, S1, S2;
   load(S0, 0);
-  if constexpr (PF == 2) load(S1, nsteps > 1 ? 1 : 0);
+  load(S1, nsteps > 1 ? 1 : 0);
   store_a(S0, 0);
   __syncthreads();
 
@@ -311,22 +311,13 @@ __global__ void __launch_bounds__(256)
   };
 
   int64_t step = 0;
-  if constexpr (PF == 2) {
-    for (; step + 3 <= nsteps; step += 3) {  // straight-line triples: one path through the loop
-      body(S0, S1, S2, step);
-      body(S1, S2, S0, step + 1);
-      body(S2, S0, S1, step + 2);
-    }
-    if (step < nsteps) body(S0, S1, S2, step);
-    if (step + 1 < nsteps) body(S1, S2, S0, step + 1);
-  } else {
-    (void)S2;
-    for (; step + 2 <= nsteps; step += 2) {
-      body(S0, S1, S1, step);
-      body(S1, S0, S0, step + 1);
-    }
-    if (step < nsteps) body(S0, S1, S1, step);
+  for (; step + 3 <= nsteps; step += 3) {  // straight-line triples: one path through the loop
+    body(S0, S1, S2, step);
+    body(S1, S2, S0, step + 1);
+    body(S2, S0, S1, step + 2);
   }
+  if (step < nsteps) body(S0, S1, S2, step);
+  if (step + 1 < nsteps) body(S1, S2, S0, step + 1);
 
   // ------------------------------------------------------------------ epilogue
   // 32x32 accumulator layout: element e of lane l is (row 8(e/4) + 4(l/32) + e%4, col l%32).
