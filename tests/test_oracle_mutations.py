@@ -92,3 +92,23 @@ def test_signed_mean_mutant_caught():
     exact = [Fraction(4, 2), Fraction(5, 4)]
     assert [float(v) for v in exact] != mutant.tolist()
     assert oracle.activation_mean_abs(X)[0].tolist() == [float(v) for v in exact]
+
+
+def test_3bit_plane_mutants_caught():
+    """Plausible 3-bit layout slips differ from the hand-derived words: the two channels of a
+    pair in adjacent fields instead of the two halves, the planes swapped (bit 2 with the low
+    field), or the high bits one per channel in channel order."""
+    q = (np.arange(128, dtype=np.uint8) * 5 % 8).reshape(1, 128)
+    qw, _, _ = oracle.pack(q, np.zeros((1, 1), np.uint8), np.ones((1, 1), np.float16), w_bit=3)
+    # hand-derived: low word 0 = bits 0-1 of channels 0,2,..,14 (low half), 1,3,..,15 (high)
+    lo0 = sum((int(q[0, 2 * f]) & 3) << (2 * f) for f in range(8)) | \
+        sum((int(q[0, 2 * f + 1]) & 3) << (16 + 2 * f) for f in range(8))
+    hi0 = sum((int(q[0, 2 * p]) >> 2) << p for p in range(16)) | \
+        sum((int(q[0, 2 * p + 1]) >> 2) << (16 + p) for p in range(16))
+    assert int(qw[0, 0]) == lo0 and int(qw[0, 8]) == hi0
+    adjacent = sum((int(q[0, c]) & 3) << (2 * c) for c in range(16))
+    assert adjacent != int(qw[0, 0])
+    swapped = sum((int(q[0, 2 * f]) >> 2) << (2 * f) for f in range(8))
+    assert swapped != int(qw[0, 0])
+    in_order = sum((int(q[0, c]) >> 2) << c for c in range(32))
+    assert in_order != int(qw[0, 8])
