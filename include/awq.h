@@ -88,7 +88,8 @@ typedef enum awq_linear_kernel {
                           codes: vector GEMV up to 8, skinny up to 32)         */
   AWQ_LINEAR_GEMV = 1, /* wave-per-rows dequant-fused GEMV (any M <= 8)       */
   AWQ_LINEAR_GEMM = 2, /* MFMA dequant-GEMM (any M)                           */
-  AWQ_LINEAR_SKINNY = 3 /* MFMA GEMV for small batches, split K (M <= 32)     */
+  AWQ_LINEAR_SKINNY = 3 /* MFMA GEMV for small batches, split K (M <= 64;     
+                           8- and 3-bit codes: M <= 32)                      */
 } awq_linear_kernel;
 
 /*
@@ -179,16 +180,17 @@ awq_status awq_search_scales(const void* X, int64_t T, const void* W, int64_t N,
  *   "主要功能和特点" (GEMV kernel for single-token decode, GEMM kernel for batches).
  *   deq(W)_nk = (q_nk - z_nj) * sc_nj; products accumulate in fp32; Y is rounded to fp16.
  *   X fp16 [M][K]; qweight/scales/zeros as written by awq_quantize_pack; Y fp16 [M][N].
- *   Dispatch: M <= 3 runs the vector-ALU dequant-fused GEMV, M <= 32 the skinny MFMA
- *   GEMV (dots on the matrix cores, K split over the waves of a block), larger M the
- *   MFMA dequant-GEMM (thresholds measured on the Llama-2-7B layer).
+ *   Dispatch: M <= 3 runs the vector-ALU dequant-fused GEMV, M <= 64 the skinny MFMA
+ *   GEMV (dots on the matrix cores, K split over the waves of a block; two 32-token tiles
+ *   above M = 32), larger M the MFMA dequant-GEMM (thresholds measured on the Llama-2-7B
+ *   layer).
  */
 awq_status awq_linear_w4a16(const void* X, int64_t M, const uint32_t* qweight,
                             const void* scales, const uint8_t* zeros, int64_t N, int64_t K,
                             const awq_config* cfg, void* Y, uint32_t* flags, void* stream);
 
 /* Same as awq_linear_w4a16 with an explicit kernel choice (GEMV requires M <= 8,
- * SKINNY M <= 32; otherwise AWQ_ERR_BAD_SHAPE). */
+ * SKINNY M <= 64, or M <= 32 with 8- and 3-bit codes; otherwise AWQ_ERR_BAD_SHAPE). */
 awq_status awq_linear_w4a16_ex(const void* X, int64_t M, const uint32_t* qweight,
                                const void* scales, const uint8_t* zeros, int64_t N, int64_t K,
                                const awq_config* cfg, void* Y, uint32_t* flags,
@@ -275,8 +277,9 @@ awq_status awq_quantize_pack_clipped(const void* W, int64_t N, int64_t K, const 
 awq_status awq_apply_inverse_scale(const void* A, int64_t rows, int64_t cols, const void* s,
                                    int32_t axis, void* out, uint32_t* flags, void* stream);
 
-/* Largest M served by a GEMV-class kernel under AWQ_LINEAR_AUTO (32, or the value of
- * the AWQ_GEMV_MAX_M environment variable clamped to 0..32, read at library load). */
+/* Largest M served by a GEMV-class kernel under AWQ_LINEAR_AUTO with 4-bit codes (64, or
+ * the value of the AWQ_GEMV_MAX_M environment variable clamped to 0..64, read at library
+ * load). */
 int32_t awq_gemv_max_m(void);
 
 /* Human-readable text of a status code (static storage). */

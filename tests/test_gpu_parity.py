@@ -207,11 +207,12 @@ def test_gemv_matches_oracle(M, N, K):
     _check_linear(si.activations(M, K, offset=M), p, ref, "gemv")
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 7, 8, 9, 16, 17, 31, 32])
+@pytest.mark.parametrize("M", [1, 2, 3, 7, 8, 9, 16, 17, 31, 32, 33, 47, 64])
 @pytest.mark.parametrize("N,K", [(1, 128), (67, 384), (256, 4096), (130, 11008), (33, 1152)])
 def test_skinny_matches_oracle(M, N, K):
-    """Small-batch MFMA GEMV: every accumulator bucket (M <= 8, 16, 32), ragged N, K
-    splits that leave some waves without a group (K = 128) or uneven (K = 1152)."""
+    """Small-batch MFMA GEMV: every accumulator bucket (M <= 8, 16, 32, and two token tiles
+    up to 64), ragged N, K splits that leave some waves without a group (K = 128) or uneven
+    (K = 1152)."""
     p, ref = _packed_case(N, K, off=N + 13 * K)
     _check_linear(si.activations(M, K, offset=M + 400), p, ref, "skinny")
 
@@ -245,13 +246,13 @@ def test_linear_zero_input(kernel):
 
 
 def test_linear_auto_dispatch_and_determinism():
-    """AUTO picks the vector GEMV up to M = 3, the skinny MFMA GEMV up to 32, the GEMM above
+    """AUTO picks the vector GEMV up to M = 3, the skinny MFMA GEMV up to 64, the GEMM above
     (each result equals its explicit kernel's bit for bit), deterministically."""
     p, ref = _packed_case(300, 1024, off=63)
-    X = si.activations(40, 1024, offset=63)
-    assert awq.gemv_max_m() == 32
+    X = si.activations(80, 1024, offset=63)
+    assert awq.gemv_max_m() == 64
     for M, kern in ((1, "gemv"), (3, "gemv"), (4, "skinny"), (8, "skinny"), (32, "skinny"),
-                    (33, "gemm"), (40, "gemm")):
+                    (33, "skinny"), (64, "skinny"), (65, "gemm"), (80, "gemm")):
         Xm = X[:M]
         a = host(awq.linear_w4a16(to_dev(Xm), p))
         b = host(awq.linear_w4a16(to_dev(Xm), p))

@@ -70,13 +70,13 @@ ClipLayout clip_layout(int64_t T, int64_t N, int64_t K, int n_shrink, int group)
 }
 
 // Largest M that AWQ_LINEAR_AUTO serves with a GEMV-class kernel (above it, the MFMA
-// GEMM); AWQ_GEMV_MAX_M overrides it (0 .. 32) to measure the crossover.
+// GEMM); AWQ_GEMV_MAX_M overrides it (0 .. 64) to measure the crossover.
 int gemv_max_m_from_env() {
   const char* e = getenv("AWQ_GEMV_MAX_M");
-  if (!e) return awq::kSkinnyMaxM;
+  if (!e) return awq::kSkinnyMaxM4;
   int v = atoi(e);
   if (v < 0) v = 0;
-  if (v > awq::kSkinnyMaxM) v = awq::kSkinnyMaxM;
+  if (v > awq::kSkinnyMaxM4) v = awq::kSkinnyMaxM4;
   return v;
 }
 const int g_gemv_max_m = gemv_max_m_from_env();
@@ -213,7 +213,8 @@ static awq_status linear_common(const void* X, int64_t M, const uint32_t* qweigh
       kernel != AWQ_LINEAR_SKINNY)
     return AWQ_ERR_UNSUPPORTED;
   if (kernel == AWQ_LINEAR_GEMV && M > awq::kGemvMaxM) return AWQ_ERR_BAD_SHAPE;
-  if (kernel == AWQ_LINEAR_SKINNY && M > awq::kSkinnyMaxM) return AWQ_ERR_BAD_SHAPE;
+  if (kernel == AWQ_LINEAR_SKINNY && M > (c.w_bit == 4 ? awq::kSkinnyMaxM4 : awq::kSkinnyMaxM))
+    return AWQ_ERR_BAD_SHAPE;
   if (!aligned16(X) || !aligned16(qweight) || !aligned16(scales) || !aligned16(zeros) ||
       !aligned16(Y))
     return AWQ_ERR_MISALIGNED;

@@ -1,4 +1,4 @@
-// Skinny MFMA GEMV for small batches (a7 / a9): Y[M][N] = X[M][K] deq(W)^T for M <= 32.
+// Skinny MFMA GEMV for small batches (a7 / a9): Y[M][N] = X[M][K] deq(W)^T for M <= 64.
 //
 // "AWQ量化实战" §3.4: decode is memory-bound, so the packed weights are streamed once and
 // dequantized on the fly; "AWQ量化技术Skill", "主要功能和特点": a GEMV kernel serves the
@@ -21,6 +21,11 @@
 //     MFMAs form two partial tiles of four, each with its own scale; with 32-channel
 //     groups the two lane halves of one k16 slice lie in different groups, so there the
 //     operand itself carries the scale ((q - z) sc in fp16, one rounding, as in the GEMM);
+//   - M up to 32 is one token tile; 33..64 two (MT = 2): each widened B operand then feeds
+//     one MFMA per token tile, so the vector work per byte of codes stays that of one tile.
+//     To fit the registers of two tiles, the operand carries the group scale there for
+//     every group size ((q - z) sc in fp16, one rounding, as in the GEMM) and the MFMAs
+//     accumulate straight into the two tiles;
 //   - the S waves of a block split K and meet in LDS at the end, where wave 0 adds the S
 //     partial tiles in a fixed order: results do not depend on scheduling.
 // Loads of group g + 1 are in flight while group g is multiplied (two register stages
@@ -36,9 +41,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 namespace {
 
+template <int MT>
 struct SkinnyStage {
   uint4 b[2];     // 8 packed words: channels 32 h + [0, 32) and 64 + 32 h + [0, 32), row l % 32
-  uint4 a[8];     // X[token][same channels], one 16-byte piece per k16 step
+  uint4 a[MT][8]; // X[token][same channels] per token tile, one 16-byte piece per k16 step
   uint32_t sc[2], zb;  // the lane's scales of words 0-3 and 4-7; the step's zero byte(s)
 };
 
@@ -60,12 +66,13 @@ __device__ __forceinline__ half8 widen_word(uint32_t w, half2v zz, uint32_t magi
 }  // namespace
 
 // E = accumulator elements kept per lane: rows 8 (e / 4) + 4 h + e % 4 of the 32 x 32 tile;
-// E = 4 serves M <= 8, 8 serves M <= 16, 16 serves M <= 32.
-template <int S, int E, bool GATED>
+// E = 4 serves M <= 8, 8 serves M <= 16, 16 serves M <= 32; MT = 2 token tiles of 32 (rows
+// 32 t + ...) serve M <= 64.
+template <int S, int E, int MT, bool GATED>
 __global__ void __launch_bounds__(S * 64)
     k_gemv_mfma(const uint16_t* X, int64_t M, const uint32_t* qweight, const uint16_t* scales,
                 const uint8_t* zeros, int64_t N, int64_t K, int group, uint16_t* Y) {
-  __shared__ float red[S][E][64];
+  __shared__ float red[S][MT * E][64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -84,12 +91,14 @@ __global__ void __launch_bounds__(S * 64)
     const int64_t o = (int64_t)blockIdx.x * 32 + j;
     n = o < N ? o : N - 1;
   }
-  const int64_t xrow = (j < M ? j : M - 1) * K;
+  int64_t xrow[MT];  // token row of lane l in tile t: 32 t + l % 32 (past M: row M - 1, never stored)
+#pragma unroll
+  for (int t = 0; t < MT; ++t) xrow[t] = (32 * t + j < M ? 32 * t + j : M - 1) * K;
   // this wave's groups: an even split of the G groups over the S waves
   const int64_t g0 = G * wave / S, g1 = G * (wave + 1) / S;
   const uint32_t magic = skinny_magic();
 
-  auto load = [&](SkinnyStage& st, int64_t g) {
+  auto load = [&](SkinnyStage<MT>& st, int64_t g) {
     if (g32) {
       // words 0-3 of lane half h: group 4g + h; words 4-7: group 4g + 2 + h
       st.zb = (uint32_t)zeros[n * zbytes + 2 * g] | ((uint32_t)zeros[n * zbytes + 2 * g + 1] << 8);
@@ -107,63 +116,99 @@ __global__ void __launch_bounds__(S * 64)
     st.b[0] = *reinterpret_cast<const uint4*>(cp);
     st.b[1] = *reinterpret_cast<const uint4*>(cp + 8);
     // word s (k16 step s) covers channels 8 s' + 32 h + 64 (s / 4), s' = s % 4
-    const uint16_t* xp = X + xrow + g * kGroup + h * 32;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) st.a[s] = *reinterpret_cast<const uint4*>(xp + (s & 3) * 8 + (s >> 2) * 64);
+    for (int t = 0; t < MT; ++t) {
+      const uint16_t* xp = X + xrow[t] + g * kGroup + h * 32;
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        st.a[t][s] = *reinterpret_cast<const uint4*>(xp + (s & 3) * 8 + (s >> 2) * 64);
+    }
   };
 
-  float acc[E];
+  float acc[MT][E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = 0.0f;
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[t][e] = 0.0f;
+  auto mfma = [&](const SkinnyStage<MT>& st, int s, half8 b, f32x16 (&d)[MT]) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+      d[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, st.a[t][s]), b, d[t], 0, 0, 0);
+  };
 
-  auto body = [&](const SkinnyStage& st, int64_t g) {
+  f32x16 acc2[MT];  // MT = 2: the two token tiles, accumulated by the MFMAs themselves
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc2[t] = f32x16{};
+
+  auto body = [&](const SkinnyStage<MT>& st, int64_t g) {
     const uint32_t wd[8] = {st.b[0].x, st.b[0].y, st.b[0].z, st.b[0].w,
                             st.b[1].x, st.b[1].y, st.b[1].z, st.b[1].w};
     auto zz_of = [](uint32_t z) {
       const uint32_t zbits = 0x6400u + z;
       return -__builtin_bit_cast(half2v, zbits | (zbits << 16));
     };
-    if (g32) {
-      f32x16 d = f32x16{};
+    if constexpr (MT == 2) {
+      // words 0-3 / 4-7 of lane half h: zero nibble and scale of their group (128: the
+      // step's group; 64: groups 2g, 2g + 1; 32: groups 4g + h, 4g + 2 + h)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const uint32_t z = g32 ? (st.zb >> (8 * half + 4 * h)) & 0xF
+                           : g64 ? (st.zb >> (4 * half)) & 0xF
+                                 : ((g & 1) ? (st.zb >> 4) & 0xF : st.zb & 0xF);
+        const half2v zz = zz_of(z);
+        const half2v s2 = __builtin_bit_cast(half2v, st.sc[half] | (st.sc[half] << 16));
+#pragma unroll
+        for (int s = 4 * half; s < 4 * half + 4; ++s)
+          mfma(st, s, widen_word(wd[s], zz, magic) * half8{s2[0], s2[1], s2[0], s2[1], s2[0], s2[1], s2[0], s2[1]}, acc2);
+      }
+    } else if (g32) {
+      f32x16 d[MT];
+#pragma unroll
+      for (int t = 0; t < MT; ++t) d[t] = f32x16{};
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const half2v zz = zz_of((st.zb >> (8 * half + 4 * h)) & 0xF);
         const half2v s2 = __builtin_bit_cast(half2v, st.sc[half] | (st.sc[half] << 16));
 #pragma unroll
         for (int s = 4 * half; s < 4 * half + 4; ++s)
-          d = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-              __builtin_bit_cast(half8, st.a[s]), widen_word(wd[s], zz, magic) * half8{s2[0], s2[1], s2[0], s2[1], s2[0], s2[1], s2[0], s2[1]}, d, 0, 0, 0);
+          mfma(st, s, widen_word(wd[s], zz, magic) * half8{s2[0], s2[1], s2[0], s2[1], s2[0], s2[1], s2[0], s2[1]}, d);
       }
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] += d[e];
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[t][e] += d[t][e];
     } else if (g64) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const half2v zz = zz_of((st.zb >> (4 * half)) & 0xF);
-        f32x16 d = f32x16{};
+        f32x16 d[MT];
 #pragma unroll
-        for (int s = 4 * half; s < 4 * half + 4; ++s)
-          d = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, st.a[s]),
-                                                     widen_word(wd[s], zz, magic), d, 0, 0, 0);
+        for (int t = 0; t < MT; ++t) d[t] = f32x16{};
+#pragma unroll
+        for (int s = 4 * half; s < 4 * half + 4; ++s) mfma(st, s, widen_word(wd[s], zz, magic), d);
         const float scf = h2f((uint16_t)st.sc[half]);
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(scf, d[e], acc[e]);
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[t][e] = __builtin_fmaf(scf, d[t][e], acc[t][e]);
       }
     } else {
       const half2v zz = zz_of((g & 1) ? (st.zb >> 4) & 0xF : st.zb & 0xF);
-      f32x16 d = f32x16{};
+      f32x16 d[MT];
 #pragma unroll
-      for (int s = 0; s < 8; ++s)
-        d = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, st.a[s]),
-                                                   widen_word(wd[s], zz, magic), d, 0, 0, 0);
+      for (int t = 0; t < MT; ++t) d[t] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) mfma(st, s, widen_word(wd[s], zz, magic), d);
       const float scf = h2f((uint16_t)st.sc[0]);
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(scf, d[e], acc[e]);
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[t][e] = __builtin_fmaf(scf, d[t][e], acc[t][e]);
     }
   };
 
   if (g1 > g0) {
-    SkinnyStage s0, s1;
+    SkinnyStage<MT> s0, s1;
     load(s0, g0);
     int64_t g = g0;
     for (; g + 2 <= g1; g += 2) {
@@ -175,46 +220,60 @@ __global__ void __launch_bounds__(S * 64)
     if (g < g1) body(s0, g);
   }
 
+  if constexpr (MT == 2) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[t][e] = acc2[t][e];
+  }
   // fixed-order reduction of the S partial tiles
 #pragma unroll
-  for (int e = 0; e < E; ++e) red[wave][e][lane] = acc[e];
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int e = 0; e < E; ++e) red[wave][t * E + e][lane] = acc[t][e];
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    float v = red[0][e][lane];
+  for (int t = 0; t < MT; ++t)
 #pragma unroll
-    for (int w = 1; w < S; ++w) v += red[w][e][lane];
-    acc[e] = v;
-  }
+    for (int e = 0; e < E; ++e) {
+      float v = red[0][t * E + e][lane];
+#pragma unroll
+      for (int w = 1; w < S; ++w) v += red[w][t * E + e][lane];
+      acc[t][e] = v;
+    }
   // 32x32 accumulator layout: element e of lane l is (row 8(e/4) + 4(l/32) + e%4, col l%32)
   if constexpr (GATED) {
     // up partner of column j (< 16) is column j + 16, held by lane + 16 for the same rows
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const float u = __shfl_down(acc[e], 16, 32);
-      const int64_t o = (int64_t)blockIdx.x * 16 + j;
-      const int64_t i = 8 * (e >> 2) + 4 * h + (e & 3);
-      if (j < 16 && o < nh && i < M) Y[i * nh + o] = f2h_bits(silu_f32(acc[e]) * u);
-    }
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float u = __shfl_down(acc[t][e], 16, 32);
+        const int64_t o = (int64_t)blockIdx.x * 16 + j;
+        const int64_t i = 32 * t + 8 * (e >> 2) + 4 * h + (e & 3);
+        if (j < 16 && o < nh && i < M) Y[i * nh + o] = f2h_bits(silu_f32(acc[t][e]) * u);
+      }
   } else {
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int64_t o = (int64_t)blockIdx.x * 32 + j;
-      const int64_t i = 8 * (e >> 2) + 4 * h + (e & 3);
-      if (o < N && i < M) Y[i * N + o] = f2h_bits(acc[e]);
-    }
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int64_t o = (int64_t)blockIdx.x * 32 + j;
+        const int64_t i = 32 * t + 8 * (e >> 2) + 4 * h + (e & 3);
+        if (o < N && i < M) Y[i * N + o] = f2h_bits(acc[t][e]);
+      }
   }
 }
 
-template <int S, int E, bool GATED>
+template <int S, int E, int MT, bool GATED>
 static hipError_t launch_skinny_x(const uint16_t* X, int64_t M, const uint32_t* qw,
                                   const uint16_t* sc, const uint8_t* z, int64_t N, int64_t K,
                                   int group, uint16_t* Y, hipStream_t stream) {
   const int64_t outs = GATED ? N / 2 : N;
   const int64_t per = GATED ? 16 : 32;
   const int64_t blocks = (outs + per - 1) / per;
-  hipLaunchKernelGGL((k_gemv_mfma<S, E, GATED>), dim3((unsigned)blocks), dim3(S * 64), 0, stream,
+  hipLaunchKernelGGL((k_gemv_mfma<S, E, MT, GATED>), dim3((unsigned)blocks), dim3(S * 64), 0, stream,
                      X, M, qw, sc, z, N, K, group, Y);
   return hipGetLastError();
 }
@@ -223,15 +282,17 @@ template <bool GATED>
 static hipError_t launch_skinny_t(const uint16_t* X, int64_t M, const uint32_t* qw,
                                   const uint16_t* sc, const uint8_t* z, int64_t N, int64_t K,
                                   int group, uint16_t* Y, hipStream_t stream) {
-  if (M <= 8) return launch_skinny_x<8, 4, GATED>(X, M, qw, sc, z, N, K, group, Y, stream);
-  if (M <= 16) return launch_skinny_x<8, 8, GATED>(X, M, qw, sc, z, N, K, group, Y, stream);
-  return launch_skinny_x<8, 16, GATED>(X, M, qw, sc, z, N, K, group, Y, stream);
+  if (M <= 8) return launch_skinny_x<8, 4, 1, GATED>(X, M, qw, sc, z, N, K, group, Y, stream);
+  if (M <= 16) return launch_skinny_x<8, 8, 1, GATED>(X, M, qw, sc, z, N, K, group, Y, stream);
+  if (M <= 32) return launch_skinny_x<8, 16, 1, GATED>(X, M, qw, sc, z, N, K, group, Y, stream);
+  // two token tiles: 4 waves per block, so a wave may also use the accumulation registers
+  return launch_skinny_x<4, 16, 2, GATED>(X, M, qw, sc, z, N, K, group, Y, stream);
 }
 
 hipError_t launch_gemv_mfma(const uint16_t* X, int64_t M, const uint32_t* qweight,
                             const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
                             int group, uint16_t* Y, bool gated, hipStream_t stream) {
-  if (M < 1 || M > kSkinnyMaxM) return hipErrorInvalidValue;
+  if (M < 1 || M > kSkinnyMaxM4) return hipErrorInvalidValue;
   return gated ? launch_skinny_t<true>(X, M, qweight, scales, zeros, N, K, group, Y, stream)
                : launch_skinny_t<false>(X, M, qweight, scales, zeros, N, K, group, Y, stream);
 }
