@@ -85,11 +85,10 @@ typedef struct awq_config {
 typedef enum awq_linear_kernel {
   AWQ_LINEAR_AUTO = 0, /* vector GEMV for M <= 3, skinny MFMA GEMV up to
                           awq_gemv_max_m(), MFMA GEMM above (8- and 3-bit
-                          codes: vector GEMV up to 8, skinny up to 32)         */
+                          codes: vector GEMV up to 8, skinny up to 64)         */
   AWQ_LINEAR_GEMV = 1, /* wave-per-rows dequant-fused GEMV (any M <= 8)       */
   AWQ_LINEAR_GEMM = 2, /* MFMA dequant-GEMM (any M)                           */
-  AWQ_LINEAR_SKINNY = 3 /* MFMA GEMV for small batches, split K (M <= 64;     
-                           8- and 3-bit codes: M <= 32)                      */
+  AWQ_LINEAR_SKINNY = 3 /* MFMA GEMV for small batches, split K (M <= 64)     */
 } awq_linear_kernel;
 
 /*
@@ -190,7 +189,7 @@ awq_status awq_linear_w4a16(const void* X, int64_t M, const uint32_t* qweight,
                             const awq_config* cfg, void* Y, uint32_t* flags, void* stream);
 
 /* Same as awq_linear_w4a16 with an explicit kernel choice (GEMV requires M <= 8,
- * SKINNY M <= 64, or M <= 32 with 8- and 3-bit codes; otherwise AWQ_ERR_BAD_SHAPE). */
+ * SKINNY M <= 64; otherwise AWQ_ERR_BAD_SHAPE). */
 awq_status awq_linear_w4a16_ex(const void* X, int64_t M, const uint32_t* qweight,
                                const void* scales, const uint8_t* zeros, int64_t N, int64_t K,
                                const awq_config* cfg, void* Y, uint32_t* flags,

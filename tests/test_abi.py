@@ -109,7 +109,7 @@ def test_linear_validation(lib):
     assert call(M=9, kern=1) == 2       # GEMV serves M <= 8 only
     assert call(M=65, kern=3) == 2      # the skinny MFMA GEMV serves M <= 64 (4-bit codes)
     w8 = _abi.config(w_bit=8)
-    assert lib.awq_linear_w4a16_ex(FAKE, 33, FAKE, FAKE, FAKE, 64, 256, C.byref(w8), FAKE, None, 3, None) == 2
+    assert lib.awq_linear_w4a16_ex(FAKE, 65, FAKE, FAKE, FAKE, 64, 256, C.byref(w8), FAKE, None, 3, None) == 2
     assert call(kern=7) == 3
     assert call(Y=FAKE_ODD) == 4
     assert lib.awq_linear_w4a16(None, 1, FAKE, FAKE, FAKE, 64, 256, None, FAKE, None, None) == 1

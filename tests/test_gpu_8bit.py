@@ -103,12 +103,16 @@ def test_clip_search_and_clipped_pack(T, N, K, n_shrink, group):
     (7, 130, 1152, "skinny", 64),
     (16, 64, 4096, "skinny", 32),
     (32, 96, 11008, "skinny", 128),
+    (33, 130, 1152, "skinny", 64),
+    (64, 67, 4096, "skinny", 32),
+    (50, 96, 11008, "skinny", 128),
     (40, 300, 1152, "gemm", 128),
     (129, 256, 4096, "gemm", 64),
     (70, 96, 1152, "gemm", 32),
     (5, 1000, 384, "auto", 128),
     (20, 300, 512, "auto", 128),
     (50, 300, 512, "auto", 128),
+    (70, 300, 512, "auto", 128),
 ])
 def test_linear_kernels(M, N, K, kernel, group):
     W = si.weights(N, K, offset=M + N + K + 8)
@@ -124,6 +128,7 @@ def test_linear_kernels(M, N, K, kernel, group):
     (1, 96, 4096, "gemv", 128),
     (4, 67, 1152, "gemv", 32),
     (12, 80, 4096, "skinny", 64),
+    (40, 67, 1152, "skinny", 128),
     (70, 130, 1152, "gemm", 128),
     (40, 64, 512, "gemm", 32),
 ])

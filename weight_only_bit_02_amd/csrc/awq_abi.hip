@@ -73,10 +73,10 @@ ClipLayout clip_layout(int64_t T, int64_t N, int64_t K, int n_shrink, int group)
 // GEMM); AWQ_GEMV_MAX_M overrides it (0 .. 64) to measure the crossover.
 int gemv_max_m_from_env() {
   const char* e = getenv("AWQ_GEMV_MAX_M");
-  if (!e) return awq::kSkinnyMaxM4;
+  if (!e) return awq::kSkinnyMaxM;
   int v = atoi(e);
   if (v < 0) v = 0;
-  if (v > awq::kSkinnyMaxM4) v = awq::kSkinnyMaxM4;
+  if (v > awq::kSkinnyMaxM) v = awq::kSkinnyMaxM;
   return v;
 }
 const int g_gemv_max_m = gemv_max_m_from_env();
@@ -213,8 +213,7 @@ static awq_status linear_common(const void* X, int64_t M, const uint32_t* qweigh
       kernel != AWQ_LINEAR_SKINNY)
     return AWQ_ERR_UNSUPPORTED;
   if (kernel == AWQ_LINEAR_GEMV && M > awq::kGemvMaxM) return AWQ_ERR_BAD_SHAPE;
-  if (kernel == AWQ_LINEAR_SKINNY && M > (c.w_bit == 4 ? awq::kSkinnyMaxM4 : awq::kSkinnyMaxM))
-    return AWQ_ERR_BAD_SHAPE;
+  if (kernel == AWQ_LINEAR_SKINNY && M > awq::kSkinnyMaxM) return AWQ_ERR_BAD_SHAPE;
   if (!aligned16(X) || !aligned16(qweight) || !aligned16(scales) || !aligned16(zeros) ||
       !aligned16(Y))
     return AWQ_ERR_MISALIGNED;
@@ -232,7 +231,7 @@ static awq_status linear_common(const void* X, int64_t M, const uint32_t* qweigh
   const auto* sc = (const uint16_t*)scales;
   auto* Yh = (uint16_t*)Y;
   if (c.w_bit == 8) {
-    // 8-bit codes: the vector GEMV (M <= 8), the skinny MFMA GEMV (M <= 32), the GEMM
+    // 8-bit codes: the vector GEMV (M <= 8), the skinny MFMA GEMV (M <= 64), the GEMM
     if (kernel == AWQ_LINEAR_GEMV)
       return hip_status(
           awq::launch_gemv8(Xh, M, qweight, sc, zeros, N, K, c.group_size, Yh, gated, st));

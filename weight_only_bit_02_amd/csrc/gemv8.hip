@@ -127,9 +127,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 namespace {
 
+template <int MT>
 struct SkinnyStage8 {
   uint4 b[4];          // words 8h .. 8h + 7 and 16 + 8h .. 16 + 8h + 7 of the step, row l % 32
-  uint4 a[8];          // X[token][same channels], one 16-byte piece per k16 step
+  uint4 a[MT][8];      // X[token][same channels] per token tile, one 16-byte piece per k16 step
   uint32_t sc[2], zb;  // scales and zero bytes of the lane's two halves
 };
 
@@ -143,11 +144,11 @@ __device__ __forceinline__ half8 widen8(uint32_t w0, uint32_t w1, half2v zz, uin
 
 }  // namespace
 
-template <int S, int E, bool GATED>
+template <int S, int E, int MT, bool GATED>
 __global__ void __launch_bounds__(S * 64)
     k_gemv_mfma8(const uint16_t* X, int64_t M, const uint32_t* qweight, const uint16_t* scales,
                  const uint8_t* zeros, int64_t N, int64_t K, int group, uint16_t* Y) {
-  __shared__ float red[S][E][64];
+  __shared__ float red[S][MT * E][64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -165,11 +166,13 @@ __global__ void __launch_bounds__(S * 64)
     const int64_t o = (int64_t)blockIdx.x * 32 + j;
     n = o < N ? o : N - 1;
   }
-  const int64_t xrow = (j < M ? j : M - 1) * K;
+  int64_t xrow[MT];  // token row of lane l in tile t: 32 t + l % 32 (past M: row M - 1, never stored)
+#pragma unroll
+  for (int t = 0; t < MT; ++t) xrow[t] = (32 * t + j < M ? 32 * t + j : M - 1) * K;
   const int64_t g0 = G * wave / S, g1 = G * (wave + 1) / S;
   const uint32_t magic = magic_64x4();
 
-  auto load = [&](SkinnyStage8& st, int64_t g) {
+  auto load = [&](SkinnyStage8<MT>& st, int64_t g) {
     const int64_t q0 = (g * kGroup + 32 * h) >> lg, q1 = (g * kGroup + 64 + 32 * h) >> lg;
     st.zb = (uint32_t)zeros[n * Gs + q0] | ((uint32_t)zeros[n * Gs + q1] << 8);
     st.sc[0] = scales[n * Gs + q0];
@@ -179,16 +182,25 @@ __global__ void __launch_bounds__(S * 64)
     st.b[1] = cp[1];
     st.b[2] = cp[4];
     st.b[3] = cp[5];
-    const uint16_t* xp = X + xrow + g * kGroup + h * 32;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) st.a[s] = *reinterpret_cast<const uint4*>(xp + (s & 3) * 8 + (s >> 2) * 64);
+    for (int t = 0; t < MT; ++t) {
+      const uint16_t* xp = X + xrow[t] + g * kGroup + h * 32;
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        st.a[t][s] = *reinterpret_cast<const uint4*>(xp + (s & 3) * 8 + (s >> 2) * 64);
+    }
   };
 
-  float acc[E];
+  float acc[MT][E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = 0.0f;
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[t][e] = 0.0f;
+  f32x16 acc2[MT];  // MT = 2: the two token tiles, accumulated by the MFMAs themselves
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc2[t] = f32x16{};
 
-  auto body = [&](const SkinnyStage8& st) {
+  auto body = [&](const SkinnyStage8<MT>& st) {
     const uint32_t wd[16] = {st.b[0].x, st.b[0].y, st.b[0].z, st.b[0].w, st.b[1].x, st.b[1].y,
                              st.b[1].z, st.b[1].w, st.b[2].x, st.b[2].y, st.b[2].z, st.b[2].w,
                              st.b[3].x, st.b[3].y, st.b[3].z, st.b[3].w};
@@ -202,44 +214,57 @@ __global__ void __launch_bounds__(S * 64)
       const int w = 8 * (s >> 2) + 2 * (s & 3);
       return widen8(wd[w], wd[w + 1], zz[s >> 2], magic);
     };
-    if (g32) {
+    if constexpr (MT == 2) {
+      // two token tiles: the operand carries the scale of its 32-channel half for every
+      // group size ((q - z) sc in fp16, one rounding), the MFMAs accumulate the tiles
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const uint32_t sb = st.sc[s >> 2];
+        const half2v s2 = __builtin_bit_cast(half2v, sb | (sb << 16));
+        const half8 b = operand(s) * half8{s2[0], s2[1], s2[0], s2[1], s2[0], s2[1], s2[0], s2[1]};
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+          acc2[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, st.a[t][s]), b,
+                                                            acc2[t], 0, 0, 0);
+      }
+    } else if (g32) {
       f32x16 d = f32x16{};
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const uint32_t sb = st.sc[s >> 2];
         const half2v s2 = __builtin_bit_cast(half2v, sb | (sb << 16));
         d = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-            __builtin_bit_cast(half8, st.a[s]),
+            __builtin_bit_cast(half8, st.a[0][s]),
             operand(s) * half8{s2[0], s2[1], s2[0], s2[1], s2[0], s2[1], s2[0], s2[1]}, d, 0, 0, 0);
       }
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] += d[e];
+      for (int e = 0; e < E; ++e) acc[0][e] += d[e];
     } else if (g128) {
       f32x16 d = f32x16{};
 #pragma unroll
       for (int s = 0; s < 8; ++s)
-        d = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, st.a[s]), operand(s), d,
+        d = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, st.a[0][s]), operand(s), d,
                                                    0, 0, 0);
       const float scf = h2f((uint16_t)st.sc[0]);
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(scf, d[e], acc[e]);
+      for (int e = 0; e < E; ++e) acc[0][e] = __builtin_fmaf(scf, d[e], acc[0][e]);
     } else {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         f32x16 d = f32x16{};
 #pragma unroll
         for (int s = 4 * half; s < 4 * half + 4; ++s)
-          d = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, st.a[s]), operand(s),
+          d = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, st.a[0][s]), operand(s),
                                                      d, 0, 0, 0);
         const float scf = h2f((uint16_t)st.sc[half]);
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(scf, d[e], acc[e]);
+        for (int e = 0; e < E; ++e) acc[0][e] = __builtin_fmaf(scf, d[e], acc[0][e]);
       }
     }
   };
 
   if (g1 > g0) {
-    SkinnyStage8 s0, s1;
+    SkinnyStage8<MT> s0, s1;
     load(s0, g0);
     int64_t g = g0;
     for (; g + 2 <= g1; g += 2) {
@@ -251,44 +276,58 @@ __global__ void __launch_bounds__(S * 64)
     if (g < g1) body(s0);
   }
 
+  if constexpr (MT == 2) {
 #pragma unroll
-  for (int e = 0; e < E; ++e) red[wave][e][lane] = acc[e];
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[t][e] = acc2[t][e];
+  }
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int e = 0; e < E; ++e) red[wave][t * E + e][lane] = acc[t][e];
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    float v = red[0][e][lane];
+  for (int t = 0; t < MT; ++t)
 #pragma unroll
-    for (int w = 1; w < S; ++w) v += red[w][e][lane];
-    acc[e] = v;
-  }
+    for (int e = 0; e < E; ++e) {
+      float v = red[0][t * E + e][lane];
+#pragma unroll
+      for (int w = 1; w < S; ++w) v += red[w][t * E + e][lane];
+      acc[t][e] = v;
+    }
   // 32x32 accumulator layout: element e of lane l is (row 8(e/4) + 4(l/32) + e%4, col l%32)
   if constexpr (GATED) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const float u = __shfl_down(acc[e], 16, 32);
-      const int64_t o = (int64_t)blockIdx.x * 16 + j;
-      const int64_t i = 8 * (e >> 2) + 4 * h + (e & 3);
-      if (j < 16 && o < nh && i < M) Y[i * nh + o] = f2h_bits(silu_f32(acc[e]) * u);
-    }
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float u = __shfl_down(acc[t][e], 16, 32);
+        const int64_t o = (int64_t)blockIdx.x * 16 + j;
+        const int64_t i = 32 * t + 8 * (e >> 2) + 4 * h + (e & 3);
+        if (j < 16 && o < nh && i < M) Y[i * nh + o] = f2h_bits(silu_f32(acc[t][e]) * u);
+      }
   } else {
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int64_t o = (int64_t)blockIdx.x * 32 + j;
-      const int64_t i = 8 * (e >> 2) + 4 * h + (e & 3);
-      if (o < N && i < M) Y[i * N + o] = f2h_bits(acc[e]);
-    }
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int64_t o = (int64_t)blockIdx.x * 32 + j;
+        const int64_t i = 32 * t + 8 * (e >> 2) + 4 * h + (e & 3);
+        if (o < N && i < M) Y[i * N + o] = f2h_bits(acc[t][e]);
+      }
   }
 }
 
-template <int S, int E, bool GATED>
+template <int S, int E, int MT, bool GATED>
 static hipError_t launch_skinny8_x(const uint16_t* X, int64_t M, const uint32_t* qw,
                                    const uint16_t* sc, const uint8_t* z, int64_t N, int64_t K,
                                    int group, uint16_t* Y, hipStream_t stream) {
   const int64_t outs = GATED ? N / 2 : N;
   const int64_t per = GATED ? 16 : 32;
   const int64_t blocks = (outs + per - 1) / per;
-  hipLaunchKernelGGL((k_gemv_mfma8<S, E, GATED>), dim3((unsigned)blocks), dim3(S * 64), 0, stream,
+  hipLaunchKernelGGL((k_gemv_mfma8<S, E, MT, GATED>), dim3((unsigned)blocks), dim3(S * 64), 0, stream,
                      X, M, qw, sc, z, N, K, group, Y);
   return hipGetLastError();
 }
@@ -297,9 +336,11 @@ template <bool GATED>
 static hipError_t launch_skinny8_t(const uint16_t* X, int64_t M, const uint32_t* qw,
                                    const uint16_t* sc, const uint8_t* z, int64_t N, int64_t K,
                                    int group, uint16_t* Y, hipStream_t stream) {
-  if (M <= 8) return launch_skinny8_x<8, 4, GATED>(X, M, qw, sc, z, N, K, group, Y, stream);
-  if (M <= 16) return launch_skinny8_x<8, 8, GATED>(X, M, qw, sc, z, N, K, group, Y, stream);
-  return launch_skinny8_x<8, 16, GATED>(X, M, qw, sc, z, N, K, group, Y, stream);
+  if (M <= 8) return launch_skinny8_x<8, 4, 1, GATED>(X, M, qw, sc, z, N, K, group, Y, stream);
+  if (M <= 16) return launch_skinny8_x<8, 8, 1, GATED>(X, M, qw, sc, z, N, K, group, Y, stream);
+  if (M <= 32) return launch_skinny8_x<8, 16, 1, GATED>(X, M, qw, sc, z, N, K, group, Y, stream);
+  // two token tiles: 4 waves per block, so a wave may also use the accumulation registers
+  return launch_skinny8_x<4, 16, 2, GATED>(X, M, qw, sc, z, N, K, group, Y, stream);
 }
 
 hipError_t launch_gemv_mfma8(const uint16_t* X, int64_t M, const uint32_t* qweight,

@@ -292,7 +292,7 @@ static hipError_t launch_skinny_t(const uint16_t* X, int64_t M, const uint32_t* 
 hipError_t launch_gemv_mfma(const uint16_t* X, int64_t M, const uint32_t* qweight,
                             const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
                             int group, uint16_t* Y, bool gated, hipStream_t stream) {
-  if (M < 1 || M > kSkinnyMaxM4) return hipErrorInvalidValue;
+  if (M < 1 || M > kSkinnyMaxM) return hipErrorInvalidValue;
   return gated ? launch_skinny_t<true>(X, M, qweight, scales, zeros, N, K, group, Y, stream)
                : launch_skinny_t<false>(X, M, qweight, scales, zeros, N, K, group, Y, stream);
 }

@@ -92,10 +92,9 @@ hipError_t launch_gemm(const uint16_t* X, int64_t M, const uint32_t* qweight,
 hipError_t launch_inverse_scale(const uint16_t* A, int64_t rows, int64_t cols, const uint16_t* s,
                                 int axis, uint16_t* out, uint32_t* flags, hipStream_t stream);
 
-// a7 / a9 for small batches: 32-row MFMA tiles, K split over the waves of a block; two
-// token tiles (M <= 64) with 4-bit codes, one (M <= 32) with 8- and 3-bit codes.
-constexpr int kSkinnyMaxM4 = 64;
-constexpr int kSkinnyMaxM = 32;
+// a7 / a9 for small batches: 32-row MFMA tiles, K split over the waves of a block; one
+// token tile up to M = 32, two up to 64.
+constexpr int kSkinnyMaxM = 64;
 hipError_t launch_gemv_mfma(const uint16_t* X, int64_t M, const uint32_t* qweight,
                             const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
                             int group, uint16_t* Y, bool gated, hipStream_t stream);
