@@ -241,7 +241,7 @@ __global__ void __launch_bounds__(256)
   if constexpr (GATED) Y[n_out] = f2h_bits(silu_f32(sums[0]) * sums[RPW - 1]);
 }
 
-// ------------------------------------------------------------------ skinny MFMA, M <= 32
+// ------------------------------------------------------------------ skinny MFMA, M <= 64
 // The 4-bit skinny kernel's mapping: a wave owns 32 weight rows and a slice of the
 // 128-channel steps; lane l takes row l % 32 and, with h = l / 32, the 32-channel chunks h
 // and 2 + h of each step (channels [32 h, 32 h + 32) and [64 + 32 h, 96 + 32 h)). Chunk ch
@@ -250,6 +250,8 @@ __global__ void __launch_bounds__(256)
 // the 4-bit kernel: a fresh partial tile per group (one per step for 128-channel groups, one
 // per half for 64), and for 32-channel groups, where the two lane halves of a slice lie in
 // different groups, the fp16 operand carries the scale.
+// M = 33..64: two 32-token tiles share each widened operand (4 waves per block), with the
+// scale carried by the operand for every group size, as in the 4-bit kernel.
 namespace {
 
 template <int MT>

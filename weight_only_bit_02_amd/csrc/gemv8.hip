@@ -122,6 +122,8 @@ __global__ void __launch_bounds__(256)
 // channels. Scales as in the 4-bit kernel: a fresh partial tile per group (one per step
 // for 128-channel groups, one per half for 64), and for 32-channel groups, where the two
 // lane halves of a slice lie in different groups, the fp16 operand carries the scale.
+// M = 33..64: two 32-token tiles share each widened operand (4 waves per block), with the
+// scale carried by the operand for every group size, as in the 4-bit kernel.
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
