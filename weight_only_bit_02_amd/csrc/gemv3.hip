@@ -26,36 +26,27 @@ __device__ __forceinline__ uint32_t magic_6400() {
   return m;
 }
 
-// Sum over the 16 pairs of a chunk of x * (q - z), with the low-plane field masked in place:
-// pair p = 4 a + e (e = p % 4) reads its 2 low bits at bits 2e, 2e + 1 of low word a / 2,
-// shifted right by 8 for odd a (one shift per 4 pairs), and its high bit moved to bit 2e + 2
-// (one shift) and merged by a bit-field insert, so the fp16 half is 1024 + 4^e q, exactly
-// (4^3 * 7 < 1024). Subtracting 1024 + 4^e z leaves 4^e (q - z), exact; the pairs of each e
-// accumulate in their own fp32 partial, whose power-of-two factor is removed at the end (it
-// commutes with every rounding, so each partial equals its unscaled sum).
-__device__ __forceinline__ float chunk_dot3(uint2 lo, uint32_t hi, uint32_t z, const half2v (&xq)[16],
-                                            uint32_t magic) {
+// Sum over the 16 pairs of a chunk of x * q (the zero point is taken out by the caller:
+// sum x (q - z) = sum x q - z sum x). Pair p = 4 a + e (e = p % 4) keeps its 2 low bits in
+// place, at bits 2e, 2e + 1 of low word a / 2 (shifted right by 8 for odd a: one shift per
+// 4 pairs), and its high bit is moved to bit 2e + 2 (one shift) and inserted (v_bfi_b32).
+// The pair is then the fp16 subnormal pair 4^e q 2^-24, exactly (4^3 * 7 < 1024), which
+// v_dot2 multiplies by the activations exactly and accumulates in fp32; each e has its own
+// partial, and the powers of two (4^-e 2^24) are removed at the end (they commute with the
+// rounding). One shift, one AND, one insert and one dot per pair.
+__device__ __forceinline__ float chunk_dot3(uint2 lo, uint32_t hi, const half2v (&xq)[16]) {
   const uint32_t lw[4] = {lo.x, lo.x >> 8, lo.y, lo.y >> 8};
-  half2v zz[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const uint32_t zb = 0x6400u + (z << (2 * e));  // fp16 of 1024 + 4^e z
-    zz[e] = -__builtin_bit_cast(half2v, zb | (zb << 16));
-  }
   float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int p = 0; p < 16; ++p) {
     const int e = p & 3, sh = p - 2 * e - 2;  // high bit p -> bit 2e + 2
     const uint32_t hm = 0x00040004u << (2 * e);
     const uint32_t hs = sh > 0 ? (hi >> sh) : sh < 0 ? (hi << -sh) : hi;
-    // (low word & field mask) | magic, then the high bit inserted: one VALU op each (the
-    // compiler otherwise spends an AND on each operand and an OR3)
-    uint32_t lm, u;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(lm) : "v"(lw[p >> 2]), "s"(0x00030003u << (2 * e)), "v"(magic));
-    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(u) : "s"(hm), "v"(hs), "v"(lm));
-    part[e] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, u) + zz[e], xq[p], part[e], false);
+    uint32_t u;
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(u) : "s"(hm), "v"(hs), "v"(lw[p >> 2] & (0x00030003u << (2 * e))));
+    part[e] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, u), xq[p], part[e], false);
   }
-  return part[0] + part[1] * 0.25f + part[2] * 0.0625f + part[3] * 0.015625f;
+  return (part[0] + part[1] * 0.25f + part[2] * 0.0625f + part[3] * 0.015625f) * 16777216.0f;
 }
 
 __device__ __forceinline__ uint32_t zero_nibble(const uint8_t* zrow, int64_t g) {
@@ -209,11 +200,25 @@ __global__ void __launch_bounds__(256)
     }
   }
   __builtin_amdgcn_sched_barrier(0);
+  // U * 256 >= K / 8 entries, then the fp32 sum of each 32-channel chunk (four
+  // consecutive lanes hold one chunk's activations)
+  float* xsum = reinterpret_cast<float*>(xs + U * 256);
+  const half2v one = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
-  for (int j = 0; j < U; ++j) xs[j * 256 + tid] = vgpr_copy(v[j]);  // U * 256 >= K / 8 entries
+  for (int j = 0; j < U; ++j) {
+    const int i = j * 256 + tid;
+    xs[i] = vgpr_copy(v[j]);
+    float t = 0.0f;
+    t = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, v[j].x), one, t, false);
+    t = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, v[j].y), one, t, false);
+    t = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, v[j].z), one, t, false);
+    t = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, v[j].w), one, t, false);
+    t += __shfl_xor(t, 1);
+    t += __shfl_xor(t, 2);
+    if ((i & 3) == 0) xsum[i >> 2] = t;
+  }
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // LDS only: codes stay in flight
 
-  const uint32_t magic = magic_6400();
   float sums[RPW];
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
@@ -231,8 +236,8 @@ __global__ void __launch_bounds__(256)
           xq[w * 4 + 2] = __builtin_bit_cast(half2v, xv.z);
           xq[w * 4 + 3] = __builtin_bit_cast(half2v, xv.w);
         }
-        const uint32_t z = ((uint32_t)zb[r][u] >> (4 * ((c >> gsh) & 1))) & 0xFu;
-        acc = __builtin_fmaf(h2f(sc[r][u]), chunk_dot3(lo[r][u], hi[r][u], z, xq, magic), acc);
+        const float z = (float)(((uint32_t)zb[r][u] >> (4 * ((c >> gsh) & 1))) & 0xFu);
+        acc = __builtin_fmaf(h2f(sc[r][u]), __builtin_fmaf(-z, xsum[c], chunk_dot3(lo[r][u], hi[r][u], xq)), acc);
       }
     }
     sums[r] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_sum(acc)), 0));
@@ -515,7 +520,7 @@ static hipError_t launch_gemv3_1x(const uint16_t* X, const uint32_t* qw, const u
   const int64_t waves = GATED ? N / 2 : (N + RPW - 1) / RPW;
   const int64_t blocks = (waves + 3) / 4;
   hipLaunchKernelGGL((k_gemv3_1<U, RPW, GATED>), dim3((unsigned)blocks), dim3(256),
-                     (size_t)U * 256 * 16, stream, X, qw, sc, z, N, K, gsh, Y);
+                     (size_t)U * 256 * 17, stream, X, qw, sc, z, N, K, gsh, Y);
   return hipGetLastError();
 }
 
