@@ -27,6 +27,19 @@ on), so each part is measured in the steady state it has in service; HIP events 
 launch stream bracket each phase. The headline value is the GEMV bandwidth; the GEMM
 rate is reported beside it.
 
+Beside the step, the same run measures and reports:
+  * the chip's peaks, measured in this process: a read stream at the fused decode
+    launch's size, at 1 GiB and at 8 GiB, and an fp16 MFMA loop; every roofline fraction
+    is given against the published peak (`frac`) and the measured one;
+  * per-replay distributions (median, p10, p90 over --reps replays) of every part, and
+    the GPU clocks before and after;
+  * the single-linear workload (K = N = 1024: search with T = 256, pack, M = 1 and 16);
+  * the Llama-2-70B decode sweep: 80 layers' packed weights resident (35.6 GB), M = 1
+    and M = 32;
+  * the single-layer "hot" decode (105 MB, resident in the last-level cache; labelled);
+  * the crossover table, the format variants, and the CPU oracle on the host cores
+    (one thread and all threads) on bounded samples.
+
 Prints ONE JSON line. `python bench.py --gpus N` with N > 1 exits: this build runs
 on one GPU.
 """
@@ -37,6 +50,7 @@ import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -48,6 +62,7 @@ FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published
 CALIB_T = 512
 PREFILL_M = 2048
 DECODE_LAYERS = 32
+LAYERS_70B = 80
 GROUP = 128
 
 MATRICES = [  # name, search group, row offset inside the group, N, K
@@ -57,6 +72,10 @@ MATRICES = [  # name, search group, row offset inside the group, N, K
     ("down_proj", "down", 0, 4096, 11008),
 ]
 SEARCH_GROUPS = {"qkv": (12288, 4096), "o": (4096, 4096), "gate_up": (22016, 4096), "down": (4096, 11008)}
+# Llama-2-70B decoder layer as launched in decode: q|k|v (GQA, 8 kv heads), o, gate|up
+# (fused, SiLU epilogue), down
+GROUPS_70B = {"qkv": (10240, 8192), "o": (8192, 8192), "gate_up": (57344, 8192), "down": (8192, 28672)}
+GATED = {"gate_up"}  # the fused MLP module: SiLU(gate) * up in the launch's epilogue
 
 
 def packed_bytes(N, K, group=GROUP, w_bit=4):
@@ -66,11 +85,19 @@ def packed_bytes(N, K, group=GROUP, w_bit=4):
 
 
 def linear_bytes(M, N, K, gated=False, group=GROUP, w_bit=4):
-    """Algorithmic HBM bytes of one W4A16 linear: packed weight + X + Y (gated: Y is N/2 wide)."""
+    """Algorithmic HBM bytes of one W4A16 linear: the packed weight, X and Y as written
+    (a gated launch writes Y of N/2 columns: SiLU(gate) * up)."""
     return packed_bytes(N, K, group, w_bit) + 2 * M * K + 2 * M * (N // 2 if gated else N)
 
 
-GATED = {"gate_up"}  # the fused MLP module: SiLU(gate) * up in the launch's epilogue
+def kernel_source_hash(files=("gemv.hip", "common.hpp")):
+    """Hash of the sources of the measured decode kernel (HBM counters are reported only
+    while these are unchanged)."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "weight_only_bit_02_amd", "csrc")
+    for f in files:
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def source_hash():
@@ -81,6 +108,114 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
+def pct(v, q):
+    s = sorted(v)
+    if not s:
+        return None
+    i = min(len(s) - 1, max(0, int(round(q * (len(s) - 1)))))
+    return s[i]
+
+
+def dist(ms_list):
+    """median / p10 / p90 / mean of per-replay times (ms)."""
+    return {"median_ms": round(pct(ms_list, 0.5), 5), "p10_ms": round(pct(ms_list, 0.1), 5),
+            "p90_ms": round(pct(ms_list, 0.9), 5), "mean_ms": round(sum(ms_list) / len(ms_list), 5),
+            "n": len(ms_list)}
+
+
+def gpu_clocks():
+    """Current GPU shader and memory clocks as the driver reports them (rocm-smi), or None."""
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        d = json.loads(r.stdout)
+        card = d[sorted(d)[0]]
+        return {k: v for k, v in card.items() if "sclk" in k or "mclk" in k or "fclk" in k}
+    except Exception as e:  # noqa: BLE001 -- clocks are context only
+        return {"error": type(e).__name__}
+
+
+class Timer:
+    """Per-replay HIP event pairs on one stream."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+
+    def replays(self, fn, reps):
+        ev = [(self.torch.cuda.Event(enable_timing=True), self.torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for a, b in ev:
+            a.record(self.stream)
+            fn()
+            b.record(self.stream)
+        ev[-1][1].synchronize()
+        return [a.elapsed_time(b) for a, b in ev]
+
+    def block(self, fn, reps):
+        a, b = self.torch.cuda.Event(enable_timing=True), self.torch.cuda.Event(enable_timing=True)
+        a.record(self.stream)
+        for _ in range(reps):
+            fn()
+        b.record(self.stream)
+        b.synchronize()
+        return a.elapsed_time(b) / reps
+
+
+def capture(torch, stream, fn):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        fn()
+    return g
+
+
+# ---------------------------------------------------------------------------- peaks
+def measure_peaks(torch, lib, dev, stream, timer, reps, sizes):
+    """Read-stream bandwidth at each size and the fp16 MFMA rate, measured on this machine."""
+    import ctypes as C
+    out = {"read_stream": {}, "method": "awq_peak_read_stream / awq_peak_mfma (include/awq_peaks.h); "
+                                        "median over replays, HIP events"}
+    for label, nbytes in sizes:
+        n = nbytes // 16 * 16
+        buf = torch.empty(n, dtype=torch.uint8, device=dev)
+        buf.fill_(7)
+        sink = torch.empty(4 * (n // 16384 + 1), dtype=torch.int32, device=dev)
+        best = None
+        for per_thread in (4, 8, 16):
+            def run(u=per_thread, buf=buf):
+                lib.awq_peak_read_stream(C.c_void_p(buf.data_ptr()), n, C.c_void_p(sink.data_ptr()),
+                                         u, C.c_void_p(stream.cuda_stream))
+            with torch.cuda.stream(stream):
+                for _ in range(3):
+                    run()
+                g = capture(torch, stream, run)
+                t = timer.replays(g.replay, reps if nbytes < 2 ** 31 else max(5, reps // 5))
+            med = pct(t, 0.5)
+            if best is None or med < best[0]:
+                best = (med, per_thread, t)
+        med, per_thread, t = best
+        out["read_stream"][label] = {"bytes": n, "gbs": round(n / (med * 1e-3) / 1e9, 1),
+                                     "gbs_p10": round(n / (pct(t, 0.9) * 1e-3) / 1e9, 1),
+                                     "gbs_p90": round(n / (pct(t, 0.1) * 1e-3) / 1e9, 1),
+                                     "median_us": round(med * 1e3, 3), "loads_per_thread": per_thread}
+        del buf, sink
+    fs = torch.empty(4 * 8192, dtype=torch.float32, device=dev)
+    iters, blocks = 4096, 2048  # 8 waves per CU
+    flops = blocks * 4 * iters * 8 * 2 * 32 * 32 * 16
+
+    def mfma():
+        lib.awq_peak_mfma(iters, C.c_void_p(fs.data_ptr()), blocks, C.c_void_p(stream.cuda_stream))
+    with torch.cuda.stream(stream):
+        mfma()
+        g = capture(torch, stream, mfma)
+        t = timer.replays(g.replay, max(10, reps // 5))
+    out["mfma_f16_tflops"] = round(flops / (pct(t, 0.5) * 1e-3) / 1e12, 1)
+    out["mfma_loop"] = {"blocks": blocks, "waves_per_block": 4, "iters": iters,
+                        "median_ms": round(pct(t, 0.5), 4)}
+    torch.cuda.synchronize()
+    return out
+
+
+# ---------------------------------------------------------------------------- crossover
 def crossover(awq, packed, dev, stream, ms=(1, 2, 4, 8, 16, 32, 64), reps=20):
     """GEMV vs GEMM time (us) over the four 7B groups per M (one launch per group, events
     around `reps` back-to-back sweeps): the data behind the M <= awq_gemv_max_m dispatch."""
@@ -107,6 +242,7 @@ def crossover(awq, packed, dev, stream, ms=(1, 2, 4, 8, 16, 32, 64), reps=20):
     return out
 
 
+# ---------------------------------------------------------------------------- variants
 # Format variants measured beside the headline (4-bit, asymmetric, 128-channel groups):
 # the same parts on the same inputs with one config field changed each.
 VARIANTS = {"group64": {"group_size": 64}, "group32": {"group_size": 32},
@@ -171,9 +307,7 @@ def time_variants(awq, si, dev, stream, Xcal, Wg, s_best, xdec, xpre, steps, war
             torch.cuda.synchronize()
             y_eager = {g: yfus[g].clone() for g in yfus}
             for pname, fn in parts.items():
-                graph = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(graph, stream=stream):
-                    fn()
+                graph = capture(torch, stream, fn)
                 for _ in range(warmup):
                     graph.replay()
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -215,38 +349,185 @@ def time_variants(awq, si, dev, stream, Xcal, Wg, s_best, xdec, xpre, steps, war
     return out
 
 
-def cpu_baseline(budget_s: float = 15.0):
-    """The CPU oracle's W4A16 linear at M = 1 on the 7B matrices, bounded to ~budget_s."""
+# ---------------------------------------------------------------------------- single linear
+def single_linear(awq, si, dev, stream, timer, reps):
+    """The single-linear workload: K = N = 1024, W ~ N(0, 0.02^2), calibration X of 256
+    tokens with 10 outlier channels x20; the 20-point search, the pack with the chosen
+    scale, and the linear at M = 1 and M = 16."""
+    import torch
+    N = K = 1024
+    W = si.torch_weights(N, K, 7000, dev)
+    Xc = si.torch_activations(256, K, 7001, dev, channel_offset=K)
+    xs = {M: si.torch_activations(M, K, 7002 + M, dev, channel_offset=K) for M in (1, 16)}
+    ws = awq.SearchWorkspace(256, N, K, dev)
+    with torch.cuda.stream(stream):
+        res = awq.search_scales(Xc, W, workspace=ws)
+        p = awq.quantize_pack(W, res.s_best)
+        ys = {M: awq.linear_w4a16(xs[M], p) for M in xs}
+        parts = {"search": lambda: awq.search_scales(Xc, W, workspace=ws, out=res),
+                 "quant_pack": lambda: awq.quantize_pack(W, res.s_best, out=p)}
+        for M in xs:
+            parts[f"linear_m{M}"] = (lambda M=M: awq.linear_w4a16(xs[M], p, out=ys[M]))
+        out = {"workload": "single linear K=N=1024, calibration T=256, 20 alpha, group 128; "
+                           "linear at M=1 and M=16"}
+        for name, fn in parts.items():
+            # 32 calls per graph: one call of this size is a few microseconds
+            def many(fn=fn):
+                for _ in range(32):
+                    fn()
+            g = capture(torch, stream, many)
+            g.replay()
+            t = [x / 32 for x in timer.replays(g.replay, reps)]
+            out[name] = {"us_median": round(pct(t, 0.5) * 1e3, 3), "us_p10": round(pct(t, 0.1) * 1e3, 3),
+                         "us_p90": round(pct(t, 0.9) * 1e3, 3)}
+    out["search"]["tflops_algorithmic"] = round(2 * 256 * N * K * 20 / (out["search"]["us_median"] * 1e-6) / 1e12, 2)
+    out["quant_pack"]["gbs"] = round((2 * N * K + packed_bytes(N, K)) / (out["quant_pack"]["us_median"] * 1e-6) / 1e9, 1)
+    for M in xs:
+        out[f"linear_m{M}"]["gbs"] = round(linear_bytes(M, N, K) / (out[f"linear_m{M}"]["us_median"] * 1e-6) / 1e9, 1)
+    out["best_alpha_index"] = int(res.best_idx.item())
+    out["note"] = "each figure is one call's time inside a graph of 32 back-to-back calls (L2-resident operands)"
+    return out
+
+
+# ---------------------------------------------------------------------------- 70B sweep
+def sweep_70b(awq, si, dev, stream, timer, reps, log):
+    """Decode over 80 Llama-2-70B layers whose packed weights (35.6 GB) are all resident:
+    per layer q|k|v, o, gate|up (fused, SiLU epilogue) and down, at M = 1 and M = 32."""
+    import torch
+    log(f"bench: packing {LAYERS_70B} Llama-2-70B layers")
+    layers = []
+    with torch.cuda.stream(stream):
+        for c in range(LAYERS_70B):
+            layer = {}
+            for i, (g, (N, K)) in enumerate(GROUPS_70B.items()):
+                w = si.torch_weights(N, K, 20000 + 7 * c + i, dev)
+                layer[g] = awq.quantize_pack(w)
+                del w
+            layers.append(layer)
+        torch.cuda.synchronize()
+    resident = sum(p.nbytes() for layer in layers for p in layer.values())
+    out = {"workload": "Llama-2-70B decoder layers (q|k|v 10240x8192, o 8192x8192, gate|up 2x28672x8192 "
+                       "fused with SiLU epilogue, down 8192x28672), 80 layers resident",
+           "resident_packed_bytes": resident, "launches_per_sweep": 4 * LAYERS_70B}
+    for M in (1, 32):
+        xin = {K: si.torch_activations(M, K, 21000 + K + M, dev, channel_offset=K) for K in (8192, 28672)}
+        ys = {g: torch.empty((M, N // 2 if g in GATED else N), dtype=torch.float16, device=dev)
+              for g, (N, K) in GROUPS_70B.items()}
+
+        def sweep():
+            for layer in layers:
+                for g, (N, K) in GROUPS_70B.items():
+                    linear = awq.linear_w4a16_gated_silu if g in GATED else awq.linear_w4a16
+                    linear(xin[K], layer[g], out=ys[g])
+        with torch.cuda.stream(stream):
+            sweep()
+            g = capture(torch, stream, sweep)
+            for _ in range(2):
+                g.replay()
+            t = timer.replays(g.replay, max(10, reps // 3))
+        nbytes = LAYERS_70B * sum(linear_bytes(M, N, K, gname in GATED) for gname, (N, K) in GROUPS_70B.items())
+        flops = LAYERS_70B * sum(2 * M * N * K for N, K in GROUPS_70B.values())
+        med = pct(t, 0.5)
+        out[f"m{M}"] = {"gbs": round(nbytes / (med * 1e-3) / 1e9, 1), "ms_median": round(med, 4),
+                        "ms_p10": round(pct(t, 0.1), 4), "ms_p90": round(pct(t, 0.9), 4),
+                        "frac": round(nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "tflops": round(flops / (med * 1e-3) / 1e12, 2), "bytes": nbytes,
+                        "kernel": "vector GEMV" if M == 1 else "skinny MFMA GEMV"}
+        log(f"bench: 70B decode M={M}: {out[f'm{M}']['gbs']:.0f} GB/s")
+        del g
+    del layers
+    torch.cuda.empty_cache()
+    return out
+
+
+# ---------------------------------------------------------------------------- CPU oracle
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline():
+    """The CPU oracle (plain NumPy, fp64 where the method's arithmetic is exact) timed on
+    this machine's host cores on bounded samples of the benchmark's work, with one BLAS thread
+    and with all of them. The headline figure is the oracle's W4A16 linear at M = 1 (the
+    GPU's headline metric) with all threads."""
     import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
     import oracle
     import synthetic_inputs as si
-    done_bytes, wall, cpu, names = 0, 0.0, 0.0, []
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    # inputs (untimed)
+    mats = {}
     for i, (name, _, _, N, K) in enumerate(MATRICES):
         W = si.weights(N, K, offset=500 + i)
-        qw, sc, zb, _ = oracle.quantize_pack(W)
-        x = si.activations(1, K, offset=600 + i)
-        t0, c0 = time.perf_counter(), time.process_time()
-        oracle.linear_reference(x, qw, sc, zb, K)
-        wall += time.perf_counter() - t0
-        cpu += time.process_time() - c0
-        done_bytes += linear_bytes(1, N, K)
-        names.append(name)
-        if wall > budget_s:
-            break
-    return {"value": round(done_bytes / wall / 1e9, 4), "unit": "GB/s",
-            "cores": max(1, round(cpu / wall)), "kind": "oracle",
-            "sample": f"oracle fp64 W4A16 linear, M=1, on {len(names)} of the 7 Llama-2-7B matrices "
-                      f"({', '.join(names)}); {done_bytes / 1e6:.1f} MB algorithmic in {wall:.2f} s"}
+        mats[name] = (W, oracle.quantize_pack(W)[:3], si.activations(1, K, offset=600 + i, channel_offset=K))
+    W_o, pk_o, _ = mats["o_proj"]
+    x16 = si.activations(16, 4096, offset=616, channel_offset=4096)
+    x2048 = si.activations(2048, 4096, offset=617, channel_offset=4096)
+    rows2048 = 512  # sample: the M = 2048 linear on 512 of o_proj's 4096 rows
+    pk_o_rows = tuple(a[:rows2048] for a in pk_o)
+    Wc1 = si.weights(1024, 1024, offset=7000)
+    Xc1 = si.activations(256, 1024, offset=7001, channel_offset=1024)
+    Xc4 = si.activations(CALIB_T, 4096, offset=7100, channel_offset=4096)
+
+    legs = {}
+    blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+    all_threads = max((p.get("num_threads", 1) for p in blas), default=1)
+    for label, nthreads in (("threads_1", 1), ("threads_all", all_threads)):
+        with threadpool_limits(limits=nthreads, user_api="blas"):
+            r = {}
+            t = sum(timed(lambda m=m: oracle.linear_reference(m[2], *m[1], m[0].shape[1])) for m in mats.values())
+            b = sum(linear_bytes(1, m[0].shape[0], m[0].shape[1]) for m in mats.values())
+            r["linear_m1"] = {"gbs": round(b / t / 1e9, 4), "s": round(t, 3),
+                              "sample": "7 Llama-2-7B matrices, M=1"}
+            t = timed(lambda: oracle.linear_reference(x16, *pk_o, 4096))
+            r["linear_m16"] = {"gbs": round(linear_bytes(16, 4096, 4096) / t / 1e9, 4), "s": round(t, 3),
+                               "sample": "o_proj 4096x4096, M=16"}
+            t = timed(lambda: oracle.linear_reference(x2048, *pk_o_rows, 4096))
+            r["linear_m2048"] = {"gflops": round(2 * 2048 * rows2048 * 4096 / t / 1e9, 3), "s": round(t, 3),
+                                 "sample": f"o_proj rows 0..{rows2048 - 1} (of 4096), M=2048"}
+            pack_names = ("q_proj", "o_proj", "down_proj")
+            t = sum(timed(lambda n=n: oracle.quantize_pack(mats[n][0])) for n in pack_names)
+            b = sum(2 * mats[n][0].size + packed_bytes(*mats[n][0].shape) for n in pack_names)
+            r["quant_pack"] = {"gbs": round(b / t / 1e9, 4), "s": round(t, 3),
+                               "sample": "O1-O6 on q_proj, o_proj, down_proj (3 of the 7 matrices)"}
+            t = timed(lambda: oracle.search_scales(Xc1, Wc1))
+            r["search_single_linear"] = {"gflops": round(2 * 256 * 1024 * 1024 * 20 / t / 1e9, 3), "s": round(t, 3),
+                                         "sample": "full 20-point search, K=N=1024, T=256"}
+            t = timed(lambda: oracle.search_errors(Xc4, W_o, grid_points=[7]))
+            r["search_7b_block"] = {"gflops": round(2 * CALIB_T * 4096 * 4096 / t / 1e9, 3), "s": round(t, 3),
+                                    "sample": "one grid point of the o_proj search (T=512); the full 7B "
+                                              "block search is 4.145 TFLOP (4 groups x 20 points)",
+                                    "est_full_block_s": round(t * 4.145e12 / (2 * CALIB_T * 4096 * 4096), 1)}
+            legs[label] = r
+    nproc = os.cpu_count()
+    return {"value": legs["threads_all"]["linear_m1"]["gbs"], "unit": "GB/s", "cores": all_threads,
+            "kind": "oracle",
+            "sample": "oracle fp64 W4A16 linear, M=1, on the 7 Llama-2-7B matrices (105.3 MB algorithmic), "
+                      f"{all_threads} BLAS threads; other legs below, with 1 and {all_threads} threads",
+            "nproc": nproc, "cpu_model": cpu_model(), "blas": blas[0].get("internal_api") if blas else None,
+            "legs": legs}
 
 
 def load_traffic(kernel_key):
     """HBM bytes per launch measured with rocprofv3 counters (profiles/traffic.json), or None
-    when the kernels changed since the counters were taken."""
+    when the measured kernel's sources changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     d = json.load(open(path))
-    if d.get("source_hash") != source_hash():
+    if d.get("kernel_source_hash") != kernel_source_hash():
         return None
     return d.get("kernels", {}).get(kernel_key)
 
@@ -254,12 +535,15 @@ def load_traffic(kernel_key):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--reps", type=int, default=50, help="replays per part for the distributions")
     ap.add_argument("--layers", type=int, default=DECODE_LAYERS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the format variants (64/32-channel groups, symmetric, 8- and 3-bit)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the headline step (no peaks, distributions, 70B, single linear, crossover)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying graphs")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="first run one plain device copy of BYTES (a known-size kernel for "
@@ -273,10 +557,12 @@ def main():
     import torch
     import synthetic_inputs as si
     import weight_only_bit_02_amd as awq
+    from weight_only_bit_02_amd import _abi
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
+    lib = _abi.load()
     if args.copy_probe:
         src = torch.empty(args.copy_probe, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -342,6 +628,12 @@ def main():
             for name, _, _, N, K in MATRICES:
                 awq.linear_w4a16(xdec[K], views[c][name], out=ydec[name])
 
+    def part_gemv_hot():  # the same four launches on ONE layer copy, 32 times (cache-resident)
+        for _ in range(args.layers):
+            for g, (N, K) in SEARCH_GROUPS.items():
+                linear = awq.linear_w4a16_gated_silu if g in GATED else awq.linear_w4a16
+                linear(xdec[K], packed[0][g], out=yfus[g])
+
     # The equivalent transform's other half: each group's 1/s folded into what produces its
     # input -- the two norm weights (q|k|v, gate|up), the v_proj rows (o), the up_proj rows
     # (down) -- out of place, so the search inputs are untouched.
@@ -354,7 +646,7 @@ def main():
     # Weight clipping after the scale search: 20 shrink ratios (r = 1 .. 0.905 on the
     # clip_steps = 200 grid) per group of each group's W diag(s).
     CLIP_SHRINK = 20
-    clip_ws = {g: torch.empty(awq.load_library().awq_clip_search_workspace_size(CALIB_T, N, K, CLIP_SHRINK, None),
+    clip_ws = {g: torch.empty(lib.awq_clip_search_workspace_size(CALIB_T, N, K, CLIP_SHRINK, None),
                               dtype=torch.uint8, device=dev) for g, (N, K) in SEARCH_GROUPS.items()}
     clip_out = {}
 
@@ -373,9 +665,9 @@ def main():
             linear(xpre[K], packed[0][g], out=ypre[g])
 
     parts = [("search", part_search), ("clip", part_clip), ("quant_pack", part_pack), ("fold", part_fold),
-             ("gemv", part_gemv),
-             ("gemv_unfused", part_gemv_unfused), ("gemm", part_gemm)]
+             ("gemv", part_gemv), ("gemv_unfused", part_gemv_unfused), ("gemm", part_gemm)]
     stream = torch.cuda.Stream()
+    timer = Timer(torch, stream)
     runners = {}
     with torch.cuda.stream(stream):
         for _, fn in parts:  # eager warm-up (also loads the code objects)
@@ -385,13 +677,7 @@ def main():
                      "y": {n: ydec[n].clone() for n in ydec}, "yf": {g: yfus[g].clone() for g in yfus},
                      "Y": {g: ypre[g].clone() for g in ypre}, "fold": [o.clone() for o in fold_out]}
         for pname, fn in parts:
-            if args.no_graph:
-                runners[pname] = fn
-            else:
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=stream):
-                    fn()
-                runners[pname] = g.replay
+            runners[pname] = fn if args.no_graph else capture(torch, stream, fn).replay
         torch.cuda.synchronize()
 
         # Timed in phases: the K steps run part by part (K decode sweeps, then K prefill
@@ -405,6 +691,7 @@ def main():
             for _ in range(args.warmup):
                 runners[pname]()
         torch.cuda.synchronize()
+        clocks_before = None if args.no_extras else gpu_clocks()
         ev = {pname: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for pname in order}
         log(f"bench: timing {args.steps} steps")
@@ -418,6 +705,7 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         part_ms = {pname: ev[pname][0].elapsed_time(ev[pname][1]) / args.steps for pname in order}
+        clocks_after = None if args.no_extras else gpu_clocks()
 
         # graph replays must reproduce the eager results bit for bit
         for g in SEARCH_GROUPS:
@@ -428,6 +716,17 @@ def main():
             assert torch.equal(ydec[n], eager_ref["y"][n]), "graph replay differs (gemv, per matrix)"
         for o, e in zip(fold_out, eager_ref["fold"]):
             assert torch.equal(o, e), "graph replay differs (fold)"
+
+        # per-replay distributions (after the timed steps, the same graphs)
+        distributions = {}
+        if not args.no_extras:
+            log(f"bench: distributions over {args.reps} replays per part")
+            for pname in order:
+                runners[pname]()
+                distributions[pname] = dist(timer.replays(runners[pname], args.reps))
+            hot = runners["gemv_hot"] = capture(torch, stream, part_gemv_hot).replay
+            hot()
+            distributions["gemv_hot"] = dist(timer.replays(hot, args.reps))
 
     # ------------------------------------------------------------------ figures
     n_gemv = args.layers * len(SEARCH_GROUPS)
@@ -471,18 +770,20 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(gemv_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gemv_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "k_gemv1 (M=1)",
+                     "kernel": "awq::k_gemv1s (M=1 decode GEMV; q|k|v, o, gate|up gated, down)",
                      "avg_launch_us": round(part_ms["gemv"] * 1e3 / n_gemv, 3),
                      "algorithmic_bytes_per_launch": round(gemv_bytes / n_gemv)},
         "gemm": {"tflops": round(gemm_tflops, 2), "ms": round(part_ms["gemm"], 4),
                  "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2),
                               "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                              "frac": round(gemm_tflops / FP16_MFMA_PEAK_TFLOPS, 4)}},
+                              "frac": round(gemm_tflops / FP16_MFMA_PEAK_TFLOPS, 4),
+                              "kernel": "awq::k_gemm"}},
         "search": {"tflops_algorithmic": round(search_tflops, 2), "ms": round(part_ms["search"], 4),
                    "best_alpha_index": best,
                    "roofline": {"bound": "mfma", "achieved": round(search_tflops, 2),
                                 "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                "frac": round(search_tflops / FP16_MFMA_PEAK_TFLOPS, 4)}},
+                                "frac": round(search_tflops / FP16_MFMA_PEAK_TFLOPS, 4),
+                                "kernel": "awq::k_search_err (plus its statistic, scale and reduce kernels)"}},
         "clip_search": {"tflops_algorithmic": round(clip_tflops, 2), "ms": round(part_ms["clip"], 4),
                         "ratios": CLIP_SHRINK, "clip_steps": 200,
                         "roofline": {"bound": "mfma", "achieved": round(clip_tflops, 2),
@@ -502,15 +803,52 @@ def main():
                             "avg_launch_us": round(part_ms["gemv_unfused"] * 1e3 / n_gemv_u, 3)},
         "source_hash": source_hash(),
     }
-    result["crossover"] = crossover(awq, packed[0], dev, stream)
+    if not args.no_extras:
+        result["clocks"] = {"before": clocks_before, "after": clocks_after}
+        result["distributions"] = distributions
+        dh = distributions["gemv_hot"]
+        result["decode_hot"] = {
+            "label": "single layer copy replayed (105 MB, resident in the 256 MB last-level cache): "
+                     "not an HBM figure",
+            "gbs": round(gemv_bytes / (dh["median_ms"] * 1e-3) / 1e9, 1), "median_ms": dh["median_ms"]}
+        log("bench: measured peaks")
+        peaks = measure_peaks(torch, lib, dev, stream, timer, args.reps,
+                              [("fused_decode_launch", round(gemv_bytes / n_gemv)),
+                               ("1GiB", 2 ** 30), ("8GiB", 2 ** 33)])
+        result["peaks"] = peaks
+        rs = peaks["read_stream"]
+        # the measured peak: the best read stream; beside it the read stream of the decode
+        # launch's own size (the same fixed launch cost per 26 MB)
+        hbm_meas = max(v["gbs"] for v in rs.values())
+        peaks["hbm_measured_gbs"] = hbm_meas
+        result["roofline"]["measured_peak"] = hbm_meas
+        result["roofline"]["frac_of_measured_peak"] = round(gemv_gbs / hbm_meas, 4)
+        result["roofline"]["same_size_read_stream_gbs"] = rs["fused_decode_launch"]["gbs"]
+        result["roofline"]["frac_of_same_size_read_stream"] = round(gemv_gbs / rs["fused_decode_launch"]["gbs"], 4)
+        for key, tf in (("gemm", gemm_tflops), ("search", search_tflops), ("clip_search", clip_tflops)):
+            result[key]["roofline"]["measured_peak"] = peaks["mfma_f16_tflops"]
+            result[key]["roofline"]["frac_of_measured_peak"] = round(tf / peaks["mfma_f16_tflops"], 4)
+        for key, gbs in (("quant_pack", pack_gbs), ("fold_inverse_scale", fold_gbs)):
+            result[key]["roofline"]["measured_peak"] = hbm_meas
+            result[key]["roofline"]["frac_of_measured_peak"] = round(gbs / hbm_meas, 4)
+        log("bench: single linear")
+        result["single_linear"] = single_linear(awq, si, dev, stream, timer, args.reps)
+        result["crossover"] = crossover(awq, packed[0], dev, stream)
     if not args.no_variants:
-        del packed, views
+        del views
+        packed = packed[:1]
         torch.cuda.empty_cache()
         result["variants"] = time_variants(awq, si, dev, stream, Xcal, Wg,
                                            {g: sres[g].s_best for g in SEARCH_GROUPS},
                                            xdec, xpre, args.steps, args.warmup, log)
+    if not args.no_extras:
+        del packed, runners
+        torch.cuda.empty_cache()
+        r70 = sweep_70b(awq, si, dev, stream, timer, args.reps, log)
+        r70["m1"]["frac_of_measured_peak"] = round(r70["m1"]["gbs"] / result["peaks"]["hbm_measured_gbs"], 4)
+        result["llama2_70b_decode"] = r70
     if not args.no_cpu_baseline:
-        log("bench: timing the CPU oracle (bounded sample)")
+        log("bench: timing the CPU oracle (bounded samples)")
         result["cpu_baseline"] = cpu_baseline()
     print(json.dumps(result), flush=True)
 

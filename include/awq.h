@@ -51,8 +51,8 @@ typedef enum awq_status {
 
 /* Quantization config ([SKILL] "如何使用该技能 / 步骤 2": quant_config zero_point, q_group_size,
  * w_bit; the page's "version" GEMM/GEMV switch becomes dispatch on M inside
- * awq_linear_w4a16). Supported: w_bit = 4, 8 ([PRACTICE] §5.1 raises w_bit when 4-bit
- * accuracy falls short) or 3 ([PRACTICE] §4.3 names 3-bit weights as the extreme low
+ * awq_linear_w4a16). Supported: w_bit = 4, 8 ([PRACTICE] §3.3: near lossless; §5.2 / §5.3
+ * raise w_bit when 4-bit accuracy falls short) or 3 ([PRACTICE] §4.3 names 3-bit weights as the extreme low
  * width), group_size = 128, 64 or 32 ([PRACTICE] §2.3:
  * 128 is the usual group, 64 and 32 also in use), zero_point = 1 or 0, 1 <= n_grid <= 64.
  * NULL config pointers mean {4, 128, 1, 20}. Every entry point takes the group size from
@@ -76,7 +76,6 @@ typedef struct awq_config {
 
 #define AWQ_FLAG_NONFINITE_INPUT 1u /* NaN or Inf met in W, s or X (outputs unspecified) */
 #define AWQ_FLAG_SCALE_CLAMPED 2u   /* a group scale above 65504 was clamped to 65504   */
-#define AWQ_FLAG_SEARCH_RANGE 4u    /* a search error term left the fp16 split's range  */
 #define AWQ_FLAG_OVERFLOW 8u        /* a finite value folded by 1/s overflowed fp16      */
 
 #define AWQ_MAX_CALIB_TOKENS 8192
@@ -164,7 +163,12 @@ awq_status awq_candidate_scales(const double* act_mean, int64_t K, const awq_con
  *   s_grid    fp16 [n_grid][K]  out (may be NULL): every candidate scale
  *   workspace device scratch of awq_search_workspace_size(T, N, K, cfg) bytes (statistics,
  *             candidate scales, partial errors and a copy of X in MFMA operand order)
- *   flags     NONFINITE_INPUT, SCALE_CLAMPED, SEARCH_RANGE
+ *   flags     NONFINITE_INPUT (a NaN or Inf in X or W, or a non-finite error), SCALE_CLAMPED
+ *   Accuracy: the contraction runs on the matrix cores with D = W - deq / s split into
+ *   fp16 hi + lo (22 significant bits) after scaling each (row, 128-channel step) of D by
+ *   its own power of two, so the errors hold about 1e-6 relative whatever the spread of s
+ *   across a row (a row whose |D| spans more than about 2^80 can overflow the fp32 running
+ *   error: the error is then non-finite and NONFINITE_INPUT is raised).
  *   Follow with awq_quantize_pack(W, s_best) to obtain the packed weights.
  */
 size_t awq_search_workspace_size(int64_t T, int64_t N, int64_t K, const awq_config* cfg);
@@ -179,6 +183,9 @@ awq_status awq_search_scales(const void* X, int64_t T, const void* W, int64_t N,
  *   "主要功能和特点" (GEMV kernel for single-token decode, GEMM kernel for batches).
  *   deq(W)_nk = (q_nk - z_nj) * sc_nj; products accumulate in fp32; Y is rounded to fp16.
  *   X fp16 [M][K]; qweight/scales/zeros as written by awq_quantize_pack; Y fp16 [M][N].
+ *   flags uint32 [1] or NULL: NONFINITE_INPUT when X or the group scales hold an Inf or a
+ *   NaN (Y is then unspecified where they reach). Only with a flags word does the call
+ *   add a scan of X and the scales (2 bytes per element) ahead of the linear kernel.
  *   Dispatch: M <= 3 runs the vector-ALU dequant-fused GEMV, M <= 64 the skinny MFMA
  *   GEMV (dots on the matrix cores, K split over the waves of a block; two 32-token tiles
  *   above M = 32), larger M the MFMA dequant-GEMM (thresholds measured on the Llama-2-7B

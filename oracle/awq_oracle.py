@@ -70,7 +70,7 @@ __all__ = [
 
 GROUP = 128                       # [AWQ-PRACTICE] §2.3; [AWQ-SKILL] q_group_size
 QMAX = 15                         # 4-bit unsigned codes 0..15 with a zero point
-W_BITS = (3, 4, 8)                # code widths: 4 (the format measured), 3 and 8 ([AWQ-PRACTICE] §5.1, §4.3)
+W_BITS = (3, 4, 8)                # code widths: 4 (the format measured), 8 ([AWQ-PRACTICE] §3.3, §5.2, §5.3) and 3 (§4.3)
 N_GRID = 20                       # alpha grid: 20 points in [0, 1)
 ACT_FLOOR = 2.0 ** -14            # floor of the activation statistic (smallest normal fp16)
 SCALE_FLOOR = np.float32(2.0 ** -14)
@@ -156,7 +156,7 @@ def quantize_groups(W16: np.ndarray, s16: np.ndarray | None = None, clip_ratio: 
       3'. sc = max(|mx|, |mn|) / 7             6'. z = 8
     so q - 8 = clamp(rint(w' / sc_h), -8, 7) is the signed code, stored offset by 8 in the
     same format (every zero nibble 8).
-    8-bit codes (w_bit = 8; [AWQ-PRACTICE] §5.1 raises w_bit when accuracy drops): the same
+    8-bit codes (w_bit = 8; [AWQ-PRACTICE] §3.3 offers it as the near-lossless setting, §5.2 / §5.3 raise w_bit when accuracy drops): the same
     steps with 15 -> 255 (codes 0..255) and, symmetric, 7 -> 127 and z = 128. 3-bit codes
     (w_bit = 3, the extreme low width [AWQ-PRACTICE] §4.3 names): 15 -> 7 (codes 0..7) and,
     symmetric, 7 -> 3 and z = 4 (signed range -4..3).

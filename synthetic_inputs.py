@@ -92,3 +92,16 @@ def torch_activations(T: int, K: int, offset: int, device, channel_offset: int =
     ch = torch.from_numpy(outlier_channels(K, channel_offset)).to(device)
     x[:, ch] *= OUTLIER_MULT
     return x.to(torch.float16)
+
+
+def activations_wide(T: int, K: int, offset: int, log2_lo: float, log2_hi: float,
+                     n_zero: int = 0) -> np.ndarray:
+    """fp16 [T][K] activations N(0, 1) times a per-channel magnitude 2^u, u uniform in
+    [log2_lo, log2_hi] (activation magnitudes spread over many octaves), with n_zero
+    channels (chosen without replacement) set to zero: dead channels."""
+    g = rng(2_000 + offset)
+    x = g.standard_normal((T, K), dtype=np.float32)
+    x *= np.exp2(g.uniform(log2_lo, log2_hi, K)).astype(np.float32)[None, :]
+    if n_zero:
+        x[:, g.choice(K, size=n_zero, replace=False)] = 0.0
+    return x.astype(np.float16)

@@ -1,4 +1,4 @@
-"""The C-ABI library loads, exports every entry point include/awq.h declares, and
+"""The C-ABI library loads, exports every entry point include/*.h declares, and
 rejects bad arguments on the host before enqueuing anything (no GPU needed: every
 call here fails validation, so no kernel is launched)."""
 
@@ -11,15 +11,18 @@ import pytest
 from weight_only_bit_02_amd import _abi
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "awq.h")
+HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if f.endswith(".h")]
 
 FAKE = C.c_void_p(0x7F0000000000)      # 16-byte aligned, never dereferenced
 FAKE_ODD = C.c_void_p(0x7F0000000008)  # misaligned
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(awq_\w+)\s*\(", text, re.M)))
+    names = set()
+    for h in HEADERS:
+        names |= set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(awq_\w+)\s*\(", open(h).read(), re.M))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -161,3 +164,16 @@ def test_clip_validation(lib):
     assert lib.awq_clip_search_workspace_size(64, 64, 256, 20, C.byref(bad)) == 0
     assert lib.awq_quantize_pack_clipped(FAKE, 64, 256, None, FAKE, 0, None, FAKE, FAKE, FAKE,
                                          None, None) == 2
+
+
+def test_peak_probes_reject_bad_arguments(lib):
+    """The calibration probes validate on the host (2 = bad argument, nothing launched)."""
+    assert lib.awq_peak_read_stream(None, 4096, FAKE, 16, None) == 2
+    assert lib.awq_peak_read_stream(FAKE, 4095, FAKE, 16, None) == 2
+    assert lib.awq_peak_read_stream(FAKE, 4096, None, 16, None) == 2
+    assert lib.awq_peak_read_stream(FAKE, 4096, FAKE, 0, None) == 2
+    assert lib.awq_peak_read_stream(FAKE, 4096, FAKE, 5, None) == 2
+    assert lib.awq_peak_mfma(0, FAKE, 16, None) == 2
+    assert lib.awq_peak_mfma(16, None, 16, None) == 2
+    assert lib.awq_peak_mfma(16, FAKE, 0, None) == 2
+

@@ -7,11 +7,12 @@ clip search (errors to 1e-5, decisions wherever the oracle's ranking is decidabl
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 import synthetic_inputs as si
 import weight_only_bit_02_amd as awq
-from tests.gpu_util import flags_tensor, host, packed_host, to_dev
+from tests.gpu_util import flags_tensor, guarded, host, packed_host, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -122,7 +123,9 @@ def test_linear_kernels(M, N, K, kernel, group):
     W = si.weights(N, K, offset=M + N + K + 8)
     ref, p = _pack_both(W, group, _s(K, M + 1))
     X = si.activations(M, K, offset=M + 6)
-    Y = host(awq.linear_w4a16(to_dev(X), p, kernel=kernel)).astype(np.float64)
+    out, check = guarded((X.shape[0], p.N), torch.float16)
+    Y = host(awq.linear_w4a16(to_dev(X), p, kernel=kernel, out=out)).astype(np.float64)
+    check()
     y_ref, bound = oracle.linear_reference(X, *ref, K)
     ok = oracle.linear_within_tolerance(Y, y_ref, bound)
     assert ok.all(), (kernel, np.argwhere(~ok)[:4])
@@ -141,7 +144,9 @@ def test_gated_kernels(M, nh, K, kernel, group):
     W = si.weights(2 * nh, K, offset=M + nh + 8)
     ref, p = _pack_both(W, group, _s(K, M + 2))
     X = si.activations(M, K, offset=M + 10)
-    H = host(awq.linear_w4a16_gated_silu(to_dev(X), p, kernel=kernel))
+    out, check = guarded((X.shape[0], p.N // 2), torch.float16)
+    H = host(awq.linear_w4a16_gated_silu(to_dev(X), p, kernel=kernel, out=out))
+    check()
     h, g, u, bg, bu = oracle.gated_silu_reference(X, *ref, K)
     assert oracle.gated_silu_within_tolerance(H, g, u, bg, bu).all(), kernel
 

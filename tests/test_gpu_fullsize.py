@@ -1,10 +1,9 @@
 """GPU parity at the full Llama-2-7B / 70B sizes, in the launch configuration the benchmark
 times (same entry points, same shapes, device-resident inputs).
 
-Where the oracle can finish the whole problem in seconds it does (quantize+pack of a
-group, the full search of o_proj and down_proj); elsewhere it checks sampled outputs
-it computes one by one (rows of a packed matrix, elements of Y), or properties that
-hold at any size (the chosen error is the smallest, s = 1 at grid point 0).
+Where the oracle can finish the whole problem in a minute or two it does (the full
+20-point search of every shared-input group); elsewhere it checks sampled outputs it
+computes one by one (rows of a packed matrix, elements of Y).
 """
 
 import functools
@@ -51,39 +50,30 @@ def test_quantize_pack_7b_group(group):
     assert np.array_equal(zb[rows], rzb)
 
 
-@pytest.mark.parametrize("group", ["o", "down"])
+@pytest.mark.parametrize("group", list(GROUPS_7B))
 def test_search_7b_group_full(group):
-    """The full 20-point search of one 7B shared-input group (T = 512), against the oracle."""
+    """The full 20-point search of each 7B shared-input group (T = 512), the benchmark's
+    searches, against the oracle: all 20 errors, the first-minimum index, every candidate
+    scale and the chosen one (q|k|v and gate|up take the oracle about a minute each)."""
     N, K = GROUPS_7B[group]
-    X = si.activations(CALIB_T, K, offset=40, channel_offset=K)
-    W = si.weights(N, K, offset=41)
+    off = {"qkv": 42, "o": 40, "gate_up": 44, "down": 46}[group]
+    X = si.activations(CALIB_T, K, offset=off, channel_offset=K)
+    W = si.weights(N, K, offset=off + 1)
+    r = awq.search_scales(to_dev(X), to_dev(W))
+    err, best = host(r.err), int(host(r.best_idx)[0])
     ref = oracle.search_errors(X, W)
-    r = awq.search_scales(to_dev(X), to_dev(W))
-    err = host(r.err)
-    assert np.all(np.abs(err - ref["err"]) <= 1e-5 * ref["err"]), np.max(np.abs(err / ref["err"] - 1))
-    if oracle.relative_gap(ref["err"]) >= 1e-5:
-        assert int(host(r.best_idx)[0]) == int(np.argmin(ref["err"]))
+    rel = np.abs(err - ref["err"]) / ref["err"]
+    assert np.all(rel <= 1e-5), (rel.max(), int(rel.argmax()))
     hazard = oracle.fp16_midpoint_distance(ref["s64"]) < 2.0 ** -40
     assert np.all((host(r.s_grid).view(np.uint16) == ref["s16"].view(np.uint16)) | hazard)
-
-
-@pytest.mark.parametrize("group", ["qkv", "gate_up"])
-def test_search_7b_group_sampled(group):
-    """The largest groups: every candidate scale exact, chosen error the smallest, and the
-    oracle's error at grid points 0, the chosen one and its neighbours."""
-    N, K = GROUPS_7B[group]
-    X = si.activations(CALIB_T, K, offset=42, channel_offset=K)
-    W = si.weights(N, K, offset=43)
-    r = awq.search_scales(to_dev(X), to_dev(W))
-    err = host(r.err)
-    best = int(host(r.best_idx)[0])
-    assert err[best] == err.min() and best == int(np.argmin(err)) and err[best] < err[0]
-    pts = sorted({0, best, max(best - 1, 0), min(best + 1, 19)})
-    ref = oracle.search_errors(X, W, grid_points=pts)
-    for i in pts:
-        assert abs(err[i] - ref["err"][i]) <= 1e-5 * ref["err"][i], (i, err[i], ref["err"][i])
-    hazard = oracle.fp16_midpoint_distance(ref["s64"]) < 2.0 ** -40
-    assert np.all((host(r.s_grid).view(np.uint16) == ref["s16"].view(np.uint16)) | hazard)
+    ref_best = 0
+    for i in range(1, len(ref["err"])):    # the oracle's first minimum
+        if ref["err"][i] < ref["err"][ref_best]:
+            ref_best = i
+    if oracle.relative_gap(ref["err"]) < 1e-5:
+        pytest.skip(f"near tie in the oracle: index parity unpinned for {group}")
+    assert best == ref_best, (best, ref_best)
+    assert np.array_equal(host(r.s_best).view(np.uint16), ref["s16"][ref_best].view(np.uint16))
 
 
 def _check_sampled_linear(X, p, W_rows_ref, rows, Y):

@@ -13,7 +13,7 @@ import torch
 import oracle
 import synthetic_inputs as si
 import weight_only_bit_02_amd as awq
-from tests.gpu_util import DEV, host, packed_host, to_dev
+from tests.gpu_util import DEV, guarded, host, packed_host, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -29,7 +29,9 @@ def _gated_case(nh, K, off):
 
 
 def _check(X, p, ref, kernel):
-    H = host(awq.linear_w4a16_gated_silu(to_dev(X), p, kernel=kernel))
+    out, check = guarded((X.shape[0], p.N // 2), torch.float16)
+    H = host(awq.linear_w4a16_gated_silu(to_dev(X), p, kernel=kernel, out=out))
+    check()
     h, g, u, bg, bu = oracle.gated_silu_reference(X, *ref, p.K)
     assert H.shape == h.shape
     ok = oracle.gated_silu_within_tolerance(H.astype(np.float64), g, u, bg, bu)
@@ -51,11 +53,31 @@ def test_gated_gemv_long_rows_and_tall(nh, K):
     _check(si.activations(1, K, offset=nh), p, ref, "gemv")
 
 
-@pytest.mark.parametrize("M", [1, 5, 8, 16, 17, 32])
+@pytest.mark.parametrize("M", [1, 5, 8, 16, 17, 32, 33, 47, 64])
 @pytest.mark.parametrize("nh,K", [(1, 128), (67, 384), (200, 1152), (40, 11008)])
 def test_gated_skinny_matches_oracle(M, nh, K):
+    """Every accumulator bucket of the skinny kernel, the two-token-tile form (M = 33..64)
+    included, with ragged outputs."""
     p, ref = _gated_case(nh, K, off=nh + 17 * K)
     _check(si.activations(M, K, offset=M + 500), p, ref, "skinny")
+
+
+@pytest.mark.parametrize("M", [33, 47, 64])
+@pytest.mark.parametrize("group", [64, 32])
+def test_gated_skinny_two_tiles_small_groups(M, group):
+    """The two-token-tile gated skinny kernel with 64- and 32-channel groups (ragged
+    outputs: 67 gate|up pairs)."""
+    nh, K = 67, 1152
+    W = si.weights(2 * nh, K, offset=M + group)
+    qw, sc, zb, _ = oracle.quantize_pack(W, None, None, True, group, 4)
+    p = awq.quantize_pack(to_dev(W), group_size=group)
+    gq, gs, gz = packed_host(p)
+    assert np.array_equal(gq, qw) and np.array_equal(gz, zb)
+    assert np.array_equal(gs.view(np.uint16), sc.view(np.uint16))
+    X = si.activations(M, K, offset=M + 600)
+    H = host(awq.linear_w4a16_gated_silu(to_dev(X), p, kernel="skinny"))
+    h, g, u, bg, bu = oracle.gated_silu_reference(X, qw, sc, zb, K)
+    assert oracle.gated_silu_within_tolerance(H.astype(np.float64), g, u, bg, bu).all()
 
 
 @pytest.mark.parametrize("M", [1, 9, 64, 130, 257])
@@ -78,9 +100,11 @@ def test_gated_zero_input_and_determinism():
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("M", [1, 2048])
+@pytest.mark.parametrize("M", [1, 64, 2048])
 def test_gated_7b_gate_up_sampled(M):
-    """Llama-2-7B gate|up (2 x 11008 rows, K = 4096): the benchmark's fused launch."""
+    """Llama-2-7B gate|up (2 x 11008 rows, K = 4096) under the automatic kernel choice: the
+    benchmark's fused decode launch (M = 1), the two-token-tile skinny kernel (M = 64) and
+    the GEMM (M = 2048)."""
     nh, K = 11008, 4096
     W = si.weights(2 * nh, K, offset=94)
     p = awq.quantize_pack(to_dev(W))

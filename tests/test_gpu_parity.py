@@ -13,7 +13,7 @@ import torch
 import oracle
 import synthetic_inputs as si
 import weight_only_bit_02_amd as awq
-from tests.gpu_util import DEV, flags_tensor, host, packed_host, to_dev
+from tests.gpu_util import DEV, flags_tensor, guarded, guarded_packed, host, packed_host, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -31,9 +31,11 @@ def _assert_pack_equal(gpu, ref):
 def test_quantize_pack_rtn(N, K):
     W = si.weights(N, K, offset=N + K)
     f = flags_tensor()
-    p = awq.quantize_pack(to_dev(W), flags=f)
+    out, check = guarded_packed(awq, N, K)
+    p = awq.quantize_pack(to_dev(W), flags=f, out=out)
     _assert_pack_equal(packed_host(p), oracle.quantize_pack(W))
     assert int(host(f)[0]) == 0
+    check()
 
 
 @pytest.mark.parametrize("N,K", [(5, 256), (260, 1024)])
@@ -193,7 +195,9 @@ def _packed_case(N, K, off):
 
 
 def _check_linear(X, p, ref_pack, kernel):
-    Y = host(awq.linear_w4a16(to_dev(X), p, kernel=kernel))
+    out, check = guarded((X.shape[0], p.N), torch.float16)
+    Y = host(awq.linear_w4a16(to_dev(X), p, kernel=kernel, out=out))
+    check()
     y_ref, bound = oracle.linear_reference(X, *ref_pack, p.K)
     ok = oracle.linear_within_tolerance(Y.astype(np.float64), y_ref, bound)
     assert ok.all(), (np.argwhere(~ok)[:5].tolist(),
@@ -273,3 +277,26 @@ def test_gemv_m1_launch_shapes(N, K):
     """Every M = 1 launch shape of the dispatch, ragged row counts included."""
     p, ref = _packed_case(N, K, off=N + K + 7)
     _check_linear(si.activations(1, K, offset=N), p, ref, "gemv")
+
+
+@pytest.mark.parametrize("kernel,M", [("gemv", 1), ("gemv", 5), ("skinny", 12), ("skinny", 40),
+                                      ("gemm", 70), ("auto", 1)])
+@pytest.mark.parametrize("where", ["x_nan", "x_inf", "scale_inf", "none"])
+def test_linear_flags_nonfinite(kernel, M, where):
+    """The linear path reports a NaN or Inf in X or in the group scales in the flags word
+    (plain and gated), and leaves it clear for finite data; Y is unchanged by the flag."""
+    N, K = 64, 384
+    p, ref = _packed_case(N, K, off=64)
+    X = si.activations(M, K, offset=65)
+    if where == "x_nan":
+        X[M - 1, 200] = np.nan
+    elif where == "x_inf":
+        X[0, 5] = -np.inf
+    elif where == "scale_inf":
+        p.scales[N - 1, 2] = float("inf")
+    for fn in (awq.linear_w4a16, awq.linear_w4a16_gated_silu):
+        f = flags_tensor()
+        Y = host(fn(to_dev(X), p, kernel=kernel, flags=f))
+        Y0 = host(fn(to_dev(X), p, kernel=kernel))
+        assert np.array_equal(Y.view(np.uint16), Y0.view(np.uint16))
+        assert int(host(f)[0]) == (0 if where == "none" else oracle.FLAG_NONFINITE_INPUT), where

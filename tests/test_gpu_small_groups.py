@@ -9,11 +9,12 @@ the linear tolerance |y - y_ref| <= 2e-3 * (|X| |deq W|). Every test runs for bo
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 import synthetic_inputs as si
 import weight_only_bit_02_amd as awq
-from tests.gpu_util import host, packed_host, to_dev
+from tests.gpu_util import guarded, host, packed_host, to_dev
 
 pytestmark = [pytest.mark.gpu, pytest.mark.parametrize("group", [64, 32])]
 
@@ -60,7 +61,9 @@ def test_pack_bit_exact(N, K, with_s, zp, group):
 def _linear_ok(X, ref, p, kernel):
     qw, sc, zb = ref
     K = X.shape[1]
-    Y = host(awq.linear_w4a16(to_dev(X), p, kernel=kernel)).astype(np.float64)
+    out, check = guarded((X.shape[0], p.N), torch.float16)
+    Y = host(awq.linear_w4a16(to_dev(X), p, kernel=kernel, out=out)).astype(np.float64)
+    check()
     y_ref, bound = oracle.linear_reference(X, qw, sc, zb, K)
     ok = oracle.linear_within_tolerance(Y, y_ref, bound)
     assert ok.all(), (kernel, np.argwhere(~ok)[:4])
@@ -114,7 +117,9 @@ def test_gated_kernels(M, nh, K, kernel, group):
     W = si.weights(2 * nh, K, offset=M + nh)
     ref, p = _pack_both(W, group, _s(K, M + 2))
     X = si.activations(M, K, offset=M + 9)
-    H = host(awq.linear_w4a16_gated_silu(to_dev(X), p, kernel=kernel))
+    out, check = guarded((X.shape[0], p.N // 2), torch.float16)
+    H = host(awq.linear_w4a16_gated_silu(to_dev(X), p, kernel=kernel, out=out))
+    check()
     h, g, u, bg, bu = oracle.gated_silu_reference(X, *ref, K)
     assert oracle.gated_silu_within_tolerance(H, g, u, bg, bu).all(), kernel
 

@@ -17,7 +17,7 @@ STATUS_NAMES = {0: "AWQ_OK", 1: "AWQ_ERR_NULL_POINTER", 2: "AWQ_ERR_BAD_SHAPE",
 
 FLAG_NONFINITE_INPUT = 1
 FLAG_SCALE_CLAMPED = 2
-FLAG_SEARCH_RANGE = 4
+FLAG_OVERFLOW = 8
 
 KERNEL_AUTO, KERNEL_GEMV, KERNEL_GEMM, KERNEL_SKINNY = 0, 1, 2, 3
 
@@ -49,6 +49,9 @@ SIGNATURES = {
     "awq_linear_w4a16_gated_silu_ex": (C.c_int, [P, I64, P, P, P, I64, I64, CFG, P, P, C.c_int, P]),
     "awq_apply_inverse_scale": (C.c_int, [P, I64, I64, P, C.c_int32, P, P, P]),
     "awq_gemv_max_m": (C.c_int32, []),
+    # calibration probes (include/awq_peaks.h)
+    "awq_peak_read_stream": (C.c_int, [P, C.c_size_t, P, C.c_int32, P]),
+    "awq_peak_mfma": (C.c_int, [I64, P, C.c_int32, P]),
     "awq_status_string": (C.c_char_p, [C.c_int]),
 }
 

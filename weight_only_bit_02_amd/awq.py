@@ -112,10 +112,15 @@ def clip_search(X: torch.Tensor, W: torch.Tensor, s: torch.Tensor | None = None,
         raise ValueError("X and W disagree on K")
     if s is not None:
         _need(s, torch.float16, "s")
+        if s.shape != (K,):
+            raise ValueError(f"s must have shape ({K},)")
+    if flags is not None:
+        _need(flags, torch.int32, "flags")
     cfg = _abi.config(zero_point=int(zero_point), group_size=group_size, w_bit=w_bit)
     nbytes = int(lib.awq_clip_search_workspace_size(T, N, K, n_shrink, C.byref(cfg)))
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=X.device)
+    _need(workspace, torch.uint8, "workspace")
     G = K // group_size
     idx = torch.empty((N, G), dtype=torch.uint8, device=X.device)
     err = torch.empty((N, G), dtype=torch.float64, device=X.device)
@@ -190,7 +195,18 @@ def search_scales(X: torch.Tensor, W: torch.Tensor, n_grid: int = 20,
                            torch.empty(1, dtype=torch.int32, device=dev),
                            torch.empty(n_grid, dtype=torch.float64, device=dev),
                            torch.empty((n_grid, K), dtype=torch.float16, device=dev))
+    _need(out.s_best, torch.float16, "out.s_best")
+    _need(out.best_idx, torch.int32, "out.best_idx")
+    _need(out.err, torch.float64, "out.err")
+    _need(out.s_grid, torch.float16, "out.s_grid")
+    if (out.s_best.shape != (K,) or out.best_idx.numel() < 1 or out.err.shape != (n_grid,)
+            or out.s_grid.shape != (n_grid, K)):
+        raise ValueError("out buffers have the wrong shapes for this search")
     ws = workspace if workspace is not None else SearchWorkspace(T, N, K, dev, n_grid)
+    if ws.buf.numel() < int(lib.awq_search_workspace_size(
+            T, N, K, C.byref(_abi.config(n_grid, zero_point=int(zero_point), group_size=group_size,
+                                         w_bit=w_bit)))):
+        raise ValueError("search workspace is too small for this shape")
     if flags is not None:
         _need(flags, torch.int32, "flags")
     cfg = _abi.config(n_grid, zero_point=int(zero_point), group_size=group_size, w_bit=w_bit)
@@ -205,10 +221,14 @@ _KERNELS = {"auto": _abi.KERNEL_AUTO, "gemv": _abi.KERNEL_GEMV, "gemm": _abi.KER
 
 
 def linear_w4a16(X: torch.Tensor, w: PackedLinear, kernel: str = "auto",
-                 out: torch.Tensor | None = None) -> torch.Tensor:
-    """awq_linear_w4a16: Y[M][N] = X[M][K] deq(W)^T in fp16 with fp32 accumulation."""
+                 out: torch.Tensor | None = None, flags: torch.Tensor | None = None) -> torch.Tensor:
+    """awq_linear_w4a16: Y[M][N] = X[M][K] deq(W)^T in fp16 with fp32 accumulation.
+    flags (int32 [1] on the GPU, optional): NONFINITE_INPUT is OR-ed in when X or the group
+    scales hold an Inf or a NaN."""
     lib = _abi.load()
     _need(X, torch.float16, "X")
+    if flags is not None:
+        _need(flags, torch.int32, "flags")
     M, K = X.shape
     if K != w.K:
         raise ValueError("X and the packed weight disagree on K")
@@ -219,16 +239,20 @@ def linear_w4a16(X: torch.Tensor, w: PackedLinear, kernel: str = "auto",
     cfg = _abi.config(group_size=w.group, w_bit=w.w_bit)
     _abi.check("awq_linear_w4a16_ex", lib.awq_linear_w4a16_ex(
         _ptr(X), M, _ptr(w.qweight), _ptr(w.scales), _ptr(w.zeros), w.N, K, C.byref(cfg),
-        _ptr(Y), None, _KERNELS[kernel], _stream()))
+        _ptr(Y), _ptr(flags), _KERNELS[kernel], _stream()))
     return Y
 
 
 def linear_w4a16_gated_silu(X: torch.Tensor, w: PackedLinear, kernel: str = "auto",
-                            out: torch.Tensor | None = None) -> torch.Tensor:
+                            out: torch.Tensor | None = None,
+                            flags: torch.Tensor | None = None) -> torch.Tensor:
     """awq_linear_w4a16_gated_silu: Y[M][N/2] = SiLU(X deq(W_gate)^T) * (X deq(W_up)^T),
-    where w packs the gate rows [0, N/2) and the up rows [N/2, N) (fused MLP module)."""
+    where w packs the gate rows [0, N/2) and the up rows [N/2, N) (fused MLP module).
+    flags as for linear_w4a16."""
     lib = _abi.load()
     _need(X, torch.float16, "X")
+    if flags is not None:
+        _need(flags, torch.int32, "flags")
     M, K = X.shape
     if K != w.K:
         raise ValueError("X and the packed weight disagree on K")
@@ -241,7 +265,7 @@ def linear_w4a16_gated_silu(X: torch.Tensor, w: PackedLinear, kernel: str = "aut
     cfg = _abi.config(group_size=w.group, w_bit=w.w_bit)
     _abi.check("awq_linear_w4a16_gated_silu_ex", lib.awq_linear_w4a16_gated_silu_ex(
         _ptr(X), M, _ptr(w.qweight), _ptr(w.scales), _ptr(w.zeros), w.N, K, C.byref(cfg),
-        _ptr(Y), None, _KERNELS[kernel], _stream()))
+        _ptr(Y), _ptr(flags), _KERNELS[kernel], _stream()))
     return Y
 
 
@@ -252,6 +276,8 @@ def apply_inverse_scale(A: torch.Tensor, s: torch.Tensor, axis: int, out: torch.
     lib = _abi.load()
     _need(A, torch.float16, "A")
     _need(s, torch.float16, "s")
+    if flags is not None:
+        _need(flags, torch.int32, "flags")
     A2 = A.reshape(1, -1) if A.dim() == 1 else A
     if A2.dim() != 2:
         raise ValueError("A must be 1-D or 2-D")

@@ -22,7 +22,7 @@ SOURCES = [  # the slowest units (GEMM instantiations, the searches) first: they
     "gemm_i3_plain.hip", "gemm_i3_gated.hip", "gemm_i3_plain_g32.hip", "gemm_i3_gated_g32.hip",
     "gemm_i8_plain.hip", "gemm_i8_gated.hip", "gemm_i4_plain.hip", "gemm_i4_gated.hip",
     "gemm_i4_plain_g32.hip", "gemm_i4_gated_g32.hip", "search.hip", "gemv.hip", "gemv_mfma.hip",
-    "gemv8.hip", "gemv3.hip", "quant_pack.hip", "stats.hip", "fold.hip", "gemm.hip", "awq_abi.hip"]
+    "gemv8.hip", "gemv3.hip", "quant_pack.hip", "stats.hip", "fold.hip", "check.hip", "peaks.hip", "gemm.hip", "awq_abi.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -38,9 +38,17 @@ FLAGS = [
 ]
 
 
+# Units whose results must be bit-exact against the oracle's step-by-step fp32 / fp64
+# arithmetic (the group quantizer, the statistic, the candidate scales, the fold): no
+# contraction of a multiply and an add into an FMA anywhere in them, not only inside the
+# functions that say so with a pragma.
+EXACT_UNITS = {"quant_pack.hip", "stats.hip", "search.hip", "fold.hip", "check.hip"}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    extra = ["-ffp-contract=off"] if src in EXACT_UNITS else []
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -31,11 +31,11 @@ awq_status hip_status(hipError_t e) { return e == hipSuccess ? AWQ_OK : AWQ_ERR_
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Search workspace: [u: int64 K][act: fp64 K][s_grid: fp16 n_grid K][rowmax: f32 N]
-// [srange: f32 n_grid][partials: fp64 n_grid x row tiles x token chunks]
+// Search workspace: [u: int64 K][act: fp64 K][s_grid: fp16 n_grid K]
+// [partials: fp64 n_grid x row tiles x token chunks]
 // [xp: X in MFMA operand order, T rounded up to 64 tokens]
 struct SearchLayout {
-  size_t u, act, sgrid, rowmax, srange, partials, xp, total;
+  size_t u, act, sgrid, partials, xp, total;
   int64_t n_partials;  // per grid point
 };
 
@@ -47,9 +47,7 @@ SearchLayout search_layout(int64_t T, int64_t N, int64_t K, int n_grid) {
   L.u = 0;
   L.act = align256(L.u + (size_t)K * 8);
   L.sgrid = align256(L.act + (size_t)K * 8);
-  L.rowmax = align256(L.sgrid + (size_t)n_grid * K * 2);
-  L.srange = align256(L.rowmax + (size_t)N * 4);
-  L.partials = align256(L.srange + (size_t)n_grid * 4);
+  L.partials = align256(L.sgrid + (size_t)n_grid * K * 2);
   L.xp = align256(L.partials + (size_t)n_grid * L.n_partials * 8);
   L.total = align256(L.xp + awq::packed_x_bytes(T, K));
   return L;
@@ -192,8 +190,7 @@ awq_status awq_search_scales(const void* X, int64_t T, const void* W, int64_t N,
   if (e == hipSuccess) e = awq::launch_scalegen(act, K, c.n_grid, sg, st);
   if (e == hipSuccess)
     e = awq::launch_search_err(Xh, T, (const uint16_t*)W, N, K, sg, c.n_grid, c.zero_point == 0,
-                               c.group_size, c.w_bit, (float*)(ws + L.rowmax), (float*)(ws + L.srange),
-                               (uint4*)(ws + L.xp), partials, flags, st);
+                               c.group_size, c.w_bit, (uint4*)(ws + L.xp), partials, flags, st);
   if (e == hipSuccess)
     e = awq::launch_search_reduce(partials, c.n_grid, L.n_partials, sg, K, (uint16_t*)s_best,
                                   best_idx, err, flags, st);
@@ -202,8 +199,8 @@ awq_status awq_search_scales(const void* X, int64_t T, const void* W, int64_t N,
 
 static awq_status linear_common(const void* X, int64_t M, const uint32_t* qweight,
                                 const void* scales, const uint8_t* zeros, int64_t N, int64_t K,
-                                const awq_config* cfg, void* Y, awq_linear_kernel kernel,
-                                bool gated, void* stream) {
+                                const awq_config* cfg, void* Y, uint32_t* flags,
+                                awq_linear_kernel kernel, bool gated, void* stream) {
   const awq_config c = resolve(cfg);
   if (!X || !qweight || !scales || !zeros || !Y) return AWQ_ERR_NULL_POINTER;
   if (!supported(c)) return AWQ_ERR_UNSUPPORTED;
@@ -215,8 +212,16 @@ static awq_status linear_common(const void* X, int64_t M, const uint32_t* qweigh
   if (kernel == AWQ_LINEAR_GEMV && M > awq::kGemvMaxM) return AWQ_ERR_BAD_SHAPE;
   if (kernel == AWQ_LINEAR_SKINNY && M > awq::kSkinnyMaxM) return AWQ_ERR_BAD_SHAPE;
   if (!aligned16(X) || !aligned16(qweight) || !aligned16(scales) || !aligned16(zeros) ||
-      !aligned16(Y))
+      !aligned16(Y) || (flags && !aligned4(flags)))
     return AWQ_ERR_MISALIGNED;
+  hipStream_t st = (hipStream_t)stream;
+  if (flags) {
+    // data conditions: a scan of X and the group scales ahead of the linear kernel
+    const hipError_t e = awq::launch_nonfinite_scan((const uint16_t*)X, M * K,
+                                                    (const uint16_t*)scales,
+                                                    N * (K / c.group_size), flags, st);
+    if (e != hipSuccess) return AWQ_ERR_HIP;
+  }
   // AUTO, measured on the Llama-2-7B layer: the vector-ALU GEMV up to M = 3 (its dot cost
   // grows with M), the MFMA skinny GEMV up to g_gemv_max_m, the MFMA GEMM above.
   if (kernel == AWQ_LINEAR_AUTO && c.w_bit != 4)
@@ -226,7 +231,6 @@ static awq_status linear_common(const void* X, int64_t M, const uint32_t* qweigh
     kernel = M <= awq::kVgemvAutoMaxM && M <= g_gemv_max_m ? AWQ_LINEAR_GEMV
              : M <= g_gemv_max_m                            ? AWQ_LINEAR_SKINNY
                                                             : AWQ_LINEAR_GEMM;
-  hipStream_t st = (hipStream_t)stream;
   const auto* Xh = (const uint16_t*)X;
   const auto* sc = (const uint16_t*)scales;
   auto* Yh = (uint16_t*)Y;
@@ -269,8 +273,7 @@ awq_status awq_linear_w4a16_ex(const void* X, int64_t M, const uint32_t* qweight
                                const void* scales, const uint8_t* zeros, int64_t N, int64_t K,
                                const awq_config* cfg, void* Y, uint32_t* flags,
                                awq_linear_kernel kernel, void* stream) {
-  (void)flags;
-  return linear_common(X, M, qweight, scales, zeros, N, K, cfg, Y, kernel, false, stream);
+  return linear_common(X, M, qweight, scales, zeros, N, K, cfg, Y, flags, kernel, false, stream);
 }
 
 awq_status awq_linear_w4a16(const void* X, int64_t M, const uint32_t* qweight,
@@ -285,8 +288,7 @@ awq_status awq_linear_w4a16_gated_silu_ex(const void* X, int64_t M, const uint32
                                           int64_t K, const awq_config* cfg, void* Y,
                                           uint32_t* flags, awq_linear_kernel kernel,
                                           void* stream) {
-  (void)flags;
-  return linear_common(X, M, qweight, scales, zeros, N, K, cfg, Y, kernel, true, stream);
+  return linear_common(X, M, qweight, scales, zeros, N, K, cfg, Y, flags, kernel, true, stream);
 }
 
 awq_status awq_linear_w4a16_gated_silu(const void* X, int64_t M, const uint32_t* qweight,

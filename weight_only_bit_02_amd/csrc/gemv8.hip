@@ -1,7 +1,8 @@
 // Vector GEMV for 8-bit codes (a7 with w_bit = 8): Y[M][N] = X[M][K] deq(W)^T, M <= 8.
 //
-// "AWQ量化实战" §5.1: raising w_bit is the remedy when 4-bit accuracy falls short; the
-// decode GEMV then streams one byte per weight instead of half a byte.
+// "AWQ量化实战" §3.3 (w_bit = 8, near lossless) and §5.2 / §5.3 (raise w_bit when 4-bit
+// accuracy falls short); the decode GEMV then streams one byte per weight instead of half
+// a byte.
 //
 // Same mapping as the 4-bit batched GEMV: a wave owns R rows, lane l walks 32-channel
 // chunks c = l, l + 64, ...; a chunk's 32 codes are 8 words (two 16-byte loads), word u

@@ -49,11 +49,11 @@ hipError_t launch_scalegen(const double* act, int64_t K, int n_grid, uint16_t* s
 // a5: per (alpha, row tile, token chunk) partial sums of the squared output error.
 int search_row_tile();
 int search_token_chunk(int64_t T);
-// rowmax [N] and srange [n_grid] are scratch (per-row max |W|, per-grid-point max s / min s).
+// xp: scratch for the copy of X in MFMA operand order (packed_x_bytes(T, K)).
 hipError_t launch_search_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N,
                              int64_t K, const uint16_t* s_grid, int n_grid, bool sym, int group,
-                             int w_bit, float* rowmax, float* srange, uint4* xp, double* partials,
-                             uint32_t* flags, hipStream_t stream);
+                             int w_bit, uint4* xp, double* partials, uint32_t* flags,
+                             hipStream_t stream);
 // a6: fixed-order sums of the partials, first-minimum argmin, s_best copy.
 hipError_t launch_search_reduce(const double* partials, int n_grid, int64_t n_partials,
                                 const uint16_t* s_grid, int64_t K, uint16_t* s_best,
@@ -86,6 +86,11 @@ hipError_t launch_gemv(const uint16_t* X, int64_t M, const uint32_t* qweight,
 hipError_t launch_gemm(const uint16_t* X, int64_t M, const uint32_t* qweight,
                        const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
                        int group, int w_bit, uint16_t* Y, bool gated, hipStream_t stream);
+
+// Data conditions of the linear path: OR AWQ_FLAG_NONFINITE_INPUT into *flags when a
+// (n fp16 values, n % 8 == 0) or b (m fp16 values) holds an Inf or a NaN.
+hipError_t launch_nonfinite_scan(const uint16_t* a, int64_t n, const uint16_t* b, int64_t m,
+                                 uint32_t* flags, hipStream_t stream);
 
 // f2: out = fp16(A / s) along columns (axis 1, len(s) = cols) or rows (axis 0,
 // len(s) = rows); cols % 8 == 0; out may alias A.

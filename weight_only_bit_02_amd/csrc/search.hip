@@ -6,17 +6,21 @@
 // backpropagation. For grid point i the score is
 //   err_i = sum_t sum_n ( sum_k X_tk D_nk )^2,   D = W - Q(W diag(s_i)) diag(1/s_i).
 //
-// One block owns (grid point i, 64 rows of W, up to 64 * NW tokens) and walks K one
-// quantization group at a time:
-//   1. quantize: 16 lanes per (row, group), 8 weights each; the same group quantizer
-//      as the pack kernel gives the codes; D is formed in fp32, scaled by a power of
-//      two P chosen per (row, group) from a bound on |D| so that |D P| < 2^14, and
-//      split into two fp16 halves hi + lo (22 significant bits). hi and lo go to LDS.
-//   2. contract: each wave multiplies its 64 tokens of X (fp16, straight from global)
-//      by the hi and lo tiles with v_mfma_f32_32x32x16_f16 into a per-group
-//      accumulator, then folds it into the running E tile with the factor 1/P of its
-//      column.
-// After the last group the block squares and sums its E tile (fp64) and writes one
+// One block owns (grid point i, 128 rows of W, up to 64 * NW tokens) and walks K one
+// 128-channel step at a time:
+//   1. quantize: 16 lanes per (row, step), 8 weights each; the same group quantizer as
+//      the pack kernel gives the codes; D is formed in fp32, scaled by a power of two P
+//      of its (row, step) so that |D P| < 2^14, and split into two fp16 halves hi + lo
+//      (22 significant bits). hi, lo and the exponent of P go to LDS.
+//   2. contract: each wave multiplies its 64 tokens of X (fp16, from a copy of X in
+//      operand order) by the hi and lo tiles with v_mfma_f32_32x32x16_f16 into its running
+//      E tile, which is kept in the scale of the current step's P: when a row's P changes,
+//      the row's accumulators are first multiplied by the ratio, an exact power of two.
+// P follows each row's largest |D| with hysteresis: it is re-chosen (2 bits of headroom)
+// only when the step's largest |D| would leave the fp16 range or falls 2^8 below it, so
+// most steps keep it and skip the rescale; every term keeps 22 significant bits unless it
+// is 2^8 below its step's largest, whatever the spread of s across the row.
+// After the last step the block squares and sums its E tile (fp64) and writes one
 // partial; a second kernel adds the partials of each grid point in a fixed order and
 // takes the first minimum. No floating-point atomics: results are bitwise
 // reproducible.
@@ -41,66 +45,18 @@ constexpr int kTokPerWave = 64;      // tokens per wave (2 MFMA row tiles)
 constexpr int kLdsStride = 128 + 8;  // halves per LDS row (16-byte pad against bank conflicts)
 constexpr int kXcds = 8;
 
-// Per-row power-of-two scale of D. For every channel k of row n,
-//   |D_nk| = |w'_nk - deq_nk| / s_k <= (max|w'| + 15 sc_h) / s_k
-//          <= 3.01 * max_k |W_nk| * (max_k s_k / min_k s_k),
-// so P_n = 2^(14 - e) with that bound in [2^(e-1), 2^e) keeps |D P| < 2^14 and the fp16
-// hi part finite; hi + lo then carries 22 significant bits of D P.
-__device__ __forceinline__ float row_scale(float rowmax, float srange) {
-  const float bound = 3.01f * rowmax * srange;
-  int ex = 0;
-  (void)__builtin_frexpf(bound, &ex);
-  if (!(bound > 0.0f) || !__builtin_isfinite(bound)) ex = 0;
-  ex = ex < -100 ? -100 : (ex > 100 ? 100 : ex);
-  return __builtin_ldexpf(1.0f, 14 - ex);
-}
-
-// max |W| per row (fp16 magnitudes compared as integers: order-free, exact).
-__global__ void __launch_bounds__(256) k_row_absmax(const uint16_t* __restrict__ W, int64_t N,
-                                                    int64_t K, float* __restrict__ rowmax) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-  if (row >= N) return;
-  uint32_t m = 0;
-  for (int64_t c = lane; c < K / 8; c += 64) {
-    const uint4 v = *reinterpret_cast<const uint4*>(W + row * K + c * 8);
-    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      m = max(m, d[i] & 0x7FFFu);
-      m = max(m, (d[i] >> 16) & 0x7FFFu);
-    }
-  }
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
-  if (lane == 0) rowmax[row] = m >= 0x7C00u ? __builtin_inff() : h2f((uint16_t)m);
-}
-
-// max s / min s of every grid point (one block per grid point; min/max are order-free).
-__global__ void __launch_bounds__(256) k_scale_range(const uint16_t* __restrict__ s_grid, int64_t K,
-                                                     float* __restrict__ srange,
-                                                     uint32_t* __restrict__ flags) {
-  __shared__ float lmin[256], lmax[256];
-  const uint16_t* s = s_grid + (int64_t)blockIdx.x * K;
-  float mn = __builtin_inff(), mx = 0.0f;
-  for (int64_t k = threadIdx.x; k < K; k += 256) {
-    const float v = h2f(s[k]);
-    mn = fminf(mn, v);
-    mx = fmaxf(mx, v);
-  }
-  lmin[threadIdx.x] = mn;
-  lmax[threadIdx.x] = mx;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int i = 1; i < 256; ++i) {
-      mn = fminf(mn, lmin[i]);
-      mx = fmaxf(mx, lmax[i]);
-    }
-    const float r = mx / mn;
-    srange[blockIdx.x] = r;
-    // beyond 2^10 the per-row scale leaves fewer than 12 of the 22 bits for small terms
-    if (!(r <= 1024.0f) && flags) atomicOr(flags, AWQ_FLAG_SEARCH_RANGE);
-  }
+// Exponent state of the search's per-(row, step) scale P = 2^(14 - E): E is re-chosen as
+// e + 2 (e: the exponent of the step's largest |D|, which lies in [2^(e-1), 2^e)) when
+// unset, when e > E (|D P| would reach 2^14) or when e < E - 8; otherwise kept. Hence
+// 2^5 <= max |D P| < 2^14 on every step. E stays within [-98, 102].
+constexpr int kEUnset = -100000;
+__device__ __forceinline__ int search_exponent(float dmx, int E) {
+  int e = 0;
+  (void)__builtin_frexpf(dmx, &e);
+  if (!(dmx > 0.0f) || !__builtin_isfinite(dmx)) return E == kEUnset ? 0 : E;  // no constraint
+  e = e < -100 ? -100 : (e > 100 ? 100 : e);
+  if (E == kEUnset || e > E || e < E - 8) E = e + 2;
+  return E;
 }
 
 // X in the order the MFMA A operand reads it. For 64-token tile t (tokens 64 t .. 64 t + 63,
@@ -142,15 +98,24 @@ __device__ __forceinline__ const uint4* packed_x(const uint4* xp, int64_t G, int
 // threads from 0). With CLIP the group's extremes are shrunk by r before the quantizer
 // sees them (weight clipping). 16 lanes per (row, 128 channels), 8 weights each; returns
 // whether a non-finite value was met.
+template <int NW, int NROWS>
+constexpr int quant_passes() {
+  return NROWS / (NW * 4);
+}
+
+// Search (CLIP = false): the scale of each (row, step) comes from the row's exponent state
+// e_state[pass] (search_exponent), and its exponent E is written to pe_out[row]. Clip
+// search: each group's own largest |D| sets its P, written to pg_out[row * 4 + group].
 template <int NW, bool CLIP, int NROWS>
 __device__ __forceinline__ bool quantize_tile_group(const uint16_t* W, int64_t N, int64_t K,
                                                     const uint16_t* s, float r, bool sym,
                                                     int group, float qmax, int64_t n0, int64_t j,
-                                                    const float* lds_p, uint16_t* hi_buf,
+                                                    int (&e_state)[quant_passes<NW, NROWS>()],
+                                                    int* pe_out, uint16_t* hi_buf,
                                                     uint16_t* lo_buf, int tid, int row_base,
                                                     float* pg_out) {
   constexpr int kRowsPerPass = NW * 4;
-  constexpr int kPasses = NROWS / kRowsPerPass;
+  constexpr int kPasses = quant_passes<NW, NROWS>();
   static_assert(kPasses * kRowsPerPass == NROWS, "whole passes");
   const int q_row = row_base + (tid >> 4);
   const int li = tid & 15;
@@ -229,7 +194,16 @@ __device__ __forceinline__ bool quantize_tile_group(const uint16_t* W, int64_t N
       const int gl = group >> 3;  // lanes per group
       if ((li & (gl - 1)) == 0) pg_out[row * 4 + li / gl] = P;
     } else {
-      P = lds_p[row];
+      // the (row, step) scale: the largest |D| over the step's 128 channels (16 lanes)
+      float dmx = 0.0f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) dmx = fmaxf(dmx, __builtin_fabsf(dg[c]));
+      float dmn = dmx;
+      row16_minmax(dmn, dmx);
+      const int E = search_exponent(dmx, e_state[p]);
+      e_state[p] = E;
+      P = __builtin_ldexpf(1.0f, 14 - E);
+      if (li == 0) pe_out[row] = E;
     }
     uint32_t hi[4], lo[4];
 #pragma unroll
@@ -255,13 +229,11 @@ template <int NW>
 __global__ void __launch_bounds__(NW * 64)
     k_search_err(const uint4* xp, int64_t T, const uint16_t* W, int64_t N, int64_t K,
                  const uint16_t* s_grid, int n_grid, int sym, int group, int w_bit,
-                 const float* rowmax,
-                 const float* srange,
                  double* __restrict__ partials, uint32_t* __restrict__ flags, int64_t n_ntiles,
                  int64_t per_xcd) {
   __shared__ __attribute__((aligned(16))) uint16_t lds_hi[2][kRowTile * kLdsStride];
   __shared__ __attribute__((aligned(16))) uint16_t lds_lo[2][kRowTile * kLdsStride];
-  __shared__ float lds_p[kRowTile];
+  __shared__ int lds_pe[2][kRowTile];  // exponent E of each row's P = 2^(14 - E), per buffer
   __shared__ double lds_red[NW];
 
   // XCD-aware order: consecutive blocks of one XCD share a row tile (different grid
@@ -284,11 +256,6 @@ __global__ void __launch_bounds__(NW * 64)
   const int m32 = lane & 31;
   const int khalf = lane >> 5;
 
-  const float sr = srange[alpha];
-  for (int r = tid; r < kRowTile; r += NW * 64)
-    lds_p[r] = row_scale(n0 + r < N ? rowmax[n0 + r] : 0.0f, sr);
-  __syncthreads();
-
   // The waves form two sets of NW / 2 (one wave of each per SIMD), each quantizing half
   // of the tile's rows. Per step, set A multiplies the current group and then quantizes
   // its half of the next one, set B does the same in the opposite order, so on each SIMD
@@ -299,9 +266,11 @@ __global__ void __launch_bounds__(NW * 64)
   const bool set_b = wave >= NH;
   const int tid_set = set_b ? tid - NH * 64 : tid;
   bool bad = false;
+  int e_state[quant_passes<NH, kRowTile / 2>()];
   auto quantize = [&](int64_t j, int buf) {
-    bad |= quantize_tile_group<NH, false, kRowTile / 2>(W, N, K, s, 1.0f, sym, group, qmax, n0, j, lds_p,
-                                                       lds_hi[buf], lds_lo[buf], tid_set,
+    bad |= quantize_tile_group<NH, false, kRowTile / 2>(W, N, K, s, 1.0f, sym, group, qmax, n0, j,
+                                                       e_state, lds_pe[buf], lds_hi[buf],
+                                                       lds_lo[buf], tid_set,
                                                        set_b ? kRowTile / 2 : 0, nullptr);
   };
 
@@ -315,8 +284,32 @@ __global__ void __launch_bounds__(NW * 64)
       for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
 
     const int64_t tile = tw / kTokPerWave;  // the wave's 64-token tile of the packed X
+    int e_prev[4] = {0, 0, 0, 0};  // exponent of the P the accumulators of tile b are in
+#pragma unroll
+    for (int i = 0; i < quant_passes<NH, kRowTile / 2>(); ++i) e_state[i] = kEUnset;
     auto multiply = [&](int64_t j, int buf) {
       if (!active) return;
+      // bring each row's running E into the scale of this step's P (exact powers of two;
+      // the whole wave skips it when no row changed)
+      int en[4];
+      bool changed = false;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        en[b] = lds_pe[buf][b * 32 + m32];
+        changed |= en[b] != e_prev[b];
+      }
+      if (__builtin_amdgcn_ballot_w64(changed)) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int d = e_prev[b] - en[b];  // P_new / P_old = 2^d
+#pragma unroll
+          for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[a][b][e] = __builtin_ldexpf(acc[a][b][e], d);
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < 4; ++b) e_prev[b] = en[b];
 #pragma unroll 2
       for (int st = 0; st < kGroup / 16; ++st) {
         const int koff = st * 16 + khalf * 8;
@@ -361,7 +354,7 @@ __global__ void __launch_bounds__(NW * 64)
     double ss = 0.0;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      const double pinv = 1.0 / (double)lds_p[b * 32 + m32];  // output column = lane % 32
+      const double pinv = __builtin_ldexp(1.0, e_prev[b] - 14);  // 1 / P; column = lane % 32
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -428,10 +421,12 @@ __global__ void __launch_bounds__(NW * 64)
   const bool set_b = wave >= NH;
   const int tid_set = set_b ? tid - NH * 64 : tid;
   bool bad = false;
+  int e_unused[quant_passes<NH, kRowTile / 2>()];
   auto quantize = [&](int64_t jq, int qbuf) {
     bad |= quantize_tile_group<NH, true, kRowTile / 2>(W, N, K, s, r, sym, group, qmax, n0, jq,
-                                                      nullptr, lds_hi[qbuf], lds_lo[qbuf], tid_set,
-                                                      set_b ? kRowTile / 2 : 0, lds_pg[qbuf]);
+                                                      e_unused, nullptr, lds_hi[qbuf], lds_lo[qbuf],
+                                                      tid_set, set_b ? kRowTile / 2 : 0,
+                                                      lds_pg[qbuf]);
   };
   quantize(0, 0);
   __syncthreads();
@@ -666,25 +661,19 @@ int search_token_chunk(int64_t T) { return T <= 4 * kTokPerWave ? 4 * kTokPerWav
 
 hipError_t launch_search_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N,
                              int64_t K, const uint16_t* s_grid, int n_grid, bool sym, int group,
-                             int w_bit, float* rowmax, float* srange, uint4* xp, double* partials,
-                             uint32_t* flags, hipStream_t stream) {
-  hipLaunchKernelGGL(k_row_absmax, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, stream, W, N, K, rowmax);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  e = launch_pack_x(X, T, K, xp, stream);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_scale_range, dim3((unsigned)n_grid), dim3(256), 0, stream, s_grid, K, srange, flags);
-  e = hipGetLastError();
+                             int w_bit, uint4* xp, double* partials, uint32_t* flags,
+                             hipStream_t stream) {
+  hipError_t e = launch_pack_x(X, T, K, xp, stream);
   if (e != hipSuccess) return e;
   const int64_t n_ntiles = (N + kRowTile - 1) / kRowTile;
   const int64_t per_xcd = (n_ntiles * n_grid + kXcds - 1) / kXcds;
   const dim3 grid((unsigned)(per_xcd * kXcds));
   if (T <= 4 * kTokPerWave)
     hipLaunchKernelGGL(k_search_err<4>, grid, dim3(256), 0, stream, xp, T, W, N, K, s_grid, n_grid,
-                       (int)sym, group, w_bit, rowmax, srange, partials, flags, n_ntiles, per_xcd);
+                       (int)sym, group, w_bit, partials, flags, n_ntiles, per_xcd);
   else
     hipLaunchKernelGGL(k_search_err<8>, grid, dim3(512), 0, stream, xp, T, W, N, K, s_grid, n_grid,
-                       (int)sym, group, w_bit, rowmax, srange, partials, flags, n_ntiles, per_xcd);
+                       (int)sym, group, w_bit, partials, flags, n_ntiles, per_xcd);
   return hipGetLastError();
 }
 
