@@ -46,7 +46,8 @@ typedef enum awq_status {
   AWQ_ERR_UNSUPPORTED = 3,   /* config outside w_bit 3,4,8 / group 128,64,32 / zp 0,1 */
   AWQ_ERR_MISALIGNED = 4,    /* a base pointer is not 16-byte aligned                */
   AWQ_ERR_WORKSPACE = 5,     /* workspace missing or smaller than the query returns  */
-  AWQ_ERR_HIP = 6            /* the HIP runtime reported an error on launch          */
+  AWQ_ERR_HIP = 6,           /* the HIP runtime reported an error on launch          */
+  AWQ_ERR_SCRATCH_LIMIT = 7  /* a no-allocation call needs more than its static array */
 } awq_status;
 
 /* Quantization config ([SKILL] "如何使用该技能 / 步骤 2": quant_config zero_point, q_group_size,
@@ -176,6 +177,26 @@ awq_status awq_search_scales(const void* X, int64_t T, const void* W, int64_t N,
                              const awq_config* cfg, void* s_best, int32_t* best_idx,
                              double* err, void* s_grid, void* workspace,
                              size_t workspace_bytes, uint32_t* flags, void* stream);
+
+/*
+ * awq_search_scales_noalloc -- awq_search_scales for callers that cannot allocate device
+ *   memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ *   hipMalloc. Same arguments without the workspace, same kernels and bit-identical
+ *   results. The workspace is a static device array of AWQ_NOALLOC_SCRATCH_BYTES that
+ *   the library holds on every GPU it runs on until the process ends; its address is
+ *   looked up on the first call on each device, so the current device must be the one
+ *   `stream` belongs to. The call allocates nothing.
+ *   Limit: awq_search_workspace_size(T, N, K, cfg) <= AWQ_NOALLOC_SCRATCH_BYTES (32 MiB:
+ *   e.g. T = 512 calibration tokens up to K = 28672), else AWQ_ERR_SCRATCH_LIMIT before
+ *   anything is enqueued. Every call on one GPU uses the same array (it keeps the last
+ *   call's contents; each call clears what it needs): calls that overlap on one GPU
+ *   (different streams or host threads) race and must be serialized by the caller.
+ */
+#define AWQ_NOALLOC_SCRATCH_BYTES (32u << 20)
+awq_status awq_search_scales_noalloc(const void* X, int64_t T, const void* W, int64_t N,
+                                     int64_t K, const awq_config* cfg, void* s_best,
+                                     int32_t* best_idx, double* err, void* s_grid,
+                                     uint32_t* flags, void* stream);
 
 /*
  * awq_linear_w4a16 -- Y = X * deq(W)^T with 4-bit packed weights and fp16 activations.

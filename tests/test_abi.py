@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for s in range(7):
+    for s in range(8):
         assert lib.awq_status_string(s)
     assert lib.awq_gemv_max_m() == 64
 
@@ -177,3 +177,18 @@ def test_peak_probes_reject_bad_arguments(lib):
     assert lib.awq_peak_mfma(16, None, 16, None) == 2
     assert lib.awq_peak_mfma(16, FAKE, 0, None) == 2
 
+
+def test_search_noalloc_rejects_oversize_on_the_host(lib):
+    """The no-allocation search refuses shapes whose workspace exceeds its static array
+    before touching any device (AWQ_ERR_SCRATCH_LIMIT = 7), and validates like the search."""
+    cfg = _abi.config()
+    sb, best = FAKE, FAKE
+    assert lib.awq_search_workspace_size(8192, 4096, 28672, C.byref(cfg)) > _abi.NOALLOC_SCRATCH_BYTES
+    assert lib.awq_search_scales_noalloc(FAKE, 8192, FAKE, 4096, 28672, C.byref(cfg), sb, best,
+                                         None, None, None, None) == 7
+    assert lib.awq_search_scales_noalloc(None, 512, FAKE, 4096, 4096, C.byref(cfg), sb, best,
+                                         None, None, None, None) == 1
+    assert lib.awq_search_scales_noalloc(FAKE, 0, FAKE, 4096, 4096, C.byref(cfg), sb, best,
+                                         None, None, None, None) == 2
+    # the largest calibration the array covers: T = 512 up to K = 28672 (the 70B down_proj)
+    assert 0 < lib.awq_search_workspace_size(512, 8192, 28672, C.byref(cfg)) <= _abi.NOALLOC_SCRATCH_BYTES

@@ -13,11 +13,13 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "liba
 AWQ_OK = 0
 STATUS_NAMES = {0: "AWQ_OK", 1: "AWQ_ERR_NULL_POINTER", 2: "AWQ_ERR_BAD_SHAPE",
                 3: "AWQ_ERR_UNSUPPORTED", 4: "AWQ_ERR_MISALIGNED", 5: "AWQ_ERR_WORKSPACE",
-                6: "AWQ_ERR_HIP"}
+                6: "AWQ_ERR_HIP", 7: "AWQ_ERR_SCRATCH_LIMIT"}
 
 FLAG_NONFINITE_INPUT = 1
 FLAG_SCALE_CLAMPED = 2
 FLAG_OVERFLOW = 8
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # AWQ_NOALLOC_SCRATCH_BYTES
 
 KERNEL_AUTO, KERNEL_GEMV, KERNEL_GEMM, KERNEL_SKINNY = 0, 1, 2, 3
 
@@ -43,6 +45,7 @@ SIGNATURES = {
     "awq_candidate_scales": (C.c_int, [P, I64, CFG, P, P]),
     "awq_search_workspace_size": (C.c_size_t, [I64, I64, I64, CFG]),
     "awq_search_scales": (C.c_int, [P, I64, P, I64, I64, CFG, P, P, P, P, P, C.c_size_t, P, P]),
+    "awq_search_scales_noalloc": (C.c_int, [P, I64, P, I64, I64, CFG, P, P, P, P, P, P]),
     "awq_linear_w4a16": (C.c_int, [P, I64, P, P, P, I64, I64, CFG, P, P, P]),
     "awq_linear_w4a16_ex": (C.c_int, [P, I64, P, P, P, I64, I64, CFG, P, P, C.c_int, P]),
     "awq_linear_w4a16_gated_silu": (C.c_int, [P, I64, P, P, P, I64, I64, CFG, P, P, P]),

@@ -2,8 +2,21 @@
 // The operations and their sources are documented in include/awq.h.
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "awq.h"
 #include "launch.hpp"
+
+// Workspace of awq_search_scales_noalloc: a static device array, one copy per GPU for as
+// long as the process lives. Host code never passes `scratch` itself to a kernel (on the
+// host it is only a stand-in for the symbol): its device address is looked up once per
+// device with hipGetSymbolAddress and kept in g_scratch_ptr.
+static __device__ __attribute__((aligned(256))) unsigned char scratch[AWQ_NOALLOC_SCRATCH_BYTES];
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+}  // namespace
 
 namespace {
 
@@ -92,6 +105,8 @@ const char* awq_status_string(awq_status s) {
     case AWQ_ERR_MISALIGNED: return "a base pointer is not 16-byte aligned";
     case AWQ_ERR_WORKSPACE: return "workspace missing or too small";
     case AWQ_ERR_HIP: return "HIP launch error";
+    case AWQ_ERR_SCRATCH_LIMIT:
+      return "the call needs more scratch than the static AWQ_NOALLOC_SCRATCH_BYTES array";
   }
   return "unknown status";
 }
@@ -195,6 +210,33 @@ awq_status awq_search_scales(const void* X, int64_t T, const void* W, int64_t N,
     e = awq::launch_search_reduce(partials, c.n_grid, L.n_partials, sg, K, (uint16_t*)s_best,
                                   best_idx, err, flags, st);
   return hip_status(e);
+}
+
+awq_status awq_search_scales_noalloc(const void* X, int64_t T, const void* W, int64_t N,
+                                     int64_t K, const awq_config* cfg, void* s_best,
+                                     int32_t* best_idx, double* err, void* s_grid,
+                                     uint32_t* flags, void* stream) {
+  const awq_config c = resolve(cfg);
+  if (!X || !W || !s_best || !best_idx) return AWQ_ERR_NULL_POINTER;
+  if (!supported(c)) return AWQ_ERR_UNSUPPORTED;
+  if (T < 1 || T > AWQ_MAX_CALIB_TOKENS || !good_nk(N, K)) return AWQ_ERR_BAD_SHAPE;
+  if (search_layout(T, N, K, c.n_grid).total > (size_t)AWQ_NOALLOC_SCRATCH_BYTES)
+    return AWQ_ERR_SCRATCH_LIMIT;
+  // the current device's copy of the array (looked up on the first call on each device)
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return AWQ_ERR_HIP;
+  void* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+      void* p = nullptr;
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return AWQ_ERR_HIP;
+      g_scratch_ptr[dev] = p;
+    }
+    ws = g_scratch_ptr[dev];
+  }
+  return awq_search_scales(X, T, W, N, K, cfg, s_best, best_idx, err, s_grid, ws,
+                           (size_t)AWQ_NOALLOC_SCRATCH_BYTES, flags, stream);
 }
 
 static awq_status linear_common(const void* X, int64_t M, const uint32_t* qweight,
