@@ -88,7 +88,11 @@ typedef enum awq_linear_kernel {
                           codes: vector GEMV up to 8, skinny up to 64)         */
   AWQ_LINEAR_GEMV = 1, /* wave-per-rows dequant-fused GEMV (any M <= 8)       */
   AWQ_LINEAR_GEMM = 2, /* MFMA dequant-GEMM (any M)                           */
-  AWQ_LINEAR_SKINNY = 3 /* MFMA GEMV for small batches, split K (M <= 64)     */
+  AWQ_LINEAR_SKINNY = 3, /* MFMA GEMV for small batches, split K (M <= 64)    */
+  AWQ_LINEAR_GEMM_WIDE = 4 /* MFMA dequant-GEMM on 256 x 256 tiles, two waves per
+                              SIMD (4-bit codes, 128- or 64-channel groups, 256 K <
+                              2^32; else AWQ_ERR_UNSUPPORTED); AUTO takes it over
+                              the GEMM when it has at least 384 tiles          */
 } awq_linear_kernel;
 
 /*
@@ -217,7 +221,8 @@ awq_status awq_linear_w4a16(const void* X, int64_t M, const uint32_t* qweight,
                             const awq_config* cfg, void* Y, uint32_t* flags, void* stream);
 
 /* Same as awq_linear_w4a16 with an explicit kernel choice (GEMV requires M <= 8,
- * SKINNY M <= 64; otherwise AWQ_ERR_BAD_SHAPE). */
+ * SKINNY M <= 64, otherwise AWQ_ERR_BAD_SHAPE; GEMM_WIDE a config it supports, otherwise
+ * AWQ_ERR_UNSUPPORTED). */
 awq_status awq_linear_w4a16_ex(const void* X, int64_t M, const uint32_t* qweight,
                                const void* scales, const uint8_t* zeros, int64_t N, int64_t K,
                                const awq_config* cfg, void* Y, uint32_t* flags,

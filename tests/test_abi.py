@@ -192,3 +192,13 @@ def test_search_noalloc_rejects_oversize_on_the_host(lib):
                                          None, None, None, None) == 2
     # the largest calibration the array covers: T = 512 up to K = 28672 (the 70B down_proj)
     assert 0 < lib.awq_search_workspace_size(512, 8192, 28672, C.byref(cfg)) <= _abi.NOALLOC_SCRATCH_BYTES
+
+
+def test_gemm_wide_rejects_other_formats(lib):
+    """The wide GEMM takes 4-bit codes with 128- or 64-channel groups only (3 = UNSUPPORTED)."""
+    for w_bit, group in ((8, 128), (3, 128), (4, 32)):
+        cfg = _abi.config(w_bit=w_bit, group_size=group)
+        assert lib.awq_linear_w4a16_ex(FAKE, 512, FAKE, FAKE, FAKE, 256, 1024, C.byref(cfg), FAKE,
+                                       None, 4, None) == 3
+    assert lib.awq_linear_w4a16_ex(FAKE, 512, FAKE, FAKE, FAKE, 256, 1024, None, FAKE, None, 5,
+                                   None) == 3

@@ -300,3 +300,56 @@ def test_linear_flags_nonfinite(kernel, M, where):
         Y0 = host(fn(to_dev(X), p, kernel=kernel))
         assert np.array_equal(Y.view(np.uint16), Y0.view(np.uint16))
         assert int(host(f)[0]) == (0 if where == "none" else oracle.FLAG_NONFINITE_INPUT), where
+
+
+@pytest.mark.parametrize("M", [1, 65, 256, 257, 300])
+@pytest.mark.parametrize("N,K", [(1, 128), (67, 384), (256, 4096), (300, 1152)])
+def test_gemm_wide_matches_oracle_and_gemm(M, N, K):
+    """The 256 x 256-tile GEMM: ragged M and N (partial tiles on both axes), K of 1..32 steps;
+    within the linear tolerance and bit-identical to the 128-row GEMM (same channel order,
+    same fp16 widening)."""
+    p, ref = _packed_case(N, K, off=N + 9 * K)
+    X = si.activations(M, K, offset=M + 700)
+    _check_linear(X, p, ref, "gemm_wide")
+    a = host(awq.linear_w4a16(to_dev(X), p, kernel="gemm_wide"))
+    b = host(awq.linear_w4a16(to_dev(X), p, kernel="gemm"))
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+@pytest.mark.parametrize("group", [128, 64])
+@pytest.mark.parametrize("M", [70, 513])
+def test_gemm_wide_gated_and_groups(group, M):
+    """Gated (fused gate|up, 67 outputs: a partial column tile) and 64-channel groups, against
+    the oracle and bit-identical to the 128-row GEMM."""
+    nh, K = 67, 1152
+    W = si.weights(2 * nh, K, offset=M + group + 1)
+    qw, sc, zb, _ = oracle.quantize_pack(W, None, None, True, group, 4)
+    p = awq.quantize_pack(to_dev(W), group_size=group)
+    X = si.activations(M, K, offset=M + 800)
+    out, check = guarded((M, nh), torch.float16)
+    H = host(awq.linear_w4a16_gated_silu(to_dev(X), p, kernel="gemm_wide", out=out))
+    check()
+    h, g, u, bg, bu = oracle.gated_silu_reference(X, qw, sc, zb, K)
+    assert oracle.gated_silu_within_tolerance(H.astype(np.float64), g, u, bg, bu).all()
+    H1 = host(awq.linear_w4a16_gated_silu(to_dev(X), p, kernel="gemm"))
+    assert np.array_equal(H.view(np.uint16), H1.view(np.uint16))
+    Y = host(awq.linear_w4a16(to_dev(X), p, kernel="gemm_wide"))
+    Y1 = host(awq.linear_w4a16(to_dev(X), p, kernel="gemm"))
+    assert np.array_equal(Y.view(np.uint16), Y1.view(np.uint16))
+    y_ref, bound = oracle.linear_reference(X, qw, sc, zb, K)
+    assert oracle.linear_within_tolerance(Y.astype(np.float64), y_ref, bound).all()
+
+
+def test_gemm_auto_takes_wide_from_384_tiles():
+    """AUTO: the 256 x 256 GEMM once it has 384 tiles (M = 2048, N = 12288), the 128-row GEMM
+    below (N = 4096: 128 tiles); either result equals the explicit kernel's bit for bit."""
+    for N, wide in ((12288, True), (4096, False)):
+        K = 256
+        p, ref = _packed_case(N, K, off=N + 11)
+        X = to_dev(si.activations(2048, K, offset=N))
+        a = host(awq.linear_w4a16(X, p))
+        e = host(awq.linear_w4a16(X, p, kernel="gemm_wide" if wide else "gemm"))
+        assert np.array_equal(a.view(np.uint16), e.view(np.uint16))
+        rows = np.arange(0, 2048, 97)
+        y_ref, bound = oracle.linear_reference(host(X)[rows], *ref, K)
+        assert oracle.linear_within_tolerance(a[rows].astype(np.float64), y_ref, bound).all()

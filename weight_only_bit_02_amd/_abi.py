@@ -21,7 +21,7 @@ FLAG_OVERFLOW = 8
 
 NOALLOC_SCRATCH_BYTES = 32 << 20  # AWQ_NOALLOC_SCRATCH_BYTES
 
-KERNEL_AUTO, KERNEL_GEMV, KERNEL_GEMM, KERNEL_SKINNY = 0, 1, 2, 3
+KERNEL_AUTO, KERNEL_GEMV, KERNEL_GEMM, KERNEL_SKINNY, KERNEL_GEMM_WIDE = 0, 1, 2, 3, 4
 
 
 class AwqConfig(C.Structure):

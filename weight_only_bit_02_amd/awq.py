@@ -217,7 +217,7 @@ def search_scales(X: torch.Tensor, W: torch.Tensor, n_grid: int = 20,
 
 
 _KERNELS = {"auto": _abi.KERNEL_AUTO, "gemv": _abi.KERNEL_GEMV, "gemm": _abi.KERNEL_GEMM,
-            "skinny": _abi.KERNEL_SKINNY}
+            "skinny": _abi.KERNEL_SKINNY, "gemm_wide": _abi.KERNEL_GEMM_WIDE}
 
 
 def linear_w4a16(X: torch.Tensor, w: PackedLinear, kernel: str = "auto",

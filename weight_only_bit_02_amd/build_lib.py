@@ -21,7 +21,7 @@ LIB = os.path.join(LIB_DIR, "libawq_mi355x.so")
 SOURCES = [  # the slowest units (GEMM instantiations, the searches) first: they bound the build
     "gemm_i3_plain.hip", "gemm_i3_gated.hip", "gemm_i3_plain_g32.hip", "gemm_i3_gated_g32.hip",
     "gemm_i8_plain.hip", "gemm_i8_gated.hip", "gemm_i4_plain.hip", "gemm_i4_gated.hip",
-    "gemm_i4_plain_g32.hip", "gemm_i4_gated_g32.hip", "search.hip", "gemv.hip", "gemv_mfma.hip",
+    "gemm_i4_plain_g32.hip", "gemm_i4_gated_g32.hip", "search.hip", "gemm_wide.hip", "gemv.hip", "gemv_mfma.hip",
     "gemv8.hip", "gemv3.hip", "quant_pack.hip", "stats.hip", "fold.hip", "check.hip", "peaks.hip", "gemm.hip", "awq_abi.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

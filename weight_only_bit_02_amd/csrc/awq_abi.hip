@@ -249,7 +249,9 @@ static awq_status linear_common(const void* X, int64_t M, const uint32_t* qweigh
   if (M < 1 || M >= kMaxDim || !good_nk(N, K)) return AWQ_ERR_BAD_SHAPE;
   if (gated && (N < 2 || N % 2 != 0)) return AWQ_ERR_BAD_SHAPE;
   if (kernel != AWQ_LINEAR_AUTO && kernel != AWQ_LINEAR_GEMV && kernel != AWQ_LINEAR_GEMM &&
-      kernel != AWQ_LINEAR_SKINNY)
+      kernel != AWQ_LINEAR_SKINNY && kernel != AWQ_LINEAR_GEMM_WIDE)
+    return AWQ_ERR_UNSUPPORTED;
+  if (kernel == AWQ_LINEAR_GEMM_WIDE && !awq::gemm_wide_supported(K, c.group_size, c.w_bit))
     return AWQ_ERR_UNSUPPORTED;
   if (kernel == AWQ_LINEAR_GEMV && M > awq::kGemvMaxM) return AWQ_ERR_BAD_SHAPE;
   if (kernel == AWQ_LINEAR_SKINNY && M > awq::kSkinnyMaxM) return AWQ_ERR_BAD_SHAPE;
@@ -273,6 +275,11 @@ static awq_status linear_common(const void* X, int64_t M, const uint32_t* qweigh
     kernel = M <= awq::kVgemvAutoMaxM && M <= g_gemv_max_m ? AWQ_LINEAR_GEMV
              : M <= g_gemv_max_m                            ? AWQ_LINEAR_SKINNY
                                                             : AWQ_LINEAR_GEMM;
+  // the 256 x 256 tiling once it gives the chip 1.5 tiles per CU or more (measured on the
+  // Llama-2-7B shapes at M = 2048: ahead from 384 tiles, behind at 128)
+  if (kernel == AWQ_LINEAR_GEMM && awq::gemm_wide_supported(K, c.group_size, c.w_bit) &&
+      awq::gemm_wide_tiles(M, N, gated) >= awq::kWideMinTiles)
+    kernel = AWQ_LINEAR_GEMM_WIDE;
   const auto* Xh = (const uint16_t*)X;
   const auto* sc = (const uint16_t*)scales;
   auto* Yh = (uint16_t*)Y;
@@ -299,6 +306,9 @@ static awq_status linear_common(const void* X, int64_t M, const uint32_t* qweigh
         awq::launch_gemm(Xh, M, qweight, sc, zeros, N, K, c.group_size, 3, Yh, gated, st));
   }
   switch (kernel) {
+    case AWQ_LINEAR_GEMM_WIDE:
+      return hip_status(
+          awq::launch_gemm_wide(Xh, M, qweight, sc, zeros, N, K, c.group_size, Yh, gated, st));
     case AWQ_LINEAR_GEMV:
       return hip_status(
           awq::launch_gemv(Xh, M, qweight, sc, zeros, N, K, c.group_size, Yh, gated, st));

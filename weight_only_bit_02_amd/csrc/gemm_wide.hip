@@ -1,0 +1,274 @@
+// MFMA dequant-GEMM with 256 x 256 tiles and two waves per SIMD (a8, 4-bit codes with 128- or
+// 64-channel groups): Y[M][N] = X[M][K] deq(W)^T for batches large enough to give every CU
+// more than one such tile.
+//
+// "AWQ量化技术Skill", "主要功能和特点": a GEMM kernel serves batch sizes above one;
+// "AWQ量化实战" §2.3 / §3.4: weights stay 4-bit in memory and are dequantized on the fly.
+//
+// Block = 8 waves (two per SIMD), tile 256 (tokens) x 256 (output channels), K step 128
+// (one group of 128, or two of 64: a lane half's 64 channels are then one group). Wave w
+// owns rows [128 (w / 4), +128) and columns [64 (w % 4), +64) of the tile: 4 x 2
+// accumulators of v_mfma_f32_32x32x16_f16.
+//   - Both operands travel global -> LDS by 16-byte LDS DMA (global_load_lds_dwordx4),
+//     issued at the top of a step for the next one into the other of two buffers; every
+//     buffer is its own LDS object, so the compiler waits only for the DMA of the buffer
+//     a step reads. A (activations, 256 rows x 16 chunks of 16 bytes per step) is stored
+//     with chunk c of row r in slot c ^ (r & 15), so the 32 rows a fragment read touches
+//     fall in distinct banks; B (codes, 256 columns x 64 bytes) as it is in memory.
+//   - Each wave widens its own B words from LDS to (q - z) sc in fp16 (the packed layout
+//     puts channels 2p, 2p + 1 in nibbles p and p + 4, so one mask per pair and the 0x6400
+//     exponent give the pair exactly, then a packed subtract of 1024 + z and a packed
+//     multiply by the scale: one fp16 rounding), as the 128-row GEMM does, so both GEMMs
+//     give bit-identical results: lane half kh covers channels [64 kh, 64 kh + 64) of a
+//     step and k16 slice s covers 8 of them, A read from LDS with the same channel map.
+// Tiles are handed to the XCDs in contiguous runs (blocks of one XCD share an A panel in
+// that XCD's L2). Against the 128 x 256 tile of one wave per SIMD this halves the A tile
+// reads per MFMA and hides each wave's waits behind the other wave on its SIMD; it only
+// pays when the chip gets more than one 256 x 256 tile per CU (the dispatcher's rule).
+//
+// Fused gate|up (GATED): a block covers 128 outputs; a wave's first 32-column MFMA tile is
+// gate column n, its second the up column n + N/2, and the epilogue stores SiLU(g) * u.
+#include <type_traits>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace awq {
+
+namespace {
+
+typedef _Float16 half8w __attribute__((ext_vector_type(8)));
+typedef _Float16 half2w __attribute__((ext_vector_type(2)));
+typedef float f32x16w __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kWM = 256, kWN = 256, kWK = 128;
+
+__device__ __forceinline__ uint32_t wide_magic() {
+  uint32_t m;
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(m));
+  return m;
+}
+
+// One packed word -> its 8 dequantized fp16 channels (q - z) sc, in channel order.
+__device__ __forceinline__ half8w widen_word(uint32_t w, half2w zz, half2w s2, uint32_t magic) {
+  half2w d[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t u = ((w >> (4 * p)) & 0x000F000Fu) | magic;
+    d[p] = (__builtin_bit_cast(half2w, u) + zz) * s2;
+  }
+  return half8w{d[0][0], d[0][1], d[1][0], d[1][1], d[2][0], d[2][1], d[3][0], d[3][1]};
+}
+
+template <bool GATED>
+__global__ void __launch_bounds__(512)
+    k_gemm_wide(const uint16_t* X, int64_t M, const uint32_t* qweight, const uint16_t* scales,
+                const uint8_t* zeros, int64_t N, int64_t K, int group, uint16_t* __restrict__ Y,
+                int64_t mt, int64_t nt, int64_t per_xcd) {
+  __shared__ __attribute__((aligned(16))) uint4 a0s[kWM * 16];
+  __shared__ __attribute__((aligned(16))) uint4 a1s[kWM * 16];
+  __shared__ __attribute__((aligned(16))) uint4 b0s[kWN * 4];
+  __shared__ __attribute__((aligned(16))) uint4 b1s[kWN * 4];
+  const int64_t t = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (t >= mt * nt) return;
+  const int64_t m0 = (t / nt) * kWM;
+  const int64_t n0 = (t % nt) * (GATED ? kWN / 2 : kWN);
+  const int64_t nh = N / 2;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int m32 = lane & 31, kh = lane >> 5;
+  const int g64 = group == 64;
+  const int64_t Gs = K / group, zbw = (Gs + 1) / 2, words = K / 8;
+  const int64_t nsteps = K / kWK;
+  const uint32_t magic = wide_magic();
+
+  // A DMA map: wave instruction i (0..7) fills slots (wave * 8 + i) * 64 + lane of the
+  // buffer: row r = (wave * 8 + i) * 4 + lane / 16, slot lane % 16 <- chunk (lane % 16) ^ (r % 16).
+  // Rows past M read row M - 1 (their outputs are never stored). Offsets fit 32 bits: the
+  // launcher takes this kernel only for 256 K < 2^32.
+  const uint16_t* xblk = X + m0 * K;
+  uint32_t aoff[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = (wave * 8 + i) * 4 + (lane >> 4);
+    const int64_t gr = m0 + r < M ? r : M - 1 - m0;
+    aoff[i] = (uint32_t)(gr * K + ((lane & 15) ^ (r & 15)) * 8);
+  }
+  // B DMA map: slot (wave * 2 + i) * 64 + lane = tile column c (slot / 4), 16-byte quarter
+  // q (slot % 4) of the column's 64 code bytes of a step. Gated: tile column c is wave
+  // tile c / 64's gate column (c % 64 < 32) or up column. Columns past the end read the
+  // last one (never stored).
+  const uint32_t* bptr[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int slot = (wave * 2 + i) * 64 + lane;
+    const int c = slot >> 2, q = slot & 3;
+    int64_t n;
+    if constexpr (GATED) {
+      int64_t o = n0 + (c >> 6) * 32 + (c & 31);
+      o = o < nh ? o : nh - 1;
+      n = (c & 63) >= 32 ? o + nh : o;
+    } else {
+      n = n0 + c < N ? n0 + c : N - 1;
+    }
+    bptr[i] = qweight + n * words + q * 4;
+  }
+  // this lane's two weight rows (gated: gate row n and up row n + N/2): scales and zeros
+  int64_t bcol[2];
+  if constexpr (GATED) {
+    const int64_t n = n0 + wn * 32 + m32;
+    bcol[0] = n < nh ? n : nh - 1;
+    bcol[1] = bcol[0] + nh;
+  } else {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int64_t n = n0 + wn * 64 + b * 32 + m32;
+      bcol[b] = n < N ? n : N - 1;
+    }
+  }
+  struct ScaleZero {
+    uint32_t zb[2], sc[2];
+  };
+  auto load_sz = [&](ScaleZero& st, int64_t step) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      st.zb[b] = zeros[bcol[b] * zbw + (step >> (1 - g64))];
+      st.sc[b] = scales[bcol[b] * Gs + (step << g64) + (g64 & kh)];
+    }
+  };
+  auto dma = [&](int64_t step, uint4* ad, uint4* bd) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(xblk + step * kWK + aoff[i]),
+                                       (lds_void*)&ad[(wave * 8 + i) * 64], 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(bptr[i] + step * 16),
+                                       (lds_void*)&bd[(wave * 2 + i) * 64], 16, 0, 0);
+  };
+
+  f32x16w acc[4][2];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16w{};
+
+  ScaleZero s0, s1;
+  dma(0, a0s, b0s);
+  load_sz(s0, 0);
+  __syncthreads();
+
+  // One K step on buffer BUF (a compile-time constant, so each LDS access names one object).
+  auto body = [&](auto bufc, ScaleZero& cur, ScaleZero& nxt, int64_t step) {
+    constexpr int BUF = decltype(bufc)::value;
+    const uint4* ab = BUF ? a1s : a0s;
+    const uint4* bb = BUF ? b1s : b0s;
+    // the next step's operands (clamped: the last step reloads itself into the idle buffer)
+    const int64_t sn = step + 1 < nsteps ? step + 1 : nsteps - 1;
+    dma(sn, BUF ? a0s : a1s, BUF ? b0s : b1s);
+    load_sz(nxt, sn);
+    __builtin_amdgcn_sched_barrier(0);  // keep those loads at the top of the step
+    half2w zz[2], s2[2];
+    const int hi = g64 ? kh : (int)(step & 1);  // zero nibble: group of 128 (step) or 64 (2 step + kh)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const uint32_t z = hi ? (cur.zb[b] >> 4) : (cur.zb[b] & 0xF);
+      const uint32_t zbits = 0x6400u + z;
+      zz[b] = -__builtin_bit_cast(half2w, zbits | (zbits << 16));
+      s2[b] = __builtin_bit_cast(half2w, cur.sc[b] | (cur.sc[b] << 16));
+    }
+    auto frags = [&](int s, half8w (&A)[4], half8w (&B)[2]) {
+      const int c = kh * 8 + s;
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int r = wm * 128 + a * 32 + m32;
+        A[a] = __builtin_bit_cast(half8w, ab[r * 16 + (c ^ (r & 15))]);
+      }
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int col = wn * 64 + b * 32 + m32;
+        const uint32_t w = reinterpret_cast<const uint32_t*>(bb)[col * 16 + kh * 8 + s];
+        B[b] = widen_word(w, zz[b], s2[b], magic);
+      }
+    };
+    half8w A0[4], B0[2], A1[4], B1[2];
+    frags(0, A0, B0);
+#pragma unroll
+    for (int s = 0; s < kWK / 16; s += 2) {
+      frags(s + 1, A1, B1);
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A0[a], B0[b], acc[a][b], 0, 0, 0);
+      if (s + 2 < kWK / 16) frags(s + 2, A0, B0);
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A1[a], B1[b], acc[a][b], 0, 0, 0);
+    }
+    __syncthreads();  // the next step's DMA has landed; this step's buffer is free
+  };
+  int64_t step = 0;
+  for (; step + 2 <= nsteps; step += 2) {
+    body(std::integral_constant<int, 0>{}, s0, s1, step);
+    body(std::integral_constant<int, 1>{}, s1, s0, step + 1);
+  }
+  if (step < nsteps) body(std::integral_constant<int, 0>{}, s0, s1, step);
+
+  // 32x32 accumulator layout: element e of lane l is (row 8(e/4) + 4(l/32) + e%4, col l%32).
+  if constexpr (GATED) {
+    const int64_t col = n0 + wn * 32 + m32;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t row = m0 + wm * 128 + a * 32 + 8 * (e >> 2) + 4 * kh + (e & 3);
+        if (row < M && col < nh) Y[row * nh + col] = f2h_bits(silu_f32(acc[a][0][e]) * acc[a][1][e]);
+      }
+  } else {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int64_t col = n0 + wn * 64 + b * 32 + m32;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int64_t row = m0 + wm * 128 + a * 32 + 8 * (e >> 2) + 4 * kh + (e & 3);
+          if (row < M && col < N) Y[row * N + col] = f2h_bits(acc[a][b][e]);
+        }
+      }
+  }
+}
+
+}  // namespace
+
+int64_t gemm_wide_tiles(int64_t M, int64_t N, bool gated) {
+  const int64_t mt = (M + kWM - 1) / kWM;
+  const int64_t nt = gated ? (N / 2 + kWN / 2 - 1) / (kWN / 2) : (N + kWN - 1) / kWN;
+  return mt * nt;
+}
+
+bool gemm_wide_supported(int64_t K, int group, int w_bit) {
+  return w_bit == 4 && (group == 128 || group == 64) && (int64_t)kWM * K < ((int64_t)1 << 32);
+}
+
+hipError_t launch_gemm_wide(const uint16_t* X, int64_t M, const uint32_t* qweight,
+                            const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
+                            int group, uint16_t* Y, bool gated, hipStream_t stream) {
+  const int64_t mt = (M + kWM - 1) / kWM;
+  const int64_t nt = gated ? (N / 2 + kWN / 2 - 1) / (kWN / 2) : (N + kWN - 1) / kWN;
+  const int64_t per_xcd = (mt * nt + 7) / 8;
+  const dim3 grid((unsigned)(per_xcd * 8));
+  if (gated)
+    hipLaunchKernelGGL(k_gemm_wide<true>, grid, dim3(512), 0, stream, X, M, qweight, scales, zeros,
+                       N, K, group, Y, mt, nt, per_xcd);
+  else
+    hipLaunchKernelGGL(k_gemm_wide<false>, grid, dim3(512), 0, stream, X, M, qweight, scales, zeros,
+                       N, K, group, Y, mt, nt, per_xcd);
+  return hipGetLastError();
+}
+
+}  // namespace awq
