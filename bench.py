@@ -174,21 +174,24 @@ def measure_peaks(torch, lib, dev, stream, timer, reps, sizes):
     import ctypes as C
     out = {"read_stream": {}, "method": "awq_peak_read_stream / awq_peak_mfma (include/awq_peaks.h); "
                                         "median over replays, HIP events"}
-    for label, nbytes in sizes:
+    for label, nbytes, copies in sizes:
+        # `copies` distinct buffers read one after another inside one graph (their sum far
+        # beyond the 256 MB last-level cache), so every launch streams from HBM and the
+        # graph launch overhead is shared: per-launch time = replay time / copies
         n = nbytes // 16 * 16
-        buf = torch.empty(n, dtype=torch.uint8, device=dev)
-        buf.fill_(7)
+        bufs = [torch.full((n,), 7, dtype=torch.uint8, device=dev) for _ in range(copies)]
         sink = torch.empty(4 * (n // 16384 + 1), dtype=torch.int32, device=dev)
         best = None
         for per_thread in (4, 8, 16):
-            def run(u=per_thread, buf=buf):
-                lib.awq_peak_read_stream(C.c_void_p(buf.data_ptr()), n, C.c_void_p(sink.data_ptr()),
-                                         u, C.c_void_p(stream.cuda_stream))
+            def run(u=per_thread):
+                for b in bufs:
+                    lib.awq_peak_read_stream(C.c_void_p(b.data_ptr()), n, C.c_void_p(sink.data_ptr()),
+                                             u, C.c_void_p(stream.cuda_stream))
             with torch.cuda.stream(stream):
-                for _ in range(3):
-                    run()
+                run()
                 g = capture(torch, stream, run)
-                t = timer.replays(g.replay, reps if nbytes < 2 ** 31 else max(5, reps // 5))
+                g.replay()
+                t = [x / copies for x in timer.replays(g.replay, max(10, reps // 2))]
             med = pct(t, 0.5)
             if best is None or med < best[0]:
                 best = (med, per_thread, t)
@@ -196,8 +199,10 @@ def measure_peaks(torch, lib, dev, stream, timer, reps, sizes):
         out["read_stream"][label] = {"bytes": n, "gbs": round(n / (med * 1e-3) / 1e9, 1),
                                      "gbs_p10": round(n / (pct(t, 0.9) * 1e-3) / 1e9, 1),
                                      "gbs_p90": round(n / (pct(t, 0.1) * 1e-3) / 1e9, 1),
-                                     "median_us": round(med * 1e3, 3), "loads_per_thread": per_thread}
-        del buf, sink
+                                     "median_us": round(med * 1e3, 3), "loads_per_thread": per_thread,
+                                     "launches_per_graph": copies}
+        del bufs, sink
+        torch.cuda.empty_cache()
     fs = torch.empty(4 * 8192, dtype=torch.float32, device=dev)
     iters, blocks = 4096, 2048  # 8 waves per CU
     flops = blocks * 4 * iters * 8 * 2 * 32 * 32 * 16
@@ -813,8 +818,8 @@ def main():
             "gbs": round(gemv_bytes / (dh["median_ms"] * 1e-3) / 1e9, 1), "median_ms": dh["median_ms"]}
         log("bench: measured peaks")
         peaks = measure_peaks(torch, lib, dev, stream, timer, args.reps,
-                              [("fused_decode_launch", round(gemv_bytes / n_gemv)),
-                               ("1GiB", 2 ** 30), ("8GiB", 2 ** 33)])
+                              [("fused_decode_launch", round(gemv_bytes / n_gemv), 32),
+                               ("1GiB", 2 ** 30, 4), ("8GiB", 2 ** 33, 2)])
         result["peaks"] = peaks
         rs = peaks["read_stream"]
         # the measured peak: the best read stream; beside it the read stream of the decode

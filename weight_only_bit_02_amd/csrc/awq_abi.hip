@@ -1,6 +1,7 @@
 // C ABI of libawq_mi355x: argument validation, workspace layout, kernel dispatch.
 // The operations and their sources are documented in include/awq.h.
 #include <stdlib.h>
+#include <string.h>
 
 #include <mutex>
 
@@ -97,7 +98,12 @@ const int g_gemv_max_m = gemv_max_m_from_env();
 extern "C" {
 
 const char* awq_status_string(awq_status s) {
-  switch (s) {
+  // callers may pass any integer: read it as one (a value outside the enumerators is not a
+  // valid awq_status in C++, so it must not be switched on as one)
+  int v = 0;
+  static_assert(sizeof(s) == sizeof(v), "awq_status is an int-sized enum");
+  memcpy(&v, &s, sizeof v);
+  switch (v) {
     case AWQ_OK: return "ok";
     case AWQ_ERR_NULL_POINTER: return "a required pointer is NULL";
     case AWQ_ERR_BAD_SHAPE: return "bad shape (sizes must be >= 1, K a multiple of 128, T <= 8192)";
@@ -242,15 +248,18 @@ awq_status awq_search_scales_noalloc(const void* X, int64_t T, const void* W, in
 static awq_status linear_common(const void* X, int64_t M, const uint32_t* qweight,
                                 const void* scales, const uint8_t* zeros, int64_t N, int64_t K,
                                 const awq_config* cfg, void* Y, uint32_t* flags,
-                                awq_linear_kernel kernel, bool gated, void* stream) {
+                                awq_linear_kernel kernel_arg, bool gated, void* stream) {
+  // the caller may pass any integer: validate it as one before it is used as the enum
+  int kv = 0;
+  static_assert(sizeof(kernel_arg) == sizeof(kv), "awq_linear_kernel is an int-sized enum");
+  memcpy(&kv, &kernel_arg, sizeof kv);
   const awq_config c = resolve(cfg);
   if (!X || !qweight || !scales || !zeros || !Y) return AWQ_ERR_NULL_POINTER;
   if (!supported(c)) return AWQ_ERR_UNSUPPORTED;
   if (M < 1 || M >= kMaxDim || !good_nk(N, K)) return AWQ_ERR_BAD_SHAPE;
   if (gated && (N < 2 || N % 2 != 0)) return AWQ_ERR_BAD_SHAPE;
-  if (kernel != AWQ_LINEAR_AUTO && kernel != AWQ_LINEAR_GEMV && kernel != AWQ_LINEAR_GEMM &&
-      kernel != AWQ_LINEAR_SKINNY && kernel != AWQ_LINEAR_GEMM_WIDE)
-    return AWQ_ERR_UNSUPPORTED;
+  if (kv < AWQ_LINEAR_AUTO || kv > AWQ_LINEAR_GEMM_WIDE) return AWQ_ERR_UNSUPPORTED;
+  awq_linear_kernel kernel = (awq_linear_kernel)kv;
   if (kernel == AWQ_LINEAR_GEMM_WIDE && !awq::gemm_wide_supported(K, c.group_size, c.w_bit))
     return AWQ_ERR_UNSUPPORTED;
   if (kernel == AWQ_LINEAR_GEMV && M > awq::kGemvMaxM) return AWQ_ERR_BAD_SHAPE;
