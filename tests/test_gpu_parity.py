@@ -270,7 +270,8 @@ def test_linear_auto_dispatch_and_determinism():
 @pytest.mark.parametrize("N,K", [
     (4097, 4096), (9000, 1152), (11008, 4096), (4096, 11008),  # one row per wave
     (16389, 4096), (16387, 2048),  # tall: two rows per wave, odd N (last row clamped)
-    (129, 18432),                  # more than 8 chunks per lane: batched kernel, 3 batches
+    (129, 18432), (130, 28672),    # 9 and 14 chunks per lane: one batch, one row per wave
+    (7, 32768),                    # 16 chunks per lane (the longest row that fits LDS)
     (65, 33024),                   # activation row beyond 64 KiB of LDS: generic kernel
 ])
 def test_gemv_m1_launch_shapes(N, K):

@@ -394,8 +394,8 @@ static hipError_t launch_gemv1s(const uint16_t* X, const uint32_t* qw, const uin
 // M = 1 dispatch (K <= 32768, so the activation row fits 64 KiB of LDS). Up to eight
 // chunks per lane (K <= 16384): the single-batch kernel, two rows per wave for tall
 // matrices with at most two chunks per lane (measured on the Llama-2 7B shapes), else
-// one; gated, always the gate row and the up row. Longer rows: the batched kernel, four
-// chunks per lane per batch.
+// one; gated, always the gate row and the up row. Longer rows: plain, the single-batch
+// kernel with one row per wave; gated, the batched kernel, four chunks per lane per batch.
 template <bool GATED>
 static hipError_t launch_gemv_m1(const uint16_t* X, const uint32_t* qw, const uint16_t* sc,
                                  const uint8_t* z, int64_t N, int64_t K, int gsh, uint16_t* Y,
@@ -419,9 +419,21 @@ static hipError_t launch_gemv_m1(const uint16_t* X, const uint32_t* qw, const ui
                          : launch_gemv1s<7, 1, false>(X, qw, sc, z, N, K, gsh, Y, stream);
     case 8: return GATED ? launch_gemv1s<8, 2, GATED>(X, qw, sc, z, N, K, gsh, Y, stream)
                          : launch_gemv1s<8, 1, false>(X, qw, sc, z, N, K, gsh, Y, stream);
-    default: return GATED ? launch_gemv1<2, 4, GATED>(X, qw, sc, z, N, K, gsh, Y, stream)
-                          : launch_gemv1<1, 4, false>(X, qw, sc, z, N, K, gsh, Y, stream);
+    // longer rows (K up to 32768), plain: still one batch of all of a lane's loads (on the
+    // Llama-2-70B down_proj, K = 28672, 25% faster than batches of four); gated: the
+    // batched kernel (two rows per wave with all loads up front would take every register)
+    case 9: if (!GATED) return launch_gemv1s<9, 1, false>(X, qw, sc, z, N, K, gsh, Y, stream); break;
+    case 10: if (!GATED) return launch_gemv1s<10, 1, false>(X, qw, sc, z, N, K, gsh, Y, stream); break;
+    case 11: if (!GATED) return launch_gemv1s<11, 1, false>(X, qw, sc, z, N, K, gsh, Y, stream); break;
+    case 12: if (!GATED) return launch_gemv1s<12, 1, false>(X, qw, sc, z, N, K, gsh, Y, stream); break;
+    case 13: if (!GATED) return launch_gemv1s<13, 1, false>(X, qw, sc, z, N, K, gsh, Y, stream); break;
+    case 14: if (!GATED) return launch_gemv1s<14, 1, false>(X, qw, sc, z, N, K, gsh, Y, stream); break;
+    case 15: if (!GATED) return launch_gemv1s<15, 1, false>(X, qw, sc, z, N, K, gsh, Y, stream); break;
+    case 16: if (!GATED) return launch_gemv1s<16, 1, false>(X, qw, sc, z, N, K, gsh, Y, stream); break;
+    default: break;
   }
+  return GATED ? launch_gemv1<2, 4, GATED>(X, qw, sc, z, N, K, gsh, Y, stream)
+               : launch_gemv1<1, 4, false>(X, qw, sc, z, N, K, gsh, Y, stream);
 }
 
 template <int M, bool GATED>

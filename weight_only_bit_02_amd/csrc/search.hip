@@ -135,12 +135,20 @@ __device__ __forceinline__ bool quantize_tile_group(const uint16_t* W, int64_t N
     for (int i = 0; i < 8; ++i) rs[i] = __builtin_amdgcn_rcpf(sf[i]);
   }
   bool bad = false;
+  // every pass's weights are loaded before any is used: the passes are separated by the
+  // quantizer's wave-uniform branches, past which the compiler would not hoist the loads,
+  // so each pass would otherwise wait out a full memory latency on its own
+  uint4 wvs[kPasses];
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    const int64_t n = n0 + p * kRowsPerPass + q_row;
+    wvs[p] = *reinterpret_cast<const uint4*>(W + (n < N ? n : N - 1) * K + k0);
+  }
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) {
     const int row = p * kRowsPerPass + q_row;
     const int64_t n = n0 + row;
-    const int64_t nc = n < N ? n : N - 1;
-    uint4 wv = *reinterpret_cast<const uint4*>(W + nc * K + k0);
+    uint4 wv = wvs[p];
     if (n >= N) wv = make_uint4(0, 0, 0, 0);
     const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
     float wf[8], wp[8];
