@@ -280,15 +280,16 @@ static awq_status linear_common(const void* X, int64_t M, const uint32_t* qweigh
   if (kernel == AWQ_LINEAR_AUTO && c.w_bit != 4)
     kernel = M <= awq::kGemvMaxM ? AWQ_LINEAR_GEMV
              : M <= awq::kSkinnyMaxM ? AWQ_LINEAR_SKINNY : AWQ_LINEAR_GEMM;
-  if (kernel == AWQ_LINEAR_AUTO)
+  if (kernel == AWQ_LINEAR_AUTO) {
     kernel = M <= awq::kVgemvAutoMaxM && M <= g_gemv_max_m ? AWQ_LINEAR_GEMV
              : M <= g_gemv_max_m                            ? AWQ_LINEAR_SKINNY
                                                             : AWQ_LINEAR_GEMM;
-  // the 256 x 256 tiling once it gives the chip 1.5 tiles per CU or more (measured on the
-  // Llama-2-7B shapes at M = 2048: ahead from 384 tiles, behind at 128)
-  if (kernel == AWQ_LINEAR_GEMM && awq::gemm_wide_supported(K, c.group_size, c.w_bit) &&
-      awq::gemm_wide_tiles(M, N, gated) >= awq::kWideMinTiles)
-    kernel = AWQ_LINEAR_GEMM_WIDE;
+    // the 256 x 256 tiling once it gives the chip 1.5 tiles per CU or more (measured on the
+    // Llama-2-7B shapes at M = 2048: ahead from 384 tiles, behind at 128)
+    if (kernel == AWQ_LINEAR_GEMM && awq::gemm_wide_supported(K, c.group_size, c.w_bit) &&
+        awq::gemm_wide_tiles(M, N, gated) >= awq::kWideMinTiles)
+      kernel = AWQ_LINEAR_GEMM_WIDE;
+  }
   const auto* Xh = (const uint16_t*)X;
   const auto* sc = (const uint16_t*)scales;
   auto* Yh = (uint16_t*)Y;

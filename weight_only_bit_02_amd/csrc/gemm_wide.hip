@@ -14,7 +14,8 @@
 //     buffer is its own LDS object, so the compiler waits only for the DMA of the buffer
 //     a step reads. A (activations, 256 rows x 16 chunks of 16 bytes per step) is stored
 //     with chunk c of row r in slot c ^ (r & 15), so the 32 rows a fragment read touches
-//     fall in distinct banks; B (codes, 256 columns x 64 bytes) as it is in memory.
+//     fall in distinct banks; B (codes, 256 columns x 64 bytes) quarter-major, so a lane's
+//     16-byte read of 4 words for its column is conflict-free.
 //   - Each wave widens its own B words from LDS to (q - z) sc in fp16 (the packed layout
 //     puts channels 2p, 2p + 1 in nibbles p and p + 4, so one mask per pair and the 0x6400
 //     exponent give the pair exactly, then a packed subtract of 1024 + z and a packed
@@ -95,15 +96,16 @@ __global__ void __launch_bounds__(512)
     const int64_t gr = m0 + r < M ? r : M - 1 - m0;
     aoff[i] = (uint32_t)(gr * K + ((lane & 15) ^ (r & 15)) * 8);
   }
-  // B DMA map: slot (wave * 2 + i) * 64 + lane = tile column c (slot / 4), 16-byte quarter
-  // q (slot % 4) of the column's 64 code bytes of a step. Gated: tile column c is wave
-  // tile c / 64's gate column (c % 64 < 32) or up column. Columns past the end read the
-  // last one (never stored).
+  // B DMA map, quarter-major: slot (wave * 2 + i) * 64 + lane = 16-byte quarter q (slot /
+  // 256) of tile column c (slot % 256) of the columns' 64 code bytes of a step, so a wave's
+  // read of one quarter of 32 consecutive columns is 512 contiguous bytes (no bank
+  // conflicts). Gated: tile column c is wave tile c / 64's gate column (c % 64 < 32) or up
+  // column. Columns past the end read the last one (never stored).
   const uint32_t* bptr[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int slot = (wave * 2 + i) * 64 + lane;
-    const int c = slot >> 2, q = slot & 3;
+    const int c = slot & 255, q = slot >> 8;
     int64_t n;
     if constexpr (GATED) {
       int64_t o = n0 + (c >> 6) * 32 + (c & 31);
@@ -178,6 +180,13 @@ __global__ void __launch_bounds__(512)
       zz[b] = -__builtin_bit_cast(half2w, zbits | (zbits << 16));
       s2[b] = __builtin_bit_cast(half2w, cur.sc[b] | (cur.sc[b] << 16));
     }
+    // this lane's code words of the step: words 8 kh .. 8 kh + 7 of each of its two columns,
+    // quarters 2 kh and 2 kh + 1 (one 16-byte read each)
+    uint4 bq[2][2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) bq[b][h] = bb[(2 * kh + h) * 256 + wn * 64 + b * 32 + m32];
     auto frags = [&](int s, half8w (&A)[4], half8w (&B)[2]) {
       const int c = kh * 8 + s;
 #pragma unroll
@@ -187,8 +196,8 @@ __global__ void __launch_bounds__(512)
       }
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
-        const int col = wn * 64 + b * 32 + m32;
-        const uint32_t w = reinterpret_cast<const uint32_t*>(bb)[col * 16 + kh * 8 + s];
+        const uint4 q = bq[b][s >> 2];
+        const uint32_t w = (s & 3) == 0 ? q.x : (s & 3) == 1 ? q.y : (s & 3) == 2 ? q.z : q.w;
         B[b] = widen_word(w, zz[b], s2[b], magic);
       }
     };

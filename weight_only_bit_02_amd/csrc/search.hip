@@ -120,6 +120,15 @@ __device__ __forceinline__ bool quantize_tile_group(const uint16_t* W, int64_t N
   const int q_row = row_base + (tid >> 4);
   const int li = tid & 15;
   const int64_t k0 = j * kGroup + li * 8;
+  // every pass's weights and the scales are loaded before any is used: the passes are
+  // separated by the quantizer's wave-uniform branches, past which the compiler would not
+  // hoist the loads, so each pass would otherwise wait out a full memory latency on its own
+  uint4 wvs[kPasses];
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    const int64_t n = n0 + p * kRowsPerPass + q_row;
+    wvs[p] = *reinterpret_cast<const uint4*>(W + (n < N ? n : N - 1) * K + k0);
+  }
   // the thread's 8 channels are the same in every pass: s and 1/s once
   uint4 sv = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);  // s = 1
   if (!CLIP || s) sv = *reinterpret_cast<const uint4*>(s + k0);
@@ -135,15 +144,6 @@ __device__ __forceinline__ bool quantize_tile_group(const uint16_t* W, int64_t N
     for (int i = 0; i < 8; ++i) rs[i] = __builtin_amdgcn_rcpf(sf[i]);
   }
   bool bad = false;
-  // every pass's weights are loaded before any is used: the passes are separated by the
-  // quantizer's wave-uniform branches, past which the compiler would not hoist the loads,
-  // so each pass would otherwise wait out a full memory latency on its own
-  uint4 wvs[kPasses];
-#pragma unroll
-  for (int p = 0; p < kPasses; ++p) {
-    const int64_t n = n0 + p * kRowsPerPass + q_row;
-    wvs[p] = *reinterpret_cast<const uint4*>(W + (n < N ? n : N - 1) * K + k0);
-  }
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) {
     const int row = p * kRowsPerPass + q_row;
