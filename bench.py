@@ -550,6 +550,10 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="only the headline step (no peaks, distributions, 70B, single linear, crossover)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying graphs")
+    ap.add_argument("--only", default="", metavar="PARTS",
+                    help="comma-separated parts (search, clip, quant_pack, fold, gemv, gemv_unfused, "
+                         "gemm, mfma_loop, read_stream) run eagerly --steps times each, then exit without timing: "
+                         "a short driver for hardware counter passes")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="first run one plain device copy of BYTES (a known-size kernel for "
                          "calibrating HBM traffic counters)")
@@ -672,6 +676,36 @@ def main():
     parts = [("search", part_search), ("clip", part_clip), ("quant_pack", part_pack), ("fold", part_fold),
              ("gemv", part_gemv), ("gemv_unfused", part_gemv_unfused), ("gemm", part_gemm)]
     stream = torch.cuda.Stream()
+    if args.only:
+        fs = torch.empty(4 * 8192, dtype=torch.float32, device=dev)
+
+        def part_mfma_loop():  # the fp16 MFMA loop of the peak measurement (counter calibration)
+            import ctypes as C
+            lib.awq_peak_mfma(4096, C.c_void_p(fs.data_ptr()), 2048, C.c_void_p(stream.cuda_stream))
+        rs_n = sum(linear_bytes(1, N, K, g in GATED) for g, (N, K) in SEARCH_GROUPS.items()) // 4 // 16 * 16
+        rs_bufs = [torch.full((rs_n,), 7, dtype=torch.uint8, device=dev) for _ in range(8)] \
+            if "read_stream" in args.only else []
+        rs_sink = torch.empty(4 * (rs_n // 16384 + 1), dtype=torch.int32, device=dev)
+
+        def part_read_stream():  # plain reads of one average fused decode launch's bytes
+            import ctypes as C
+            for b in rs_bufs:
+                lib.awq_peak_read_stream(C.c_void_p(b.data_ptr()), rs_n, C.c_void_p(rs_sink.data_ptr()),
+                                         4, C.c_void_p(stream.cuda_stream))
+        known = dict(parts, mfma_loop=part_mfma_loop, read_stream=part_read_stream)
+        chosen = [p for p in args.only.split(",") if p]
+        unknown = [p for p in chosen if p not in known]
+        if unknown:
+            print(f"bench.py: unknown part(s) {unknown}; choose from {sorted(known)}", file=sys.stderr)
+            sys.exit(2)
+        with torch.cuda.stream(stream):
+            for pname in chosen:
+                log(f"bench: part {pname} x{args.steps} (eager)")
+                for _ in range(args.steps):
+                    known[pname]()
+                torch.cuda.synchronize()
+        print(json.dumps({"only": chosen, "steps": args.steps}), flush=True)
+        return
     timer = Timer(torch, stream)
     runners = {}
     with torch.cuda.stream(stream):
@@ -782,7 +816,8 @@ def main():
                  "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2),
                               "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                               "frac": round(gemm_tflops / FP16_MFMA_PEAK_TFLOPS, 4),
-                              "kernel": "awq::k_gemm"}},
+                              "kernel": "awq::k_gemm_wide (q|k|v, gate|up: 384 tiles or more) and "
+                                        "awq::k_gemm (o, down)"}},
         "search": {"tflops_algorithmic": round(search_tflops, 2), "ms": round(part_ms["search"], 4),
                    "best_alpha_index": best,
                    "roofline": {"bound": "mfma", "achieved": round(search_tflops, 2),
