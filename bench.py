@@ -354,6 +354,38 @@ def time_variants(awq, si, dev, stream, Xcal, Wg, s_best, xdec, xpre, steps, war
     return out
 
 
+# ---------------------------------------------------------------------------- dense reference
+def dense_reference(torch, dev, stream, timer, reps):
+    """torch's dense fp16 GEMM (the vendor library, no weight widening) on the four 7B GEMM
+    shapes at M = 2048: a measured practical ceiling for the W4A16 GEMM, same box, same run."""
+    out = {"library": "torch.mm fp16 (hipBLASLt / rocBLAS), operands contiguous, fp16 output", "shapes": {}}
+    tot_ms = tot_fl = 0.0
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    for name, (N, K) in SEARCH_GROUPS.items():
+        a = torch.randn((PREFILL_M, K), generator=g, device=dev).half()
+        b = torch.randn((K, N), generator=g, device=dev).half()  # W^T, contiguous
+        c = torch.empty((PREFILL_M, N), dtype=torch.float16, device=dev)
+
+        def mm(a=a, b=b, c=c):
+            torch.mm(a, b, out=c)
+        with torch.cuda.stream(stream):
+            mm()
+            torch.cuda.synchronize()
+            gr = capture(torch, stream, mm)
+            gr.replay()
+            t = pct(timer.replays(gr.replay, reps), 0.5)
+        fl = 2 * PREFILL_M * N * K
+        out["shapes"][name] = {"N": N, "K": K, "ms": round(t, 4), "tflops": round(fl / (t * 1e-3) / 1e12, 1)}
+        tot_ms += t
+        tot_fl += fl
+        del a, b, c, gr
+    out["tflops"] = round(tot_fl / (tot_ms * 1e-3) / 1e12, 1)
+    out["ms"] = round(tot_ms, 4)
+    torch.cuda.synchronize()
+    return out
+
+
 # ---------------------------------------------------------------------------- single linear
 def single_linear(awq, si, dev, stream, timer, reps):
     """The single-linear workload: K = N = 1024, W ~ N(0, 0.02^2), calibration X of 256
@@ -874,6 +906,10 @@ def main():
         log("bench: single linear")
         result["single_linear"] = single_linear(awq, si, dev, stream, timer, args.reps)
         result["crossover"] = crossover(awq, packed[0], dev, stream)
+        log("bench: dense fp16 reference GEMM")
+        dref = dense_reference(torch, dev, stream, timer, args.reps)
+        dref["w4a16_over_dense"] = round(gemm_tflops / dref["tflops"], 3)
+        result["gemm"]["dense_fp16_reference"] = dref
     if not args.no_variants:
         del views
         packed = packed[:1]

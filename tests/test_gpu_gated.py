@@ -62,6 +62,16 @@ def test_gated_skinny_matches_oracle(M, nh, K):
     _check(si.activations(M, K, offset=M + 500), p, ref, "skinny")
 
 
+@pytest.mark.parametrize("M", [2, 16, 30, 33, 64])
+@pytest.mark.parametrize("nh,K", [(16400, 128), (16384, 384)])
+def test_gated_skinny_two_row_tiles(M, nh, K):
+    """The gated skinny kernel's two-row-tile form (taken from 512 blocks of 32 outputs),
+    ragged (16400 outputs: 513 blocks, the last one's second tile wholly past the end) and
+    even (16384: exactly the threshold)."""
+    p, ref = _gated_case(nh, K, off=nh + 29 * K)
+    _check(si.activations(M, K, offset=M + 520), p, ref, "skinny")
+
+
 @pytest.mark.parametrize("M", [33, 47, 64])
 @pytest.mark.parametrize("group", [64, 32])
 def test_gated_skinny_two_tiles_small_groups(M, group):

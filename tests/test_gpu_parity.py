@@ -221,6 +221,17 @@ def test_skinny_matches_oracle(M, N, K):
     _check_linear(si.activations(M, K, offset=M + 400), p, ref, "skinny")
 
 
+@pytest.mark.parametrize("M", [1, 5, 16, 29, 32, 37, 64])
+@pytest.mark.parametrize("N,K", [(10301, 256), (12288, 128), (10240, 1152)])
+def test_skinny_two_row_tiles_matches_oracle(M, N, K):
+    """The skinny kernel's two-row-tile form (a wave multiplies each X piece into two tiles
+    of 32 rows; taken from 160 blocks of 64 rows), with ragged rows (10301: 161 blocks, the
+    last one 61 rows, its second tile 3 rows past N), the threshold itself (10240) and
+    uneven K splits."""
+    p, ref = _packed_case(N, K, off=N + 7 * K)
+    _check_linear(si.activations(M, K, offset=M + 450), p, ref, "skinny")
+
+
 @pytest.mark.parametrize("M", [1, 8, 9, 16, 63, 64, 65, 130, 257])
 @pytest.mark.parametrize("N,K", [(1, 128), (67, 384), (256, 4096), (130, 1152)])
 def test_gemm_matches_oracle(M, N, K):

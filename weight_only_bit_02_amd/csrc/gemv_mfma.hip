@@ -7,8 +7,9 @@
 // With more than one token, dot products on the vector ALU cost one v_dot2 per channel
 // pair per token; here they go to the matrix cores instead, so the vector work per byte
 // of codes (the exact widening to q - z) does not grow with M:
-//   - a wave owns 32 weight rows (the 32 columns of a v_mfma_f32_32x32x16_f16 tile) and
-//     a slice of the K groups; lane l works on row l % 32 and, h = l / 32, on channels
+//   - a wave owns R tiles of 32 weight rows (each the 32 columns of a
+//     v_mfma_f32_32x32x16_f16 tile; R = 2 on launches with enough rows, so each X piece
+//     feeds both tiles) and a slice of the K groups; lane l works on row l % 32 and, h = l / 32, on channels
 //     [32 h, 32 h + 32) and [64 + 32 h, 96 + 32 h) of each group (two 16-byte code loads
 //     per group; lanes l and l + 32 read 32 contiguous bytes of the row together);
 //   - word s of those 64 channels is the lane's B operand of k16 step s, widened exactly
@@ -41,11 +42,14 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 namespace {
 
-template <int MT>
+// dispatch: two row tiles per wave from this many blocks (see launch_skinny_t)
+constexpr int64_t kSkinnyR2MinBlocks = 160, kSkinnyR2MinBlocksGated = 512;
+
+template <int MT, int R>
 struct SkinnyStage {
-  uint4 b[2];     // 8 packed words: channels 32 h + [0, 32) and 64 + 32 h + [0, 32), row l % 32
-  uint4 a[MT][8]; // X[token][same channels] per token tile, one 16-byte piece per k16 step
-  uint32_t sc[2], zb;  // the lane's scales of words 0-3 and 4-7; the step's zero byte(s)
+  uint4 b[R][2];     // per row tile: 8 packed words, channels 32 h + [0, 32) and 64 + 32 h + [0, 32), row l % 32
+  uint4 a[MT][8];    // X[token][same channels] per token tile, one 16-byte piece per k16 step
+  uint32_t sc[R][2], zb[R];  // per row tile: the lane's scales of words 0-3 and 4-7; the step's zero byte(s)
 };
 
 __device__ __forceinline__ uint32_t skinny_magic() {
@@ -67,12 +71,13 @@ __device__ __forceinline__ half8 widen_word(uint32_t w, half2v zz, uint32_t magi
 
 // E = accumulator elements kept per lane: rows 8 (e / 4) + 4 h + e % 4 of the 32 x 32 tile;
 // E = 4 serves M <= 8, 8 serves M <= 16, 16 serves M <= 32; MT = 2 token tiles of 32 (rows
-// 32 t + ...) serve M <= 64.
-template <int S, int E, int MT, bool GATED>
+// 32 t + ...) serve M <= 64. R = row tiles of 32 per wave, all multiplied by the same X
+// pieces: R = 2 halves the activation bytes a wave loads per weight byte.
+template <int S, int E, int MT, int R, bool GATED>
 __global__ void __launch_bounds__(S * 64)
     k_gemv_mfma(const uint16_t* X, int64_t M, const uint32_t* qweight, const uint16_t* scales,
                 const uint8_t* zeros, int64_t N, int64_t K, int group, uint16_t* Y) {
-  __shared__ float red[S][MT * E][64];
+  __shared__ float red[S][R * MT * E][64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -83,13 +88,16 @@ __global__ void __launch_bounds__(S * 64)
   // rows of this tile: plain, 32 consecutive rows; gated, 16 gate rows then their 16 up
   // rows (tile columns j and j + 16 hold g and u of output n0 + j)
   const int64_t nh = N / 2;
-  int64_t n;
-  if constexpr (GATED) {
-    const int64_t o = (int64_t)blockIdx.x * 16 + (j & 15);
-    n = (o < nh ? o : nh - 1) + (j >> 4) * nh;
-  } else {
-    const int64_t o = (int64_t)blockIdx.x * 32 + j;
-    n = o < N ? o : N - 1;
+  int64_t n[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if constexpr (GATED) {
+      const int64_t o = ((int64_t)blockIdx.x * R + r) * 16 + (j & 15);
+      n[r] = (o < nh ? o : nh - 1) + (j >> 4) * nh;
+    } else {
+      const int64_t o = ((int64_t)blockIdx.x * R + r) * 32 + j;
+      n[r] = o < N ? o : N - 1;
+    }
   }
   int64_t xrow[MT];  // token row of lane l in tile t: 32 t + l % 32 (past M: row M - 1, never stored)
 #pragma unroll
@@ -98,23 +106,27 @@ __global__ void __launch_bounds__(S * 64)
   const int64_t g0 = G * wave / S, g1 = G * (wave + 1) / S;
   const uint32_t magic = skinny_magic();
 
-  auto load = [&](SkinnyStage<MT>& st, int64_t g) {
-    if (g32) {
-      // words 0-3 of lane half h: group 4g + h; words 4-7: group 4g + 2 + h
-      st.zb = (uint32_t)zeros[n * zbytes + 2 * g] | ((uint32_t)zeros[n * zbytes + 2 * g + 1] << 8);
-      st.sc[0] = scales[n * Gs + 4 * g + h];
-      st.sc[1] = scales[n * Gs + 4 * g + 2 + h];
-    } else if (g64) {
-      st.zb = zeros[n * zbytes + g];  // groups 2g (low nibble) and 2g + 1 (high)
-      st.sc[0] = scales[n * Gs + 2 * g];
-      st.sc[1] = scales[n * Gs + 2 * g + 1];
-    } else {
-      st.zb = zeros[n * zbytes + (g >> 1)];
-      st.sc[0] = st.sc[1] = scales[n * Gs + g];
+  auto load = [&](SkinnyStage<MT, R>& st, int64_t g) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t nr = n[r];
+      if (g32) {
+        // words 0-3 of lane half h: group 4g + h; words 4-7: group 4g + 2 + h
+        st.zb[r] = (uint32_t)zeros[nr * zbytes + 2 * g] | ((uint32_t)zeros[nr * zbytes + 2 * g + 1] << 8);
+        st.sc[r][0] = scales[nr * Gs + 4 * g + h];
+        st.sc[r][1] = scales[nr * Gs + 4 * g + 2 + h];
+      } else if (g64) {
+        st.zb[r] = zeros[nr * zbytes + g];  // groups 2g (low nibble) and 2g + 1 (high)
+        st.sc[r][0] = scales[nr * Gs + 2 * g];
+        st.sc[r][1] = scales[nr * Gs + 2 * g + 1];
+      } else {
+        st.zb[r] = zeros[nr * zbytes + (g >> 1)];
+        st.sc[r][0] = st.sc[r][1] = scales[nr * Gs + g];
+      }
+      const uint32_t* cp = qweight + nr * words + g * 16 + h * 4;
+      st.b[r][0] = *reinterpret_cast<const uint4*>(cp);
+      st.b[r][1] = *reinterpret_cast<const uint4*>(cp + 8);
     }
-    const uint32_t* cp = qweight + n * words + g * 16 + h * 4;
-    st.b[0] = *reinterpret_cast<const uint4*>(cp);
-    st.b[1] = *reinterpret_cast<const uint4*>(cp + 8);
     // word s (k16 step s) covers channels 8 s' + 32 h + 64 (s / 4), s' = s % 4
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
@@ -125,24 +137,30 @@ __global__ void __launch_bounds__(S * 64)
     }
   };
 
-  float acc[MT][E];
+  float acc[R][MT][E];
 #pragma unroll
-  for (int t = 0; t < MT; ++t)
+  for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[t][e] = 0.0f;
-  auto mfma = [&](const SkinnyStage<MT>& st, int s, half8 b, f32x16 (&d)[MT]) {
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[r][t][e] = 0.0f;
+  auto mfma = [&](const SkinnyStage<MT, R>& st, int s, half8 b, f32x16 (&d)[MT]) {
 #pragma unroll
     for (int t = 0; t < MT; ++t)
       d[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, st.a[t][s]), b, d[t], 0, 0, 0);
   };
 
-  f32x16 acc2[MT];  // MT = 2: the two token tiles, accumulated by the MFMAs themselves
+  f32x16 acc2[R][MT];  // MT = 2: the two token tiles, accumulated by the MFMAs themselves
 #pragma unroll
-  for (int t = 0; t < MT; ++t) acc2[t] = f32x16{};
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc2[r][t] = f32x16{};
 
-  auto body = [&](const SkinnyStage<MT>& st, int64_t g) {
-    const uint32_t wd[8] = {st.b[0].x, st.b[0].y, st.b[0].z, st.b[0].w,
-                            st.b[1].x, st.b[1].y, st.b[1].z, st.b[1].w};
+  auto body = [&](const SkinnyStage<MT, R>& st, int64_t g) {
+#pragma unroll
+   for (int r = 0; r < R; ++r) {
+    const uint32_t wd[8] = {st.b[r][0].x, st.b[r][0].y, st.b[r][0].z, st.b[r][0].w,
+                            st.b[r][1].x, st.b[r][1].y, st.b[r][1].z, st.b[r][1].w};
     auto zz_of = [](uint32_t z) {
       const uint32_t zbits = 0x6400u + z;
       return -__builtin_bit_cast(half2v, zbits | (zbits << 16));
@@ -152,14 +170,14 @@ __global__ void __launch_bounds__(S * 64)
       // step's group; 64: groups 2g, 2g + 1; 32: groups 4g + h, 4g + 2 + h)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const uint32_t z = g32 ? (st.zb >> (8 * half + 4 * h)) & 0xF
-                           : g64 ? (st.zb >> (4 * half)) & 0xF
-                                 : ((g & 1) ? (st.zb >> 4) & 0xF : st.zb & 0xF);
+        const uint32_t z = g32 ? (st.zb[r] >> (8 * half + 4 * h)) & 0xF
+                           : g64 ? (st.zb[r] >> (4 * half)) & 0xF
+                                 : ((g & 1) ? (st.zb[r] >> 4) & 0xF : st.zb[r] & 0xF);
         const half2v zz = zz_of(z);
-        const half2v s2 = __builtin_bit_cast(half2v, st.sc[half] | (st.sc[half] << 16));
+        const half2v s2 = __builtin_bit_cast(half2v, st.sc[r][half] | (st.sc[r][half] << 16));
 #pragma unroll
         for (int s = 4 * half; s < 4 * half + 4; ++s)
-          mfma(st, s, widen_word(wd[s], zz, magic) * half8{s2[0], s2[1], s2[0], s2[1], s2[0], s2[1], s2[0], s2[1]}, acc2);
+          mfma(st, s, widen_word(wd[s], zz, magic) * half8{s2[0], s2[1], s2[0], s2[1], s2[0], s2[1], s2[0], s2[1]}, acc2[r]);
       }
     } else if (g32) {
       f32x16 d[MT];
@@ -167,8 +185,8 @@ __global__ void __launch_bounds__(S * 64)
       for (int t = 0; t < MT; ++t) d[t] = f32x16{};
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const half2v zz = zz_of((st.zb >> (8 * half + 4 * h)) & 0xF);
-        const half2v s2 = __builtin_bit_cast(half2v, st.sc[half] | (st.sc[half] << 16));
+        const half2v zz = zz_of((st.zb[r] >> (8 * half + 4 * h)) & 0xF);
+        const half2v s2 = __builtin_bit_cast(half2v, st.sc[r][half] | (st.sc[r][half] << 16));
 #pragma unroll
         for (int s = 4 * half; s < 4 * half + 4; ++s)
           mfma(st, s, widen_word(wd[s], zz, magic) * half8{s2[0], s2[1], s2[0], s2[1], s2[0], s2[1], s2[0], s2[1]}, d);
@@ -176,39 +194,40 @@ __global__ void __launch_bounds__(S * 64)
 #pragma unroll
       for (int t = 0; t < MT; ++t)
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[t][e] += d[t][e];
+        for (int e = 0; e < E; ++e) acc[r][t][e] += d[t][e];
     } else if (g64) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const half2v zz = zz_of((st.zb >> (4 * half)) & 0xF);
+        const half2v zz = zz_of((st.zb[r] >> (4 * half)) & 0xF);
         f32x16 d[MT];
 #pragma unroll
         for (int t = 0; t < MT; ++t) d[t] = f32x16{};
 #pragma unroll
         for (int s = 4 * half; s < 4 * half + 4; ++s) mfma(st, s, widen_word(wd[s], zz, magic), d);
-        const float scf = h2f((uint16_t)st.sc[half]);
+        const float scf = h2f((uint16_t)st.sc[r][half]);
 #pragma unroll
         for (int t = 0; t < MT; ++t)
 #pragma unroll
-          for (int e = 0; e < E; ++e) acc[t][e] = __builtin_fmaf(scf, d[t][e], acc[t][e]);
+          for (int e = 0; e < E; ++e) acc[r][t][e] = __builtin_fmaf(scf, d[t][e], acc[r][t][e]);
       }
     } else {
-      const half2v zz = zz_of((g & 1) ? (st.zb >> 4) & 0xF : st.zb & 0xF);
+      const half2v zz = zz_of((g & 1) ? (st.zb[r] >> 4) & 0xF : st.zb[r] & 0xF);
       f32x16 d[MT];
 #pragma unroll
       for (int t = 0; t < MT; ++t) d[t] = f32x16{};
 #pragma unroll
       for (int s = 0; s < 8; ++s) mfma(st, s, widen_word(wd[s], zz, magic), d);
-      const float scf = h2f((uint16_t)st.sc[0]);
+      const float scf = h2f((uint16_t)st.sc[r][0]);
 #pragma unroll
       for (int t = 0; t < MT; ++t)
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[t][e] = __builtin_fmaf(scf, d[t][e], acc[t][e]);
+        for (int e = 0; e < E; ++e) acc[r][t][e] = __builtin_fmaf(scf, d[t][e], acc[r][t][e]);
     }
+   }
   };
 
   if (g1 > g0) {
-    SkinnyStage<MT> s0, s1;
+    SkinnyStage<MT, R> s0, s1;
     load(s0, g0);
     int64_t g = g0;
     for (; g + 2 <= g1; g += 2) {
@@ -222,71 +241,96 @@ __global__ void __launch_bounds__(S * 64)
 
   if constexpr (MT == 2) {
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[t][e] = acc2[t][e];
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[r][t][e] = acc2[r][t][e];
   }
   // fixed-order reduction of the S partial tiles
 #pragma unroll
-  for (int t = 0; t < MT; ++t)
+  for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int e = 0; e < E; ++e) red[wave][t * E + e][lane] = acc[t][e];
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int e = 0; e < E; ++e) red[wave][(r * MT + t) * E + e][lane] = acc[r][t][e];
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
-  for (int t = 0; t < MT; ++t)
+  for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      float v = red[0][t * E + e][lane];
+    for (int t = 0; t < MT; ++t)
 #pragma unroll
-      for (int w = 1; w < S; ++w) v += red[w][t * E + e][lane];
-      acc[t][e] = v;
-    }
+      for (int e = 0; e < E; ++e) {
+        float v = red[0][(r * MT + t) * E + e][lane];
+#pragma unroll
+        for (int w = 1; w < S; ++w) v += red[w][(r * MT + t) * E + e][lane];
+        acc[r][t][e] = v;
+      }
   // 32x32 accumulator layout: element e of lane l is (row 8(e/4) + 4(l/32) + e%4, col l%32)
   if constexpr (GATED) {
     // up partner of column j (< 16) is column j + 16, held by lane + 16 for the same rows
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const float u = __shfl_down(acc[t][e], 16, 32);
-        const int64_t o = (int64_t)blockIdx.x * 16 + j;
-        const int64_t i = 32 * t + 8 * (e >> 2) + 4 * h + (e & 3);
-        if (j < 16 && o < nh && i < M) Y[i * nh + o] = f2h_bits(silu_f32(acc[t][e]) * u);
-      }
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float u = __shfl_down(acc[r][t][e], 16, 32);
+          const int64_t o = ((int64_t)blockIdx.x * R + r) * 16 + j;
+          const int64_t i = 32 * t + 8 * (e >> 2) + 4 * h + (e & 3);
+          if (j < 16 && o < nh && i < M) Y[i * nh + o] = f2h_bits(silu_f32(acc[r][t][e]) * u);
+        }
   } else {
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int64_t o = (int64_t)blockIdx.x * 32 + j;
-        const int64_t i = 32 * t + 8 * (e >> 2) + 4 * h + (e & 3);
-        if (o < N && i < M) Y[i * N + o] = f2h_bits(acc[t][e]);
-      }
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int64_t o = ((int64_t)blockIdx.x * R + r) * 32 + j;
+          const int64_t i = 32 * t + 8 * (e >> 2) + 4 * h + (e & 3);
+          if (o < N && i < M) Y[i * N + o] = f2h_bits(acc[r][t][e]);
+        }
   }
 }
 
-template <int S, int E, int MT, bool GATED>
+template <int S, int E, int MT, int R, bool GATED>
 static hipError_t launch_skinny_x(const uint16_t* X, int64_t M, const uint32_t* qw,
                                   const uint16_t* sc, const uint8_t* z, int64_t N, int64_t K,
                                   int group, uint16_t* Y, hipStream_t stream) {
   const int64_t outs = GATED ? N / 2 : N;
-  const int64_t per = GATED ? 16 : 32;
+  const int64_t per = (GATED ? 16 : 32) * R;
   const int64_t blocks = (outs + per - 1) / per;
-  hipLaunchKernelGGL((k_gemv_mfma<S, E, MT, GATED>), dim3((unsigned)blocks), dim3(S * 64), 0, stream,
+  hipLaunchKernelGGL((k_gemv_mfma<S, E, MT, R, GATED>), dim3((unsigned)blocks), dim3(S * 64), 0, stream,
                      X, M, qw, sc, z, N, K, group, Y);
   return hipGetLastError();
 }
 
+template <int R, bool GATED>
+static hipError_t launch_skinny_r(const uint16_t* X, int64_t M, const uint32_t* qw,
+                                  const uint16_t* sc, const uint8_t* z, int64_t N, int64_t K,
+                                  int group, uint16_t* Y, hipStream_t stream) {
+  if (M <= 8) return launch_skinny_x<8, 4, 1, R, GATED>(X, M, qw, sc, z, N, K, group, Y, stream);
+  if (M <= 16) return launch_skinny_x<8, 8, 1, R, GATED>(X, M, qw, sc, z, N, K, group, Y, stream);
+  if (M <= 32) return launch_skinny_x<8, 16, 1, R, GATED>(X, M, qw, sc, z, N, K, group, Y, stream);
+  // two token tiles: 4 waves per block, so a wave may also use the accumulation registers
+  return launch_skinny_x<4, 16, 2, R, GATED>(X, M, qw, sc, z, N, K, group, Y, stream);
+}
+
+// Two row tiles per wave halve the activation bytes loaded per weight byte but also halve
+// the blocks; measured on the Llama-2 7B and 70B shapes it pays from 160 blocks of two
+// tiles (7B q|k|v: +25% at M = 8..32; 70B gate|up: +14..20%), and loses below (7B o_proj
+// and down_proj, 64 blocks: -30%); fused gate|up needs more (7B, 344 blocks: -4% at M = 64).
 template <bool GATED>
 static hipError_t launch_skinny_t(const uint16_t* X, int64_t M, const uint32_t* qw,
                                   const uint16_t* sc, const uint8_t* z, int64_t N, int64_t K,
                                   int group, uint16_t* Y, hipStream_t stream) {
-  if (M <= 8) return launch_skinny_x<8, 4, 1, GATED>(X, M, qw, sc, z, N, K, group, Y, stream);
-  if (M <= 16) return launch_skinny_x<8, 8, 1, GATED>(X, M, qw, sc, z, N, K, group, Y, stream);
-  if (M <= 32) return launch_skinny_x<8, 16, 1, GATED>(X, M, qw, sc, z, N, K, group, Y, stream);
-  // two token tiles: 4 waves per block, so a wave may also use the accumulation registers
-  return launch_skinny_x<4, 16, 2, GATED>(X, M, qw, sc, z, N, K, group, Y, stream);
+  const int64_t outs = GATED ? N / 2 : N;
+  const int64_t blocks2 = (outs + (GATED ? 32 : 64) - 1) / (GATED ? 32 : 64);
+  if (blocks2 >= (GATED ? kSkinnyR2MinBlocksGated : kSkinnyR2MinBlocks))
+    return launch_skinny_r<2, GATED>(X, M, qw, sc, z, N, K, group, Y, stream);
+  return launch_skinny_r<1, GATED>(X, M, qw, sc, z, N, K, group, Y, stream);
 }
 
 hipError_t launch_gemv_mfma(const uint16_t* X, int64_t M, const uint32_t* qweight,
