@@ -152,6 +152,7 @@ __device__ __forceinline__ void rint_quotients(const float (&w)[NV], float scf, 
     q[i] = qa;
   }
   if (__builtin_amdgcn_ballot_w64(any)) {
+    asm volatile("");  // keeps the division in this branch (not speculated into the common path)
 #pragma unroll
     for (int i = 0; i < NV; ++i)
       if (close[i]) q[i] = w[i] / scf;  // correctly rounded division
@@ -175,7 +176,7 @@ __device__ __forceinline__ GroupQ group_params(float mn, float mx, float qmax) {
   const float nmn[1] = {-mn};
   float zq[1];
   rint_quotients(nmn, g.scf, g.rcp, zq);
-  g.z = fminf(fmaxf(zq[0], 0.0f), qmax);
+  g.z = __builtin_amdgcn_fmed3f(zq[0], 0.0f, qmax);  // clamp to [0, qmax]
   return g;
 }
 
@@ -230,7 +231,37 @@ __device__ __forceinline__ void quant_codes(const float (&w)[NV], const GroupQ& 
       if (close[i]) q[i] = __builtin_rintf(w[i] / g.scf);  // correctly rounded division
   }
 #pragma unroll
-  for (int i = 0; i < NV; ++i) q[i] = fminf(fmaxf(q[i] + g.z, 0.0f), g.qmax);
+  for (int i = 0; i < NV; ++i) q[i] = __builtin_amdgcn_fmed3f(q[i] + g.z, 0.0f, g.qmax);  // clamp
+}
+
+// The centered codes q - z of quant_codes, formed directly as clamp(rint(w / sc_h), -z,
+// qmax - z): small integers, so the same values as clamping rint(w / sc_h) + z to [0, qmax]
+// and subtracting z. For the searches, which only need (q - z) sc_h. The guess is kept on
+// the same exact-residual test; here a large guess (|q0| >= 2^12, only in groups whose scale
+// is floored) whose residual fails it also takes the division, which changes no result.
+template <int NV>
+__device__ __forceinline__ void quant_centered(const float (&w)[NV], const GroupQ& g,
+                                               float (&qz)[NV]) {
+#pragma clang fp contract(off)
+  const float half_sc = 0.5f * g.scf;  // exact
+  bool close[NV];
+  bool any = false;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    qz[i] = __builtin_rintf(w[i] * g.rcp);
+    const float e = __builtin_fmaf(-qz[i], g.scf, w[i]);
+    close[i] = !(__builtin_fabsf(e) < half_sc);
+    any |= close[i];
+  }
+  if (__builtin_amdgcn_ballot_w64(any)) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (close[i]) qz[i] = __builtin_rintf(w[i] / g.scf);  // correctly rounded division
+  }
+  const float lo = -g.z, hi = g.qmax - g.z;  // exact
+  // the clamp as a median of three (one instruction, the same value for every input)
+#pragma unroll
+  for (int i = 0; i < NV; ++i) qz[i] = __builtin_amdgcn_fmed3f(qz[i], lo, hi);
 }
 
 // The packed word of 8 codes of channels 8w .. 8w + 7 (channel i in nibble kNibbleOf[i]):

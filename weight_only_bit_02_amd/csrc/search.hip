@@ -103,9 +103,120 @@ constexpr int quant_passes() {
   return NROWS / (NW * 4);
 }
 
-// Search (CLIP = false): the scale of each (row, step) comes from the row's exponent state
-// e_state[pass] (search_exponent), and its exponent E is written to pe_out[row]. Clip
-// search: each group's own largest |D| sets its P, written to pg_out[row * 4 + group].
+// The scales of a lane's 8 channels of one 128-channel step (fp32) and their hardware
+// reciprocals (1 ulp); s == nullptr (clip search without s): s = 1.
+struct StepScales {
+  float sf[8], rs[8];
+};
+
+template <bool CLIP>
+__device__ __forceinline__ StepScales step_scales(const uint16_t* s, int64_t k0) {
+  uint4 sv = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);  // s = 1
+  if (!CLIP || s) sv = *reinterpret_cast<const uint4*>(s + k0);
+  StepScales sc;
+  const uint32_t sd[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sc.sf[2 * i] = h2f((uint16_t)(sd[i] & 0xFFFF));
+    sc.sf[2 * i + 1] = h2f((uint16_t)(sd[i] >> 16));
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sc.rs[i] = __builtin_amdgcn_rcpf(sc.sf[i]);
+  return sc;
+}
+
+// One row's 8 weights wv of a lane (16 lanes per (row, 128 channels)) -> (D P) split into
+// fp16 hi + lo at hi_buf / lo_buf[row * kLdsStride + li * 8]; returns whether a non-finite
+// value was met. Search (CLIP = false): the scale of each (row, step) comes from the row's
+// exponent state e_state (search_exponent), and its exponent E is written to pe_out[row].
+// Clip search: each group's own largest |D| sets its P, written to pg_out[row * 4 + group].
+template <bool CLIP>
+__device__ __forceinline__ bool quantize_row(uint4 wv, const StepScales& sc, float r, bool sym,
+                                             int group, float qmax, int& e_state, int* pe_out,
+                                             uint16_t* hi_buf, uint16_t* lo_buf, int row, int li,
+                                             float* pg_out) {
+  const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
+  float wp[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    wp[2 * i] = h2f((uint16_t)(wd[i] & 0xFFFF)) * sc.sf[2 * i];
+    wp[2 * i + 1] = h2f((uint16_t)(wd[i] >> 16)) * sc.sf[2 * i + 1];
+  }
+  float mn = wp[0], mx = wp[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) {
+    mn = fminf(mn, wp[i]);
+    mx = fmaxf(mx, wp[i]);
+  }
+  group_minmax(mn, mx, group);  // 16 lanes = one 128-channel group, two of 64, four of 32
+  const bool bad = !__builtin_isfinite(mn) || !__builtin_isfinite(mx);
+  if (CLIP) {
+    mn = r * mn;
+    mx = r * mx;
+  }
+  const GroupQ g = sym ? group_params_sym(mn, mx, qmax) : group_params(mn, mx, qmax);
+  float qz[8];
+  quant_centered(wp, g, qz);
+  // D = (w' - deq) / s: w' = w s and deq = (q - z) sc_h are exact, and so is their
+  // difference (both are multiples of the finer ulp and close in magnitude), so the
+  // reciprocal's error (1 ulp) is relative to D itself; w - deq / s would carry it
+  // relative to w, which is 30 (4-bit) to 500 (8-bit) times larger than D
+  float dg[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const float deq = qz[c] * g.scf;  // exact: small integer times an fp16
+    dg[c] = (wp[c] - deq) * sc.rs[c];
+  }
+  float P;
+  if constexpr (CLIP) {
+    // each group is scored on its own, so its scale comes from its own largest |D|:
+    // P = 2^(14 - e) with that maximum in [2^(e-1), 2^e), so |D P| < 2^14 and hi + lo
+    // keep 22 significant bits of every group, whatever the code width
+    float dmx = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) dmx = fmaxf(dmx, __builtin_fabsf(dg[c]));
+    float dmn = dmx;
+    group_minmax(dmn, dmx, group);
+    int ex = 0;
+    (void)__builtin_frexpf(dmx, &ex);
+    if (!(dmx > 0.0f) || !__builtin_isfinite(dmx)) ex = 0;
+    ex = ex < -100 ? -100 : (ex > 100 ? 100 : ex);
+    P = __builtin_ldexpf(1.0f, 14 - ex);
+    const int gl = group >> 3;  // lanes per group
+    if ((li & (gl - 1)) == 0) pg_out[row * 4 + li / gl] = P;
+  } else {
+    // the (row, step) scale: the largest |D| over the step's 128 channels (16 lanes)
+    float dmx = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) dmx = fmaxf(dmx, __builtin_fabsf(dg[c]));
+    float dmn = dmx;
+    row16_minmax(dmn, dmx);
+    const int E = search_exponent(dmx, e_state);
+    e_state = E;
+    P = __builtin_ldexpf(1.0f, 14 - E);
+    if (li == 0) pe_out[row] = E;
+  }
+  uint32_t hi[4], lo[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint16_t h2[2], l2[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int c = 2 * i + e;
+      const float d = dg[c] * P;
+      h2[e] = f2h_bits(d);
+      l2[e] = f2h_bits(d - h2f(h2[e]));
+    }
+    hi[i] = (uint32_t)h2[0] | ((uint32_t)h2[1] << 16);
+    lo[i] = (uint32_t)l2[0] | ((uint32_t)l2[1] << 16);
+  }
+  *reinterpret_cast<uint4*>(&hi_buf[row * kLdsStride + li * 8]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+  *reinterpret_cast<uint4*>(&lo_buf[row * kLdsStride + li * 8]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+  return bad;
+}
+
+// Quantizes step j of rows [row_base, row_base + NROWS) of the tile with NW waves (tid
+// counts their threads from 0), 4 rows per wave per pass.
 template <int NW, bool CLIP, int NROWS>
 __device__ __forceinline__ bool quantize_tile_group(const uint16_t* W, int64_t N, int64_t K,
                                                     const uint16_t* s, float r, bool sym,
@@ -130,105 +241,14 @@ __device__ __forceinline__ bool quantize_tile_group(const uint16_t* W, int64_t N
     wvs[p] = *reinterpret_cast<const uint4*>(W + (n < N ? n : N - 1) * K + k0);
   }
   // the thread's 8 channels are the same in every pass: s and 1/s once
-  uint4 sv = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);  // s = 1
-  if (!CLIP || s) sv = *reinterpret_cast<const uint4*>(s + k0);
-  float sf[8], rs[8];
-  {
-    const uint32_t sd[4] = {sv.x, sv.y, sv.z, sv.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sf[2 * i] = h2f((uint16_t)(sd[i] & 0xFFFF));
-      sf[2 * i + 1] = h2f((uint16_t)(sd[i] >> 16));
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) rs[i] = __builtin_amdgcn_rcpf(sf[i]);
-  }
+  const StepScales sc = step_scales<CLIP>(s, k0);
   bool bad = false;
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) {
     const int row = p * kRowsPerPass + q_row;
-    const int64_t n = n0 + row;
-    uint4 wv = wvs[p];
-    if (n >= N) wv = make_uint4(0, 0, 0, 0);
-    const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
-    float wf[8], wp[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      wf[2 * i] = h2f((uint16_t)(wd[i] & 0xFFFF));
-      wf[2 * i + 1] = h2f((uint16_t)(wd[i] >> 16));
-      wp[2 * i] = wf[2 * i] * sf[2 * i];
-      wp[2 * i + 1] = wf[2 * i + 1] * sf[2 * i + 1];
-    }
-    float mn = wp[0], mx = wp[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) {
-      mn = fminf(mn, wp[i]);
-      mx = fmaxf(mx, wp[i]);
-    }
-    group_minmax(mn, mx, group);  // 16 lanes = one 128-channel group, two of 64, four of 32
-    bad |= !__builtin_isfinite(mn) || !__builtin_isfinite(mx);
-    if (CLIP) {
-      mn = r * mn;
-      mx = r * mx;
-    }
-    const GroupQ g = sym ? group_params_sym(mn, mx, qmax) : group_params(mn, mx, qmax);
-    float qc[8];
-    quant_codes(wp, g, qc);
-    // D = (w' - deq) / s: w' = w s and deq = (q - z) sc_h are exact, and so is their
-    // difference (both are multiples of the finer ulp and close in magnitude), so the
-    // reciprocal's error (1 ulp) is relative to D itself; w - deq / s would carry it
-    // relative to w, which is 30 (4-bit) to 500 (8-bit) times larger than D
-    float dg[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const float deq = (qc[c] - g.z) * g.scf;  // exact: small integer times an fp16
-      dg[c] = (wp[c] - deq) * rs[c];
-    }
-    float P;
-    if constexpr (CLIP) {
-      // each group is scored on its own, so its scale comes from its own largest |D|:
-      // P = 2^(14 - e) with that maximum in [2^(e-1), 2^e), so |D P| < 2^14 and hi + lo
-      // keep 22 significant bits of every group, whatever the code width
-      float dmx = 0.0f;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) dmx = fmaxf(dmx, __builtin_fabsf(dg[c]));
-      float dmn = dmx;
-      group_minmax(dmn, dmx, group);
-      int ex = 0;
-      (void)__builtin_frexpf(dmx, &ex);
-      if (!(dmx > 0.0f) || !__builtin_isfinite(dmx)) ex = 0;
-      ex = ex < -100 ? -100 : (ex > 100 ? 100 : ex);
-      P = __builtin_ldexpf(1.0f, 14 - ex);
-      const int gl = group >> 3;  // lanes per group
-      if ((li & (gl - 1)) == 0) pg_out[row * 4 + li / gl] = P;
-    } else {
-      // the (row, step) scale: the largest |D| over the step's 128 channels (16 lanes)
-      float dmx = 0.0f;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) dmx = fmaxf(dmx, __builtin_fabsf(dg[c]));
-      float dmn = dmx;
-      row16_minmax(dmn, dmx);
-      const int E = search_exponent(dmx, e_state[p]);
-      e_state[p] = E;
-      P = __builtin_ldexpf(1.0f, 14 - E);
-      if (li == 0) pe_out[row] = E;
-    }
-    uint32_t hi[4], lo[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint16_t h2[2], l2[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int c = 2 * i + e;
-        const float d = dg[c] * P;
-        h2[e] = f2h_bits(d);
-        l2[e] = f2h_bits(d - h2f(h2[e]));
-      }
-      hi[i] = (uint32_t)h2[0] | ((uint32_t)h2[1] << 16);
-      lo[i] = (uint32_t)l2[0] | ((uint32_t)l2[1] << 16);
-    }
-    *reinterpret_cast<uint4*>(&hi_buf[row * kLdsStride + li * 8]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-    *reinterpret_cast<uint4*>(&lo_buf[row * kLdsStride + li * 8]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    const uint4 wv = n0 + row < N ? wvs[p] : make_uint4(0, 0, 0, 0);
+    bad |= quantize_row<CLIP>(wv, sc, r, sym, group, qmax, e_state[p], pe_out, hi_buf, lo_buf,
+                              row, li, pg_out);
   }
   return bad;
 }
@@ -345,14 +365,13 @@ __global__ void __launch_bounds__(NW * 64)
     __syncthreads();
     for (int64_t j = 0; j < G; ++j) {
       const int buf = (int)(j & 1);
-      // next group's quantization (unconditional, clamped: the last one is redundant and
-      // lands in the buffer nobody reads)
-      const int64_t jn = j + 1 < G ? j + 1 : G - 1;
+      // the next step's quantization (none after the last step: block-uniform)
+      const bool more = j + 1 < G;
       if (!set_b) {
         multiply(j, buf);
-        quantize(jn, buf ^ 1);
+        if (more) quantize(j + 1, buf ^ 1);
       } else {
-        quantize(jn, buf ^ 1);
+        if (more) quantize(j + 1, buf ^ 1);
         multiply(j, buf);
       }
       __syncthreads();
@@ -440,8 +459,8 @@ __global__ void __launch_bounds__(NW * 64)
   __syncthreads();
   for (int64_t j = 0; j < G; ++j) {
     const int buf = (int)(j & 1);
-    const int64_t jn = j + 1 < G ? j + 1 : G - 1;
-    if (set_b) quantize(jn, buf ^ 1);
+    const bool more = j + 1 < G;  // the next step's quantization (none after the last step)
+    if (set_b && more) quantize(j + 1, buf ^ 1);
     f32x16 acc[2][4];
     // the step's 8 k16 slices in quarters of two; a group spans per = 8, 4 or 2 slices and
     // its error is taken when its last slice is done
@@ -506,7 +525,7 @@ __global__ void __launch_bounds__(NW * 64)
         }
       }
     }
-    if (!set_b) quantize(jn, buf ^ 1);
+    if (!set_b && more) quantize(j + 1, buf ^ 1);
     // end of step: the next one reads the buffer just written (by both sets) and, with one
     // group per step, this step's errors are complete in their slot
     __syncthreads();
