@@ -63,6 +63,22 @@ AWQ_DPP_MINMAX(minmax_row_ror8, "row_ror:8")
 AWQ_DPP_MINMAX(minmax_row_half_mirror, "row_half_mirror")
 #undef AWQ_DPP_MINMAX
 
+// max only (the reductions of a nonnegative largest |D|): one DPP-modified instruction
+#define AWQ_DPP_MAX(NAME, CTRL)                                                           \
+  __device__ __forceinline__ void NAME(float& mx) {                                       \
+    float b;                                                                              \
+    asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 " CTRL " row_mask:0xf bank_mask:0xf"         \
+        : "=&v"(b)                                                                        \
+        : "v"(mx));                                                                       \
+    mx = b;                                                                               \
+  }
+AWQ_DPP_MAX(max_quad_xor1, "quad_perm:[1,0,3,2]")
+AWQ_DPP_MAX(max_quad_xor2, "quad_perm:[2,3,0,1]")
+AWQ_DPP_MAX(max_row_ror4, "row_ror:4")
+AWQ_DPP_MAX(max_row_ror8, "row_ror:8")
+AWQ_DPP_MAX(max_row_half_mirror, "row_half_mirror")
+#undef AWQ_DPP_MAX
+
 // Min / max over each 16-lane DPP row (128-channel groups): quad butterflies, then row
 // rotations; every lane of the row ends up with the result.
 __device__ __forceinline__ void row16_minmax(float& mn, float& mx) {
@@ -92,6 +108,24 @@ __device__ __forceinline__ void group_minmax(float& mn, float& mx, int group) {
   if (group == 128) row16_minmax(mn, mx);
   else if (group == 64) row8_minmax(mn, mx);
   else quad_minmax(mn, mx);
+}
+
+// Max over each 16-lane row / each group of g / 8 adjacent lanes, as group_minmax.
+__device__ __forceinline__ void row16_max(float& mx) {
+  max_quad_xor1(mx);
+  max_quad_xor2(mx);
+  max_row_ror4(mx);
+  max_row_ror8(mx);
+}
+__device__ __forceinline__ void group_max(float& mx, int group) {
+  max_quad_xor1(mx);
+  max_quad_xor2(mx);
+  if (group == 128) {
+    max_row_ror4(mx);
+    max_row_ror8(mx);
+  } else if (group == 64) {
+    max_row_half_mirror(mx);
+  }
 }
 
 __device__ __forceinline__ float row16_sum(float v) {
@@ -161,12 +195,38 @@ __device__ __forceinline__ void rint_quotients(const float (&w)[NV], float scf, 
   for (int i = 0; i < NV; ++i) q[i] = __builtin_rintf(q[i]);
 }
 
-// Asymmetric group parameters for codes 0..qmax (qmax = 2^w_bit - 1).
-__device__ __forceinline__ GroupQ group_params(float mn, float mx, float qmax) {
+// x / d correctly rounded, for the divisors of the group scales (d = 3, 7, 15, 127, 255),
+// given y = RN(1 / d): q0 = RN(x y), the residual r = x - q0 d exactly (one fma), then
+// RN(q0 + r y) (one fma), Markstein's correction. For these five divisors it equals the
+// IEEE quotient for every fp32 significand (checked exhaustively: the test of the
+// division method); scaling by a power of two commutes with it while r stays normal, and
+// below that the quotient is far under the 2^-14 floor the scales take. Non-finite x: x y
+// (Inf or NaN, as the division gives). Three instructions and a select instead of the
+// division's ten.
+__device__ __forceinline__ float div_small(float x, float d, float y) {
+#pragma clang fp contract(off)
+  const float q0 = x * y;
+  const float r = __builtin_fmaf(-q0, d, x);
+  const float q1 = __builtin_fmaf(r, y, q0);
+  return __builtin_isfinite(x) ? q1 : q0;
+}
+
+// The divisor of the group scale and its correctly rounded reciprocal: qmax for asymmetric
+// codes, h - 1 = (qmax - 1) / 2 for symmetric ones. Uniform: computed once per kernel.
+struct ScaleDiv {
+  float d, y;
+};
+__device__ __forceinline__ ScaleDiv scale_divisor(float qmax, bool sym) {
+  const float d = sym ? 0.5f * (qmax + 1.0f) - 1.0f : qmax;  // exact
+  return ScaleDiv{d, 1.0f / d};                               // correctly rounded
+}
+
+// Asymmetric group parameters for codes 0..qmax (qmax = 2^w_bit - 1); sd = scale_divisor(qmax, false).
+__device__ __forceinline__ GroupQ group_params(float mn, float mx, float qmax, ScaleDiv sd) {
 #pragma clang fp contract(off)
   GroupQ g;
   g.qmax = qmax;
-  float sc = (mx - mn) / qmax;  // correctly rounded division (no fast-math)
+  float sc = div_small(mx - mn, sd.d, sd.y);  // the correctly rounded (mx - mn) / qmax
   sc = fmaxf(sc, 0x1p-14f);
   g.clamped = sc > 65504.0f;
   sc = fminf(sc, 65504.0f);
@@ -184,12 +244,13 @@ __device__ __forceinline__ GroupQ group_params(float mn, float mx, float qmax) {
 // and clamp, and the fixed zero h = 2^(w_bit - 1) (8 or 128), so q - h = clamp(rint(w /
 // sc_h), -h, h - 1) is the signed code and the stored format (and its dequantization
 // (q - z) sc) is unchanged.
-__device__ __forceinline__ GroupQ group_params_sym(float mn, float mx, float qmax) {
+// sd = scale_divisor(qmax, true).
+__device__ __forceinline__ GroupQ group_params_sym(float mn, float mx, float qmax, ScaleDiv sd) {
 #pragma clang fp contract(off)
   GroupQ g;
   g.qmax = qmax;
   const float h = 0.5f * (qmax + 1.0f);  // exact
-  float sc = fmaxf(__builtin_fabsf(mx), __builtin_fabsf(mn)) / (h - 1.0f);
+  float sc = div_small(fmaxf(__builtin_fabsf(mx), __builtin_fabsf(mn)), sd.d, sd.y);  // / (h - 1)
   sc = fmaxf(sc, 0x1p-14f);
   g.clamped = sc > 65504.0f;
   sc = fminf(sc, 65504.0f);

@@ -39,6 +39,7 @@ __global__ void __launch_bounds__(256) k_quant_pack(const uint16_t* __restrict__
   const int64_t chunks = (G + gpu - 1) / gpu;
   const bool w8 = w_bit == 8, w3 = w_bit == 3;
   const float qmax = (float)((1 << w_bit) - 1);
+  const ScaleDiv sdiv = scale_divisor(qmax, sym);
   const int64_t words = K * w_bit / 32;  // packed words per row
   const int64_t zbytes = w8 ? G : (G + 1) / 2;  // 8-bit: one zero byte per group
   // unit u = (row n, chunk ch) = n * chunks + ch; the wave walks u = wave0, wave0 + nwaves,
@@ -86,7 +87,7 @@ __global__ void __launch_bounds__(256) k_quant_pack(const uint16_t* __restrict__
       mn = r * mn;
       mx = r * mx;
     }
-    const GroupQ g = sym ? group_params_sym(mn, mx, qmax) : group_params(mn, mx, qmax);
+    const GroupQ g = sym ? group_params_sym(mn, mx, qmax, sdiv) : group_params(mn, mx, qmax, sdiv);
     float qc[8];
     quant_codes(w, g, qc);
 

@@ -132,9 +132,9 @@ __device__ __forceinline__ StepScales step_scales(const uint16_t* s, int64_t k0)
 // Clip search: each group's own largest |D| sets its P, written to pg_out[row * 4 + group].
 template <bool CLIP>
 __device__ __forceinline__ bool quantize_row(uint4 wv, const StepScales& sc, float r, bool sym,
-                                             int group, float qmax, int& e_state, int* pe_out,
-                                             uint16_t* hi_buf, uint16_t* lo_buf, int row, int li,
-                                             float* pg_out) {
+                                             int group, float qmax, ScaleDiv sd, int& e_state,
+                                             int* pe_out, uint16_t* hi_buf, uint16_t* lo_buf,
+                                             int row, int li, float* pg_out) {
   const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
   float wp[8];
 #pragma unroll
@@ -154,7 +154,7 @@ __device__ __forceinline__ bool quantize_row(uint4 wv, const StepScales& sc, flo
     mn = r * mn;
     mx = r * mx;
   }
-  const GroupQ g = sym ? group_params_sym(mn, mx, qmax) : group_params(mn, mx, qmax);
+  const GroupQ g = sym ? group_params_sym(mn, mx, qmax, sd) : group_params(mn, mx, qmax, sd);
   float qz[8];
   quant_centered(wp, g, qz);
   // D = (w' - deq) / s: w' = w s and deq = (q - z) sc_h are exact, and so is their
@@ -175,8 +175,7 @@ __device__ __forceinline__ bool quantize_row(uint4 wv, const StepScales& sc, flo
     float dmx = 0.0f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) dmx = fmaxf(dmx, __builtin_fabsf(dg[c]));
-    float dmn = dmx;
-    group_minmax(dmn, dmx, group);
+    group_max(dmx, group);
     int ex = 0;
     (void)__builtin_frexpf(dmx, &ex);
     if (!(dmx > 0.0f) || !__builtin_isfinite(dmx)) ex = 0;
@@ -189,8 +188,7 @@ __device__ __forceinline__ bool quantize_row(uint4 wv, const StepScales& sc, flo
     float dmx = 0.0f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) dmx = fmaxf(dmx, __builtin_fabsf(dg[c]));
-    float dmn = dmx;
-    row16_minmax(dmn, dmx);
+    row16_max(dmx);
     const int E = search_exponent(dmx, e_state);
     e_state = E;
     P = __builtin_ldexpf(1.0f, 14 - E);
@@ -247,8 +245,8 @@ __device__ __forceinline__ bool quantize_tile_group(const uint16_t* W, int64_t N
   for (int p = 0; p < kPasses; ++p) {
     const int row = p * kRowsPerPass + q_row;
     const uint4 wv = n0 + row < N ? wvs[p] : make_uint4(0, 0, 0, 0);
-    bad |= quantize_row<CLIP>(wv, sc, r, sym, group, qmax, e_state[p], pe_out, hi_buf, lo_buf,
-                              row, li, pg_out);
+    bad |= quantize_row<CLIP>(wv, sc, r, sym, group, qmax, scale_divisor(qmax, sym), e_state[p],
+                              pe_out, hi_buf, lo_buf, row, li, pg_out);
   }
   return bad;
 }
