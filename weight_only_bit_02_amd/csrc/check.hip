@@ -12,9 +12,9 @@
 
 namespace awq {
 
-// true when either fp16 half of w has the all-ones exponent (Inf or NaN)
-__device__ __forceinline__ bool nonfinite_pair(uint32_t w) {
-  return (w & 0x7C00u) == 0x7C00u || (w & 0x7C000000u) == 0x7C000000u;
+// 1 when either fp16 half of w has the all-ones exponent (Inf or NaN), else 0
+__device__ __forceinline__ uint32_t nonfinite_pair(uint32_t w) {
+  return (uint32_t)((w & 0x7C00u) == 0x7C00u) | (uint32_t)((w & 0x7C000000u) == 0x7C000000u);
 }
 
 // Scans a (n elements, n % 8 == 0, 16-byte aligned) and b (m elements, any m, 2-byte
@@ -27,7 +27,7 @@ __global__ void __launch_bounds__(256)
   bool bad = false;
   for (int64_t i = tid; i < n / 8; i += stride) {
     const uint4 v = *reinterpret_cast<const uint4*>(a + i * 8);
-    bad |= nonfinite_pair(v.x) | nonfinite_pair(v.y) | nonfinite_pair(v.z) | nonfinite_pair(v.w);
+    bad |= (nonfinite_pair(v.x) | nonfinite_pair(v.y) | nonfinite_pair(v.z) | nonfinite_pair(v.w)) != 0;
   }
   for (int64_t i = tid; i < m; i += stride) bad |= (b[i] & 0x7C00u) == 0x7C00u;
   const uint64_t hit = __builtin_amdgcn_ballot_w64(bad);
