@@ -879,7 +879,7 @@ def main():
                  "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2),
                               "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                               "frac": round(gemm_tflops / FP16_MFMA_PEAK_TFLOPS, 4),
-                              "kernel": "awq::k_gemm_wide (q|k|v, gate|up: 384 tiles or more) and "
+                              "kernel": "awq::k_gemm_wide (q|k|v, gate|up: 160 tiles or more) and "
                                         "awq::k_gemm (o, down)"}},
         "search": {"tflops_algorithmic": round(search_tflops, 2), "ms": round(part_ms["search"], 4),
                    "best_alpha_index": best,

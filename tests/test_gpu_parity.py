@@ -352,16 +352,24 @@ def test_gemm_wide_gated_and_groups(group, M):
     assert oracle.linear_within_tolerance(Y.astype(np.float64), y_ref, bound).all()
 
 
-def test_gemm_auto_takes_wide_from_384_tiles():
-    """AUTO: the 256 x 256 GEMM once it has 384 tiles (M = 2048, N = 12288), the 128-row GEMM
-    below (N = 4096: 128 tiles); either result equals the explicit kernel's bit for bit."""
-    for N, wide in ((12288, True), (4096, False)):
-        K = 256
-        p, ref = _packed_case(N, K, off=N + 11)
-        X = to_dev(si.activations(2048, K, offset=N))
-        a = host(awq.linear_w4a16(X, p))
-        e = host(awq.linear_w4a16(X, p, kernel="gemm_wide" if wide else "gemm"))
-        assert np.array_equal(a.view(np.uint16), e.view(np.uint16))
-        rows = np.arange(0, 2048, 97)
-        y_ref, bound = oracle.linear_reference(host(X)[rows], *ref, K)
-        assert oracle.linear_within_tolerance(a[rows].astype(np.float64), y_ref, bound).all()
+def test_gemm_auto_takes_wide_from_160_tiles():
+    """AUTO: the 256 x 256 GEMM once it has 160 tiles (M = 1024, N = 12288: 192 tiles; M = 2048,
+    N = 12288: 384; gated M = 512, N = 22016: 172), the 128-row GEMM below (M = 2048, N = 4096:
+    128 tiles; M = 768, N = 10240: 120); either result equals the explicit kernel's bit for bit,
+    and the two GEMMs agree bit for bit."""
+    K = 256
+    for M, N, gated, wide in ((1024, 12288, False, True), (2048, 12288, False, True),
+                              (512, 22016, True, True), (2048, 4096, False, False),
+                              (768, 10240, False, False)):
+        p, ref = _packed_case(N, K, off=N + M + 11)
+        X = to_dev(si.activations(M, K, offset=N + M))
+        fn = awq.linear_w4a16_gated_silu if gated else awq.linear_w4a16
+        a = host(fn(X, p))
+        e = host(fn(X, p, kernel="gemm_wide" if wide else "gemm"))
+        assert np.array_equal(a.view(np.uint16), e.view(np.uint16)), (M, N, gated)
+        o = host(fn(X, p, kernel="gemm" if wide else "gemm_wide"))
+        assert np.array_equal(a.view(np.uint16), o.view(np.uint16)), (M, N, gated)
+        if not gated:
+            rows = np.arange(0, M, 97)
+            y_ref, bound = oracle.linear_reference(host(X)[rows], *ref, K)
+            assert oracle.linear_within_tolerance(a[rows].astype(np.float64), y_ref, bound).all()

@@ -284,8 +284,9 @@ static awq_status linear_common(const void* X, int64_t M, const uint32_t* qweigh
     kernel = M <= awq::kVgemvAutoMaxM && M <= g_gemv_max_m ? AWQ_LINEAR_GEMV
              : M <= g_gemv_max_m                            ? AWQ_LINEAR_SKINNY
                                                             : AWQ_LINEAR_GEMM;
-    // the 256 x 256 tiling once it gives the chip 1.5 tiles per CU or more (measured on the
-    // Llama-2-7B shapes at M = 2048: ahead from 384 tiles, behind at 128)
+    // the 256 x 256 tiling once it has 160 tiles or more (measured on the Llama-2-7B shapes
+    // at M = 512..2048: ahead of the 128-row GEMM from 172 tiles, behind at 128 and below,
+    // where the 128-row tiles give twice as many CUs work)
     if (kernel == AWQ_LINEAR_GEMM && awq::gemm_wide_supported(K, c.group_size, c.w_bit) &&
         awq::gemm_wide_tiles(M, N, gated) >= awq::kWideMinTiles)
       kernel = AWQ_LINEAR_GEMM_WIDE;

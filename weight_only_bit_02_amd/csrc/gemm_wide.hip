@@ -1,31 +1,34 @@
-// MFMA dequant-GEMM with 256 x 256 tiles and two waves per SIMD (a8, 4-bit codes with 128- or
-// 64-channel groups): Y[M][N] = X[M][K] deq(W)^T for batches large enough to give every CU
-// more than one such tile.
+// MFMA dequant-GEMM with 256 x 256 tiles and one wave per SIMD (a8, 4-bit codes with 128- or
+// 64-channel groups): Y[M][N] = X[M][K] deq(W)^T for batches that give most CUs a tile.
 //
 // "AWQ量化技术Skill", "主要功能和特点": a GEMM kernel serves batch sizes above one;
 // "AWQ量化实战" §2.3 / §3.4: weights stay 4-bit in memory and are dequantized on the fly.
 //
-// Block = 8 waves (two per SIMD), tile 256 (tokens) x 256 (output channels), K step 128
+// Block = 4 waves (one per SIMD), tile 256 (tokens) x 256 (output channels), K step 128
 // (one group of 128, or two of 64: a lane half's 64 channels are then one group). Wave w
-// owns rows [128 (w / 4), +128) and columns [64 (w % 4), +64) of the tile: 4 x 2
-// accumulators of v_mfma_f32_32x32x16_f16.
-//   - Both operands travel global -> LDS by 16-byte LDS DMA (global_load_lds_dwordx4),
-//     issued at the top of a step for the next one into the other of two buffers; every
-//     buffer is its own LDS object, so the compiler waits only for the DMA of the buffer
-//     a step reads. A (activations, 256 rows x 16 chunks of 16 bytes per step) is stored
-//     with chunk c of row r in slot c ^ (r & 15), so the 32 rows a fragment read touches
-//     fall in distinct banks; B (codes, 256 columns x 64 bytes) quarter-major, so a lane's
-//     16-byte read of 4 words for its column is conflict-free.
-//   - Each wave widens its own B words from LDS to (q - z) sc in fp16 (the packed layout
-//     puts channels 2p, 2p + 1 in nibbles p and p + 4, so one mask per pair and the 0x6400
-//     exponent give the pair exactly, then a packed subtract of 1024 + z and a packed
-//     multiply by the scale: one fp16 rounding), as the 128-row GEMM does, so both GEMMs
-//     give bit-identical results: lane half kh covers channels [64 kh, 64 kh + 64) of a
-//     step and k16 slice s covers 8 of them, A read from LDS with the same channel map.
-// Tiles are handed to the XCDs in contiguous runs (blocks of one XCD share an A panel in
-// that XCD's L2). Against the 128 x 256 tile of one wave per SIMD this halves the A tile
-// reads per MFMA and hides each wave's waits behind the other wave on its SIMD; it only
-// pays when the chip gets more than one 256 x 256 tile per CU (the dispatcher's rule).
+// owns all 256 rows and columns [64 w, 64 w + 64) of the tile: 8 x 2 accumulators of
+// v_mfma_f32_32x32x16_f16 (256 registers, which the compiler keeps in AGPRs), so every B
+// column is widened by exactly one wave and each A fragment read feeds two MFMAs.
+//   - Both operands travel global -> LDS by 16-byte LDS DMA (global_load_lds_dwordx4) into
+//     the other of two buffers for the next step; every buffer is its own LDS object, so the
+//     compiler waits only for the DMA of the buffer a step reads. A wave's 20 transfers of a
+//     step (16 of A, 4 of B) are issued in four groups of five, one at the head of each pair
+//     of k16 slices, where the wave's MFMA queue is full: issued all at once they stall the
+//     wave behind its own loads for longer than the matrix core can run ahead.
+//   - A (activations, 256 rows x 16 chunks of 16 bytes per step) is stored with chunk c of
+//     row r in slot c ^ (r & 15), so the 32 rows a fragment read touches fall in distinct
+//     banks; B (codes, 256 columns x 64 bytes) quarter-major, so a lane's 16-byte read of 4
+//     words for its column is conflict-free.
+//   - Each wave widens its own B words from LDS to (q - z) sc in fp16: the packed layout puts
+//     channels 2p, 2p + 1 in nibbles p and p + 4, so a mask and an exponent give a channel
+//     pair as 1024 + q (nibbles at bits 0 / 16 under 0x6400) or 64 + q (nibbles at bits 4 /
+//     20 under 0x5400, where one unit is 2^-4), one shift per word serving pairs 2 and 3;
+//     a packed subtract of the same bias plus z gives q - z exactly and a packed multiply by
+//     the scale rounds once. The 128-row GEMM computes the same fp16 values and the same
+//     MFMA sequence per output (lane half kh covers channels [64 kh, 64 kh + 64) of a step,
+//     k16 slice s covers 8 of them), so both GEMMs give bit-identical results.
+// Tiles go to the XCDs in contiguous runs, ordered four row tiles at a time with the column
+// index moving slowest, so the blocks of one XCD share A panels and B columns in its L2.
 //
 // Fused gate|up (GATED): a block covers 128 outputs; a wave's first 32-column MFMA tile is
 // gate column n, its second the up column n + N/2, and the epilogue stores SiLU(g) * u.
@@ -44,6 +47,8 @@ typedef float f32x16w __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWM = 256, kWN = 256, kWK = 128;
+constexpr int kRT = 8, kCT = 2;   // a wave's 32 x 32 MFMA tiles: 8 along rows, 2 along columns
+constexpr int64_t kGroupRows = 4;  // row tiles per group of the tile order
 
 __device__ __forceinline__ uint32_t wide_magic() {
   uint32_t m;
@@ -51,19 +56,22 @@ __device__ __forceinline__ uint32_t wide_magic() {
   return m;
 }
 
-// One packed word -> its 8 dequantized fp16 channels (q - z) sc, in channel order.
-__device__ __forceinline__ half8w widen_word(uint32_t w, half2w zz, half2w s2, uint32_t magic) {
-  half2w d[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const uint32_t u = ((w >> (4 * p)) & 0x000F000Fu) | magic;
-    d[p] = (__builtin_bit_cast(half2w, u) + zz) * s2;
-  }
-  return half8w{d[0][0], d[0][1], d[1][0], d[1][1], d[2][0], d[2][1], d[3][0], d[3][1]};
+// One packed word -> its 8 dequantized fp16 channels (q - z) sc, in channel order. zz holds
+// -(1024 + z) and zz64 -(64 + z) in both halves, s2 the scale in both halves.
+__device__ __forceinline__ half8w widen_word(uint32_t w, half2w zz, half2w zz64, half2w s2,
+                                             uint32_t magic) {
+  const uint32_t w8 = w >> 8;
+  const uint32_t u0 = (w & 0x000F000Fu) | magic, u1 = (w & 0x00F000F0u) | 0x54005400u;
+  const uint32_t u2 = (w8 & 0x000F000Fu) | magic, u3 = (w8 & 0x00F000F0u) | 0x54005400u;
+  const half2w d0 = (__builtin_bit_cast(half2w, u0) + zz) * s2;
+  const half2w d1 = (__builtin_bit_cast(half2w, u1) + zz64) * s2;
+  const half2w d2 = (__builtin_bit_cast(half2w, u2) + zz) * s2;
+  const half2w d3 = (__builtin_bit_cast(half2w, u3) + zz64) * s2;
+  return half8w{d0[0], d0[1], d1[0], d1[1], d2[0], d2[1], d3[0], d3[1]};
 }
 
 template <bool GATED>
-__global__ void __launch_bounds__(512)
+__global__ void __launch_bounds__(256)
     k_gemm_wide(const uint16_t* X, int64_t M, const uint32_t* qweight, const uint16_t* scales,
                 const uint8_t* zeros, int64_t N, int64_t K, int group, uint16_t* __restrict__ Y,
                 int64_t mt, int64_t nt, int64_t per_xcd) {
@@ -71,40 +79,45 @@ __global__ void __launch_bounds__(512)
   __shared__ __attribute__((aligned(16))) uint4 a1s[kWM * 16];
   __shared__ __attribute__((aligned(16))) uint4 b0s[kWN * 4];
   __shared__ __attribute__((aligned(16))) uint4 b1s[kWN * 4];
+  // tile t: XCD blockIdx % 8 takes tiles [per_xcd (blockIdx % 8), +per_xcd); within a group
+  // of kGroupRows row tiles the row index moves fastest
   const int64_t t = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   if (t >= mt * nt) return;
-  const int64_t m0 = (t / nt) * kWM;
-  const int64_t n0 = (t % nt) * (GATED ? kWN / 2 : kWN);
+  const int64_t grp = t / (kGroupRows * nt), first_m = grp * kGroupRows;
+  const int64_t gsz = mt - first_m < kGroupRows ? mt - first_m : kGroupRows;
+  const int64_t within = t - grp * kGroupRows * nt;
+  const int64_t m0 = (first_m + within % gsz) * kWM;
+  const int64_t n0 = (within / gsz) * (GATED ? kWN / 2 : kWN);
   const int64_t nh = N / 2;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
   const int m32 = lane & 31, kh = lane >> 5;
   const int g64 = group == 64;
   const int64_t Gs = K / group, zbw = (Gs + 1) / 2, words = K / 8;
   const int64_t nsteps = K / kWK;
   const uint32_t magic = wide_magic();
 
-  // A DMA map: wave instruction i (0..7) fills slots (wave * 8 + i) * 64 + lane of the
-  // buffer: row r = (wave * 8 + i) * 4 + lane / 16, slot lane % 16 <- chunk (lane % 16) ^ (r % 16).
+  // A DMA map: wave transfer i (0..15) fills slots (wave * 16 + i) * 64 + lane of the buffer:
+  // row r = (wave * 16 + i) * 4 + lane / 16, slot lane % 16 <- chunk (lane % 16) ^ (r % 16).
   // Rows past M read row M - 1 (their outputs are never stored). Offsets fit 32 bits: the
   // launcher takes this kernel only for 256 K < 2^32.
   const uint16_t* xblk = X + m0 * K;
-  uint32_t aoff[8];
+  uint32_t aoff[16];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = (wave * 8 + i) * 4 + (lane >> 4);
+  for (int i = 0; i < 16; ++i) {
+    const int r = (wave * 16 + i) * 4 + (lane >> 4);
     const int64_t gr = m0 + r < M ? r : M - 1 - m0;
     aoff[i] = (uint32_t)(gr * K + ((lane & 15) ^ (r & 15)) * 8);
   }
-  // B DMA map, quarter-major: slot (wave * 2 + i) * 64 + lane = 16-byte quarter q (slot /
+  // B DMA map, quarter-major: slot (wave * 4 + i) * 64 + lane = 16-byte quarter q (slot /
   // 256) of tile column c (slot % 256) of the columns' 64 code bytes of a step, so a wave's
   // read of one quarter of 32 consecutive columns is 512 contiguous bytes (no bank
-  // conflicts). Gated: tile column c is wave tile c / 64's gate column (c % 64 < 32) or up
-  // column. Columns past the end read the last one (never stored).
-  const uint32_t* bptr[2];
+  // conflicts). Gated: tile columns [64 w, 64 w + 32) hold the gate rows and [64 w + 32,
+  // 64 w + 64) the up rows of outputs n0 + 32 w .. n0 + 32 w + 31. Columns past the end
+  // read the last one (never stored).
+  const uint32_t* bptr[4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int slot = (wave * 2 + i) * 64 + lane;
+  for (int i = 0; i < 4; ++i) {
+    const int slot = (wave * 4 + i) * 64 + lane;
     const int c = slot & 255, q = slot >> 8;
     int64_t n;
     if constexpr (GATED) {
@@ -117,47 +130,44 @@ __global__ void __launch_bounds__(512)
     bptr[i] = qweight + n * words + q * 4;
   }
   // this lane's two weight rows (gated: gate row n and up row n + N/2): scales and zeros
-  int64_t bcol[2];
+  int64_t bcol[kCT];
   if constexpr (GATED) {
-    const int64_t n = n0 + wn * 32 + m32;
-    bcol[0] = n < nh ? n : nh - 1;
+    const int64_t o = n0 + wave * 32 + m32;
+    bcol[0] = o < nh ? o : nh - 1;
     bcol[1] = bcol[0] + nh;
   } else {
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int64_t n = n0 + wn * 64 + b * 32 + m32;
+    for (int b = 0; b < kCT; ++b) {
+      const int64_t n = n0 + wave * 64 + b * 32 + m32;
       bcol[b] = n < N ? n : N - 1;
     }
   }
   struct ScaleZero {
-    uint32_t zb[2], sc[2];
+    uint32_t zb[kCT], sc[kCT];
   };
   auto load_sz = [&](ScaleZero& st, int64_t step) {
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < kCT; ++b) {
       st.zb[b] = zeros[bcol[b] * zbw + (step >> (1 - g64))];
       st.sc[b] = scales[bcol[b] * Gs + (step << g64) + (g64 & kh)];
     }
   };
-  auto dma = [&](int64_t step, uint4* ad, uint4* bd) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(xblk + step * kWK + aoff[i]),
-                                       (lds_void*)&ad[(wave * 8 + i) * 64], 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(bptr[i] + step * 16),
-                                       (lds_void*)&bd[(wave * 2 + i) * 64], 16, 0, 0);
-  };
 
-  f32x16w acc[4][2];
+  f32x16w acc[kRT][kCT];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < kRT; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16w{};
+    for (int b = 0; b < kCT; ++b) acc[a][b] = f32x16w{};
 
   ScaleZero s0, s1;
-  dma(0, a0s, b0s);
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    __builtin_amdgcn_global_load_lds((const void*)(xblk + aoff[i]),
+                                     (lds_void*)&a0s[(wave * 16 + i) * 64], 16, 0, 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    __builtin_amdgcn_global_load_lds((const void*)(bptr[i]), (lds_void*)&b0s[(wave * 4 + i) * 64],
+                                     16, 0, 0);
   load_sz(s0, 0);
   __syncthreads();
 
@@ -168,54 +178,71 @@ __global__ void __launch_bounds__(512)
     const uint4* bb = BUF ? b1s : b0s;
     // the next step's operands (clamped: the last step reloads itself into the idle buffer)
     const int64_t sn = step + 1 < nsteps ? step + 1 : nsteps - 1;
-    dma(sn, BUF ? a0s : a1s, BUF ? b0s : b1s);
     load_sz(nxt, sn);
-    __builtin_amdgcn_sched_barrier(0);  // keep those loads at the top of the step
-    half2w zz[2], s2[2];
+    __builtin_amdgcn_sched_barrier(0);  // keep the scale loads at the top of the step
+    uint4* const adn = BUF ? a0s : a1s;
+    uint4* const bdn = BUF ? b0s : b1s;
+    auto dma_a = [&](int i) {
+      __builtin_amdgcn_global_load_lds((const void*)(xblk + sn * kWK + aoff[i]),
+                                       (lds_void*)&adn[(wave * 16 + i) * 64], 16, 0, 0);
+    };
+    auto dma_b = [&](int i) {
+      __builtin_amdgcn_global_load_lds((const void*)(bptr[i] + sn * 16),
+                                       (lds_void*)&bdn[(wave * 4 + i) * 64], 16, 0, 0);
+    };
+    half2w zz[kCT], zz64[kCT], s2[kCT];
     const int hi = g64 ? kh : (int)(step & 1);  // zero nibble: group of 128 (step) or 64 (2 step + kh)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < kCT; ++b) {
       const uint32_t z = hi ? (cur.zb[b] >> 4) : (cur.zb[b] & 0xF);
-      const uint32_t zbits = 0x6400u + z;
-      zz[b] = -__builtin_bit_cast(half2w, zbits | (zbits << 16));
+      const uint32_t z1024 = 0x6400u + z, z64 = 0x5400u + (z << 4);
+      zz[b] = -__builtin_bit_cast(half2w, z1024 | (z1024 << 16));
+      zz64[b] = -__builtin_bit_cast(half2w, z64 | (z64 << 16));
       s2[b] = __builtin_bit_cast(half2w, cur.sc[b] | (cur.sc[b] << 16));
     }
     // this lane's code words of the step: words 8 kh .. 8 kh + 7 of each of its two columns,
     // quarters 2 kh and 2 kh + 1 (one 16-byte read each)
-    uint4 bq[2][2];
+    uint4 bq[kCT][2];
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < kCT; ++b)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) bq[b][h] = bb[(2 * kh + h) * 256 + wn * 64 + b * 32 + m32];
-    auto frags = [&](int s, half8w (&A)[4], half8w (&B)[2]) {
+      for (int h = 0; h < 2; ++h) bq[b][h] = bb[(2 * kh + h) * 256 + wave * 64 + b * 32 + m32];
+    auto frags = [&](int s, half8w (&A)[kRT], half8w (&B)[kCT]) {
       const int c = kh * 8 + s;
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int r = wm * 128 + a * 32 + m32;
+      for (int a = 0; a < kRT; ++a) {
+        const int r = a * 32 + m32;
         A[a] = __builtin_bit_cast(half8w, ab[r * 16 + (c ^ (r & 15))]);
       }
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
+      for (int b = 0; b < kCT; ++b) {
         const uint4 q = bq[b][s >> 2];
         const uint32_t w = (s & 3) == 0 ? q.x : (s & 3) == 1 ? q.y : (s & 3) == 2 ? q.z : q.w;
-        B[b] = widen_word(w, zz[b], s2[b], magic);
+        B[b] = widen_word(w, zz[b], zz64[b], s2[b], magic);
       }
     };
-    half8w A0[4], B0[2], A1[4], B1[2];
+    half8w A0[kRT], B0[kCT], A1[kRT], B1[kCT];
     frags(0, A0, B0);
 #pragma unroll
     for (int s = 0; s < kWK / 16; s += 2) {
+      {  // a quarter of the next step's transfers: A 4 s / 2 .. + 3 and B s / 2
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma_a(2 * s + i);
+        dma_b(s >> 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       frags(s + 1, A1, B1);
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < kRT; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < kCT; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A0[a], B0[b], acc[a][b], 0, 0, 0);
       if (s + 2 < kWK / 16) frags(s + 2, A0, B0);
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < kRT; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < kCT; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A1[a], B1[b], acc[a][b], 0, 0, 0);
     }
     __syncthreads();  // the next step's DMA has landed; this step's buffer is free
@@ -229,23 +256,23 @@ __global__ void __launch_bounds__(512)
 
   // 32x32 accumulator layout: element e of lane l is (row 8(e/4) + 4(l/32) + e%4, col l%32).
   if constexpr (GATED) {
-    const int64_t col = n0 + wn * 32 + m32;
+    const int64_t col = n0 + wave * 32 + m32;
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < kRT; ++a)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int64_t row = m0 + wm * 128 + a * 32 + 8 * (e >> 2) + 4 * kh + (e & 3);
+        const int64_t row = m0 + a * 32 + 8 * (e >> 2) + 4 * kh + (e & 3);
         if (row < M && col < nh) Y[row * nh + col] = f2h_bits(silu_f32(acc[a][0][e]) * acc[a][1][e]);
       }
   } else {
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < kRT; ++a)
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int64_t col = n0 + wn * 64 + b * 32 + m32;
+      for (int b = 0; b < kCT; ++b) {
+        const int64_t col = n0 + wave * 64 + b * 32 + m32;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int64_t row = m0 + wm * 128 + a * 32 + 8 * (e >> 2) + 4 * kh + (e & 3);
+          const int64_t row = m0 + a * 32 + 8 * (e >> 2) + 4 * kh + (e & 3);
           if (row < M && col < N) Y[row * N + col] = f2h_bits(acc[a][b][e]);
         }
       }
@@ -272,10 +299,10 @@ hipError_t launch_gemm_wide(const uint16_t* X, int64_t M, const uint32_t* qweigh
   const int64_t per_xcd = (mt * nt + 7) / 8;
   const dim3 grid((unsigned)(per_xcd * 8));
   if (gated)
-    hipLaunchKernelGGL(k_gemm_wide<true>, grid, dim3(512), 0, stream, X, M, qweight, scales, zeros,
+    hipLaunchKernelGGL(k_gemm_wide<true>, grid, dim3(256), 0, stream, X, M, qweight, scales, zeros,
                        N, K, group, Y, mt, nt, per_xcd);
   else
-    hipLaunchKernelGGL(k_gemm_wide<false>, grid, dim3(512), 0, stream, X, M, qweight, scales, zeros,
+    hipLaunchKernelGGL(k_gemm_wide<false>, grid, dim3(256), 0, stream, X, M, qweight, scales, zeros,
                        N, K, group, Y, mt, nt, per_xcd);
   return hipGetLastError();
 }
