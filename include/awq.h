@@ -89,10 +89,11 @@ typedef enum awq_linear_kernel {
   AWQ_LINEAR_GEMV = 1, /* wave-per-rows dequant-fused GEMV (any M <= 8)       */
   AWQ_LINEAR_GEMM = 2, /* MFMA dequant-GEMM (any M)                           */
   AWQ_LINEAR_SKINNY = 3, /* MFMA GEMV for small batches, split K (M <= 64)    */
-  AWQ_LINEAR_GEMM_WIDE = 4 /* MFMA dequant-GEMM on 256 x 256 tiles, one wave per
-                              SIMD (4-bit codes, 128- or 64-channel groups, 256 K <
+  AWQ_LINEAR_GEMM_WIDE = 4 /* MFMA dequant-GEMM on 256-row tiles, one wave per SIMD
+                              (4-bit codes, 128- or 64-channel groups, 256 K <
                               2^32; else AWQ_ERR_UNSUPPORTED); AUTO takes it over
-                              the GEMM when it has at least 160 tiles          */
+                              the GEMM from M = 128 (fused gate|up: from 160
+                              tiles of 128 outputs)                            */
 } awq_linear_kernel;
 
 /*

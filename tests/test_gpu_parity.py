@@ -317,9 +317,9 @@ def test_linear_flags_nonfinite(kernel, M, where):
 @pytest.mark.parametrize("M", [1, 65, 256, 257, 300])
 @pytest.mark.parametrize("N,K", [(1, 128), (67, 384), (256, 4096), (300, 1152)])
 def test_gemm_wide_matches_oracle_and_gemm(M, N, K):
-    """The 256 x 256-tile GEMM: ragged M and N (partial tiles on both axes), K of 1..32 steps;
-    within the linear tolerance and bit-identical to the 128-row GEMM (same channel order,
-    same fp16 widening)."""
+    """The 256-row GEMM (128-column tiles at these sizes): ragged M and N (partial tiles on
+    both axes), K of 1..32 steps; within the linear tolerance and bit-identical to the 128-row
+    GEMM (same channel order, same fp16 widening)."""
     p, ref = _packed_case(N, K, off=N + 9 * K)
     X = si.activations(M, K, offset=M + 700)
     _check_linear(X, p, ref, "gemm_wide")
@@ -352,15 +352,16 @@ def test_gemm_wide_gated_and_groups(group, M):
     assert oracle.linear_within_tolerance(Y.astype(np.float64), y_ref, bound).all()
 
 
-def test_gemm_auto_takes_wide_from_160_tiles():
-    """AUTO: the 256 x 256 GEMM once it has 160 tiles (M = 1024, N = 12288: 192 tiles; M = 2048,
-    N = 12288: 384; gated M = 512, N = 22016: 172), the 128-row GEMM below (M = 2048, N = 4096:
-    128 tiles; M = 768, N = 10240: 120); either result equals the explicit kernel's bit for bit,
-    and the two GEMMs agree bit for bit."""
+def test_gemm_auto_kernel_choice():
+    """AUTO among the two GEMMs: the 256-row GEMM for plain outputs from M = 128 (M = 1024,
+    N = 12288 takes its 256-column tiles; M = 2048, N = 12288 and N = 4096 its 128-column
+    tiles), for fused gate|up from 160 tiles (gated M = 512, N = 22016: 172); the 128-row GEMM
+    below (M = 100; gated M = 256, N = 22016: 86 tiles). Either result equals the explicit
+    kernel's bit for bit, and the two GEMMs agree bit for bit."""
     K = 256
     for M, N, gated, wide in ((1024, 12288, False, True), (2048, 12288, False, True),
-                              (512, 22016, True, True), (2048, 4096, False, False),
-                              (768, 10240, False, False)):
+                              (2048, 4096, False, True), (100, 4096, False, False),
+                              (512, 22016, True, True), (256, 22016, True, False)):
         p, ref = _packed_case(N, K, off=N + M + 11)
         X = to_dev(si.activations(M, K, offset=N + M))
         fn = awq.linear_w4a16_gated_silu if gated else awq.linear_w4a16
@@ -373,3 +374,22 @@ def test_gemm_auto_takes_wide_from_160_tiles():
             rows = np.arange(0, M, 97)
             y_ref, bound = oracle.linear_reference(host(X)[rows], *ref, K)
             assert oracle.linear_within_tolerance(a[rows].astype(np.float64), y_ref, bound).all()
+
+
+@pytest.mark.parametrize("M,N,group", [(2047, 8191, 128), (1000, 12300, 64)])
+def test_gemm_wide_256_column_tiles_ragged(M, N, group):
+    """Shapes where the 256-row GEMM keeps 256-column tiles (their whole waves fill the chip
+    as well as 128-column tiles would) with a partial last row and column tile, 128- and
+    64-channel groups: bit-identical to the 128-row GEMM, sampled rows within the linear
+    tolerance of the oracle."""
+    K = 128
+    W = si.weights(N, K, offset=N + group)
+    qw, sc, zb, _ = oracle.quantize_pack(W, None, None, True, group, 4)
+    p = awq.quantize_pack(to_dev(W), group_size=group)
+    X = to_dev(si.activations(M, K, offset=M + 5))
+    a = host(awq.linear_w4a16(X, p, kernel="gemm_wide"))
+    b = host(awq.linear_w4a16(X, p, kernel="gemm"))
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+    rows = np.r_[np.arange(0, M, 131), M - 1]
+    y_ref, bound = oracle.linear_reference(host(X)[rows], qw, sc, zb, K)
+    assert oracle.linear_within_tolerance(a[rows].astype(np.float64), y_ref, bound).all()

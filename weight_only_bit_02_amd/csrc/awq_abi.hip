@@ -284,11 +284,12 @@ static awq_status linear_common(const void* X, int64_t M, const uint32_t* qweigh
     kernel = M <= awq::kVgemvAutoMaxM && M <= g_gemv_max_m ? AWQ_LINEAR_GEMV
              : M <= g_gemv_max_m                            ? AWQ_LINEAR_SKINNY
                                                             : AWQ_LINEAR_GEMM;
-    // the 256 x 256 tiling once it has 160 tiles or more (measured on the Llama-2-7B shapes
-    // at M = 512..2048: ahead of the 128-row GEMM from 172 tiles, behind at 128 and below,
-    // where the 128-row tiles give twice as many CUs work)
+    // the 256-row tiling (measured on the Llama-2-7B shapes at M = 128..2048): plain outputs
+    // from 128 rows, where its 128-column tiles already beat the 128-row GEMM on every shape;
+    // fused gate|up (256-column tiles only) once it has 160 tiles (ahead from 172, behind at
+    // 86 and below, where the 128-row tiles give twice as many CUs work)
     if (kernel == AWQ_LINEAR_GEMM && awq::gemm_wide_supported(K, c.group_size, c.w_bit) &&
-        awq::gemm_wide_tiles(M, N, gated) >= awq::kWideMinTiles)
+        (gated ? awq::gemm_wide_tiles(M, N, true) >= awq::kWideMinTilesGated : M >= awq::kWideMinM))
       kernel = AWQ_LINEAR_GEMM_WIDE;
   }
   const auto* Xh = (const uint16_t*)X;

@@ -1,23 +1,25 @@
-// MFMA dequant-GEMM with 256 x 256 tiles and one wave per SIMD (a8, 4-bit codes with 128- or
-// 64-channel groups): Y[M][N] = X[M][K] deq(W)^T for batches that give most CUs a tile.
+// MFMA dequant-GEMM with 256-row tiles and one wave per SIMD (a8, 4-bit codes with 128- or
+// 64-channel groups): Y[M][N] = X[M][K] deq(W)^T for batches of 128 rows and more.
 //
 // "AWQ量化技术Skill", "主要功能和特点": a GEMM kernel serves batch sizes above one;
 // "AWQ量化实战" §2.3 / §3.4: weights stay 4-bit in memory and are dequantized on the fly.
 //
-// Block = 4 waves (one per SIMD), tile 256 (tokens) x 256 (output channels), K step 128
-// (one group of 128, or two of 64: a lane half's 64 channels are then one group). Wave w
-// owns all 256 rows and columns [64 w, 64 w + 64) of the tile: 8 x 2 accumulators of
-// v_mfma_f32_32x32x16_f16 (256 registers, which the compiler keeps in AGPRs), so every B
-// column is widened by exactly one wave and each A fragment read feeds two MFMAs.
+// Block = 4 waves (one per SIMD), tile 256 (tokens) x WN (output channels, 256 or 128), K
+// step 128 (one group of 128, or two of 64: a lane half's 64 channels are then one group).
+// Wave w owns all 256 rows and columns [WN / 4 w, +WN / 4) of the tile: 8 x (WN / 128)
+// accumulators of v_mfma_f32_32x32x16_f16 (256 or 128 registers, which the compiler keeps
+// in AGPRs), so every B column is widened by exactly one wave. The launcher takes WN = 128
+// when that fills more of the chip's 256 CUs (whole waves of tiles counted), else 256, whose
+// tiles do twice the MFMA work per A fragment read and per barrier.
 //   - Both operands travel global -> LDS by 16-byte LDS DMA (global_load_lds_dwordx4) into
 //     the other of two buffers for the next step; every buffer is its own LDS object, so the
-//     compiler waits only for the DMA of the buffer a step reads. A wave's 20 transfers of a
-//     step (16 of A, 4 of B) are issued in four groups of five, one at the head of each pair
+//     compiler waits only for the DMA of the buffer a step reads. A wave's transfers of a
+//     step (16 of A, WN / 64 of B) are issued in four groups, one at the head of each pair
 //     of k16 slices, where the wave's MFMA queue is full: issued all at once they stall the
 //     wave behind its own loads for longer than the matrix core can run ahead.
 //   - A (activations, 256 rows x 16 chunks of 16 bytes per step) is stored with chunk c of
 //     row r in slot c ^ (r & 15), so the 32 rows a fragment read touches fall in distinct
-//     banks; B (codes, 256 columns x 64 bytes) quarter-major, so a lane's 16-byte read of 4
+//     banks; B (codes, WN columns x 64 bytes) quarter-major, so a lane's 16-byte read of 4
 //     words for its column is conflict-free.
 //   - Each wave widens its own B words from LDS to (q - z) sc in fp16: the packed layout puts
 //     channels 2p, 2p + 1 in nibbles p and p + 4, so a mask and an exponent give a channel
@@ -30,8 +32,9 @@
 // Tiles go to the XCDs in contiguous runs, ordered four row tiles at a time with the column
 // index moving slowest, so the blocks of one XCD share A panels and B columns in its L2.
 //
-// Fused gate|up (GATED): a block covers 128 outputs; a wave's first 32-column MFMA tile is
-// gate column n, its second the up column n + N/2, and the epilogue stores SiLU(g) * u.
+// Fused gate|up (GATED, WN = 256 only): a block covers 128 outputs; a wave's first 32-column
+// MFMA tile is gate column n, its second the up column n + N/2, and the epilogue stores
+// SiLU(g) * u.
 #include <type_traits>
 
 #include "common.hpp"
@@ -46,8 +49,8 @@ typedef _Float16 half2w __attribute__((ext_vector_type(2)));
 typedef float f32x16w __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kWM = 256, kWN = 256, kWK = 128;
-constexpr int kRT = 8, kCT = 2;   // a wave's 32 x 32 MFMA tiles: 8 along rows, 2 along columns
+constexpr int kWM = 256, kWK = 128;
+constexpr int kRT = 8;            // a wave's 32 x 32 MFMA tiles along rows
 constexpr int64_t kGroupRows = 4;  // row tiles per group of the tile order
 
 __device__ __forceinline__ uint32_t wide_magic() {
@@ -70,15 +73,18 @@ __device__ __forceinline__ half8w widen_word(uint32_t w, half2w zz, half2w zz64,
   return half8w{d0[0], d0[1], d1[0], d1[1], d2[0], d2[1], d3[0], d3[1]};
 }
 
-template <bool GATED>
+template <bool GATED, int WN>
 __global__ void __launch_bounds__(256)
     k_gemm_wide(const uint16_t* X, int64_t M, const uint32_t* qweight, const uint16_t* scales,
                 const uint8_t* zeros, int64_t N, int64_t K, int group, uint16_t* __restrict__ Y,
                 int64_t mt, int64_t nt, int64_t per_xcd) {
   __shared__ __attribute__((aligned(16))) uint4 a0s[kWM * 16];
   __shared__ __attribute__((aligned(16))) uint4 a1s[kWM * 16];
-  __shared__ __attribute__((aligned(16))) uint4 b0s[kWN * 4];
-  __shared__ __attribute__((aligned(16))) uint4 b1s[kWN * 4];
+  static_assert(WN == 256 || (WN == 128 && !GATED), "tile widths");
+  constexpr int kCT = WN / 128;  // a wave's 32 x 32 MFMA tiles along columns
+  constexpr int kBT = WN / 64;   // B transfers per wave and step
+  __shared__ __attribute__((aligned(16))) uint4 b0s[WN * 4];
+  __shared__ __attribute__((aligned(16))) uint4 b1s[WN * 4];
   // tile t: XCD blockIdx % 8 takes tiles [per_xcd (blockIdx % 8), +per_xcd); within a group
   // of kGroupRows row tiles the row index moves fastest
   const int64_t t = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
@@ -87,7 +93,7 @@ __global__ void __launch_bounds__(256)
   const int64_t gsz = mt - first_m < kGroupRows ? mt - first_m : kGroupRows;
   const int64_t within = t - grp * kGroupRows * nt;
   const int64_t m0 = (first_m + within % gsz) * kWM;
-  const int64_t n0 = (within / gsz) * (GATED ? kWN / 2 : kWN);
+  const int64_t n0 = (within / gsz) * (GATED ? WN / 2 : WN);
   const int64_t nh = N / 2;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m32 = lane & 31, kh = lane >> 5;
@@ -108,17 +114,17 @@ __global__ void __launch_bounds__(256)
     const int64_t gr = m0 + r < M ? r : M - 1 - m0;
     aoff[i] = (uint32_t)(gr * K + ((lane & 15) ^ (r & 15)) * 8);
   }
-  // B DMA map, quarter-major: slot (wave * 4 + i) * 64 + lane = 16-byte quarter q (slot /
-  // 256) of tile column c (slot % 256) of the columns' 64 code bytes of a step, so a wave's
+  // B DMA map, quarter-major: slot (wave * kBT + i) * 64 + lane = 16-byte quarter q (slot /
+  // WN) of tile column c (slot % WN) of the columns' 64 code bytes of a step, so a wave's
   // read of one quarter of 32 consecutive columns is 512 contiguous bytes (no bank
   // conflicts). Gated: tile columns [64 w, 64 w + 32) hold the gate rows and [64 w + 32,
   // 64 w + 64) the up rows of outputs n0 + 32 w .. n0 + 32 w + 31. Columns past the end
   // read the last one (never stored).
-  const uint32_t* bptr[4];
+  const uint32_t* bptr[kBT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int slot = (wave * 4 + i) * 64 + lane;
-    const int c = slot & 255, q = slot >> 8;
+  for (int i = 0; i < kBT; ++i) {
+    const int slot = (wave * kBT + i) * 64 + lane;
+    const int c = slot % WN, q = slot / WN;
     int64_t n;
     if constexpr (GATED) {
       int64_t o = n0 + (c >> 6) * 32 + (c & 31);
@@ -129,7 +135,7 @@ __global__ void __launch_bounds__(256)
     }
     bptr[i] = qweight + n * words + q * 4;
   }
-  // this lane's two weight rows (gated: gate row n and up row n + N/2): scales and zeros
+  // this lane's weight rows (gated: gate row n and up row n + N/2): scales and zeros
   int64_t bcol[kCT];
   if constexpr (GATED) {
     const int64_t o = n0 + wave * 32 + m32;
@@ -138,7 +144,7 @@ __global__ void __launch_bounds__(256)
   } else {
 #pragma unroll
     for (int b = 0; b < kCT; ++b) {
-      const int64_t n = n0 + wave * 64 + b * 32 + m32;
+      const int64_t n = n0 + wave * kCT * 32 + b * 32 + m32;
       bcol[b] = n < N ? n : N - 1;
     }
   }
@@ -165,8 +171,8 @@ __global__ void __launch_bounds__(256)
     __builtin_amdgcn_global_load_lds((const void*)(xblk + aoff[i]),
                                      (lds_void*)&a0s[(wave * 16 + i) * 64], 16, 0, 0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    __builtin_amdgcn_global_load_lds((const void*)(bptr[i]), (lds_void*)&b0s[(wave * 4 + i) * 64],
+  for (int i = 0; i < kBT; ++i)
+    __builtin_amdgcn_global_load_lds((const void*)(bptr[i]), (lds_void*)&b0s[(wave * kBT + i) * 64],
                                      16, 0, 0);
   load_sz(s0, 0);
   __syncthreads();
@@ -188,7 +194,7 @@ __global__ void __launch_bounds__(256)
     };
     auto dma_b = [&](int i) {
       __builtin_amdgcn_global_load_lds((const void*)(bptr[i] + sn * 16),
-                                       (lds_void*)&bdn[(wave * 4 + i) * 64], 16, 0, 0);
+                                       (lds_void*)&bdn[(wave * kBT + i) * 64], 16, 0, 0);
     };
     half2w zz[kCT], zz64[kCT], s2[kCT];
     const int hi = g64 ? kh : (int)(step & 1);  // zero nibble: group of 128 (step) or 64 (2 step + kh)
@@ -200,13 +206,13 @@ __global__ void __launch_bounds__(256)
       zz64[b] = -__builtin_bit_cast(half2w, z64 | (z64 << 16));
       s2[b] = __builtin_bit_cast(half2w, cur.sc[b] | (cur.sc[b] << 16));
     }
-    // this lane's code words of the step: words 8 kh .. 8 kh + 7 of each of its two columns,
+    // this lane's code words of the step: words 8 kh .. 8 kh + 7 of each of its columns,
     // quarters 2 kh and 2 kh + 1 (one 16-byte read each)
     uint4 bq[kCT][2];
 #pragma unroll
     for (int b = 0; b < kCT; ++b)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) bq[b][h] = bb[(2 * kh + h) * 256 + wave * 64 + b * 32 + m32];
+      for (int h = 0; h < 2; ++h) bq[b][h] = bb[(2 * kh + h) * WN + wave * kCT * 32 + b * 32 + m32];
     auto frags = [&](int s, half8w (&A)[kRT], half8w (&B)[kCT]) {
       const int c = kh * 8 + s;
 #pragma unroll
@@ -225,11 +231,11 @@ __global__ void __launch_bounds__(256)
     frags(0, A0, B0);
 #pragma unroll
     for (int s = 0; s < kWK / 16; s += 2) {
-      {  // a quarter of the next step's transfers: A 4 s / 2 .. + 3 and B s / 2
+      {  // a quarter of the next step's A transfers (4 s / 2 .. + 3) and B transfer s / 2
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) dma_a(2 * s + i);
-        dma_b(s >> 1);
+        if ((s >> 1) < kBT) dma_b(s >> 1);
         __builtin_amdgcn_sched_barrier(0);
       }
       frags(s + 1, A1, B1);
@@ -269,7 +275,7 @@ __global__ void __launch_bounds__(256)
     for (int a = 0; a < kRT; ++a)
 #pragma unroll
       for (int b = 0; b < kCT; ++b) {
-        const int64_t col = n0 + wave * 64 + b * 32 + m32;
+        const int64_t col = n0 + wave * kCT * 32 + b * 32 + m32;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int64_t row = m0 + a * 32 + 8 * (e >> 2) + 4 * kh + (e & 3);
@@ -281,9 +287,21 @@ __global__ void __launch_bounds__(256)
 
 }  // namespace
 
+// Tile width for an M x N output: 128 columns when whole waves of those tiles keep more of
+// the 256 CUs busy than 256-column tiles do (ties go to 256); gated outputs always 256.
+int gemm_wide_cols(int64_t M, int64_t N, bool gated) {
+  if (gated) return 256;
+  const int64_t mt = (M + kWM - 1) / kWM;
+  const int64_t t256 = mt * ((N + 255) / 256), t128 = mt * ((N + 127) / 128);
+  const int64_t w256 = (t256 + 255) / 256, w128 = (t128 + 255) / 256;  // waves of tiles
+  // fill fraction t / (256 w): compare t128 / w128 against t256 / w256
+  return t128 * w256 > t256 * w128 ? 128 : 256;
+}
+
 int64_t gemm_wide_tiles(int64_t M, int64_t N, bool gated) {
   const int64_t mt = (M + kWM - 1) / kWM;
-  const int64_t nt = gated ? (N / 2 + kWN / 2 - 1) / (kWN / 2) : (N + kWN - 1) / kWN;
+  const int cols = gemm_wide_cols(M, N, gated);
+  const int64_t nt = gated ? (N / 2 + cols / 2 - 1) / (cols / 2) : (N + cols - 1) / cols;
   return mt * nt;
 }
 
@@ -294,16 +312,20 @@ bool gemm_wide_supported(int64_t K, int group, int w_bit) {
 hipError_t launch_gemm_wide(const uint16_t* X, int64_t M, const uint32_t* qweight,
                             const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
                             int group, uint16_t* Y, bool gated, hipStream_t stream) {
+  const int cols = gemm_wide_cols(M, N, gated);
   const int64_t mt = (M + kWM - 1) / kWM;
-  const int64_t nt = gated ? (N / 2 + kWN / 2 - 1) / (kWN / 2) : (N + kWN - 1) / kWN;
+  const int64_t nt = gated ? (N / 2 + cols / 2 - 1) / (cols / 2) : (N + cols - 1) / cols;
   const int64_t per_xcd = (mt * nt + 7) / 8;
   const dim3 grid((unsigned)(per_xcd * 8));
   if (gated)
-    hipLaunchKernelGGL(k_gemm_wide<true>, grid, dim3(256), 0, stream, X, M, qweight, scales, zeros,
-                       N, K, group, Y, mt, nt, per_xcd);
+    hipLaunchKernelGGL((k_gemm_wide<true, 256>), grid, dim3(256), 0, stream, X, M, qweight, scales,
+                       zeros, N, K, group, Y, mt, nt, per_xcd);
+  else if (cols == 256)
+    hipLaunchKernelGGL((k_gemm_wide<false, 256>), grid, dim3(256), 0, stream, X, M, qweight, scales,
+                       zeros, N, K, group, Y, mt, nt, per_xcd);
   else
-    hipLaunchKernelGGL(k_gemm_wide<false>, grid, dim3(256), 0, stream, X, M, qweight, scales, zeros,
-                       N, K, group, Y, mt, nt, per_xcd);
+    hipLaunchKernelGGL((k_gemm_wide<false, 128>), grid, dim3(256), 0, stream, X, M, qweight, scales,
+                       zeros, N, K, group, Y, mt, nt, per_xcd);
   return hipGetLastError();
 }
 
