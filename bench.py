@@ -879,8 +879,8 @@ def main():
                  "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2),
                               "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                               "frac": round(gemm_tflops / FP16_MFMA_PEAK_TFLOPS, 4),
-                              "kernel": "awq::k_gemm_wide (q|k|v, gate|up: 160 tiles or more) and "
-                                        "awq::k_gemm (o, down)"}},
+                              "kernel": "awq::k_gemm_wide (256-row tiles: 256 x 128 for q|k|v, o "
+                                        "and down, 256 x 256 for gate|up)"}},
         "search": {"tflops_algorithmic": round(search_tflops, 2), "ms": round(part_ms["search"], 4),
                    "best_alpha_index": best,
                    "roofline": {"bound": "mfma", "achieved": round(search_tflops, 2),
