@@ -321,7 +321,25 @@ __global__ void __launch_bounds__(256)
 
   // ------------------------------------------------------------------ epilogue
   // 32x32 accumulator layout: element e of lane l is (row 8(e/4) + 4(l/32) + e%4, col l%32).
-  if constexpr (GATED) {
+  // Tiles wholly inside the output store without per-element bounds checks: a lane's rows
+  // are then uniform offsets from its own column pointer.
+  const int64_t ldy = GATED ? nh : N;
+  const bool full = m0 + kBM <= M && n0 + (GATED ? kBN / 2 : kBN) <= ldy;
+  if (full) {
+    uint16_t* yl = Y + (m0 + 4 * kh) * ldy + n0 + wave * (GATED ? 32 : 64) + m32;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t ro = (int64_t)(a * 32 + 8 * (e >> 2) + (e & 3)) * ldy;
+        if constexpr (GATED) {
+          yl[ro] = f2h_bits(silu_f32(acc[a][0][e]) * acc[a][1][e]);
+        } else {
+#pragma unroll
+          for (int b = 0; b < 2; ++b) yl[ro + b * 32] = f2h_bits(acc[a][b][e]);
+        }
+      }
+  } else if constexpr (GATED) {
     const int64_t col = n0 + wave * 32 + m32;
 #pragma unroll
     for (int a = 0; a < 4; ++a)
