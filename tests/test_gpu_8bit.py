@@ -160,9 +160,52 @@ def test_dequant_identity_rows(group):
         X[i, k] = 1.0
     want = np.stack([((q[:, k].astype(np.float64) - z[:, k // group]) * sc[:, k // group].astype(np.float64))
                      for k in ks]).astype(np.float16)
-    for kernel in ("skinny", "gemm"):
+    for kernel in ("skinny", "gemm") + (("gemm_wide",) if group != 32 else ()):
         Y = host(awq.linear_w4a16(to_dev(X), p, kernel=kernel))
         assert np.array_equal(Y.view(np.uint16), want.view(np.uint16)), kernel
     for i0 in range(0, len(ks), 8):
         Y = host(awq.linear_w4a16(to_dev(X[i0:i0 + 8]), p, kernel="gemv"))
         assert np.array_equal(Y.view(np.uint16), want[i0:i0 + 8].view(np.uint16))
+
+
+@pytest.mark.parametrize("M,N,K,group,zp", [
+    (65, 67, 384, 128, True),
+    (256, 300, 1152, 64, True),
+    (257, 256, 4096, 128, False),
+    (300, 1, 128, 128, True),
+    (1000, 1000, 512, 64, False),
+])
+def test_gemm_wide_8bit(M, N, K, group, zp):
+    """The 256-row GEMM on 8-bit codes (128-column tiles): ragged M and N, 1 to 32 steps, both
+    groups it takes, with and without the zero point; bit-identical to the 128-row GEMM (same
+    widening, same MFMA sequence per output), within the linear tolerance of the oracle, and
+    what AUTO runs from M = 128."""
+    W = si.weights(N, K, offset=M + N + K + 31)
+    ref, p = _pack_both(W, group, _s(K, M + 3), zero_point=zp)
+    X = si.activations(M, K, offset=M + 17)
+    out, check = guarded((M, N), torch.float16)
+    Y = host(awq.linear_w4a16(to_dev(X), p, kernel="gemm_wide", out=out))
+    check()
+    Yg = host(awq.linear_w4a16(to_dev(X), p, kernel="gemm"))
+    assert np.array_equal(Y.view(np.uint16), Yg.view(np.uint16))
+    rows = np.r_[np.arange(0, M, 7), M - 1]
+    y_ref, bound = oracle.linear_reference(X[rows], *ref, K)
+    ok = oracle.linear_within_tolerance(Y[rows].astype(np.float64), y_ref, bound)
+    assert ok.all(), np.argwhere(~ok)[:4]
+    if M >= 128:
+        Ya = host(awq.linear_w4a16(to_dev(X), p))
+        assert np.array_equal(Ya.view(np.uint16), Y.view(np.uint16))
+
+
+def test_gemm_wide_8bit_auto_threshold_and_gated():
+    """AUTO keeps the 128-row GEMM below M = 128; the gated epilogue on 8-bit codes stays on the
+    128-row GEMM (an explicit wide request is refused)."""
+    N, K = 256, 512
+    W = si.weights(N, K, offset=91)
+    ref, p = _pack_both(W, 128, _s(K, 92))
+    X = to_dev(si.activations(100, K, offset=93))
+    a = host(awq.linear_w4a16(X, p))
+    e = host(awq.linear_w4a16(X, p, kernel="gemm"))
+    assert np.array_equal(a.view(np.uint16), e.view(np.uint16))
+    with pytest.raises(awq.AwqError):
+        awq.linear_w4a16_gated_silu(X, p, kernel="gemm_wide")

@@ -260,7 +260,7 @@ static awq_status linear_common(const void* X, int64_t M, const uint32_t* qweigh
   if (gated && (N < 2 || N % 2 != 0)) return AWQ_ERR_BAD_SHAPE;
   if (kv < AWQ_LINEAR_AUTO || kv > AWQ_LINEAR_GEMM_WIDE) return AWQ_ERR_UNSUPPORTED;
   awq_linear_kernel kernel = (awq_linear_kernel)kv;
-  if (kernel == AWQ_LINEAR_GEMM_WIDE && !awq::gemm_wide_supported(K, c.group_size, c.w_bit))
+  if (kernel == AWQ_LINEAR_GEMM_WIDE && !awq::gemm_wide_supported(K, c.group_size, c.w_bit, gated))
     return AWQ_ERR_UNSUPPORTED;
   if (kernel == AWQ_LINEAR_GEMV && M > awq::kGemvMaxM) return AWQ_ERR_BAD_SHAPE;
   if (kernel == AWQ_LINEAR_SKINNY && M > awq::kSkinnyMaxM) return AWQ_ERR_BAD_SHAPE;
@@ -277,9 +277,14 @@ static awq_status linear_common(const void* X, int64_t M, const uint32_t* qweigh
   }
   // AUTO, measured on the Llama-2-7B layer: the vector-ALU GEMV up to M = 3 (its dot cost
   // grows with M), the MFMA skinny GEMV up to g_gemv_max_m, the MFMA GEMM above.
-  if (kernel == AWQ_LINEAR_AUTO && c.w_bit != 4)
+  if (kernel == AWQ_LINEAR_AUTO && c.w_bit != 4) {
     kernel = M <= awq::kGemvMaxM ? AWQ_LINEAR_GEMV
              : M <= awq::kSkinnyMaxM ? AWQ_LINEAR_SKINNY : AWQ_LINEAR_GEMM;
+    // 8-bit codes, plain outputs: the 256-row GEMM (128-column tiles) from 128 rows
+    if (kernel == AWQ_LINEAR_GEMM && M >= awq::kWideMinM &&
+        awq::gemm_wide_supported(K, c.group_size, c.w_bit, gated))
+      kernel = AWQ_LINEAR_GEMM_WIDE;
+  }
   if (kernel == AWQ_LINEAR_AUTO) {
     kernel = M <= awq::kVgemvAutoMaxM && M <= g_gemv_max_m ? AWQ_LINEAR_GEMV
              : M <= g_gemv_max_m                            ? AWQ_LINEAR_SKINNY
@@ -288,15 +293,19 @@ static awq_status linear_common(const void* X, int64_t M, const uint32_t* qweigh
     // from 128 rows, where its 128-column tiles already beat the 128-row GEMM on every shape;
     // fused gate|up (256-column tiles only) once it has 160 tiles (ahead from 172, behind at
     // 86 and below, where the 128-row tiles give twice as many CUs work)
-    if (kernel == AWQ_LINEAR_GEMM && awq::gemm_wide_supported(K, c.group_size, c.w_bit) &&
-        (gated ? awq::gemm_wide_tiles(M, N, true) >= awq::kWideMinTilesGated : M >= awq::kWideMinM))
+    if (kernel == AWQ_LINEAR_GEMM && awq::gemm_wide_supported(K, c.group_size, c.w_bit, gated) &&
+        (gated ? awq::gemm_wide_tiles(M, N, true, c.w_bit) >= awq::kWideMinTilesGated
+               : M >= awq::kWideMinM))
       kernel = AWQ_LINEAR_GEMM_WIDE;
   }
   const auto* Xh = (const uint16_t*)X;
   const auto* sc = (const uint16_t*)scales;
   auto* Yh = (uint16_t*)Y;
   if (c.w_bit == 8) {
-    // 8-bit codes: the vector GEMV (M <= 8), the skinny MFMA GEMV (M <= 64), the GEMM
+    // 8-bit codes: the vector GEMV (M <= 8), the skinny MFMA GEMV (M <= 64), the GEMMs
+    if (kernel == AWQ_LINEAR_GEMM_WIDE)
+      return hip_status(awq::launch_gemm_wide(Xh, M, qweight, sc, zeros, N, K, c.group_size, 8, Yh,
+                                              gated, st));
     if (kernel == AWQ_LINEAR_GEMV)
       return hip_status(
           awq::launch_gemv8(Xh, M, qweight, sc, zeros, N, K, c.group_size, Yh, gated, st));
@@ -320,7 +329,7 @@ static awq_status linear_common(const void* X, int64_t M, const uint32_t* qweigh
   switch (kernel) {
     case AWQ_LINEAR_GEMM_WIDE:
       return hip_status(
-          awq::launch_gemm_wide(Xh, M, qweight, sc, zeros, N, K, c.group_size, Yh, gated, st));
+          awq::launch_gemm_wide(Xh, M, qweight, sc, zeros, N, K, c.group_size, 4, Yh, gated, st));
     case AWQ_LINEAR_GEMV:
       return hip_status(
           awq::launch_gemv(Xh, M, qweight, sc, zeros, N, K, c.group_size, Yh, gated, st));

@@ -73,18 +73,33 @@ __device__ __forceinline__ half8w widen_word(uint32_t w, half2w zz, half2w zz64,
   return half8w{d0[0], d0[1], d1[0], d1[1], d2[0], d2[1], d3[0], d3[1]};
 }
 
-template <bool GATED, int WN>
+// Two packed 8-bit words -> their 8 channels (q - z) sc, in channel order: v_perm_b32 against
+// 0x64646464 puts byte pairs under the 0x64 exponent byte, (1024 + a, 1024 + b) exactly; zz holds
+// -(1024 + z) in both halves.
+__device__ __forceinline__ half8w widen_word8(uint32_t w0, uint32_t w1, half2w zz, half2w s2,
+                                              uint32_t magic8) {
+  const half2w d0 = (__builtin_bit_cast(half2w, __builtin_amdgcn_perm(magic8, w0, 0x04010400u)) + zz) * s2;
+  const half2w d1 = (__builtin_bit_cast(half2w, __builtin_amdgcn_perm(magic8, w0, 0x04030402u)) + zz) * s2;
+  const half2w d2 = (__builtin_bit_cast(half2w, __builtin_amdgcn_perm(magic8, w1, 0x04010400u)) + zz) * s2;
+  const half2w d3 = (__builtin_bit_cast(half2w, __builtin_amdgcn_perm(magic8, w1, 0x04030402u)) + zz) * s2;
+  return half8w{d0[0], d0[1], d1[0], d1[1], d2[0], d2[1], d3[0], d3[1]};
+}
+
+template <bool GATED, int WN, int BITS>
 __global__ void __launch_bounds__(256)
     k_gemm_wide(const uint16_t* X, int64_t M, const uint32_t* qweight, const uint16_t* scales,
                 const uint8_t* zeros, int64_t N, int64_t K, int group, uint16_t* __restrict__ Y,
                 int64_t mt, int64_t nt, int64_t per_xcd) {
   __shared__ __attribute__((aligned(16))) uint4 a0s[kWM * 16];
   __shared__ __attribute__((aligned(16))) uint4 a1s[kWM * 16];
-  static_assert(WN == 256 || (WN == 128 && !GATED), "tile widths");
-  constexpr int kCT = WN / 128;  // a wave's 32 x 32 MFMA tiles along columns
-  constexpr int kBT = WN / 64;   // B transfers per wave and step
-  __shared__ __attribute__((aligned(16))) uint4 b0s[WN * 4];
-  __shared__ __attribute__((aligned(16))) uint4 b1s[WN * 4];
+  static_assert((BITS == 4 && (WN == 256 || (WN == 128 && !GATED))) ||
+                    (BITS == 8 && WN == 128 && !GATED),
+                "tile widths: 8-bit codes fill LDS at 128 columns");
+  constexpr int kCT = WN / 128;         // a wave's 32 x 32 MFMA tiles along columns
+  constexpr int kQ = BITS;              // 16-byte quarters of a column's 16 BITS code bytes per step
+  constexpr int kBT = WN * kQ / 256;    // B transfers per wave and step
+  __shared__ __attribute__((aligned(16))) uint4 b0s[WN * kQ];
+  __shared__ __attribute__((aligned(16))) uint4 b1s[WN * kQ];
   // tile t: XCD blockIdx % 8 takes tiles [per_xcd (blockIdx % 8), +per_xcd); within a group
   // of kGroupRows row tiles the row index moves fastest
   const int64_t t = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
@@ -98,9 +113,12 @@ __global__ void __launch_bounds__(256)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m32 = lane & 31, kh = lane >> 5;
   const int g64 = group == 64;
-  const int64_t Gs = K / group, zbw = (Gs + 1) / 2, words = K / 8;
+  // zeros: 4-bit, two nibbles per byte; 8-bit, one byte per group
+  const int64_t Gs = K / group, zbw = BITS == 8 ? Gs : (Gs + 1) / 2, words = K * BITS / 32;
   const int64_t nsteps = K / kWK;
   const uint32_t magic = wide_magic();
+  uint32_t magic8 = 0;
+  if constexpr (BITS == 8) asm volatile("v_mov_b32 %0, 0x64646464" : "=v"(magic8));
 
   // A DMA map: wave transfer i (0..15) fills slots (wave * 16 + i) * 64 + lane of the buffer:
   // row r = (wave * 16 + i) * 4 + lane / 16, slot lane % 16 <- chunk (lane % 16) ^ (r % 16).
@@ -115,7 +133,7 @@ __global__ void __launch_bounds__(256)
     aoff[i] = (uint32_t)(gr * K + ((lane & 15) ^ (r & 15)) * 8);
   }
   // B DMA map, quarter-major: slot (wave * kBT + i) * 64 + lane = 16-byte quarter q (slot /
-  // WN) of tile column c (slot % WN) of the columns' 64 code bytes of a step, so a wave's
+  // WN) of tile column c (slot % WN) of the columns' 16 kQ code bytes of a step, so a wave's
   // read of one quarter of 32 consecutive columns is 512 contiguous bytes (no bank
   // conflicts). Gated: tile columns [64 w, 64 w + 32) hold the gate rows and [64 w + 32,
   // 64 w + 64) the up rows of outputs n0 + 32 w .. n0 + 32 w + 31. Columns past the end
@@ -154,7 +172,7 @@ __global__ void __launch_bounds__(256)
   auto load_sz = [&](ScaleZero& st, int64_t step) {
 #pragma unroll
     for (int b = 0; b < kCT; ++b) {
-      st.zb[b] = zeros[bcol[b] * zbw + (step >> (1 - g64))];
+      st.zb[b] = zeros[bcol[b] * zbw + (BITS == 8 ? (step << g64) + (g64 & kh) : step >> (1 - g64))];
       st.sc[b] = scales[bcol[b] * Gs + (step << g64) + (g64 & kh)];
     }
   };
@@ -193,26 +211,27 @@ __global__ void __launch_bounds__(256)
                                        (lds_void*)&adn[(wave * 16 + i) * 64], 16, 0, 0);
     };
     auto dma_b = [&](int i) {
-      __builtin_amdgcn_global_load_lds((const void*)(bptr[i] + sn * 16),
+      __builtin_amdgcn_global_load_lds((const void*)(bptr[i] + sn * (kQ * 4)),
                                        (lds_void*)&bdn[(wave * kBT + i) * 64], 16, 0, 0);
     };
     half2w zz[kCT], zz64[kCT], s2[kCT];
     const int hi = g64 ? kh : (int)(step & 1);  // zero nibble: group of 128 (step) or 64 (2 step + kh)
 #pragma unroll
     for (int b = 0; b < kCT; ++b) {
-      const uint32_t z = hi ? (cur.zb[b] >> 4) : (cur.zb[b] & 0xF);
+      const uint32_t z = BITS == 8 ? cur.zb[b] : hi ? (cur.zb[b] >> 4) : (cur.zb[b] & 0xF);
       const uint32_t z1024 = 0x6400u + z, z64 = 0x5400u + (z << 4);
       zz[b] = -__builtin_bit_cast(half2w, z1024 | (z1024 << 16));
       zz64[b] = -__builtin_bit_cast(half2w, z64 | (z64 << 16));
       s2[b] = __builtin_bit_cast(half2w, cur.sc[b] | (cur.sc[b] << 16));
     }
-    // this lane's code words of the step: words 8 kh .. 8 kh + 7 of each of its columns,
-    // quarters 2 kh and 2 kh + 1 (one 16-byte read each)
-    uint4 bq[kCT][2];
+    // this lane's code words of the step: words 2 kQ kh .. of each of its columns, the
+    // quarters kQ / 2 kh .. kQ / 2 kh + kQ / 2 - 1 (one 16-byte read each)
+    uint4 bq[kCT][kQ / 2];
 #pragma unroll
     for (int b = 0; b < kCT; ++b)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) bq[b][h] = bb[(2 * kh + h) * WN + wave * kCT * 32 + b * 32 + m32];
+      for (int h = 0; h < kQ / 2; ++h)
+        bq[b][h] = bb[(kQ / 2 * kh + h) * WN + wave * kCT * 32 + b * 32 + m32];
     auto frags = [&](int s, half8w (&A)[kRT], half8w (&B)[kCT]) {
       const int c = kh * 8 + s;
 #pragma unroll
@@ -222,9 +241,16 @@ __global__ void __launch_bounds__(256)
       }
 #pragma unroll
       for (int b = 0; b < kCT; ++b) {
-        const uint4 q = bq[b][s >> 2];
-        const uint32_t w = (s & 3) == 0 ? q.x : (s & 3) == 1 ? q.y : (s & 3) == 2 ? q.z : q.w;
-        B[b] = widen_word(w, zz[b], zz64[b], s2[b], magic);
+        if constexpr (BITS == 8) {
+          // slice s: words 2 s, 2 s + 1 of the lane half's 16
+          const uint4 q = bq[b][s >> 1];
+          B[b] = (s & 1) ? widen_word8(q.z, q.w, zz[b], s2[b], magic8)
+                         : widen_word8(q.x, q.y, zz[b], s2[b], magic8);
+        } else {
+          const uint4 q = bq[b][s >> 2];
+          const uint32_t w = (s & 3) == 0 ? q.x : (s & 3) == 1 ? q.y : (s & 3) == 2 ? q.z : q.w;
+          B[b] = widen_word(w, zz[b], zz64[b], s2[b], magic);
+        }
       }
     };
     half8w A0[kRT], B0[kCT], A1[kRT], B1[kCT];
@@ -306,9 +332,11 @@ __global__ void __launch_bounds__(256)
 }  // namespace
 
 // Tile width for an M x N output: 128 columns when whole waves of those tiles keep more of
-// the 256 CUs busy than 256-column tiles do (ties go to 256); gated outputs always 256.
-int gemm_wide_cols(int64_t M, int64_t N, bool gated) {
+// the 256 CUs busy than 256-column tiles do (ties go to 256); gated outputs always 256,
+// 8-bit codes always 128 (256 columns of them would not fit LDS with the A tile).
+int gemm_wide_cols(int64_t M, int64_t N, bool gated, int w_bit) {
   if (gated) return 256;
+  if (w_bit == 8) return 128;
   const int64_t mt = (M + kWM - 1) / kWM;
   const int64_t t256 = mt * ((N + 255) / 256), t128 = mt * ((N + 127) / 128);
   const int64_t w256 = (t256 + 255) / 256, w128 = (t128 + 255) / 256;  // waves of tiles
@@ -316,34 +344,39 @@ int gemm_wide_cols(int64_t M, int64_t N, bool gated) {
   return t128 * w256 > t256 * w128 ? 128 : 256;
 }
 
-int64_t gemm_wide_tiles(int64_t M, int64_t N, bool gated) {
+int64_t gemm_wide_tiles(int64_t M, int64_t N, bool gated, int w_bit) {
   const int64_t mt = (M + kWM - 1) / kWM;
-  const int cols = gemm_wide_cols(M, N, gated);
+  const int cols = gemm_wide_cols(M, N, gated, w_bit);
   const int64_t nt = gated ? (N / 2 + cols / 2 - 1) / (cols / 2) : (N + cols - 1) / cols;
   return mt * nt;
 }
 
-bool gemm_wide_supported(int64_t K, int group, int w_bit) {
-  return w_bit == 4 && (group == 128 || group == 64) && (int64_t)kWM * K < ((int64_t)1 << 32);
+bool gemm_wide_supported(int64_t K, int group, int w_bit, bool gated) {
+  return (w_bit == 4 || (w_bit == 8 && !gated)) && (group == 128 || group == 64) &&
+         (int64_t)kWM * K < ((int64_t)1 << 32);
 }
 
 hipError_t launch_gemm_wide(const uint16_t* X, int64_t M, const uint32_t* qweight,
                             const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
-                            int group, uint16_t* Y, bool gated, hipStream_t stream) {
-  const int cols = gemm_wide_cols(M, N, gated);
+                            int group, int w_bit, uint16_t* Y, bool gated, hipStream_t stream) {
+  if (!gemm_wide_supported(K, group, w_bit, gated)) return hipErrorInvalidValue;
+  const int cols = gemm_wide_cols(M, N, gated, w_bit);
   const int64_t mt = (M + kWM - 1) / kWM;
   const int64_t nt = gated ? (N / 2 + cols / 2 - 1) / (cols / 2) : (N + cols - 1) / cols;
   const int64_t per_xcd = (mt * nt + 7) / 8;
   const dim3 grid((unsigned)(per_xcd * 8));
-  if (gated)
-    hipLaunchKernelGGL((k_gemm_wide<true, 256>), grid, dim3(256), 0, stream, X, M, qweight, scales,
-                       zeros, N, K, group, Y, mt, nt, per_xcd);
+  if (w_bit == 8)
+    hipLaunchKernelGGL((k_gemm_wide<false, 128, 8>), grid, dim3(256), 0, stream, X, M, qweight,
+                       scales, zeros, N, K, group, Y, mt, nt, per_xcd);
+  else if (gated)
+    hipLaunchKernelGGL((k_gemm_wide<true, 256, 4>), grid, dim3(256), 0, stream, X, M, qweight,
+                       scales, zeros, N, K, group, Y, mt, nt, per_xcd);
   else if (cols == 256)
-    hipLaunchKernelGGL((k_gemm_wide<false, 256>), grid, dim3(256), 0, stream, X, M, qweight, scales,
-                       zeros, N, K, group, Y, mt, nt, per_xcd);
+    hipLaunchKernelGGL((k_gemm_wide<false, 256, 4>), grid, dim3(256), 0, stream, X, M, qweight,
+                       scales, zeros, N, K, group, Y, mt, nt, per_xcd);
   else
-    hipLaunchKernelGGL((k_gemm_wide<false, 128>), grid, dim3(256), 0, stream, X, M, qweight, scales,
-                       zeros, N, K, group, Y, mt, nt, per_xcd);
+    hipLaunchKernelGGL((k_gemm_wide<false, 128, 4>), grid, dim3(256), 0, stream, X, M, qweight,
+                       scales, zeros, N, K, group, Y, mt, nt, per_xcd);
   return hipGetLastError();
 }
 

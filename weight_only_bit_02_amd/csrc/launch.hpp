@@ -87,16 +87,17 @@ hipError_t launch_gemm(const uint16_t* X, int64_t M, const uint32_t* qweight,
                        const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
                        int group, int w_bit, uint16_t* Y, bool gated, hipStream_t stream);
 
-// a8, 4-bit codes with 128- or 64-channel groups: the GEMM with 256-row tiles (256 or 128
-// columns) and one wave per SIMD (gemm_wide.hip). gemm_wide_supported: the configs and sizes
-// it takes; gemm_wide_tiles: its tile count for an M x N output (gated: N / 2 outputs).
-bool gemm_wide_supported(int64_t K, int group, int w_bit);
-int64_t gemm_wide_tiles(int64_t M, int64_t N, bool gated);
+// a8, 4-bit codes (and 8-bit codes, plain outputs) with 128- or 64-channel groups: the GEMM
+// with 256-row tiles (256 or 128 columns) and one wave per SIMD (gemm_wide.hip).
+// gemm_wide_supported: the configs and sizes it takes; gemm_wide_tiles: its tile count for an
+// M x N output (gated: N / 2 outputs).
+bool gemm_wide_supported(int64_t K, int group, int w_bit, bool gated);
+int64_t gemm_wide_tiles(int64_t M, int64_t N, bool gated, int w_bit);
 constexpr int64_t kWideMinM = 128;         // AUTO: the wide GEMM from 128 rows (plain output)
 constexpr int64_t kWideMinTilesGated = 160;  // and from 160 tiles (fused gate|up)
 hipError_t launch_gemm_wide(const uint16_t* X, int64_t M, const uint32_t* qweight,
                             const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
-                            int group, uint16_t* Y, bool gated, hipStream_t stream);
+                            int group, int w_bit, uint16_t* Y, bool gated, hipStream_t stream);
 
 // Data conditions of the linear path: OR AWQ_FLAG_NONFINITE_INPUT into *flags when a
 // (n fp16 values, n % 8 == 0) or b (m fp16 values) holds an Inf or a NaN.
