@@ -165,7 +165,7 @@ def test_dequant_identity_rows(group):
         X[i, k] = 1.0
     want = np.stack([((q[:, k].astype(np.float64) - z[:, k // group]) * sc[:, k // group].astype(np.float64))
                      for k in ks]).astype(np.float16)
-    for kernel in ("skinny", "gemm"):
+    for kernel in ("skinny", "gemm") + (("gemm_wide",) if group != 32 else ()):
         Y = host(awq.linear_w4a16(to_dev(X), p, kernel=kernel))
         assert np.array_equal(Y.view(np.uint16), want.view(np.uint16)), kernel
     for i0 in range(0, len(ks), 8):
@@ -174,3 +174,49 @@ def test_dequant_identity_rows(group):
     for i in range(len(ks)):  # one token: the single-token kernel
         Y = host(awq.linear_w4a16(to_dev(X[i:i + 1]), p, kernel="gemv"))
         assert np.array_equal(Y.view(np.uint16), want[i:i + 1].view(np.uint16))
+
+
+@pytest.mark.parametrize("M,N,K,group,zp", [
+    (65, 67, 384, 128, True),
+    (256, 300, 1152, 64, True),
+    (257, 256, 4096, 128, False),
+    (300, 1, 128, 128, True),
+    (1000, 1000, 512, 64, False),
+])
+def test_gemm_wide_3bit(M, N, K, group, zp):
+    """The 256-row GEMM on 3-bit codes (256-column tiles): ragged M and N, 1 to 32 steps, both
+    groups it takes, with and without the zero point; bit-identical to the 128-row GEMM (same
+    two-plane widening, same MFMA sequence per output), within the linear tolerance of the
+    oracle, and what AUTO runs from M = 128."""
+    W = si.weights(N, K, offset=M + N + K + 37)
+    ref, p = _pack_both(W, group, _s(K, M + 3), zero_point=zp)
+    X = si.activations(M, K, offset=M + 19)
+    out, check = guarded((M, N), torch.float16)
+    Y = host(awq.linear_w4a16(to_dev(X), p, kernel="gemm_wide", out=out))
+    check()
+    Yg = host(awq.linear_w4a16(to_dev(X), p, kernel="gemm"))
+    assert np.array_equal(Y.view(np.uint16), Yg.view(np.uint16))
+    rows = np.r_[np.arange(0, M, 7), M - 1]
+    y_ref, bound = oracle.linear_reference(X[rows], *ref, K)
+    ok = oracle.linear_within_tolerance(Y[rows].astype(np.float64), y_ref, bound)
+    assert ok.all(), np.argwhere(~ok)[:4]
+    if M >= 128:
+        Ya = host(awq.linear_w4a16(to_dev(X), p))
+        assert np.array_equal(Ya.view(np.uint16), Y.view(np.uint16))
+
+
+@pytest.mark.parametrize("M,nh,group", [(70, 67, 128), (513, 130, 64)])
+def test_gemm_wide_3bit_gated(M, nh, group):
+    """Fused gate|up on 3-bit codes through the 256-row GEMM: a partial column tile of outputs,
+    against the oracle and bit-identical to the 128-row GEMM."""
+    K = 1152
+    W = si.weights(2 * nh, K, offset=M + nh + 41)
+    ref, p = _pack_both(W, group, _s(K, M + 4))
+    X = si.activations(M, K, offset=M + 23)
+    out, check = guarded((M, nh), torch.float16)
+    H = host(awq.linear_w4a16_gated_silu(to_dev(X), p, kernel="gemm_wide", out=out))
+    check()
+    H1 = host(awq.linear_w4a16_gated_silu(to_dev(X), p, kernel="gemm"))
+    assert np.array_equal(H.view(np.uint16), H1.view(np.uint16))
+    h, g, u, bg, bu = oracle.gated_silu_reference(X, *ref, K)
+    assert oracle.gated_silu_within_tolerance(H, g, u, bg, bu).all()

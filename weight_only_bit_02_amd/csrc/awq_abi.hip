@@ -280,9 +280,11 @@ static awq_status linear_common(const void* X, int64_t M, const uint32_t* qweigh
   if (kernel == AWQ_LINEAR_AUTO && c.w_bit != 4) {
     kernel = M <= awq::kGemvMaxM ? AWQ_LINEAR_GEMV
              : M <= awq::kSkinnyMaxM ? AWQ_LINEAR_SKINNY : AWQ_LINEAR_GEMM;
-    // 8-bit codes, plain outputs: the 256-row GEMM (128-column tiles) from 128 rows
-    if (kernel == AWQ_LINEAR_GEMM && M >= awq::kWideMinM &&
-        awq::gemm_wide_supported(K, c.group_size, c.w_bit, gated))
+    // the 256-row GEMM where it takes the format (8-bit: plain outputs on 128-column tiles;
+    // 3-bit: 256-column tiles), by the 4-bit rule below
+    if (kernel == AWQ_LINEAR_GEMM && awq::gemm_wide_supported(K, c.group_size, c.w_bit, gated) &&
+        (gated ? awq::gemm_wide_tiles(M, N, true, c.w_bit) >= awq::kWideMinTilesGated
+               : M >= awq::kWideMinM))
       kernel = AWQ_LINEAR_GEMM_WIDE;
   }
   if (kernel == AWQ_LINEAR_AUTO) {
@@ -316,7 +318,10 @@ static awq_status linear_common(const void* X, int64_t M, const uint32_t* qweigh
         awq::launch_gemm(Xh, M, qweight, sc, zeros, N, K, c.group_size, 8, Yh, gated, st));
   }
   if (c.w_bit == 3) {
-    // 3-bit codes: the same three kernels' 3-bit forms, with the same thresholds
+    // 3-bit codes: the same kernels' 3-bit forms, with the same thresholds
+    if (kernel == AWQ_LINEAR_GEMM_WIDE)
+      return hip_status(awq::launch_gemm_wide(Xh, M, qweight, sc, zeros, N, K, c.group_size, 3, Yh,
+                                              gated, st));
     if (kernel == AWQ_LINEAR_GEMV)
       return hip_status(
           awq::launch_gemv3(Xh, M, qweight, sc, zeros, N, K, c.group_size, Yh, gated, st));

@@ -85,6 +85,18 @@ __device__ __forceinline__ half8w widen_word8(uint32_t w0, uint32_t w1, half2w z
   return half8w{d0[0], d0[1], d1[0], d1[1], d2[0], d2[1], d3[0], d3[1]};
 }
 
+// Four channel pairs of 3-bit codes -> 8 channels (q - z) sc: pair t takes its low bits from
+// field f + t of the low-plane word and bit 2 from bit p + t of the high-plane word (both in
+// each 16-bit half), under the 0x6400 exponent: exactly (1024 + q, 1024 + q').
+__device__ __forceinline__ half8w widen_word3(uint32_t lo, uint32_t hi, int f, int p, half2w zz,
+                                              half2w s2, uint32_t magic) {
+  half2w d[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    d[t] = (__builtin_bit_cast(half2w, widen3_pair(lo, hi, f + t, p + t, magic)) + zz) * s2;
+  return half8w{d[0][0], d[0][1], d[1][0], d[1][1], d[2][0], d[2][1], d[3][0], d[3][1]};
+}
+
 template <bool GATED, int WN, int BITS>
 __global__ void __launch_bounds__(256)
     k_gemm_wide(const uint16_t* X, int64_t M, const uint32_t* qweight, const uint16_t* scales,
@@ -93,8 +105,8 @@ __global__ void __launch_bounds__(256)
   __shared__ __attribute__((aligned(16))) uint4 a0s[kWM * 16];
   __shared__ __attribute__((aligned(16))) uint4 a1s[kWM * 16];
   static_assert((BITS == 4 && (WN == 256 || (WN == 128 && !GATED))) ||
-                    (BITS == 8 && WN == 128 && !GATED),
-                "tile widths: 8-bit codes fill LDS at 128 columns");
+                    (BITS == 8 && WN == 128 && !GATED) || (BITS == 3 && WN == 256),
+                "tile widths: 8-bit codes fill LDS at 128 columns; 3-bit codes take 256");
   constexpr int kCT = WN / 128;         // a wave's 32 x 32 MFMA tiles along columns
   constexpr int kQ = BITS;              // 16-byte quarters of a column's 16 BITS code bytes per step
   constexpr int kBT = WN * kQ / 256;    // B transfers per wave and step
@@ -224,14 +236,25 @@ __global__ void __launch_bounds__(256)
       zz64[b] = -__builtin_bit_cast(half2w, z64 | (z64 << 16));
       s2[b] = __builtin_bit_cast(half2w, cur.sc[b] | (cur.sc[b] << 16));
     }
-    // this lane's code words of the step: words 2 kQ kh .. of each of its columns, the
-    // quarters kQ / 2 kh .. kQ / 2 kh + kQ / 2 - 1 (one 16-byte read each)
-    uint4 bq[kCT][kQ / 2];
+    // this lane's code words of the step, per column: 4- and 8-bit, words 2 kQ kh .., the
+    // quarters kQ / 2 kh .. kQ / 2 kh + kQ / 2 - 1 (one 16-byte read each); 3-bit, low-plane
+    // words 4 kh .. 4 kh + 3 (quarter kh) and high-plane words 8 + 2 kh, 9 + 2 kh (half of
+    // quarter 2)
+    constexpr int kQL = BITS == 3 ? 1 : kQ / 2;
+    uint4 bq[kCT][kQL];
+    uint2 bh[kCT];
 #pragma unroll
-    for (int b = 0; b < kCT; ++b)
+    for (int b = 0; b < kCT; ++b) {
+      const int col = wave * kCT * 32 + b * 32 + m32;
+      if constexpr (BITS == 3) {
+        bq[b][0] = bb[kh * WN + col];
+        const uint4 h4 = bb[2 * WN + col];
+        bh[b] = kh ? make_uint2(h4.z, h4.w) : make_uint2(h4.x, h4.y);
+      } else {
 #pragma unroll
-      for (int h = 0; h < kQ / 2; ++h)
-        bq[b][h] = bb[(kQ / 2 * kh + h) * WN + wave * kCT * 32 + b * 32 + m32];
+        for (int h = 0; h < kQL; ++h) bq[b][h] = bb[(kQL * kh + h) * WN + col];
+      }
+    }
     auto frags = [&](int s, half8w (&A)[kRT], half8w (&B)[kCT]) {
       const int c = kh * 8 + s;
 #pragma unroll
@@ -246,6 +269,13 @@ __global__ void __launch_bounds__(256)
           const uint4 q = bq[b][s >> 1];
           B[b] = (s & 1) ? widen_word8(q.z, q.w, zz[b], s2[b], magic8)
                          : widen_word8(q.x, q.y, zz[b], s2[b], magic8);
+        } else if constexpr (BITS == 3) {
+          // slice s = channel pairs 4 s .. 4 s + 3 of the half: low word s / 2 (fields
+          // 4 (s % 2) ..), high word s / 4 (bits 4 (s % 4) ..)
+          const uint4 q = bq[b][0];
+          const uint32_t lo = (s >> 1) == 0 ? q.x : (s >> 1) == 1 ? q.y : (s >> 1) == 2 ? q.z : q.w;
+          const uint32_t hiw = (s >> 2) ? bh[b].y : bh[b].x;
+          B[b] = widen_word3(lo, hiw, 4 * (s & 1), 4 * (s & 3), zz[b], s2[b], magic);
         } else {
           const uint4 q = bq[b][s >> 2];
           const uint32_t w = (s & 3) == 0 ? q.x : (s & 3) == 1 ? q.y : (s & 3) == 2 ? q.z : q.w;
@@ -332,10 +362,10 @@ __global__ void __launch_bounds__(256)
 }  // namespace
 
 // Tile width for an M x N output: 128 columns when whole waves of those tiles keep more of
-// the 256 CUs busy than 256-column tiles do (ties go to 256); gated outputs always 256,
-// 8-bit codes always 128 (256 columns of them would not fit LDS with the A tile).
+// the 256 CUs busy than 256-column tiles do (ties go to 256); gated outputs and 3-bit codes
+// always 256, 8-bit codes always 128 (256 columns of them would not fit LDS with the A tile).
 int gemm_wide_cols(int64_t M, int64_t N, bool gated, int w_bit) {
-  if (gated) return 256;
+  if (gated || w_bit == 3) return 256;
   if (w_bit == 8) return 128;
   const int64_t mt = (M + kWM - 1) / kWM;
   const int64_t t256 = mt * ((N + 255) / 256), t128 = mt * ((N + 127) / 128);
@@ -352,7 +382,7 @@ int64_t gemm_wide_tiles(int64_t M, int64_t N, bool gated, int w_bit) {
 }
 
 bool gemm_wide_supported(int64_t K, int group, int w_bit, bool gated) {
-  return (w_bit == 4 || (w_bit == 8 && !gated)) && (group == 128 || group == 64) &&
+  return (w_bit == 4 || w_bit == 3 || (w_bit == 8 && !gated)) && (group == 128 || group == 64) &&
          (int64_t)kWM * K < ((int64_t)1 << 32);
 }
 
@@ -367,6 +397,12 @@ hipError_t launch_gemm_wide(const uint16_t* X, int64_t M, const uint32_t* qweigh
   const dim3 grid((unsigned)(per_xcd * 8));
   if (w_bit == 8)
     hipLaunchKernelGGL((k_gemm_wide<false, 128, 8>), grid, dim3(256), 0, stream, X, M, qweight,
+                       scales, zeros, N, K, group, Y, mt, nt, per_xcd);
+  else if (w_bit == 3 && gated)
+    hipLaunchKernelGGL((k_gemm_wide<true, 256, 3>), grid, dim3(256), 0, stream, X, M, qweight,
+                       scales, zeros, N, K, group, Y, mt, nt, per_xcd);
+  else if (w_bit == 3)
+    hipLaunchKernelGGL((k_gemm_wide<false, 256, 3>), grid, dim3(256), 0, stream, X, M, qweight,
                        scales, zeros, N, K, group, Y, mt, nt, per_xcd);
   else if (gated)
     hipLaunchKernelGGL((k_gemm_wide<true, 256, 4>), grid, dim3(256), 0, stream, X, M, qweight,
