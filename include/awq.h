@@ -91,8 +91,8 @@ typedef enum awq_linear_kernel {
   AWQ_LINEAR_SKINNY = 3, /* MFMA GEMV for small batches, split K (M <= 64)    */
   AWQ_LINEAR_GEMM_WIDE = 4 /* MFMA dequant-GEMM on 256-row tiles, one wave per SIMD
                               (4- and 3-bit codes, or 8-bit codes without the
-                              gated epilogue; 128- or 64-channel groups;
-                              256 K < 2^32; else AWQ_ERR_UNSUPPORTED); AUTO takes
+                              gated epilogue; any group size; 256 K < 2^32;
+                              else AWQ_ERR_UNSUPPORTED); AUTO takes
                               it over the GEMM from M = 128 (fused gate|up: from
                               160 tiles of 128 outputs)                        */
 } awq_linear_kernel;

@@ -92,8 +92,6 @@ int main() {
   EXPECT(awq_linear_w4a16_ex(F, 9, Fu, F, Fb, 64, 256, cfg, F, nullptr, AWQ_LINEAR_GEMV, nullptr), AWQ_ERR_BAD_SHAPE);
   EXPECT(awq_linear_w4a16_ex(F, 65, Fu, F, Fb, 64, 256, cfg, F, nullptr, AWQ_LINEAR_SKINNY, nullptr), AWQ_ERR_BAD_SHAPE);
   EXPECT(awq_linear_w4a16_ex(F, 4, Fu, F, Fb, 64, 256, cfg, F, nullptr, (awq_linear_kernel)5, nullptr), AWQ_ERR_UNSUPPORTED);
-  *bad = awq_config{8, 32, 1, 20};
-  EXPECT(awq_linear_w4a16_ex(F, 512, Fu, F, Fb, 64, 256, bad, F, nullptr, AWQ_LINEAR_GEMM_WIDE, nullptr), AWQ_ERR_UNSUPPORTED);
   *bad = awq_config{8, 128, 1, 20};
   EXPECT(awq_linear_w4a16_gated_silu_ex(F, 512, Fu, F, Fb, 64, 256, bad, F, nullptr, AWQ_LINEAR_GEMM_WIDE, nullptr), AWQ_ERR_UNSUPPORTED);
   EXPECT(awq_linear_w4a16_gated_silu(F, 1, Fu, F, Fb, 65, 256, cfg, F, nullptr, nullptr), AWQ_ERR_BAD_SHAPE);

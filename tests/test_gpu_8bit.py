@@ -160,7 +160,7 @@ def test_dequant_identity_rows(group):
         X[i, k] = 1.0
     want = np.stack([((q[:, k].astype(np.float64) - z[:, k // group]) * sc[:, k // group].astype(np.float64))
                      for k in ks]).astype(np.float16)
-    for kernel in ("skinny", "gemm") + (("gemm_wide",) if group != 32 else ()):
+    for kernel in ("skinny", "gemm", "gemm_wide"):
         Y = host(awq.linear_w4a16(to_dev(X), p, kernel=kernel))
         assert np.array_equal(Y.view(np.uint16), want.view(np.uint16)), kernel
     for i0 in range(0, len(ks), 8):
@@ -174,10 +174,12 @@ def test_dequant_identity_rows(group):
     (257, 256, 4096, 128, False),
     (300, 1, 128, 128, True),
     (1000, 1000, 512, 64, False),
+    (129, 200, 1152, 32, True),
+    (512, 256, 512, 32, False),
 ])
 def test_gemm_wide_8bit(M, N, K, group, zp):
-    """The 256-row GEMM on 8-bit codes (128-column tiles): ragged M and N, 1 to 32 steps, both
-    groups it takes, with and without the zero point; bit-identical to the 128-row GEMM (same
+    """The 256-row GEMM on 8-bit codes (128-column tiles): ragged M and N, 1 to 32 steps, 128-,
+    64- and 32-channel groups, with and without the zero point; bit-identical to the 128-row GEMM (same
     widening, same MFMA sequence per output), within the linear tolerance of the oracle, and
     what AUTO runs from M = 128."""
     W = si.weights(N, K, offset=M + N + K + 31)

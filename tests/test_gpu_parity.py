@@ -393,3 +393,32 @@ def test_gemm_wide_256_column_tiles_ragged(M, N, group):
     rows = np.r_[np.arange(0, M, 131), M - 1]
     y_ref, bound = oracle.linear_reference(host(X)[rows], qw, sc, zb, K)
     assert oracle.linear_within_tolerance(a[rows].astype(np.float64), y_ref, bound).all()
+
+
+@pytest.mark.parametrize("M,N,K,gated", [(65, 67, 384, False), (300, 300, 1152, False),
+                                          (513, 256, 512, False), (257, 134, 1152, True)])
+def test_gemm_wide_32_channel_groups(M, N, K, gated):
+    """32-channel groups through the 256-row GEMM (two scales and zero nibbles per lane half
+    and step): plain and fused gate|up, ragged shapes, bit-identical to the 128-row GEMM and
+    within the linear tolerance of the oracle; what AUTO runs from M = 128 (gated: from 160
+    tiles, so the 128-row GEMM here)."""
+    W = si.weights(N, K, offset=M + N + 5)
+    qw, sc, zb, _ = oracle.quantize_pack(W, None, None, True, 32, 4)
+    p = awq.quantize_pack(to_dev(W), group_size=32)
+    X = si.activations(M, K, offset=M + 29)
+    fn = awq.linear_w4a16_gated_silu if gated else awq.linear_w4a16
+    out, check = guarded((M, N // 2 if gated else N), torch.float16)
+    Y = host(fn(to_dev(X), p, kernel="gemm_wide", out=out))
+    check()
+    Yg = host(fn(to_dev(X), p, kernel="gemm"))
+    assert np.array_equal(Y.view(np.uint16), Yg.view(np.uint16))
+    if gated:
+        h, g, u, bg, bu = oracle.gated_silu_reference(X, qw, sc, zb, K)
+        assert oracle.gated_silu_within_tolerance(Y, g, u, bg, bu).all()
+    else:
+        y_ref, bound = oracle.linear_reference(X, qw, sc, zb, K)
+        assert oracle.linear_within_tolerance(Y.astype(np.float64), y_ref, bound).all()
+        if M >= 128:
+            Ya = host(awq.linear_w4a16(to_dev(X), p))
+            assert np.array_equal(Ya.view(np.uint16), Y.view(np.uint16))
+

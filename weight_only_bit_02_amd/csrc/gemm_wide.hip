@@ -1,11 +1,13 @@
-// MFMA dequant-GEMM with 256-row tiles and one wave per SIMD (a8, 4-bit codes with 128- or
-// 64-channel groups): Y[M][N] = X[M][K] deq(W)^T for batches of 128 rows and more.
+// MFMA dequant-GEMM with 256-row tiles and one wave per SIMD (a8; 4- and 3-bit codes, and
+// 8-bit codes without the gated epilogue; 128-, 64- or 32-channel groups): Y[M][N] =
+// X[M][K] deq(W)^T for batches of 128 rows and more.
 //
 // "AWQ量化技术Skill", "主要功能和特点": a GEMM kernel serves batch sizes above one;
 // "AWQ量化实战" §2.3 / §3.4: weights stay 4-bit in memory and are dequantized on the fly.
 //
 // Block = 4 waves (one per SIMD), tile 256 (tokens) x WN (output channels, 256 or 128), K
-// step 128 (one group of 128, or two of 64: a lane half's 64 channels are then one group).
+// step 128 (one group of 128; two of 64: a lane half's 64 channels are then one group; four
+// of 32: a lane half's words 0-3 one group, 4-7 the next).
 // Wave w owns all 256 rows and columns [WN / 4 w, +WN / 4) of the tile: 8 x (WN / 128)
 // accumulators of v_mfma_f32_32x32x16_f16 (256 or 128 registers, which the compiler keeps
 // in AGPRs), so every B column is widened by exactly one wave. The launcher takes WN = 128
@@ -97,7 +99,7 @@ __device__ __forceinline__ half8w widen_word3(uint32_t lo, uint32_t hi, int f, i
   return half8w{d[0][0], d[0][1], d[1][0], d[1][1], d[2][0], d[2][1], d[3][0], d[3][1]};
 }
 
-template <bool GATED, int WN, int BITS>
+template <bool GATED, int WN, int BITS, bool G32>
 __global__ void __launch_bounds__(256)
     k_gemm_wide(const uint16_t* X, int64_t M, const uint32_t* qweight, const uint16_t* scales,
                 const uint8_t* zeros, int64_t N, int64_t K, int group, uint16_t* __restrict__ Y,
@@ -178,14 +180,28 @@ __global__ void __launch_bounds__(256)
       bcol[b] = n < N ? n : N - 1;
     }
   }
+  // per column, the zero(s) and scale(s) of the lane half's 64 channels of a step: one group
+  // (128 channels: step; 64: 2 step + kh), or with 32-channel groups two (4 step + 2 kh for
+  // words 0-3 of the half, the next for words 4-7)
+  constexpr int kZ = G32 ? 2 : 1;
   struct ScaleZero {
-    uint32_t zb[kCT], sc[kCT];
+    uint32_t zb[kCT], sc[kCT][kZ];
   };
   auto load_sz = [&](ScaleZero& st, int64_t step) {
 #pragma unroll
     for (int b = 0; b < kCT; ++b) {
-      st.zb[b] = zeros[bcol[b] * zbw + (BITS == 8 ? (step << g64) + (g64 & kh) : step >> (1 - g64))];
-      st.sc[b] = scales[bcol[b] * Gs + (step << g64) + (g64 & kh)];
+      if constexpr (G32) {
+        const int64_t g0 = 4 * step + 2 * kh;
+        if constexpr (BITS == 8)
+          st.zb[b] = (uint32_t)zeros[bcol[b] * zbw + g0] | ((uint32_t)zeros[bcol[b] * zbw + g0 + 1] << 8);
+        else
+          st.zb[b] = zeros[bcol[b] * zbw + 2 * step + kh];  // nibbles: groups g0, g0 + 1
+        st.sc[b][0] = scales[bcol[b] * Gs + g0];
+        st.sc[b][1] = scales[bcol[b] * Gs + g0 + 1];
+      } else {
+        st.zb[b] = zeros[bcol[b] * zbw + (BITS == 8 ? (step << g64) + (g64 & kh) : step >> (1 - g64))];
+        st.sc[b][0] = scales[bcol[b] * Gs + (step << g64) + (g64 & kh)];
+      }
     }
   };
 
@@ -226,16 +242,22 @@ __global__ void __launch_bounds__(256)
       __builtin_amdgcn_global_load_lds((const void*)(bptr[i] + sn * (kQ * 4)),
                                        (lds_void*)&bdn[(wave * kBT + i) * 64], 16, 0, 0);
     };
-    half2w zz[kCT], zz64[kCT], s2[kCT];
+    half2w zz[kCT][kZ], zz64[kCT][kZ], s2[kCT][kZ];
     const int hi = g64 ? kh : (int)(step & 1);  // zero nibble: group of 128 (step) or 64 (2 step + kh)
 #pragma unroll
-    for (int b = 0; b < kCT; ++b) {
-      const uint32_t z = BITS == 8 ? cur.zb[b] : hi ? (cur.zb[b] >> 4) : (cur.zb[b] & 0xF);
-      const uint32_t z1024 = 0x6400u + z, z64 = 0x5400u + (z << 4);
-      zz[b] = -__builtin_bit_cast(half2w, z1024 | (z1024 << 16));
-      zz64[b] = -__builtin_bit_cast(half2w, z64 | (z64 << 16));
-      s2[b] = __builtin_bit_cast(half2w, cur.sc[b] | (cur.sc[b] << 16));
-    }
+    for (int b = 0; b < kCT; ++b)
+#pragma unroll
+      for (int i = 0; i < kZ; ++i) {
+        uint32_t z;
+        if constexpr (G32)
+          z = BITS == 8 ? (cur.zb[b] >> (8 * i)) & 0xFF : (cur.zb[b] >> (4 * i)) & 0xF;
+        else
+          z = BITS == 8 ? cur.zb[b] : hi ? (cur.zb[b] >> 4) : (cur.zb[b] & 0xF);
+        const uint32_t z1024 = 0x6400u + z, z64 = 0x5400u + (z << 4);
+        zz[b][i] = -__builtin_bit_cast(half2w, z1024 | (z1024 << 16));
+        zz64[b][i] = -__builtin_bit_cast(half2w, z64 | (z64 << 16));
+        s2[b][i] = __builtin_bit_cast(half2w, cur.sc[b][i] | (cur.sc[b][i] << 16));
+      }
     // this lane's code words of the step, per column: 4- and 8-bit, words 2 kQ kh .., the
     // quarters kQ / 2 kh .. kQ / 2 kh + kQ / 2 - 1 (one 16-byte read each); 3-bit, low-plane
     // words 4 kh .. 4 kh + 3 (quarter kh) and high-plane words 8 + 2 kh, 9 + 2 kh (half of
@@ -257,6 +279,7 @@ __global__ void __launch_bounds__(256)
     }
     auto frags = [&](int s, half8w (&A)[kRT], half8w (&B)[kCT]) {
       const int c = kh * 8 + s;
+      const int zi = G32 ? (s >> 2) : 0;  // slices 0-3 lie in the half's first 32 channels
 #pragma unroll
       for (int a = 0; a < kRT; ++a) {
         const int r = a * 32 + m32;
@@ -267,19 +290,19 @@ __global__ void __launch_bounds__(256)
         if constexpr (BITS == 8) {
           // slice s: words 2 s, 2 s + 1 of the lane half's 16
           const uint4 q = bq[b][s >> 1];
-          B[b] = (s & 1) ? widen_word8(q.z, q.w, zz[b], s2[b], magic8)
-                         : widen_word8(q.x, q.y, zz[b], s2[b], magic8);
+          B[b] = (s & 1) ? widen_word8(q.z, q.w, zz[b][zi], s2[b][zi], magic8)
+                         : widen_word8(q.x, q.y, zz[b][zi], s2[b][zi], magic8);
         } else if constexpr (BITS == 3) {
           // slice s = channel pairs 4 s .. 4 s + 3 of the half: low word s / 2 (fields
           // 4 (s % 2) ..), high word s / 4 (bits 4 (s % 4) ..)
           const uint4 q = bq[b][0];
           const uint32_t lo = (s >> 1) == 0 ? q.x : (s >> 1) == 1 ? q.y : (s >> 1) == 2 ? q.z : q.w;
           const uint32_t hiw = (s >> 2) ? bh[b].y : bh[b].x;
-          B[b] = widen_word3(lo, hiw, 4 * (s & 1), 4 * (s & 3), zz[b], s2[b], magic);
+          B[b] = widen_word3(lo, hiw, 4 * (s & 1), 4 * (s & 3), zz[b][zi], s2[b][zi], magic);
         } else {
           const uint4 q = bq[b][s >> 2];
           const uint32_t w = (s & 3) == 0 ? q.x : (s & 3) == 1 ? q.y : (s & 3) == 2 ? q.z : q.w;
-          B[b] = widen_word(w, zz[b], zz64[b], s2[b], magic);
+          B[b] = widen_word(w, zz[b][zi], zz64[b][zi], s2[b][zi], magic);
         }
       }
     };
@@ -382,9 +405,25 @@ int64_t gemm_wide_tiles(int64_t M, int64_t N, bool gated, int w_bit) {
 }
 
 bool gemm_wide_supported(int64_t K, int group, int w_bit, bool gated) {
-  return (w_bit == 4 || w_bit == 3 || (w_bit == 8 && !gated)) && (group == 128 || group == 64) &&
-         (int64_t)kWM * K < ((int64_t)1 << 32);
+  return (w_bit == 4 || w_bit == 3 || (w_bit == 8 && !gated)) &&
+         (group == 128 || group == 64 || group == 32) && (int64_t)kWM * K < ((int64_t)1 << 32);
 }
+
+namespace {
+
+template <bool GATED, int WN, int BITS>
+void launch_wide_t(dim3 grid, hipStream_t stream, const uint16_t* X, int64_t M, const uint32_t* qw,
+                   const uint16_t* sc, const uint8_t* z, int64_t N, int64_t K, int group,
+                   uint16_t* Y, int64_t mt, int64_t nt, int64_t per_xcd) {
+  if (group == 32)
+    hipLaunchKernelGGL((k_gemm_wide<GATED, WN, BITS, true>), grid, dim3(256), 0, stream, X, M, qw,
+                       sc, z, N, K, group, Y, mt, nt, per_xcd);
+  else
+    hipLaunchKernelGGL((k_gemm_wide<GATED, WN, BITS, false>), grid, dim3(256), 0, stream, X, M, qw,
+                       sc, z, N, K, group, Y, mt, nt, per_xcd);
+}
+
+}  // namespace
 
 hipError_t launch_gemm_wide(const uint16_t* X, int64_t M, const uint32_t* qweight,
                             const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
@@ -396,23 +435,17 @@ hipError_t launch_gemm_wide(const uint16_t* X, int64_t M, const uint32_t* qweigh
   const int64_t per_xcd = (mt * nt + 7) / 8;
   const dim3 grid((unsigned)(per_xcd * 8));
   if (w_bit == 8)
-    hipLaunchKernelGGL((k_gemm_wide<false, 128, 8>), grid, dim3(256), 0, stream, X, M, qweight,
-                       scales, zeros, N, K, group, Y, mt, nt, per_xcd);
+    launch_wide_t<false, 128, 8>(grid, stream, X, M, qweight, scales, zeros, N, K, group, Y, mt, nt, per_xcd);
   else if (w_bit == 3 && gated)
-    hipLaunchKernelGGL((k_gemm_wide<true, 256, 3>), grid, dim3(256), 0, stream, X, M, qweight,
-                       scales, zeros, N, K, group, Y, mt, nt, per_xcd);
+    launch_wide_t<true, 256, 3>(grid, stream, X, M, qweight, scales, zeros, N, K, group, Y, mt, nt, per_xcd);
   else if (w_bit == 3)
-    hipLaunchKernelGGL((k_gemm_wide<false, 256, 3>), grid, dim3(256), 0, stream, X, M, qweight,
-                       scales, zeros, N, K, group, Y, mt, nt, per_xcd);
+    launch_wide_t<false, 256, 3>(grid, stream, X, M, qweight, scales, zeros, N, K, group, Y, mt, nt, per_xcd);
   else if (gated)
-    hipLaunchKernelGGL((k_gemm_wide<true, 256, 4>), grid, dim3(256), 0, stream, X, M, qweight,
-                       scales, zeros, N, K, group, Y, mt, nt, per_xcd);
+    launch_wide_t<true, 256, 4>(grid, stream, X, M, qweight, scales, zeros, N, K, group, Y, mt, nt, per_xcd);
   else if (cols == 256)
-    hipLaunchKernelGGL((k_gemm_wide<false, 256, 4>), grid, dim3(256), 0, stream, X, M, qweight,
-                       scales, zeros, N, K, group, Y, mt, nt, per_xcd);
+    launch_wide_t<false, 256, 4>(grid, stream, X, M, qweight, scales, zeros, N, K, group, Y, mt, nt, per_xcd);
   else
-    hipLaunchKernelGGL((k_gemm_wide<false, 128, 4>), grid, dim3(256), 0, stream, X, M, qweight,
-                       scales, zeros, N, K, group, Y, mt, nt, per_xcd);
+    launch_wide_t<false, 128, 4>(grid, stream, X, M, qweight, scales, zeros, N, K, group, Y, mt, nt, per_xcd);
   return hipGetLastError();
 }
 

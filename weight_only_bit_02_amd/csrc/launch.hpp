@@ -87,7 +87,7 @@ hipError_t launch_gemm(const uint16_t* X, int64_t M, const uint32_t* qweight,
                        const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
                        int group, int w_bit, uint16_t* Y, bool gated, hipStream_t stream);
 
-// a8, 4- and 3-bit codes (and 8-bit codes, plain outputs) with 128- or 64-channel groups: the GEMM
+// a8, 4- and 3-bit codes (and 8-bit codes, plain outputs), every group size: the GEMM
 // with 256-row tiles (256 or 128 columns) and one wave per SIMD (gemm_wide.hip).
 // gemm_wide_supported: the configs and sizes it takes; gemm_wide_tiles: its tile count for an
 // M x N output (gated: N / 2 outputs).
