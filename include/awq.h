@@ -176,6 +176,13 @@ awq_status awq_candidate_scales(const double* act_mean, int64_t K, const awq_con
  *   its own power of two, so the errors hold about 1e-6 relative whatever the spread of s
  *   across a row (a row whose |D| spans more than about 2^80 can overflow the fp32 running
  *   error: the error is then non-finite and NONFINITE_INPUT is raised).
+ *   From N * K >= 2^22 weights and T >= 256 tokens every grid point is first scored with
+ *   hi alone (half the matrix-core work; over that many terms the rounding moves an error
+ *   by about 2e-6 relative at most), then every point whose error lies within 2^-12
+ *   (relative) of the smallest is scored again with hi + lo: the chosen index is always
+ *   decided by hi + lo errors, and err holds hi + lo errors for those points, hi-only
+ *   errors for the others. No host synchronization: both passes and the choice of points
+ *   run on the stream.
  *   Follow with awq_quantize_pack(W, s_best) to obtain the packed weights.
  */
 size_t awq_search_workspace_size(int64_t T, int64_t N, int64_t K, const awq_config* cfg);

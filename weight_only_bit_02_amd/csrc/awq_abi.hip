@@ -46,10 +46,10 @@ awq_status hip_status(hipError_t e) { return e == hipSuccess ? AWQ_OK : AWQ_ERR_
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Search workspace: [u: int64 K][act: fp64 K][s_grid: fp16 n_grid K]
-// [partials: fp64 n_grid x row tiles x token chunks]
+// [partials: fp64 n_grid x row tiles x token chunks][errf: fp64 n_grid][cand: n_grid bytes]
 // [xp: X in MFMA operand order, T rounded up to 64 tokens]
 struct SearchLayout {
-  size_t u, act, sgrid, partials, xp, total;
+  size_t u, act, sgrid, partials, errf, cand, xp, total;
   int64_t n_partials;  // per grid point
 };
 
@@ -62,7 +62,9 @@ SearchLayout search_layout(int64_t T, int64_t N, int64_t K, int n_grid) {
   L.act = align256(L.u + (size_t)K * 8);
   L.sgrid = align256(L.act + (size_t)K * 8);
   L.partials = align256(L.sgrid + (size_t)n_grid * K * 2);
-  L.xp = align256(L.partials + (size_t)n_grid * L.n_partials * 8);
+  L.errf = align256(L.partials + (size_t)n_grid * L.n_partials * 8);
+  L.cand = align256(L.errf + (size_t)n_grid * 8);
+  L.xp = align256(L.cand + (size_t)n_grid);
   L.total = align256(L.xp + awq::packed_x_bytes(T, K));
   return L;
 }
@@ -209,12 +211,16 @@ awq_status awq_search_scales(const void* X, int64_t T, const void* W, int64_t N,
   if (e == hipSuccess) e = awq::launch_act_sums(Xh, T, K, u, flags, st);
   if (e == hipSuccess) e = awq::launch_act_finalize(u, T, K, act, st);
   if (e == hipSuccess) e = awq::launch_scalegen(act, K, c.n_grid, sg, st);
+  const bool one_term = awq::search_one_term(T, N, K);
+  auto* errf = (double*)(ws + L.errf);
+  auto* cand = (uint8_t*)(ws + L.cand);
   if (e == hipSuccess)
     e = awq::launch_search_err(Xh, T, (const uint16_t*)W, N, K, sg, c.n_grid, c.zero_point == 0,
-                               c.group_size, c.w_bit, (uint4*)(ws + L.xp), partials, flags, st);
+                               c.group_size, c.w_bit, (uint4*)(ws + L.xp), partials, errf, cand,
+                               one_term, flags, st);
   if (e == hipSuccess)
-    e = awq::launch_search_reduce(partials, c.n_grid, L.n_partials, sg, K, (uint16_t*)s_best,
-                                  best_idx, err, flags, st);
+    e = awq::launch_search_reduce(partials, c.n_grid, L.n_partials, one_term ? cand : nullptr,
+                                  errf, sg, K, (uint16_t*)s_best, best_idx, err, flags, st);
   return hip_status(e);
 }
 

@@ -49,16 +49,22 @@ hipError_t launch_scalegen(const double* act, int64_t K, int n_grid, uint16_t* s
 // a5: per (alpha, row tile, token chunk) partial sums of the squared output error.
 int search_row_tile();
 int search_token_chunk(int64_t T);
-// xp: scratch for the copy of X in MFMA operand order (packed_x_bytes(T, K)).
+// Whether a search of this size scores every grid point with one fp16 term of D first and
+// re-scores only the near-minimal points with two (else two terms throughout).
+bool search_one_term(int64_t T, int64_t N, int64_t K);
+// xp: scratch for the copy of X in MFMA operand order (packed_x_bytes(T, K)). one_term:
+// errf (fp64 n_grid) receives the one-term errors and cand (n_grid bytes) the points that
+// the two-term pass re-scored into partials; both unused otherwise.
 hipError_t launch_search_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N,
                              int64_t K, const uint16_t* s_grid, int n_grid, bool sym, int group,
-                             int w_bit, uint4* xp, double* partials, uint32_t* flags,
-                             hipStream_t stream);
-// a6: fixed-order sums of the partials, first-minimum argmin, s_best copy.
+                             int w_bit, uint4* xp, double* partials, double* errf, uint8_t* cand,
+                             bool one_term, uint32_t* flags, hipStream_t stream);
+// a6: fixed-order sums of the partials (with cand: of the marked points only, errf for the
+// rest), first-minimum argmin, s_best copy.
 hipError_t launch_search_reduce(const double* partials, int n_grid, int64_t n_partials,
-                                const uint16_t* s_grid, int64_t K, uint16_t* s_best,
-                                int32_t* best_idx, double* err, uint32_t* flags,
-                                hipStream_t stream);
+                                const uint8_t* cand, const double* errf, const uint16_t* s_grid,
+                                int64_t K, uint16_t* s_best, int32_t* best_idx, double* err,
+                                uint32_t* flags, hipStream_t stream);
 
 // a7 / a8: Y = X deq(W)^T. gated (f1): W is gate|up stacked (N/2 rows each) and
 // Y[M][N/2] = SiLU(X deq(W_gate)^T) * (X deq(W_up)^T); N is even.

@@ -24,6 +24,12 @@
 // partial; a second kernel adds the partials of each grid point in a fixed order and
 // takes the first minimum. No floating-point atomics: results are bitwise
 // reproducible.
+// Large searches (many weights and tokens) first score every grid point with hi alone:
+// the rounding of D P to one fp16 term moves an error by a few 1e-6 relative at most once
+// millions of terms are summed, and the pass does half the MFMA work and half the LDS
+// operand reads. The grid points within a small relative gap of the smallest such error
+// are then scored again with hi + lo (the other blocks of that launch leave at once), so
+// the chosen index is always taken on two-term errors.
 //
 // Weight clipping (f3; the nxmr.cn article "AWQ技术概述：重新定义大语言模型量化", §5.1
 // "精度下降严重", names clip_steps, 200 suggested): with s fixed, every
@@ -44,6 +50,14 @@ constexpr int kRowTile = 128;        // rows of W per block
 constexpr int kTokPerWave = 64;      // tokens per wave (2 MFMA row tiles)
 constexpr int kLdsStride = 128 + 8;  // halves per LDS row (16-byte pad against bank conflicts)
 constexpr int kXcds = 8;
+// Error terms as hi alone (then hi + lo for the near-minimal grid points) from this many
+// weights and tokens: over that many terms the fp16 rounding of D P moves a grid point's
+// error by ~2e-6 relative at most (CPU simulation of the rounding on 2048 x 2048 weights,
+// 64 and 512 tokens, ordinary, wide-range and dead-channel activations, 3/4/8-bit codes),
+// and kRefineGap re-scores with hi + lo every point within 2^-12 of the smallest error.
+constexpr int64_t kOneTermMinWeights = (int64_t)1 << 22;
+constexpr int64_t kOneTermMinTokens = 256;
+constexpr double kRefineGap = 1.0 / 4096.0;
 
 // Exponent state of the search's per-(row, step) scale P = 2^(14 - E): E is re-chosen as
 // e + 2 (e: the exponent of the step's largest |D|, which lies in [2^(e-1), 2^e)) when
@@ -130,7 +144,8 @@ __device__ __forceinline__ StepScales step_scales(const uint16_t* s, int64_t k0)
 // value was met. Search (CLIP = false): the scale of each (row, step) comes from the row's
 // exponent state e_state (search_exponent), and its exponent E is written to pe_out[row].
 // Clip search: each group's own largest |D| sets its P, written to pg_out[row * 4 + group].
-template <bool CLIP>
+// LO = false keeps only hi (one fp16 term, 11 significant bits; lo_buf unused).
+template <bool CLIP, bool LO = true>
 __device__ __forceinline__ bool quantize_row(uint4 wv, const StepScales& sc, float r, bool sym,
                                              int group, float qmax, ScaleDiv sd, int& e_state,
                                              int* pe_out, uint16_t* hi_buf, uint16_t* lo_buf,
@@ -197,25 +212,26 @@ __device__ __forceinline__ bool quantize_row(uint4 wv, const StepScales& sc, flo
   uint32_t hi[4], lo[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    uint16_t h2[2], l2[2];
+    uint16_t h2[2], l2[2] = {0, 0};
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int c = 2 * i + e;
       const float d = dg[c] * P;
       h2[e] = f2h_bits(d);
-      l2[e] = f2h_bits(d - h2f(h2[e]));
+      if constexpr (LO) l2[e] = f2h_bits(d - h2f(h2[e]));
     }
     hi[i] = (uint32_t)h2[0] | ((uint32_t)h2[1] << 16);
     lo[i] = (uint32_t)l2[0] | ((uint32_t)l2[1] << 16);
   }
   *reinterpret_cast<uint4*>(&hi_buf[row * kLdsStride + li * 8]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-  *reinterpret_cast<uint4*>(&lo_buf[row * kLdsStride + li * 8]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+  if constexpr (LO)
+    *reinterpret_cast<uint4*>(&lo_buf[row * kLdsStride + li * 8]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
   return bad;
 }
 
 // Quantizes step j of rows [row_base, row_base + NROWS) of the tile with NW waves (tid
 // counts their threads from 0), 4 rows per wave per pass.
-template <int NW, bool CLIP, int NROWS>
+template <int NW, bool CLIP, int NROWS, bool LO = true>
 __device__ __forceinline__ bool quantize_tile_group(const uint16_t* W, int64_t N, int64_t K,
                                                     const uint16_t* s, float r, bool sym,
                                                     int group, float qmax, int64_t n0, int64_t j,
@@ -245,20 +261,23 @@ __device__ __forceinline__ bool quantize_tile_group(const uint16_t* W, int64_t N
   for (int p = 0; p < kPasses; ++p) {
     const int row = p * kRowsPerPass + q_row;
     const uint4 wv = n0 + row < N ? wvs[p] : make_uint4(0, 0, 0, 0);
-    bad |= quantize_row<CLIP>(wv, sc, r, sym, group, qmax, scale_divisor(qmax, sym), e_state[p],
+    bad |= quantize_row<CLIP, LO>(wv, sc, r, sym, group, qmax, scale_divisor(qmax, sym), e_state[p],
                               pe_out, hi_buf, lo_buf, row, li, pg_out);
   }
   return bad;
 }
 
-template <int NW>
+// LO: D P as two fp16 terms hi + lo (22 significant bits) or as hi alone (11 bits, half
+// the MFMA work and LDS operand reads). cand (optional): only grid points with cand[i] != 0
+// are scored; the other blocks leave at once (their partials are left as they were).
+template <int NW, bool LO>
 __global__ void __launch_bounds__(NW * 64)
     k_search_err(const uint4* xp, int64_t T, const uint16_t* W, int64_t N, int64_t K,
                  const uint16_t* s_grid, int n_grid, int sym, int group, int w_bit,
                  double* __restrict__ partials, uint32_t* __restrict__ flags, int64_t n_ntiles,
-                 int64_t per_xcd) {
+                 int64_t per_xcd, const uint8_t* __restrict__ cand) {
   __shared__ __attribute__((aligned(16))) uint16_t lds_hi[2][kRowTile * kLdsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_lo[2][kRowTile * kLdsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_lo[LO ? 2 : 1][LO ? kRowTile * kLdsStride : 8];
   __shared__ int lds_pe[2][kRowTile];  // exponent E of each row's P = 2^(14 - E), per buffer
   __shared__ double lds_red[NW];
 
@@ -268,6 +287,7 @@ __global__ void __launch_bounds__(NW * 64)
   if (t >= n_ntiles * n_grid) return;
   const int64_t ntile = t / n_grid;
   const int alpha = (int)(t % n_grid);
+  if (cand && cand[alpha] == 0) return;  // block-uniform, before any barrier
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -294,9 +314,9 @@ __global__ void __launch_bounds__(NW * 64)
   bool bad = false;
   int e_state[quant_passes<NH, kRowTile / 2>()];
   auto quantize = [&](int64_t j, int buf) {
-    bad |= quantize_tile_group<NH, false, kRowTile / 2>(W, N, K, s, 1.0f, sym, group, qmax, n0, j,
-                                                       e_state, lds_pe[buf], lds_hi[buf],
-                                                       lds_lo[buf], tid_set,
+    bad |= quantize_tile_group<NH, false, kRowTile / 2, LO>(W, N, K, s, 1.0f, sym, group, qmax, n0,
+                                                           j, e_state, lds_pe[buf], lds_hi[buf],
+                                                           lds_lo[LO ? buf : 0], tid_set,
                                                        set_b ? kRowTile / 2 : 0, nullptr);
   };
 
@@ -347,14 +367,16 @@ __global__ void __launch_bounds__(NW * 64)
         for (int b = 0; b < 4; ++b) {
           const int r = b * 32 + m32;
           Bh[b] = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(&lds_hi[buf][r * kLdsStride + koff]));
-          Bl[b] = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(&lds_lo[buf][r * kLdsStride + koff]));
+          if constexpr (LO)
+            Bl[b] = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(&lds_lo[buf][r * kLdsStride + koff]));
         }
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
           for (int b = 0; b < 4; ++b) {
             acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[a], Bh[b], acc[a][b], 0, 0, 0);
-            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[a], Bl[b], acc[a][b], 0, 0, 0);
+            if constexpr (LO)
+              acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[a], Bl[b], acc[a][b], 0, 0, 0);
           }
       }
     };
@@ -649,11 +671,45 @@ hipError_t launch_clip_reduce(const void* err, int64_t T, int n_shrink, int64_t 
   return hipGetLastError();
 }
 
-// One block: err_i = sum of partials of grid point i in index order; first minimum. A
-// non-finite error can only come from a NaN or Inf weight or activation (the tile's
-// min / max drop a NaN), so it raises NONFINITE_INPUT.
+// Fixed-order fp64 sum of grid point i's partials.
+__device__ __forceinline__ double sum_partials(const double* partials, int i, int64_t n_partials) {
+  double tot = 0.0;
+  const double* p = partials + (int64_t)i * n_partials;
+  for (int64_t u = 0; u < n_partials; ++u) tot += p[u];
+  return tot;
+}
+
+// After a one-term pass: errf_i from its partials, and cand_i = 1 for every grid point whose
+// one-term error lies within a relative kRefineGap of the smallest one, when there are at
+// least two such points (a lone minimum is already decided). One block, one thread per point.
+__global__ void __launch_bounds__(64)
+    k_search_candidates(const double* __restrict__ partials, int n_grid, int64_t n_partials,
+                        double refine_gap, double* __restrict__ errf, uint8_t* __restrict__ cand) {
+  __shared__ double lds_err[64];
+  __shared__ int lds_n;
+  const int tid = threadIdx.x;
+  if (tid < n_grid) lds_err[tid] = sum_partials(partials, tid, n_partials);
+  if (tid == 0) lds_n = 0;
+  __syncthreads();
+  double mn = lds_err[0];
+  for (int i = 1; i < n_grid; ++i) mn = lds_err[i] < mn ? lds_err[i] : mn;
+  const double lim = mn + refine_gap * __builtin_fabs(mn);
+  const bool near = tid < n_grid && lds_err[tid] <= lim;  // false for NaN
+  if (near) atomicAdd(&lds_n, 1);
+  __syncthreads();
+  if (tid < n_grid) {
+    errf[tid] = lds_err[tid];
+    cand[tid] = (uint8_t)(near && lds_n > 1 ? 1 : 0);
+  }
+}
+
+// One block: err_i = sum of partials of grid point i in index order (with cand, only for
+// the points marked in it; the others take errf_i), then the first minimum. A non-finite
+// error can only come from a NaN or Inf weight or activation (the tile's min / max drop a
+// NaN), so it raises NONFINITE_INPUT.
 __global__ void __launch_bounds__(256)
     k_search_reduce(const double* __restrict__ partials, int n_grid, int64_t n_partials,
+                    const uint8_t* __restrict__ cand, const double* __restrict__ errf,
                     const uint16_t* __restrict__ s_grid, int64_t K, uint16_t* __restrict__ s_best,
                     int32_t* __restrict__ best_idx, double* __restrict__ err,
                     uint32_t* __restrict__ flags) {
@@ -661,9 +717,8 @@ __global__ void __launch_bounds__(256)
   __shared__ int lds_best;
   const int tid = threadIdx.x;
   if (tid < n_grid) {
-    double tot = 0.0;
-    const double* p = partials + (int64_t)tid * n_partials;
-    for (int64_t i = 0; i < n_partials; ++i) tot += p[i];
+    const double tot =
+        (!cand || cand[tid]) ? sum_partials(partials, tid, n_partials) : errf[tid];
     lds_err[tid] = tot;
     if (!__builtin_isfinite(tot) && flags) atomicOr(flags, AWQ_FLAG_NONFINITE_INPUT);
   }
@@ -684,30 +739,60 @@ __global__ void __launch_bounds__(256)
 int search_row_tile() { return kRowTile; }
 int search_token_chunk(int64_t T) { return T <= 4 * kTokPerWave ? 4 * kTokPerWave : 8 * kTokPerWave; }
 
-hipError_t launch_search_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N,
-                             int64_t K, const uint16_t* s_grid, int n_grid, bool sym, int group,
-                             int w_bit, uint4* xp, double* partials, uint32_t* flags,
-                             hipStream_t stream) {
-  hipError_t e = launch_pack_x(X, T, K, xp, stream);
-  if (e != hipSuccess) return e;
+bool search_one_term(int64_t T, int64_t N, int64_t K) {
+  return T >= kOneTermMinTokens && N * K >= kOneTermMinWeights;
+}
+
+static void launch_search_pass(const uint4* xp, int64_t T, const uint16_t* W, int64_t N,
+                               int64_t K, const uint16_t* s_grid, int n_grid, bool sym, int group,
+                               int w_bit, double* partials, uint32_t* flags, bool lo,
+                               const uint8_t* cand, hipStream_t stream) {
   const int64_t n_ntiles = (N + kRowTile - 1) / kRowTile;
   const int64_t per_xcd = (n_ntiles * n_grid + kXcds - 1) / kXcds;
   const dim3 grid((unsigned)(per_xcd * kXcds));
-  if (T <= 4 * kTokPerWave)
-    hipLaunchKernelGGL(k_search_err<4>, grid, dim3(256), 0, stream, xp, T, W, N, K, s_grid, n_grid,
-                       (int)sym, group, w_bit, partials, flags, n_ntiles, per_xcd);
-  else
-    hipLaunchKernelGGL(k_search_err<8>, grid, dim3(512), 0, stream, xp, T, W, N, K, s_grid, n_grid,
-                       (int)sym, group, w_bit, partials, flags, n_ntiles, per_xcd);
+#define AWQ_SEARCH_LAUNCH(NW_, LO_)                                                              \
+  hipLaunchKernelGGL((k_search_err<NW_, LO_>), grid, dim3(NW_ * 64), 0, stream, xp, T, W, N, K, \
+                     s_grid, n_grid, (int)sym, group, w_bit, partials, flags, n_ntiles, per_xcd, \
+                     cand)
+  if (T <= 4 * kTokPerWave) {
+    if (lo) AWQ_SEARCH_LAUNCH(4, true); else AWQ_SEARCH_LAUNCH(4, false);
+  } else {
+    if (lo) AWQ_SEARCH_LAUNCH(8, true); else AWQ_SEARCH_LAUNCH(8, false);
+  }
+#undef AWQ_SEARCH_LAUNCH
+}
+
+hipError_t launch_search_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N,
+                             int64_t K, const uint16_t* s_grid, int n_grid, bool sym, int group,
+                             int w_bit, uint4* xp, double* partials, double* errf, uint8_t* cand,
+                             bool one_term, uint32_t* flags, hipStream_t stream) {
+  hipError_t e = launch_pack_x(X, T, K, xp, stream);
+  if (e != hipSuccess) return e;
+  if (!one_term) {
+    launch_search_pass(xp, T, W, N, K, s_grid, n_grid, sym, group, w_bit, partials, flags, true,
+                       nullptr, stream);
+    return hipGetLastError();
+  }
+  // one-term pass over every grid point, then the two-term pass over the near-minimal ones
+  launch_search_pass(xp, T, W, N, K, s_grid, n_grid, sym, group, w_bit, partials, flags, false,
+                     nullptr, stream);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_search_candidates, dim3(1), dim3(64), 0, stream, partials, n_grid,
+                     (int64_t)((N + kRowTile - 1) / kRowTile) *
+                         ((T + search_token_chunk(T) - 1) / search_token_chunk(T)),
+                     kRefineGap, errf, cand);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  launch_search_pass(xp, T, W, N, K, s_grid, n_grid, sym, group, w_bit, partials, flags, true,
+                     cand, stream);
   return hipGetLastError();
 }
 
 hipError_t launch_search_reduce(const double* partials, int n_grid, int64_t n_partials,
-                                const uint16_t* s_grid, int64_t K, uint16_t* s_best,
-                                int32_t* best_idx, double* err, uint32_t* flags,
-                                hipStream_t stream) {
+                                const uint8_t* cand, const double* errf, const uint16_t* s_grid,
+                                int64_t K, uint16_t* s_best, int32_t* best_idx, double* err,
+                                uint32_t* flags, hipStream_t stream) {
   hipLaunchKernelGGL(k_search_reduce, dim3(1), dim3(256), 0, stream, partials, n_grid,
-                     n_partials, s_grid, K, s_best, best_idx, err, flags);
+                     n_partials, cand, errf, s_grid, K, s_best, best_idx, err, flags);
   return hipGetLastError();
 }
 
