@@ -70,7 +70,8 @@ SearchLayout search_layout(int64_t T, int64_t N, int64_t K, int n_grid) {
 }
 
 // Clip-search workspace: [err: fp64 n_shrink x N x G]
-// [xp: X in MFMA operand order, T rounded up to 64 tokens]
+// [xp: X in MFMA operand order, T rounded up to 64 tokens; or, in the Gram form, the
+//  per-group G' and the channel scales]
 struct ClipLayout {
   size_t err, xp, total;
 };
@@ -79,7 +80,7 @@ ClipLayout clip_layout(int64_t T, int64_t N, int64_t K, int n_shrink, int group)
   ClipLayout L;
   L.err = 0;
   L.xp = align256(L.err + awq::clip_err_bytes(T, N, K, n_shrink, group));
-  L.total = align256(L.xp + awq::packed_x_bytes(T, K));
+  L.total = align256(L.xp + awq::clip_scratch_bytes(T, K, group));
   return L;
 }
 

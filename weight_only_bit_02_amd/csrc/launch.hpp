@@ -29,6 +29,10 @@ size_t clip_err_bytes(int64_t T, int64_t N, int64_t K, int n_shrink, int group);
 // Bytes of the MFMA-ordered copy of X (T tokens rounded up to 64, K channels) that the
 // scale and clip searches read their activations from.
 size_t packed_x_bytes(int64_t T, int64_t K);
+// Bytes of the clip search's scratch: the copy of X above, or for the Gram form (128-channel
+// groups, T > 256) the per-group Gram matrices G' in operand order and the channel scales,
+// whichever is larger.
+size_t clip_scratch_bytes(int64_t T, int64_t K, int group);
 hipError_t launch_clip_reduce(const void* err, int64_t T, int n_shrink, int64_t N, int64_t K,
                               int group, uint8_t* clip_idx, double* err_best, uint32_t* flags,
                               hipStream_t stream);

@@ -238,7 +238,7 @@ __device__ __forceinline__ bool quantize_tile_group(const uint16_t* W, int64_t N
                                                     int (&e_state)[quant_passes<NW, NROWS>()],
                                                     int* pe_out, uint16_t* hi_buf,
                                                     uint16_t* lo_buf, int tid, int row_base,
-                                                    float* pg_out) {
+                                                    float* pg_out, const float* cmul = nullptr) {
   constexpr int kRowsPerPass = NW * 4;
   constexpr int kPasses = quant_passes<NW, NROWS>();
   static_assert(kPasses * kRowsPerPass == NROWS, "whole passes");
@@ -255,7 +255,15 @@ __device__ __forceinline__ bool quantize_tile_group(const uint16_t* W, int64_t N
     wvs[p] = *reinterpret_cast<const uint4*>(W + (n < N ? n : N - 1) * K + k0);
   }
   // the thread's 8 channels are the same in every pass: s and 1/s once
-  const StepScales sc = step_scales<CLIP>(s, k0);
+  StepScales sc = step_scales<CLIP>(s, k0);
+  if (cmul) {
+    // D is wanted times a per-channel power of two: folded into 1/s (exact)
+    const float4 c0 = *reinterpret_cast<const float4*>(cmul + k0);
+    const float4 c1 = *reinterpret_cast<const float4*>(cmul + k0 + 4);
+    const float cm[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sc.rs[i] *= cm[i];
+  }
   bool bad = false;
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) {
@@ -560,6 +568,203 @@ __global__ void __launch_bounds__(NW * 64)
   if (bad && flags && ci == 0) atomicOr(flags, AWQ_FLAG_NONFINITE_INPUT);
 }
 
+// ------------------------------------------------------------------ Gram form (f3)
+// With 128-channel groups, a group's error is a quadratic form in its weight errors:
+//   err(n, g) = sum_t (sum_{k in g} X_tk D_nk)^2 = d^T G_g d,  G_g = X_g^T X_g (128 x 128),
+// so once G_g is formed (2 T 128 flop per weight, shared by every ratio and row) a ratio
+// costs 2 * 128 flop per weight instead of 2 T. Channels are balanced by powers of two:
+// c_k = 2^-e_k with G_kk c_k^2 in (1/4, 1], G' = diag(c) G diag(c), D' = D diag(1/c), so
+// d'^T G' d' is the same number, every |G'_kj| <= 1 (Cauchy-Schwarz) and D' carries each
+// channel's weight error times its activation size. G' is kept as fp16 hi + lo and D' P
+// (the group's own power of two, as in the direct form) as fp16 hi + lo; V = G' D'^T takes
+// the products hi hi, lo hi and hi lo on the matrix cores (fp32), and err = sum_j D'_j V_j
+// with D'_j = hi + lo (exact in fp32).
+
+// e_k of every channel: G_kk = sum_t X_tk^2 (fp64) = m 2^E, m in [1/2, 1), e_k = ceil(E / 2),
+// so G_kk 2^(-2 e_k) lies in [1/4, 1); cmul[k] = 2^e_k (multiplies D); a zero or non-finite
+// G_kk takes e_k = 0.
+__global__ void __launch_bounds__(256)
+    k_gram_scale(const uint16_t* __restrict__ X, int64_t T, int64_t K, int* __restrict__ cexp,
+                 float* __restrict__ cmul) {
+  const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= K) return;
+  double g = 0.0;
+  for (int64_t t = 0; t < T; ++t) {
+    const double x = (double)h2f(X[t * K + k]);
+    g = __builtin_fma(x, x, g);
+  }
+  int E = 0;
+  if (g > 0.0 && __builtin_isfinite(g)) (void)__builtin_frexp(g, &E);
+  const int e = (E + 1) >> 1;  // ceil(E / 2), E may be negative
+  cexp[k] = e;
+  cmul[k] = __builtin_ldexpf(1.0f, e);
+}
+
+// G' in MFMA A-operand order: for group g, 32-row slice jt (0..3), k16 slice st (0..7) and
+// part (hi, lo), lane l's 16 bytes are G'[32 jt + l % 32][16 st + 8 (l / 32) .. + 8], so a
+// wave's load of one (jt, st, part) is 1 KiB contiguous. One thread per 16 bytes: 8 fp64
+// sums over the tokens, scaled by 2^-(e_j + e_k) (exact), hi = fp16(v), lo = fp16(v - hi).
+__global__ void __launch_bounds__(256)
+    k_gram_build(const uint16_t* __restrict__ X, int64_t T, int64_t K,
+                 const int* __restrict__ cexp, uint4* __restrict__ gp,
+                 uint32_t* __restrict__ flags) {
+  const int64_t G = K / kGroup;
+  const int64_t total = G * 4 * 8 * 64;  // threads
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int lane = (int)(i & 63);
+  const int st = (int)((i >> 6) & 7);
+  const int jt = (int)((i >> 9) & 3);
+  const int64_t g = i >> 11;
+  const int64_t kj = g * kGroup + jt * 32 + (lane & 31);
+  const int64_t kk = g * kGroup + st * 16 + (lane >> 5) * 8;
+  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int64_t t = 0; t < T; ++t) {
+    const double xj = (double)h2f(X[t * K + kj]);
+    const uint4 v = *reinterpret_cast<const uint4*>(X + t * K + kk);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc[2 * q] = __builtin_fma(xj, (double)h2f((uint16_t)(w[q] & 0xFFFF)), acc[2 * q]);
+      acc[2 * q + 1] = __builtin_fma(xj, (double)h2f((uint16_t)(w[q] >> 16)), acc[2 * q + 1]);
+    }
+  }
+  uint32_t hi[4], lo[4];
+  bool bad = false;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint16_t h2[2], l2[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int c = 2 * q + e;
+      const double v = __builtin_ldexp(acc[c], -(cexp[kj] + cexp[kk + c]));
+      bad |= !__builtin_isfinite(v);
+      h2[e] = f2h_bits((float)v);
+      l2[e] = f2h_bits((float)(v - (double)h2f(h2[e])));
+    }
+    hi[q] = (uint32_t)h2[0] | ((uint32_t)h2[1] << 16);
+    lo[q] = (uint32_t)l2[0] | ((uint32_t)l2[1] << 16);
+  }
+  uint4* base = gp + (((g * 4 + jt) * 8 + st) * 2) * 64;
+  base[lane] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+  base[64 + lane] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+  if (bad && flags) atomicOr(flags, AWQ_FLAG_NONFINITE_INPUT);
+}
+
+// Clip-search errors in the Gram form, 128-channel groups. A block owns (ratio i, 128 rows);
+// per step (= group) the two wave sets quantize D' P into LDS as in k_clip_err (set A
+// contracts then quantizes its half of the next group's rows, set B the reverse), and
+// wave w computes the slice (j rows 32 (w % 4) .., W rows 32 NT (w / 4) ..; NT = 16 / NW
+// tiles of 32 rows) of V^T = G' (D' P)^T: per k16 slice, G' hi / lo fragments from gp and D' P hi / lo
+// fragments from LDS, three MFMAs per 32 x 32 tile. Then each lane forms
+// sum_j V^T[j][n] (D' P)[n][j] over its 16 j of each tile (fp32), the lane halves and
+// the four j slices add in fp64, scaled by 1 / P^2 (exact).
+template <int NW>
+__global__ void __launch_bounds__(NW * 64)
+    k_clip_err_gram(const uint4* __restrict__ gp, const float* __restrict__ cmul,
+                    const uint16_t* W, int64_t N, int64_t K, const uint16_t* s, int clip_steps,
+                    int n_shrink, int sym, int w_bit, double* __restrict__ err,
+                    uint32_t* __restrict__ flags, int64_t n_ntiles, int64_t per_xcd) {
+  constexpr int NT = 16 / NW;  // 32 x 32 output tiles per wave
+  __shared__ __attribute__((aligned(16))) uint16_t lds_hi[2][kRowTile * kLdsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_lo[2][kRowTile * kLdsStride];
+  __shared__ float lds_pg[2][kRowTile * 4];
+  __shared__ double lds_red[2][4][kRowTile];  // [step parity][j slice][row]
+
+  const int64_t t = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (t >= n_ntiles * n_shrink) return;
+  const int64_t ntile = t / n_shrink;
+  const int ci = (int)(t % n_shrink);
+  const float r = clip_ratio(ci, clip_steps);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t n0 = ntile * kRowTile;
+  const float qmax = (float)((1 << w_bit) - 1);
+  const int64_t G = K / kGroup;
+  const int m32 = lane & 31;
+  const int khalf = lane >> 5;
+  const int jt = wave & 3;          // j slice of G' this wave multiplies
+  const int nb = (wave >> 2) * NT;  // first of its 32-row tiles of the block's rows
+
+  constexpr int NH = NW / 2;
+  const bool set_b = wave >= NH;
+  const int tid_set = set_b ? tid - NH * 64 : tid;
+  bool bad = false;
+  int e_unused[quant_passes<NH, kRowTile / 2>()];
+  auto quantize = [&](int64_t jq, int qbuf) {
+    bad |= quantize_tile_group<NH, true, kRowTile / 2>(W, N, K, s, r, sym, kGroup, qmax, n0, jq,
+                                                      e_unused, nullptr, lds_hi[qbuf], lds_lo[qbuf],
+                                                      tid_set, set_b ? kRowTile / 2 : 0,
+                                                      lds_pg[qbuf], cmul);
+  };
+  auto contract = [&](int64_t j, int buf) {
+    f32x16 acc[NT];
+#pragma unroll
+    for (int b = 0; b < NT; ++b) acc[b] = f32x16{};
+    const uint4* gbase = gp + (((j * 4 + jt) * 8) * 2) * 64;
+#pragma unroll 2
+    for (int st = 0; st < 8; ++st) {
+      const half8 Ah = __builtin_bit_cast(half8, gbase[(st * 2) * 64 + lane]);
+      const half8 Al = __builtin_bit_cast(half8, gbase[(st * 2 + 1) * 64 + lane]);
+      const int koff = st * 16 + khalf * 8;
+#pragma unroll
+      for (int b = 0; b < NT; ++b) {
+        const int row = (nb + b) * 32 + m32;
+        const half8 Bh = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(&lds_hi[buf][row * kLdsStride + koff]));
+        const half8 Bl = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(&lds_lo[buf][row * kLdsStride + koff]));
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ah, Bh, acc[b], 0, 0, 0);
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Al, Bh, acc[b], 0, 0, 0);
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ah, Bl, acc[b], 0, 0, 0);
+      }
+    }
+    // acc[b][e] = V^T[j][n], n = 32 (nb + b) + lane % 32, j = 32 jt + 8 (e / 4) + 4 (lane / 32)
+    // + e % 4: the lane's four runs of 4 consecutive j of row n
+#pragma unroll
+    for (int b = 0; b < NT; ++b) {
+      const int row = (nb + b) * 32 + m32;
+      float s32 = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int jj = jt * 32 + q * 8 + khalf * 4;
+        const uint2 h = *reinterpret_cast<const uint2*>(&lds_hi[buf][row * kLdsStride + jj]);
+        const uint2 l = *reinterpret_cast<const uint2*>(&lds_lo[buf][row * kLdsStride + jj]);
+        const uint32_t hw[2] = {h.x, h.y}, lw[2] = {l.x, l.y};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint16_t hb = (uint16_t)(hw[u >> 1] >> (16 * (u & 1)));
+          const uint16_t lb = (uint16_t)(lw[u >> 1] >> (16 * (u & 1)));
+          const float d = h2f(hb) + h2f(lb);  // exact: 22 significant bits
+          s32 = __builtin_fmaf(acc[b][q * 4 + u], d, s32);
+        }
+      }
+      int pe = 0;
+      (void)__builtin_frexpf(lds_pg[buf][row * 4], &pe);  // P = 2^(pe - 1)
+      double ss = __builtin_ldexp((double)s32, -2 * (pe - 1));
+      ss += __shfl_xor(ss, 32);
+      if (khalf == 0) lds_red[buf][jt][row] = ss;
+    }
+  };
+
+  quantize(0, 0);
+  __syncthreads();
+  for (int64_t j = 0; j < G; ++j) {
+    const int buf = (int)(j & 1);
+    const bool more = j + 1 < G;
+    if (set_b && more) quantize(j + 1, buf ^ 1);
+    contract(j, buf);
+    if (!set_b && more) quantize(j + 1, buf ^ 1);
+    __syncthreads();
+    if (tid < kRowTile && n0 + tid < N) {
+      const double tot = ((lds_red[buf][0][tid] + lds_red[buf][1][tid]) + lds_red[buf][2][tid]) +
+                         lds_red[buf][3][tid];
+      err[((int64_t)ci * N + n0 + tid) * G + j] = tot;
+    }
+  }
+  if (bad && flags && ci == 0) atomicOr(flags, AWQ_FLAG_NONFINITE_INPUT);
+}
+
 // One thread per (row, group): the first ratio index with the smallest error. A
 // non-finite error can only come from a NaN or Inf weight or activation (the tile's
 // min / max drop a NaN), so it raises NONFINITE_INPUT.
@@ -637,15 +842,43 @@ size_t clip_err_bytes(int64_t T, int64_t N, int64_t K, int n_shrink, int group) 
   return (size_t)n_shrink * N * (K / group) * per;
 }
 
+// The Gram form serves 128-channel groups from more than 256 calibration tokens (where it
+// needs fewer matrix-core passes than the direct form: 3 x 128 against 2 x T per weight).
+static bool clip_gram(int64_t T, int group) { return group == kGroup && T > 4 * kTokPerWave; }
+
+static size_t gram_bytes(int64_t K) {
+  return (size_t)K * kGroup * 2 * 2 + (size_t)K * 4 * 2;  // G' hi + lo, cexp, cmul
+}
+
+size_t clip_scratch_bytes(int64_t T, int64_t K, int group) {
+  const size_t px = packed_x_bytes(T, K);
+  return clip_gram(T, group) && gram_bytes(K) > px ? gram_bytes(K) : px;
+}
+
 hipError_t launch_clip_err(const uint16_t* X, int64_t T, const uint16_t* W, int64_t N,
                            int64_t K, const uint16_t* s, int clip_steps, int n_shrink, bool sym,
                            int group, int w_bit, uint4* xp, void* err, uint32_t* flags,
                            hipStream_t stream) {
-  hipError_t e = launch_pack_x(X, T, K, xp, stream);
-  if (e != hipSuccess) return e;
   const int64_t n_ntiles = (N + kRowTile - 1) / kRowTile;
   const int64_t per_xcd = (n_ntiles * n_shrink + kXcds - 1) / kXcds;
   const dim3 grid((unsigned)(per_xcd * kXcds));
+  if (clip_gram(T, group)) {
+    // scratch: [G' in operand order: K * 512 B][cexp: int K][cmul: fp32 K]
+    uint4* gp = xp;
+    int* cexp = reinterpret_cast<int*>(reinterpret_cast<char*>(xp) + (size_t)K * kGroup * 4);
+    float* cmul = reinterpret_cast<float*>(cexp + K);
+    hipLaunchKernelGGL(k_gram_scale, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, stream, X,
+                       T, K, cexp, cmul);
+    const int64_t threads = (K / kGroup) * 4 * 8 * 64;
+    hipLaunchKernelGGL(k_gram_build, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                       stream, X, T, K, cexp, gp, flags);
+    hipLaunchKernelGGL(k_clip_err_gram<16>, grid, dim3(1024), 0, stream, gp, cmul, W, N, K, s,
+                       clip_steps, n_shrink, (int)sym, w_bit, (double*)err, flags, n_ntiles,
+                       per_xcd);
+    return hipGetLastError();
+  }
+  hipError_t e = launch_pack_x(X, T, K, xp, stream);
+  if (e != hipSuccess) return e;
   double* e64 = (double*)err;
   float* e32 = (float*)err;
   if (clip_waves(T) == 4)
