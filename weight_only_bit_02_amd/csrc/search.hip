@@ -580,46 +580,58 @@ __global__ void __launch_bounds__(NW * 64)
 // the products hi hi, lo hi and hi lo on the matrix cores (fp32), and err = sum_j D'_j V_j
 // with D'_j = hi + lo (exact in fp32).
 
+// Both Gram kernels split the tokens over kGramSlices thread slices (contiguous token
+// ranges) and add the slices' fp64 partials in slice order through LDS, so each sum is
+// formed in a fixed order and enough waves are in flight to cover the load latency.
+constexpr int kGramSlices = 8;
+
 // e_k of every channel: G_kk = sum_t X_tk^2 (fp64) = m 2^E, m in [1/2, 1), e_k = ceil(E / 2),
 // so G_kk 2^(-2 e_k) lies in [1/4, 1); cmul[k] = 2^e_k (multiplies D); a zero or non-finite
-// G_kk takes e_k = 0.
-__global__ void __launch_bounds__(256)
+// G_kk takes e_k = 0. Block: 64 channels x kGramSlices token slices.
+__global__ void __launch_bounds__(64 * kGramSlices)
     k_gram_scale(const uint16_t* __restrict__ X, int64_t T, int64_t K, int* __restrict__ cexp,
                  float* __restrict__ cmul) {
-  const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (k >= K) return;
+  __shared__ double part[kGramSlices][64];
+  const int c = threadIdx.x & 63, sl = threadIdx.x >> 6;
+  const int64_t k = (int64_t)blockIdx.x * 64 + c;  // K is a multiple of 128
+  const int64_t t0 = T * sl / kGramSlices, t1 = T * (sl + 1) / kGramSlices;
   double g = 0.0;
-  for (int64_t t = 0; t < T; ++t) {
+  for (int64_t t = t0; t < t1; ++t) {
     const double x = (double)h2f(X[t * K + k]);
     g = __builtin_fma(x, x, g);
   }
-  int E = 0;
-  if (g > 0.0 && __builtin_isfinite(g)) (void)__builtin_frexp(g, &E);
-  const int e = (E + 1) >> 1;  // ceil(E / 2), E may be negative
-  cexp[k] = e;
-  cmul[k] = __builtin_ldexpf(1.0f, e);
+  part[sl][c] = g;
+  __syncthreads();
+  if (sl == 0) {
+    for (int u = 1; u < kGramSlices; ++u) g += part[u][c];
+    int E = 0;
+    if (g > 0.0 && __builtin_isfinite(g)) (void)__builtin_frexp(g, &E);
+    const int e = (E + 1) >> 1;  // ceil(E / 2), E may be negative
+    cexp[k] = e;
+    cmul[k] = __builtin_ldexpf(1.0f, e);
+  }
 }
 
 // G' in MFMA A-operand order: for group g, 32-row slice jt (0..3), k16 slice st (0..7) and
 // part (hi, lo), lane l's 16 bytes are G'[32 jt + l % 32][16 st + 8 (l / 32) .. + 8], so a
-// wave's load of one (jt, st, part) is 1 KiB contiguous. One thread per 16 bytes: 8 fp64
-// sums over the tokens, scaled by 2^-(e_j + e_k) (exact), hi = fp16(v), lo = fp16(v - hi).
-__global__ void __launch_bounds__(256)
+// wave's load of one (jt, st, part) is 1 KiB contiguous. Block: one (g, jt, st) piece, 64
+// lanes x kGramSlices token slices; lane l forms its 8 fp64 sums over the tokens, scaled by
+// 2^-(e_j + e_k) (exact), hi = fp16(v), lo = fp16(v - hi).
+__global__ void __launch_bounds__(64 * kGramSlices)
     k_gram_build(const uint16_t* __restrict__ X, int64_t T, int64_t K,
                  const int* __restrict__ cexp, uint4* __restrict__ gp,
                  uint32_t* __restrict__ flags) {
-  const int64_t G = K / kGroup;
-  const int64_t total = G * 4 * 8 * 64;  // threads
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= total) return;
-  const int lane = (int)(i & 63);
-  const int st = (int)((i >> 6) & 7);
-  const int jt = (int)((i >> 9) & 3);
-  const int64_t g = i >> 11;
+  __shared__ double part[kGramSlices - 1][8][64];
+  const int lane = threadIdx.x & 63, sl = threadIdx.x >> 6;
+  const int64_t piece = blockIdx.x;  // (g * 4 + jt) * 8 + st
+  const int st = (int)(piece & 7);
+  const int jt = (int)((piece >> 3) & 3);
+  const int64_t g = piece >> 5;
   const int64_t kj = g * kGroup + jt * 32 + (lane & 31);
   const int64_t kk = g * kGroup + st * 16 + (lane >> 5) * 8;
+  const int64_t t0 = T * sl / kGramSlices, t1 = T * (sl + 1) / kGramSlices;
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int64_t t = 0; t < T; ++t) {
+  for (int64_t t = t0; t < t1; ++t) {
     const double xj = (double)h2f(X[t * K + kj]);
     const uint4 v = *reinterpret_cast<const uint4*>(X + t * K + kk);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -629,6 +641,15 @@ __global__ void __launch_bounds__(256)
       acc[2 * q + 1] = __builtin_fma(xj, (double)h2f((uint16_t)(w[q] >> 16)), acc[2 * q + 1]);
     }
   }
+  if (sl > 0) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) part[sl - 1][c][lane] = acc[c];
+  }
+  __syncthreads();
+  if (sl != 0) return;
+  for (int u = 0; u < kGramSlices - 1; ++u)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] += part[u][c][lane];
   uint32_t hi[4], lo[4];
   bool bad = false;
 #pragma unroll
@@ -645,7 +666,7 @@ __global__ void __launch_bounds__(256)
     hi[q] = (uint32_t)h2[0] | ((uint32_t)h2[1] << 16);
     lo[q] = (uint32_t)l2[0] | ((uint32_t)l2[1] << 16);
   }
-  uint4* base = gp + (((g * 4 + jt) * 8 + st) * 2) * 64;
+  uint4* base = gp + piece * 2 * 64;
   base[lane] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
   base[64 + lane] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
   if (bad && flags) atomicOr(flags, AWQ_FLAG_NONFINITE_INPUT);
@@ -867,11 +888,10 @@ hipError_t launch_clip_err(const uint16_t* X, int64_t T, const uint16_t* W, int6
     uint4* gp = xp;
     int* cexp = reinterpret_cast<int*>(reinterpret_cast<char*>(xp) + (size_t)K * kGroup * 4);
     float* cmul = reinterpret_cast<float*>(cexp + K);
-    hipLaunchKernelGGL(k_gram_scale, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, stream, X,
-                       T, K, cexp, cmul);
-    const int64_t threads = (K / kGroup) * 4 * 8 * 64;
-    hipLaunchKernelGGL(k_gram_build, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                       stream, X, T, K, cexp, gp, flags);
+    hipLaunchKernelGGL(k_gram_scale, dim3((unsigned)(K / 64)), dim3(64 * kGramSlices), 0,
+                       stream, X, T, K, cexp, cmul);
+    hipLaunchKernelGGL(k_gram_build, dim3((unsigned)((K / kGroup) * 4 * 8)),
+                       dim3(64 * kGramSlices), 0, stream, X, T, K, cexp, gp, flags);
     hipLaunchKernelGGL(k_clip_err_gram<16>, grid, dim3(1024), 0, stream, gp, cmul, W, N, K, s,
                        clip_steps, n_shrink, (int)sym, w_bit, (double*)err, flags, n_ntiles,
                        per_xcd);
