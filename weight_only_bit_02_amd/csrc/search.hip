@@ -596,7 +596,18 @@ __global__ void __launch_bounds__(64 * kGramSlices)
   const int64_t k = (int64_t)blockIdx.x * 64 + c;  // K is a multiple of 128
   const int64_t t0 = T * sl / kGramSlices, t1 = T * (sl + 1) / kGramSlices;
   double g = 0.0;
-  for (int64_t t = t0; t < t1; ++t) {
+  int64_t t = t0;
+  for (; t + 8 <= t1; t += 8) {  // eight loads in flight before the first is used
+    uint16_t xv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) xv[u] = X[(t + u) * K + k];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const double x = (double)h2f(xv[u]);
+      g = __builtin_fma(x, x, g);
+    }
+  }
+  for (; t < t1; ++t) {
     const double x = (double)h2f(X[t * K + k]);
     g = __builtin_fma(x, x, g);
   }
@@ -631,16 +642,28 @@ __global__ void __launch_bounds__(64 * kGramSlices)
   const int64_t kk = g * kGroup + st * 16 + (lane >> 5) * 8;
   const int64_t t0 = T * sl / kGramSlices, t1 = T * (sl + 1) / kGramSlices;
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int64_t t = t0; t < t1; ++t) {
-    const double xj = (double)h2f(X[t * K + kj]);
-    const uint4 v = *reinterpret_cast<const uint4*>(X + t * K + kk);
+  auto add = [&](uint16_t xh, uint4 v) {
+    const double xj = (double)h2f(xh);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       acc[2 * q] = __builtin_fma(xj, (double)h2f((uint16_t)(w[q] & 0xFFFF)), acc[2 * q]);
       acc[2 * q + 1] = __builtin_fma(xj, (double)h2f((uint16_t)(w[q] >> 16)), acc[2 * q + 1]);
     }
+  };
+  int64_t t = t0;
+  for (; t + 4 <= t1; t += 4) {  // four tokens' loads in flight before the first is used
+    uint16_t xh[4];
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      xh[u] = X[(t + u) * K + kj];
+      v[u] = *reinterpret_cast<const uint4*>(X + (t + u) * K + kk);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) add(xh[u], v[u]);
   }
+  for (; t < t1; ++t) add(X[t * K + kj], *reinterpret_cast<const uint4*>(X + t * K + kk));
   if (sl > 0) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) part[sl - 1][c][lane] = acc[c];
