@@ -229,6 +229,214 @@ __device__ __forceinline__ bool quantize_row(uint4 wv, const StepScales& sc, flo
   return bad;
 }
 
+// NR rows at once: the arithmetic of quantize_row value for value (so the same bits), with
+// the rows' wave-uniform branches shared, one group-size branch and one close-call ballot
+// per stage for all NR rows, so the compiler can interleave the rows' independent chains
+// (DPP reductions, the group parameters, the codes) instead of running one row's latency
+// after the other's.
+template <int NR>
+__device__ __forceinline__ void group_minmax_rows(float (&mn)[NR], float (&mx)[NR], int group) {
+  if (group == 128) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) row16_minmax(mn[r], mx[r]);
+  } else if (group == 64) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) row8_minmax(mn[r], mx[r]);
+  } else {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) quad_minmax(mn[r], mx[r]);
+  }
+}
+
+template <int NR>
+__device__ __forceinline__ void group_max_rows(float (&mx)[NR], int group) {
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    max_quad_xor1(mx[r]);
+    max_quad_xor2(mx[r]);
+  }
+  if (group == 128) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      max_row_ror4(mx[r]);
+      max_row_ror8(mx[r]);
+    }
+  } else if (group == 64) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) max_row_half_mirror(mx[r]);
+  }
+}
+
+// group_params for NR rows: the zero points' close calls share one ballot.
+template <int NR>
+__device__ __forceinline__ void group_params_rows(const float (&mn)[NR], const float (&mx)[NR],
+                                                  float qmax, ScaleDiv sd, bool sym,
+                                                  GroupQ (&g)[NR]) {
+#pragma clang fp contract(off)
+  if (sym) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) g[r] = group_params_sym(mn[r], mx[r], qmax, sd);
+    return;
+  }
+  float qa[NR];
+  bool close[NR];
+  bool any = false;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    g[r].qmax = qmax;
+    float sc = div_small(mx[r] - mn[r], sd.d, sd.y);  // the correctly rounded (mx - mn) / qmax
+    sc = fmaxf(sc, 0x1p-14f);
+    g[r].clamped = sc > 65504.0f;
+    sc = fminf(sc, 65504.0f);
+    g[r].sch = f2h_bits(sc);
+    g[r].scf = h2f(g[r].sch);
+    g[r].rcp = __builtin_amdgcn_rcpf(g[r].scf);
+    // z = rint(-mn / sc_h) as rint_quotients takes it
+    qa[r] = -mn[r] * g[r].rcp;
+    const float fl = __builtin_floorf(qa[r]);
+    const float d = __builtin_fabsf((qa[r] - fl) - 0.5f);
+    close[r] = !(d > __builtin_fabsf(qa[r]) * 0x1p-21f + 0x1p-60f);
+    any |= close[r];
+  }
+  if (__builtin_amdgcn_ballot_w64(any)) {
+    asm volatile("");  // keeps the division in this branch (not speculated into the common path)
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+      if (close[r]) qa[r] = -mn[r] / g[r].scf;  // correctly rounded division
+  }
+#pragma unroll
+  for (int r = 0; r < NR; ++r) g[r].z = __builtin_amdgcn_fmed3f(__builtin_rintf(qa[r]), 0.0f, qmax);
+}
+
+// quant_centered for NR rows of 8 values, each row with its own group parameters.
+template <int NR>
+__device__ __forceinline__ void quant_centered_rows(const float (&w)[NR][8], const GroupQ (&g)[NR],
+                                                    float (&qz)[NR][8]) {
+#pragma clang fp contract(off)
+  bool close[NR][8];
+  bool any = false;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const float half_sc = 0.5f * g[r].scf;  // exact
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      qz[r][i] = __builtin_rintf(w[r][i] * g[r].rcp);
+      const float e = __builtin_fmaf(-qz[r][i], g[r].scf, w[r][i]);
+      close[r][i] = !(__builtin_fabsf(e) < half_sc);
+      any |= close[r][i];
+    }
+  }
+  if (__builtin_amdgcn_ballot_w64(any)) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (close[r][i]) qz[r][i] = __builtin_rintf(w[r][i] / g[r].scf);  // correctly rounded
+  }
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const float lo = -g[r].z, hi = g[r].qmax - g[r].z;  // exact
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qz[r][i] = __builtin_amdgcn_fmed3f(qz[r][i], lo, hi);
+  }
+}
+
+// quantize_row for NR rows (rows[r], weights wv[r], exponent states e_state[r]).
+template <bool CLIP, bool LO, int NR>
+__device__ __forceinline__ bool quantize_rows(const uint4 (&wv)[NR], const StepScales& sc, float rr,
+                                              bool sym, int group, float qmax, ScaleDiv sd,
+                                              int* e_state, int* pe_out, uint16_t* hi_buf,
+                                              uint16_t* lo_buf, const int (&row)[NR], int li,
+                                              float* pg_out) {
+#pragma clang fp contract(off)
+  float wp[NR][8], mn[NR], mx[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const uint32_t wd[4] = {wv[r].x, wv[r].y, wv[r].z, wv[r].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      wp[r][2 * i] = h2f((uint16_t)(wd[i] & 0xFFFF)) * sc.sf[2 * i];
+      wp[r][2 * i + 1] = h2f((uint16_t)(wd[i] >> 16)) * sc.sf[2 * i + 1];
+    }
+    mn[r] = wp[r][0];
+    mx[r] = wp[r][0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) {
+      mn[r] = fminf(mn[r], wp[r][i]);
+      mx[r] = fmaxf(mx[r], wp[r][i]);
+    }
+  }
+  group_minmax_rows<NR>(mn, mx, group);
+  bool bad = false;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    bad |= !__builtin_isfinite(mn[r]) || !__builtin_isfinite(mx[r]);
+    if (CLIP) {
+      mn[r] = rr * mn[r];
+      mx[r] = rr * mx[r];
+    }
+  }
+  GroupQ g[NR];
+  group_params_rows<NR>(mn, mx, qmax, sd, sym, g);
+  float qz[NR][8];
+  quant_centered_rows<NR>(wp, g, qz);
+  float dg[NR][8], dmx[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    dmx[r] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float deq = qz[r][c] * g[r].scf;  // exact: small integer times an fp16
+      dg[r][c] = (wp[r][c] - deq) * sc.rs[c];
+      dmx[r] = fmaxf(dmx[r], __builtin_fabsf(dg[r][c]));
+    }
+  }
+  float P[NR];
+  if constexpr (CLIP) {
+    group_max_rows<NR>(dmx, group);
+    const int gl = group >> 3;  // lanes per group
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      int ex = 0;
+      (void)__builtin_frexpf(dmx[r], &ex);
+      if (!(dmx[r] > 0.0f) || !__builtin_isfinite(dmx[r])) ex = 0;
+      ex = ex < -100 ? -100 : (ex > 100 ? 100 : ex);
+      P[r] = __builtin_ldexpf(1.0f, 14 - ex);
+      if ((li & (gl - 1)) == 0) pg_out[row[r] * 4 + li / gl] = P[r];
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) row16_max(dmx[r]);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int E = search_exponent(dmx[r], e_state[r]);
+      e_state[r] = E;
+      P[r] = __builtin_ldexpf(1.0f, 14 - E);
+      if (li == 0) pe_out[row[r]] = E;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint16_t h2[2], l2[2] = {0, 0};
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float d = dg[r][2 * i + e] * P[r];
+        h2[e] = f2h_bits(d);
+        if constexpr (LO) l2[e] = f2h_bits(d - h2f(h2[e]));
+      }
+      hi[i] = (uint32_t)h2[0] | ((uint32_t)h2[1] << 16);
+      lo[i] = (uint32_t)l2[0] | ((uint32_t)l2[1] << 16);
+    }
+    *reinterpret_cast<uint4*>(&hi_buf[row[r] * kLdsStride + li * 8]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    if constexpr (LO)
+      *reinterpret_cast<uint4*>(&lo_buf[row[r] * kLdsStride + li * 8]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+  }
+  return bad;
+}
+
 // Quantizes step j of rows [row_base, row_base + NROWS) of the tile with NW waves (tid
 // counts their threads from 0), 4 rows per wave per pass.
 template <int NW, bool CLIP, int NROWS, bool LO = true>
@@ -265,12 +473,19 @@ __device__ __forceinline__ bool quantize_tile_group(const uint16_t* W, int64_t N
     for (int i = 0; i < 8; ++i) sc.rs[i] *= cm[i];
   }
   bool bad = false;
+  // passes in pairs: two rows per lane through quantize_rows (kPasses is 1, 2 or 4)
+  constexpr int NR = kPasses >= 2 ? 2 : 1;
 #pragma unroll
-  for (int p = 0; p < kPasses; ++p) {
-    const int row = p * kRowsPerPass + q_row;
-    const uint4 wv = n0 + row < N ? wvs[p] : make_uint4(0, 0, 0, 0);
-    bad |= quantize_row<CLIP, LO>(wv, sc, r, sym, group, qmax, scale_divisor(qmax, sym), e_state[p],
-                              pe_out, hi_buf, lo_buf, row, li, pg_out);
+  for (int p = 0; p < kPasses; p += NR) {
+    uint4 wv[NR];
+    int rows[NR];
+#pragma unroll
+    for (int u = 0; u < NR; ++u) {
+      rows[u] = (p + u) * kRowsPerPass + q_row;
+      wv[u] = n0 + rows[u] < N ? wvs[p + u] : make_uint4(0, 0, 0, 0);
+    }
+    bad |= quantize_rows<CLIP, LO, NR>(wv, sc, r, sym, group, qmax, scale_divisor(qmax, sym),
+                                       &e_state[p], pe_out, hi_buf, lo_buf, rows, li, pg_out);
   }
   return bad;
 }
