@@ -269,7 +269,10 @@ awq_status awq_linear_w4a16_gated_silu_ex(const void* X, int64_t M, const uint32
  *   min/max), quantized from the extremes r_i max and r_i min (fp32), scored by
  *     err_i(n, g) = sum_t ( sum_{k in g} X_tk D_nk )^2,  D = W - Q_{r_i}(W diag(s)) diag(1/s),
  *   and keeps the first minimum. Contraction as in awq_search_scales (D as fp16 hi + lo
- *   against fp16 X on the matrix cores, fp32 accumulation, fp64 reduction).
+ *   against fp16 X on the matrix cores, fp32 accumulation, fp64 reduction). For
+ *   128-channel groups and T > 256 the same score is formed as d^T G d with the group's
+ *   Gram matrix G = X_g^T X_g (fp64 sums, channels balanced by exact powers of two, kept
+ *   as fp16 hi + lo): 2 * 128 instead of 2 * T flop per weight and ratio.
  *   X fp16 [T][K], 1 <= T <= 512 (else AWQ_ERR_BAD_SHAPE: one block scores all tokens);
  *   W fp16 [N][K]; s fp16 [K] or NULL; 1 <= n_shrink <= min(clip_steps, 256).
  *   clip_idx uint8 [N][G] out (pass to awq_quantize_pack_clipped); err fp64 [N][G]
@@ -277,7 +280,8 @@ awq_status awq_linear_w4a16_gated_silu_ex(const void* X, int64_t M, const uint32
  *   awq_clip_search_workspace_size bytes (the errors: n_shrink N G doubles for
  *   128-channel groups, n_shrink N G w floats for smaller ones, w = 4 per-wave partials
  *   for T <= 256, else 8; and a copy of X in MFMA operand order, T rounded up to 64
- *   tokens; 0 for an unsupported config or shape, T included), 16-byte aligned. Accuracy: each group's D is scaled by a power of two
+ *   tokens, or the Gram matrices (512 B per channel) and channel scales, whichever is
+ *   larger; 0 for an unsupported config or shape, T included), 16-byte aligned. Accuracy: each group's D is scaled by a power of two
  *   from its own largest |D| before the fp16 hi + lo split, so every group keeps 22
  *   significant bits whatever its magnitude or the code width.
  *   flags: NONFINITE_INPUT (a NaN or Inf in W or s, or in X through a non-finite error).
