@@ -14,7 +14,8 @@
 
 namespace awq {
 
-constexpr int kStatRows = 64;  // tokens summed per thread before the atomic add
+constexpr int kStatRows = 8;     // tokens summed per thread before the atomic add
+constexpr int kStatThreads = 64;  // one wave per block: many waves even for small K
 
 __global__ void k_zero_u64(unsigned long long* __restrict__ p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
@@ -22,18 +23,26 @@ __global__ void k_zero_u64(unsigned long long* __restrict__ p, int64_t n) {
     p[i] = 0ull;
 }
 
-// Thread = 8 consecutive channels x one slice of kStatRows tokens.
-__global__ void __launch_bounds__(256) k_act_sums(const uint16_t* __restrict__ X, int64_t T,
-                                                  int64_t K, unsigned long long* __restrict__ u,
-                                                  uint32_t* __restrict__ flags) {
+// Thread = 8 consecutive channels x one slice of kStatRows tokens, all of the slice's loads
+// issued before the first is used (rows past T read row T - 1 and are not added).
+__global__ void __launch_bounds__(kStatThreads)
+    k_act_sums(const uint16_t* __restrict__ X, int64_t T, int64_t K,
+               unsigned long long* __restrict__ u, uint32_t* __restrict__ flags) {
   const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // 8-channel chunk
   if (c * 8 >= K) return;
   const int64_t t0 = (int64_t)blockIdx.y * kStatRows;
-  const int64_t t1 = t0 + kStatRows < T ? t0 + kStatRows : T;
+  uint4 vs[kStatRows];
+#pragma unroll
+  for (int r = 0; r < kStatRows; ++r) {
+    const int64_t t = t0 + r < T ? t0 + r : T - 1;
+    vs[r] = *reinterpret_cast<const uint4*>(X + t * K + c * 8);
+  }
   int64_t acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   bool bad = false;
-  for (int64_t t = t0; t < t1; ++t) {
-    const uint4 v = *reinterpret_cast<const uint4*>(X + t * K + c * 8);
+#pragma unroll
+  for (int r = 0; r < kStatRows; ++r) {
+    if (t0 + r >= T) break;
+    const uint4 v = vs[r];
     const uint32_t d[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -79,8 +88,9 @@ hipError_t launch_zero_u64(unsigned long long* p, int64_t n, hipStream_t stream)
 hipError_t launch_act_sums(const uint16_t* X, int64_t T, int64_t K, unsigned long long* u,
                            uint32_t* flags, hipStream_t stream) {
   const int64_t chunks = K / 8;
-  dim3 grid((unsigned)((chunks + 255) / 256), (unsigned)((T + kStatRows - 1) / kStatRows));
-  hipLaunchKernelGGL(k_act_sums, grid, dim3(256), 0, stream, X, T, K, u, flags);
+  dim3 grid((unsigned)((chunks + kStatThreads - 1) / kStatThreads),
+            (unsigned)((T + kStatRows - 1) / kStatRows));
+  hipLaunchKernelGGL(k_act_sums, grid, dim3(kStatThreads), 0, stream, X, T, K, u, flags);
   return hipGetLastError();
 }
 
