@@ -66,16 +66,20 @@ __global__ void k_act_finalize(const unsigned long long* __restrict__ u, int64_t
   act[k] = ((double)u[k] * 0x1p-24) / (double)T;
 }
 
+// One thread per (grid point i, channel k): the n_grid pows of a channel run in parallel.
 __global__ void k_scalegen(const double* __restrict__ act, int64_t K, int n_grid,
                            uint16_t* __restrict__ s_grid) {
-  const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (k >= K) return;
-  const double a = fmax(act[k], 0x1p-14);
-  s_grid[k] = 0x3C00;  // alpha = 0: s = 1
-  for (int i = 1; i < n_grid; ++i) {
-    const double alpha = (double)i / (double)n_grid;
-    s_grid[(int64_t)i * K + k] = f64_to_f16_rne(pow(a, alpha));
+  const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (u >= (int64_t)n_grid * K) return;
+  const int i = (int)(u / K);
+  const int64_t k = u % K;
+  if (i == 0) {
+    s_grid[k] = 0x3C00;  // alpha = 0: s = 1
+    return;
   }
+  const double a = fmax(act[k], 0x1p-14);
+  const double alpha = (double)i / (double)n_grid;
+  s_grid[u] = f64_to_f16_rne(pow(a, alpha));
 }
 
 hipError_t launch_zero_u64(unsigned long long* p, int64_t n, hipStream_t stream) {
@@ -103,7 +107,8 @@ hipError_t launch_act_finalize(const unsigned long long* u, int64_t T, int64_t K
 
 hipError_t launch_scalegen(const double* act, int64_t K, int n_grid, uint16_t* s_grid,
                            hipStream_t stream) {
-  hipLaunchKernelGGL(k_scalegen, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, stream, act, K,
+  const int64_t n = (int64_t)n_grid * K;
+  hipLaunchKernelGGL(k_scalegen, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, act, K,
                      n_grid, s_grid);
   return hipGetLastError();
 }
