@@ -795,44 +795,46 @@ __global__ void __launch_bounds__(NW * 64)
 // the products hi hi, lo hi and hi lo on the matrix cores (fp32), and err = sum_j D'_j V_j
 // with D'_j = hi + lo (exact in fp32).
 
-// Both Gram kernels split the tokens over kGramSlices thread slices (contiguous token
-// ranges) and add the slices' fp64 partials in slice order through LDS, so each sum is
-// formed in a fixed order and enough waves are in flight to cover the load latency.
+// The Gram kernels split the tokens over thread slices (contiguous token ranges) and add
+// the slices' fp64 partials in slice order through LDS, so each sum is formed in a fixed
+// order and enough waves are in flight to cover the load latency.
 constexpr int kGramSlices = 8;
 
 // e_k of every channel: G_kk = sum_t X_tk^2 (fp64) = m 2^E, m in [1/2, 1), e_k = ceil(E / 2),
 // so G_kk 2^(-2 e_k) lies in [1/4, 1); cmul[k] = 2^e_k (multiplies D); a zero or non-finite
-// G_kk takes e_k = 0. Block: 64 channels x kGramSlices token slices.
-__global__ void __launch_bounds__(64 * kGramSlices)
+// G_kk takes e_k = 0. Block: 64 channels (8 threads of 8 channels, 16-byte loads) x 64 token
+// slices, the slices' fp64 partials added in slice order through LDS.
+constexpr int kScaleSlices = 64;
+__global__ void __launch_bounds__(8 * kScaleSlices)
     k_gram_scale(const uint16_t* __restrict__ X, int64_t T, int64_t K, int* __restrict__ cexp,
                  float* __restrict__ cmul) {
-  __shared__ double part[kGramSlices][64];
-  const int c = threadIdx.x & 63, sl = threadIdx.x >> 6;
-  const int64_t k = (int64_t)blockIdx.x * 64 + c;  // K is a multiple of 128
-  const int64_t t0 = T * sl / kGramSlices, t1 = T * (sl + 1) / kGramSlices;
-  double g = 0.0;
-  int64_t t = t0;
-  for (; t + 8 <= t1; t += 8) {  // eight loads in flight before the first is used
-    uint16_t xv[8];
+  __shared__ double part[kScaleSlices][64];
+  const int q = threadIdx.x & 7, sl = threadIdx.x >> 3;
+  const int64_t k0 = (int64_t)blockIdx.x * 64 + q * 8;  // K is a multiple of 128
+  const int64_t t0 = T * sl / kScaleSlices, t1 = T * (sl + 1) / kScaleSlices;
+  double g[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int64_t t = t0; t < t1; ++t) {
+    const uint4 v = *reinterpret_cast<const uint4*>(X + t * K + k0);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int u = 0; u < 8; ++u) xv[u] = X[(t + u) * K + k];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const double x = (double)h2f(xv[u]);
-      g = __builtin_fma(x, x, g);
+    for (int i = 0; i < 4; ++i) {
+      const double a = (double)h2f((uint16_t)(w[i] & 0xFFFF));
+      const double b = (double)h2f((uint16_t)(w[i] >> 16));
+      g[2 * i] = __builtin_fma(a, a, g[2 * i]);
+      g[2 * i + 1] = __builtin_fma(b, b, g[2 * i + 1]);
     }
   }
-  for (; t < t1; ++t) {
-    const double x = (double)h2f(X[t * K + k]);
-    g = __builtin_fma(x, x, g);
-  }
-  part[sl][c] = g;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) part[sl][q * 8 + i] = g[i];
   __syncthreads();
-  if (sl == 0) {
-    for (int u = 1; u < kGramSlices; ++u) g += part[u][c];
+  if (threadIdx.x < 64) {
+    const int c = threadIdx.x;
+    double tot = 0.0;
+    for (int u = 0; u < kScaleSlices; ++u) tot += part[u][c];
     int E = 0;
-    if (g > 0.0 && __builtin_isfinite(g)) (void)__builtin_frexp(g, &E);
+    if (tot > 0.0 && __builtin_isfinite(tot)) (void)__builtin_frexp(tot, &E);
     const int e = (E + 1) >> 1;  // ceil(E / 2), E may be negative
+    const int64_t k = (int64_t)blockIdx.x * 64 + c;
     cexp[k] = e;
     cmul[k] = __builtin_ldexpf(1.0f, e);
   }
@@ -1126,7 +1128,7 @@ hipError_t launch_clip_err(const uint16_t* X, int64_t T, const uint16_t* W, int6
     uint4* gp = xp;
     int* cexp = reinterpret_cast<int*>(reinterpret_cast<char*>(xp) + (size_t)K * kGroup * 4);
     float* cmul = reinterpret_cast<float*>(cexp + K);
-    hipLaunchKernelGGL(k_gram_scale, dim3((unsigned)(K / 64)), dim3(64 * kGramSlices), 0,
+    hipLaunchKernelGGL(k_gram_scale, dim3((unsigned)(K / 64)), dim3(8 * kScaleSlices), 0,
                        stream, X, T, K, cexp, cmul);
     hipLaunchKernelGGL(k_gram_build, dim3((unsigned)((K / kGroup) * 4 * 8)),
                        dim3(64 * kGramSlices), 0, stream, X, T, K, cexp, gp, flags);
